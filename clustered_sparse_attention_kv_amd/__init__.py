@@ -1,0 +1,256 @@
+"""Cluster-granular sparse KV recall on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding of ``libkvcluster.so`` (C ABI declared in
+``include/kvcluster.h``). Every step of the path runs in the library's HIP
+kernels; this module only checks tensor shapes, passes device pointers and the
+current stream, and turns status codes into exceptions. PyTorch supplies the
+device memory and streams.
+
+There is no CPU fallback: when the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvcluster.so")
+
+KVC_F32, KVC_BF16 = 0, 1
+HEAD_DIM, MAX_C, MAX_G = 128, 512, 8
+
+_lib = None
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class _Index(C.Structure):
+    _fields_ = [("heads", C.c_int32), ("d", C.c_int32), ("C", C.c_int32), ("capacity", C.c_int32),
+                ("dtype", C.c_int32), ("n_build", C.c_int32), ("n_tokens", C.c_int32), ("reserved", C.c_int32),
+                ("centroids", C.c_void_p), ("centroids_op", C.c_void_p), ("labels", C.c_void_p),
+                ("sizes", C.c_void_p), ("offsets", C.c_void_p), ("token_ids", C.c_void_p),
+                ("app_offsets", C.c_void_p), ("app_ids", C.c_void_p), ("dev_flags", C.c_void_p)]
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with clustered_sparse_attention_kv_amd.build_lib()")
+        L = C.CDLL(LIB_PATH)
+        p, i, sz, f = C.c_void_p, C.c_int, C.c_size_t, C.c_float
+        L.kv_cluster_cpad.argtypes = [i]
+        L.kv_cluster_cpad.restype = i
+        L.kv_cluster_build_workspace_bytes.argtypes = [i, i, i, i]
+        L.kv_cluster_build_workspace_bytes.restype = sz
+        L.kv_cluster_build.argtypes = [p, p, i, i, p, p, sz, p]
+        L.kv_cluster_append.argtypes = [p, p, p, p, p, i, p]
+        L.kv_cluster_select.argtypes = [p, p, i, i, p, p, p]
+        L.kv_sparse_decode_workspace_bytes.argtypes = [i, i, i, i]
+        L.kv_sparse_decode_workspace_bytes.restype = sz
+        L.kv_sparse_decode.argtypes = [p, i, p, p, i, i, i, i, p, p, i, f, p, p, sz, p]
+        L.kv_cluster_export_csr.argtypes = [p, p, p, p]
+        L.kv_cluster_debug_assign.argtypes = [p, p, i, p, p, p, p, p, sz, p]
+        L.kv_cluster_debug_update.argtypes = [p, p, i, p, sz, p]
+        L.kv_cluster_status_string.argtypes = [i]
+        L.kv_cluster_status_string.restype = C.c_char_p
+        for name in ("kv_cluster_build", "kv_cluster_append", "kv_cluster_select", "kv_sparse_decode",
+                     "kv_cluster_export_csr", "kv_cluster_debug_assign", "kv_cluster_debug_update"):
+            getattr(L, name).restype = i
+        _lib = L
+    return _lib
+
+
+def build_lib() -> str:
+    from ._build import build
+    return build()
+
+
+def status_string(status: int) -> str:
+    return lib().kv_cluster_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise KvcError(status, what)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return KVC_BF16
+    if t == torch.float32:
+        return KVC_F32
+    raise TypeError(f"unsupported element type {t} (bfloat16 or float32)")
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the library must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> C.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def cpad(C_: int) -> int:
+    return lib().kv_cluster_cpad(C_)
+
+
+def build_workspace_bytes(heads: int, L: int, C_: int, iters: int) -> int:
+    return lib().kv_cluster_build_workspace_bytes(heads, L, C_, iters)
+
+
+def decode_workspace_bytes(heads: int, q_heads: int, B: int, d: int = HEAD_DIM) -> int:
+    return lib().kv_sparse_decode_workspace_bytes(heads, q_heads, d, B)
+
+
+class ClusterIndex:
+    """Device memory of one cluster index (``kvc_index``), allocated with torch."""
+
+    def __init__(self, heads: int, C_: int, capacity: int, dtype: torch.dtype = torch.bfloat16,
+                 d: int = HEAD_DIM, device="cuda"):
+        self.heads, self.C, self.capacity, self.d, self.dtype = heads, C_, capacity, d, dtype
+        i32 = dict(dtype=torch.int32, device=device)
+        self.centroids = torch.zeros(heads, C_, d, dtype=torch.float32, device=device)
+        self.centroids_op = torch.zeros(heads, cpad(C_), d, dtype=dtype, device=device)
+        self.labels = torch.full((heads, capacity), -1, **i32)
+        self.sizes = torch.zeros(heads, C_, **i32)
+        self.offsets = torch.zeros(heads, C_ + 1, **i32)
+        self.token_ids = torch.full((heads, capacity), -1, **i32)
+        self.app_offsets = torch.zeros(heads, C_ + 1, **i32)
+        self.app_ids = torch.full((heads, capacity), -1, **i32)
+        self.dev_flags = torch.zeros(1, **i32)
+        self._s = _Index(heads, d, C_, capacity, _dtype_code(dtype), 0, 0, 0,
+                         self.centroids.data_ptr(), self.centroids_op.data_ptr(), self.labels.data_ptr(),
+                         self.sizes.data_ptr(), self.offsets.data_ptr(), self.token_ids.data_ptr(),
+                         self.app_offsets.data_ptr(), self.app_ids.data_ptr(), self.dev_flags.data_ptr())
+
+    @property
+    def n_build(self) -> int:
+        return self._s.n_build
+
+    @property
+    def n_tokens(self) -> int:
+        return self._s.n_tokens
+
+    def ref(self):
+        return C.byref(self._s)
+
+
+def _cache_check(idx: ClusterIndex, t: torch.Tensor, name: str):
+    if t.dtype != idx.dtype or tuple(t.shape) != (idx.heads, idx.capacity, idx.d):
+        raise ValueError(f"{name} must be {idx.dtype} [{idx.heads}, {idx.capacity}, {idx.d}], got "
+                         f"{t.dtype} {list(t.shape)}")
+
+
+def build(idx: ClusterIndex, keys: torch.Tensor, L: int, iters: int, init_idx: torch.Tensor,
+          workspace: torch.Tensor | None = None, stream=None):
+    """kv_cluster_build: cluster the first L rows of keys [heads, capacity, d]."""
+    _cache_check(idx, keys, "keys")
+    if init_idx.dtype != torch.int32 or tuple(init_idx.shape) != (idx.heads, idx.C):
+        raise ValueError("init_idx must be int32 [heads, C]")
+    need = build_workspace_bytes(idx.heads, L, idx.C, iters)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=keys.device)
+    _check(lib().kv_cluster_build(idx.ref(), _ptr(keys), L, iters, _ptr(init_idx), _ptr(workspace),
+                                  workspace.numel(), _stream(stream)), "kv_cluster_build")
+    return workspace
+
+
+def append(idx: ClusterIndex, k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+           v_new: torch.Tensor, stream=None):
+    """kv_cluster_append: k_new, v_new [heads, n_new, d]."""
+    _cache_check(idx, k_cache, "k_cache")
+    _cache_check(idx, v_cache, "v_cache")
+    if k_new.dim() == 2:
+        k_new, v_new = k_new.unsqueeze(1), v_new.unsqueeze(1)
+    n_new = k_new.shape[1]
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        if t.dtype != idx.dtype or tuple(t.shape) != (idx.heads, n_new, idx.d):
+            raise ValueError(f"{nm} must be {idx.dtype} [{idx.heads}, n_new, {idx.d}]")
+    _check(lib().kv_cluster_append(idx.ref(), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), n_new,
+                                   _stream(stream)), "kv_cluster_append")
+
+
+def select(idx: ClusterIndex, q: torch.Tensor, B: int, sel_ids: torch.Tensor | None = None,
+           sel_count: torch.Tensor | None = None, stream=None):
+    """kv_cluster_select: q [q_heads, d] -> (sel_ids [heads, B], sel_count [heads])."""
+    if q.dtype != idx.dtype or q.dim() != 2 or q.shape[1] != idx.d:
+        raise ValueError(f"q must be {idx.dtype} [q_heads, {idx.d}]")
+    if sel_ids is None:
+        sel_ids = torch.empty(idx.heads, B, dtype=torch.int32, device=q.device)
+    if sel_count is None:
+        sel_count = torch.empty(idx.heads, dtype=torch.int32, device=q.device)
+    if sel_ids.dtype != torch.int32 or tuple(sel_ids.shape) != (idx.heads, B) or sel_count.numel() != idx.heads:
+        raise ValueError("sel_ids must be int32 [heads, B], sel_count int32 [heads]")
+    _check(lib().kv_cluster_select(idx.ref(), _ptr(q), q.shape[0], B, _ptr(sel_ids), _ptr(sel_count),
+                                   _stream(stream)), "kv_cluster_select")
+    return sel_ids, sel_count
+
+
+def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, sel_ids: torch.Tensor,
+                  sel_count: torch.Tensor, scale: float, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, stream=None):
+    """kv_sparse_decode: attention of q [q_heads, d] over the selected rows -> fp32 [q_heads, d].
+
+    The workspace must be zero-filled before its first use (torch.zeros)."""
+    heads, capacity, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype or q.dtype != k_cache.dtype:
+        raise ValueError("q, k_cache and v_cache must share a type; k and v caches a shape")
+    B = sel_ids.shape[1]
+    if sel_ids.dtype != torch.int32 or sel_ids.shape[0] != heads or sel_count.numel() != heads:
+        raise ValueError("sel_ids must be int32 [heads, B], sel_count int32 [heads]")
+    if out is None:
+        out = torch.empty(q.shape[0], d, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.zeros(max(decode_workspace_bytes(heads, q.shape[0], B, d), 1), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().kv_sparse_decode(_ptr(q), q.shape[0], _ptr(k_cache), _ptr(v_cache), _dtype_code(q.dtype), heads,
+                                  capacity, d, _ptr(sel_ids), _ptr(sel_count), B, float(scale), _ptr(out),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)), "kv_sparse_decode")
+    return out
+
+
+def export_csr(idx: ClusterIndex, stream=None):
+    """Canonical index (built + appended parts): (offsets [heads, C+1], token_ids [heads, capacity])."""
+    off = torch.empty(idx.heads, idx.C + 1, dtype=torch.int32, device=idx.labels.device)
+    ids = torch.full((idx.heads, idx.capacity), -1, dtype=torch.int32, device=idx.labels.device)
+    _check(lib().kv_cluster_export_csr(idx.ref(), _ptr(off), _ptr(ids), _stream(stream)), "kv_cluster_export_csr")
+    return off, ids
+
+
+def debug_assign(idx: ClusterIndex, keys: torch.Tensor, L: int, chat: torch.Tensor, want_top2: bool = False,
+                 stream=None):
+    """One assignment under the operand chat [heads, cpad(C), d] -> (labels, top2, flagged per head)."""
+    _cache_check(idx, keys, "keys")
+    if chat.dtype != idx.dtype or tuple(chat.shape) != (idx.heads, cpad(idx.C), idx.d):
+        raise ValueError("chat must match centroids_op")
+    labels = torch.full((idx.heads, idx.capacity), -1, dtype=torch.int32, device=keys.device)
+    top2 = torch.empty(idx.heads, L, 2, dtype=torch.float32, device=keys.device) if want_top2 else None
+    flagged = torch.zeros(idx.heads, dtype=torch.int32, device=keys.device)
+    ws = torch.empty(max(build_workspace_bytes(idx.heads, L, idx.C, 1), 1), dtype=torch.uint8, device=keys.device)
+    _check(lib().kv_cluster_debug_assign(idx.ref(), _ptr(keys), L, _ptr(chat), _ptr(labels), _ptr(top2),
+                                         _ptr(flagged), _ptr(ws), ws.numel(), _stream(stream)),
+           "kv_cluster_debug_assign")
+    return labels, top2, flagged
+
+
+def debug_update(idx: ClusterIndex, keys: torch.Tensor, L: int, stream=None):
+    """Index arrays and centroid update from idx.labels (first L tokens)."""
+    _cache_check(idx, keys, "keys")
+    ws = torch.empty(max(build_workspace_bytes(idx.heads, L, idx.C, 1), 1), dtype=torch.uint8, device=keys.device)
+    _check(lib().kv_cluster_debug_update(idx.ref(), _ptr(keys), L, _ptr(ws), ws.numel(), _stream(stream)),
+           "kv_cluster_debug_update")

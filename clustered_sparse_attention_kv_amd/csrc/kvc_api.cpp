@@ -1,0 +1,199 @@
+// C ABI of kvcluster: argument checks (before anything is enqueued),
+// workspace carving and launch sequencing on the caller's stream. The library
+// allocates nothing and never synchronises.
+#include "kvcluster.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kvc_internal.h"
+
+using namespace kvc;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool index_ok(const kvc_index* idx) {
+  return idx && idx->centroids && idx->centroids_op && idx->labels && idx->sizes && idx->offsets && idx->token_ids &&
+         idx->app_offsets && idx->app_ids && idx->dev_flags && idx->heads >= 1 && idx->capacity >= 1 && idx->C >= 1 &&
+         (idx->dtype == KVC_F32 || idx->dtype == KVC_BF16);
+}
+
+int index_support(const kvc_index* idx) {
+  if (idx->d != KVC_HEAD_DIM || idx->C > KVC_MAX_C) return KVC_ERR_UNSUPPORTED;
+  if ((long long)idx->heads * idx->capacity >= (1ll << 31)) return KVC_ERR_UNSUPPORTED;
+  return KVC_OK;
+}
+
+struct BuildWs {
+  uint32_t* qcount;  // [iters, heads]
+  int32_t* queue;    // [heads, L]
+  int32_t* hist;     // [heads, nblk, C]
+  size_t bytes;
+};
+
+BuildWs carve_build(void* base, int heads, int L, int C, int iters) {
+  BuildWs w{};
+  size_t o = 0;
+  char* b = static_cast<char*>(base);
+  w.qcount = reinterpret_cast<uint32_t*>(b + o);
+  o = align_up(o + sizeof(uint32_t) * (size_t)iters * heads);
+  w.queue = reinterpret_cast<int32_t*>(b + o);
+  o = align_up(o + sizeof(int32_t) * (size_t)heads * L);
+  w.hist = reinterpret_cast<int32_t*>(b + o);
+  o = align_up(o + sizeof(int32_t) * (size_t)heads * csr_blocks(L) * C);
+  w.bytes = o;
+  return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int kv_cluster_cpad(int C) { return C < 1 ? 0 : (C + 31) / 32 * 32; }
+
+size_t kv_cluster_build_workspace_bytes(int heads, int L, int C, int iters) {
+  if (heads < 1 || L < 1 || C < 1 || iters < 1) return 0;
+  return carve_build(nullptr, heads, L, C, iters).bytes;
+}
+
+int kv_cluster_build(kvc_index* idx, const void* keys, int L, int iters, const int32_t* init_idx, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!index_ok(idx) || !keys || !init_idx || !ws) return KVC_ERR_INVALID_ARG;
+  if (int s = index_support(idx)) return s;
+  const int H = idx->heads, C = idx->C, cap = idx->capacity, cpad = kv_cluster_cpad(C);
+  if (L < C || L > cap || iters < 1 || iters > 100000) return KVC_ERR_INVALID_ARG;
+  const BuildWs w = carve_build(ws, H, L, C, iters);
+  if (ws_bytes < w.bytes) return KVC_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const long long hs = (long long)cap * KVC_HEAD_DIM;
+  hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.qcount), (size_t)iters * H, 0, st);
+  if (e == hipSuccess) e = launch_fill_i32(idx->app_offsets, (size_t)H * (C + 1), 0, st);
+  if (e == hipSuccess)
+    e = launch_init_centroids(idx->dtype, keys, hs, H, L, init_idx, C, cpad, idx->centroids, idx->centroids_op,
+                              idx->dev_flags, st);
+  for (int t = 0; t < iters && e == hipSuccess; ++t) {
+    e = launch_assign(idx->dtype, keys, hs, H, L, idx->centroids_op, C, cpad, idx->labels, cap, w.queue,
+                      w.qcount + (size_t)t * H, nullptr, st);
+    if (e == hipSuccess)
+      e = launch_csr(idx->labels, cap, H, L, C, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, st);
+    if (e == hipSuccess)
+      e = launch_update(idx->dtype, keys, hs, H, C, cpad, idx->sizes, idx->offsets, idx->token_ids, cap,
+                        idx->centroids, idx->centroids_op, st);
+  }
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  idx->n_build = L;
+  idx->n_tokens = L;
+  return KVC_OK;
+}
+
+int kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const void* chat, int32_t* labels,
+                            float* top2, int32_t* flagged, void* ws, size_t ws_bytes, void* stream) {
+  if (!index_ok(idx) || !keys || !chat || !labels || !ws) return KVC_ERR_INVALID_ARG;
+  if (int s = index_support(idx)) return s;
+  const int H = idx->heads, C = idx->C, cap = idx->capacity, cpad = kv_cluster_cpad(C);
+  if (L < 1 || L > cap) return KVC_ERR_INVALID_ARG;
+  const BuildWs w = carve_build(ws, H, L, C, 1);
+  if (ws_bytes < w.bytes) return KVC_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.qcount), (size_t)H, 0, st);
+  if (e == hipSuccess)
+    e = launch_assign(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, L, chat, C, cpad, labels, cap, w.queue,
+                      w.qcount, top2, st);
+  if (e == hipSuccess && flagged)
+    e = hipMemcpyAsync(flagged, w.qcount, sizeof(int32_t) * H, hipMemcpyDeviceToDevice, st);
+  return hip_status(e);
+}
+
+int kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, size_t ws_bytes, void* stream) {
+  if (!index_ok(idx) || !keys || !ws) return KVC_ERR_INVALID_ARG;
+  if (int s = index_support(idx)) return s;
+  const int H = idx->heads, C = idx->C, cap = idx->capacity, cpad = kv_cluster_cpad(C);
+  if (L < 1 || L > cap) return KVC_ERR_INVALID_ARG;
+  const BuildWs w = carve_build(ws, H, L, C, 1);
+  if (ws_bytes < w.bytes) return KVC_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_csr(idx->labels, cap, H, L, C, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, st);
+  if (e == hipSuccess)
+    e = launch_update(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, C, cpad, idx->sizes, idx->offsets,
+                      idx->token_ids, cap, idx->centroids, idx->centroids_op, st);
+  return hip_status(e);
+}
+
+int kv_cluster_append(kvc_index* idx, void* k_cache, void* v_cache, const void* k_new, const void* v_new, int n_new,
+                      void* stream) {
+  if (!index_ok(idx) || !k_cache || !v_cache || !k_new || !v_new || n_new < 1) return KVC_ERR_INVALID_ARG;
+  if (int s = index_support(idx)) return s;
+  if (idx->n_build < 1) return KVC_ERR_INVALID_ARG;
+  if ((long long)idx->n_tokens + n_new > idx->capacity) return KVC_ERR_CAPACITY;
+  const int C = idx->C, cap = idx->capacity;
+  hipError_t e = launch_append(idx->dtype, k_cache, v_cache, (long long)cap * KVC_HEAD_DIM, idx->heads, k_new, v_new,
+                               n_new, idx->n_tokens, idx->n_build, idx->centroids_op, C, kv_cluster_cpad(C),
+                               idx->labels, cap, idx->sizes, idx->app_offsets, idx->app_ids,
+                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  idx->n_tokens += n_new;
+  return KVC_OK;
+}
+
+int kv_cluster_select(const kvc_index* idx, const void* q, int q_heads, int B, int32_t* sel_ids, int32_t* sel_count,
+                      void* stream) {
+  if (!index_ok(idx) || !q || !sel_ids || !sel_count || B < 1 || q_heads < 1) return KVC_ERR_INVALID_ARG;
+  if (int s = index_support(idx)) return s;
+  if (idx->n_build < 1 || q_heads % idx->heads != 0) return KVC_ERR_INVALID_ARG;
+  const int G = q_heads / idx->heads;
+  if (G > KVC_MAX_G) return KVC_ERR_UNSUPPORTED;
+  if ((long long)idx->heads * B >= (1ll << 31)) return KVC_ERR_INVALID_ARG;
+  return hip_status(launch_select(idx->dtype, q, G, idx->centroids, idx->heads, idx->C, idx->sizes, idx->offsets,
+                                  idx->token_ids, idx->app_offsets, idx->app_ids, idx->capacity, B, sel_ids,
+                                  sel_count, static_cast<hipStream_t>(stream)));
+}
+
+size_t kv_sparse_decode_workspace_bytes(int heads, int q_heads, int d, int B) {
+  if (heads < 1 || q_heads < heads || d < 1 || B < 1) return 0;
+  const int G = q_heads / heads;
+  const size_t nsplit = (size_t)(B + DEC_TOK - 1) / DEC_TOK;
+  return align_up(sizeof(uint32_t) * (size_t)heads) + align_up(sizeof(float) * heads * nsplit * G * (d + 2));
+}
+
+int kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
+                     int capacity, int d, const int32_t* sel_ids, const int32_t* sel_count, int B, float scale,
+                     float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !sel_ids || !sel_count || !out || !ws) return KVC_ERR_INVALID_ARG;
+  if (heads < 1 || q_heads < 1 || capacity < 1 || B < 1 || q_heads % heads != 0) return KVC_ERR_INVALID_ARG;
+  if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_INVALID_ARG;
+  if (d != KVC_HEAD_DIM) return KVC_ERR_UNSUPPORTED;
+  const int G = q_heads / heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KVC_ERR_UNSUPPORTED;
+  if ((long long)heads * B >= (1ll << 31) || (B + DEC_TOK - 1) / DEC_TOK > 65535) return KVC_ERR_INVALID_ARG;
+  if (ws_bytes < kv_sparse_decode_workspace_bytes(heads, q_heads, d, B)) return KVC_ERR_WORKSPACE;
+  uint32_t* counters = static_cast<uint32_t*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(sizeof(uint32_t) * (size_t)heads));
+  return hip_status(launch_decode(dtype, q, G, k_cache, v_cache, (long long)capacity * d, heads, sel_ids, sel_count, B,
+                                  scale, out, part, counters, static_cast<hipStream_t>(stream)));
+}
+
+int kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token_ids, void* stream) {
+  if (!index_ok(idx) || !offsets || !token_ids) return KVC_ERR_INVALID_ARG;
+  if (int s = index_support(idx)) return s;
+  return hip_status(launch_export_csr(idx->heads, idx->C, idx->offsets, idx->token_ids, idx->app_offsets,
+                                      idx->app_ids, idx->capacity, offsets, token_ids,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+const char* kv_cluster_status_string(int status) {
+  switch (status) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_INVALID_ARG: return "invalid argument";
+    case KVC_ERR_UNSUPPORTED: return "unsupported by the GPU path (d must be 128, C <= 512, G in {1,2,4,8})";
+    case KVC_ERR_WORKSPACE: return "workspace too small";
+    case KVC_ERR_CAPACITY: return "index capacity exceeded";
+    case KVC_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

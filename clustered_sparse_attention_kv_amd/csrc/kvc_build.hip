@@ -1,0 +1,518 @@
+// Prefill clustering kernels: initial centroids, cosine assignment on the
+// matrix cores with a certified argmax, fp64 re-scoring of uncertified keys,
+// the stable counting sort that builds the cluster index, and the centroid
+// update fused with normalisation.
+//
+// Method: ClusterKV (arXiv 2412.03213), paper summary page sections III.B
+// "Clustering in the Semantic Space" (cosine k-means over keys), Sys-B
+// "Semantic Clustering" (batched per-head clustering; accumulate assigned keys
+// and counts, then divide) and Sys-C "Selection and Indexing" (sizes, prefix
+// sums, token ids sorted by cluster).
+#include "kvc_device.h"
+#include "kvc_internal.h"
+
+namespace kvc {
+
+// ---------------------------------------------------------------------------
+// Normalisation of one centroid row held by one wave (2 channels per lane).
+// norm = sqrt(fp64 sum of c_j^2 over ascending j); chat_j = c_j / norm rounded
+// once to the operand type (zero when the norm is zero). The ascending sum is
+// one lane's chain so its order is fixed.
+template <typename OT>
+__device__ void normalize_row(const float c0, const float c1, float* lds_row, OT* out_row) {
+  const int lane = lane_id();
+  lds_row[2 * lane] = c0;
+  lds_row[2 * lane + 1] = c1;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  double ss = 0.0;
+  if (lane == 0) {
+    for (int j = 0; j < D; ++j) {
+      const double v = (double)lds_row[j];
+      ss = fma(v, v, ss);
+    }
+  }
+  // broadcast lane 0's sum
+  const int lo = __builtin_amdgcn_readfirstlane((int)(__double_as_longlong(ss) & 0xFFFFFFFFll));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(__double_as_longlong(ss) >> 32));
+  ss = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
+  const double nrm = sqrt(ss);
+  const double v0 = nrm > 0.0 ? (double)c0 / nrm : 0.0;
+  const double v1 = nrm > 0.0 ? (double)c1 / nrm : 0.0;
+  store_op(out_row, 2 * lane, v0);
+  store_op(out_row, 2 * lane + 1, v1);
+}
+
+// ---------------------------------------------------------------------------
+// a1 + a2: initial centroids c_k = K[init_idx[k]] (exact copy to fp32) and
+// their normalised operand. One wave per centroid row, 4 rows per block.
+// Rows k in [C, cpad) of the operand are zeroed.
+template <typename KT>
+__global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restrict__ keys, long long head_stride,
+                                                             int L, const int32_t* __restrict__ init_idx, int C,
+                                                             int cpad, float* __restrict__ cent, KT* __restrict__ chat,
+                                                             int32_t* __restrict__ dev_flags) {
+  __shared__ float rows[4][D];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.y;
+  const int k = blockIdx.x * 4 + w;
+  if (k >= cpad) return;
+  KT* out = chat + ((size_t)h * cpad + k) * D;
+  if (k >= C) {
+    store_op(out, 2 * lane, 0.0);
+    store_op(out, 2 * lane + 1, 0.0);
+    return;
+  }
+  int tok = init_idx[(size_t)h * C + k];
+  if (tok < 0 || tok >= L) {
+    if (lane == 0) atomicOr(dev_flags, 1);
+    tok = 0;
+  }
+  const KT* src = keys + (size_t)h * head_stride + (size_t)tok * D;
+  const float c0 = load_f32(src, 2 * lane), c1 = load_f32(src, 2 * lane + 1);
+  float* cr = cent + ((size_t)h * C + k) * D;
+  cr[2 * lane] = c0;
+  cr[2 * lane + 1] = c1;
+  normalize_row(c0, c1, rows[w], out);
+}
+
+// ---------------------------------------------------------------------------
+// a3: assignment of bf16 keys on the matrix cores.
+//
+// Block = 8 waves x 64 keys. The whole operand chat [cpad, 128] of the head
+// sits in LDS; each wave keeps its keys in registers as the B operand of
+// v_mfma_f32_32x32x16_bf16 (32 keys per tile, two tiles) and streams 32
+// centroids at a time as the A operand, so D[centroid][key] lands with one
+// key per lane column. The channel order inside the contraction is permuted
+// the same way for both operands (lane half b, k-step s <-> channels
+// 64b + 8s .. 64b + 8s + 7), which leaves every dot product unchanged.
+//
+// Each lane keeps the best score, its centroid id and the runner-up score of
+// its key; lanes l and l^32 (the two halves of the centroid rows) merge at the
+// end. The fp32 order is certified against the exact (fp64) order when
+//   best - runner_up > 2 * 4 * (d + 16) * 2^-24 * ||K_i|| * max||chat_k|| * 1.02,
+// a bound on the error of any fp32 accumulation of d exact products (the
+// products of bf16 operands are exact) with a safety factor of 4. Keys that
+// fail it are queued for exact re-scoring (fix-up kernel below). Ties and
+// near-ties therefore always resolve by the fp64 rule, lowest id first.
+constexpr int AS_WAVES = 8;
+constexpr int AS_THREADS = AS_WAVES * WAVE;
+constexpr int AS_TILE = AS_WAVES * 64;
+
+__device__ __forceinline__ void top2_update(float s, int k, float& m1, float& m2, int& i1) {
+  i1 = s > m1 ? k : i1;
+  m2 = __builtin_amdgcn_fmed3f(m1, m2, s);
+  m1 = fmaxf(m1, s);
+}
+
+__global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
+    const uint16_t* __restrict__ keys, long long head_stride, int L, const uint16_t* __restrict__ chat, int C,
+    int cpad, int32_t* __restrict__ labels, long long label_stride, int32_t* __restrict__ queue,
+    uint32_t* __restrict__ qcount, float* __restrict__ top2) {
+  extern __shared__ u32x4 sC[];  // cpad rows x 16 chunks of 16 B, chunk c of row r at c ^ (r & 7)
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int tile0 = blockIdx.x * AS_TILE + wave * 64;
+
+  const u32x4* Cg = reinterpret_cast<const u32x4*>(chat + (size_t)h * cpad * D);
+  for (int e = tid; e < cpad * 16; e += AS_THREADS) {
+    const int r = e >> 4, c = e & 15;
+    sC[r * 16 + (c ^ (r & 7))] = Cg[e];
+  }
+
+  const uint16_t* Kh = keys + (size_t)h * head_stride;
+  bf16x8 bk[2][8];
+  float n2[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    int row = tile0 + t * 32 + col;
+    row = row < L ? row : L - 1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(Kh + (size_t)row * D + half * 64);
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const u32x4 v = src[s];
+      bk[t][s] = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = __uint_as_float(v[q] << 16), hi = __uint_as_float(v[q] & 0xFFFF0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+    }
+    n2[t] = ss;
+  }
+  __syncthreads();
+
+  float m1[2] = {-INFINITY, -INFINITY}, m2[2] = {-INFINITY, -INFINITY};
+  int i1[2] = {0, 0};
+  const int nct = cpad >> 5;
+  for (int ct = 0; ct < nct; ++ct) {
+    f32x16 acc0 = {}, acc1 = {};
+    const int arow = ct * 32 + col;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, sC[arow * 16 + ((half * 8 + s) ^ (arow & 7))]);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bk[0][s], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bk[1][s], acc1, 0, 0, 0);
+    }
+    const int kb = ct * 32 + 4 * half;
+    if (ct * 32 + 32 <= C) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int k = kb + 8 * (r >> 2) + (r & 3);
+        top2_update(acc0[r], k, m1[0], m2[0], i1[0]);
+        top2_update(acc1[r], k, m1[1], m2[1], i1[1]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int k = kb + 8 * (r >> 2) + (r & 3);
+        const bool ok = k < C;
+        top2_update(ok ? acc0[r] : -INFINITY, k, m1[0], m2[0], i1[0]);
+        top2_update(ok ? acc1[r] : -INFINITY, k, m1[1], m2[1], i1[1]);
+      }
+    }
+  }
+
+  // merge the two halves of the centroid rows, then certify
+  const float gamma = 2.0f * 4.0f * (float)(D + 16) * 5.9604644775390625e-8f * 1.02f;
+  int my_label = 0;
+  bool my_flag = false;
+  float my_m1 = 0.f, my_m2 = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float o1 = __shfl_xor(m1[t], 32), o2 = __shfl_xor(m2[t], 32), on = __shfl_xor(n2[t], 32);
+    const int oi = __shfl_xor(i1[t], 32);
+    const float M1 = fmaxf(m1[t], o1);
+    const int I1 = m1[t] > o1 ? i1[t] : (o1 > m1[t] ? oi : min(i1[t], oi));
+    const float M2 = fmaxf(fminf(m1[t], o1), fmaxf(m2[t], o2));
+    const float nk = sqrtf(n2[t] + on);
+    const bool cert = (M1 - M2) > gamma * nk;  // false for NaN and for ties
+    if (t == half) {
+      my_label = I1;
+      my_flag = !cert;
+      my_m1 = M1;
+      my_m2 = M2;
+    }
+  }
+  const int row = tile0 + half * 32 + col;
+  const bool valid = row < L;
+  if (valid) {
+    labels[(size_t)h * label_stride + row] = my_label;
+    if (top2) {
+      top2[((size_t)h * L + row) * 2] = my_m1;
+      top2[((size_t)h * L + row) * 2 + 1] = my_m2;
+    }
+  }
+  const bool push = valid && my_flag;
+  const unsigned long long bal = __ballot(push);
+  if (bal) {
+    const int n = __popcll(bal);
+    int base = 0;
+    if (lane == __ffsll((long long)bal) - 1) base = (int)atomicAdd(qcount + h, (uint32_t)n);
+    base = __shfl(base, __ffsll((long long)bal) - 1);
+    const int slot = base + __popcll(bal & ((1ull << lane) - 1ull));
+    if (push) queue[(size_t)h * L + slot] = row;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// a3 exact path: label_i = argmax_k of the fp64 chain sum_j K_ij * chat_kj over
+// ascending j, lowest k on ties. Used for keys the matrix-core pass could not
+// certify, and for every key of fp32 inputs. One wave per key; lane c handles
+// centroids c, c+64, ...; the key's channel j reaches every lane through
+// readlane. Rows come from the per-head queue (queue != null) or are all rows.
+template <typename KT>
+__global__ __launch_bounds__(256) void assign_exact_kernel(const KT* __restrict__ keys, long long head_stride, int L,
+                                                           const KT* __restrict__ chat, int C, int cpad,
+                                                           int32_t* __restrict__ labels, long long label_stride,
+                                                           const int32_t* __restrict__ queue,
+                                                           const uint32_t* __restrict__ qcount) {
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nw = gridDim.x * 4;
+  const int n = queue ? (int)__atomic_load_n(qcount + h, __ATOMIC_RELAXED) : L;
+  const KT* Kh = keys + (size_t)h * head_stride;
+  const KT* Ch = chat + (size_t)h * cpad * D;
+  constexpr int MAXT = (512 + 63) / 64;
+  for (int e = gw; e < n; e += nw) {
+    const int row = queue ? queue[(size_t)h * L + e] : e;
+    const double k0 = (double)load_f32(Kh, (size_t)row * D + lane);
+    const double k1 = (double)load_f32(Kh, (size_t)row * D + 64 + lane);
+    double s[MAXT];
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) s[t] = 0.0;
+    for (int j = 0; j < D; ++j) {
+      const double src = j < 64 ? k0 : k1;
+      const int jl = j & 63;
+      const int lo = __builtin_amdgcn_readlane((int)(__double_as_longlong(src) & 0xFFFFFFFFll), jl);
+      const int hi = __builtin_amdgcn_readlane((int)(__double_as_longlong(src) >> 32), jl);
+      const double kj = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t) {
+        const int c = lane + 64 * t;
+        if (c < C) s[t] = fma(kj, (double)load_f32(Ch, (size_t)c * D + j), s[t]);
+      }
+    }
+    double best = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      const int c = lane + 64 * t;
+      if (c < C && s[t] > best) {
+        best = s[t];
+        bi = c;
+      }
+    }
+    // wave argmax: larger score, then smaller id
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ob = __shfl_xor(best, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ob > best || (ob == best && oi < bi)) {
+        best = ob;
+        bi = oi;
+      }
+    }
+    if (lane == 0) labels[(size_t)h * label_stride + row] = bi;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// a5: stable counting sort of labels into the cluster index.
+// Blocks of CS_BLOCK tokens. count: per-block histograms. scan: per cluster
+// the exclusive prefix over blocks (block bases), sizes, and offsets as the
+// exclusive prefix of sizes over clusters. scatter: within a block, each
+// wave's histogram gives the wave bases; inside a wave the rank of a lane
+// among lower lanes of the same label comes from matching label bits with
+// ballots. Position = block base + wave base + rank keeps token order.
+constexpr int CS_BLOCK = 1024;
+
+__global__ __launch_bounds__(256) void csr_count_kernel(const int32_t* __restrict__ labels, long long label_stride,
+                                                        int L, int C, int nblk, int32_t* __restrict__ hist) {
+  __shared__ int cnt[512];
+  const int h = blockIdx.y, b = blockIdx.x;
+  for (int c = threadIdx.x; c < C; c += 256) cnt[c] = 0;
+  __syncthreads();
+  const int32_t* lab = labels + (size_t)h * label_stride;
+  for (int i = b * CS_BLOCK + threadIdx.x; i < min(L, (b + 1) * CS_BLOCK); i += 256) atomicAdd(&cnt[lab[i]], 1);
+  __syncthreads();
+  int32_t* out = hist + ((size_t)h * nblk + b) * C;
+  for (int c = threadIdx.x; c < C; c += 256) out[c] = cnt[c];
+}
+
+__global__ __launch_bounds__(512) void csr_scan_kernel(int C, int nblk, int32_t* __restrict__ hist,
+                                                       int32_t* __restrict__ sizes, int32_t* __restrict__ offsets) {
+  __shared__ int sc[512];
+  const int h = blockIdx.x, c = threadIdx.x;
+  int32_t* hh = hist + (size_t)h * nblk * C;
+  int run = 0;
+  if (c < C) {
+    for (int b = 0; b < nblk; ++b) {
+      const int v = hh[(size_t)b * C + c];
+      hh[(size_t)b * C + c] = run;
+      run += v;
+    }
+    sizes[(size_t)h * C + c] = run;
+  }
+  sc[c] = c < C ? run : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over 512 entries
+  for (int off = 1; off < 512; off <<= 1) {
+    const int v = c >= off ? sc[c - off] : 0;
+    __syncthreads();
+    sc[c] += v;
+    __syncthreads();
+  }
+  const int excl = sc[c] - (c < C ? run : 0);
+  if (c < C) {
+    offsets[(size_t)h * (C + 1) + c] = excl;
+    for (int b = 0; b < nblk; ++b) hh[(size_t)b * C + c] += excl;
+  }
+  if (c == C - 1) offsets[(size_t)h * (C + 1) + C] = sc[c];
+}
+
+__global__ __launch_bounds__(CS_BLOCK) void csr_scatter_kernel(const int32_t* __restrict__ labels,
+                                                               long long label_stride, int L, int C, int nblk,
+                                                               const int32_t* __restrict__ hist,
+                                                               int32_t* __restrict__ token_ids, long long ids_stride) {
+  constexpr int NW = CS_BLOCK / WAVE;
+  __shared__ int wh[NW][512];
+  const int h = blockIdx.y, b = blockIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < NW * 512; e += CS_BLOCK) (&wh[0][0])[e] = 0;
+  __syncthreads();
+  const int i = b * CS_BLOCK + tid;
+  const int lab = i < L ? labels[(size_t)h * label_stride + i] : -1;
+  if (lab >= 0) atomicAdd(&wh[w][lab], 1);
+  __syncthreads();
+  const int32_t* base = hist + ((size_t)h * nblk + b) * C;
+  for (int c = tid; c < C; c += CS_BLOCK) {
+    int run = base[c];
+    for (int v = 0; v < NW; ++v) {
+      const int t = wh[v][c];
+      wh[v][c] = run;
+      run += t;
+    }
+  }
+  __syncthreads();
+  unsigned long long same = __ballot(lab >= 0);
+  const int nbits = 32 - __clz(C > 1 ? C - 1 : 1);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool set = lab >= 0 && ((lab >> bit) & 1);
+    const unsigned long long bal = __ballot(set);
+    same &= set ? bal : ~bal;
+  }
+  if (lab >= 0) {
+    const int rank = __popcll(same & ((1ull << lane) - 1ull));
+    token_ids[(size_t)h * ids_stride + wh[w][lab] + rank] = i;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// a4 + a2: centroid update fused with normalisation. One wave per cluster,
+// lane = channels 2*lane, 2*lane+1. Members are read through the index in
+// ascending token order and summed in fp64 in that order; the mean is the
+// fp64 sum / count rounded once to fp32 (an empty cluster keeps its
+// centroid). The new operand row is the normalised mean.
+template <typename KT>
+__global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys, long long head_stride, int C,
+                                                     int cpad, const int32_t* __restrict__ sizes,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ token_ids, long long ids_stride,
+                                                     float* __restrict__ cent, KT* __restrict__ chat) {
+  __shared__ float rows[4][D];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.y;
+  const int k = blockIdx.x * 4 + w;
+  if (k >= C) return;
+  const int n = sizes[(size_t)h * C + k];
+  const int off = offsets[(size_t)h * (C + 1) + k];
+  const int32_t* ids = token_ids + (size_t)h * ids_stride + off;
+  const KT* Kh = keys + (size_t)h * head_stride + 2 * lane;
+  float* cr = cent + ((size_t)h * C + k) * D;
+  float c0, c1;
+  if (n > 0) {
+    double a0 = 0.0, a1 = 0.0;
+    constexpr int U = 8;
+    int m = 0;
+    for (; m + U <= n; m += U) {
+      float x0[U], x1[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_pair(Kh + (size_t)ids[m + u] * D, x0[u], x1[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        a0 += (double)x0[u];
+        a1 += (double)x1[u];
+      }
+    }
+    for (; m < n; ++m) {
+      float x0, x1;
+      load_pair(Kh + (size_t)ids[m] * D, x0, x1);
+      a0 += (double)x0;
+      a1 += (double)x1;
+    }
+    c0 = (float)(a0 / (double)n);
+    c1 = (float)(a1 / (double)n);
+    cr[2 * lane] = c0;
+    cr[2 * lane + 1] = c1;
+  } else {
+    c0 = cr[2 * lane];
+    c1 = cr[2 * lane + 1];
+  }
+  normalize_row(c0, c1, rows[w], chat + ((size_t)h * cpad + k) * D);
+}
+
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, size_t n, int32_t v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers.
+
+static int grid1(size_t n, int per) { return (int)((n + per - 1) / per); }
+
+hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int blocks = grid1(n, 256) < 1024 ? grid1(n, 256) : 1024;
+  fill_i32_kernel<<<blocks, 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_centroids(int dtype, const void* keys, long long head_stride, int heads, int L,
+                                 const int32_t* init_idx, int C, int cpad, float* cent, void* chat, int32_t* flags,
+                                 hipStream_t st) {
+  dim3 grid(grid1(cpad, 4), heads);
+  if (dtype == DT_BF16)
+    init_centroids_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, L, init_idx, C, cpad,
+                                                          cent, (uint16_t*)chat, flags);
+  else
+    init_centroids_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, L, init_idx, C, cpad, cent,
+                                                       (float*)chat, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
+                         int cpad, int32_t* labels, long long label_stride, int32_t* queue, uint32_t* qcount,
+                         float* top2, hipStream_t st) {
+  if (dtype == DT_BF16) {
+    const size_t lds = (size_t)cpad * D * 2;
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void*)assign_bf16_mfma_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    dim3 grid(grid1(L, AS_TILE), heads);
+    assign_bf16_mfma_kernel<<<grid, AS_THREADS, lds, st>>>((const uint16_t*)keys, head_stride, L,
+                                                             (const uint16_t*)chat, C, cpad, labels, label_stride,
+                                                             queue, qcount, top2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // exact re-scoring of the uncertified keys; blocks without work exit at once
+    dim3 g2(16, heads);
+    assign_exact_kernel<uint16_t><<<g2, 256, 0, st>>>((const uint16_t*)keys, head_stride, L, (const uint16_t*)chat, C,
+                                                      cpad, labels, label_stride, queue, qcount);
+    return hipGetLastError();
+  }
+  dim3 g2(grid1(L, 4) < 64 ? grid1(L, 4) : 64, heads);
+  assign_exact_kernel<float><<<g2, 256, 0, st>>>((const float*)keys, head_stride, L, (const float*)chat, C, cpad,
+                                                 labels, label_stride, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, int L, int C, int32_t* hist,
+                      int32_t* sizes, int32_t* offsets, int32_t* token_ids, long long ids_stride, hipStream_t st) {
+  const int nblk = csr_blocks(L);
+  csr_count_kernel<<<dim3(nblk, heads), 256, 0, st>>>(labels, label_stride, L, C, nblk, hist);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  csr_scan_kernel<<<heads, 512, 0, st>>>(C, nblk, hist, sizes, offsets);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  csr_scatter_kernel<<<dim3(nblk, heads), CS_BLOCK, 0, st>>>(labels, label_stride, L, C, nblk, hist, token_ids,
+                                                             ids_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cpad,
+                         const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
+                         float* cent, void* chat, hipStream_t st) {
+  dim3 grid(grid1(C, 4), heads);
+  if (dtype == DT_BF16)
+    update_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, C, cpad, sizes, offsets,
+                                                  token_ids, ids_stride, cent, (uint16_t*)chat);
+  else
+    update_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, C, cpad, sizes, offsets, token_ids,
+                                               ids_stride, cent, (float*)chat);
+  return hipGetLastError();
+}
+
+int csr_blocks(int L) { return (L + CS_BLOCK - 1) / CS_BLOCK; }
+
+}  // namespace kvc

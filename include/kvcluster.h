@@ -1,0 +1,203 @@
+/*
+ * kvcluster: cluster-granular sparse KV recall on AMD Instinct MI355X (gfx950).
+ *
+ * The method is ClusterKV, "Manipulating LLM KV Cache in Semantic Space for
+ * Recallable Compression" (arXiv 2412.03213). Section names below refer to
+ * the paper summary page (paperlayer.ai, 2412.03213v2).
+ *
+ *  - At prefill, each head's keys are grouped into C semantic clusters by
+ *    cosine k-means (III.B "Clustering in the Semantic Space", Sys-B
+ *    "Semantic Clustering"). The result is an index: centroids, cluster
+ *    sizes, prefix sums and the token ids sorted by cluster (Sys-C
+ *    "Selection and Indexing").
+ *  - At each decode step, the query scores the centroids and whole clusters
+ *    are taken in score order until the token budget B is met, with the last
+ *    cluster trimmed (III.C, Sys-C with Fig. 8). Single-query attention then
+ *    runs over only the recalled tokens (II.A, III.A "Problem Formulation").
+ *
+ * Conventions shared by every call:
+ *  - Memory. Every pointer argument is DEVICE memory unless stated otherwise,
+ *    owned by the caller. The library never allocates, frees or
+ *    synchronises, and it keeps no device state between calls.
+ *  - Streams. `stream` is a hipStream_t passed as void* (NULL is the null
+ *    stream). Every call only enqueues work on it; results are valid once
+ *    the stream has been synchronised.
+ *  - Errors. Arguments are checked on the host before anything is enqueued.
+ *    On any error nothing is enqueued and the call returns a nonzero
+ *    kvc_status. A kernel launch failure returns KVC_ERR_HIP. Faults inside
+ *    kernels surface through HIP at the caller's next synchronisation.
+ *  - Layout. heads = batch x KV heads, flattened. K/V caches are row-major
+ *    [heads, capacity, d] with head stride capacity*d. Query heads are
+ *    [q_heads, d] with q_heads = G * heads; query head g reads KV head g / G.
+ *    The GPU path supports d = 128 and C <= 512.
+ *  - Element types. KVC_BF16 (the production path; bf16 inputs, fp32
+ *    accumulation) or KVC_F32. Keys, values, queries and new tokens of one
+ *    index share the type.
+ */
+#ifndef KVCLUSTER_H
+#define KVCLUSTER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_HEAD_DIM 128 /* the only head dimension the GPU path supports */
+#define KVC_MAX_C 512    /* largest cluster count per head */
+#define KVC_MAX_G 8      /* largest number of query heads per KV head */
+
+typedef enum kvc_dtype { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+typedef enum kvc_status {
+  KVC_OK = 0,
+  KVC_ERR_INVALID_ARG = 1, /* a null pointer, a size out of range, ... */
+  KVC_ERR_UNSUPPORTED = 2, /* valid for the method, not for this GPU path (d != 128, C > 512, G > 8) */
+  KVC_ERR_WORKSPACE = 3,   /* workspace smaller than the matching *_workspace_bytes() */
+  KVC_ERR_CAPACITY = 4,    /* an append would pass the index capacity */
+  KVC_ERR_HIP = 5          /* a kernel launch failed */
+} kvc_status;
+
+/*
+ * The cluster index of `heads` independent heads: centroids plus the
+ * cluster-to-token metadata that Sys-C keeps after clustering (sizes, prefix
+ * sums, token indices sorted by cluster). The caller allocates every array
+ * (device memory) and fills in the pointers and sizes; kv_cluster_build
+ * writes the contents.
+ *
+ * Tokens appended at decode time (kv_cluster_append) are kept in a second,
+ * cluster-major list so that no append moves the built index: the members of
+ * cluster k are token_ids[offsets[k] .. offsets[k+1]) followed by
+ * app_ids[app_offsets[k] .. app_offsets[k+1]), in ascending token order.
+ */
+typedef struct kvc_index {
+  int32_t heads;    /* independent problems (batch x KV heads) */
+  int32_t d;        /* head dimension; must be 128 */
+  int32_t C;        /* clusters per head, 1 <= C <= 512 */
+  int32_t capacity; /* rows per head of the K/V caches (and of labels/token_ids/app_ids) */
+  int32_t dtype;    /* kvc_dtype of keys, queries and the centroid operand */
+  int32_t n_build;  /* host mirror: tokens clustered by the last build */
+  int32_t n_tokens; /* host mirror: n_build + tokens appended since */
+  int32_t reserved;
+  float* centroids;       /* [heads, C, d] fp32: mean of each cluster's keys */
+  void* centroids_op;     /* [heads, kv_cluster_cpad(C), d] unit-length centroids in `dtype`
+                             (the assignment operand); rows >= C are zero */
+  int32_t* labels;        /* [heads, capacity] cluster of every token */
+  int32_t* sizes;         /* [heads, C] members per cluster, appended tokens included */
+  int32_t* offsets;       /* [heads, C+1] prefix sums of the built part's sizes */
+  int32_t* token_ids;     /* [heads, capacity] built tokens sorted by cluster, ascending within */
+  int32_t* app_offsets;   /* [heads, C+1] prefix sums of the appended part */
+  int32_t* app_ids;       /* [heads, capacity] appended tokens, cluster-major, ascending within */
+  int32_t* dev_flags;     /* [1] error bits set by kernels (bit 0: an init index out of range) */
+} kvc_index;
+
+/* Rows of centroids_op per head: C rounded up to the matrix-core tile (32). */
+int kv_cluster_cpad(int C);
+
+/* Bytes of workspace kv_cluster_build needs for these sizes. */
+size_t kv_cluster_build_workspace_bytes(int heads, int L, int C, int iters);
+
+/*
+ * Prefill clustering (III.B; Sys-B). For every head, the first L rows of
+ * `keys` ([heads, capacity, d], idx->dtype) are clustered into idx->C
+ * clusters by `iters` iterations of cosine k-means:
+ *   - initial centroids are the keys at init_idx[h*C + k] ([heads, C] int32
+ *     token positions, distinct, in [0, L); the seeded shuffle that picks them
+ *     is the caller's input). An index out of range sets bit 0 of
+ *     *idx->dev_flags and row 0 is used instead;
+ *   - each iteration normalises the centroids (rounded once to idx->dtype),
+ *     assigns every key to the centroid of largest cosine similarity (lowest
+ *     id on an exact tie) and replaces each centroid by the mean of its keys
+ *     (an empty cluster keeps its centroid).
+ * On return (after synchronisation) the index holds the means of the final
+ * assignment, their normalised operand, labels, sizes, offsets and
+ * token_ids; the appended part is empty. idx->n_build and idx->n_tokens are
+ * set to L on the host. Requires 1 <= C <= L <= capacity, iters >= 1, and a
+ * workspace of kv_cluster_build_workspace_bytes(heads, L, C, iters) bytes
+ * (contents need not be initialised).
+ */
+int kv_cluster_build(kvc_index* idx, const void* keys, int L, int iters, const int32_t* init_idx, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * Decode-time append of n_new tokens per head (rows idx->n_tokens ..
+ * idx->n_tokens+n_new-1). k_new and v_new are [heads, n_new, d] in
+ * idx->dtype and are written into the caches; each new key joins the cluster
+ * of largest cosine similarity under the current centroid operand, whose
+ * centroids do not move. Sizes, labels and the appended list are updated;
+ * idx->n_tokens advances on the host. Returns KVC_ERR_CAPACITY, enqueuing
+ * nothing, if the tokens would not fit. (The pages re-cluster generated
+ * tokens periodically instead, III.B; joining the nearest centroid is the
+ * per-token alternative this call provides.)
+ */
+int kv_cluster_append(kvc_index* idx, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                      int n_new, void* stream);
+
+/*
+ * Cluster-granular selection (III.C; Sys-C, Fig. 8) for every KV head h:
+ *   - the G = q_heads / heads query heads of h are summed (fp64),
+ *   - score_k = fp64 dot product of that sum with centroid k (ascending
+ *     channel order), the logit of the centroid's attention weight,
+ *   - clusters are taken in order of (score descending, id ascending), each
+ *     contributing its tokens in ascending position order, until B tokens are
+ *     taken; the last cluster is trimmed to fit.
+ * q is [q_heads, d] in idx->dtype. sel_ids [heads, B] receives the selected
+ * token positions (in rank order; -1 past the count) and sel_count [heads]
+ * receives min(B, tokens in the index). Requires B >= 1 and G <= 8.
+ */
+int kv_cluster_select(const kvc_index* idx, const void* q, int q_heads, int B, int32_t* sel_ids,
+                      int32_t* sel_count, void* stream);
+
+/* Bytes of workspace kv_sparse_decode needs. */
+size_t kv_sparse_decode_workspace_bytes(int heads, int q_heads, int d, int B);
+
+/*
+ * Single-query attention over the recalled tokens (II.A; III.A). For query
+ * head g (KV head h = g / G):
+ *   out[g] = sum_i softmax_i(scale * q_g . K[h, i]) V[h, i]
+ * over i in sel_ids[h*B .. h*B + sel_count[h]) (fp32 accumulation, fp32
+ * output [q_heads, d]; zero when sel_count[h] is 0). k_cache and v_cache are
+ * [heads, capacity, d] in `dtype`, q is [q_heads, d] in `dtype`. The selected
+ * positions must lie in [0, capacity). The workspace must hold
+ * kv_sparse_decode_workspace_bytes(heads, q_heads, d, B) bytes and must be
+ * zero-filled once before its first use; every call leaves it reusable.
+ * Calls that share a workspace must not run concurrently.
+ */
+int kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
+                     int capacity, int d, const int32_t* sel_ids, const int32_t* sel_count, int B, float scale,
+                     float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The canonical index of every head (built and appended tokens merged):
+ * offsets [heads, C+1] and token_ids [heads, capacity] with each cluster's
+ * members in ascending order, as a stable counting sort of all labels would
+ * give (Sys-C). For tests and checkpoints.
+ */
+int kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token_ids, void* stream);
+
+/*
+ * Single steps of the build, for checking each kernel on its own.
+ *  - kv_cluster_debug_assign: labels [heads, capacity] of the first L keys
+ *    under the given operand chat [heads, cpad(C), d] (same rule as the
+ *    build). top2 (optional, [heads, L, 2] fp32) receives the matrix-core
+ *    best and runner-up scores of bf16 keys; flagged (optional, [1]) the
+ *    number of keys whose order the fp32 scores could not certify and which
+ *    were re-scored in fp64. ws as for the build.
+ *  - kv_cluster_debug_update: from labels [heads, capacity] of the first L
+ *    keys, the index arrays (sizes, offsets, token_ids) and the centroid
+ *    update plus normalisation, writing idx->centroids (in: previous
+ *    centroids, kept for empty clusters) and idx->centroids_op.
+ */
+int kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const void* chat, int32_t* labels,
+                            float* top2, int32_t* flagged, void* ws, size_t ws_bytes, void* stream);
+int kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* kv_cluster_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVCLUSTER_H */

@@ -1,0 +1,212 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the same
+seeded inputs: each kernel step on its own, then the whole path.
+
+Bars: cluster index and selection bit-exact given identical inputs; labels
+bit-exact given an identical operand (the certified argmax resolves every
+near-tie in fp64); centroids within 1e-3 relative; attention within 2e-3
+max-abs (bf16 inputs, fp32 accumulation)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _helpers import make_inputs, queries, to_dev, to_np, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+kvc = pytest.importorskip("clustered_sparse_attention_kv_amd")
+
+SMALL = synth.Workload("small_bf16_ragged", 90, heads=3, G=2, L=1500, d=128, dtype=synth.BF16, M=20, sigma=0.3,
+                       n_out=4, out_scale=10.0, C=40, iters=6, B=200, steps=3, query="noisy_key", q_sigma=0.1)
+SMALL_APPEND = synth.Workload("small_bf16_append", 91, heads=2, G=1, L=1100, d=128, dtype=synth.BF16, M=24,
+                              sigma=0.3, n_out=4, out_scale=10.0, C=37, iters=5, B=300, steps=20, query="noisy_key",
+                              q_sigma=0.1, append=True)
+CASES = {"cfg1_fp32": synth.workload(1), "small_bf16": SMALL}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def pad_op(chat: np.ndarray, cpad: int) -> np.ndarray:
+    H, C, d = chat.shape
+    out = np.zeros((H, cpad, d), dtype=chat.dtype)
+    out[:, :C] = chat
+    return out
+
+
+def built_gpu(w, K, init):
+    idx = kvc.ClusterIndex(K.shape[0], w.C, w.capacity, torch_dtype(w))
+    Kd = to_dev(K)
+    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    torch.cuda.synchronize()
+    return idx, Kd
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_assign_step_bit_exact(case):
+    w = CASES[case]
+    say(f"[assign step] {case}")
+    base, K, V, init, _ = make_inputs(w)
+    H = K.shape[0]
+    opt = oracle.BF16 if w.dtype == synth.BF16 else oracle.F32
+    # operand: normalised initial centroids, then one oracle iteration later
+    c0 = np.stack([K[h, init[h]].astype(np.float32) if w.dtype == synth.F32 else oracle.to_f64(K[h, init[h]])
+                   .astype(np.float32) for h in range(H)])
+    for it in range(2):
+        chat = np.stack([oracle.normalize(c0[h], opt) for h in range(H)])
+        want = np.stack([oracle.assign(K[h, :w.L], chat[h])[0] for h in range(H)])
+        idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w))
+        labels, top2, flagged = kvc.debug_assign(idx, to_dev(K), w.L, to_dev(pad_op(chat, kvc.cpad(w.C))),
+                                                 want_top2=(w.dtype == synth.BF16))
+        got = to_np(labels)[:, :w.L]
+        say(f"  iter {it}: flagged per head {to_np(flagged).tolist()}, mismatches {(got != want).sum()}")
+        assert np.array_equal(got, want)
+        if top2 is not None:
+            # the matrix-core best score is within the certification bound of the exact one
+            t2 = to_np(top2)
+            best = np.stack([oracle.assign(K[h, :w.L], chat[h])[1] for h in range(H)])
+            kn = np.linalg.norm(oracle.to_f64(K[:, :w.L]), axis=2)
+            bound = 4 * (w.d + 16) * 2.0 ** -24 * kn * 1.004
+            err = np.abs(t2[..., 0] - best)
+            say(f"  max |fp32 best - fp64 best| / bound = {(err / bound).max():.3e}")
+            assert np.all(err <= bound)
+        c0 = np.stack([oracle.update(K[h, :w.L], want[h], c0[h])[0] for h in range(H)])
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_update_step_bit_exact(case):
+    w = CASES[case]
+    say(f"[update step] {case}")
+    base, K, V, init, _ = make_inputs(w)
+    H = K.shape[0]
+    rng = np.random.default_rng(11)
+    labels = rng.integers(0, w.C, (H, w.L)).astype(np.int32)
+    labels[labels == 3] = 4  # cluster 3 empty: keeps its previous centroid
+    prev = rng.standard_normal((H, w.C, w.d)).astype(np.float32)
+    idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w))
+    lab_full = np.full((H, w.capacity), -1, np.int32)
+    lab_full[:, :w.L] = labels
+    idx.labels.copy_(to_dev(lab_full))
+    idx.centroids.copy_(to_dev(prev))
+    kvc.debug_update(idx, to_dev(K), w.L)
+    torch.cuda.synchronize()
+    opt = oracle.BF16 if w.dtype == synth.BF16 else oracle.F32
+    for h in range(H):
+        s, o, i = oracle.csr(labels[h], w.C)
+        assert np.array_equal(to_np(idx.sizes)[h], s)
+        assert np.array_equal(to_np(idx.offsets)[h], o)
+        assert np.array_equal(to_np(idx.token_ids)[h, :w.L], i)
+        c, _ = oracle.update(K[h, :w.L], labels[h], prev[h])
+        assert np.array_equal(to_np(idx.centroids)[h], c)
+        assert np.array_equal(to_np(idx.centroids_op)[h, :w.C], oracle.normalize(c, opt))
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_build_select_decode_end_to_end(case):
+    w = CASES[case]
+    say(f"[end to end] {case}")
+    base, K, V, init, means = make_inputs(w)
+    H = K.shape[0]
+    idx, Kd = built_gpu(w, K, init)
+    assert int(to_np(idx.dev_flags)[0]) == 0
+    ref = oracle.build(np.ascontiguousarray(K[:, :w.L]), w.C, w.iters, init)
+    gl = to_np(idx.labels)[:, :w.L]
+    agree = (gl == ref["labels"]).mean()
+    say(f"  label agreement {agree:.6f}")
+    assert agree >= 0.999
+    gc = to_np(idx.centroids)
+    same = [(h, k) for h in range(H) for k in range(w.C)
+            if np.array_equal(np.flatnonzero(gl[h] == k), np.flatnonzero(ref["labels"][h] == k))]
+    rel = max(np.linalg.norm(gc[h, k] - ref["c"][h, k]) / max(np.linalg.norm(ref["c"][h, k]), 1e-30)
+              for h, k in same)
+    say(f"  centroid rel err (same membership, {len(same)} clusters) {rel:.3e}")
+    assert rel <= 1e-3
+    # index bit-exact given the GPU's labels; operand bit-exact given its centroids
+    opt = oracle.BF16 if w.dtype == synth.BF16 else oracle.F32
+    for h in range(H):
+        s, o, i = oracle.csr(gl[h], w.C)
+        assert np.array_equal(to_np(idx.sizes)[h], s) and np.array_equal(to_np(idx.offsets)[h], o)
+        assert np.array_equal(to_np(idx.token_ids)[h, :w.L], i)
+        assert np.array_equal(to_np(idx.centroids_op)[h, :w.C], oracle.normalize(gc[h], opt))
+    # selection (bit-exact given the GPU's index) and sparse decode (<= 2e-3)
+    Vd = to_dev(V)
+    ws = torch.zeros(kvc.decode_workspace_bytes(H, H * w.G, max(w.B, 1)) + 4096, dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(w.d)
+    for step, B in enumerate([w.B, 1, 7, w.L + 50]):
+        q = queries(w, base, step, K, w.L, means)
+        sel, cnt = kvc.select(idx, to_dev(q), B)
+        ws_b = torch.zeros(kvc.decode_workspace_bytes(H, H * w.G, B), dtype=torch.uint8, device="cuda")
+        out = kvc.sparse_decode(to_dev(q), Kd, Vd, sel, cnt, scale, workspace=ws_b)
+        torch.cuda.synchronize()
+        osel, ocnt, _, _ = oracle.select(q, w.G, gc, to_np(idx.sizes), to_np(idx.offsets), to_np(idx.token_ids), B)
+        assert np.array_equal(to_np(cnt), ocnt), B
+        assert np.array_equal(to_np(sel), osel), B
+        od = oracle.decode(q, w.G, K, V, to_np(sel), to_np(cnt), scale)
+        err = np.abs(to_np(out) - od).max()
+        say(f"  B={B}: count {to_np(cnt).tolist()[:4]}, decode max abs err {err:.3e}")
+        assert err <= 2e-3
+    del ws
+
+
+def test_append_then_select_decode():
+    w = SMALL_APPEND
+    say("[append]")
+    base, K, V, init, means = make_inputs(w)
+    H = K.shape[0]
+    idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w))
+    Kc = np.zeros_like(K)
+    Vc = np.zeros_like(V)
+    Kc[:, :w.L], Vc[:, :w.L] = K[:, :w.L], V[:, :w.L]
+    Kd, Vd = to_dev(Kc), to_dev(Vc)
+    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    torch.cuda.synchronize()
+    # the oracle index continues from the GPU's built state (identical centroids)
+    built = dict(labels=to_np(idx.labels)[:, :w.L], sizes=to_np(idx.sizes), offsets=to_np(idx.offsets),
+                 token_ids=to_np(idx.token_ids)[:, :w.L], c=to_np(idx.centroids),
+                 chat=to_np(idx.centroids_op)[:, :w.C])
+    oi = oracle.Index(built, w.capacity)
+    n = w.L
+    scale = 1.0 / math.sqrt(w.d)
+    steps = [1] * 12 + [3, 1, 4]
+    for s, nn in enumerate(steps):
+        kvc.append(idx, Kd, Vd, to_dev(np.ascontiguousarray(K[:, n:n + nn])),
+                   to_dev(np.ascontiguousarray(V[:, n:n + nn])))
+        for t in range(nn):
+            oi.append(np.ascontiguousarray(K[:, n + t]))
+        n += nn
+        assert idx.n_tokens == n
+        q = queries(w, base, s, K, n, means)
+        sel, cnt = kvc.select(idx, to_dev(q), w.B)
+        out = kvc.sparse_decode(to_dev(q), Kd, Vd, sel, cnt, scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(idx.labels)[:, :n], oi.labels[:, :n])
+        assert np.array_equal(to_np(idx.sizes), oi.sizes)
+        osel, ocnt, _, _ = oracle.select(q, w.G, oi.c, oi.sizes, oi.offsets, oi.token_ids, w.B)
+        assert np.array_equal(to_np(sel), osel) and np.array_equal(to_np(cnt), ocnt)
+        od = oracle.decode(q, w.G, K, V, osel, ocnt, scale)
+        assert np.abs(to_np(out) - od).max() <= 2e-3
+    off, ids = kvc.export_csr(idx)
+    assert np.array_equal(to_np(off), oi.offsets)
+    assert np.array_equal(to_np(ids)[:, :n], oi.token_ids[:, :n])
+    assert np.array_equal(to_np(Kd)[:, :n], K[:, :n]) and np.array_equal(to_np(Vd)[:, :n], V[:, :n])
+    with pytest.raises(kvc.KvcError):
+        kvc.append(idx, Kd, Vd, to_dev(np.ascontiguousarray(K[:, :w.capacity - n + 1])),
+                   to_dev(np.ascontiguousarray(V[:, :w.capacity - n + 1])))
+    say(f"  appended {n - w.L} tokens; final sizes sum {to_np(idx.sizes).sum(axis=1).tolist()}")
+
+
+def test_init_index_out_of_range_flag():
+    w = SMALL
+    base, K, V, init, _ = make_inputs(w)
+    bad = init.copy()
+    bad[1, 5] = w.L + 3
+    idx = kvc.ClusterIndex(K.shape[0], w.C, w.capacity, torch.bfloat16)
+    kvc.build(idx, to_dev(K), w.L, 1, to_dev(bad))
+    torch.cuda.synchronize()
+    assert int(to_np(idx.dev_flags)[0]) & 1
