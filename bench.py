@@ -1,0 +1,357 @@
+#!/usr/bin/env python3
+"""Throughput of the clustered sparse-KV hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+prefill clustering of every KV head (10 cosine k-means iterations and the
+cluster index), then the workload's decode steps, each of which selects
+clusters for every KV head and runs sparse attention over the recalled tokens
+(for append workloads, a new token is first appended per head).
+
+Inputs are generated on the host with the seeded generator and copied to HBM
+before timing starts. The timed region holds exactly --steps passes between
+two synchronisations. Kernel durations come from HIP events recorded on the
+stream the kernels run on. The CPU oracle is timed on a bounded sample of
+the same workload as a reported baseline.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode steps/s at L=32k, B=1k (select+gather+attn); k-means TFLOP/s; % roofline"
+PEAK_HBM = 8.0e12    # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15   # flop/s, dense bf16 matrix cores
+PEAK_F64 = 78.6e12   # flop/s, fp64 vector
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch has loaded."""
+
+    def __init__(self, n: int):
+        import torch  # noqa: F401  (loads the runtime)
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        self.rt = ctypes.CDLL(path or "libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.rt.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev[i] = h
+        self.n = n
+
+    def record(self, i: int, stream_handle: int):
+        assert self.rt.hipEventRecord(self.ev[i], ctypes.c_void_p(stream_handle)) == 0
+
+    def ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        assert self.rt.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) == 0
+        return float(out.value)
+
+    def sub(self, start: int, count: int):
+        return (ctypes.c_void_p * count)(*[self.ev[start + i] for i in range(count)])
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in ("kvc_build.hip", "kvc_decode.hip", "kvc_device.h"):
+        with open(os.path.join(ROOT, "clustered_sparse_attention_kv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(w):
+    """Algorithmic work of one pass, per kernel launch."""
+    e = 2 if w.dtype == 1 else 4
+    S = min(w.B, w.capacity)
+    H, G, C, d = w.heads, w.G, w.C, w.d
+    return {
+        # assignment contraction of one k-means iteration: 2 L C d flops per head
+        "assign_flops": 2.0 * H * w.L * C * d,
+        # select: centroids, sizes, offsets, the emitted members' ids (read) and sel_ids (written), queries
+        "select_bytes": H * (C * d * 4 + C * 4 + (C + 1) * 4 + S * 4 + S * 4 + G * d * e),
+        # decode: selected ids, K and V rows, queries, fp32 output
+        "decode_bytes": H * (S * 4 + 2 * S * d * e + G * d * e + G * d * 4),
+        # whole decode step (select + gather + attention), each byte once
+        "step_bytes": H * (C * d * 4 + C * 4 + (C + 1) * 4 + S * 4 + 2 * S * d * e + G * d * e + G * d * 4),
+        "kmeans_flops": 2.0 * w.iters * H * w.L * C * d,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=4, help="synthetic configuration 1-5 (default 4)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--decode-path", choices=["fused", "split"], default="fused",
+                    help="fused: kv_cluster_select_decode (one kernel per step); "
+                         "split: kv_cluster_select then kv_sparse_decode")
+    ap.add_argument("--cpu-heads", type=int, default=16, help="KV heads in the CPU baseline sample")
+    ap.add_argument("--cpu-steps", type=int, default=32, help="decode steps in the CPU baseline sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build runs the path on a single MI355X "
+              "(the path shards by KV head with no exchange; see DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import clustered_sparse_attention_kv_amd as kvc
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kvc.lib()  # fails loudly without the built library
+    dev = torch.device("cuda:0")
+    w = synth.workload(args.workload)
+    if w.layers > 1:
+        print("multi-layer workloads are run by bench_stack (not in this script)", file=sys.stderr)
+        sys.exit(2)
+    H, G, L, d, C, B, cap = w.heads, w.G, w.L, w.d, w.C, w.B, w.capacity
+    tdt = torch.bfloat16 if w.dtype == synth.BF16 else torch.float32
+
+    # ---------------- inputs (host generation, then copy to HBM) -------------
+    t0 = time.time()
+    base = synth.config_seed(w.config, 0)
+    K, _, means = synth.mixture_keys(base, H, cap, d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype,
+                                     want_means=(w.query == "mixture"))
+    V = synth.values(base, H, cap, d, w.dtype)
+    init = synth.init_idx(base, H, L, C)
+    qs = []
+    for s in range(w.steps):
+        n_cur = L + (s + 1 if w.append else 0)
+        if w.query == "mixture":
+            qs.append(synth.queries_mixture(base, s, H * G, G, means, w.q_sigma, w.dtype))
+        else:
+            qs.append(synth.queries_noisy_key(base, s, H * G, G, K, n_cur, w.q_sigma))
+    Q = np.stack(qs)
+    log(f"[bench] generated {w.name} inputs in {time.time() - t0:.1f}s")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    Kp = K.copy()
+    Vp = V.copy()
+    if w.append:  # appended rows come in through the append call
+        Kp[:, L:] = 0
+        Vp[:, L:] = 0
+    Kd, Vd = to_dev(Kp), to_dev(Vp)
+    Qd = to_dev(Q)
+    init_d = to_dev(init)
+    if w.append:
+        Knew = to_dev(np.ascontiguousarray(K[:, L:].transpose(1, 0, 2)))  # [steps, H, d]
+        Vnew = to_dev(np.ascontiguousarray(V[:, L:].transpose(1, 0, 2)))
+    del K, V, Kp, Vp
+    idx = kvc.ClusterIndex(H, C, cap, tdt, device=dev)
+    ws_build = torch.empty(kvc.build_workspace_bytes(H, L, C, w.iters), dtype=torch.uint8, device=dev)
+    ws_dec = torch.empty(kvc.decode_workspace_bytes(H, H * G, B), dtype=torch.uint8, device=dev)
+    fused = args.decode_path == "fused"
+    sel = torch.empty(H, B, dtype=torch.int32, device=dev)
+    cnt = torch.empty(H, dtype=torch.int32, device=dev)
+    out = torch.empty(H * G, d, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    # plain copy of a known size, for scaling the profiler's byte counters
+    cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    del cal_src, cal_dst
+
+    # events: per pass, 2*iters around the assignment kernel, build bracket,
+    # and 2 per phase of every decode step (append, select, decode)
+    per_pass = 2 * w.iters + 2 + 6 * w.steps
+    total_passes = args.warmup + args.steps
+    ev = HipEvents(per_pass * total_passes + 2)
+
+    def one_pass(p: int):
+        o = p * per_pass
+        ev.record(o + 2 * w.iters, sh)
+        kvc.build(idx, Kd, L, w.iters, init_d, workspace=ws_build, assign_events=ev.sub(o, 2 * w.iters))
+        ev.record(o + 2 * w.iters + 1, sh)
+        b = o + 2 * w.iters + 2
+        for s in range(w.steps):
+            e6 = b + 6 * s
+            if w.append:
+                ev.record(e6, sh)
+                kvc.append(idx, Kd, Vd, Knew[s].unsqueeze(1), Vnew[s].unsqueeze(1))
+                ev.record(e6 + 1, sh)
+            ev.record(e6 + 2, sh)
+            if fused:
+                ev.record(e6 + 3, sh)
+                kvc.select_decode(idx, Qd[s], Kd, Vd, B, scale, out=out)
+            else:
+                kvc.select(idx, Qd[s], B, sel, cnt)
+                ev.record(e6 + 3, sh)
+                kvc.sparse_decode(Qd[s], Kd, Vd, sel, cnt, scale, out=out, workspace=ws_dec)
+            ev.record(e6 + 4, sh)
+
+    for p in range(args.warmup):
+        one_pass(p)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev.record(per_pass * total_passes, sh)
+    for p in range(args.warmup, total_passes):
+        one_pass(p)
+    ev.record(per_pass * total_passes + 1, sh)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    total_ms = ev.ms(per_pass * total_passes, per_pass * total_passes + 1)
+
+    assign_ms, build_ms, select_ms, decode_ms, append_ms, dstep_ms = [], [], [], [], [], []
+    for p in range(args.warmup, total_passes):
+        o = p * per_pass
+        assign_ms += [ev.ms(o + 2 * t, o + 2 * t + 1) for t in range(w.iters)]
+        build_ms.append(ev.ms(o + 2 * w.iters, o + 2 * w.iters + 1))
+        b = o + 2 * w.iters + 2
+        for s in range(w.steps):
+            e6 = b + 6 * s
+            if w.append:
+                append_ms.append(ev.ms(e6, e6 + 1))
+            select_ms.append(ev.ms(e6 + 2, e6 + 3))
+            decode_ms.append(ev.ms(e6 + 3, e6 + 4))
+            dstep_ms.append(ev.ms(e6 if w.append else e6 + 2, e6 + 4))
+
+    alg = algorithmic(w)
+    mean = lambda x: sum(x) / len(x) if x else 0.0
+    a_ms, s_ms, dd_ms = mean(assign_ms), mean(select_ms), mean(decode_ms)
+    decode_phase_s = sum(dstep_ms) / 1e3
+    n_dec = args.steps * w.steps
+    value = n_dec / decode_phase_s
+    kmeans_tflops = alg["kmeans_flops"] * args.steps / (sum(build_ms) / 1e3) / 1e12
+
+    assign_peak = PEAK_BF16 if w.dtype == synth.BF16 else PEAK_F64
+    rl = {
+        "assign": {"bound": "mfma" if w.dtype == synth.BF16 else "alu", "achieved": alg["assign_flops"] / (a_ms / 1e3) / 1e12,
+                   "peak": assign_peak / 1e12, "unit": "TFLOP/s", "avg_us": a_ms * 1e3,
+                   "share": sum(assign_ms) / (total_ms)},
+    }
+    kernel_names = {"assign": "assign_bf16_mfma_kernel" if w.dtype == synth.BF16 else "assign_exact_kernel"}
+    if fused:
+        rl["select_decode"] = {"bound": "hbm", "achieved": alg["step_bytes"] / (dd_ms / 1e3) / 1e9,
+                               "peak": PEAK_HBM / 1e9, "unit": "GB/s", "avg_us": dd_ms * 1e3,
+                               "share": sum(decode_ms) / total_ms}
+        kernel_names["select_decode"] = "select_decode_kernel"
+    else:
+        rl["sparse_decode"] = {"bound": "hbm", "achieved": alg["decode_bytes"] / (dd_ms / 1e3) / 1e9,
+                               "peak": PEAK_HBM / 1e9, "unit": "GB/s", "avg_us": dd_ms * 1e3,
+                               "share": sum(decode_ms) / total_ms}
+        rl["select"] = {"bound": "hbm", "achieved": alg["select_bytes"] / (s_ms / 1e3) / 1e9, "peak": PEAK_HBM / 1e9,
+                        "unit": "GB/s", "avg_us": s_ms * 1e3, "share": sum(select_ms) / total_ms}
+        kernel_names["sparse_decode"] = "decode_split_kernel + decode_combine_kernel"
+        kernel_names["select"] = "select_kernel"
+    traffic = {}
+    if os.path.exists(PROFILE_TRAFFIC):
+        with open(PROFILE_TRAFFIC) as f:
+            prof = json.load(f)
+        rec = prof.get(w.name, {})
+        if rec.get("source_digest") == source_digest():
+            traffic = rec.get("bytes_per_launch", {})
+    for k, r in rl.items():
+        r["frac"] = r["achieved"] / r["peak"]
+        r["traffic"] = traffic.get(kernel_names[k])
+        r["kernel"] = kernel_names[k]
+    dominant = max(rl, key=lambda k: rl[k]["share"])
+    roofline = {k2: rl[dominant][k2] for k2 in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roofline["kernel"] = kernel_names[dominant]
+    roofline["avg_us"] = rl[dominant]["avg_us"]
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == synth.BF16 else "f32",
+        "data": "synthetic (seeded Gaussian-mixture keys with outlier channels, N(0,1) values)",
+        "config": {"workload": w.name, "kv_heads_total": H, "q_heads_total": H * G, "G": G, "L": L, "d": d, "C": C,
+                   "kmeans_iters": w.iters, "B": B, "decode_steps_per_step": w.steps, "append": w.append,
+                   "decode_path": args.decode_path},
+        "kmeans_tflops": kmeans_tflops,
+        "kmeans_ms": mean(build_ms),
+        "decode_step_us": mean(dstep_ms) * 1e3,
+        "decode_step_hbm_frac": alg["step_bytes"] / (mean(dstep_ms) / 1e3) / PEAK_HBM,
+        "wall_s_timed": wall,
+        "roofline": roofline,
+        "rooflines": rl,
+    }
+    if w.append:
+        result["append_us"] = mean(append_ms) * 1e3
+
+    # ---------------- CPU oracle baseline (bounded sample) -----------------
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, args, base, init, Q)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, args, base, init, Q):
+    """The oracle as it stands on the host cores: select + decode of a sample
+    of KV heads over a few decode steps, scaled to the whole workload's heads."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    nh = min(args.cpu_heads, w.heads)
+    ns = min(args.cpu_steps, w.steps)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    # the sample's inputs: the first nh KV heads of the same workload
+    K, _, _ = synth.mixture_keys(base, nh, w.L, w.d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype)
+    V = synth.values(base, nh, w.L, w.d, w.dtype)
+    t0 = time.perf_counter()
+    built = oracle.build(K, w.C, 1, init[:nh], early_exit=False)   # one k-means iteration of the sample
+    t_iter = time.perf_counter() - t0
+    scale = 1.0 / math.sqrt(w.d)
+    t0 = time.perf_counter()
+    for s in range(ns):
+        q = np.ascontiguousarray(Q[s, :nh * w.G])
+        sel, cnt, _, _ = oracle.select(q, w.G, built["c"], built["sizes"], built["offsets"], built["token_ids"], w.B)
+        oracle.decode(q, w.G, K, V, sel, cnt, scale)
+    t_dec = (time.perf_counter() - t0) / ns
+    per_step_full = t_dec * w.heads / nh
+    flops_iter = 2.0 * nh * w.L * w.C * w.d
+    return {"value": 1.0 / per_step_full, "unit": "decode steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nh} of {w.heads} KV heads x {ns} decode steps (select + decode), scaled x{w.heads / nh:.0f}; "
+                      f"plus one k-means iteration of the {nh} heads",
+            "kmeans_gflops": flops_iter / t_iter / 1e9}
+
+
+if __name__ == "__main__":
+    main()

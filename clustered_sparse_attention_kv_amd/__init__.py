@@ -35,7 +35,8 @@ class _Index(C.Structure):
                 ("dtype", C.c_int32), ("n_build", C.c_int32), ("n_tokens", C.c_int32), ("reserved", C.c_int32),
                 ("centroids", C.c_void_p), ("centroids_op", C.c_void_p), ("labels", C.c_void_p),
                 ("sizes", C.c_void_p), ("offsets", C.c_void_p), ("token_ids", C.c_void_p),
-                ("app_offsets", C.c_void_p), ("app_ids", C.c_void_p), ("dev_flags", C.c_void_p)]
+                ("app_offsets", C.c_void_p), ("app_ids", C.c_void_p), ("dev_flags", C.c_void_p),
+                ("centroids_t", C.c_void_p)]
 
 
 def lib():
@@ -51,18 +52,20 @@ def lib():
         L.kv_cluster_build_workspace_bytes.argtypes = [i, i, i, i]
         L.kv_cluster_build_workspace_bytes.restype = sz
         L.kv_cluster_build.argtypes = [p, p, i, i, p, p, sz, p]
+        L.kv_cluster_build_timed.argtypes = [p, p, i, i, p, p, sz, p, p]
         L.kv_cluster_append.argtypes = [p, p, p, p, p, i, p]
         L.kv_cluster_select.argtypes = [p, p, i, i, p, p, p]
         L.kv_sparse_decode_workspace_bytes.argtypes = [i, i, i, i]
         L.kv_sparse_decode_workspace_bytes.restype = sz
         L.kv_sparse_decode.argtypes = [p, i, p, p, i, i, i, i, p, p, i, f, p, p, sz, p]
+        L.kv_cluster_select_decode.argtypes = [p, p, i, p, p, i, f, p, p, p, p]
         L.kv_cluster_export_csr.argtypes = [p, p, p, p]
         L.kv_cluster_debug_assign.argtypes = [p, p, i, p, p, p, p, p, sz, p]
         L.kv_cluster_debug_update.argtypes = [p, p, i, p, sz, p]
         L.kv_cluster_status_string.argtypes = [i]
         L.kv_cluster_status_string.restype = C.c_char_p
-        for name in ("kv_cluster_build", "kv_cluster_append", "kv_cluster_select", "kv_sparse_decode",
-                     "kv_cluster_export_csr", "kv_cluster_debug_assign", "kv_cluster_debug_update"):
+        for name in ("kv_cluster_build", "kv_cluster_build_timed", "kv_cluster_append", "kv_cluster_select", "kv_sparse_decode",
+                     "kv_cluster_select_decode", "kv_cluster_export_csr", "kv_cluster_debug_assign", "kv_cluster_debug_update"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -133,10 +136,12 @@ class ClusterIndex:
         self.app_offsets = torch.zeros(heads, C_ + 1, **i32)
         self.app_ids = torch.full((heads, capacity), -1, **i32)
         self.dev_flags = torch.zeros(1, **i32)
+        self.centroids_t = torch.zeros(heads, d // 4, C_, 4, dtype=torch.float32, device=device)
         self._s = _Index(heads, d, C_, capacity, _dtype_code(dtype), 0, 0, 0,
                          self.centroids.data_ptr(), self.centroids_op.data_ptr(), self.labels.data_ptr(),
                          self.sizes.data_ptr(), self.offsets.data_ptr(), self.token_ids.data_ptr(),
-                         self.app_offsets.data_ptr(), self.app_ids.data_ptr(), self.dev_flags.data_ptr())
+                         self.app_offsets.data_ptr(), self.app_ids.data_ptr(), self.dev_flags.data_ptr(),
+                         self.centroids_t.data_ptr())
 
     @property
     def n_build(self) -> int:
@@ -157,16 +162,26 @@ def _cache_check(idx: ClusterIndex, t: torch.Tensor, name: str):
 
 
 def build(idx: ClusterIndex, keys: torch.Tensor, L: int, iters: int, init_idx: torch.Tensor,
-          workspace: torch.Tensor | None = None, stream=None):
-    """kv_cluster_build: cluster the first L rows of keys [heads, capacity, d]."""
+          workspace: torch.Tensor | None = None, stream=None, assign_events=None):
+    """kv_cluster_build: cluster the first L rows of keys [heads, capacity, d].
+
+    assign_events: optional ctypes array of 2*iters hipEvent_t handles
+    (kv_cluster_build_timed) recorded around each assignment kernel."""
     _cache_check(idx, keys, "keys")
     if init_idx.dtype != torch.int32 or tuple(init_idx.shape) != (idx.heads, idx.C):
         raise ValueError("init_idx must be int32 [heads, C]")
     need = build_workspace_bytes(idx.heads, L, idx.C, iters)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=keys.device)
-    _check(lib().kv_cluster_build(idx.ref(), _ptr(keys), L, iters, _ptr(init_idx), _ptr(workspace),
-                                  workspace.numel(), _stream(stream)), "kv_cluster_build")
+    if assign_events is None:
+        _check(lib().kv_cluster_build(idx.ref(), _ptr(keys), L, iters, _ptr(init_idx), _ptr(workspace),
+                                      workspace.numel(), _stream(stream)), "kv_cluster_build")
+    else:
+        if len(assign_events) < 2 * iters:
+            raise ValueError("assign_events needs 2 * iters handles")
+        _check(lib().kv_cluster_build_timed(idx.ref(), _ptr(keys), L, iters, _ptr(init_idx), _ptr(workspace),
+                                            workspace.numel(), assign_events, _stream(stream)),
+               "kv_cluster_build_timed")
     return workspace
 
 
@@ -204,9 +219,7 @@ def select(idx: ClusterIndex, q: torch.Tensor, B: int, sel_ids: torch.Tensor | N
 def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, sel_ids: torch.Tensor,
                   sel_count: torch.Tensor, scale: float, out: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None, stream=None):
-    """kv_sparse_decode: attention of q [q_heads, d] over the selected rows -> fp32 [q_heads, d].
-
-    The workspace must be zero-filled before its first use (torch.zeros)."""
+    """kv_sparse_decode: attention of q [q_heads, d] over the selected rows -> fp32 [q_heads, d]."""
     heads, capacity, d = k_cache.shape
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype or q.dtype != k_cache.dtype:
         raise ValueError("q, k_cache and v_cache must share a type; k and v caches a shape")
@@ -216,11 +229,31 @@ def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if out is None:
         out = torch.empty(q.shape[0], d, dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = torch.zeros(max(decode_workspace_bytes(heads, q.shape[0], B, d), 1), dtype=torch.uint8,
+        workspace = torch.empty(max(decode_workspace_bytes(heads, q.shape[0], B, d), 1), dtype=torch.uint8,
                                 device=q.device)
     _check(lib().kv_sparse_decode(_ptr(q), q.shape[0], _ptr(k_cache), _ptr(v_cache), _dtype_code(q.dtype), heads,
                                   capacity, d, _ptr(sel_ids), _ptr(sel_count), B, float(scale), _ptr(out),
                                   _ptr(workspace), workspace.numel(), _stream(stream)), "kv_sparse_decode")
+    return out
+
+
+def select_decode(idx: ClusterIndex, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, B: int,
+                  scale: float, out: torch.Tensor | None = None, sel_ids: torch.Tensor | None = None,
+                  sel_count: torch.Tensor | None = None, stream=None):
+    """kv_cluster_select_decode: selection and sparse attention in one kernel -> fp32 [q_heads, d]."""
+    _cache_check(idx, k_cache, "k_cache")
+    _cache_check(idx, v_cache, "v_cache")
+    if q.dtype != idx.dtype or q.dim() != 2 or q.shape[1] != idx.d:
+        raise ValueError(f"q must be {idx.dtype} [q_heads, {idx.d}]")
+    if out is None:
+        out = torch.empty(q.shape[0], idx.d, dtype=torch.float32, device=q.device)
+    if sel_ids is not None and (sel_ids.dtype != torch.int32 or tuple(sel_ids.shape) != (idx.heads, B)):
+        raise ValueError("sel_ids must be int32 [heads, B]")
+    if sel_count is not None and (sel_count.dtype != torch.int32 or sel_count.numel() != idx.heads):
+        raise ValueError("sel_count must be int32 [heads]")
+    _check(lib().kv_cluster_select_decode(idx.ref(), _ptr(q), q.shape[0], _ptr(k_cache), _ptr(v_cache), B,
+                                          float(scale), _ptr(out), _ptr(sel_ids), _ptr(sel_count), _stream(stream)),
+           "kv_cluster_select_decode")
     return out
 
 

@@ -16,7 +16,7 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 bool index_ok(const kvc_index* idx) {
   return idx && idx->centroids && idx->centroids_op && idx->labels && idx->sizes && idx->offsets && idx->token_ids &&
-         idx->app_offsets && idx->app_ids && idx->dev_flags && idx->heads >= 1 && idx->capacity >= 1 && idx->C >= 1 &&
+         idx->app_offsets && idx->app_ids && idx->dev_flags && idx->centroids_t && idx->heads >= 1 && idx->capacity >= 1 && idx->C >= 1 &&
          (idx->dtype == KVC_F32 || idx->dtype == KVC_BF16);
 }
 
@@ -62,6 +62,11 @@ size_t kv_cluster_build_workspace_bytes(int heads, int L, int C, int iters) {
 
 int kv_cluster_build(kvc_index* idx, const void* keys, int L, int iters, const int32_t* init_idx, void* ws,
                      size_t ws_bytes, void* stream) {
+  return kv_cluster_build_timed(idx, keys, L, iters, init_idx, ws, ws_bytes, nullptr, stream);
+}
+
+int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, const int32_t* init_idx, void* ws,
+                           size_t ws_bytes, void* const* assign_events, void* stream) {
   if (!index_ok(idx) || !keys || !init_idx || !ws) return KVC_ERR_INVALID_ARG;
   if (int s = index_support(idx)) return s;
   const int H = idx->heads, C = idx->C, cap = idx->capacity, cpad = kv_cluster_cpad(C);
@@ -73,16 +78,17 @@ int kv_cluster_build(kvc_index* idx, const void* keys, int L, int iters, const i
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.qcount), (size_t)iters * H, 0, st);
   if (e == hipSuccess) e = launch_fill_i32(idx->app_offsets, (size_t)H * (C + 1), 0, st);
   if (e == hipSuccess)
-    e = launch_init_centroids(idx->dtype, keys, hs, H, L, init_idx, C, cpad, idx->centroids, idx->centroids_op,
-                              idx->dev_flags, st);
+    e = launch_init_centroids(idx->dtype, keys, hs, H, L, init_idx, C, cpad, idx->centroids, idx->centroids_t,
+                              idx->centroids_op, idx->dev_flags, st);
   for (int t = 0; t < iters && e == hipSuccess; ++t) {
+    hipEvent_t* ev = assign_events ? (hipEvent_t*)assign_events + 2 * t : nullptr;
     e = launch_assign(idx->dtype, keys, hs, H, L, idx->centroids_op, C, cpad, idx->labels, cap, w.queue,
-                      w.qcount + (size_t)t * H, nullptr, st);
+                      w.qcount + (size_t)t * H, nullptr, ev, st);
     if (e == hipSuccess)
       e = launch_csr(idx->labels, cap, H, L, C, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, st);
     if (e == hipSuccess)
       e = launch_update(idx->dtype, keys, hs, H, C, cpad, idx->sizes, idx->offsets, idx->token_ids, cap,
-                        idx->centroids, idx->centroids_op, st);
+                        idx->centroids, idx->centroids_t, idx->centroids_op, st);
   }
   if (e != hipSuccess) return KVC_ERR_HIP;
   idx->n_build = L;
@@ -102,7 +108,7 @@ int kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.qcount), (size_t)H, 0, st);
   if (e == hipSuccess)
     e = launch_assign(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, L, chat, C, cpad, labels, cap, w.queue,
-                      w.qcount, top2, st);
+                      w.qcount, top2, nullptr, st);
   if (e == hipSuccess && flagged)
     e = hipMemcpyAsync(flagged, w.qcount, sizeof(int32_t) * H, hipMemcpyDeviceToDevice, st);
   return hip_status(e);
@@ -119,7 +125,7 @@ int kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, s
   hipError_t e = launch_csr(idx->labels, cap, H, L, C, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, st);
   if (e == hipSuccess)
     e = launch_update(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, C, cpad, idx->sizes, idx->offsets,
-                      idx->token_ids, cap, idx->centroids, idx->centroids_op, st);
+                      idx->token_ids, cap, idx->centroids, idx->centroids_t, idx->centroids_op, st);
   return hip_status(e);
 }
 
@@ -147,7 +153,7 @@ int kv_cluster_select(const kvc_index* idx, const void* q, int q_heads, int B, i
   const int G = q_heads / idx->heads;
   if (G > KVC_MAX_G) return KVC_ERR_UNSUPPORTED;
   if ((long long)idx->heads * B >= (1ll << 31)) return KVC_ERR_INVALID_ARG;
-  return hip_status(launch_select(idx->dtype, q, G, idx->centroids, idx->heads, idx->C, idx->sizes, idx->offsets,
+  return hip_status(launch_select(idx->dtype, q, G, idx->centroids_t, idx->heads, idx->C, idx->sizes, idx->offsets,
                                   idx->token_ids, idx->app_offsets, idx->app_ids, idx->capacity, B, sel_ids,
                                   sel_count, static_cast<hipStream_t>(stream)));
 }
@@ -156,7 +162,7 @@ size_t kv_sparse_decode_workspace_bytes(int heads, int q_heads, int d, int B) {
   if (heads < 1 || q_heads < heads || d < 1 || B < 1) return 0;
   const int G = q_heads / heads;
   const size_t nsplit = (size_t)(B + DEC_TOK - 1) / DEC_TOK;
-  return align_up(sizeof(uint32_t) * (size_t)heads) + align_up(sizeof(float) * heads * nsplit * G * (d + 2));
+  return align_up(sizeof(float) * heads * nsplit * G * (d + 2));
 }
 
 int kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
@@ -168,12 +174,26 @@ int kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void
   if (d != KVC_HEAD_DIM) return KVC_ERR_UNSUPPORTED;
   const int G = q_heads / heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVC_ERR_UNSUPPORTED;
-  if ((long long)heads * B >= (1ll << 31) || (B + DEC_TOK - 1) / DEC_TOK > 65535) return KVC_ERR_INVALID_ARG;
+  if ((long long)heads * B >= (1ll << 31)) return KVC_ERR_INVALID_ARG;
+  if ((long long)((B + DEC_TOK - 1) / DEC_TOK) * G > DEC_MAX_PAIRS) return KVC_ERR_UNSUPPORTED;
   if (ws_bytes < kv_sparse_decode_workspace_bytes(heads, q_heads, d, B)) return KVC_ERR_WORKSPACE;
-  uint32_t* counters = static_cast<uint32_t*>(ws);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(sizeof(uint32_t) * (size_t)heads));
   return hip_status(launch_decode(dtype, q, G, k_cache, v_cache, (long long)capacity * d, heads, sel_ids, sel_count, B,
-                                  scale, out, part, counters, static_cast<hipStream_t>(stream)));
+                                  scale, out, static_cast<float*>(ws), static_cast<hipStream_t>(stream)));
+}
+
+int kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, const void* k_cache,
+                             const void* v_cache, int B, float scale, float* out, int32_t* sel_ids,
+                             int32_t* sel_count, void* stream) {
+  if (!index_ok(idx) || !q || !k_cache || !v_cache || !out || B < 1 || q_heads < 1) return KVC_ERR_INVALID_ARG;
+  if (int s = index_support(idx)) return s;
+  if (idx->n_build < 1 || q_heads % idx->heads != 0) return KVC_ERR_INVALID_ARG;
+  const int G = q_heads / idx->heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KVC_ERR_UNSUPPORTED;
+  if ((long long)idx->heads * B >= (1ll << 31)) return KVC_ERR_INVALID_ARG;
+  return hip_status(launch_select_decode(idx->dtype, q, G, idx->centroids_t, idx->heads, idx->C, idx->sizes,
+                                         idx->offsets, idx->token_ids, idx->app_offsets, idx->app_ids, idx->capacity,
+                                         k_cache, v_cache, B, scale, out, sel_ids, sel_count,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token_ids, void* stream) {

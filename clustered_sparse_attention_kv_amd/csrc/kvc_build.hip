@@ -19,7 +19,7 @@ namespace kvc {
 // once to the operand type (zero when the norm is zero). The ascending sum is
 // one lane's chain so its order is fixed.
 template <typename OT>
-__device__ void normalize_row(const float c0, const float c1, float* lds_row, OT* out_row) {
+__device__ __forceinline__ void normalize_row(const float c0, const float c1, float* lds_row, OT* out_row) {
   const int lane = lane_id();
   lds_row[2 * lane] = c0;
   lds_row[2 * lane + 1] = c1;
@@ -48,10 +48,23 @@ __device__ void normalize_row(const float c0, const float c1, float* lds_row, OT
 // a1 + a2: initial centroids c_k = K[init_idx[k]] (exact copy to fp32) and
 // their normalised operand. One wave per centroid row, 4 rows per block.
 // Rows k in [C, cpad) of the operand are zeroed.
+// The centroid pair (c0, c1) of channels 2*lane, 2*lane+1 of cluster k, also
+// stored in the chunk-major copy [d/4, C, 4] that selection reads coalesced.
+__device__ __forceinline__ void store_centroid(float* cent_row, float* cent_t_head, int C, int k, float c0, float c1) {
+  const int lane = lane_id();
+  cent_row[2 * lane] = c0;
+  cent_row[2 * lane + 1] = c1;
+  const int j = 2 * lane;
+  float* t = cent_t_head + ((size_t)(j >> 2) * C + k) * 4 + (j & 3);
+  t[0] = c0;
+  t[1] = c1;
+}
+
 template <typename KT>
 __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restrict__ keys, long long head_stride,
                                                              int L, const int32_t* __restrict__ init_idx, int C,
-                                                             int cpad, float* __restrict__ cent, KT* __restrict__ chat,
+                                                             int cpad, float* __restrict__ cent,
+                                                             float* __restrict__ cent_t, KT* __restrict__ chat,
                                                              int32_t* __restrict__ dev_flags) {
   __shared__ float rows[4][D];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -71,9 +84,7 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restric
   }
   const KT* src = keys + (size_t)h * head_stride + (size_t)tok * D;
   const float c0 = load_f32(src, 2 * lane), c1 = load_f32(src, 2 * lane + 1);
-  float* cr = cent + ((size_t)h * C + k) * D;
-  cr[2 * lane] = c0;
-  cr[2 * lane + 1] = c1;
+  store_centroid(cent + ((size_t)h * C + k) * D, cent_t + (size_t)h * C * D, C, k, c0, c1);
   normalize_row(c0, c1, rows[w], out);
 }
 
@@ -222,23 +233,39 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
 // ---------------------------------------------------------------------------
 // a3 exact path: label_i = argmax_k of the fp64 chain sum_j K_ij * chat_kj over
 // ascending j, lowest k on ties. Used for keys the matrix-core pass could not
-// certify, and for every key of fp32 inputs. One wave per key; lane c handles
-// centroids c, c+64, ...; the key's channel j reaches every lane through
-// readlane. Rows come from the per-head queue (queue != null) or are all rows.
+// certify, and for every key of fp32 inputs. One wave per key; lane c owns
+// centroids c, c+64, ...; channel j of the key reaches every lane through
+// readlane (a scalar operand of the fp64 fma). Operand rows are read in
+// 16-byte chunks; for bf16 the head's operand is staged in LDS once per block
+// with the chunk index of row r XOR-ed by r (mod the chunk count), so the 64
+// lanes of a wave, reading 64 different rows at one chunk, spread over the
+// banks. Rows come from the per-head queue (queue != null) or are all rows.
 template <typename KT>
 __global__ __launch_bounds__(256) void assign_exact_kernel(const KT* __restrict__ keys, long long head_stride, int L,
                                                            const KT* __restrict__ chat, int C, int cpad,
                                                            int32_t* __restrict__ labels, long long label_stride,
                                                            const int32_t* __restrict__ queue,
                                                            const uint32_t* __restrict__ qcount) {
+  constexpr bool STAGE = sizeof(KT) == 2;
+  constexpr int CHUNKS = D * (int)sizeof(KT) / 16;  // 16-byte chunks per operand row
+  constexpr int EPC = 16 / (int)sizeof(KT);         // elements per chunk
+  constexpr int MAXT = (512 + 63) / 64;
+  extern __shared__ u32x4 smem[];
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
   const int n = queue ? (int)__atomic_load_n(qcount + h, __ATOMIC_RELAXED) : L;
+  if (blockIdx.x * 4 >= n) return;  // no key for this block (uniform)
   const KT* Kh = keys + (size_t)h * head_stride;
-  const KT* Ch = chat + (size_t)h * cpad * D;
-  constexpr int MAXT = (512 + 63) / 64;
+  const u32x4* Cg = reinterpret_cast<const u32x4*>(chat + (size_t)h * cpad * D);
+  if constexpr (STAGE) {
+    for (int e = threadIdx.x; e < cpad * CHUNKS; e += 256) {
+      const int r = e / CHUNKS, c = e % CHUNKS;
+      smem[r * CHUNKS + (c ^ (r & (CHUNKS - 1)))] = Cg[e];
+    }
+    __syncthreads();
+  }
   for (int e = gw; e < n; e += nw) {
     const int row = queue ? queue[(size_t)h * L + e] : e;
     const double k0 = (double)load_f32(Kh, (size_t)row * D + lane);
@@ -246,16 +273,30 @@ __global__ __launch_bounds__(256) void assign_exact_kernel(const KT* __restrict_
     double s[MAXT];
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) s[t] = 0.0;
-    for (int j = 0; j < D; ++j) {
-      const double src = j < 64 ? k0 : k1;
-      const int jl = j & 63;
-      const int lo = __builtin_amdgcn_readlane((int)(__double_as_longlong(src) & 0xFFFFFFFFll), jl);
-      const int hi = __builtin_amdgcn_readlane((int)(__double_as_longlong(src) >> 32), jl);
-      const double kj = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
+#pragma unroll
+    for (int q = 0; q < CHUNKS; ++q) {
+      double kj[EPC];
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) {
+        const int j = q * EPC + i;
+        const double src = j < 64 ? k0 : k1;
+        const int lo = __builtin_amdgcn_readlane((int)(__double_as_longlong(src) & 0xFFFFFFFFll), j & 63);
+        const int hi = __builtin_amdgcn_readlane((int)(__double_as_longlong(src) >> 32), j & 63);
+        kj[i] = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
+      }
 #pragma unroll
       for (int t = 0; t < MAXT; ++t) {
         const int c = lane + 64 * t;
-        if (c < C) s[t] = fma(kj, (double)load_f32(Ch, (size_t)c * D + j), s[t]);
+        if (c < C) {
+          const u32x4 v = STAGE ? smem[c * CHUNKS + (q ^ (c & (CHUNKS - 1)))] : Cg[(size_t)c * CHUNKS + q];
+#pragma unroll
+          for (int i = 0; i < EPC; ++i) {
+            float x;
+            if constexpr (STAGE) x = (i & 1) ? __uint_as_float(v[i >> 1] & 0xFFFF0000u) : __uint_as_float(v[i >> 1] << 16);
+            else x = __uint_as_float(v[i]);
+            s[t] = fma(kj[i], (double)x, s[t]);
+          }
+        }
       }
     }
     double best = -INFINITY;
@@ -384,7 +425,8 @@ __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys
                                                      int cpad, const int32_t* __restrict__ sizes,
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ token_ids, long long ids_stride,
-                                                     float* __restrict__ cent, KT* __restrict__ chat) {
+                                                     float* __restrict__ cent, float* __restrict__ cent_t,
+                                                     KT* __restrict__ chat) {
   __shared__ float rows[4][D];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.y;
@@ -418,8 +460,7 @@ __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys
     }
     c0 = (float)(a0 / (double)n);
     c1 = (float)(a1 / (double)n);
-    cr[2 * lane] = c0;
-    cr[2 * lane + 1] = c1;
+    store_centroid(cr, cent_t + (size_t)h * C * D, C, k, c0, c1);
   } else {
     c0 = cr[2 * lane];
     c1 = cr[2 * lane + 1];
@@ -444,21 +485,21 @@ hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t v, hipStream_t st) {
 }
 
 hipError_t launch_init_centroids(int dtype, const void* keys, long long head_stride, int heads, int L,
-                                 const int32_t* init_idx, int C, int cpad, float* cent, void* chat, int32_t* flags,
-                                 hipStream_t st) {
+                                 const int32_t* init_idx, int C, int cpad, float* cent, float* cent_t, void* chat,
+                                 int32_t* flags, hipStream_t st) {
   dim3 grid(grid1(cpad, 4), heads);
   if (dtype == DT_BF16)
     init_centroids_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, L, init_idx, C, cpad,
-                                                          cent, (uint16_t*)chat, flags);
+                                                          cent, cent_t, (uint16_t*)chat, flags);
   else
     init_centroids_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, L, init_idx, C, cpad, cent,
-                                                       (float*)chat, flags);
+                                                       cent_t, (float*)chat, flags);
   return hipGetLastError();
 }
 
 hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
                          int cpad, int32_t* labels, long long label_stride, int32_t* queue, uint32_t* qcount,
-                         float* top2, hipStream_t st) {
+                         float* top2, hipEvent_t* events, hipStream_t st) {
   if (dtype == DT_BF16) {
     const size_t lds = (size_t)cpad * D * 2;
     static bool attr_set = false;
@@ -469,21 +510,42 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
       attr_set = true;
     }
     dim3 grid(grid1(L, AS_TILE), heads);
+    if (events) {
+      hipError_t e0 = hipEventRecord(events[0], st);
+      if (e0 != hipSuccess) return e0;
+    }
     assign_bf16_mfma_kernel<<<grid, AS_THREADS, lds, st>>>((const uint16_t*)keys, head_stride, L,
                                                              (const uint16_t*)chat, C, cpad, labels, label_stride,
                                                              queue, qcount, top2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (events) {
+      e = hipEventRecord(events[1], st);
+      if (e != hipSuccess) return e;
+    }
     // exact re-scoring of the uncertified keys; blocks without work exit at once
-    dim3 g2(16, heads);
-    assign_exact_kernel<uint16_t><<<g2, 256, 0, st>>>((const uint16_t*)keys, head_stride, L, (const uint16_t*)chat, C,
-                                                      cpad, labels, label_stride, queue, qcount);
+    static bool attr2 = false;
+    if (!attr2) {
+      e = hipFuncSetAttribute((const void*)assign_exact_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+      if (e != hipSuccess) return e;
+      attr2 = true;
+    }
+    dim3 g2(8, heads);
+    assign_exact_kernel<uint16_t><<<g2, 256, lds, st>>>((const uint16_t*)keys, head_stride, L, (const uint16_t*)chat, C,
+                                                        cpad, labels, label_stride, queue, qcount);
     return hipGetLastError();
   }
   dim3 g2(grid1(L, 4) < 64 ? grid1(L, 4) : 64, heads);
+  if (events) {
+    hipError_t e0 = hipEventRecord(events[0], st);
+    if (e0 != hipSuccess) return e0;
+  }
   assign_exact_kernel<float><<<g2, 256, 0, st>>>((const float*)keys, head_stride, L, (const float*)chat, C, cpad,
                                                  labels, label_stride, nullptr, nullptr);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && events) e = hipEventRecord(events[1], st);
+  return e;
 }
 
 hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, int L, int C, int32_t* hist,
@@ -502,14 +564,14 @@ hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, 
 
 hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cpad,
                          const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
-                         float* cent, void* chat, hipStream_t st) {
+                         float* cent, float* cent_t, void* chat, hipStream_t st) {
   dim3 grid(grid1(C, 4), heads);
   if (dtype == DT_BF16)
     update_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, C, cpad, sizes, offsets,
-                                                  token_ids, ids_stride, cent, (uint16_t*)chat);
+                                                  token_ids, ids_stride, cent, cent_t, (uint16_t*)chat);
   else
     update_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, C, cpad, sizes, offsets, token_ids,
-                                               ids_stride, cent, (float*)chat);
+                                               ids_stride, cent, cent_t, (float*)chat);
   return hipGetLastError();
 }
 

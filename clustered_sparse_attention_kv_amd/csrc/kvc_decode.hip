@@ -97,127 +97,594 @@ __global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __
 }
 
 // ---------------------------------------------------------------------------
-// a7-a9: selection, one block of 512 threads per KV head (C <= 512).
+// a7-a9: selection, computed by one block of 512 threads per KV head (C <= 512).
 //  1. qbar_j = fp64 sum over the head's G query heads (ascending g).
 //  2. score_k = fp64 chain qbar . c_k over ascending j; thread k owns cluster k.
-//  3. Bitonic sort of (score, k) into (score descending, k ascending) order.
+//  3. Bitonic sort of (score, k) into (score descending, k ascending) order;
+//     strides below 64 exchange through wave shuffles, larger ones through LDS.
 //  4. Exclusive prefix W_r of sizes in rank order: rank r starts at W_r.
-//  5. Output position p < min(B, N) belongs to the last rank r with W_r <= p;
-//     it takes member p - W_r of that cluster (built part, then appended part),
-//     so every cluster before the cut is whole and the last one is trimmed.
+//  5. Output position p < min(B, N) belongs to the last rank r with W_r <= p
+//     and takes member p - W_r of that cluster (built part, then appended
+//     part), so every cluster before the cut is whole and the last is trimmed.
+constexpr int SEL_THREADS = 512;
+
+struct SelShared {
+  double qbar[D];
+  unsigned long long xkey[SEL_THREADS];
+  int xid[SEL_THREADS];
+  int W[SEL_THREADS];      // exclusive prefix of sizes in rank order
+  int obase[SEL_THREADS];  // offsets[k_r]
+  int nbase[SEL_THREADS];  // built members of k_r
+  int abase[SEL_THREADS];  // app_offsets[k_r]
+  int mn[SEL_THREADS], mo[SEL_THREADS], mb[SEL_THREADS], ma[SEL_THREADS];  // per cluster k: size, offset, built, app offset
+  int wsum[SEL_THREADS / WAVE];
+  int total;
+};
+
+// Value of lane (lane ^ S) within the wave: DPP quad permutes for S = 1, 2,
+// ds_swizzle in bit mode (xor mask, within 32 lanes) for S = 4 .. 16, and a
+// crossbar permute for S = 32.
+template <int S>
+__device__ __forceinline__ int lane_xor(int v) {
+  if constexpr (S == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (S == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (S < 32) return __builtin_amdgcn_ds_swizzle(v, (S << 10) | 0x1F);
+  else return __shfl_xor(v, S);
+}
+
+// One compare-exchange stage of the bitonic sort over the block (thread t
+// holds element t): partner t ^ STRIDE, through LDS when it lies in another
+// wave. Sub-sequences of SIZE end up best-first where t & SIZE == 0.
+template <int SIZE, int STRIDE, typename Sh>
+__device__ __forceinline__ void bitonic_stage(Sh& S, unsigned long long& key, int& id, int tid) {
+  unsigned long long ok;
+  int oi;
+  if constexpr (STRIDE >= WAVE) {
+    S.xkey[tid] = key;
+    S.xid[tid] = id;
+    __syncthreads();
+    ok = S.xkey[tid ^ STRIDE];
+    oi = S.xid[tid ^ STRIDE];
+    __syncthreads();
+  } else {
+    const int lo = lane_xor<STRIDE>((int)(key & 0xFFFFFFFFull));
+    const int hi = lane_xor<STRIDE>((int)(key >> 32));
+    ok = ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
+    oi = lane_xor<STRIDE>(id);
+  }
+  const bool want_better = ((tid & SIZE) == 0) == ((tid & STRIDE) == 0);
+  const bool partner_better = ok > key || (ok == key && oi < id);
+  if (want_better == partner_better) {
+    key = ok;
+    id = oi;
+  }
+  if constexpr (STRIDE > 1) bitonic_stage<SIZE, STRIDE / 2>(S, key, id, tid);
+}
+
+template <int SIZE, int N, typename Sh>
+__device__ __forceinline__ void bitonic_sort(Sh& S, unsigned long long& key, int& id, int tid) {
+  bitonic_stage<SIZE, SIZE / 2>(S, key, id, tid);
+  if constexpr (SIZE < N) bitonic_sort<SIZE * 2, N>(S, key, id, tid);
+}
+
+// cent_t is the chunk-major copy [d/4, C, 4] of the head's centroids: thread k
+// reads chunk jj of its row at ((jj * C) + k) * 16 bytes, so a wave's loads are
+// contiguous. The chain still runs over ascending j.
 template <typename QT>
-__global__ __launch_bounds__(512) void select_kernel(const QT* __restrict__ q, int G, const float* __restrict__ cent,
-                                                     int C, const int32_t* __restrict__ sizes,
-                                                     const int32_t* __restrict__ offsets,
-                                                     const int32_t* __restrict__ token_ids,
-                                                     const int32_t* __restrict__ app_offsets,
-                                                     const int32_t* __restrict__ app_ids, long long cap, int B,
-                                                     int32_t* __restrict__ sel_ids, int32_t* __restrict__ sel_count) {
-  __shared__ double qbar[D];
-  __shared__ unsigned long long key[512];
-  __shared__ int kid[512];
-  __shared__ int W[512];
-  const int h = blockIdx.x, tid = threadIdx.x;
+__device__ __forceinline__ void select_phase(SelShared& S, const QT* __restrict__ q, int G,
+                                             const float* __restrict__ cent_t, int C,
+                                             const int32_t* __restrict__ sizes, const int32_t* __restrict__ offsets,
+                                             const int32_t* __restrict__ app_offsets, int h) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid < C) {  // per-cluster metadata, read while the scores are computed
+    S.mn[tid] = sizes[(size_t)h * C + tid];
+    const int o = offsets[(size_t)h * (C + 1) + tid];
+    S.mo[tid] = o;
+    S.mb[tid] = offsets[(size_t)h * (C + 1) + tid + 1] - o;
+    S.ma[tid] = app_offsets[(size_t)h * (C + 1) + tid];
+  }
   if (tid < D) {
     double s = 0.0;
     for (int g = 0; g < G; ++g) s = s + (double)load_f32(q, ((size_t)h * G + g) * D + tid);
-    qbar[tid] = s;
+    S.qbar[tid] = s;
   }
   __syncthreads();
-  unsigned long long u = 0;
-  int k = 0x7FFFFFFF;
+  unsigned long long key = 0;
+  int id = 0x7FFFFFFF;
   if (tid < C) {
-    const f32x4* cr = reinterpret_cast<const f32x4*>(cent + ((size_t)h * C + tid) * D);
+    const f32x4* ct = reinterpret_cast<const f32x4*>(cent_t + (size_t)h * C * D) + tid;
     double s = 0.0;
-#pragma unroll 4
-    for (int jj = 0; jj < D / 4; ++jj) {
-      const f32x4 v = cr[jj];
-      s = fma(qbar[4 * jj], (double)v[0], s);
-      s = fma(qbar[4 * jj + 1], (double)v[1], s);
-      s = fma(qbar[4 * jj + 2], (double)v[2], s);
-      s = fma(qbar[4 * jj + 3], (double)v[3], s);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      f32x4 v[16];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) v[jj] = ct[(size_t)(half * 16 + jj) * C];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = fma(S.qbar[half * 64 + 4 * jj + i], (double)v[jj][i], s);
     }
-    u = ordered_key(s);
-    k = tid;
+    key = ordered_key(s);
+    id = tid;
   }
-  key[tid] = u;
-  kid[tid] = k;
-  __syncthreads();
-  // bitonic sort, best first: "better" = larger key, then smaller id
-  for (int size = 2; size <= 512; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int o = tid ^ stride;
-      if (o > tid) {
-        const unsigned long long ua = key[tid], ub = key[o];
-        const int ka = kid[tid], kb = kid[o];
-        const bool a_better = ua > ub || (ua == ub && ka < kb);
-        const bool swap = (tid & size) == 0 ? !a_better : a_better;
-        if (swap) {
-          key[tid] = ub;
-          key[o] = ua;
-          kid[tid] = kb;
-          kid[o] = ka;
-        }
-      }
-      __syncthreads();
-    }
+  // bitonic sort, best first ("better" = larger key, then smaller id)
+  bitonic_sort<2, SEL_THREADS>(S, key, id, tid);
+  // thread r now holds rank r; prefix of sizes in rank order
+  int n = 0, ob = 0, nb = 0, ab = 0;
+  if (id < C) {
+    n = S.mn[id];
+    ob = S.mo[id];
+    nb = S.mb[id];
+    ab = S.ma[id];
   }
-  const int kr = kid[tid];
-  const int nr = kr < C ? sizes[(size_t)h * C + kr] : 0;
-  W[tid] = nr;
-  __syncthreads();
-  for (int off = 1; off < 512; off <<= 1) {
-    const int v = tid >= off ? W[tid - off] : 0;
-    __syncthreads();
-    W[tid] += v;
-    __syncthreads();
+  int x = n;
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  const int total = W[511];
-  const int incl = W[tid];
+  if (lane == WAVE - 1) S.wsum[w] = x;
   __syncthreads();
-  W[tid] = incl - nr;  // exclusive
-  __syncthreads();
-  const int cnt = total < B ? total : B;
-  const int32_t* off = offsets + (size_t)h * (C + 1);
-  const int32_t* aoff = app_offsets + (size_t)h * (C + 1);
-  for (int p = tid; p < B; p += 512) {
-    int tok = -1;
-    if (p < cnt) {
-      int lo = 0, hi = 511;  // last r with W[r] <= p
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (W[mid] <= p) lo = mid;
-        else hi = mid - 1;
-      }
-      const int kk = kid[lo];
-      const int e = p - W[lo];
-      const int nb = off[kk + 1] - off[kk];
-      tok = e < nb ? token_ids[(size_t)h * cap + off[kk] + e] : app_ids[(size_t)h * cap + aoff[kk] + (e - nb)];
-    }
-    sel_ids[(size_t)h * B + p] = tok;
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int v = 0; v < SEL_THREADS / WAVE; ++v) {
+    base += v < w ? S.wsum[v] : 0;
+    tot += S.wsum[v];
   }
+  S.W[tid] = base + x - n;
+  S.obase[tid] = ob;
+  S.nbase[tid] = nb;
+  S.abase[tid] = ab;
+  if (tid == 0) S.total = tot;
+  __syncthreads();
+}
+
+// Token at output position p (< total) of the ranked, trimmed selection.
+__device__ __forceinline__ int select_emit(const SelShared& S, int p, const int32_t* __restrict__ ids_h,
+                                           const int32_t* __restrict__ app_h) {
+  int lo = 0, hi = SEL_THREADS - 1;  // last r with W[r] <= p
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (S.W[mid] <= p) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = p - S.W[lo];
+  const int nb = S.nbase[lo];
+  return e < nb ? ids_h[S.obase[lo] + e] : app_h[S.abase[lo] + (e - nb)];
+}
+
+template <typename QT>
+__global__ __launch_bounds__(SEL_THREADS) void select_kernel(const QT* __restrict__ q, int G,
+                                                             const float* __restrict__ cent_t, int C,
+                                                             const int32_t* __restrict__ sizes,
+                                                             const int32_t* __restrict__ offsets,
+                                                             const int32_t* __restrict__ token_ids,
+                                                             const int32_t* __restrict__ app_offsets,
+                                                             const int32_t* __restrict__ app_ids, long long cap, int B,
+                                                             int32_t* __restrict__ sel_ids,
+                                                             int32_t* __restrict__ sel_count) {
+  __shared__ SelShared S;
+  const int h = blockIdx.x, tid = threadIdx.x;
+  select_phase(S, q, G, cent_t, C, sizes, offsets, app_offsets, h);
+  const int cnt = S.total < B ? S.total : B;
+  const int32_t* ids_h = token_ids + (size_t)h * cap;
+  const int32_t* app_h = app_ids + (size_t)h * cap;
+  for (int p = tid; p < B; p += SEL_THREADS)
+    sel_ids[(size_t)h * B + p] = p < cnt ? select_emit(S, p, ids_h, app_h) : -1;
   if (tid == 0) sel_count[h] = cnt;
 }
 
+// Sum over each row of 16 lanes, left in every lane of the row: quad swaps,
+// then the mirrored half-row, then the mirrored row (DPP, no LDS traffic).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // half-row mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row mirror
+  return v;
+}
+
 // ---------------------------------------------------------------------------
-// a10 + a11: gather + split-K single-query attention.
-// Grid (ceil(B / 64), heads); block = 4 waves over 64 selected tokens. In a
-// wave, 16 lanes cover one 128-channel row (8 channels each), so one load
-// instruction gathers 4 rows of K (or V) with 16-byte accesses per lane. The
-// G query heads of the KV head share every gathered row. Each block writes
-// (m, l, o[d]) per query head in the log2 domain (q is pre-scaled by
-// scale * log2 e); the last block of a head to finish merges the splits in
-// split order (a per-head arrival counter, reset by that block).
+// Rows of 8 channels as loaded: bf16 rows stay packed (4 VGPRs), fp32 rows are
+// two 16-byte vectors.
+template <typename KT>
+struct Row8;
+template <>
+struct Row8<uint16_t> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ float at(int c) const {
+    const uint32_t u = v[c >> 1];
+    return (c & 1) ? __uint_as_float(u & 0xFFFF0000u) : __uint_as_float(u << 16);
+  }
+};
+template <>
+struct Row8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ float at(int c) const { return c < 4 ? a[c] : b[c - 4]; }
+};
+
+// ---------------------------------------------------------------------------
+// a7-a11 fused: selection, gather and single-query attention of one KV head
+// in one block of 512 threads, with no exchange between blocks.
+// After the selection phase, the selected tokens are processed in chunks of
+// 512: each wave gathers 64 rows (16 lanes per 128-channel row, 8 channels
+// per lane, 16-byte loads), scores them against the G query heads sharing the
+// KV head (q pre-scaled by scale * log2 e), and the block keeps an online
+// softmax (running max and sum per query head, block-uniform) with per-lane
+// partial outputs rescaled at each chunk. The waves' partial outputs are
+// summed through LDS at the end.
 template <typename KT, int G>
-__global__ __launch_bounds__(256) void decode_kernel(const KT* __restrict__ q, const KT* __restrict__ kc,
-                                                     const KT* __restrict__ vc, long long head_stride,
-                                                     const int32_t* __restrict__ sel_ids,
-                                                     const int32_t* __restrict__ sel_count, int B, float qscale,
-                                                     float* __restrict__ out, float* __restrict__ part,
-                                                     uint32_t* __restrict__ counters) {
+__global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
+    const KT* __restrict__ q, const float* __restrict__ cent_t, int C, const int32_t* __restrict__ sizes,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ token_ids,
+    const int32_t* __restrict__ app_offsets, const int32_t* __restrict__ app_ids, long long cap,
+    const KT* __restrict__ kc, const KT* __restrict__ vc, int B, float qscale, float* __restrict__ out,
+    int32_t* __restrict__ sel_ids, int32_t* __restrict__ sel_count) {
+  constexpr int NW = SEL_THREADS / WAVE;                       // 8 waves
+  constexpr int RS = (G <= 4 && sizeof(KT) == 2) ? 16 : (G <= 2 ? 8 : 4);  // row steps per load batch
+  constexpr int NB = 16 / RS;                                  // batches per chunk
+  constexpr bool V_EARLY = NB == 1;                            // V gathered together with K
+  __shared__ SelShared S;
+  __shared__ int sel[SEL_THREADS];
+  __shared__ float sc[G][SEL_THREADS];
+  __shared__ float wred[NW][G];
+  __shared__ float ored[NW][G][D];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = lane >> 4, gl = lane & 15;
+  select_phase(S, q, G, cent_t, C, sizes, offsets, app_offsets, h);
+  const int cnt = S.total < B ? S.total : B;
+  if (sel_count && tid == 0) sel_count[h] = cnt;
+  if (sel_ids)
+    for (int p = cnt + tid; p < B; p += SEL_THREADS) sel_ids[(size_t)h * B + p] = -1;
+  const int32_t* ids_h = token_ids + (size_t)h * cap;
+  const int32_t* app_h = app_ids + (size_t)h * cap;
+  const KT* Kh = kc + (size_t)h * cap * D + 8 * gl;
+  const KT* Vh = vc + (size_t)h * cap * D + 8 * gl;
+
+  float qv[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    load8(q + ((size_t)h * G + g) * D + 8 * gl, qv[g]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qv[g][c] *= qscale;
+  }
+  float o[G][8];
+  float m_run[G], l_run[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[g][c] = 0.f;
+  }
+
+  for (int c0 = 0; c0 < cnt; c0 += SEL_THREADS) {
+    const int nchunk = cnt - c0 < SEL_THREADS ? cnt - c0 : SEL_THREADS;
+    {
+      const int p = c0 + tid;
+      const int tok = tid < nchunk ? select_emit(S, p, ids_h, app_h) : -1;
+      sel[tid] = tok;
+      if (sel_ids && tid < nchunk) sel_ids[(size_t)h * B + p] = tok;
+    }
+    __syncthreads();
+    Row8<KT> vrow[V_EARLY ? RS : 1];
+#pragma unroll 1
+    for (int b = 0; b < NB; ++b) {
+      Row8<KT> krow[RS];
+#pragma unroll
+      for (int r = 0; r < RS; ++r) {
+        const int t = w * 64 + (b * RS + r) * 4 + grp;
+        const int id = t < nchunk ? sel[t] : 0;
+        krow[r].load(Kh + (size_t)id * D);
+        if constexpr (V_EARLY) vrow[r].load(Vh + (size_t)id * D);
+      }
+#pragma unroll
+      for (int r = 0; r < RS; ++r) {
+        const int t = w * 64 + (b * RS + r) * 4 + grp;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float s = 0.f;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) s = fmaf(qv[g][c], krow[r].at(c), s);
+          s = row16_sum(s);
+          if (gl == 0) sc[g][t] = t < nchunk ? s : -INFINITY;
+        }
+      }
+    }
+    __syncthreads();
+    float mnew[G], f[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float m = sc[g][w * 64 + lane];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      if (lane == 0) wred[w][g] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float m = m_run[g];
+#pragma unroll
+      for (int v = 0; v < NW; ++v) m = fmaxf(m, wred[v][g]);
+      mnew[g] = m;
+      f[g] = m_run[g] == -INFINITY ? 0.f : exp2f(m_run[g] - m);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float s = sc[g][w * 64 + lane];
+      const float p = mnew[g] == -INFINITY ? 0.f : exp2f(s - mnew[g]);
+      sc[g][w * 64 + lane] = p;
+      float l = p;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+      if (lane == 0) wred[w][g] = l;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float l = 0.f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) l += wred[v][g];
+      l_run[g] = l_run[g] * f[g] + l;
+      m_run[g] = mnew[g];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o[g][c] *= f[g];
+    }
+#pragma unroll 1
+    for (int b = 0; b < NB; ++b) {
+      Row8<KT> vb[V_EARLY ? 1 : RS];
+      if constexpr (!V_EARLY) {
+#pragma unroll
+        for (int r = 0; r < RS; ++r) {
+          const int t = w * 64 + (b * RS + r) * 4 + grp;
+          const int id = t < nchunk ? sel[t] : 0;
+          vb[r].load(Vh + (size_t)id * D);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RS; ++r) {
+        const int t = w * 64 + (b * RS + r) * 4 + grp;
+        const Row8<KT>& vr = V_EARLY ? vrow[r] : vb[r];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float p = sc[g][t];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o[g][c] = fmaf(p, vr.at(c), o[g][c]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float v = o[g][c];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      o[g][c] = v;
+    }
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ored[w][g][8 * gl + c] = o[g][c];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * D; e += SEL_THREADS) {
+    const int g = e / D, j = e % D;
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) s += ored[v][g][j];
+    out[((size_t)h * G + g) * D + j] = l_run[g] > 0.f ? s / l_run[g] : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// a7-a11 fused, bf16: as above, with the query-key products of each chunk on
+// the matrix cores. Per wave and chunk, 64 selected keys form the B operand
+// of two v_mfma_f32_32x32x16_bf16 tiles (lane = key column, 64 channels of
+// its row in eight 16-byte pieces, channel order 64 * half + 8 * step + i for
+// both operands), the A operand holds the G query heads in its first rows
+// (bf16 inputs, fp32 accumulation; the scale multiplies the fp32 result), and
+// score (g, key) lands in lane key % 32 + 32 * (g / 4), register g % 4. The
+// value rows are gathered in the 16-lanes-per-row layout and weighted in fp32
+// on the vector units.
+template <int G>
+__global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ cent_t, int C, const int32_t* __restrict__ sizes,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ token_ids,
+    const int32_t* __restrict__ app_offsets, const int32_t* __restrict__ app_ids, long long cap,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int B, float qscale, float* __restrict__ out,
+    int32_t* __restrict__ sel_ids, int32_t* __restrict__ sel_count) {
+  static_assert(G <= 8, "at most 8 query heads per KV head");
+  constexpr int NW = SEL_THREADS / WAVE;
+  __shared__ SelShared S;
+  __shared__ int sel[SEL_THREADS];
+  __shared__ float sc[G][SEL_THREADS];
+  __shared__ float wred[NW][G];
+  __shared__ float ored[NW][G][D];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int grp = lane >> 4, gl = lane & 15;
+  select_phase(S, q, G, cent_t, C, sizes, offsets, app_offsets, h);
+  const int cnt = S.total < B ? S.total : B;
+  if (sel_count && tid == 0) sel_count[h] = cnt;
+  if (sel_ids)
+    for (int p = cnt + tid; p < B; p += SEL_THREADS) sel_ids[(size_t)h * B + p] = -1;
+  const int32_t* ids_h = token_ids + (size_t)h * cap;
+  const int32_t* app_h = app_ids + (size_t)h * cap;
+  const uint16_t* Kh = kc + (size_t)h * cap * D + 64 * half;
+  const uint16_t* Vh = vc + (size_t)h * cap * D + 8 * gl;
+
+  bf16x8 qa[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (col < G) v = *reinterpret_cast<const u32x4*>(q + ((size_t)h * G + col) * D + 64 * half + 8 * s);
+    qa[s] = __builtin_bit_cast(bf16x8, v);
+  }
+  float o[G][8];
+  float m_run[G], l_run[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[g][c] = 0.f;
+  }
+
+  for (int c0 = 0; c0 < cnt; c0 += SEL_THREADS) {
+    const int nchunk = cnt - c0 < SEL_THREADS ? cnt - c0 : SEL_THREADS;
+    {
+      const int p = c0 + tid;
+      const int tok = tid < nchunk ? select_emit(S, p, ids_h, app_h) : -1;
+      sel[tid] = tok;
+      if (sel_ids && tid < nchunk) sel_ids[(size_t)h * B + p] = tok;
+    }
+    __syncthreads();
+    bf16x8 kb[2][8];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      const int t = w * 64 + tile * 32 + col;
+      const int id = t < nchunk ? sel[t] : 0;
+      const u32x4* src = reinterpret_cast<const u32x4*>(Kh + (size_t)id * D);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) kb[tile][s] = __builtin_bit_cast(bf16x8, src[s]);
+    }
+    f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kb[0][s], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kb[1][s], acc1, 0, 0, 0);
+    }
+    // value rows: all 16 row steps in flight for G <= 2, two batches of 8 for more heads
+    constexpr int VB = G <= 2 ? 16 : 8;
+    Row8<uint16_t> vrow[VB];
+#pragma unroll
+    for (int r = 0; r < VB; ++r) {
+      const int t = w * 64 + r * 4 + grp;
+      const int id = t < nchunk ? sel[t] : 0;
+      vrow[r].load(Vh + (size_t)id * D);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * half + r;
+      if (g < G) {
+        const int t0 = w * 64 + col, t1 = t0 + 32;
+        sc[g][t0] = t0 < nchunk ? acc0[r] * qscale : -INFINITY;
+        sc[g][t1] = t1 < nchunk ? acc1[r] * qscale : -INFINITY;
+      }
+    }
+    __syncthreads();
+    float mnew[G], f[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float m = sc[g][w * 64 + lane];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      if (lane == 0) wred[w][g] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float m = m_run[g];
+#pragma unroll
+      for (int v = 0; v < NW; ++v) m = fmaxf(m, wred[v][g]);
+      mnew[g] = m;
+      f[g] = m_run[g] == -INFINITY ? 0.f : exp2f(m_run[g] - m);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float sv = sc[g][w * 64 + lane];
+      const float p = mnew[g] == -INFINITY ? 0.f : exp2f(sv - mnew[g]);
+      sc[g][w * 64 + lane] = p;
+      float l = p;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+      if (lane == 0) wred[w][g] = l;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float l = 0.f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) l += wred[v][g];
+      l_run[g] = l_run[g] * f[g] + l;
+      m_run[g] = mnew[g];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o[g][c] *= f[g];
+    }
+#pragma unroll
+    for (int b = 0; b < 16 / VB; ++b) {
+      if (b > 0) {
+#pragma unroll
+        for (int r = 0; r < VB; ++r) {
+          const int t = w * 64 + (b * VB + r) * 4 + grp;
+          const int id = t < nchunk ? sel[t] : 0;
+          vrow[r].load(Vh + (size_t)id * D);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < VB; ++r) {
+        const int t = w * 64 + (b * VB + r) * 4 + grp;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float p = sc[g][t];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o[g][c] = fmaf(p, vrow[r].at(c), o[g][c]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float v = o[g][c];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      o[g][c] = v;
+    }
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ored[w][g][8 * gl + c] = o[g][c];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * D; e += SEL_THREADS) {
+    const int g = e / D, j = e % D;
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) sum += ored[v][g][j];
+    out[((size_t)h * G + g) * D + j] = l_run[g] > 0.f ? sum / l_run[g] : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// a10 + a11 standalone: gather + split-K attention over given selections.
+// Grid (ceil(B / 64), heads); block = 4 waves over 64 selected tokens, 16
+// lanes per 128-channel row. Each block writes (m, l, o[d]) per query head
+// (log2 domain; q pre-scaled by scale * log2 e); a second kernel merges the
+// splits of each head in split order.
+template <typename KT, int G>
+__global__ __launch_bounds__(256) void decode_split_kernel(const KT* __restrict__ q, const KT* __restrict__ kc,
+                                                           const KT* __restrict__ vc, long long head_stride,
+                                                           const int32_t* __restrict__ sel_ids,
+                                                           const int32_t* __restrict__ sel_count, int B,
+                                                           float qscale, float* __restrict__ part) {
   __shared__ float ps[G][DEC_TOK];
   __shared__ float ored[4][G][D];
-  __shared__ int s_last;
+  __shared__ float sm[G], sl[G];
   const int h = blockIdx.y, sp = blockIdx.x, nsplit = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = lane >> 4, gl = lane & 15;
@@ -234,34 +701,27 @@ __global__ __launch_bounds__(256) void decode_kernel(const KT* __restrict__ q, c
   }
   const KT* Kh = kc + (size_t)h * head_stride + 8 * gl;
   const KT* Vh = vc + (size_t)h * head_stride + 8 * gl;
-  float kr[4][8], vr[4][8];
-  bool valid[4];
+  Row8<KT> kr[4], vr[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = w * 16 + r * 4 + grp;
-    valid[r] = t < ntok;
-    const int id = valid[r] ? sel_ids[(size_t)h * B + t0 + t] : 0;
-    load8(Kh + (size_t)id * D, kr[r]);
-    load8(Vh + (size_t)id * D, vr[r]);
+    const int id = t < ntok ? sel_ids[(size_t)h * B + t0 + t] : 0;
+    kr[r].load(Kh + (size_t)id * D);
+    vr[r].load(Vh + (size_t)id * D);
   }
-  // scores
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
+    const int t = w * 16 + r * 4 + grp;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float s = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) s = fmaf(qv[g][c], kr[r][c], s);
-      s += __shfl_xor(s, 8);
-      s += __shfl_xor(s, 4);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 1);
-      if (gl == 0) ps[g][w * 16 + r * 4 + grp] = valid[r] ? s : -INFINITY;
+      for (int c = 0; c < 8; ++c) s = fmaf(qv[g][c], kr[r].at(c), s);
+      s = row16_sum(s);
+      if (gl == 0) ps[g][t] = t < ntok ? s : -INFINITY;
     }
   }
   __syncthreads();
-  // per query head: split max, weights, sum (one wave per head)
-  __shared__ float sm[G], sl[G];
   for (int g = w; g < G; g += 4) {
     const float v = ps[g][lane];
     float m = v;
@@ -290,7 +750,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const KT* __restrict__ q, c
     for (int g = 0; g < G; ++g) {
       const float p = ps[g][t];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) o[g][c] = fmaf(p, vr[r][c], o[g][c]);
+      for (int c = 0; c < 8; ++c) o[g][c] = fmaf(p, vr[r].at(c), o[g][c]);
     }
   }
 #pragma unroll
@@ -318,30 +778,52 @@ __global__ __launch_bounds__(256) void decode_kernel(const KT* __restrict__ q, c
     pp[tid * (D + 2) + D] = sm[tid];
     pp[tid * (D + 2) + D + 1] = sl[tid];
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(counters + h, 1u) == (uint32_t)(nsplit - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
+
+// Merge of the splits of one head, in split order: M = max m_s,
+// out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s (zero without tokens).
+// The (m, l) pairs and the split weights go through LDS first so that every
+// thread's loads of the partial outputs are independent.
+constexpr int COMB_MAX = DEC_MAX_PAIRS;  // (split, query head) pairs held in LDS
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part, int nsplit, int G,
+                                                             float* __restrict__ out) {
+  __shared__ float wt[COMB_MAX];
+  __shared__ float Ls[8];  // query heads per KV head (at most 8)
+  const int h = blockIdx.x;
   const float* ph = part + (size_t)h * nsplit * G * (D + 2);
-  for (int e = tid; e < G * D; e += 256) {
-    const int g = e / D, j = e % D;
+  for (int e = threadIdx.x; e < nsplit * G; e += 256) wt[e] = ph[(size_t)e * (D + 2) + D];
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, __builtin_nontemporal_load(ph + ((size_t)s * G + g) * (D + 2) + D));
-    float Ls = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float* ps2 = ph + ((size_t)s * G + g) * (D + 2);
-        const float ms = __builtin_nontemporal_load(ps2 + D);
-        const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
-        Ls = fmaf(f, __builtin_nontemporal_load(ps2 + D + 1), Ls);
-        O = fmaf(f, __builtin_nontemporal_load(ps2 + j), O);
-      }
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, wt[s * G + g]);
+    float L = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = wt[s * G + g];
+      const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      L = fmaf(f, ph[((size_t)s * G + g) * (D + 2) + D + 1], L);
+      wt[s * G + g] = f;
     }
-    out[((size_t)h * G + g) * D + j] = Ls > 0.f ? O / Ls : 0.f;
+    Ls[g] = L;
   }
-  if (tid == 0) counters[h] = 0;
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * D; e += 256) {
+    const int g = e / D, j = e % D;
+    float O = 0.f;
+    int s = 0;
+    for (; s + 4 <= nsplit; s += 4) {
+      const float o0 = ph[((size_t)(s + 0) * G + g) * (D + 2) + j];
+      const float o1 = ph[((size_t)(s + 1) * G + g) * (D + 2) + j];
+      const float o2 = ph[((size_t)(s + 2) * G + g) * (D + 2) + j];
+      const float o3 = ph[((size_t)(s + 3) * G + g) * (D + 2) + j];
+      O = fmaf(wt[(s + 0) * G + g], o0, O);
+      O = fmaf(wt[(s + 1) * G + g], o1, O);
+      O = fmaf(wt[(s + 2) * G + g], o2, O);
+      O = fmaf(wt[(s + 3) * G + g], o3, O);
+    }
+    for (; s < nsplit; ++s) O = fmaf(wt[s * G + g], ph[((size_t)s * G + g) * (D + 2) + j], O);
+    out[((size_t)h * G + g) * D + j] = Ls[g] > 0.f ? O / Ls[g] : 0.f;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -387,41 +869,86 @@ hipError_t launch_select(int dtype, const void* q, int G, const float* cent, int
                          const int32_t* app_ids, long long cap, int B, int32_t* sel_ids, int32_t* sel_count,
                          hipStream_t st) {
   if (dtype == DT_BF16)
-    select_kernel<uint16_t><<<heads, 512, 0, st>>>((const uint16_t*)q, G, cent, C, sizes, offsets, token_ids,
-                                                   app_offsets, app_ids, cap, B, sel_ids, sel_count);
+    select_kernel<uint16_t><<<heads, SEL_THREADS, 0, st>>>((const uint16_t*)q, G, cent, C, sizes, offsets, token_ids,
+                                                           app_offsets, app_ids, cap, B, sel_ids, sel_count);
   else
-    select_kernel<float><<<heads, 512, 0, st>>>((const float*)q, G, cent, C, sizes, offsets, token_ids, app_offsets,
-                                                app_ids, cap, B, sel_ids, sel_count);
+    select_kernel<float><<<heads, SEL_THREADS, 0, st>>>((const float*)q, G, cent, C, sizes, offsets, token_ids,
+                                                        app_offsets, app_ids, cap, B, sel_ids, sel_count);
   return hipGetLastError();
 }
 
+template <typename KT, int G>
+static void launch_fused(const void* q, const float* cent, int heads, int C, const int32_t* sizes,
+                         const int32_t* offsets, const int32_t* token_ids, const int32_t* app_offsets,
+                         const int32_t* app_ids, long long cap, const void* kc, const void* vc, int B, float qscale,
+                         float* out, int32_t* sel_ids, int32_t* sel_count, hipStream_t st) {
+  if constexpr (sizeof(KT) == 2)
+    select_decode_bf16_kernel<G><<<heads, SEL_THREADS, 0, st>>>((const uint16_t*)q, cent, C, sizes, offsets,
+                                                                token_ids, app_offsets, app_ids, cap,
+                                                                (const uint16_t*)kc, (const uint16_t*)vc, B, qscale,
+                                                                out, sel_ids, sel_count);
+  else
+    select_decode_kernel<KT, G><<<heads, SEL_THREADS, 0, st>>>((const KT*)q, cent, C, sizes, offsets, token_ids,
+                                                               app_offsets, app_ids, cap, (const KT*)kc,
+                                                               (const KT*)vc, B, qscale, out, sel_ids, sel_count);
+}
+
 template <typename KT>
-static hipError_t decode_dispatch(const void* q, int G, const void* kc, const void* vc, long long head_stride,
-                                  int heads, const int32_t* sel_ids, const int32_t* sel_count, int B, float qscale,
-                                  float* out, float* part, uint32_t* counters, hipStream_t st) {
-  dim3 grid((B + DEC_TOK - 1) / DEC_TOK, heads);
-  const KT* qq = (const KT*)q;
-  const KT* kk = (const KT*)kc;
-  const KT* vv = (const KT*)vc;
+static hipError_t fused_dispatch(int G, const void* q, const float* cent, int heads, int C, const int32_t* sizes,
+                                 const int32_t* offsets, const int32_t* token_ids, const int32_t* app_offsets,
+                                 const int32_t* app_ids, long long cap, const void* kc, const void* vc, int B,
+                                 float qscale, float* out, int32_t* sel_ids, int32_t* sel_count, hipStream_t st) {
   switch (G) {
-    case 1: decode_kernel<KT, 1><<<grid, 256, 0, st>>>(qq, kk, vv, head_stride, sel_ids, sel_count, B, qscale, out, part, counters); break;
-    case 2: decode_kernel<KT, 2><<<grid, 256, 0, st>>>(qq, kk, vv, head_stride, sel_ids, sel_count, B, qscale, out, part, counters); break;
-    case 4: decode_kernel<KT, 4><<<grid, 256, 0, st>>>(qq, kk, vv, head_stride, sel_ids, sel_count, B, qscale, out, part, counters); break;
-    case 8: decode_kernel<KT, 8><<<grid, 256, 0, st>>>(qq, kk, vv, head_stride, sel_ids, sel_count, B, qscale, out, part, counters); break;
+    case 1: launch_fused<KT, 1>(q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc, vc, B, qscale, out, sel_ids, sel_count, st); break;
+    case 2: launch_fused<KT, 2>(q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc, vc, B, qscale, out, sel_ids, sel_count, st); break;
+    case 4: launch_fused<KT, 4>(q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc, vc, B, qscale, out, sel_ids, sel_count, st); break;
+    case 8: launch_fused<KT, 8>(q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc, vc, B, qscale, out, sel_ids, sel_count, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int dtype, const void* q, int G, const void* kc, const void* vc, long long head_stride,
-                         int heads, const int32_t* sel_ids, const int32_t* sel_count, int B, float scale, float* out,
-                         float* part, uint32_t* counters, hipStream_t st) {
+hipError_t launch_select_decode(int dtype, const void* q, int G, const float* cent, int heads, int C,
+                                const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids,
+                                const int32_t* app_offsets, const int32_t* app_ids, long long cap, const void* kc,
+                                const void* vc, int B, float scale, float* out, int32_t* sel_ids,
+                                int32_t* sel_count, hipStream_t st) {
   const float qscale = scale * 1.4426950408889634f;
   if (dtype == DT_BF16)
-    return decode_dispatch<uint16_t>(q, G, kc, vc, head_stride, heads, sel_ids, sel_count, B, qscale, out, part,
-                                     counters, st);
-  return decode_dispatch<float>(q, G, kc, vc, head_stride, heads, sel_ids, sel_count, B, qscale, out, part, counters,
-                                st);
+    return fused_dispatch<uint16_t>(G, q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc,
+                                    vc, B, qscale, out, sel_ids, sel_count, st);
+  return fused_dispatch<float>(G, q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc, vc, B,
+                               qscale, out, sel_ids, sel_count, st);
+}
+
+template <typename KT>
+static hipError_t decode_dispatch(const void* q, int G, const void* kc, const void* vc, long long head_stride,
+                                  int heads, const int32_t* sel_ids, const int32_t* sel_count, int B, float qscale,
+                                  float* out, float* part, hipStream_t st) {
+  dim3 grid((B + DEC_TOK - 1) / DEC_TOK, heads);
+  const KT* qq = (const KT*)q;
+  const KT* kk = (const KT*)kc;
+  const KT* vv = (const KT*)vc;
+  switch (G) {
+    case 1: decode_split_kernel<KT, 1><<<grid, 256, 0, st>>>(qq, kk, vv, head_stride, sel_ids, sel_count, B, qscale, part); break;
+    case 2: decode_split_kernel<KT, 2><<<grid, 256, 0, st>>>(qq, kk, vv, head_stride, sel_ids, sel_count, B, qscale, part); break;
+    case 4: decode_split_kernel<KT, 4><<<grid, 256, 0, st>>>(qq, kk, vv, head_stride, sel_ids, sel_count, B, qscale, part); break;
+    case 8: decode_split_kernel<KT, 8><<<grid, 256, 0, st>>>(qq, kk, vv, head_stride, sel_ids, sel_count, B, qscale, part); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_combine_kernel<<<heads, 256, 0, st>>>(part, (int)grid.x, G, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(int dtype, const void* q, int G, const void* kc, const void* vc, long long head_stride,
+                         int heads, const int32_t* sel_ids, const int32_t* sel_count, int B, float scale, float* out,
+                         float* part, hipStream_t st) {
+  const float qscale = scale * 1.4426950408889634f;
+  if (dtype == DT_BF16)
+    return decode_dispatch<uint16_t>(q, G, kc, vc, head_stride, heads, sel_ids, sel_count, B, qscale, out, part, st);
+  return decode_dispatch<float>(q, G, kc, vc, head_stride, heads, sel_ids, sel_count, B, qscale, out, part, st);
 }
 
 hipError_t launch_export_csr(int heads, int C, const int32_t* offsets, const int32_t* token_ids,

@@ -7,22 +7,23 @@ namespace kvc {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
-constexpr int DEC_TOK = 64;  // selected tokens per decode block (split)
+constexpr int DEC_TOK = 64;      // selected tokens per decode block (split)
+constexpr int DEC_MAX_PAIRS = 512;  // splits x query heads one merge block holds
 
 int csr_blocks(int L);
 
 hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t v, hipStream_t st);
 hipError_t launch_init_centroids(int dtype, const void* keys, long long head_stride, int heads, int L,
-                                 const int32_t* init_idx, int C, int cpad, float* cent, void* chat, int32_t* flags,
-                                 hipStream_t st);
+                                 const int32_t* init_idx, int C, int cpad, float* cent, float* cent_t, void* chat,
+                                 int32_t* flags, hipStream_t st);
 hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
                          int cpad, int32_t* labels, long long label_stride, int32_t* queue, uint32_t* qcount,
-                         float* top2, hipStream_t st);
+                         float* top2, hipEvent_t* events, hipStream_t st);
 hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, int L, int C, int32_t* hist,
                       int32_t* sizes, int32_t* offsets, int32_t* token_ids, long long ids_stride, hipStream_t st);
 hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cpad,
                          const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
-                         float* cent, void* chat, hipStream_t st);
+                         float* cent, float* cent_t, void* chat, hipStream_t st);
 
 hipError_t launch_append(int dtype, void* kc, void* vc, long long head_stride, int heads, const void* knew,
                          const void* vnew, int n_new, int n0, int n_build, const void* chat, int C, int cpad,
@@ -34,7 +35,12 @@ hipError_t launch_select(int dtype, const void* q, int G, const float* cent, int
                          hipStream_t st);
 hipError_t launch_decode(int dtype, const void* q, int G, const void* kc, const void* vc, long long head_stride,
                          int heads, const int32_t* sel_ids, const int32_t* sel_count, int B, float scale, float* out,
-                         float* part, uint32_t* counters, hipStream_t st);
+                         float* part, hipStream_t st);
+hipError_t launch_select_decode(int dtype, const void* q, int G, const float* cent, int heads, int C,
+                                const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids,
+                                const int32_t* app_offsets, const int32_t* app_ids, long long cap, const void* kc,
+                                const void* vc, int B, float scale, float* out, int32_t* sel_ids,
+                                int32_t* sel_count, hipStream_t st);
 hipError_t launch_export_csr(int heads, int C, const int32_t* offsets, const int32_t* token_ids,
                              const int32_t* app_offsets, const int32_t* app_ids, long long cap, int32_t* out_offsets,
                              int32_t* out_ids, hipStream_t st);

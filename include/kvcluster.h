@@ -90,6 +90,8 @@ typedef struct kvc_index {
   int32_t* app_offsets;   /* [heads, C+1] prefix sums of the appended part */
   int32_t* app_ids;       /* [heads, capacity] appended tokens, cluster-major, ascending within */
   int32_t* dev_flags;     /* [1] error bits set by kernels (bit 0: an init index out of range) */
+  float* centroids_t;     /* [heads, d/4, C, 4] fp32: the same centroids with 4-channel chunks
+                             cluster-minor, written by the build and read by selection */
 } kvc_index;
 
 /* Rows of centroids_op per head: C rounded up to the matrix-core tile (32). */
@@ -119,6 +121,16 @@ size_t kv_cluster_build_workspace_bytes(int heads, int L, int C, int iters);
  */
 int kv_cluster_build(kvc_index* idx, const void* keys, int L, int iters, const int32_t* init_idx, void* ws,
                      size_t ws_bytes, void* stream);
+
+/*
+ * kv_cluster_build with timing: assign_events (host array of 2*iters
+ * hipEvent_t handles created by the caller, or NULL) receives, for iteration
+ * t, events recorded on `stream` right before and right after the launch of
+ * that iteration's assignment kernel (the matrix-core pass for bf16 keys, the
+ * fp64 pass for fp32 keys). Otherwise identical to kv_cluster_build.
+ */
+int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, const int32_t* init_idx, void* ws,
+                           size_t ws_bytes, void* const* assign_events, void* stream);
 
 /*
  * Decode-time append of n_new tokens per head (rows idx->n_tokens ..
@@ -153,20 +165,33 @@ int kv_cluster_select(const kvc_index* idx, const void* q, int q_heads, int B, i
 size_t kv_sparse_decode_workspace_bytes(int heads, int q_heads, int d, int B);
 
 /*
- * Single-query attention over the recalled tokens (II.A; III.A). For query
- * head g (KV head h = g / G):
+ * Single-query attention over the recalled tokens (II.A; III.A); requires
+ * ceil(B / 64) * G <= 512 (B <= 4096 at G = 8). For query head g (KV head
+ * h = g / G):
  *   out[g] = sum_i softmax_i(scale * q_g . K[h, i]) V[h, i]
  * over i in sel_ids[h*B .. h*B + sel_count[h]) (fp32 accumulation, fp32
  * output [q_heads, d]; zero when sel_count[h] is 0). k_cache and v_cache are
  * [heads, capacity, d] in `dtype`, q is [q_heads, d] in `dtype`. The selected
- * positions must lie in [0, capacity). The workspace must hold
- * kv_sparse_decode_workspace_bytes(heads, q_heads, d, B) bytes and must be
- * zero-filled once before its first use; every call leaves it reusable.
- * Calls that share a workspace must not run concurrently.
+ * positions must lie in [0, capacity). The selected set is split into blocks
+ * of 64 tokens whose partial results (running max, sum, output) go to the
+ * workspace (kv_sparse_decode_workspace_bytes(heads, q_heads, d, B) bytes,
+ * contents need not be initialised) and are merged by a second kernel.
  */
 int kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
                      int capacity, int d, const int32_t* sel_ids, const int32_t* sel_count, int B, float scale,
                      float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kv_cluster_select followed by kv_sparse_decode in one kernel (one block per
+ * KV head): the same selection and the same attention, without the selected
+ * ids leaving the chip. k_cache and v_cache are [heads, idx->capacity, d] in
+ * idx->dtype; q is [q_heads, d]; out is fp32 [q_heads, d]. sel_ids [heads, B]
+ * and sel_count [heads] are optional (NULL) copies of the selection.
+ * Requires G = q_heads / heads in {1, 2, 4, 8}. No workspace.
+ */
+int kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, const void* k_cache,
+                             const void* v_cache, int B, float scale, float* out, int32_t* sel_ids,
+                             int32_t* sel_count, void* stream);
 
 /*
  * The canonical index of every head (built and appended tokens merged):

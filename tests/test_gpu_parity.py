@@ -149,8 +149,15 @@ def test_build_select_decode_end_to_end(case):
         assert np.array_equal(to_np(sel), osel), B
         od = oracle.decode(q, w.G, K, V, to_np(sel), to_np(cnt), scale)
         err = np.abs(to_np(out) - od).max()
-        say(f"  B={B}: count {to_np(cnt).tolist()[:4]}, decode max abs err {err:.3e}")
-        assert err <= 2e-3
+        # the fused kernel: same selection, same attention
+        fsel = torch.full((H, B), -7, dtype=torch.int32, device="cuda")
+        fcnt = torch.empty(H, dtype=torch.int32, device="cuda")
+        fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel, sel_count=fcnt)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(fcnt), ocnt) and np.array_equal(to_np(fsel), osel), B
+        ferr = np.abs(to_np(fout) - od).max()
+        say(f"  B={B}: count {to_np(cnt).tolist()[:4]}, decode max abs err {err:.3e}, fused {ferr:.3e}")
+        assert err <= 2e-3 and ferr <= 2e-3
     del ws
 
 
@@ -191,6 +198,9 @@ def test_append_then_select_decode():
         assert np.array_equal(to_np(sel), osel) and np.array_equal(to_np(cnt), ocnt)
         od = oracle.decode(q, w.G, K, V, osel, ocnt, scale)
         assert np.abs(to_np(out) - od).max() <= 2e-3
+        fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, w.B, scale)
+        torch.cuda.synchronize()
+        assert np.abs(to_np(fout) - od).max() <= 2e-3
     off, ids = kvc.export_csr(idx)
     assert np.array_equal(to_np(off), oi.offsets)
     assert np.array_equal(to_np(ids)[:, :n], oi.token_ids[:, :n])
