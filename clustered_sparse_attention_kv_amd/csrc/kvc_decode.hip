@@ -161,6 +161,7 @@ __device__ __forceinline__ void bitonic_stage(Sh& S, unsigned long long& key, in
   if constexpr (STRIDE > 1) bitonic_stage<SIZE, STRIDE / 2>(S, key, id, tid);
 }
 
+
 template <int SIZE, int N, typename Sh>
 __device__ __forceinline__ void bitonic_sort(Sh& S, unsigned long long& key, int& id, int tid) {
   bitonic_stage<SIZE, SIZE / 2>(S, key, id, tid);
@@ -190,7 +191,7 @@ __device__ __forceinline__ void select_phase(SelShared& S, const QT* __restrict_
   }
   __syncthreads();
   unsigned long long key = 0;
-  int id = 0x7FFFFFFF;
+  int id = C + tid;  // padding entries: worst key, distinct ids past the clusters
   if (tid < C) {
     const f32x4* ct = reinterpret_cast<const f32x4*>(cent_t + (size_t)h * C * D) + tid;
     double s = 0.0;
@@ -272,6 +273,32 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const QT* __restric
   for (int p = tid; p < B; p += SEL_THREADS)
     sel_ids[(size_t)h * B + p] = p < cnt ? select_emit(S, p, ids_h, app_h) : -1;
   if (tid == 0) sel_count[h] = cnt;
+}
+
+// Max / sum over the whole wave, result in every lane: row reductions by DPP,
+// then row broadcasts (rows 0-1, then 0-3 into the upper half), and a read of
+// lane 63.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xA, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xC, 0xF, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Sum over each row of 16 lanes, left in every lane of the row: quad swaps,
@@ -487,51 +514,73 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// a7-a11 fused, bf16: as above, with the query-key products of each chunk on
-// the matrix cores. Per wave and chunk, 64 selected keys form the B operand
-// of two v_mfma_f32_32x32x16_bf16 tiles (lane = key column, 64 channels of
-// its row in eight 16-byte pieces, channel order 64 * half + 8 * step + i for
-// both operands), the A operand holds the G query heads in its first rows
-// (bf16 inputs, fp32 accumulation; the scale multiplies the fp32 result), and
-// score (g, key) lands in lane key % 32 + 32 * (g / 4), register g % 4. The
-// value rows are gathered in the 16-lanes-per-row layout and weighted in fp32
-// on the vector units.
+// a7-a11 fused, bf16. After the selection phase the selected ids (up to 2048
+// at a time) are staged in LDS, and each wave then runs on its own over
+// 64-token slices (wave w takes slices w, w + 8, ...), keeping an online
+// softmax per query head (running max, sum and partial output); the waves'
+// states are merged once at the end. Per slice:
+//  - query-key products on the matrix cores: the 64 keys form the A operand
+//    of four v_mfma_f32_16x16x32_bf16 tiles of 16 rows (lane = row lane % 16,
+//    16-byte piece 32 s + 8 (lane / 16) of the row, so one load instruction
+//    reads 64 contiguous bytes of 16 rows); the B operand holds the G query
+//    heads in its first columns; bf16 inputs, fp32 accumulation, and the
+//    scale (times log2 e) multiplies the fp32 result;
+//  - the scores go through wave-private LDS to a lane-per-token layout for
+//    the max and sum (DPP reductions), and back as weights;
+//  - the value rows are gathered and weighted in fp32 on the vector units.
+// Two blocks share each KV head: both select and score all keys, and block
+// `part` gathers and weights channels [64 part, 64 part + 64) of the values
+// (8 lanes per 64-channel half row), writing those output channels. The two
+// blocks of a head get block indices 8 apart, so the round-robin dispatch
+// over the 8 XCDs places them on one XCD and its L2 serves the second read of
+// the keys and centroids; results do not depend on the placement.
+constexpr int DEC_PARTS = 2;
 template <int G>
 __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ cent_t, int C, const int32_t* __restrict__ sizes,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ token_ids,
     const int32_t* __restrict__ app_offsets, const int32_t* __restrict__ app_ids, long long cap,
-    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int B, float qscale, float* __restrict__ out,
-    int32_t* __restrict__ sel_ids, int32_t* __restrict__ sel_count) {
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int heads, int B, float qscale,
+    float* __restrict__ out, int32_t* __restrict__ sel_ids, int32_t* __restrict__ sel_count) {
   static_assert(G <= 8, "at most 8 query heads per KV head");
   constexpr int NW = SEL_THREADS / WAVE;
+  constexpr int EMIT = 2048;                 // selected ids staged per pass
+  constexpr int HC = D / DEC_PARTS;          // value channels per block
+  constexpr int RPS = WAVE / (HC / 8);       // value rows per load instruction (8 with 64 channels)
+  constexpr int VR = 64 / RPS;               // value rows per lane per slice
   __shared__ SelShared S;
-  __shared__ int sel[SEL_THREADS];
-  __shared__ float sc[G][SEL_THREADS];
-  __shared__ float wred[NW][G];
-  __shared__ float ored[NW][G][D];
-  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int half = lane >> 5, col = lane & 31;
-  const int grp = lane >> 4, gl = lane & 15;
+  __shared__ int sel[EMIT];
+  __shared__ float pw[NW][G][64];            // wave-private: scores, then weights, of the current slice
+  __shared__ float ored[NW][G][HC];
+  __shared__ float wm[NW][G], wl[NW][G];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int within = blockIdx.x % (8 * DEC_PARTS);
+  const int part = within / 8;
+  const int h = blockIdx.x / (8 * DEC_PARTS) * 8 + within % 8;
+  if (h >= heads) return;  // whole block: the grid covers heads rounded up to 8
+  const int vgrp = lane / (HC / 8), vgl = lane % (HC / 8);  // value row in the load, 8-channel chunk
+  const int j16 = lane & 15, kb4 = lane >> 4;
   select_phase(S, q, G, cent_t, C, sizes, offsets, app_offsets, h);
   const int cnt = S.total < B ? S.total : B;
-  if (sel_count && tid == 0) sel_count[h] = cnt;
-  if (sel_ids)
+  const bool writer = part == 0;  // one block per head publishes the selection
+  if (writer && sel_count && tid == 0) sel_count[h] = cnt;
+  if (writer && sel_ids)
     for (int p = cnt + tid; p < B; p += SEL_THREADS) sel_ids[(size_t)h * B + p] = -1;
   const int32_t* ids_h = token_ids + (size_t)h * cap;
   const int32_t* app_h = app_ids + (size_t)h * cap;
-  const uint16_t* Kh = kc + (size_t)h * cap * D + 64 * half;
-  const uint16_t* Vh = vc + (size_t)h * cap * D + 8 * gl;
+  const uint16_t* Kh = kc + (size_t)h * cap * D + 8 * kb4;
+  const uint16_t* Vh = vc + (size_t)h * cap * D + HC * part + 8 * vgl;
 
-  bf16x8 qa[8];
+  // queries as the B operand: column = query head (lane % 16 < G), k-step s
+  // holds channels 32 s + 8 (lane / 16) .. + 7
+  bf16x8 qb[4];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
+  for (int s = 0; s < 4; ++s) {
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (col < G) v = *reinterpret_cast<const u32x4*>(q + ((size_t)h * G + col) * D + 64 * half + 8 * s);
-    qa[s] = __builtin_bit_cast(bf16x8, v);
+    if (j16 < G) v = *reinterpret_cast<const u32x4*>(q + ((size_t)h * G + j16) * D + 32 * s + 8 * kb4);
+    qb[s] = __builtin_bit_cast(bf16x8, v);
   }
-  float o[G][8];
-  float m_run[G], l_run[G];
+  float o[G][8], m_run[G], l_run[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m_run[g] = -INFINITY;
@@ -540,133 +589,123 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     for (int c = 0; c < 8; ++c) o[g][c] = 0.f;
   }
 
-  for (int c0 = 0; c0 < cnt; c0 += SEL_THREADS) {
-    const int nchunk = cnt - c0 < SEL_THREADS ? cnt - c0 : SEL_THREADS;
-    {
-      const int p = c0 + tid;
-      const int tok = tid < nchunk ? select_emit(S, p, ids_h, app_h) : -1;
-      sel[tid] = tok;
-      if (sel_ids && tid < nchunk) sel_ids[(size_t)h * B + p] = tok;
+  for (int base = 0; base < cnt; base += EMIT) {
+    const int nb = cnt - base < EMIT ? cnt - base : EMIT;
+    if (base > 0) __syncthreads();  // every wave is done with the previous ids
+    for (int p = tid; p < nb; p += SEL_THREADS) {
+      const int tok = select_emit(S, base + p, ids_h, app_h);
+      sel[p] = tok;
+      if (writer && sel_ids) sel_ids[(size_t)h * B + base + p] = tok;
     }
     __syncthreads();
-    bf16x8 kb[2][8];
+    for (int t0 = w * 64; t0 < nb; t0 += NW * 64) {
+      const int n64 = nb - t0 < 64 ? nb - t0 : 64;
+      bf16x8 ka[4][4];
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      const int t = w * 64 + tile * 32 + col;
-      const int id = t < nchunk ? sel[t] : 0;
-      const u32x4* src = reinterpret_cast<const u32x4*>(Kh + (size_t)id * D);
+      for (int T = 0; T < 4; ++T) {
+        const int t = T * 16 + j16;
+        const int id = t < n64 ? sel[t0 + t] : 0;
+        const uint16_t* src = Kh + (size_t)id * D;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) kb[tile][s] = __builtin_bit_cast(bf16x8, src[s]);
-    }
-    f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kb[0][s], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kb[1][s], acc1, 0, 0, 0);
-    }
-    // value rows: all 16 row steps in flight for G <= 2, two batches of 8 for more heads
-    constexpr int VB = G <= 2 ? 16 : 8;
-    Row8<uint16_t> vrow[VB];
-#pragma unroll
-    for (int r = 0; r < VB; ++r) {
-      const int t = w * 64 + r * 4 + grp;
-      const int id = t < nchunk ? sel[t] : 0;
-      vrow[r].load(Vh + (size_t)id * D);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int g = 4 * half + r;
-      if (g < G) {
-        const int t0 = w * 64 + col, t1 = t0 + 32;
-        sc[g][t0] = t0 < nchunk ? acc0[r] * qscale : -INFINITY;
-        sc[g][t1] = t1 < nchunk ? acc1[r] * qscale : -INFINITY;
+        for (int s = 0; s < 4; ++s)
+          ka[T][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 32 * s));
       }
-    }
-    __syncthreads();
-    float mnew[G], f[G];
+      Row8<uint16_t> vrow[VR];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float m = sc[g][w * 64 + lane];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      if (lane == 0) wred[w][g] = m;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float m = m_run[g];
-#pragma unroll
-      for (int v = 0; v < NW; ++v) m = fmaxf(m, wred[v][g]);
-      mnew[g] = m;
-      f[g] = m_run[g] == -INFINITY ? 0.f : exp2f(m_run[g] - m);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float sv = sc[g][w * 64 + lane];
-      const float p = mnew[g] == -INFINITY ? 0.f : exp2f(sv - mnew[g]);
-      sc[g][w * 64 + lane] = p;
-      float l = p;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
-      if (lane == 0) wred[w][g] = l;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float l = 0.f;
-#pragma unroll
-      for (int v = 0; v < NW; ++v) l += wred[v][g];
-      l_run[g] = l_run[g] * f[g] + l;
-      m_run[g] = mnew[g];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) o[g][c] *= f[g];
-    }
-#pragma unroll
-    for (int b = 0; b < 16 / VB; ++b) {
-      if (b > 0) {
-#pragma unroll
-        for (int r = 0; r < VB; ++r) {
-          const int t = w * 64 + (b * VB + r) * 4 + grp;
-          const int id = t < nchunk ? sel[t] : 0;
-          vrow[r].load(Vh + (size_t)id * D);
-        }
+      for (int r = 0; r < VR; ++r) {
+        const int t = r * RPS + vgrp;
+        const int id = t < n64 ? sel[t0 + t] : 0;
+        vrow[r].load(Vh + (size_t)id * D);
       }
+      f32x4 acc[4] = {};
 #pragma unroll
-      for (int r = 0; r < VB; ++r) {
-        const int t = w * 64 + (b * VB + r) * 4 + grp;
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[T][s], qb[s], acc[T], 0, 0, 0);
+      // score of (row 16 T + 4 (lane / 16) + r, query head lane % 16) -> pw[w][g][row]
+      if (j16 < G) {
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = T * 16 + 4 * kb4 + r;
+            pw[w][j16][t] = t < n64 ? acc[T][r] * qscale : -INFINITY;
+          }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float sv = pw[w][g][lane];
+        const float mnew = fmaxf(m_run[g], wave_max(sv));
+        const float f = m_run[g] == -INFINITY ? 0.f : exp2f(m_run[g] - mnew);
+        const float pv = mnew == -INFINITY ? 0.f : exp2f(sv - mnew);
+        pw[w][g][lane] = pv;
+        l_run[g] = l_run[g] * f + wave_sum(pv);
+        m_run[g] = mnew;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[g][c] *= f;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int r = 0; r < VR; ++r) {
+        const int t = r * RPS + vgrp;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float p = sc[g][t];
+          const float pv = pw[w][g][t];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) o[g][c] = fmaf(p, vrow[r].at(c), o[g][c]);
+          for (int c = 0; c < 8; ++c) o[g][c] = fmaf(pv, vrow[r].at(c), o[g][c]);
         }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __syncthreads();
   }
+  // merge: the row groups of each wave (lanes 8 apart share channels), then the 8 waves
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float v = o[g][c];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
+#pragma unroll
+      for (int m = HC / 8; m < WAVE; m <<= 1) v += __shfl_xor(v, m);
       o[g][c] = v;
     }
-  if (grp == 0) {
+  if (vgrp == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) ored[w][g][8 * gl + c] = o[g][c];
+      for (int c = 0; c < 8; ++c) ored[w][g][8 * vgl + c] = o[g][c];
+  }
+  if (lane < G) {
+    // every lane holds the same running state; lane g publishes head g's
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (g == lane) {
+        wm[w][g] = m_run[g];
+        wl[w][g] = l_run[g];
+      }
   }
   __syncthreads();
-  for (int e = tid; e < G * D; e += SEL_THREADS) {
-    const int g = e / D, j = e % D;
-    float sum = 0.f;
+  for (int e = tid; e < G * HC; e += SEL_THREADS) {
+    const int g = e / HC, j = e % HC;
+    float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) sum += ored[v][g][j];
-    out[((size_t)h * G + g) * D + j] = l_run[g] > 0.f ? sum / l_run[g] : 0.f;
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, wm[v][g]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        const float f = wm[v][g] == -INFINITY ? 0.f : exp2f(wm[v][g] - M);
+        L = fmaf(f, wl[v][g], L);
+        O = fmaf(f, ored[v][g][j], O);
+      }
+    }
+    out[((size_t)h * G + g) * D + HC * part + j] = L > 0.f ? O / L : 0.f;
   }
 }
 
@@ -883,10 +922,9 @@ static void launch_fused(const void* q, const float* cent, int heads, int C, con
                          const int32_t* app_ids, long long cap, const void* kc, const void* vc, int B, float qscale,
                          float* out, int32_t* sel_ids, int32_t* sel_count, hipStream_t st) {
   if constexpr (sizeof(KT) == 2)
-    select_decode_bf16_kernel<G><<<heads, SEL_THREADS, 0, st>>>((const uint16_t*)q, cent, C, sizes, offsets,
-                                                                token_ids, app_offsets, app_ids, cap,
-                                                                (const uint16_t*)kc, (const uint16_t*)vc, B, qscale,
-                                                                out, sel_ids, sel_count);
+    select_decode_bf16_kernel<G><<<(heads + 7) / 8 * 8 * DEC_PARTS, SEL_THREADS, 0, st>>>(
+        (const uint16_t*)q, cent, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, (const uint16_t*)kc,
+        (const uint16_t*)vc, heads, B, qscale, out, sel_ids, sel_count);
   else
     select_decode_kernel<KT, G><<<heads, SEL_THREADS, 0, st>>>((const KT*)q, cent, C, sizes, offsets, token_ids,
                                                                app_offsets, app_ids, cap, (const KT*)kc,

@@ -1,0 +1,117 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects invalid arguments with the documented status codes
+before anything is enqueued (every call here fails validation, so no GPU is
+touched)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvcluster.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, CAPACITY = 0, 1, 2, 3, 4
+FAKE = 0x10000  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def kvc():
+    import clustered_sparse_attention_kv_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        m.build_lib()
+    m.lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(kv_\w+)\(", text, re.M)))
+
+
+def test_every_declared_function_is_exported(kvc):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(kvc.lib(), n), n
+
+
+def make_index(kvc, heads=4, d=128, Cn=16, cap=256, dtype=1, n_build=0, n_tokens=0, null=None):
+    ptrs = [FAKE] * 10
+    s = kvc._Index(heads, d, Cn, cap, dtype, n_build, n_tokens, 0, *ptrs)
+    if null:
+        setattr(s, null, None)
+    return s
+
+
+def test_status_strings_and_sizes(kvc):
+    L = kvc.lib()
+    for code in range(6):
+        assert L.kv_cluster_status_string(code)
+    assert L.kv_cluster_status_string(99) == b"unknown status"
+    assert [L.kv_cluster_cpad(c) for c in (1, 32, 33, 400, 512)] == [32, 32, 64, 416, 512]
+    a = L.kv_cluster_build_workspace_bytes(128, 32768, 400, 10)
+    b = L.kv_cluster_build_workspace_bytes(128, 32768, 400, 20)
+    assert 0 < a < b and a % 256 == 0
+    assert L.kv_cluster_build_workspace_bytes(0, 10, 1, 1) == 0
+    assert L.kv_sparse_decode_workspace_bytes(128, 512, 128, 1024) >= 128 * 16 * 4 * 130 * 4
+
+
+def test_build_rejects(kvc):
+    L = kvc.lib()
+    p = C.c_void_p(FAKE)
+
+    def build(idx, Lk=200, iters=10, ws_bytes=1 << 40, keys=p, init=p):
+        return L.kv_cluster_build(C.byref(idx) if idx is not None else None, keys, Lk, iters, init, p, ws_bytes, None)
+
+    assert build(None) == INVALID
+    assert build(make_index(kvc), keys=None) == INVALID
+    assert build(make_index(kvc), init=None) == INVALID
+    for field in ("centroids", "centroids_op", "labels", "sizes", "offsets", "token_ids", "app_offsets", "app_ids",
+                  "dev_flags", "centroids_t"):
+        assert build(make_index(kvc, null=field)) == INVALID, field
+    assert build(make_index(kvc, d=64)) == UNSUPPORTED
+    assert build(make_index(kvc, Cn=600)) == UNSUPPORTED
+    assert build(make_index(kvc, dtype=7)) == INVALID
+    assert build(make_index(kvc, Cn=16), Lk=15) == INVALID          # L < C
+    assert build(make_index(kvc, cap=256), Lk=257) == INVALID       # L > capacity
+    assert build(make_index(kvc), iters=0) == INVALID
+    need = L.kv_cluster_build_workspace_bytes(4, 200, 16, 10)
+    assert build(make_index(kvc), ws_bytes=need - 1) == WORKSPACE
+
+
+def test_append_select_decode_reject(kvc):
+    L = kvc.lib()
+    p = C.c_void_p(FAKE)
+    full = make_index(kvc, cap=256, n_build=200, n_tokens=250)
+    assert L.kv_cluster_append(C.byref(full), p, p, p, p, 7, None) == CAPACITY
+    assert L.kv_cluster_append(C.byref(full), p, p, p, p, 0, None) == INVALID
+    assert L.kv_cluster_append(C.byref(make_index(kvc)), p, p, p, p, 1, None) == INVALID  # never built
+    built = make_index(kvc, heads=4, n_build=200, n_tokens=200)
+    assert L.kv_cluster_select(C.byref(built), p, 6, 64, p, p, None) == INVALID       # 6 % 4 != 0
+    assert L.kv_cluster_select(C.byref(built), p, 4 * 9, 64, p, p, None) == UNSUPPORTED  # G = 9
+    assert L.kv_cluster_select(C.byref(built), p, 16, 0, p, p, None) == INVALID
+    assert L.kv_cluster_select(C.byref(make_index(kvc)), p, 16, 64, p, p, None) == INVALID
+    f = C.c_float(0.1)
+    assert L.kv_cluster_select_decode(C.byref(built), p, 12, p, p, 64, f, p, None, None, None) == UNSUPPORTED
+    assert L.kv_cluster_select_decode(C.byref(built), p, 16, None, p, 64, f, p, None, None, None) == INVALID
+    ws = L.kv_sparse_decode_workspace_bytes(4, 16, 128, 64)
+    dec = lambda **k: L.kv_sparse_decode(p, k.get("qh", 16), p, p, k.get("dt", 1), 4, 256, k.get("d", 128), p, p,
+                                         k.get("B", 64), f, p, p, k.get("ws", ws), None)
+    assert dec(d=64) == UNSUPPORTED
+    assert dec(qh=12) == UNSUPPORTED
+    assert dec(qh=10) == INVALID
+    assert dec(dt=3) == INVALID
+    assert dec(ws=ws - 1) == WORKSPACE
+    assert dec(B=0) == INVALID
+    assert dec(qh=32, B=4096 + 64, ws=1 << 40) == UNSUPPORTED   # 65 splits x 8 heads > 512 pairs
+    assert L.kv_cluster_export_csr(C.byref(built), None, p, None) == INVALID
+
+
+def test_binding_fails_loudly_without_library(kvc, monkeypatch):
+    """The product path never falls back to anything else: no library, no call."""
+    import clustered_sparse_attention_kv_amd as m
+    monkeypatch.setattr(m, "_lib", None)
+    monkeypatch.setattr(m, "LIB_PATH", "/nonexistent/libkvcluster.so")
+    with pytest.raises(RuntimeError):
+        m.lib()

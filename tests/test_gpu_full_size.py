@@ -1,0 +1,155 @@
+"""Parity at the full sizes of the synthetic workloads, in the configuration
+the benchmark times (kv_cluster_build, then kv_cluster_select_decode per
+decode step; the split select + decode path is checked beside it).
+
+The GPU runs every head. The oracle re-runs the k-means on sampled heads
+(whole heads, every key); the cluster index, selection and decode are checked
+for every head given the GPU's own clustering (integer results bit-exact,
+attention within 2e-3)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _helpers import queries, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+kvc = pytest.importorskip("clustered_sparse_attention_kv_amd")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gen(w, layer=0):
+    base = synth.config_seed(w.config, layer)
+    K, _, means = synth.mixture_keys(base, w.heads, w.capacity, w.d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype,
+                                     want_means=(w.query == "mixture"))
+    V = synth.values(base, w.heads, w.capacity, w.d, w.dtype)
+    init = synth.init_idx(base, w.heads, w.L, w.C)
+    return base, K, V, init, means
+
+
+def check_build(w, K, init, idx, sample):
+    gl = to_np(idx.labels)[:, :w.L]
+    gc = to_np(idx.centroids)
+    opt = oracle.BF16 if w.dtype == synth.BF16 else oracle.F32
+    # index: bit-exact given the GPU's labels, every head
+    sizes, offsets, ids = to_np(idx.sizes), to_np(idx.offsets), to_np(idx.token_ids)[:, :w.L]
+    for h in range(w.heads):
+        s, o, i = oracle.csr(gl[h], w.C)
+        assert np.array_equal(sizes[h], s) and np.array_equal(offsets[h], o) and np.array_equal(ids[h], i), h
+    # k-means on sampled heads, whole heads
+    Ks = np.ascontiguousarray(K[sample, :w.L])
+    ref = oracle.build(Ks, w.C, w.iters, np.ascontiguousarray(init[sample]))
+    agree = (gl[sample] == ref["labels"]).mean()
+    worst = 0.0
+    for a, h in enumerate(sample):
+        for k in range(w.C):
+            if np.array_equal(np.flatnonzero(gl[h] == k), np.flatnonzero(ref["labels"][a] == k)):
+                nrm = max(np.linalg.norm(ref["c"][a, k]), 1e-30)
+                worst = max(worst, np.linalg.norm(gc[h, k] - ref["c"][a, k]) / nrm)
+        assert np.array_equal(to_np(idx.centroids_op)[h, :w.C], oracle.normalize(gc[h], opt))
+    say(f"  heads {sample}: label agreement {agree:.6f}, centroid rel err {worst:.2e}")
+    assert agree >= 0.999 and worst <= 1e-3
+
+
+def check_step(w, idx, K, V, Kd, Vd, q, B, scale, c=None, sizes=None, offsets=None, token_ids=None, split=True):
+    H = w.heads
+    qd = to_dev(q)
+    fsel = torch.empty(H, B, dtype=torch.int32, device="cuda")
+    fcnt = torch.empty(H, dtype=torch.int32, device="cuda")
+    fout = kvc.select_decode(idx, qd, Kd, Vd, B, scale, sel_ids=fsel, sel_count=fcnt)
+    if split:
+        sel, cnt = kvc.select(idx, qd, B)
+        out = kvc.sparse_decode(qd, Kd, Vd, sel, cnt, scale)
+    torch.cuda.synchronize()
+    c = to_np(idx.centroids) if c is None else c
+    sizes = to_np(idx.sizes) if sizes is None else sizes
+    offsets = to_np(idx.offsets) if offsets is None else offsets
+    token_ids = to_np(idx.token_ids) if token_ids is None else token_ids
+    osel, ocnt, _, _ = oracle.select(q, w.G, c, sizes, offsets, token_ids, B)
+    assert np.array_equal(to_np(fcnt), ocnt) and np.array_equal(to_np(fsel), osel)
+    od = oracle.decode(q, w.G, K, V, osel, ocnt, scale)
+    ferr = float(np.abs(to_np(fout) - od).max())
+    err = float(np.abs(to_np(out) - od).max()) if split else 0.0
+    if split:
+        assert np.array_equal(to_np(sel), osel) and np.array_equal(to_np(cnt), ocnt)
+    assert ferr <= 2e-3 and err <= 2e-3
+    return ferr, err
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_full_size_build_select_decode(cfg):
+    w = synth.workload(cfg)
+    say(f"[full size] {w.name}: {w.heads} heads x {w.L} keys, C={w.C}, B={w.B}")
+    base, K, V, init, means = gen(w)
+    idx = kvc.ClusterIndex(w.heads, w.C, w.capacity, torch.bfloat16)
+    Kd, Vd = to_dev(K), to_dev(V)
+    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    torch.cuda.synchronize()
+    assert int(to_np(idx.dev_flags)[0]) == 0
+    check_build(w, K, init, idx, [0, w.heads - 1])
+    scale = 1.0 / math.sqrt(w.d)
+    for step in (0, 1, w.steps - 1):
+        q = queries(w, base, step, K, w.L, means)
+        ferr, err = check_step(w, idx, K, V, Kd, Vd, q, w.B, scale)
+        say(f"  step {step}: decode max abs err fused {ferr:.2e}, split {err:.2e}")
+
+
+def test_full_size_append_workload():
+    w = synth.workload(3)
+    say(f"[full size] {w.name}: {w.heads} heads x {w.L} keys + {w.steps} appended, C={w.C}, B={w.B}")
+    base, K, V, init, means = gen(w)
+    Kp, Vp = K.copy(), V.copy()
+    Kp[:, w.L:] = 0
+    Vp[:, w.L:] = 0
+    idx = kvc.ClusterIndex(w.heads, w.C, w.capacity, torch.bfloat16)
+    Kd, Vd = to_dev(Kp), to_dev(Vp)
+    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    torch.cuda.synchronize()
+    check_build(w, K, init, idx, [5])
+    built = dict(labels=to_np(idx.labels)[:, :w.L], sizes=to_np(idx.sizes), offsets=to_np(idx.offsets),
+                 token_ids=to_np(idx.token_ids)[:, :w.L], c=to_np(idx.centroids),
+                 chat=to_np(idx.centroids_op)[:, :w.C])
+    oi = oracle.Index(built, w.capacity)
+    scale = 1.0 / math.sqrt(w.d)
+    for s in range(w.steps):
+        n = w.L + s
+        kvc.append(idx, Kd, Vd, to_dev(np.ascontiguousarray(K[:, n])), to_dev(np.ascontiguousarray(V[:, n])))
+        oi.append(np.ascontiguousarray(K[:, n]))
+        if s % 64 == 0 or s == w.steps - 1:
+            q = queries(w, base, s, K, n + 1, means)
+            assert np.array_equal(to_np(idx.labels)[:, :n + 1], oi.labels[:, :n + 1])
+            off, ids = kvc.export_csr(idx)
+            assert np.array_equal(to_np(off), oi.offsets) and np.array_equal(to_np(ids)[:, :n + 1],
+                                                                              oi.token_ids[:, :n + 1])
+            ferr, err = check_step(w, idx, K, V, Kd, Vd, q, w.B, scale, c=oi.c, sizes=oi.sizes,
+                                   offsets=oi.offsets, token_ids=oi.token_ids)
+            say(f"  step {s}: {n + 1} tokens, decode max abs err fused {ferr:.2e}, split {err:.2e}")
+
+
+def test_full_size_layer_stack_sampled_layers():
+    """The 32-layer stack runs layer by layer through the same calls; two
+    layers (the first and the last, independent seeded mixtures) are built and
+    checked at their full size."""
+    w = synth.workload(5)
+    scale = 1.0 / math.sqrt(w.d)
+    for layer in (0, w.layers - 1):
+        say(f"[full size] {w.name} layer {layer}: {w.heads} heads x {w.L} keys, C={w.C}, B={w.B}")
+        base, K, V, init, means = gen(w, layer)
+        idx = kvc.ClusterIndex(w.heads, w.C, w.capacity, torch.bfloat16)
+        Kd, Vd = to_dev(K), to_dev(V)
+        kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+        torch.cuda.synchronize()
+        check_build(w, K, init, idx, [layer % w.heads])
+        q = queries(w, base, 0, K, w.L, means)
+        ferr, _ = check_step(w, idx, K, V, Kd, Vd, q, w.B, scale, split=False)
+        say(f"  decode max abs err fused {ferr:.2e}")
+        del Kd, Vd, idx
+        torch.cuda.empty_cache()
