@@ -91,17 +91,22 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restric
 // ---------------------------------------------------------------------------
 // a3: assignment of bf16 keys on the matrix cores.
 //
-// Block = 8 waves x 64 keys. The whole operand chat [cpad, 128] of the head
-// sits in LDS; each wave keeps its keys in registers as the B operand of
-// v_mfma_f32_32x32x16_bf16 (32 keys per tile, two tiles) and streams 32
-// centroids at a time as the A operand, so D[centroid][key] lands with one
-// key per lane column. The channel order inside the contraction is permuted
-// the same way for both operands (lane half b, k-step s <-> channels
-// 64b + 8s .. 64b + 8s + 7), which leaves every dot product unchanged.
+// v_mfma_f32_16x16x32_bf16 with the normalised centroids as the A operand
+// (16 centroids x 32 channels per tile, staged once per block in LDS) and the
+// keys as the B operand (32 channels x 16 keys): lane l holds key l % 16 of
+// its tile and channels 32 s + 8 (l / 16) .. + 7 at k-step s, so one load
+// instruction reads 64 contiguous bytes of 16 key rows. D[centroid][key]
+// gives each lane 4 centroids (4 (l / 16) + r) of one key per tile.
 //
-// Each lane keeps the best score, its centroid id and the runner-up score of
-// its key; lanes l and l^32 (the two halves of the centroid rows) merge at the
-// end. The fp32 order is certified against the exact (fp64) order when
+// Block = 8 waves x 64 keys (4 tiles of 16 per wave); the grid holds about
+// one block per compute unit and each block walks over 512-key groups of one
+// head, so the head's operand is staged in LDS once per block (row r's 16-byte
+// chunk c at c ^ (r & 15): the 16 rows one read instruction touches land in
+// distinct banks).
+//
+// Each lane keeps the best score, the tile-uniform part of its centroid id
+// and the runner-up score of each of its keys; the 4 lanes of a key merge at
+// the end. The fp32 order is certified against the exact (fp64) order when
 //   best - runner_up > 2 * 4 * (d + 16) * 2^-24 * ||K_i|| * max||chat_k|| * 1.02,
 // a bound on the error of any fp32 accumulation of d exact products (the
 // products of bf16 operands are exact) with a safety factor of 4. Keys that
@@ -111,122 +116,142 @@ constexpr int AS_WAVES = 8;
 constexpr int AS_THREADS = AS_WAVES * WAVE;
 constexpr int AS_TILE = AS_WAVES * 64;
 
-__device__ __forceinline__ void top2_update(float s, int k, float& m1, float& m2, int& i1) {
-  i1 = s > m1 ? k : i1;
+__device__ __forceinline__ void top2_update(float s, int u, float& m1, float& m2, int& i1) {
+  const bool gt = s > m1;
+  i1 = gt ? u : i1;
   m2 = __builtin_amdgcn_fmed3f(m1, m2, s);
-  m1 = fmaxf(m1, s);
+  m1 = gt ? s : m1;
 }
 
 __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     const uint16_t* __restrict__ keys, long long head_stride, int L, const uint16_t* __restrict__ chat, int C,
     int cpad, int32_t* __restrict__ labels, long long label_stride, int32_t* __restrict__ queue,
     uint32_t* __restrict__ qcount, float* __restrict__ top2) {
-  extern __shared__ u32x4 sC[];  // cpad rows x 16 chunks of 16 B, chunk c of row r at c ^ (r & 7)
+  extern __shared__ u32x4 sC[];  // cpad rows x 16 chunks of 16 B, chunk c of row r at c ^ (r & 15)
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, col = lane & 31;
-  const int tile0 = blockIdx.x * AS_TILE + wave * 64;
+  const int j16 = lane & 15, kb4 = lane >> 4;
 
   const u32x4* Cg = reinterpret_cast<const u32x4*>(chat + (size_t)h * cpad * D);
   for (int e = tid; e < cpad * 16; e += AS_THREADS) {
     const int r = e >> 4, c = e & 15;
-    sC[r * 16 + (c ^ (r & 7))] = Cg[e];
-  }
-
-  const uint16_t* Kh = keys + (size_t)h * head_stride;
-  bf16x8 bk[2][8];
-  float n2[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    int row = tile0 + t * 32 + col;
-    row = row < L ? row : L - 1;
-    const u32x4* src = reinterpret_cast<const u32x4*>(Kh + (size_t)row * D + half * 64);
-    float ss = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const u32x4 v = src[s];
-      bk[t][s] = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float lo = __uint_as_float(v[q] << 16), hi = __uint_as_float(v[q] & 0xFFFF0000u);
-        ss = fmaf(lo, lo, ss);
-        ss = fmaf(hi, hi, ss);
-      }
-    }
-    n2[t] = ss;
+    sC[r * 16 + (c ^ (r & 15))] = Cg[e];
   }
   __syncthreads();
 
-  float m1[2] = {-INFINITY, -INFINITY}, m2[2] = {-INFINITY, -INFINITY};
-  int i1[2] = {0, 0};
-  const int nct = cpad >> 5;
-  for (int ct = 0; ct < nct; ++ct) {
-    f32x16 acc0 = {}, acc1 = {};
-    const int arow = ct * 32 + col;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, sC[arow * 16 + ((half * 8 + s) ^ (arow & 7))]);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bk[0][s], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bk[1][s], acc1, 0, 0, 0);
-    }
-    const int kb = ct * 32 + 4 * half;
-    if (ct * 32 + 32 <= C) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int k = kb + 8 * (r >> 2) + (r & 3);
-        top2_update(acc0[r], k, m1[0], m2[0], i1[0]);
-        top2_update(acc1[r], k, m1[1], m2[1], i1[1]);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int k = kb + 8 * (r >> 2) + (r & 3);
-        const bool ok = k < C;
-        top2_update(ok ? acc0[r] : -INFINITY, k, m1[0], m2[0], i1[0]);
-        top2_update(ok ? acc1[r] : -INFINITY, k, m1[1], m2[1], i1[1]);
-      }
-    }
-  }
-
-  // merge the two halves of the centroid rows, then certify
+  const uint16_t* Kh = keys + (size_t)h * head_stride + 8 * kb4;
+  const int ngroups = (L + AS_TILE - 1) / AS_TILE;
+  const int nct = cpad >> 4;
   const float gamma = 2.0f * 4.0f * (float)(D + 16) * 5.9604644775390625e-8f * 1.02f;
-  int my_label = 0;
-  bool my_flag = false;
-  float my_m1 = 0.f, my_m2 = 0.f;
+  for (int grpi = blockIdx.x; grpi < ngroups; grpi += gridDim.x) {
+    const int row0 = grpi * AS_TILE + wave * 64;
+    u32x4 kn[4][4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const float o1 = __shfl_xor(m1[t], 32), o2 = __shfl_xor(m2[t], 32), on = __shfl_xor(n2[t], 32);
-    const int oi = __shfl_xor(i1[t], 32);
-    const float M1 = fmaxf(m1[t], o1);
-    const int I1 = m1[t] > o1 ? i1[t] : (o1 > m1[t] ? oi : min(i1[t], oi));
-    const float M2 = fmaxf(fminf(m1[t], o1), fmaxf(m2[t], o2));
-    const float nk = sqrtf(n2[t] + on);
-    const bool cert = (M1 - M2) > gamma * nk;  // false for NaN and for ties
-    if (t == half) {
-      my_label = I1;
-      my_flag = !cert;
-      my_m1 = M1;
-      my_m2 = M2;
+    for (int T = 0; T < 4; ++T) {
+      int row = row0 + T * 16 + j16;
+      row = row < L ? row : L - 1;  // the tail tile repeats the last key; its results are not stored
+      const uint16_t* src = Kh + (size_t)row * D;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kn[T][s] = *reinterpret_cast<const u32x4*>(src + 32 * s);
     }
-  }
-  const int row = tile0 + half * 32 + col;
-  const bool valid = row < L;
-  if (valid) {
-    labels[(size_t)h * label_stride + row] = my_label;
-    if (top2) {
-      top2[((size_t)h * L + row) * 2] = my_m1;
-      top2[((size_t)h * L + row) * 2 + 1] = my_m2;
+    bf16x8 kb[4][4];
+    float n2[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 v = kn[T][s];
+        kb[T][s] = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = __uint_as_float(v[q] << 16), hi = __uint_as_float(v[q] & 0xFFFF0000u);
+          ss = fmaf(lo, lo, ss);
+          ss = fmaf(hi, hi, ss);
+        }
+      }
+      n2[T] = ss;
     }
-  }
-  const bool push = valid && my_flag;
-  const unsigned long long bal = __ballot(push);
-  if (bal) {
-    const int n = __popcll(bal);
-    int base = 0;
-    if (lane == __ffsll((long long)bal) - 1) base = (int)atomicAdd(qcount + h, (uint32_t)n);
-    base = __shfl(base, __ffsll((long long)bal) - 1);
-    const int slot = base + __popcll(bal & ((1ull << lane) - 1ull));
-    if (push) queue[(size_t)h * L + slot] = row;
+    float m1[4], m2[4];
+    int i1[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      m1[T] = -INFINITY;
+      m2[T] = -INFINITY;
+      i1[T] = 0;
+    }
+    for (int ct = 0; ct < nct; ++ct) {
+      const int arow = ct * 16 + j16;
+      bf16x8 a[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) a[s] = __builtin_bit_cast(bf16x8, sC[arow * 16 + ((4 * s + kb4) ^ (arow & 15))]);
+      f32x4 acc[4] = {};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], kb[T][s], acc[T], 0, 0, 0);
+      const int u0 = ct * 16;  // centroid of register r in this lane: u0 + 4 (lane / 16) + r
+      if (u0 + 16 <= C) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int T = 0; T < 4; ++T) top2_update(acc[T][r], u0 + r, m1[T], m2[T], i1[T]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = u0 + 4 * kb4 + r < C;
+#pragma unroll
+          for (int T = 0; T < 4; ++T) top2_update(ok ? acc[T][r] : -INFINITY, u0 + r, m1[T], m2[T], i1[T]);
+        }
+      }
+    }
+    // merge the 4 lanes of each key (lanes 16 apart), then certify
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      i1[T] += 4 * kb4;
+#pragma unroll
+      for (int m = 16; m <= 32; m <<= 1) {
+        const float o1 = __shfl_xor(m1[T], m), o2 = __shfl_xor(m2[T], m);
+        const int oi = __shfl_xor(i1[T], m);
+        const float M2 = fmaxf(fminf(m1[T], o1), fmaxf(m2[T], o2));
+        i1[T] = m1[T] > o1 ? i1[T] : (o1 > m1[T] ? oi : min(i1[T], oi));
+        m1[T] = fmaxf(m1[T], o1);
+        m2[T] = M2;
+        n2[T] += __shfl_xor(n2[T], m);
+      }
+    }
+    // lane kb4 == T publishes key j16 of tile T
+    int my_label = 0;
+    bool my_flag = false;
+    float my_m1 = 0.f, my_m2 = 0.f;
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+      if (T == kb4) {
+        my_label = i1[T];
+        my_flag = !((m1[T] - m2[T]) > gamma * sqrtf(n2[T]));  // true for NaN and ties
+        my_m1 = m1[T];
+        my_m2 = m2[T];
+      }
+    const int row = row0 + kb4 * 16 + j16;
+    const bool valid = row < L;
+    if (valid) {
+      labels[(size_t)h * label_stride + row] = my_label;
+      if (top2) {
+        top2[((size_t)h * L + row) * 2] = my_m1;
+        top2[((size_t)h * L + row) * 2 + 1] = my_m2;
+      }
+    }
+    const bool push = valid && my_flag;
+    const unsigned long long bal = __ballot(push);
+    if (bal) {
+      const int n = __popcll(bal);
+      const int first = __ffsll((long long)bal) - 1;
+      int base = 0;
+      if (lane == first) base = (int)atomicAdd(qcount + h, (uint32_t)n);
+      base = __shfl(base, first);
+      const int slot = base + __popcll(bal & ((1ull << lane) - 1ull));
+      if (push) queue[(size_t)h * L + slot] = row;
+    }
   }
 }
 
@@ -240,7 +265,7 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
 // with the chunk index of row r XOR-ed by r (mod the chunk count), so the 64
 // lanes of a wave, reading 64 different rows at one chunk, spread over the
 // banks. Rows come from the per-head queue (queue != null) or are all rows.
-template <typename KT>
+template <typename KT, int MAXT>
 __global__ __launch_bounds__(256) void assign_exact_kernel(const KT* __restrict__ keys, long long head_stride, int L,
                                                            const KT* __restrict__ chat, int C, int cpad,
                                                            int32_t* __restrict__ labels, long long label_stride,
@@ -249,14 +274,14 @@ __global__ __launch_bounds__(256) void assign_exact_kernel(const KT* __restrict_
   constexpr bool STAGE = sizeof(KT) == 2;
   constexpr int CHUNKS = D * (int)sizeof(KT) / 16;  // 16-byte chunks per operand row
   constexpr int EPC = 16 / (int)sizeof(KT);         // elements per chunk
-  constexpr int MAXT = (512 + 63) / 64;
+  constexpr int NK = 2;                             // keys per wave and pass
   extern __shared__ u32x4 smem[];
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
   const int n = queue ? (int)__atomic_load_n(qcount + h, __ATOMIC_RELAXED) : L;
-  if (blockIdx.x * 4 >= n) return;  // no key for this block (uniform)
+  if (blockIdx.x * 4 * NK >= n) return;  // no key for this block (uniform): nothing staged
   const KT* Kh = keys + (size_t)h * head_stride;
   const u32x4* Cg = reinterpret_cast<const u32x4*>(chat + (size_t)h * cpad * D);
   if constexpr (STAGE) {
@@ -266,60 +291,78 @@ __global__ __launch_bounds__(256) void assign_exact_kernel(const KT* __restrict_
     }
     __syncthreads();
   }
-  for (int e = gw; e < n; e += nw) {
-    const int row = queue ? queue[(size_t)h * L + e] : e;
-    const double k0 = (double)load_f32(Kh, (size_t)row * D + lane);
-    const double k1 = (double)load_f32(Kh, (size_t)row * D + 64 + lane);
-    double s[MAXT];
+  // lane's centroid rows; rows past cpad read the last (zero) padding row and
+  // are excluded from the argmax, so no branch separates the chains
+  int crow[MAXT];
 #pragma unroll
-    for (int t = 0; t < MAXT; ++t) s[t] = 0.0;
+  for (int t = 0; t < MAXT; ++t) crow[t] = min(lane + 64 * t, cpad - 1);
+  for (int e = gw * NK; e < n; e += nw * NK) {
+    int row[NK];
+    double k0[NK], k1[NK];
 #pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const int ee = min(e + kk, n - 1);
+      row[kk] = queue ? queue[(size_t)h * L + ee] : ee;
+      k0[kk] = (double)load_f32(Kh, (size_t)row[kk] * D + lane);
+      k1[kk] = (double)load_f32(Kh, (size_t)row[kk] * D + 64 + lane);
+    }
+    double s[NK][MAXT];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t) s[kk][t] = 0.0;
+#pragma unroll 1
     for (int q = 0; q < CHUNKS; ++q) {
-      double kj[EPC];
+      double kj[NK][EPC];
 #pragma unroll
-      for (int i = 0; i < EPC; ++i) {
-        const int j = q * EPC + i;
-        const double src = j < 64 ? k0 : k1;
-        const int lo = __builtin_amdgcn_readlane((int)(__double_as_longlong(src) & 0xFFFFFFFFll), j & 63);
-        const int hi = __builtin_amdgcn_readlane((int)(__double_as_longlong(src) >> 32), j & 63);
-        kj[i] = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
-      }
+      for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) {
+          const int j = q * EPC + i;
+          const double src = j < 64 ? k0[kk] : k1[kk];
+          const int lo = __builtin_amdgcn_readlane((int)(__double_as_longlong(src) & 0xFFFFFFFFll), j & 63);
+          const int hi = __builtin_amdgcn_readlane((int)(__double_as_longlong(src) >> 32), j & 63);
+          kj[kk][i] = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
+        }
 #pragma unroll
       for (int t = 0; t < MAXT; ++t) {
-        const int c = lane + 64 * t;
-        if (c < C) {
-          const u32x4 v = STAGE ? smem[c * CHUNKS + (q ^ (c & (CHUNKS - 1)))] : Cg[(size_t)c * CHUNKS + q];
+        const int c = crow[t];
+        const u32x4 v = STAGE ? smem[c * CHUNKS + (q ^ (c & (CHUNKS - 1)))] : Cg[(size_t)c * CHUNKS + q];
 #pragma unroll
-          for (int i = 0; i < EPC; ++i) {
-            float x;
-            if constexpr (STAGE) x = (i & 1) ? __uint_as_float(v[i >> 1] & 0xFFFF0000u) : __uint_as_float(v[i >> 1] << 16);
-            else x = __uint_as_float(v[i]);
-            s[t] = fma(kj[i], (double)x, s[t]);
-          }
+        for (int i = 0; i < EPC; ++i) {
+          float x;
+          if constexpr (STAGE) x = (i & 1) ? __uint_as_float(v[i >> 1] & 0xFFFF0000u) : __uint_as_float(v[i >> 1] << 16);
+          else x = __uint_as_float(v[i]);
+          const double xd = (double)x;
+#pragma unroll
+          for (int kk = 0; kk < NK; ++kk) s[kk][t] = fma(kj[kk][i], xd, s[kk][t]);
         }
       }
     }
-    double best = -INFINITY;
-    int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int t = 0; t < MAXT; ++t) {
-      const int c = lane + 64 * t;
-      if (c < C && s[t] > best) {
-        best = s[t];
-        bi = c;
-      }
-    }
-    // wave argmax: larger score, then smaller id
+    for (int kk = 0; kk < NK; ++kk) {
+      double best = -INFINITY;
+      int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ob = __shfl_xor(best, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ob > best || (ob == best && oi < bi)) {
-        best = ob;
-        bi = oi;
+      for (int t = 0; t < MAXT; ++t) {
+        const int c = lane + 64 * t;
+        if (c < C && s[kk][t] > best) {
+          best = s[kk][t];
+          bi = c;
+        }
       }
+      // wave argmax: larger score, then smaller id
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const double ob = __shfl_xor(best, off);
+        const int oi = __shfl_xor(bi, off);
+        if (ob > best || (ob == best && oi < bi)) {
+          best = ob;
+          bi = oi;
+        }
+      }
+      if (lane == 0 && e + kk < n) labels[(size_t)h * label_stride + row[kk]] = bi;
     }
-    if (lane == 0) labels[(size_t)h * label_stride + row] = bi;
   }
 }
 
@@ -415,11 +458,61 @@ __global__ __launch_bounds__(CS_BLOCK) void csr_scatter_kernel(const int32_t* __
 }
 
 // ---------------------------------------------------------------------------
-// a4 + a2: centroid update fused with normalisation. One wave per cluster,
-// lane = channels 2*lane, 2*lane+1. Members are read through the index in
-// ascending token order and summed in fp64 in that order; the mean is the
-// fp64 sum / count rounded once to fp32 (an empty cluster keeps its
-// centroid). The new operand row is the normalised mean.
+// a4 + a2: centroid update fused with normalisation. Each wave updates two
+// clusters, one per half wave; lane = channels 4 * (lane % 32) .. + 3, so a
+// half wave reads one 256-byte key row per load. Members are read through the
+// index in ascending token order (16 rows in flight per lane) and summed in
+// fp64 in that order; the mean is the fp64 sum / count rounded once to fp32
+// (an empty cluster keeps its centroid). The new operand row is the
+// normalised mean.
+template <typename KT>
+__device__ __forceinline__ void load4(const KT* p, float* o);
+template <>
+__device__ __forceinline__ void load4(const uint16_t* p, float* o) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  o[0] = __uint_as_float(v.x << 16);
+  o[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  o[2] = __uint_as_float(v.y << 16);
+  o[3] = __uint_as_float(v.y & 0xFFFF0000u);
+}
+template <>
+__device__ __forceinline__ void load4(const float* p, float* o) {
+  const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+  o[0] = v[0];
+  o[1] = v[1];
+  o[2] = v[2];
+  o[3] = v[3];
+}
+
+// Normalisation of two centroid rows held by the two halves of a wave
+// (4 channels per lane); see normalize_row for the rule.
+template <typename OT>
+__device__ __forceinline__ void normalize_rows2(const float* c, float* lds2, bool active, OT* out_row) {
+  const int lane = lane_id(), hl = lane & 31, half = lane >> 5;
+  float* row = lds2 + half * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) row[4 * hl + i] = c[i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  double ss = 0.0;
+  if (hl == 0) {
+    for (int j = 0; j < D; ++j) {
+      const double v = (double)row[j];
+      ss = fma(v, v, ss);
+    }
+  }
+  // broadcast each half's sum from its lane 0
+  const int lo = __shfl((int)(__double_as_longlong(ss) & 0xFFFFFFFFll), half * 32);
+  const int hi = __shfl((int)(__double_as_longlong(ss) >> 32), half * 32);
+  ss = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
+  const double nrm = sqrt(ss);
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store_op(out_row, 4 * hl + i, nrm > 0.0 ? (double)c[i] / nrm : 0.0);
+  }
+}
+
 template <typename KT>
 __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys, long long head_stride, int C,
                                                      int cpad, const int32_t* __restrict__ sizes,
@@ -427,45 +520,48 @@ __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys
                                                      const int32_t* __restrict__ token_ids, long long ids_stride,
                                                      float* __restrict__ cent, float* __restrict__ cent_t,
                                                      KT* __restrict__ chat) {
-  __shared__ float rows[4][D];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float rows[4][2][D];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, hl = lane & 31, half = lane >> 5;
   const int h = blockIdx.y;
-  const int k = blockIdx.x * 4 + w;
-  if (k >= C) return;
-  const int n = sizes[(size_t)h * C + k];
-  const int off = offsets[(size_t)h * (C + 1) + k];
+  const int k = (blockIdx.x * 4 + w) * 2 + half;
+  if ((blockIdx.x * 4 + w) * 2 >= C) return;  // whole wave
+  const bool active = k < C;
+  const int n = active ? sizes[(size_t)h * C + k] : 0;
+  const int off = active ? offsets[(size_t)h * (C + 1) + k] : 0;
   const int32_t* ids = token_ids + (size_t)h * ids_stride + off;
-  const KT* Kh = keys + (size_t)h * head_stride + 2 * lane;
-  float* cr = cent + ((size_t)h * C + k) * D;
-  float c0, c1;
+  const KT* Kh = keys + (size_t)h * head_stride + 4 * hl;
+  float* cr = cent + ((size_t)h * C + (active ? k : 0)) * D;
+  float c[4];
   if (n > 0) {
-    double a0 = 0.0, a1 = 0.0;
-    constexpr int U = 8;
+    double a[4] = {0.0, 0.0, 0.0, 0.0};
+    constexpr int U = 16;
     int m = 0;
     for (; m + U <= n; m += U) {
-      float x0[U], x1[U];
+      float x[U][4];
 #pragma unroll
-      for (int u = 0; u < U; ++u) load_pair(Kh + (size_t)ids[m + u] * D, x0[u], x1[u]);
+      for (int u = 0; u < U; ++u) load4(Kh + (size_t)ids[m + u] * D, x[u]);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        a0 += (double)x0[u];
-        a1 += (double)x1[u];
-      }
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] += (double)x[u][i];
     }
     for (; m < n; ++m) {
-      float x0, x1;
-      load_pair(Kh + (size_t)ids[m] * D, x0, x1);
-      a0 += (double)x0;
-      a1 += (double)x1;
+      float x[4];
+      load4(Kh + (size_t)ids[m] * D, x);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] += (double)x[i];
     }
-    c0 = (float)(a0 / (double)n);
-    c1 = (float)(a1 / (double)n);
-    store_centroid(cr, cent_t + (size_t)h * C * D, C, k, c0, c1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = (float)(a[i] / (double)n);
+    *reinterpret_cast<f32x4*>(cr + 4 * hl) = f32x4{c[0], c[1], c[2], c[3]};
+    float* t = cent_t + (size_t)h * C * D + ((size_t)hl * C + k) * 4;  // chunk hl of cluster k
+    *reinterpret_cast<f32x4*>(t) = f32x4{c[0], c[1], c[2], c[3]};
   } else {
-    c0 = cr[2 * lane];
-    c1 = cr[2 * lane + 1];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(cr + 4 * hl);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = v[i];
   }
-  normalize_row(c0, c1, rows[w], chat + ((size_t)h * cpad + k) * D);
+  normalize_rows2(c, &rows[w][0][0], active, chat + ((size_t)h * cpad + (active ? k : 0)) * D);
 }
 
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, size_t n, int32_t v) {
@@ -497,6 +593,47 @@ hipError_t launch_init_centroids(int dtype, const void* keys, long long head_str
   return hipGetLastError();
 }
 
+// The exact pass instantiated for the number of 64-centroid groups a lane owns.
+template <typename KT, int MAXT>
+hipError_t launch_exact_t(const KT* keys, long long head_stride, int L, const KT* chat, int C, int cpad,
+                          int32_t* labels, long long label_stride, const int32_t* queue, const uint32_t* qcount,
+                          dim3 grid, size_t lds, hipStream_t st) {
+  if (lds > 64 * 1024) {
+    static bool attr = false;
+    if (!attr) {
+      const hipError_t e = hipFuncSetAttribute((const void*)assign_exact_kernel<KT, MAXT>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+  }
+  assign_exact_kernel<KT, MAXT><<<grid, 256, lds, st>>>(keys, head_stride, L, chat, C, cpad, labels, label_stride,
+                                                       queue, qcount);
+  return hipGetLastError();
+}
+
+template <typename KT>
+hipError_t launch_exact(const KT* keys, long long head_stride, int L, const KT* chat, int C, int cpad,
+                        int32_t* labels, long long label_stride, const int32_t* queue, const uint32_t* qcount,
+                        dim3 grid, size_t lds, hipStream_t st) {
+  switch ((C + 63) / 64) {
+#define KVC_EXACT_CASE(T) \
+  case T:                 \
+    return launch_exact_t<KT, T>(keys, head_stride, L, chat, C, cpad, labels, label_stride, queue, qcount, grid, lds, st);
+    KVC_EXACT_CASE(1)
+    KVC_EXACT_CASE(2)
+    KVC_EXACT_CASE(3)
+    KVC_EXACT_CASE(4)
+    KVC_EXACT_CASE(5)
+    KVC_EXACT_CASE(6)
+    KVC_EXACT_CASE(7)
+    KVC_EXACT_CASE(8)
+#undef KVC_EXACT_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
                          int cpad, int32_t* labels, long long label_stride, int32_t* queue, uint32_t* qcount,
                          float* top2, hipEvent_t* events, hipStream_t st) {
@@ -509,7 +646,11 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    dim3 grid(grid1(L, AS_TILE), heads);
+    // about one block per compute unit; each walks over 512-key groups of one head
+    const int ngroups = grid1(L, AS_TILE);
+    int gx = (256 + heads - 1) / heads;
+    gx = gx < 1 ? 1 : (gx > ngroups ? ngroups : gx);
+    dim3 grid(gx, heads);
     if (events) {
       hipError_t e0 = hipEventRecord(events[0], st);
       if (e0 != hipSuccess) return e0;
@@ -524,26 +665,16 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
       if (e != hipSuccess) return e;
     }
     // exact re-scoring of the uncertified keys; blocks without work exit at once
-    static bool attr2 = false;
-    if (!attr2) {
-      e = hipFuncSetAttribute((const void*)assign_exact_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
-      if (e != hipSuccess) return e;
-      attr2 = true;
-    }
-    dim3 g2(8, heads);
-    assign_exact_kernel<uint16_t><<<g2, 256, lds, st>>>((const uint16_t*)keys, head_stride, L, (const uint16_t*)chat, C,
-                                                        cpad, labels, label_stride, queue, qcount);
-    return hipGetLastError();
+    return launch_exact<uint16_t>((const uint16_t*)keys, head_stride, L, (const uint16_t*)chat, C, cpad, labels,
+                                  label_stride, queue, qcount, dim3(4, heads), lds, st);
   }
-  dim3 g2(grid1(L, 4) < 64 ? grid1(L, 4) : 64, heads);
+  dim3 g2(grid1(L, 8) < 64 ? grid1(L, 8) : 64, heads);
   if (events) {
     hipError_t e0 = hipEventRecord(events[0], st);
     if (e0 != hipSuccess) return e0;
   }
-  assign_exact_kernel<float><<<g2, 256, 0, st>>>((const float*)keys, head_stride, L, (const float*)chat, C, cpad,
-                                                 labels, label_stride, nullptr, nullptr);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_exact<float>((const float*)keys, head_stride, L, (const float*)chat, C, cpad, labels,
+                                     label_stride, nullptr, nullptr, g2, 0, st);
   if (e == hipSuccess && events) e = hipEventRecord(events[1], st);
   return e;
 }
@@ -565,7 +696,7 @@ hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, 
 hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cpad,
                          const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
                          float* cent, float* cent_t, void* chat, hipStream_t st) {
-  dim3 grid(grid1(C, 4), heads);
+  dim3 grid(grid1(C, 8), heads);
   if (dtype == DT_BF16)
     update_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, C, cpad, sizes, offsets,
                                                   token_ids, ids_stride, cent, cent_t, (uint16_t*)chat);
