@@ -270,7 +270,8 @@ def main():
         rl["select_decode"] = {"bound": "hbm", "achieved": alg["step_bytes"] / (dd_ms / 1e3) / 1e9,
                                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "avg_us": dd_ms * 1e3,
                                "share": dd_ms * n_dec / total_ms}
-        kernel_names["select_decode"] = "select_decode_kernel"
+        kernel_names["select_decode"] = ("select_decode_bf16_kernel" if w.dtype == synth.BF16
+                                         else "select_decode_kernel")
     else:
         rl["sparse_decode"] = {"bound": "hbm", "achieved": alg["decode_bytes"] / (dd_ms / 1e3) / 1e9,
                                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "avg_us": dd_ms * 1e3,
