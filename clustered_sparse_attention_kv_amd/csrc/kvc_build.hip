@@ -180,31 +180,62 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
       m2[T] = -INFINITY;
       i1[T] = 0;
     }
-    for (int ct = 0; ct < nct; ++ct) {
+    // centroid tiles in a pipeline: while the products of tile ct + 1 run on
+    // the matrix cores, the vector units fold tile ct into the running best
+    // and runner-up, and the operand of tile ct + 2 is read from LDS. The
+    // instruction scheduler is asked to alternate one product with four
+    // vector instructions so that both units stay busy within a wave. The
+    // tile count (cpad / 16) is even and only the last two tiles can hold
+    // padding rows, so the loop body folds full tiles without masks.
+    auto load_a = [&](int ct, bf16x8 (&a)[4]) {
       const int arow = ct * 16 + j16;
-      bf16x8 a[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) a[s] = __builtin_bit_cast(bf16x8, sC[arow * 16 + ((4 * s + kb4) ^ (arow & 15))]);
-      f32x4 acc[4] = {};
+    };
+    auto mma = [&](const bf16x8 (&a)[4], f32x4 (&acc)[4]) {
+#pragma unroll
+      for (int T = 0; T < 4; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], kb[T][s], acc[T], 0, 0, 0);
+    };
+    auto fold = [&](int ct, const f32x4 (&acc)[4], bool masked) {
       const int u0 = ct * 16;  // centroid of register r in this lane: u0 + 4 (lane / 16) + r
-      if (u0 + 16 <= C) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = !masked || u0 + 4 * kb4 + r < C;
 #pragma unroll
-          for (int T = 0; T < 4; ++T) top2_update(acc[T][r], u0 + r, m1[T], m2[T], i1[T]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = u0 + 4 * kb4 + r < C;
-#pragma unroll
-          for (int T = 0; T < 4; ++T) top2_update(ok ? acc[T][r] : -INFINITY, u0 + r, m1[T], m2[T], i1[T]);
-        }
+        for (int T = 0; T < 4; ++T) top2_update(ok ? acc[T][r] : -INFINITY, u0 + r, m1[T], m2[T], i1[T]);
       }
+    };
+    auto interleave = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the operand reads first
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix product
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four vector instructions
+      }
+    };
+    bf16x8 aA[4], aB[4];
+    f32x4 accA[4], accB[4];
+    load_a(0, aA);
+    mma(aA, accA);
+    load_a(1, aB);
+    int ct = 0;
+    for (; ct + 2 < nct; ct += 2) {
+      mma(aB, accB);       // tile ct + 1
+      load_a(ct + 2, aA);
+      fold(ct, accA, false);
+      interleave();
+      mma(aA, accA);       // tile ct + 2
+      load_a(ct + 3, aB);  // ct + 3 < nct: nct and ct are even
+      fold(ct + 1, accB, false);
+      interleave();
     }
+    mma(aB, accB);  // tile nct - 1
+    fold(ct, accA, true);
+    fold(ct + 1, accB, true);
     // merge the 4 lanes of each key (lanes 16 apart), then certify
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
@@ -458,60 +489,32 @@ __global__ __launch_bounds__(CS_BLOCK) void csr_scatter_kernel(const int32_t* __
 }
 
 // ---------------------------------------------------------------------------
-// a4 + a2: centroid update fused with normalisation. Each wave updates two
-// clusters, one per half wave; lane = channels 4 * (lane % 32) .. + 3, so a
-// half wave reads one 256-byte key row per load. Members are read through the
-// index in ascending token order (16 rows in flight per lane) and summed in
-// fp64 in that order; the mean is the fp64 sum / count rounded once to fp32
-// (an empty cluster keeps its centroid). The new operand row is the
-// normalised mean.
+// a4 + a2: centroid update fused with normalisation. One wave per cluster,
+// lane = channels 2 lane, 2 lane + 1. The member ids come in groups of 64
+// (one per lane, the next group requested before the current one is summed);
+// each member's id reaches the wave through a lane read, the group's rows are
+// all requested at once, and then summed in fp64 in ascending member order
+// (the index order). The mean is the fp64 sum / count rounded once to fp32 (an
+// empty cluster keeps its centroid); the new operand row is the normalised
+// mean.
 template <typename KT>
-__device__ __forceinline__ void load4(const KT* p, float* o);
+struct UpdRow;  // one row's two channels as loaded
 template <>
-__device__ __forceinline__ void load4(const uint16_t* p, float* o) {
-  const uint2 v = *reinterpret_cast<const uint2*>(p);
-  o[0] = __uint_as_float(v.x << 16);
-  o[1] = __uint_as_float(v.x & 0xFFFF0000u);
-  o[2] = __uint_as_float(v.y << 16);
-  o[3] = __uint_as_float(v.y & 0xFFFF0000u);
-}
+struct UpdRow<uint16_t> {
+  static constexpr int GROUP = 64;
+  uint32_t v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ float a() const { return __uint_as_float(v << 16); }
+  __device__ __forceinline__ float b() const { return __uint_as_float(v & 0xFFFF0000u); }
+};
 template <>
-__device__ __forceinline__ void load4(const float* p, float* o) {
-  const f32x4 v = *reinterpret_cast<const f32x4*>(p);
-  o[0] = v[0];
-  o[1] = v[1];
-  o[2] = v[2];
-  o[3] = v[3];
-}
-
-// Normalisation of two centroid rows held by the two halves of a wave
-// (4 channels per lane); see normalize_row for the rule.
-template <typename OT>
-__device__ __forceinline__ void normalize_rows2(const float* c, float* lds2, bool active, OT* out_row) {
-  const int lane = lane_id(), hl = lane & 31, half = lane >> 5;
-  float* row = lds2 + half * D;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) row[4 * hl + i] = c[i];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  double ss = 0.0;
-  if (hl == 0) {
-    for (int j = 0; j < D; ++j) {
-      const double v = (double)row[j];
-      ss = fma(v, v, ss);
-    }
-  }
-  // broadcast each half's sum from its lane 0
-  const int lo = __shfl((int)(__double_as_longlong(ss) & 0xFFFFFFFFll), half * 32);
-  const int hi = __shfl((int)(__double_as_longlong(ss) >> 32), half * 32);
-  ss = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
-  const double nrm = sqrt(ss);
-  if (active) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) store_op(out_row, 4 * hl + i, nrm > 0.0 ? (double)c[i] / nrm : 0.0);
-  }
-}
+struct UpdRow<float> {
+  static constexpr int GROUP = 32;
+  float2 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float2*>(p); }
+  __device__ __forceinline__ float a() const { return v.x; }
+  __device__ __forceinline__ float b() const { return v.y; }
+};
 
 template <typename KT>
 __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys, long long head_stride, int C,
@@ -520,48 +523,44 @@ __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys
                                                      const int32_t* __restrict__ token_ids, long long ids_stride,
                                                      float* __restrict__ cent, float* __restrict__ cent_t,
                                                      KT* __restrict__ chat) {
-  __shared__ float rows[4][2][D];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, hl = lane & 31, half = lane >> 5;
+  constexpr int GR = UpdRow<KT>::GROUP;
+  __shared__ float rows[4][D];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.y;
-  const int k = (blockIdx.x * 4 + w) * 2 + half;
-  if ((blockIdx.x * 4 + w) * 2 >= C) return;  // whole wave
-  const bool active = k < C;
-  const int n = active ? sizes[(size_t)h * C + k] : 0;
-  const int off = active ? offsets[(size_t)h * (C + 1) + k] : 0;
+  const int k = blockIdx.x * 4 + w;
+  if (k >= C) return;
+  const int n = sizes[(size_t)h * C + k];
+  const int off = offsets[(size_t)h * (C + 1) + k];
   const int32_t* ids = token_ids + (size_t)h * ids_stride + off;
-  const KT* Kh = keys + (size_t)h * head_stride + 4 * hl;
-  float* cr = cent + ((size_t)h * C + (active ? k : 0)) * D;
-  float c[4];
+  const KT* Kh = keys + (size_t)h * head_stride + 2 * lane;
+  float* cr = cent + ((size_t)h * C + k) * D;
+  float c0, c1;
   if (n > 0) {
-    double a[4] = {0.0, 0.0, 0.0, 0.0};
-    constexpr int U = 16;
-    int m = 0;
-    for (; m + U <= n; m += U) {
-      float x[U][4];
+    double a0 = 0.0, a1 = 0.0;
+    int idn = lane < n && lane < GR ? ids[lane] : 0;
+    for (int m0 = 0; m0 < n; m0 += GR) {
+      const int idc = idn;
+      if (m0 + GR < n) idn = (m0 + GR + lane < n && lane < GR) ? ids[m0 + GR + lane] : 0;
+      const int cnt = n - m0 < GR ? n - m0 : GR;
+      UpdRow<KT> x[GR];
 #pragma unroll
-      for (int u = 0; u < U; ++u) load4(Kh + (size_t)ids[m + u] * D, x[u]);
+      for (int u = 0; u < GR; ++u)
+        if (u < cnt) x[u].load(Kh + (size_t)__builtin_amdgcn_readlane(idc, u) * D);
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] += (double)x[u][i];
+      for (int u = 0; u < GR; ++u)
+        if (u < cnt) {
+          a0 += (double)x[u].a();
+          a1 += (double)x[u].b();
+        }
     }
-    for (; m < n; ++m) {
-      float x[4];
-      load4(Kh + (size_t)ids[m] * D, x);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] += (double)x[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = (float)(a[i] / (double)n);
-    *reinterpret_cast<f32x4*>(cr + 4 * hl) = f32x4{c[0], c[1], c[2], c[3]};
-    float* t = cent_t + (size_t)h * C * D + ((size_t)hl * C + k) * 4;  // chunk hl of cluster k
-    *reinterpret_cast<f32x4*>(t) = f32x4{c[0], c[1], c[2], c[3]};
+    c0 = (float)(a0 / (double)n);
+    c1 = (float)(a1 / (double)n);
+    store_centroid(cr, cent_t + (size_t)h * C * D, C, k, c0, c1);
   } else {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(cr + 4 * hl);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = v[i];
+    c0 = cr[2 * lane];
+    c1 = cr[2 * lane + 1];
   }
-  normalize_rows2(c, &rows[w][0][0], active, chat + ((size_t)h * cpad + (active ? k : 0)) * D);
+  normalize_row(c0, c1, rows[w], chat + ((size_t)h * cpad + k) * D);
 }
 
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, size_t n, int32_t v) {
@@ -696,7 +695,7 @@ hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, 
 hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cpad,
                          const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
                          float* cent, float* cent_t, void* chat, hipStream_t st) {
-  dim3 grid(grid1(C, 8), heads);
+  dim3 grid(grid1(C, 4), heads);
   if (dtype == DT_BF16)
     update_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, C, cpad, sizes, offsets,
                                                   token_ids, ids_stride, cent, cent_t, (uint16_t*)chat);
