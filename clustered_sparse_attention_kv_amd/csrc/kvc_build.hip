@@ -501,7 +501,7 @@ template <typename KT>
 struct UpdRow;  // one row's two channels as loaded
 template <>
 struct UpdRow<uint16_t> {
-  static constexpr int GROUP = 64;
+  static constexpr int GROUP = 32;
   uint32_t v;
   __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint32_t*>(p); }
   __device__ __forceinline__ float a() const { return __uint_as_float(v << 16); }
@@ -529,18 +529,17 @@ __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys
   const int h = blockIdx.y;
   const int k = blockIdx.x * 4 + w;
   if (k >= C) return;
-  const int n = sizes[(size_t)h * C + k];
-  const int off = offsets[(size_t)h * (C + 1) + k];
+  // the same value in every lane: scalar registers, uniform branches
+  const int n = __builtin_amdgcn_readfirstlane(sizes[(size_t)h * C + k]);
+  const int off = __builtin_amdgcn_readfirstlane(offsets[(size_t)h * (C + 1) + k]);
   const int32_t* ids = token_ids + (size_t)h * ids_stride + off;
   const KT* Kh = keys + (size_t)h * head_stride + 2 * lane;
   float* cr = cent + ((size_t)h * C + k) * D;
   float c0, c1;
   if (n > 0) {
     double a0 = 0.0, a1 = 0.0;
-    int idn = lane < n && lane < GR ? ids[lane] : 0;
-    for (int m0 = 0; m0 < n; m0 += GR) {
-      const int idc = idn;
-      if (m0 + GR < n) idn = (m0 + GR + lane < n && lane < GR) ? ids[m0 + GR + lane] : 0;
+    auto load_ids = [&](int m0) { return m0 + lane < n && lane < GR ? ids[m0 + lane] : 0; };
+    auto sum_group = [&](int m0, int idc) {
       const int cnt = n - m0 < GR ? n - m0 : GR;
       UpdRow<KT> x[GR];
 #pragma unroll
@@ -552,6 +551,16 @@ __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys
           a0 += (double)x[u].a();
           a1 += (double)x[u].b();
         }
+    };
+    // groups of GR members, two id registers so the next group's ids are in
+    // flight while the current group's rows are loaded and summed
+    int idA = load_ids(0), idB = 0;
+    for (int m0 = 0; m0 < n; m0 += 2 * GR) {
+      if (m0 + GR < n) idB = load_ids(m0 + GR);
+      sum_group(m0, idA);
+      if (m0 + GR >= n) break;
+      if (m0 + 2 * GR < n) idA = load_ids(m0 + 2 * GR);
+      sum_group(m0 + GR, idB);
     }
     c0 = (float)(a0 / (double)n);
     c1 = (float)(a1 / (double)n);

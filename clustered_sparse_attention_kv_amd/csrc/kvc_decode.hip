@@ -550,7 +550,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
   constexpr int VR = 64 / RPS;               // value rows per lane per slice
   __shared__ SelShared S;
   __shared__ int sel[EMIT];
-  __shared__ float pw[NW][G][64];            // wave-private: scores, then weights, of the current slice
+  constexpr int GP = G < 4 ? 4 : G;          // floats per token in pw (16-byte rows)
+  __shared__ __align__(16) float pw[NW][64][GP];  // wave-private: scores, then weights, token-major
   __shared__ float ored[NW][G][HC];
   __shared__ float wm[NW][G], wl[NW][G];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -580,6 +581,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     if (j16 < G) v = *reinterpret_cast<const u32x4*>(q + ((size_t)h * G + j16) * D + 32 * s + 8 * kb4);
     qb[s] = __builtin_bit_cast(bf16x8, v);
   }
+  // per query head: the wave's running maximum (uniform), this lane's share
+  // of the sum of weights, and the partial output of this lane's channels
   float o[G][8], m_run[G], l_run[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -622,30 +625,47 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[T][s], qb[s], acc[T], 0, 0, 0);
-      // score of (row 16 T + 4 (lane / 16) + r, query head lane % 16) -> pw[w][g][row]
+      // score of (row 16 T + 4 (lane / 16) + r, query head lane % 16) -> pw[w][row][g]
       if (j16 < G) {
 #pragma unroll
         for (int T = 0; T < 4; ++T)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int t = T * 16 + 4 * kb4 + r;
-            pw[w][j16][t] = t < n64 ? acc[T][r] * qscale : -INFINITY;
+            pw[w][t][j16] = t < n64 ? acc[T][r] * qscale : -INFINITY;
           }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // lane = token of the slice: its G scores become weights. The running
+      // maximum moves (and the partial results are rescaled) only when the
+      // slice holds a larger score; the sums stay per lane until the end.
+      {
+        float sv[GP];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float sv = pw[w][g][lane];
-        const float mnew = fmaxf(m_run[g], wave_max(sv));
-        const float f = m_run[g] == -INFINITY ? 0.f : exp2f(m_run[g] - mnew);
-        const float pv = mnew == -INFINITY ? 0.f : exp2f(sv - mnew);
-        pw[w][g][lane] = pv;
-        l_run[g] = l_run[g] * f + wave_sum(pv);
-        m_run[g] = mnew;
+        for (int g4 = 0; g4 < GP; g4 += 4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&pw[w][lane][g4]);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[g][c] *= f;
+          for (int i = 0; i < 4; ++i) sv[g4 + i] = x[i];
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float smax = wave_max(sv[g]);
+          if (smax > m_run[g]) {  // uniform over the wave
+            const float f = m_run[g] == -INFINITY ? 0.f : exp2f(m_run[g] - smax);
+            l_run[g] *= f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) o[g][c] *= f;
+            m_run[g] = smax;
+          }
+          const float pv = m_run[g] == -INFINITY ? 0.f : exp2f(sv[g] - m_run[g]);
+          sv[g] = pv;
+          l_run[g] += pv;
+        }
+#pragma unroll
+        for (int g4 = 0; g4 < GP; g4 += 4)
+          *reinterpret_cast<f32x4*>(&pw[w][lane][g4]) = f32x4{sv[g4], sv[g4 + 1], sv[g4 + 2], sv[g4 + 3]};
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -653,12 +673,17 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < VR; ++r) {
         const int t = r * RPS + vgrp;
+        float pv[GP];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float pv = pw[w][g][t];
+        for (int g4 = 0; g4 < GP; g4 += 4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&pw[w][t][g4]);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) o[g][c] = fmaf(pv, vrow[r].at(c), o[g][c]);
+          for (int i = 0; i < 4; ++i) pv[g4 + i] = x[i];
         }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o[g][c] = fmaf(pv[g], vrow[r].at(c), o[g][c]);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -681,8 +706,11 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
 #pragma unroll
       for (int c = 0; c < 8; ++c) ored[w][g][8 * vgl + c] = o[g][c];
   }
+#pragma unroll
+  for (int g = 0; g < G; ++g) l_run[g] = wave_sum(l_run[g]);
   if (lane < G) {
-    // every lane holds the same running state; lane g publishes head g's
+    // the running maximum and the reduced sum are the same in every lane;
+    // lane g publishes head g's
 #pragma unroll
     for (int g = 0; g < G; ++g)
       if (g == lane) {
