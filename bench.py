@@ -112,6 +112,8 @@ def main():
     ap.add_argument("--decode-path", choices=["fused", "split"], default="fused",
                     help="fused: kv_cluster_select_decode (one kernel per step); "
                          "split: kv_cluster_select then kv_sparse_decode")
+    ap.add_argument("--no-pack", action="store_true",
+                    help="decode from the caches through the token ids (no cluster-ordered copy)")
     ap.add_argument("--cpu-heads", type=int, default=16, help="KV heads in the CPU baseline sample")
     ap.add_argument("--cpu-steps", type=int, default=32, help="decode steps in the CPU baseline sample")
     args = ap.parse_args()
@@ -173,7 +175,8 @@ def main():
         Knew = to_dev(np.ascontiguousarray(K[:, L:].transpose(1, 0, 2)))  # [steps, H, d]
         Vnew = to_dev(np.ascontiguousarray(V[:, L:].transpose(1, 0, 2)))
     del K, V, Kp, Vp
-    idx = kvc.ClusterIndex(H, C, cap, tdt, device=dev)
+    packed = not args.no_pack and args.decode_path == "fused"
+    idx = kvc.ClusterIndex(H, C, cap, tdt, device=dev, packed=packed)
     ws_build = torch.empty(kvc.build_workspace_bytes(H, L, C, w.iters), dtype=torch.uint8, device=dev)
     ws_dec = torch.empty(kvc.decode_workspace_bytes(H, H * G, B), dtype=torch.uint8, device=dev)
     fused = args.decode_path == "fused"
@@ -191,12 +194,12 @@ def main():
     del cal_src, cal_dst
 
     # events per pass: 2*iters around the assignment kernels inside the build,
-    # 3 bracketing the build and the decode phase, and, on every SAMPLE-th
-    # decode step only (events between kernels add dispatch gaps), 6 around
-    # that step's kernels (append, select, decode)
+    # 3 bracketing the build and the decode phase, 1 after the packed copy,
+    # and, on every SAMPLE-th decode step only (events between kernels add
+    # dispatch gaps), 6 around that step's kernels (append, select, decode)
     SAMPLE = 8
     sampled = [s for s in range(w.steps) if s % SAMPLE == 0]
-    per_pass = 2 * w.iters + 3 + 6 * len(sampled)
+    per_pass = 2 * w.iters + 4 + 6 * len(sampled)
     total_passes = args.warmup + args.steps
     ev = HipEvents(per_pass * total_passes + 2)
 
@@ -204,8 +207,11 @@ def main():
         o = p * per_pass
         ev.record(o + 2 * w.iters, sh)
         kvc.build(idx, Kd, L, w.iters, init_d, workspace=ws_build, assign_events=ev.sub(o, 2 * w.iters))
+        ev.record(o + 2 * w.iters + 3, sh)
+        if packed:
+            kvc.pack(idx, Kd, Vd)
         ev.record(o + 2 * w.iters + 1, sh)
-        b = o + 2 * w.iters + 3
+        b = o + 2 * w.iters + 4
         for s in range(w.steps):
             e6 = b + 6 * (s // SAMPLE) if s % SAMPLE == 0 else None
             rec = (lambda i: ev.record(e6 + i, sh)) if e6 is not None else (lambda i: None)
@@ -236,13 +242,14 @@ def main():
     wall = time.perf_counter() - t_start
     total_ms = ev.ms(per_pass * total_passes, per_pass * total_passes + 1)
 
-    assign_ms, build_ms, select_ms, decode_ms, append_ms, phase_ms = [], [], [], [], [], []
+    assign_ms, build_ms, select_ms, decode_ms, append_ms, phase_ms, pack_ms = [], [], [], [], [], [], []
     for p in range(args.warmup, total_passes):
         o = p * per_pass
         assign_ms += [ev.ms(o + 2 * t, o + 2 * t + 1) for t in range(w.iters)]
-        build_ms.append(ev.ms(o + 2 * w.iters, o + 2 * w.iters + 1))
+        build_ms.append(ev.ms(o + 2 * w.iters, o + 2 * w.iters + 3))
+        pack_ms.append(ev.ms(o + 2 * w.iters + 3, o + 2 * w.iters + 1))
         phase_ms.append(ev.ms(o + 2 * w.iters + 1, o + 2 * w.iters + 2))
-        b = o + 2 * w.iters + 3
+        b = o + 2 * w.iters + 4
         for i in range(len(sampled)):
             e6 = b + 6 * i
             if w.append:
@@ -311,9 +318,10 @@ def main():
         "data": "synthetic (seeded Gaussian-mixture keys with outlier channels, N(0,1) values)",
         "config": {"workload": w.name, "kv_heads_total": H, "q_heads_total": H * G, "G": G, "L": L, "d": d, "C": C,
                    "kmeans_iters": w.iters, "B": B, "decode_steps_per_step": w.steps, "append": w.append,
-                   "decode_path": args.decode_path},
+                   "decode_path": args.decode_path, "packed_kv": packed},
         "kmeans_tflops": kmeans_tflops,
         "kmeans_ms": mean(build_ms),
+        "pack_ms": mean(pack_ms),
         "decode_step_us": step_ms * 1e3,
         "decode_step_hbm_frac": alg["step_bytes"] / (step_ms / 1e3) / PEAK_HBM,
         "kernel_timing": f"HIP events around every kernel of 1 in {SAMPLE} decode steps and around every "

@@ -32,11 +32,11 @@ class KvcError(RuntimeError):
 
 class _Index(C.Structure):
     _fields_ = [("heads", C.c_int32), ("d", C.c_int32), ("C", C.c_int32), ("capacity", C.c_int32),
-                ("dtype", C.c_int32), ("n_build", C.c_int32), ("n_tokens", C.c_int32), ("reserved", C.c_int32),
+                ("dtype", C.c_int32), ("n_build", C.c_int32), ("n_tokens", C.c_int32), ("packed", C.c_int32),
                 ("centroids", C.c_void_p), ("centroids_op", C.c_void_p), ("labels", C.c_void_p),
                 ("sizes", C.c_void_p), ("offsets", C.c_void_p), ("token_ids", C.c_void_p),
                 ("app_offsets", C.c_void_p), ("app_ids", C.c_void_p), ("dev_flags", C.c_void_p),
-                ("centroids_t", C.c_void_p)]
+                ("centroids_t", C.c_void_p), ("k_packed", C.c_void_p), ("v_packed", C.c_void_p)]
 
 
 def lib():
@@ -60,12 +60,14 @@ def lib():
         L.kv_sparse_decode.argtypes = [p, i, p, p, i, i, i, i, p, p, i, f, p, p, sz, p]
         L.kv_cluster_select_decode.argtypes = [p, p, i, p, p, i, f, p, p, p, p]
         L.kv_cluster_export_csr.argtypes = [p, p, p, p]
+        L.kv_cluster_pack.argtypes = [p, p, p, p]
         L.kv_cluster_debug_assign.argtypes = [p, p, i, p, p, p, p, p, sz, p]
         L.kv_cluster_debug_update.argtypes = [p, p, i, p, sz, p]
         L.kv_cluster_status_string.argtypes = [i]
         L.kv_cluster_status_string.restype = C.c_char_p
         for name in ("kv_cluster_build", "kv_cluster_build_timed", "kv_cluster_append", "kv_cluster_select", "kv_sparse_decode",
-                     "kv_cluster_select_decode", "kv_cluster_export_csr", "kv_cluster_debug_assign", "kv_cluster_debug_update"):
+                     "kv_cluster_select_decode", "kv_cluster_export_csr", "kv_cluster_pack", "kv_cluster_debug_assign",
+                     "kv_cluster_debug_update"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -124,7 +126,9 @@ class ClusterIndex:
     """Device memory of one cluster index (``kvc_index``), allocated with torch."""
 
     def __init__(self, heads: int, C_: int, capacity: int, dtype: torch.dtype = torch.bfloat16,
-                 d: int = HEAD_DIM, device="cuda"):
+                 d: int = HEAD_DIM, device="cuda", packed: bool = False):
+        """packed: also allocate the cluster-ordered copies of the keys and
+        values (``kv_cluster_pack``), two more arrays of the caches' size."""
         self.heads, self.C, self.capacity, self.d, self.dtype = heads, C_, capacity, d, dtype
         i32 = dict(dtype=torch.int32, device=device)
         self.centroids = torch.zeros(heads, C_, d, dtype=torch.float32, device=device)
@@ -137,11 +141,15 @@ class ClusterIndex:
         self.app_ids = torch.full((heads, capacity), -1, **i32)
         self.dev_flags = torch.zeros(1, **i32)
         self.centroids_t = torch.zeros(heads, d // 4, C_, 4, dtype=torch.float32, device=device)
+        self.k_packed = torch.empty(heads, capacity, d, dtype=dtype, device=device) if packed else None
+        self.v_packed = torch.empty(heads, capacity, d, dtype=dtype, device=device) if packed else None
         self._s = _Index(heads, d, C_, capacity, _dtype_code(dtype), 0, 0, 0,
                          self.centroids.data_ptr(), self.centroids_op.data_ptr(), self.labels.data_ptr(),
                          self.sizes.data_ptr(), self.offsets.data_ptr(), self.token_ids.data_ptr(),
                          self.app_offsets.data_ptr(), self.app_ids.data_ptr(), self.dev_flags.data_ptr(),
-                         self.centroids_t.data_ptr())
+                         self.centroids_t.data_ptr(),
+                         self.k_packed.data_ptr() if packed else None,
+                         self.v_packed.data_ptr() if packed else None)
 
     @property
     def n_build(self) -> int:
@@ -255,6 +263,16 @@ def select_decode(idx: ClusterIndex, q: torch.Tensor, k_cache: torch.Tensor, v_c
                                           float(scale), _ptr(out), _ptr(sel_ids), _ptr(sel_count), _stream(stream)),
            "kv_cluster_select_decode")
     return out
+
+
+def pack(idx: ClusterIndex, k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None):
+    """kv_cluster_pack: cluster-ordered copies of the built tokens' rows (the
+    index must have been created with packed=True)."""
+    _cache_check(idx, k_cache, "k_cache")
+    _cache_check(idx, v_cache, "v_cache")
+    if idx.k_packed is None:
+        raise ValueError("the index has no packed arrays (create it with packed=True)")
+    _check(lib().kv_cluster_pack(idx.ref(), _ptr(k_cache), _ptr(v_cache), _stream(stream)), "kv_cluster_pack")
 
 
 def export_csr(idx: ClusterIndex, stream=None):

@@ -75,6 +75,7 @@ int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, c
   if (ws_bytes < w.bytes) return KVC_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const long long hs = (long long)cap * KVC_HEAD_DIM;
+  idx->packed = 0;  // the index changes: any packed copy is stale
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.qcount), (size_t)iters * H, 0, st);
   if (e == hipSuccess) e = launch_fill_i32(idx->app_offsets, (size_t)H * (C + 1), 0, st);
   if (e == hipSuccess)
@@ -122,6 +123,7 @@ int kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, s
   const BuildWs w = carve_build(ws, H, L, C, 1);
   if (ws_bytes < w.bytes) return KVC_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  idx->packed = 0;  // the index changes: any packed copy is stale
   hipError_t e = launch_csr(idx->labels, cap, H, L, C, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, st);
   if (e == hipSuccess)
     e = launch_update(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, C, cpad, idx->sizes, idx->offsets,
@@ -190,10 +192,22 @@ int kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, c
   const int G = q_heads / idx->heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVC_ERR_UNSUPPORTED;
   if ((long long)idx->heads * B >= (1ll << 31)) return KVC_ERR_INVALID_ARG;
+  const bool packed = idx->packed == 1 && idx->k_packed && idx->v_packed;
   return hip_status(launch_select_decode(idx->dtype, q, G, idx->centroids_t, idx->heads, idx->C, idx->sizes,
                                          idx->offsets, idx->token_ids, idx->app_offsets, idx->app_ids, idx->capacity,
-                                         k_cache, v_cache, B, scale, out, sel_ids, sel_count,
+                                         k_cache, v_cache, packed ? idx->k_packed : nullptr,
+                                         packed ? idx->v_packed : nullptr, B, scale, out, sel_ids, sel_count,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, void* stream) {
+  if (!index_ok(idx) || !k_cache || !v_cache || !idx->k_packed || !idx->v_packed) return KVC_ERR_INVALID_ARG;
+  if (int s = index_support(idx)) return s;
+  if (idx->n_build < 1) return KVC_ERR_INVALID_ARG;
+  const int e = hip_status(launch_pack(idx->dtype, k_cache, v_cache, idx->capacity, idx->heads, idx->token_ids,
+                                       idx->n_build, idx->k_packed, idx->v_packed, static_cast<hipStream_t>(stream)));
+  if (e == KVC_OK) idx->packed = 1;
+  return e;
 }
 
 int kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token_ids, void* stream) {

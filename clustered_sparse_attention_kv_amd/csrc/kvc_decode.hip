@@ -240,9 +240,12 @@ __device__ __forceinline__ void select_phase(SelShared& S, const QT* __restrict_
   __syncthreads();
 }
 
-// Token at output position p (< total) of the ranked, trimmed selection.
+// Entry at output position p (< total) of the ranked, trimmed selection:
+// the token id, or with a packed copy (packed = true) the row of the copy for
+// a built member (its position in the index, offset + member) and ~token for
+// a token appended after the build.
 __device__ __forceinline__ int select_emit(const SelShared& S, int p, const int32_t* __restrict__ ids_h,
-                                           const int32_t* __restrict__ app_h) {
+                                           const int32_t* __restrict__ app_h, bool packed = false) {
   int lo = 0, hi = SEL_THREADS - 1;  // last r with W[r] <= p
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -251,7 +254,22 @@ __device__ __forceinline__ int select_emit(const SelShared& S, int p, const int3
   }
   const int e = p - S.W[lo];
   const int nb = S.nbase[lo];
-  return e < nb ? ids_h[S.obase[lo] + e] : app_h[S.abase[lo] + (e - nb)];
+  if (e < nb) return packed ? S.obase[lo] + e : ids_h[S.obase[lo] + e];
+  const int a = app_h[S.abase[lo] + (e - nb)];
+  return packed ? ~a : a;
+}
+
+// Row of a staged selection entry: a row of the packed copy (id >= 0) or the
+// cache row ~id of an appended token (id < 0). Without a packed copy the
+// entries are token ids and both bases are the cache.
+template <typename KT>
+__device__ __forceinline__ const KT* sel_row(const KT* packed_h, const KT* cache_h, int id) {
+  return id >= 0 ? packed_h + (size_t)id * D : cache_h + (size_t)(~id) * D;
+}
+
+// Token id of a staged selection entry (for the optional copy of the selection).
+__device__ __forceinline__ int sel_token(const int32_t* __restrict__ ids_h, int id, bool packed) {
+  return packed ? (id >= 0 ? ids_h[id] : ~id) : id;
 }
 
 template <typename QT>
@@ -350,8 +368,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
     const KT* __restrict__ q, const float* __restrict__ cent_t, int C, const int32_t* __restrict__ sizes,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ token_ids,
     const int32_t* __restrict__ app_offsets, const int32_t* __restrict__ app_ids, long long cap,
-    const KT* __restrict__ kc, const KT* __restrict__ vc, int B, float qscale, float* __restrict__ out,
-    int32_t* __restrict__ sel_ids, int32_t* __restrict__ sel_count) {
+    const KT* __restrict__ kc, const KT* __restrict__ vc, const KT* __restrict__ kp, const KT* __restrict__ vp,
+    int packed, int B, float qscale, float* __restrict__ out, int32_t* __restrict__ sel_ids,
+    int32_t* __restrict__ sel_count) {
   constexpr int NW = SEL_THREADS / WAVE;                       // 8 waves
   constexpr int RS = (G <= 4 && sizeof(KT) == 2) ? 16 : (G <= 2 ? 8 : 4);  // row steps per load batch
   constexpr int NB = 16 / RS;                                  // batches per chunk
@@ -372,6 +391,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
   const int32_t* app_h = app_ids + (size_t)h * cap;
   const KT* Kh = kc + (size_t)h * cap * D + 8 * gl;
   const KT* Vh = vc + (size_t)h * cap * D + 8 * gl;
+  const KT* Kph = kp + (size_t)h * cap * D + 8 * gl;
+  const KT* Vph = vp + (size_t)h * cap * D + 8 * gl;
 
   float qv[G][8];
 #pragma unroll
@@ -394,9 +415,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
     const int nchunk = cnt - c0 < SEL_THREADS ? cnt - c0 : SEL_THREADS;
     {
       const int p = c0 + tid;
-      const int tok = tid < nchunk ? select_emit(S, p, ids_h, app_h) : -1;
-      sel[tid] = tok;
-      if (sel_ids && tid < nchunk) sel_ids[(size_t)h * B + p] = tok;
+      const int ent = tid < nchunk ? select_emit(S, p, ids_h, app_h, packed) : 0;
+      sel[tid] = ent;
+      if (sel_ids && tid < nchunk) sel_ids[(size_t)h * B + p] = sel_token(ids_h, ent, packed);
     }
     __syncthreads();
     Row8<KT> vrow[V_EARLY ? RS : 1];
@@ -407,8 +428,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
       for (int r = 0; r < RS; ++r) {
         const int t = w * 64 + (b * RS + r) * 4 + grp;
         const int id = t < nchunk ? sel[t] : 0;
-        krow[r].load(Kh + (size_t)id * D);
-        if constexpr (V_EARLY) vrow[r].load(Vh + (size_t)id * D);
+        krow[r].load(sel_row(Kph, Kh, id));
+        if constexpr (V_EARLY) vrow[r].load(sel_row(Vph, Vh, id));
       }
 #pragma unroll
       for (int r = 0; r < RS; ++r) {
@@ -471,7 +492,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
         for (int r = 0; r < RS; ++r) {
           const int t = w * 64 + (b * RS + r) * 4 + grp;
           const int id = t < nchunk ? sel[t] : 0;
-          vb[r].load(Vh + (size_t)id * D);
+          vb[r].load(sel_row(Vph, Vh, id));
         }
       }
 #pragma unroll
@@ -540,8 +561,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ cent_t, int C, const int32_t* __restrict__ sizes,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ token_ids,
     const int32_t* __restrict__ app_offsets, const int32_t* __restrict__ app_ids, long long cap,
-    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int heads, int B, float qscale,
-    float* __restrict__ out, int32_t* __restrict__ sel_ids, int32_t* __restrict__ sel_count) {
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, const uint16_t* __restrict__ kp,
+    const uint16_t* __restrict__ vp, int packed, int heads, int B, float qscale, float* __restrict__ out,
+    int32_t* __restrict__ sel_ids, int32_t* __restrict__ sel_count) {
   static_assert(G <= 8, "at most 8 query heads per KV head");
   constexpr int NW = SEL_THREADS / WAVE;
   constexpr int EMIT = 2048;                 // selected ids staged per pass
@@ -571,6 +593,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
   const int32_t* app_h = app_ids + (size_t)h * cap;
   const uint16_t* Kh = kc + (size_t)h * cap * D + 8 * kb4;
   const uint16_t* Vh = vc + (size_t)h * cap * D + HC * part + 8 * vgl;
+  const uint16_t* Kph = kp + (size_t)h * cap * D + 8 * kb4;
+  const uint16_t* Vph = vp + (size_t)h * cap * D + HC * part + 8 * vgl;
 
   // queries as the B operand: column = query head (lane % 16 < G), k-step s
   // holds channels 32 s + 8 (lane / 16) .. + 7
@@ -596,9 +620,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     const int nb = cnt - base < EMIT ? cnt - base : EMIT;
     if (base > 0) __syncthreads();  // every wave is done with the previous ids
     for (int p = tid; p < nb; p += SEL_THREADS) {
-      const int tok = select_emit(S, base + p, ids_h, app_h);
-      sel[p] = tok;
-      if (writer && sel_ids) sel_ids[(size_t)h * B + base + p] = tok;
+      const int ent = select_emit(S, base + p, ids_h, app_h, packed);
+      sel[p] = ent;
+      if (writer && sel_ids) sel_ids[(size_t)h * B + base + p] = sel_token(ids_h, ent, packed);
     }
     __syncthreads();
     for (int t0 = w * 64; t0 < nb; t0 += NW * 64) {
@@ -608,7 +632,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
       for (int T = 0; T < 4; ++T) {
         const int t = T * 16 + j16;
         const int id = t < n64 ? sel[t0 + t] : 0;
-        const uint16_t* src = Kh + (size_t)id * D;
+        const uint16_t* src = sel_row(Kph, Kh, id);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           ka[T][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 32 * s));
@@ -618,7 +642,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
       for (int r = 0; r < VR; ++r) {
         const int t = r * RPS + vgrp;
         const int id = t < n64 ? sel[t0 + t] : 0;
-        vrow[r].load(Vh + (size_t)id * D);
+        vrow[r].load(sel_row(Vph, Vh, id));
       }
       f32x4 acc[4] = {};
 #pragma unroll
@@ -894,6 +918,28 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------------------
+// Packed copy of the built tokens' key and value rows in index order: row i of
+// head h is the cache row token_ids[h][i] (i < n). 16 bytes per lane, one row
+// per D * sizeof(KT) / 16 lanes.
+template <typename KT>
+__global__ __launch_bounds__(256) void pack_kernel(const KT* __restrict__ kc, const KT* __restrict__ vc, long long cap,
+                                                   const int32_t* __restrict__ token_ids, int n,
+                                                   KT* __restrict__ kp, KT* __restrict__ vp) {
+  constexpr int LPR = D * (int)sizeof(KT) / 16;  // lanes per row
+  constexpr int RPB = 256 / LPR;                 // rows per block and pass
+  const int h = blockIdx.y;
+  const int l = threadIdx.x % LPR, rr = threadIdx.x / LPR;
+  const size_t hb = (size_t)h * cap;
+  for (int i = blockIdx.x * RPB + rr; i < n; i += gridDim.x * RPB) {
+    const size_t src = (hb + (size_t)token_ids[hb + i]) * D, dst = (hb + (size_t)i) * D;
+    const u32x4 k = reinterpret_cast<const u32x4*>(kc + src)[l];
+    const u32x4 v = reinterpret_cast<const u32x4*>(vc + src)[l];
+    reinterpret_cast<u32x4*>(kp + dst)[l] = k;
+    reinterpret_cast<u32x4*>(vp + dst)[l] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Canonical index (built + appended parts merged), one block per head.
 __global__ __launch_bounds__(256) void export_csr_kernel(int C, const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ token_ids,
@@ -944,31 +990,40 @@ hipError_t launch_select(int dtype, const void* q, int G, const float* cent, int
   return hipGetLastError();
 }
 
+struct FusedArgs {
+  const void* q;
+  const float* cent;
+  int heads, C;
+  const int32_t *sizes, *offsets, *token_ids, *app_offsets, *app_ids;
+  long long cap;
+  const void *kc, *vc, *kp, *vp;  // kp, vp: packed copies, or the caches when not packed
+  int packed, B;
+  float qscale;
+  float* out;
+  int32_t *sel_ids, *sel_count;
+};
+
 template <typename KT, int G>
-static void launch_fused(const void* q, const float* cent, int heads, int C, const int32_t* sizes,
-                         const int32_t* offsets, const int32_t* token_ids, const int32_t* app_offsets,
-                         const int32_t* app_ids, long long cap, const void* kc, const void* vc, int B, float qscale,
-                         float* out, int32_t* sel_ids, int32_t* sel_count, hipStream_t st) {
+static void launch_fused(const FusedArgs& a, hipStream_t st) {
   if constexpr (sizeof(KT) == 2)
-    select_decode_bf16_kernel<G><<<(heads + 7) / 8 * 8 * DEC_PARTS, SEL_THREADS, 0, st>>>(
-        (const uint16_t*)q, cent, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, (const uint16_t*)kc,
-        (const uint16_t*)vc, heads, B, qscale, out, sel_ids, sel_count);
+    select_decode_bf16_kernel<G><<<(a.heads + 7) / 8 * 8 * DEC_PARTS, SEL_THREADS, 0, st>>>(
+        (const uint16_t*)a.q, a.cent, a.C, a.sizes, a.offsets, a.token_ids, a.app_offsets, a.app_ids, a.cap,
+        (const uint16_t*)a.kc, (const uint16_t*)a.vc, (const uint16_t*)a.kp, (const uint16_t*)a.vp, a.packed,
+        a.heads, a.B, a.qscale, a.out, a.sel_ids, a.sel_count);
   else
-    select_decode_kernel<KT, G><<<heads, SEL_THREADS, 0, st>>>((const KT*)q, cent, C, sizes, offsets, token_ids,
-                                                               app_offsets, app_ids, cap, (const KT*)kc,
-                                                               (const KT*)vc, B, qscale, out, sel_ids, sel_count);
+    select_decode_kernel<KT, G><<<a.heads, SEL_THREADS, 0, st>>>(
+        (const KT*)a.q, a.cent, a.C, a.sizes, a.offsets, a.token_ids, a.app_offsets, a.app_ids, a.cap,
+        (const KT*)a.kc, (const KT*)a.vc, (const KT*)a.kp, (const KT*)a.vp, a.packed, a.B, a.qscale, a.out,
+        a.sel_ids, a.sel_count);
 }
 
 template <typename KT>
-static hipError_t fused_dispatch(int G, const void* q, const float* cent, int heads, int C, const int32_t* sizes,
-                                 const int32_t* offsets, const int32_t* token_ids, const int32_t* app_offsets,
-                                 const int32_t* app_ids, long long cap, const void* kc, const void* vc, int B,
-                                 float qscale, float* out, int32_t* sel_ids, int32_t* sel_count, hipStream_t st) {
+static hipError_t fused_dispatch(int G, const FusedArgs& a, hipStream_t st) {
   switch (G) {
-    case 1: launch_fused<KT, 1>(q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc, vc, B, qscale, out, sel_ids, sel_count, st); break;
-    case 2: launch_fused<KT, 2>(q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc, vc, B, qscale, out, sel_ids, sel_count, st); break;
-    case 4: launch_fused<KT, 4>(q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc, vc, B, qscale, out, sel_ids, sel_count, st); break;
-    case 8: launch_fused<KT, 8>(q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc, vc, B, qscale, out, sel_ids, sel_count, st); break;
+    case 1: launch_fused<KT, 1>(a, st); break;
+    case 2: launch_fused<KT, 2>(a, st); break;
+    case 4: launch_fused<KT, 4>(a, st); break;
+    case 8: launch_fused<KT, 8>(a, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -977,14 +1032,13 @@ static hipError_t fused_dispatch(int G, const void* q, const float* cent, int he
 hipError_t launch_select_decode(int dtype, const void* q, int G, const float* cent, int heads, int C,
                                 const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids,
                                 const int32_t* app_offsets, const int32_t* app_ids, long long cap, const void* kc,
-                                const void* vc, int B, float scale, float* out, int32_t* sel_ids,
-                                int32_t* sel_count, hipStream_t st) {
-  const float qscale = scale * 1.4426950408889634f;
-  if (dtype == DT_BF16)
-    return fused_dispatch<uint16_t>(G, q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc,
-                                    vc, B, qscale, out, sel_ids, sel_count, st);
-  return fused_dispatch<float>(G, q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc, vc, B,
-                               qscale, out, sel_ids, sel_count, st);
+                                const void* vc, const void* kp, const void* vp, int B, float scale, float* out,
+                                int32_t* sel_ids, int32_t* sel_count, hipStream_t st) {
+  FusedArgs a{q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc, vc,
+              kp ? kp : kc, vp ? vp : vc, kp && vp ? 1 : 0, B, scale * 1.4426950408889634f, out, sel_ids,
+              sel_count};
+  if (dtype == DT_BF16) return fused_dispatch<uint16_t>(G, a, st);
+  return fused_dispatch<float>(G, a, st);
 }
 
 template <typename KT>
@@ -1021,6 +1075,18 @@ hipError_t launch_export_csr(int heads, int C, const int32_t* offsets, const int
                              const int32_t* app_offsets, const int32_t* app_ids, long long cap, int32_t* out_offsets,
                              int32_t* out_ids, hipStream_t st) {
   export_csr_kernel<<<heads, 256, 0, st>>>(C, offsets, token_ids, app_offsets, app_ids, cap, out_offsets, out_ids);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(int dtype, const void* kc, const void* vc, long long cap, int heads, const int32_t* token_ids,
+                       int n, void* kp, void* vp, hipStream_t st) {
+  const int bx = (n + 15) / 16 < 64 ? (n + 15) / 16 : 64;
+  if (dtype == DT_BF16)
+    pack_kernel<uint16_t><<<dim3(bx, heads), 256, 0, st>>>((const uint16_t*)kc, (const uint16_t*)vc, cap, token_ids,
+                                                          n, (uint16_t*)kp, (uint16_t*)vp);
+  else
+    pack_kernel<float><<<dim3(bx, heads), 256, 0, st>>>((const float*)kc, (const float*)vc, cap, token_ids, n,
+                                                       (float*)kp, (float*)vp);
   return hipGetLastError();
 }
 

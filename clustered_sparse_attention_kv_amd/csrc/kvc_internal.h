@@ -39,8 +39,11 @@ hipError_t launch_decode(int dtype, const void* q, int G, const void* kc, const 
 hipError_t launch_select_decode(int dtype, const void* q, int G, const float* cent, int heads, int C,
                                 const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids,
                                 const int32_t* app_offsets, const int32_t* app_ids, long long cap, const void* kc,
-                                const void* vc, int B, float scale, float* out, int32_t* sel_ids,
-                                int32_t* sel_count, hipStream_t st);
+                                const void* vc, const void* kp, const void* vp, int B, float scale, float* out,
+                                int32_t* sel_ids, int32_t* sel_count, hipStream_t st);
+// kp, vp: the packed copies (both non-null) or null (rows from the caches).
+hipError_t launch_pack(int dtype, const void* kc, const void* vc, long long cap, int heads, const int32_t* token_ids,
+                       int n, void* kp, void* vp, hipStream_t st);
 hipError_t launch_export_csr(int heads, int C, const int32_t* offsets, const int32_t* token_ids,
                              const int32_t* app_offsets, const int32_t* app_ids, long long cap, int32_t* out_offsets,
                              int32_t* out_ids, hipStream_t st);

@@ -79,7 +79,8 @@ typedef struct kvc_index {
   int32_t dtype;    /* kvc_dtype of keys, queries and the centroid operand */
   int32_t n_build;  /* host mirror: tokens clustered by the last build */
   int32_t n_tokens; /* host mirror: n_build + tokens appended since */
-  int32_t reserved;
+  int32_t packed;   /* host mirror: 1 once kv_cluster_pack has filled k_packed/v_packed for
+                       the current build (kv_cluster_build resets it to 0) */
   float* centroids;       /* [heads, C, d] fp32: mean of each cluster's keys */
   void* centroids_op;     /* [heads, kv_cluster_cpad(C), d] unit-length centroids in `dtype`
                              (the assignment operand); rows >= C are zero */
@@ -92,6 +93,9 @@ typedef struct kvc_index {
   int32_t* dev_flags;     /* [1] error bits set by kernels (bit 0: an init index out of range) */
   float* centroids_t;     /* [heads, d/4, C, 4] fp32: the same centroids with 4-channel chunks
                              cluster-minor, written by the build and read by selection */
+  void* k_packed;         /* optional (NULL): [heads, capacity, d] in dtype; kv_cluster_pack writes
+                             the built tokens' key rows in index order (row i = token_ids[i]) */
+  void* v_packed;         /* optional (NULL): the value rows in the same order */
 } kvc_index;
 
 /* Rows of centroids_op per head: C rounded up to the matrix-core tile (32). */
@@ -182,9 +186,23 @@ int kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void
                      float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Cluster-ordered copy of the built tokens' keys and values: row i of head h
+ * of idx->k_packed / idx->v_packed becomes row token_ids[h][i] of k_cache /
+ * v_cache ([heads, capacity, d], idx->dtype), for i < idx->n_build. The
+ * members of each cluster then lie in consecutive rows, and
+ * kv_cluster_select_decode reads the selected built tokens from the copy
+ * (tokens appended later still come from the caches through the appended
+ * list). Sets idx->packed to 1; kv_cluster_build resets it. Costs a second
+ * copy of the built part of the caches. Requires a built index and both
+ * packed arrays; otherwise KVC_ERR_INVALID_ARG.
+ */
+int kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, void* stream);
+
+/*
  * kv_cluster_select followed by kv_sparse_decode in one kernel (one block per
  * KV head): the same selection and the same attention, without the selected
- * ids leaving the chip. k_cache and v_cache are [heads, idx->capacity, d] in
+ * ids leaving the chip. With idx->packed set, the selected built tokens are
+ * read from the packed copy (the same values, consecutive rows per cluster). k_cache and v_cache are [heads, idx->capacity, d] in
  * idx->dtype; q is [q_heads, d]; out is fp32 [q_heads, d]. sel_ids [heads, B]
  * and sel_count [heads] are optional (NULL) copies of the selection.
  * Requires G = q_heads / heads in {1, 2, 4, 8}. No workspace.

@@ -106,6 +106,14 @@ def test_append_select_decode_reject(kvc):
     assert dec(B=0) == INVALID
     assert dec(qh=32, B=4096 + 64, ws=1 << 40) == UNSUPPORTED   # 65 splits x 8 heads > 512 pairs
     assert L.kv_cluster_export_csr(C.byref(built), None, p, None) == INVALID
+    # packing needs both packed arrays and a built index
+    assert L.kv_cluster_pack(C.byref(built), p, p, None) == INVALID           # no packed arrays
+    unbuilt = make_index(kvc)
+    unbuilt.k_packed, unbuilt.v_packed = FAKE, FAKE
+    assert L.kv_cluster_pack(C.byref(unbuilt), p, p, None) == INVALID         # not built
+    withp = make_index(kvc, n_build=200, n_tokens=200)
+    withp.k_packed = FAKE
+    assert L.kv_cluster_pack(C.byref(withp), p, None, None) == INVALID        # no v_cache
 
 
 def test_binding_fails_loudly_without_library(kvc, monkeypatch):

@@ -89,7 +89,7 @@ def test_full_size_build_select_decode(cfg):
     w = synth.workload(cfg)
     say(f"[full size] {w.name}: {w.heads} heads x {w.L} keys, C={w.C}, B={w.B}")
     base, K, V, init, means = gen(w)
-    idx = kvc.ClusterIndex(w.heads, w.C, w.capacity, torch.bfloat16)
+    idx = kvc.ClusterIndex(w.heads, w.C, w.capacity, torch.bfloat16, packed=True)
     Kd, Vd = to_dev(K), to_dev(V)
     kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
     torch.cuda.synchronize()
@@ -100,6 +100,12 @@ def test_full_size_build_select_decode(cfg):
         q = queries(w, base, step, K, w.L, means)
         ferr, err = check_step(w, idx, K, V, Kd, Vd, q, w.B, scale)
         say(f"  step {step}: decode max abs err fused {ferr:.2e}, split {err:.2e}")
+    # the benchmark's configuration: the fused path reading the packed copy
+    kvc.pack(idx, Kd, Vd)
+    for step in (2, w.steps - 2):
+        q = queries(w, base, step, K, w.L, means)
+        ferr, _ = check_step(w, idx, K, V, Kd, Vd, q, w.B, scale, split=False)
+        say(f"  step {step} (packed): decode max abs err fused {ferr:.2e}")
 
 
 def test_full_size_append_workload():

@@ -40,8 +40,8 @@ def pad_op(chat: np.ndarray, cpad: int) -> np.ndarray:
     return out
 
 
-def built_gpu(w, K, init):
-    idx = kvc.ClusterIndex(K.shape[0], w.C, w.capacity, torch_dtype(w))
+def built_gpu(w, K, init, packed=False):
+    idx = kvc.ClusterIndex(K.shape[0], w.C, w.capacity, torch_dtype(w), packed=packed)
     Kd = to_dev(K)
     kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
     torch.cuda.synchronize()
@@ -113,7 +113,7 @@ def test_build_select_decode_end_to_end(case):
     say(f"[end to end] {case}")
     base, K, V, init, means = make_inputs(w)
     H = K.shape[0]
-    idx, Kd = built_gpu(w, K, init)
+    idx, Kd = built_gpu(w, K, init, packed=True)
     assert int(to_np(idx.dev_flags)[0]) == 0
     ref = oracle.build(np.ascontiguousarray(K[:, :w.L]), w.C, w.iters, init)
     gl = to_np(idx.labels)[:, :w.L]
@@ -138,27 +138,43 @@ def test_build_select_decode_end_to_end(case):
     Vd = to_dev(V)
     ws = torch.zeros(kvc.decode_workspace_bytes(H, H * w.G, max(w.B, 1)) + 4096, dtype=torch.uint8, device="cuda")
     scale = 1.0 / math.sqrt(w.d)
-    for step, B in enumerate([w.B, 1, 7, w.L + 50]):
-        q = queries(w, base, step, K, w.L, means)
-        sel, cnt = kvc.select(idx, to_dev(q), B)
-        ws_b = torch.zeros(kvc.decode_workspace_bytes(H, H * w.G, B), dtype=torch.uint8, device="cuda")
-        out = kvc.sparse_decode(to_dev(q), Kd, Vd, sel, cnt, scale, workspace=ws_b)
-        torch.cuda.synchronize()
-        osel, ocnt, _, _ = oracle.select(q, w.G, gc, to_np(idx.sizes), to_np(idx.offsets), to_np(idx.token_ids), B)
-        assert np.array_equal(to_np(cnt), ocnt), B
-        assert np.array_equal(to_np(sel), osel), B
-        od = oracle.decode(q, w.G, K, V, to_np(sel), to_np(cnt), scale)
-        err = np.abs(to_np(out) - od).max()
-        # the fused kernel: same selection, same attention
-        fsel = torch.full((H, B), -7, dtype=torch.int32, device="cuda")
-        fcnt = torch.empty(H, dtype=torch.int32, device="cuda")
-        fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel, sel_count=fcnt)
-        torch.cuda.synchronize()
-        assert np.array_equal(to_np(fcnt), ocnt) and np.array_equal(to_np(fsel), osel), B
-        ferr = np.abs(to_np(fout) - od).max()
-        say(f"  B={B}: count {to_np(cnt).tolist()[:4]}, decode max abs err {err:.3e}, fused {ferr:.3e}")
-        assert err <= 2e-3 and ferr <= 2e-3
+    cases = [(step, B) for step, B in enumerate([w.B, 1, 7, w.L + 50])]
+    for pk in (False, True):
+        if pk:
+            # the packed copy: row i of head h is the cache row token_ids[h][i]
+            kvc.pack(idx, Kd, Vd)
+            torch.cuda.synchronize()
+            ids = to_np(idx.token_ids)[:, :w.L]
+            for h in range(H):
+                assert np.array_equal(to_np(idx.k_packed)[h, :w.L], K[h, ids[h]])
+                assert np.array_equal(to_np(idx.v_packed)[h, :w.L], V[h, ids[h]])
+        for step, B in cases:
+            check_step(w, idx, base, K, V, Kd, Vd, means, gc, step, B, scale, pk)
     del ws
+
+
+def check_step(w, idx, base, K, V, Kd, Vd, means, gc, step, B, scale, packed):
+    H = K.shape[0]
+    q = queries(w, base, step, K, w.L, means)
+    sel, cnt = kvc.select(idx, to_dev(q), B)
+    ws_b = torch.zeros(kvc.decode_workspace_bytes(H, H * w.G, B), dtype=torch.uint8, device="cuda")
+    out = kvc.sparse_decode(to_dev(q), Kd, Vd, sel, cnt, scale, workspace=ws_b)
+    torch.cuda.synchronize()
+    osel, ocnt, _, _ = oracle.select(q, w.G, gc, to_np(idx.sizes), to_np(idx.offsets), to_np(idx.token_ids), B)
+    assert np.array_equal(to_np(cnt), ocnt), B
+    assert np.array_equal(to_np(sel), osel), B
+    od = oracle.decode(q, w.G, K, V, to_np(sel), to_np(cnt), scale)
+    err = np.abs(to_np(out) - od).max()
+    # the fused kernel: same selection, same attention
+    fsel = torch.full((H, B), -7, dtype=torch.int32, device="cuda")
+    fcnt = torch.empty(H, dtype=torch.int32, device="cuda")
+    fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel, sel_count=fcnt)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(fcnt), ocnt) and np.array_equal(to_np(fsel), osel), B
+    ferr = np.abs(to_np(fout) - od).max()
+    say(f"  B={B}{' packed' if packed else ''}: count {to_np(cnt).tolist()[:4]}, decode max abs err {err:.3e}, "
+        f"fused {ferr:.3e}")
+    assert err <= 2e-3 and ferr <= 2e-3
 
 
 def test_append_then_select_decode():
@@ -166,13 +182,15 @@ def test_append_then_select_decode():
     say("[append]")
     base, K, V, init, means = make_inputs(w)
     H = K.shape[0]
-    idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w))
+    idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w), packed=True)
     Kc = np.zeros_like(K)
     Vc = np.zeros_like(V)
     Kc[:, :w.L], Vc[:, :w.L] = K[:, :w.L], V[:, :w.L]
     Kd, Vd = to_dev(Kc), to_dev(Vc)
     kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.pack(idx, Kd, Vd)
     torch.cuda.synchronize()
+    assert idx._s.packed == 1
     # the oracle index continues from the GPU's built state (identical centroids)
     built = dict(labels=to_np(idx.labels)[:, :w.L], sizes=to_np(idx.sizes), offsets=to_np(idx.offsets),
                  token_ids=to_np(idx.token_ids)[:, :w.L], c=to_np(idx.centroids),
@@ -198,9 +216,15 @@ def test_append_then_select_decode():
         assert np.array_equal(to_np(sel), osel) and np.array_equal(to_np(cnt), ocnt)
         od = oracle.decode(q, w.G, K, V, osel, ocnt, scale)
         assert np.abs(to_np(out) - od).max() <= 2e-3
-        fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, w.B, scale)
-        torch.cuda.synchronize()
-        assert np.abs(to_np(fout) - od).max() <= 2e-3
+        # fused, from the packed copy plus the appended rows, then from the caches alone
+        for pk in (1, 0):
+            idx._s.packed = pk
+            fsel = torch.full((H, w.B), -7, dtype=torch.int32, device="cuda")
+            fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, w.B, scale, sel_ids=fsel)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_np(fsel), osel), pk
+            assert np.abs(to_np(fout) - od).max() <= 2e-3, pk
+        idx._s.packed = 1
     off, ids = kvc.export_csr(idx)
     assert np.array_equal(to_np(off), oi.offsets)
     assert np.array_equal(to_np(ids)[:, :n], oi.token_ids[:, :n])
