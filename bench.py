@@ -135,51 +135,51 @@ def main():
     kvc.lib()  # fails loudly without the built library
     dev = torch.device("cuda:0")
     w = synth.workload(args.workload)
-    if w.layers > 1:
-        print("multi-layer workloads are run by bench_stack (not in this script)", file=sys.stderr)
-        sys.exit(2)
+    NL = w.layers
     H, G, L, d, C, B, cap = w.heads, w.G, w.L, w.d, w.C, w.B, w.capacity
     tdt = torch.bfloat16 if w.dtype == synth.BF16 else torch.float32
-
-    # ---------------- inputs (host generation, then copy to HBM) -------------
-    t0 = time.time()
-    base = synth.config_seed(w.config, 0)
-    K, _, means = synth.mixture_keys(base, H, cap, d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype,
-                                     want_means=(w.query == "mixture"))
-    V = synth.values(base, H, cap, d, w.dtype)
-    init = synth.init_idx(base, H, L, C)
-    qs = []
-    for s in range(w.steps):
-        n_cur = L + (s + 1 if w.append else 0)
-        if w.query == "mixture":
-            qs.append(synth.queries_mixture(base, s, H * G, G, means, w.q_sigma, w.dtype))
-        else:
-            qs.append(synth.queries_noisy_key(base, s, H * G, G, K, n_cur, w.q_sigma))
-    Q = np.stack(qs)
-    log(f"[bench] generated {w.name} inputs in {time.time() - t0:.1f}s")
+    packed = not args.no_pack and args.decode_path == "fused"
+    fused = args.decode_path == "fused"
 
     def to_dev(a):
         if a.dtype == np.uint16:
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    Kp = K.copy()
-    Vp = V.copy()
-    if w.append:  # appended rows come in through the append call
-        Kp[:, L:] = 0
-        Vp[:, L:] = 0
-    Kd, Vd = to_dev(Kp), to_dev(Vp)
-    Qd = to_dev(Q)
-    init_d = to_dev(init)
-    if w.append:
-        Knew = to_dev(np.ascontiguousarray(K[:, L:].transpose(1, 0, 2)))  # [steps, H, d]
-        Vnew = to_dev(np.ascontiguousarray(V[:, L:].transpose(1, 0, 2)))
-    del K, V, Kp, Vp
-    packed = not args.no_pack and args.decode_path == "fused"
-    idx = kvc.ClusterIndex(H, C, cap, tdt, device=dev, packed=packed)
+    # ---------------- inputs (host generation, then copy to HBM) -------------
+    # one independent seeded mixture per layer; each layer has its own caches
+    # and index, all resident in HBM before timing starts
+    t0 = time.time()
+    lay = []
+    for li in range(NL):
+        base = synth.config_seed(w.config, li)
+        K, _, means = synth.mixture_keys(base, H, cap, d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype,
+                                         want_means=(w.query == "mixture"))
+        V = synth.values(base, H, cap, d, w.dtype)
+        init = synth.init_idx(base, H, L, C)
+        qs = []
+        for s in range(w.steps):
+            n_cur = L + (s + 1 if w.append else 0)
+            if w.query == "mixture":
+                qs.append(synth.queries_mixture(base, s, H * G, G, means, w.q_sigma, w.dtype))
+            else:
+                qs.append(synth.queries_noisy_key(base, s, H * G, G, K, n_cur, w.q_sigma))
+        Q = np.stack(qs)
+        e = {"Qd": to_dev(Q), "init_d": to_dev(init)}
+        if w.append:  # appended rows come in through the append call
+            e["Knew"] = to_dev(np.ascontiguousarray(K[:, L:].transpose(1, 0, 2)))  # [steps, H, d]
+            e["Vnew"] = to_dev(np.ascontiguousarray(V[:, L:].transpose(1, 0, 2)))
+            K[:, L:] = 0
+            V[:, L:] = 0
+        e["Kd"], e["Vd"] = to_dev(K), to_dev(V)
+        e["idx"] = kvc.ClusterIndex(H, C, cap, tdt, device=dev, packed=packed)
+        if li == 0:
+            base0, init0, Q0 = base, init, Q
+        lay.append(e)
+        del K, V
+    log(f"[bench] generated {w.name} inputs ({NL} layer(s)) in {time.time() - t0:.1f}s")
     ws_build = torch.empty(kvc.build_workspace_bytes(H, L, C, w.iters), dtype=torch.uint8, device=dev)
     ws_dec = torch.empty(kvc.decode_workspace_bytes(H, H * G, B), dtype=torch.uint8, device=dev)
-    fused = args.decode_path == "fused"
     sel = torch.empty(H, B, dtype=torch.int32, device=dev)
     cnt = torch.empty(H, dtype=torch.int32, device=dev)
     out = torch.empty(H * G, d, dtype=torch.float32, device=dev)
@@ -193,42 +193,48 @@ def main():
     cal_dst.copy_(cal_src)
     del cal_src, cal_dst
 
-    # events per pass: 2*iters around the assignment kernels inside the build,
-    # 3 bracketing the build and the decode phase, 1 after the packed copy,
-    # and, on every SAMPLE-th decode step only (events between kernels add
-    # dispatch gaps), 6 around that step's kernels (append, select, decode)
+    # events per pass: 2*iters per layer around the assignment kernels inside
+    # the builds, 4 bracketing the builds, the packed copies and the decode
+    # phase, and, on every SAMPLE-th decode step only (events between kernels
+    # add dispatch gaps), 6 around that step's first-layer kernels (append,
+    # select, decode)
     SAMPLE = 8
     sampled = [s for s in range(w.steps) if s % SAMPLE == 0]
-    per_pass = 2 * w.iters + 4 + 6 * len(sampled)
+    A = 2 * w.iters * NL
+    per_pass = A + 4 + 6 * len(sampled)
     total_passes = args.warmup + args.steps
     ev = HipEvents(per_pass * total_passes + 2)
 
     def one_pass(p: int):
         o = p * per_pass
-        ev.record(o + 2 * w.iters, sh)
-        kvc.build(idx, Kd, L, w.iters, init_d, workspace=ws_build, assign_events=ev.sub(o, 2 * w.iters))
-        ev.record(o + 2 * w.iters + 3, sh)
+        ev.record(o + A, sh)
+        for li, e in enumerate(lay):
+            kvc.build(e["idx"], e["Kd"], L, w.iters, e["init_d"], workspace=ws_build,
+                      assign_events=ev.sub(o + 2 * w.iters * li, 2 * w.iters))
+        ev.record(o + A + 3, sh)
         if packed:
-            kvc.pack(idx, Kd, Vd)
-        ev.record(o + 2 * w.iters + 1, sh)
-        b = o + 2 * w.iters + 4
+            for e in lay:
+                kvc.pack(e["idx"], e["Kd"], e["Vd"])
+        ev.record(o + A + 1, sh)
+        b = o + A + 4
         for s in range(w.steps):
-            e6 = b + 6 * (s // SAMPLE) if s % SAMPLE == 0 else None
-            rec = (lambda i: ev.record(e6 + i, sh)) if e6 is not None else (lambda i: None)
-            if w.append:
-                rec(0)
-                kvc.append(idx, Kd, Vd, Knew[s].unsqueeze(1), Vnew[s].unsqueeze(1))
-                rec(1)
-            rec(2)
-            if fused:
-                rec(3)
-                kvc.select_decode(idx, Qd[s], Kd, Vd, B, scale, out=out)
-            else:
-                kvc.select(idx, Qd[s], B, sel, cnt)
-                rec(3)
-                kvc.sparse_decode(Qd[s], Kd, Vd, sel, cnt, scale, out=out, workspace=ws_dec)
-            rec(4)
-        ev.record(o + 2 * w.iters + 2, sh)
+            for li, e in enumerate(lay):
+                e6 = b + 6 * (s // SAMPLE) if (s % SAMPLE == 0 and li == 0) else None
+                rec = (lambda i: ev.record(e6 + i, sh)) if e6 is not None else (lambda i: None)
+                if w.append:
+                    rec(0)
+                    kvc.append(e["idx"], e["Kd"], e["Vd"], e["Knew"][s].unsqueeze(1), e["Vnew"][s].unsqueeze(1))
+                    rec(1)
+                rec(2)
+                if fused:
+                    rec(3)
+                    kvc.select_decode(e["idx"], e["Qd"][s], e["Kd"], e["Vd"], B, scale, out=out)
+                else:
+                    kvc.select(e["idx"], e["Qd"][s], B, sel, cnt)
+                    rec(3)
+                    kvc.sparse_decode(e["Qd"][s], e["Kd"], e["Vd"], sel, cnt, scale, out=out, workspace=ws_dec)
+                rec(4)
+        ev.record(o + A + 2, sh)
 
     for p in range(args.warmup):
         one_pass(p)
@@ -245,11 +251,11 @@ def main():
     assign_ms, build_ms, select_ms, decode_ms, append_ms, phase_ms, pack_ms = [], [], [], [], [], [], []
     for p in range(args.warmup, total_passes):
         o = p * per_pass
-        assign_ms += [ev.ms(o + 2 * t, o + 2 * t + 1) for t in range(w.iters)]
-        build_ms.append(ev.ms(o + 2 * w.iters, o + 2 * w.iters + 3))
-        pack_ms.append(ev.ms(o + 2 * w.iters + 3, o + 2 * w.iters + 1))
-        phase_ms.append(ev.ms(o + 2 * w.iters + 1, o + 2 * w.iters + 2))
-        b = o + 2 * w.iters + 4
+        assign_ms += [ev.ms(o + 2 * t, o + 2 * t + 1) for t in range(w.iters * NL)]
+        build_ms.append(ev.ms(o + A, o + A + 3))
+        pack_ms.append(ev.ms(o + A + 3, o + A + 1))
+        phase_ms.append(ev.ms(o + A + 1, o + A + 2))
+        b = o + A + 4
         for i in range(len(sampled)):
             e6 = b + 6 * i
             if w.append:
@@ -264,7 +270,7 @@ def main():
     n_dec = args.steps * w.steps
     value = n_dec / decode_phase_s
     step_ms = sum(phase_ms) / n_dec
-    kmeans_tflops = alg["kmeans_flops"] * args.steps / (sum(build_ms) / 1e3) / 1e12
+    kmeans_tflops = alg["kmeans_flops"] * NL * args.steps / (sum(build_ms) / 1e3) / 1e12
 
     assign_peak = PEAK_BF16 if w.dtype == synth.BF16 else PEAK_F64
     rl = {
@@ -276,15 +282,15 @@ def main():
     if fused:
         rl["select_decode"] = {"bound": "hbm", "achieved": alg["step_bytes"] / (dd_ms / 1e3) / 1e9,
                                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "avg_us": dd_ms * 1e3,
-                               "share": dd_ms * n_dec / total_ms}
+                               "share": dd_ms * n_dec * NL / total_ms}
         kernel_names["select_decode"] = ("select_decode_bf16_kernel" if w.dtype == synth.BF16
                                          else "select_decode_kernel")
     else:
         rl["sparse_decode"] = {"bound": "hbm", "achieved": alg["decode_bytes"] / (dd_ms / 1e3) / 1e9,
                                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "avg_us": dd_ms * 1e3,
-                               "share": dd_ms * n_dec / total_ms}
+                               "share": dd_ms * n_dec * NL / total_ms}
         rl["select"] = {"bound": "hbm", "achieved": alg["select_bytes"] / (s_ms / 1e3) / 1e9, "peak": PEAK_HBM / 1e9,
-                        "unit": "GB/s", "avg_us": s_ms * 1e3, "share": s_ms * n_dec / total_ms}
+                        "unit": "GB/s", "avg_us": s_ms * 1e3, "share": s_ms * n_dec * NL / total_ms}
         kernel_names["sparse_decode"] = "decode_split_kernel + decode_combine_kernel"
         kernel_names["select"] = "select_kernel"
     traffic = {}
@@ -316,14 +322,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == synth.BF16 else "f32",
         "data": "synthetic (seeded Gaussian-mixture keys with outlier channels, N(0,1) values)",
-        "config": {"workload": w.name, "kv_heads_total": H, "q_heads_total": H * G, "G": G, "L": L, "d": d, "C": C,
+        "config": {"workload": w.name, "layers": NL, "kv_heads_total": H * NL, "q_heads_total": H * G * NL, "G": G,
+                   "L": L, "d": d, "C": C,
                    "kmeans_iters": w.iters, "B": B, "decode_steps_per_step": w.steps, "append": w.append,
                    "decode_path": args.decode_path, "packed_kv": packed},
         "kmeans_tflops": kmeans_tflops,
         "kmeans_ms": mean(build_ms),
         "pack_ms": mean(pack_ms),
         "decode_step_us": step_ms * 1e3,
-        "decode_step_hbm_frac": alg["step_bytes"] / (step_ms / 1e3) / PEAK_HBM,
+        "decode_step_hbm_frac": alg["step_bytes"] * NL / (step_ms / 1e3) / PEAK_HBM,
         "kernel_timing": f"HIP events around every kernel of 1 in {SAMPLE} decode steps and around every "
                          "assignment kernel; value from events bracketing each pass's decode phase",
         "wall_s_timed": wall,
@@ -335,7 +342,7 @@ def main():
 
     # ---------------- CPU oracle baseline (bounded sample) -----------------
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, args, base, init, Q)
+        result["cpu_baseline"] = cpu_baseline(w, args, base0, init0, Q0)
     print(json.dumps(result), flush=True)
 
 
@@ -363,11 +370,11 @@ def cpu_baseline(w, args, base, init, Q):
         sel, cnt, _, _ = oracle.select(q, w.G, built["c"], built["sizes"], built["offsets"], built["token_ids"], w.B)
         oracle.decode(q, w.G, K, V, sel, cnt, scale)
     t_dec = (time.perf_counter() - t0) / ns
-    per_step_full = t_dec * w.heads / nh
+    per_step_full = t_dec * w.heads * w.layers / nh
     flops_iter = 2.0 * nh * w.L * w.C * w.d
     return {"value": 1.0 / per_step_full, "unit": "decode steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{nh} of {w.heads} KV heads x {ns} decode steps (select + decode), scaled x{w.heads / nh:.0f}; "
-                      f"plus one k-means iteration of the {nh} heads",
+            "sample": f"{nh} of {w.heads * w.layers} KV heads (layer 0) x {ns} decode steps (select + decode), "
+                      f"scaled x{w.heads * w.layers / nh:.0f}; plus one k-means iteration of the {nh} heads",
             "kmeans_gflops": flops_iter / t_iter / 1e9}
 
 
