@@ -340,9 +340,37 @@ def main():
     if w.append:
         result["append_us"] = mean(append_ms) * 1e3
 
+    # ---------------- full-KV comparator (dense decode over all L rows) -----
+    if w.dtype == synth.BF16:
+        e0 = lay[0]
+        ws_dense = torch.empty(kvc.dense_decode_workspace_bytes(H, H * G, L), dtype=torch.uint8, device=dev)
+        for i in range(3):
+            kvc.dense_decode(e0["Qd"][i % w.steps], e0["Kd"], e0["Vd"], L, scale, out=out, workspace=ws_dense)
+        R = 20
+        dev_ev = HipEvents(2)
+        dev_ev.record(0, sh)
+        for i in range(R):
+            kvc.dense_decode(e0["Qd"][i % w.steps], e0["Kd"], e0["Vd"], L, scale, out=out, workspace=ws_dense)
+        dev_ev.record(1, sh)
+        torch.cuda.synchronize()
+        dense_ms = dev_ev.ms(0, 1) / R
+        e = 2
+        full_bytes = H * (2 * L * d * e + G * d * e + G * d * 4)
+        full_step_us = dense_ms * 1e3 * NL
+        result["full_kv"] = {
+            "what": "kv_dense_decode: attention over all L rows of every KV head, per decode step (all layers)",
+            "decode_steps_per_s": 1e6 / full_step_us, "step_us": full_step_us,
+            "hbm_frac": full_bytes / (dense_ms / 1e3) / PEAK_HBM,
+            "sparse_speedup": value / (1e6 / full_step_us)}
+
     # ---------------- CPU oracle baseline (bounded sample) -----------------
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, args, base0, init0, Q0)
+        # selection quality of the GPU's selection at decode step 0, layer 0
+        # (oracle recall of the exact top-B attention tokens, sampled heads)
+        kvc.select(lay[0]["idx"], lay[0]["Qd"][0], B, sel, cnt)
+        torch.cuda.synchronize()
+        result["selection_recall"] = recall_sample(w, args, base0, Q0, sel.cpu().numpy(), cnt.cpu().numpy())
     print(json.dumps(result), flush=True)
 
 
@@ -376,6 +404,22 @@ def cpu_baseline(w, args, base, init, Q):
             "sample": f"{nh} of {w.heads * w.layers} KV heads (layer 0) x {ns} decode steps (select + decode), "
                       f"scaled x{w.heads * w.layers / nh:.0f}; plus one k-means iteration of the {nh} heads",
             "kmeans_gflops": flops_iter / t_iter / 1e9}
+
+
+def recall_sample(w, args, base, Q, sel, cnt):
+    """Recall of the exact top-B attention tokens (oracle, fp64) by the GPU's
+    selection, for the first KV heads of layer 0 at decode step 0."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    nh = min(8, w.heads)
+    K, _, _ = synth.mixture_keys(base, nh, w.L, w.d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype)
+    r = oracle.recall(np.ascontiguousarray(Q[0, :nh * w.G]), w.G, K, w.L, np.ascontiguousarray(sel[:nh]),
+                      np.ascontiguousarray(cnt[:nh]))
+    return {"mean": float(r.mean()), "min": float(r.min()), "budget": w.B,
+            "sample": f"{nh} KV heads ({nh * w.G} query heads), decode step 0, layer 0"}
 
 
 if __name__ == "__main__":

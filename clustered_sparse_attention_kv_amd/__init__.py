@@ -61,12 +61,15 @@ def lib():
         L.kv_cluster_select_decode.argtypes = [p, p, i, p, p, i, f, p, p, p, p]
         L.kv_cluster_export_csr.argtypes = [p, p, p, p]
         L.kv_cluster_pack.argtypes = [p, p, p, p]
+        L.kv_dense_decode_workspace_bytes.argtypes = [i, i, i, i]
+        L.kv_dense_decode_workspace_bytes.restype = sz
+        L.kv_dense_decode.argtypes = [p, i, p, p, i, i, i, i, i, f, p, p, sz, p]
         L.kv_cluster_debug_assign.argtypes = [p, p, i, p, p, p, p, p, sz, p]
         L.kv_cluster_debug_update.argtypes = [p, p, i, p, sz, p]
         L.kv_cluster_status_string.argtypes = [i]
         L.kv_cluster_status_string.restype = C.c_char_p
         for name in ("kv_cluster_build", "kv_cluster_build_timed", "kv_cluster_append", "kv_cluster_select", "kv_sparse_decode",
-                     "kv_cluster_select_decode", "kv_cluster_export_csr", "kv_cluster_pack", "kv_cluster_debug_assign",
+                     "kv_cluster_select_decode", "kv_cluster_export_csr", "kv_cluster_pack", "kv_dense_decode", "kv_cluster_debug_assign",
                      "kv_cluster_debug_update"):
             getattr(L, name).restype = i
         _lib = L
@@ -273,6 +276,27 @@ def pack(idx: ClusterIndex, k_cache: torch.Tensor, v_cache: torch.Tensor, stream
     if idx.k_packed is None:
         raise ValueError("the index has no packed arrays (create it with packed=True)")
     _check(lib().kv_cluster_pack(idx.ref(), _ptr(k_cache), _ptr(v_cache), _stream(stream)), "kv_cluster_pack")
+
+
+def dense_decode_workspace_bytes(heads: int, q_heads: int, n: int, d: int = HEAD_DIM) -> int:
+    return lib().kv_dense_decode_workspace_bytes(heads, q_heads, d, n)
+
+
+def dense_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, n: int, scale: float,
+                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """kv_dense_decode: full attention of q [q_heads, d] over the first n rows -> fp32 [q_heads, d]."""
+    heads, capacity, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype or q.dtype != k_cache.dtype:
+        raise ValueError("q, k_cache and v_cache must share a type; k and v caches a shape")
+    if out is None:
+        out = torch.empty(q.shape[0], d, dtype=torch.float32, device=q.device)
+    need = dense_decode_workspace_bytes(heads, q.shape[0], n, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().kv_dense_decode(_ptr(q), q.shape[0], _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache.dtype), heads,
+                                 capacity, d, n, scale, _ptr(out), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)), "kv_dense_decode")
+    return out
 
 
 def export_csr(idx: ClusterIndex, stream=None):

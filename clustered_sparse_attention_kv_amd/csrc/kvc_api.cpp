@@ -218,6 +218,30 @@ int kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token
                                       static_cast<hipStream_t>(stream)));
 }
 
+size_t kv_dense_decode_workspace_bytes(int heads, int q_heads, int d, int n) {
+  if (heads < 1 || q_heads < heads || q_heads % heads != 0 || d != KVC_HEAD_DIM || n < 1) return 0;
+  const int G = q_heads / heads;
+  if (G > KVC_MAX_G) return 0;
+  int nsplit, T;
+  dense_split(n, G, &nsplit, &T);
+  return align_up(sizeof(float) * (size_t)heads * nsplit * G * (KVC_HEAD_DIM + 2));
+}
+
+int kv_dense_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
+                    int capacity, int d, int n, float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !out || !ws || heads < 1 || q_heads < 1) return KVC_ERR_INVALID_ARG;
+  if (dtype != KVC_BF16 && dtype != KVC_F32) return KVC_ERR_INVALID_ARG;
+  if (d != KVC_HEAD_DIM || dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
+  if (q_heads % heads != 0) return KVC_ERR_INVALID_ARG;
+  const int G = q_heads / heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KVC_ERR_UNSUPPORTED;
+  if (n < 1 || n > capacity) return KVC_ERR_INVALID_ARG;
+  if ((long long)heads * capacity >= (1ll << 31)) return KVC_ERR_UNSUPPORTED;
+  if (ws_bytes < kv_dense_decode_workspace_bytes(heads, q_heads, d, n)) return KVC_ERR_WORKSPACE;
+  return hip_status(launch_dense_decode(q, G, k_cache, v_cache, capacity, heads, n, scale, out,
+                                        static_cast<float*>(ws), static_cast<hipStream_t>(stream)));
+}
+
 const char* kv_cluster_status_string(int status) {
   switch (status) {
     case KVC_OK: return "ok";

@@ -918,6 +918,185 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------------------
+// Full attention over the first n rows of each head (the dense computation
+// that cluster-granular recall approximates; the full-KV comparator). Grid
+// (nsplit, heads), 4 waves per block; split s covers tokens [s T, s T + T).
+// Each wave takes 64-token slices w, w + 4, ... of its split: query-key
+// products on the matrix cores (the 64 keys as the A operand of four
+// 16x16x32 bf16 tiles, the G queries as B), an online softmax per wave with
+// one token per lane, and the value rows weighted on the vector units, 16
+// lanes per row (8 channels each) and 4 rows per load instruction. The waves'
+// states merge in LDS and the block writes its partial (o[d], m, l), which
+// decode_combine_kernel merges over the splits.
+template <int G>
+__global__ __launch_bounds__(256) void dense_decode_bf16_kernel(const uint16_t* __restrict__ q,
+                                                                const uint16_t* __restrict__ kc,
+                                                                const uint16_t* __restrict__ vc, long long cap, int n,
+                                                                int T, float qscale, float* __restrict__ part) {
+  constexpr int NW = 4;
+  constexpr int GP = G < 4 ? 4 : G;
+  constexpr int VR = 16;  // value rows per lane per slice (4 per load instruction)
+  __shared__ __align__(16) float pw[NW][64][GP];
+  __shared__ float ored[NW][G][D];
+  __shared__ float wm[NW][G], wl[NW][G];
+  const int h = blockIdx.y, sp = blockIdx.x, nsplit = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int j16 = lane & 15, kb4 = lane >> 4;     // key tiles: row lane % 16, 16-byte piece lane / 16
+  const int grp = lane >> 4, gl = lane & 15;      // value rows: row lane / 16 of each 4, channels 8 (lane % 16)
+  const int tb = sp * T, te = tb + T < n ? tb + T : n;
+  const uint16_t* Kh = kc + (size_t)h * cap * D + 8 * kb4;
+  const uint16_t* Vh = vc + (size_t)h * cap * D + 8 * gl;
+  bf16x8 qb[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (j16 < G) v = *reinterpret_cast<const u32x4*>(q + ((size_t)h * G + j16) * D + 32 * s + 8 * kb4);
+    qb[s] = __builtin_bit_cast(bf16x8, v);
+  }
+  float o[G][8], m_run[G], l_run[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[g][c] = 0.f;
+  }
+  for (int t0 = tb + w * 64; t0 < te; t0 += NW * 64) {
+    const int n64 = te - t0 < 64 ? te - t0 : 64;
+    bf16x8 ka[4][4];
+#pragma unroll
+    for (int T4 = 0; T4 < 4; ++T4) {
+      const int t = T4 * 16 + j16;
+      const uint16_t* src = Kh + (size_t)(t0 + (t < n64 ? t : 0)) * D;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ka[T4][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 32 * s));
+    }
+    u32x4 vr[VR];
+#pragma unroll
+    for (int r = 0; r < VR; ++r) {
+      const int t = r * 4 + grp;
+      vr[r] = t < n64 ? *reinterpret_cast<const u32x4*>(Vh + (size_t)(t0 + t) * D) : u32x4{0u, 0u, 0u, 0u};
+    }
+    f32x4 acc[4] = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int T4 = 0; T4 < 4; ++T4) acc[T4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[T4][s], qb[s], acc[T4], 0, 0, 0);
+    if (j16 < G) {
+#pragma unroll
+      for (int T4 = 0; T4 < 4; ++T4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = T4 * 16 + 4 * kb4 + r;
+          pw[w][t][j16] = t < n64 ? acc[T4][r] * qscale : -INFINITY;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    {
+      float sv[GP];
+#pragma unroll
+      for (int g4 = 0; g4 < GP; g4 += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&pw[w][lane][g4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[g4 + i] = x[i];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float smax = wave_max(sv[g]);
+        if (smax > m_run[g]) {  // uniform over the wave
+          const float f = m_run[g] == -INFINITY ? 0.f : exp2f(m_run[g] - smax);
+          l_run[g] *= f;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o[g][c] *= f;
+          m_run[g] = smax;
+        }
+        const float pv = m_run[g] == -INFINITY ? 0.f : exp2f(sv[g] - m_run[g]);
+        sv[g] = pv;
+        l_run[g] += pv;
+      }
+#pragma unroll
+      for (int g4 = 0; g4 < GP; g4 += 4)
+        *reinterpret_cast<f32x4*>(&pw[w][lane][g4]) = f32x4{sv[g4], sv[g4 + 1], sv[g4 + 2], sv[g4 + 3]};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int r = 0; r < VR; ++r) {
+      const int t = r * 4 + grp;
+      float pv[GP];
+#pragma unroll
+      for (int g4 = 0; g4 < GP; g4 += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&pw[w][t][g4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[g4 + i] = x[i];
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t u = vr[r][c >> 1];
+        const float vv = (c & 1) ? __uint_as_float(u & 0xFFFF0000u) : __uint_as_float(u << 16);
+#pragma unroll
+        for (int g = 0; g < G; ++g) o[g][c] = fmaf(pv[g], vv, o[g][c]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  // merge: the 4 row groups of each wave (lanes 16 apart share channels), then the waves
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    l_run[g] = wave_sum(l_run[g]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float v = o[g][c];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      o[g][c] = v;
+    }
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ored[w][g][8 * gl + c] = o[g][c];
+  }
+  if (lane < G) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (g == lane) {
+        wm[w][g] = m_run[g];
+        wl[w][g] = l_run[g];
+      }
+  }
+  __syncthreads();
+  float* ph = part + ((size_t)h * nsplit + sp) * G * (D + 2);
+  for (int e = tid; e < G * D; e += 256) {
+    const int g = e / D, j = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, wm[v][g]);
+    float O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int v = 0; v < NW; ++v) O = fmaf(wm[v][g] == -INFINITY ? 0.f : exp2f(wm[v][g] - M), ored[v][g][j], O);
+    }
+    ph[(size_t)g * (D + 2) + j] = O;
+    if (j == 0) {
+      float Ls = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int v = 0; v < NW; ++v) Ls = fmaf(wm[v][g] == -INFINITY ? 0.f : exp2f(wm[v][g] - M), wl[v][g], Ls);
+      }
+      ph[(size_t)g * (D + 2) + D] = M;
+      ph[(size_t)g * (D + 2) + D + 1] = Ls;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Packed copy of the built tokens' key and value rows in index order: row i of
 // head h is the cache row token_ids[h][i] (i < n). 16 bytes per lane, one row
 // per D * sizeof(KT) / 16 lanes.
@@ -1075,6 +1254,44 @@ hipError_t launch_export_csr(int heads, int C, const int32_t* offsets, const int
                              const int32_t* app_offsets, const int32_t* app_ids, long long cap, int32_t* out_offsets,
                              int32_t* out_ids, hipStream_t st) {
   export_csr_kernel<<<heads, 256, 0, st>>>(C, offsets, token_ids, app_offsets, app_ids, cap, out_offsets, out_ids);
+  return hipGetLastError();
+}
+
+// Split of the dense pass: 64-token multiples, at most DEC_MAX_PAIRS / G splits.
+void dense_split(int n, int G, int* nsplit, int* T) {
+  int ns = (n + 511) / 512;
+  const int cap = DEC_MAX_PAIRS / G;
+  if (ns > cap) ns = cap;
+  if (ns < 1) ns = 1;
+  int t = (n + ns - 1) / ns;
+  t = (t + 63) / 64 * 64;
+  *T = t;
+  *nsplit = (n + t - 1) / t;
+}
+
+hipError_t launch_dense_decode(const void* q, int G, const void* kc, const void* vc, long long cap, int heads, int n,
+                               float scale, float* out, float* part, hipStream_t st) {
+  int nsplit, T;
+  dense_split(n, G, &nsplit, &T);
+  const float qscale = scale * 1.4426950408889634f;
+  const dim3 grid(nsplit, heads);
+  switch (G) {
+#define KVC_DENSE_CASE(GG)                                                                                        \
+  case GG:                                                                                                      \
+    dense_decode_bf16_kernel<GG><<<grid, 256, 0, st>>>((const uint16_t*)q, (const uint16_t*)kc,                \
+                                                       (const uint16_t*)vc, cap, n, T, qscale, part);           \
+    break;
+    KVC_DENSE_CASE(1)
+    KVC_DENSE_CASE(2)
+    KVC_DENSE_CASE(4)
+    KVC_DENSE_CASE(8)
+#undef KVC_DENSE_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_combine_kernel<<<heads, 256, 0, st>>>(part, nsplit, G, out);
   return hipGetLastError();
 }
 

@@ -42,6 +42,9 @@ hipError_t launch_select_decode(int dtype, const void* q, int G, const float* ce
                                 const void* vc, const void* kp, const void* vp, int B, float scale, float* out,
                                 int32_t* sel_ids, int32_t* sel_count, hipStream_t st);
 // kp, vp: the packed copies (both non-null) or null (rows from the caches).
+void dense_split(int n, int G, int* nsplit, int* T);
+hipError_t launch_dense_decode(const void* q, int G, const void* kc, const void* vc, long long cap, int heads, int n,
+                               float scale, float* out, float* part, hipStream_t st);
 hipError_t launch_pack(int dtype, const void* kc, const void* vc, long long cap, int heads, const int32_t* token_ids,
                        int n, void* kp, void* vp, hipStream_t st);
 hipError_t launch_export_csr(int heads, int C, const int32_t* offsets, const int32_t* token_ids,

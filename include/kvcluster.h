@@ -211,6 +211,26 @@ int kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, c
                              const void* v_cache, int B, float scale, float* out, int32_t* sel_ids,
                              int32_t* sel_count, void* stream);
 
+/* Bytes of workspace kv_dense_decode needs. */
+size_t kv_dense_decode_workspace_bytes(int heads, int q_heads, int d, int n);
+
+/*
+ * Full single-query attention over the first n rows of every head, the
+ * computation that cluster-granular recall approximates (II.A; III.A) and the
+ * full-KV comparator of the decode benchmark: for query head g (KV head
+ * h = g / G),
+ *   out[g] = sum_{i < n} softmax_i(scale * q_g . K[h, i]) V[h, i]
+ * with bf16 inputs, fp32 accumulation and fp32 output [q_heads, d].
+ * k_cache and v_cache are [heads, capacity, d] bf16 (KVC_BF16 only; KVC_F32
+ * returns KVC_ERR_UNSUPPORTED), q is [q_heads, d]. The rows are split into
+ * blocks whose partial results go to the workspace
+ * (kv_dense_decode_workspace_bytes(heads, q_heads, d, n) bytes, contents need
+ * not be initialised) and are merged by a second kernel. Requires
+ * 1 <= n <= capacity and G in {1, 2, 4, 8}.
+ */
+int kv_dense_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
+                    int capacity, int d, int n, float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
 /*
  * The canonical index of every head (built and appended tokens merged):
  * offsets [heads, C+1] and token_ids [heads, capacity] with each cluster's

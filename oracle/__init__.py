@@ -57,6 +57,7 @@ def _load():
         lib.orc_append.restype = i
         lib.orc_select.argtypes = [i, i, i, i, i, p, i, p, p, p, p, ll, p, p, p, p]
         lib.orc_decode.argtypes = [i, i, i, p, i, p, p, i, ll, p, p, i, d, p]
+        lib.orc_recall.argtypes = [i, i, i, i, i, p, i, p, i, ll, p, p, p]
         _lib = lib
     return _lib
 
@@ -253,4 +254,19 @@ def decode(q: np.ndarray, G: int, Kc: np.ndarray, Vc: np.ndarray, sel_ids: np.nd
     out = np.empty((H * G, d), dtype=np.float32)
     lib.orc_decode(H, G, d, _ptr(q), _dt(q), _ptr(Kc), _ptr(Vc), _dt(Kc), rows * d, _ptr(sel_ids),
                    _ptr(sel_count), B, float(scale), _ptr(out))
+    return out
+
+
+def recall(q: np.ndarray, G: int, Kc: np.ndarray, N: int, sel_ids: np.ndarray, sel_count: np.ndarray) -> np.ndarray:
+    """Fraction of the exact top-min(B, N) attention tokens of each query head
+    (q [H*G, d], keys Kc [H, rows, d], first N rows) that the selection
+    sel_ids [H, B] (sel_count [H] valid entries) recalls -> float64 [H*G]."""
+    lib = _load()
+    q, Kc = _c(q), _c(Kc)
+    sel_ids, sel_count = _c(sel_ids, np.int32), _c(sel_count, np.int32)
+    H, rows, d = Kc.shape
+    B = sel_ids.shape[1]
+    out = np.empty(H * G, dtype=np.float64)
+    lib.orc_recall(H, G, d, int(N), B, _ptr(q), _dt(q), _ptr(Kc), _dt(Kc), rows * d, _ptr(sel_ids),
+                   _ptr(sel_count), _ptr(out))
     return out

@@ -377,3 +377,51 @@ void orc_decode(int H, int G, int d, const void* q, int qdt, const void* Kc, con
     free(num);
   }
 }
+
+/*
+ * Selection quality (III.A: the selection that attention over B tokens
+ * should approximate is the B tokens with the largest attention weights).
+ * For query head g (KV head h = g / G) over the first N rows of the head:
+ * the exact top min(B, N) tokens by the fp64 chain q_g . K_t (equal logits:
+ * the lower position first; softmax is increasing, so logits rank like the
+ * weights), and recall[g] = |top set and selected set of h| / min(B, N),
+ * where the selected set is sel_ids[h, 0 .. sel_count[h]).
+ */
+typedef struct {
+  double s;
+  int t;
+} logit_t;
+
+static int cmp_logit(const void* a, const void* b) {
+  const logit_t* x = (const logit_t*)a;
+  const logit_t* y = (const logit_t*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->t > y->t) - (x->t < y->t);
+}
+
+void orc_recall(int H, int G, int d, int N, int B, const void* q, int qdt, const void* Kc, int kdt,
+                long long head_stride, const int32_t* sel_ids, const int32_t* sel_count, double* recall) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int g = 0; g < H * G; ++g) {
+    const int h = g / G;
+    const int top = B < N ? B : N;
+    logit_t* z = (logit_t*)malloc(sizeof(logit_t) * (size_t)(N > 0 ? N : 1));
+    unsigned char* in_top = (unsigned char*)calloc((size_t)(N > 0 ? N : 1), 1);
+    for (int t = 0; t < N; ++t) {
+      z[t].s = chain_dot(d, q, qdt, (size_t)g * d, Kc, kdt, (size_t)h * (size_t)head_stride + (size_t)t * d);
+      z[t].t = t;
+    }
+    qsort(z, (size_t)N, sizeof(logit_t), cmp_logit);
+    for (int r = 0; r < top; ++r) in_top[z[r].t] = 1;
+    int hit = 0;
+    for (int i = 0; i < sel_count[h]; ++i) {
+      const int t = sel_ids[(size_t)h * B + i];
+      if (t >= 0 && t < N && in_top[t]) ++hit;
+    }
+    recall[g] = top > 0 ? (double)hit / (double)top : 1.0;
+    free(z);
+    free(in_top);
+  }
+}
+

@@ -106,6 +106,16 @@ def test_append_select_decode_reject(kvc):
     assert dec(B=0) == INVALID
     assert dec(qh=32, B=4096 + 64, ws=1 << 40) == UNSUPPORTED   # 65 splits x 8 heads > 512 pairs
     assert L.kv_cluster_export_csr(C.byref(built), None, p, None) == INVALID
+    # the dense comparator: bf16 only, 1 <= n <= capacity, enough workspace
+    dws = L.kv_dense_decode_workspace_bytes(4, 16, 128, 200)
+    assert dws > 0 and L.kv_dense_decode_workspace_bytes(4, 16, 64, 200) == 0
+    dd = lambda **k: L.kv_dense_decode(p, k.get("qh", 16), p, p, k.get("dt", 1), 4, 256, k.get("d", 128),
+                                       k.get("n", 200), f, p, p, k.get("ws", dws), None)
+    assert dd(dt=0) == UNSUPPORTED
+    assert dd(d=64) == UNSUPPORTED
+    assert dd(qh=12) == UNSUPPORTED
+    assert dd(n=0) == INVALID and dd(n=257) == INVALID
+    assert dd(ws=dws - 1) == WORKSPACE
     # packing needs both packed arrays and a built index
     assert L.kv_cluster_pack(C.byref(built), p, p, None) == INVALID           # no packed arrays
     unbuilt = make_index(kvc)

@@ -108,6 +108,23 @@ def test_full_size_build_select_decode(cfg):
         say(f"  step {step} (packed): decode max abs err fused {ferr:.2e}")
 
 
+def test_full_size_dense_decode():
+    """The full-KV comparator at the benchmark's size: every KV head, all
+    32768 rows, against the oracle's attention."""
+    w = synth.workload(4)
+    base, K, V, init, means = gen(w)
+    Kd, Vd = to_dev(K), to_dev(V)
+    scale = 1.0 / math.sqrt(w.d)
+    q = queries(w, base, 0, K, w.L, means)
+    out = kvc.dense_decode(to_dev(q), Kd, Vd, w.L, scale)
+    torch.cuda.synchronize()
+    allsel = np.tile(np.arange(w.L, dtype=np.int32), (w.heads, 1))
+    od = oracle.decode(q, w.G, K, V, allsel, np.full(w.heads, w.L, np.int32), scale)
+    err = float(np.abs(to_np(out) - od).max())
+    say(f"[full size dense] {w.heads} heads x {w.L} rows: max abs err {err:.2e}")
+    assert err <= 2e-3
+
+
 def test_full_size_append_workload():
     w = synth.workload(3)
     say(f"[full size] {w.name}: {w.heads} heads x {w.L} keys + {w.steps} appended, C={w.C}, B={w.B}")

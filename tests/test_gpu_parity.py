@@ -235,6 +235,25 @@ def test_append_then_select_decode():
     say(f"  appended {n - w.L} tokens; final sizes sum {to_np(idx.sizes).sum(axis=1).tolist()}")
 
 
+def test_dense_decode_matches_full_attention():
+    """The full-KV comparator: attention over every one of the first n rows
+    (II.A) against the oracle's, for ragged n and a single row."""
+    w = SMALL
+    base, K, V, init, means = make_inputs(w)
+    H = K.shape[0]
+    Kd, Vd = to_dev(K), to_dev(V)
+    scale = 1.0 / math.sqrt(w.d)
+    for n in (w.L, 1, 777):
+        q = queries(w, base, n, K, n, means)
+        out = kvc.dense_decode(to_dev(q), Kd, Vd, n, scale)
+        torch.cuda.synchronize()
+        allsel = np.tile(np.arange(n, dtype=np.int32), (H, 1))
+        od = oracle.decode(q, w.G, K, V, allsel, np.full(H, n, np.int32), scale)
+        err = float(np.abs(to_np(out) - od).max())
+        say(f"  dense n={n}: max abs err {err:.2e}")
+        assert err <= 2e-3
+
+
 def test_init_index_out_of_range_flag():
     w = SMALL
     base, K, V, init, _ = make_inputs(w)

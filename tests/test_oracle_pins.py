@@ -415,3 +415,51 @@ def test_worked_example(orc):
     out = orc.decode(q, 1, K, V, sel, cnt, e["scale"])
     np.testing.assert_allclose(out[0], e["out"], rtol=0, atol=e["out_atol"])
     assert f32(e["scale"]) == e["scale"]
+
+
+# ------------------------------------------------------------------ recall
+
+def test_recall_hand_case(orc):
+    """III.A: the reference set is the B tokens of largest attention weight.
+    Logits 3, 2, 1, 0 -> the top 2 are tokens 0 and 1."""
+    K = np.array([[[3, 0], [2, 0], [1, 0], [0, 0]]], np.float32)
+    q = np.array([[1, 0]], np.float32)
+    for sel, want in (([0, 3], 0.5), ([1, 0], 1.0), ([2, 3], 0.0)):
+        r = orc.recall(q, 1, K, 4, np.array([sel], np.int32), np.array([2], np.int32))
+        assert r.tolist() == [want], sel
+    # a budget covering every token recalls everything
+    r = orc.recall(q, 1, K, 4, np.array([[3, 2, 1, 0, -1]], np.int32), np.array([4], np.int32))
+    assert r.tolist() == [1.0]
+
+
+def test_recall_one_key_per_cluster_is_exact(orc):
+    """With C = N (every key its own cluster, centroid = the key) the cluster
+    selection is the exact top-B by q . k (III.A), ties included, so its recall
+    is 1 for every budget."""
+    rng = np.random.default_rng(21)
+    H, N, d = 2, 60, 8
+    K = rng.integers(-3, 4, (H, N, d)).astype(np.float32)
+    q = rng.integers(-3, 4, (H, d)).astype(np.float32)
+    S, O, I = zip(*[orc.csr(np.arange(N, dtype=np.int32), N) for _ in range(H)])
+    S, O, I = np.stack(S), np.stack(O), np.stack(I)
+    for B in (1, 5, 17, 60, 80):
+        sel, cnt, _, _ = orc.select(q, 1, K, S, O, I, B)
+        assert np.all(orc.recall(q, 1, K, N, sel, cnt) == 1.0), B
+
+
+def test_recall_brute_force(orc):
+    """Against an independent count: exact logits from Python integers on
+    integer-valued inputs, ranking by (logit desc, position asc)."""
+    rng = np.random.default_rng(22)
+    H, G, N, d, B = 2, 2, 40, 6, 9
+    K = rng.integers(-4, 5, (H, N, d)).astype(np.float32)
+    q = rng.integers(-4, 5, (H * G, d)).astype(np.float32)
+    sel = np.stack([rng.permutation(N)[:B] for _ in range(H)]).astype(np.int32)
+    cnt = np.array([B, B - 2], np.int32)
+    r = orc.recall(q, G, K, N, sel, cnt)
+    for g in range(H * G):
+        h = g // G
+        z = [sum(int(q[g, j]) * int(K[h, t, j]) for j in range(d)) for t in range(N)]
+        top = set(sorted(range(N), key=lambda t: (-z[t], t))[:B])
+        want = len(top & set(sel[h, :cnt[h]].tolist())) / B
+        assert r[g] == want, g
