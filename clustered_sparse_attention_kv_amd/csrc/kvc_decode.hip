@@ -549,14 +549,14 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
 //  - the scores go through wave-private LDS to a lane-per-token layout for
 //    the max and sum (DPP reductions), and back as weights;
 //  - the value rows are gathered and weighted in fp32 on the vector units.
-// Two blocks share each KV head: both select and score all keys, and block
-// `part` gathers and weights channels [64 part, 64 part + 64) of the values
-// (8 lanes per 64-channel half row), writing those output channels. The two
+// P blocks share each KV head (P = 2, or 4 and 8 when there are few heads,
+// so that the grid still covers the chip): all select and score all keys,
+// and block `part` gathers and weights channels [part D / P, (part + 1) D / P)
+// of the values (8 channels per lane), writing those output channels. The
 // blocks of a head get block indices 8 apart, so the round-robin dispatch
-// over the 8 XCDs places them on one XCD and its L2 serves the second read of
-// the keys and centroids; results do not depend on the placement.
-constexpr int DEC_PARTS = 2;
-template <int G>
+// over the 8 XCDs places them on one XCD and its L2 serves the repeated reads
+// of the keys and centroids; results do not depend on the placement.
+template <int G, int P>
 __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ cent_t, int C, const int32_t* __restrict__ sizes,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ token_ids,
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
   static_assert(G <= 8, "at most 8 query heads per KV head");
   constexpr int NW = SEL_THREADS / WAVE;
   constexpr int EMIT = 2048;                 // selected ids staged per pass
-  constexpr int HC = D / DEC_PARTS;          // value channels per block
+  constexpr int HC = D / P;                  // value channels per block
   constexpr int RPS = WAVE / (HC / 8);       // value rows per load instruction (8 with 64 channels)
   constexpr int VR = 64 / RPS;               // value rows per lane per slice
   __shared__ SelShared S;
@@ -577,9 +577,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
   __shared__ float ored[NW][G][HC];
   __shared__ float wm[NW][G], wl[NW][G];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int within = blockIdx.x % (8 * DEC_PARTS);
+  const int within = blockIdx.x % (8 * P);
   const int part = within / 8;
-  const int h = blockIdx.x / (8 * DEC_PARTS) * 8 + within % 8;
+  const int h = blockIdx.x / (8 * P) * 8 + within % 8;
   if (h >= heads) return;  // whole block: the grid covers heads rounded up to 8
   const int vgrp = lane / (HC / 8), vgl = lane % (HC / 8);  // value row in the load, 8-channel chunk
   const int j16 = lane & 15, kb4 = lane >> 4;
@@ -1184,11 +1184,19 @@ struct FusedArgs {
 
 template <typename KT, int G>
 static void launch_fused(const FusedArgs& a, hipStream_t st) {
-  if constexpr (sizeof(KT) == 2)
-    select_decode_bf16_kernel<G><<<(a.heads + 7) / 8 * 8 * DEC_PARTS, SEL_THREADS, 0, st>>>(
-        (const uint16_t*)a.q, a.cent, a.C, a.sizes, a.offsets, a.token_ids, a.app_offsets, a.app_ids, a.cap,
-        (const uint16_t*)a.kc, (const uint16_t*)a.vc, (const uint16_t*)a.kp, (const uint16_t*)a.vp, a.packed,
-        a.heads, a.B, a.qscale, a.out, a.sel_ids, a.sel_count);
+  if constexpr (sizeof(KT) == 2) {
+    // enough blocks per head that the grid covers the 256 compute units
+    const int P = a.heads >= 128 ? 2 : (a.heads >= 64 ? 4 : 8);
+    const int nb = (a.heads + 7) / 8 * 8 * P;
+#define KVC_FUSED_ARGS                                                                                             \
+  (const uint16_t*)a.q, a.cent, a.C, a.sizes, a.offsets, a.token_ids, a.app_offsets, a.app_ids, a.cap,          \
+      (const uint16_t*)a.kc, (const uint16_t*)a.vc, (const uint16_t*)a.kp, (const uint16_t*)a.vp, a.packed, a.heads, \
+      a.B, a.qscale, a.out, a.sel_ids, a.sel_count
+    if (P == 2) select_decode_bf16_kernel<G, 2><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
+    else if (P == 4) select_decode_bf16_kernel<G, 4><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
+    else select_decode_bf16_kernel<G, 8><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
+#undef KVC_FUSED_ARGS
+  }
   else
     select_decode_kernel<KT, G><<<a.heads, SEL_THREADS, 0, st>>>(
         (const KT*)a.q, a.cent, a.C, a.sizes, a.offsets, a.token_ids, a.app_offsets, a.app_ids, a.cap,
