@@ -42,14 +42,50 @@ __global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __
       kv[tid] = (double)load_f32(ks, tid);
     }
     __syncthreads();
+    // thread tid scores centroids tid and tid + 256 (C <= 512): half rows of
+    // both operand rows are requested at once in 16-byte pieces, then the two
+    // fp64 chains run side by side over ascending j
     double best = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int c = tid; c < C; c += 256) {
-      double s = 0.0;
-      for (int j = 0; j < D; ++j) s = fma(kv[j], (double)load_f32(Ch, (size_t)c * D + j), s);
-      if (s > best) {
-        best = s;
-        bi = c;
+    {
+      constexpr int EPP = 16 / (int)sizeof(KT);  // elements per 16-byte piece
+      constexpr int HP = D / EPP / 2;            // pieces per half row
+      const int c0 = tid, c1 = tid + 256;
+      const u32x4* r0 = reinterpret_cast<const u32x4*>(Ch + (size_t)(c0 < C ? c0 : 0) * D);
+      const u32x4* r1 = reinterpret_cast<const u32x4*>(Ch + (size_t)(c1 < C ? c1 : 0) * D);
+      double s0 = 0.0, s1 = 0.0;
+#pragma unroll 1
+      for (int half = 0; half < 2; ++half) {
+        u32x4 x0[HP], x1[HP];
+#pragma unroll
+        for (int i = 0; i < HP; ++i) {
+          x0[i] = r0[half * HP + i];
+          x1[i] = r1[half * HP + i];
+        }
+#pragma unroll
+        for (int i = 0; i < HP; ++i)
+#pragma unroll
+          for (int e = 0; e < EPP; ++e) {
+            float a, b;
+            if constexpr (sizeof(KT) == 2) {
+              a = (e & 1) ? __uint_as_float(x0[i][e >> 1] & 0xFFFF0000u) : __uint_as_float(x0[i][e >> 1] << 16);
+              b = (e & 1) ? __uint_as_float(x1[i][e >> 1] & 0xFFFF0000u) : __uint_as_float(x1[i][e >> 1] << 16);
+            } else {
+              a = __uint_as_float(x0[i][e]);
+              b = __uint_as_float(x1[i][e]);
+            }
+            const double kj = kv[(half * HP + i) * EPP + e];
+            s0 = fma(kj, (double)a, s0);
+            s1 = fma(kj, (double)b, s1);
+          }
+      }
+      if (c0 < C) {
+        best = s0;
+        bi = c0;
+      }
+      if (c1 < C && s1 > best) {
+        best = s1;
+        bi = c1;
       }
     }
 #pragma unroll
