@@ -36,7 +36,8 @@ class _Index(C.Structure):
                 ("centroids", C.c_void_p), ("centroids_op", C.c_void_p), ("labels", C.c_void_p),
                 ("sizes", C.c_void_p), ("offsets", C.c_void_p), ("token_ids", C.c_void_p),
                 ("app_offsets", C.c_void_p), ("app_ids", C.c_void_p), ("dev_flags", C.c_void_p),
-                ("centroids_t", C.c_void_p), ("k_packed", C.c_void_p), ("v_packed", C.c_void_p)]
+                ("centroids_t", C.c_void_p), ("k_packed", C.c_void_p), ("v_packed", C.c_void_p),
+                ("n_sink", C.c_int32)]
 
 
 def lib():
@@ -129,9 +130,11 @@ class ClusterIndex:
     """Device memory of one cluster index (``kvc_index``), allocated with torch."""
 
     def __init__(self, heads: int, C_: int, capacity: int, dtype: torch.dtype = torch.bfloat16,
-                 d: int = HEAD_DIM, device="cuda", packed: bool = False):
+                 d: int = HEAD_DIM, device="cuda", packed: bool = False, n_sink: int = 0):
         """packed: also allocate the cluster-ordered copies of the keys and
-        values (``kv_cluster_pack``), two more arrays of the caches' size."""
+        values (``kv_cluster_pack``), two more arrays of the caches' size.
+        n_sink: attention sinks, kept out of the clustering and always
+        selected first."""
         self.heads, self.C, self.capacity, self.d, self.dtype = heads, C_, capacity, d, dtype
         i32 = dict(dtype=torch.int32, device=device)
         self.centroids = torch.zeros(heads, C_, d, dtype=torch.float32, device=device)
@@ -152,7 +155,8 @@ class ClusterIndex:
                          self.app_offsets.data_ptr(), self.app_ids.data_ptr(), self.dev_flags.data_ptr(),
                          self.centroids_t.data_ptr(),
                          self.k_packed.data_ptr() if packed else None,
-                         self.v_packed.data_ptr() if packed else None)
+                         self.v_packed.data_ptr() if packed else None, n_sink)
+        self.n_sink = n_sink
 
     @property
     def n_build(self) -> int:

@@ -17,7 +17,7 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 bool index_ok(const kvc_index* idx) {
   return idx && idx->centroids && idx->centroids_op && idx->labels && idx->sizes && idx->offsets && idx->token_ids &&
          idx->app_offsets && idx->app_ids && idx->dev_flags && idx->centroids_t && idx->heads >= 1 && idx->capacity >= 1 && idx->C >= 1 &&
-         (idx->dtype == KVC_F32 || idx->dtype == KVC_BF16);
+         (idx->dtype == KVC_F32 || idx->dtype == KVC_BF16) && idx->n_sink >= 0;
 }
 
 int index_support(const kvc_index* idx) {
@@ -70,23 +70,29 @@ int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, c
   if (!index_ok(idx) || !keys || !init_idx || !ws) return KVC_ERR_INVALID_ARG;
   if (int s = index_support(idx)) return s;
   const int H = idx->heads, C = idx->C, cap = idx->capacity, cpad = kv_cluster_cpad(C);
-  if (L < C || L > cap || iters < 1 || iters > 100000) return KVC_ERR_INVALID_ARG;
-  const BuildWs w = carve_build(ws, H, L, C, iters);
+  const int ns = idx->n_sink;
+  if (ns < 0 || L - ns < C || L > cap || iters < 1 || iters > 100000) return KVC_ERR_INVALID_ARG;
+  // the clustered rows: [ns, L); their labels start at labels + ns, and the
+  // index stores their absolute positions
+  const int Lc = L - ns;
+  const void* keys_c = static_cast<const char*>(keys) + (size_t)ns * KVC_HEAD_DIM * (idx->dtype == KVC_BF16 ? 2 : 4);
+  const BuildWs w = carve_build(ws, H, Lc, C, iters);
   if (ws_bytes < w.bytes) return KVC_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const long long hs = (long long)cap * KVC_HEAD_DIM;
   idx->packed = 0;  // the index changes: any packed copy is stale
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.qcount), (size_t)iters * H, 0, st);
   if (e == hipSuccess) e = launch_fill_i32(idx->app_offsets, (size_t)H * (C + 1), 0, st);
+  if (e == hipSuccess) e = launch_fill2d_i32(idx->labels, H, cap, ns, -1, st);  // sinks: in no cluster
   if (e == hipSuccess)
-    e = launch_init_centroids(idx->dtype, keys, hs, H, L, init_idx, C, cpad, idx->centroids, idx->centroids_t,
+    e = launch_init_centroids(idx->dtype, keys, hs, H, ns, L, init_idx, C, cpad, idx->centroids, idx->centroids_t,
                               idx->centroids_op, idx->dev_flags, st);
   for (int t = 0; t < iters && e == hipSuccess; ++t) {
     hipEvent_t* ev = assign_events ? (hipEvent_t*)assign_events + 2 * t : nullptr;
-    e = launch_assign(idx->dtype, keys, hs, H, L, idx->centroids_op, C, cpad, idx->labels, cap, w.queue,
+    e = launch_assign(idx->dtype, keys_c, hs, H, Lc, idx->centroids_op, C, cpad, idx->labels + ns, cap, w.queue,
                       w.qcount + (size_t)t * H, nullptr, ev, st);
     if (e == hipSuccess)
-      e = launch_csr(idx->labels, cap, H, L, C, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, st);
+      e = launch_csr(idx->labels + ns, cap, H, Lc, C, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, ns, st);
     if (e == hipSuccess)
       e = launch_update(idx->dtype, keys, hs, H, C, cpad, idx->sizes, idx->offsets, idx->token_ids, cap,
                         idx->centroids, idx->centroids_t, idx->centroids_op, st);
@@ -116,7 +122,7 @@ int kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const
 }
 
 int kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, size_t ws_bytes, void* stream) {
-  if (!index_ok(idx) || !keys || !ws) return KVC_ERR_INVALID_ARG;
+  if (!index_ok(idx) || !keys || !ws || idx->n_sink != 0) return KVC_ERR_INVALID_ARG;
   if (int s = index_support(idx)) return s;
   const int H = idx->heads, C = idx->C, cap = idx->capacity, cpad = kv_cluster_cpad(C);
   if (L < 1 || L > cap) return KVC_ERR_INVALID_ARG;
@@ -124,7 +130,7 @@ int kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, s
   if (ws_bytes < w.bytes) return KVC_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   idx->packed = 0;  // the index changes: any packed copy is stale
-  hipError_t e = launch_csr(idx->labels, cap, H, L, C, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, st);
+  hipError_t e = launch_csr(idx->labels, cap, H, L, C, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, 0, st);
   if (e == hipSuccess)
     e = launch_update(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, C, cpad, idx->sizes, idx->offsets,
                       idx->token_ids, cap, idx->centroids, idx->centroids_t, idx->centroids_op, st);
@@ -156,8 +162,8 @@ int kv_cluster_select(const kvc_index* idx, const void* q, int q_heads, int B, i
   if (G > KVC_MAX_G) return KVC_ERR_UNSUPPORTED;
   if ((long long)idx->heads * B >= (1ll << 31)) return KVC_ERR_INVALID_ARG;
   return hip_status(launch_select(idx->dtype, q, G, idx->centroids_t, idx->heads, idx->C, idx->sizes, idx->offsets,
-                                  idx->token_ids, idx->app_offsets, idx->app_ids, idx->capacity, B, sel_ids,
-                                  sel_count, static_cast<hipStream_t>(stream)));
+                                  idx->token_ids, idx->app_offsets, idx->app_ids, idx->capacity, idx->n_sink, B,
+                                  sel_ids, sel_count, static_cast<hipStream_t>(stream)));
 }
 
 size_t kv_sparse_decode_workspace_bytes(int heads, int q_heads, int d, int B) {
@@ -196,7 +202,7 @@ int kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, c
   return hip_status(launch_select_decode(idx->dtype, q, G, idx->centroids_t, idx->heads, idx->C, idx->sizes,
                                          idx->offsets, idx->token_ids, idx->app_offsets, idx->app_ids, idx->capacity,
                                          k_cache, v_cache, packed ? idx->k_packed : nullptr,
-                                         packed ? idx->v_packed : nullptr, B, scale, out, sel_ids, sel_count,
+                                         packed ? idx->v_packed : nullptr, idx->n_sink, B, scale, out, sel_ids, sel_count,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -205,7 +211,8 @@ int kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, vo
   if (int s = index_support(idx)) return s;
   if (idx->n_build < 1) return KVC_ERR_INVALID_ARG;
   const int e = hip_status(launch_pack(idx->dtype, k_cache, v_cache, idx->capacity, idx->heads, idx->token_ids,
-                                       idx->n_build, idx->k_packed, idx->v_packed, static_cast<hipStream_t>(stream)));
+                                       idx->n_build - idx->n_sink, idx->k_packed, idx->v_packed,
+                                       static_cast<hipStream_t>(stream)));
   if (e == KVC_OK) idx->packed = 1;
   return e;
 }

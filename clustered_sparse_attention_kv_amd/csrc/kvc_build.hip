@@ -62,7 +62,7 @@ __device__ __forceinline__ void store_centroid(float* cent_row, float* cent_t_he
 
 template <typename KT>
 __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restrict__ keys, long long head_stride,
-                                                             int L, const int32_t* __restrict__ init_idx, int C,
+                                                             int lo, int L, const int32_t* __restrict__ init_idx, int C,
                                                              int cpad, float* __restrict__ cent,
                                                              float* __restrict__ cent_t, KT* __restrict__ chat,
                                                              int32_t* __restrict__ dev_flags) {
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restric
     return;
   }
   int tok = init_idx[(size_t)h * C + k];
-  if (tok < 0 || tok >= L) {
+  if (tok < lo || tok >= L) {
     if (lane == 0) atomicOr(dev_flags, 1);
     tok = 0;
   }
@@ -454,7 +454,8 @@ __global__ __launch_bounds__(512) void csr_scan_kernel(int C, int nblk, int32_t*
 __global__ __launch_bounds__(CS_BLOCK) void csr_scatter_kernel(const int32_t* __restrict__ labels,
                                                                long long label_stride, int L, int C, int nblk,
                                                                const int32_t* __restrict__ hist,
-                                                               int32_t* __restrict__ token_ids, long long ids_stride) {
+                                                               int32_t* __restrict__ token_ids, long long ids_stride,
+                                                               int id_base) {
   constexpr int NW = CS_BLOCK / WAVE;
   __shared__ int wh[NW][512];
   const int h = blockIdx.y, b = blockIdx.x;
@@ -484,7 +485,7 @@ __global__ __launch_bounds__(CS_BLOCK) void csr_scatter_kernel(const int32_t* __
   }
   if (lab >= 0) {
     const int rank = __popcll(same & ((1ull << lane) - 1ull));
-    token_ids[(size_t)h * ids_stride + wh[w][lab] + rank] = i;
+    token_ids[(size_t)h * ids_stride + wh[w][lab] + rank] = id_base + i;
   }
 }
 
@@ -572,6 +573,17 @@ __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys
   normalize_row(c0, c1, rows[w], chat + ((size_t)h * cpad + k) * D);
 }
 
+// rows x cols int32 values at a row stride (the attention sinks' labels)
+__global__ void fill2d_i32_kernel(int32_t* __restrict__ p, long long stride, int cols, int value) {
+  for (int c = threadIdx.x; c < cols; c += blockDim.x) p[(size_t)blockIdx.x * stride + c] = value;
+}
+
+hipError_t launch_fill2d_i32(int32_t* p, int rows, long long stride, int cols, int value, hipStream_t st) {
+  if (rows < 1 || cols < 1) return hipSuccess;
+  fill2d_i32_kernel<<<rows, 256, 0, st>>>(p, stride, cols, value);
+  return hipGetLastError();
+}
+
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, size_t n, int32_t v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -588,15 +600,15 @@ hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t v, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_init_centroids(int dtype, const void* keys, long long head_stride, int heads, int L,
+hipError_t launch_init_centroids(int dtype, const void* keys, long long head_stride, int heads, int lo, int L,
                                  const int32_t* init_idx, int C, int cpad, float* cent, float* cent_t, void* chat,
                                  int32_t* flags, hipStream_t st) {
   dim3 grid(grid1(cpad, 4), heads);
   if (dtype == DT_BF16)
-    init_centroids_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, L, init_idx, C, cpad,
+    init_centroids_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, lo, L, init_idx, C, cpad,
                                                           cent, cent_t, (uint16_t*)chat, flags);
   else
-    init_centroids_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, L, init_idx, C, cpad, cent,
+    init_centroids_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, lo, L, init_idx, C, cpad, cent,
                                                        cent_t, (float*)chat, flags);
   return hipGetLastError();
 }
@@ -688,7 +700,8 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
 }
 
 hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, int L, int C, int32_t* hist,
-                      int32_t* sizes, int32_t* offsets, int32_t* token_ids, long long ids_stride, hipStream_t st) {
+                      int32_t* sizes, int32_t* offsets, int32_t* token_ids, long long ids_stride, int id_base,
+                      hipStream_t st) {
   const int nblk = csr_blocks(L);
   csr_count_kernel<<<dim3(nblk, heads), 256, 0, st>>>(labels, label_stride, L, C, nblk, hist);
   hipError_t e = hipGetLastError();
@@ -697,7 +710,7 @@ hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   csr_scatter_kernel<<<dim3(nblk, heads), CS_BLOCK, 0, st>>>(labels, label_stride, L, C, nblk, hist, token_ids,
-                                                             ids_stride);
+                                                             ids_stride, id_base);
   return hipGetLastError();
 }
 

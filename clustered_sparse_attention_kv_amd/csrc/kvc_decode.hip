@@ -276,12 +276,17 @@ __device__ __forceinline__ void select_phase(SelShared& S, const QT* __restrict_
   __syncthreads();
 }
 
-// Entry at output position p (< total) of the ranked, trimmed selection:
-// the token id, or with a packed copy (packed = true) the row of the copy for
-// a built member (its position in the index, offset + member) and ~token for
-// a token appended after the build.
+// Entry at output position p (< n_sink + total) of the ranked, trimmed
+// selection: positions below n_sink are the attention sinks (tokens 0 ..
+// n_sink - 1, always recalled first), the rest come from the clusters. The
+// entry is the token id, or with a packed copy (packed = true) the row of the
+// copy for a built member (its position in the index, offset + member) and
+// ~token for a sink or a token appended after the build (both are read from
+// the caches).
 __device__ __forceinline__ int select_emit(const SelShared& S, int p, const int32_t* __restrict__ ids_h,
-                                           const int32_t* __restrict__ app_h, bool packed = false) {
+                                           const int32_t* __restrict__ app_h, bool packed, int n_sink) {
+  if (p < n_sink) return packed ? ~p : p;
+  p -= n_sink;
   int lo = 0, hi = SEL_THREADS - 1;  // last r with W[r] <= p
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -316,16 +321,16 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const QT* __restric
                                                              const int32_t* __restrict__ token_ids,
                                                              const int32_t* __restrict__ app_offsets,
                                                              const int32_t* __restrict__ app_ids, long long cap, int B,
-                                                             int32_t* __restrict__ sel_ids,
+                                                             int n_sink, int32_t* __restrict__ sel_ids,
                                                              int32_t* __restrict__ sel_count) {
   __shared__ SelShared S;
   const int h = blockIdx.x, tid = threadIdx.x;
   select_phase(S, q, G, cent_t, C, sizes, offsets, app_offsets, h);
-  const int cnt = S.total < B ? S.total : B;
+  const int cnt = n_sink + S.total < B ? n_sink + S.total : B;
   const int32_t* ids_h = token_ids + (size_t)h * cap;
   const int32_t* app_h = app_ids + (size_t)h * cap;
   for (int p = tid; p < B; p += SEL_THREADS)
-    sel_ids[(size_t)h * B + p] = p < cnt ? select_emit(S, p, ids_h, app_h) : -1;
+    sel_ids[(size_t)h * B + p] = p < cnt ? select_emit(S, p, ids_h, app_h, false, n_sink) : -1;
   if (tid == 0) sel_count[h] = cnt;
 }
 
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ token_ids,
     const int32_t* __restrict__ app_offsets, const int32_t* __restrict__ app_ids, long long cap,
     const KT* __restrict__ kc, const KT* __restrict__ vc, const KT* __restrict__ kp, const KT* __restrict__ vp,
-    int packed, int B, float qscale, float* __restrict__ out, int32_t* __restrict__ sel_ids,
+    int packed, int n_sink, int B, float qscale, float* __restrict__ out, int32_t* __restrict__ sel_ids,
     int32_t* __restrict__ sel_count) {
   constexpr int NW = SEL_THREADS / WAVE;                       // 8 waves
   constexpr int RS = (G <= 4 && sizeof(KT) == 2) ? 16 : (G <= 2 ? 8 : 4);  // row steps per load batch
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = lane >> 4, gl = lane & 15;
   select_phase(S, q, G, cent_t, C, sizes, offsets, app_offsets, h);
-  const int cnt = S.total < B ? S.total : B;
+  const int cnt = n_sink + S.total < B ? n_sink + S.total : B;
   if (sel_count && tid == 0) sel_count[h] = cnt;
   if (sel_ids)
     for (int p = cnt + tid; p < B; p += SEL_THREADS) sel_ids[(size_t)h * B + p] = -1;
@@ -451,7 +456,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
     const int nchunk = cnt - c0 < SEL_THREADS ? cnt - c0 : SEL_THREADS;
     {
       const int p = c0 + tid;
-      const int ent = tid < nchunk ? select_emit(S, p, ids_h, app_h, packed) : 0;
+      const int ent = tid < nchunk ? select_emit(S, p, ids_h, app_h, packed, n_sink) : 0;
       sel[tid] = ent;
       if (sel_ids && tid < nchunk) sel_ids[(size_t)h * B + p] = sel_token(ids_h, ent, packed);
     }
@@ -598,8 +603,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ token_ids,
     const int32_t* __restrict__ app_offsets, const int32_t* __restrict__ app_ids, long long cap,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, const uint16_t* __restrict__ kp,
-    const uint16_t* __restrict__ vp, int packed, int heads, int B, float qscale, float* __restrict__ out,
-    int32_t* __restrict__ sel_ids, int32_t* __restrict__ sel_count) {
+    const uint16_t* __restrict__ vp, int packed, int n_sink, int heads, int B, float qscale,
+    float* __restrict__ out, int32_t* __restrict__ sel_ids, int32_t* __restrict__ sel_count) {
   static_assert(G <= 8, "at most 8 query heads per KV head");
   constexpr int NW = SEL_THREADS / WAVE;
   constexpr int EMIT = 2048;                 // selected ids staged per pass
@@ -620,7 +625,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
   const int vgrp = lane / (HC / 8), vgl = lane % (HC / 8);  // value row in the load, 8-channel chunk
   const int j16 = lane & 15, kb4 = lane >> 4;
   select_phase(S, q, G, cent_t, C, sizes, offsets, app_offsets, h);
-  const int cnt = S.total < B ? S.total : B;
+  const int cnt = n_sink + S.total < B ? n_sink + S.total : B;
   const bool writer = part == 0;  // one block per head publishes the selection
   if (writer && sel_count && tid == 0) sel_count[h] = cnt;
   if (writer && sel_ids)
@@ -656,7 +661,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     const int nb = cnt - base < EMIT ? cnt - base : EMIT;
     if (base > 0) __syncthreads();  // every wave is done with the previous ids
     for (int p = tid; p < nb; p += SEL_THREADS) {
-      const int ent = select_emit(S, base + p, ids_h, app_h, packed);
+      const int ent = select_emit(S, base + p, ids_h, app_h, packed, n_sink);
       sel[p] = ent;
       if (writer && sel_ids) sel_ids[(size_t)h * B + base + p] = sel_token(ids_h, ent, packed);
     }
@@ -1194,14 +1199,14 @@ hipError_t launch_append(int dtype, void* kc, void* vc, long long head_stride, i
 
 hipError_t launch_select(int dtype, const void* q, int G, const float* cent, int heads, int C, const int32_t* sizes,
                          const int32_t* offsets, const int32_t* token_ids, const int32_t* app_offsets,
-                         const int32_t* app_ids, long long cap, int B, int32_t* sel_ids, int32_t* sel_count,
-                         hipStream_t st) {
+                         const int32_t* app_ids, long long cap, int n_sink, int B, int32_t* sel_ids,
+                         int32_t* sel_count, hipStream_t st) {
   if (dtype == DT_BF16)
     select_kernel<uint16_t><<<heads, SEL_THREADS, 0, st>>>((const uint16_t*)q, G, cent, C, sizes, offsets, token_ids,
-                                                           app_offsets, app_ids, cap, B, sel_ids, sel_count);
+                                                           app_offsets, app_ids, cap, B, n_sink, sel_ids, sel_count);
   else
     select_kernel<float><<<heads, SEL_THREADS, 0, st>>>((const float*)q, G, cent, C, sizes, offsets, token_ids,
-                                                        app_offsets, app_ids, cap, B, sel_ids, sel_count);
+                                                        app_offsets, app_ids, cap, B, n_sink, sel_ids, sel_count);
   return hipGetLastError();
 }
 
@@ -1212,7 +1217,7 @@ struct FusedArgs {
   const int32_t *sizes, *offsets, *token_ids, *app_offsets, *app_ids;
   long long cap;
   const void *kc, *vc, *kp, *vp;  // kp, vp: packed copies, or the caches when not packed
-  int packed, B;
+  int packed, n_sink, B;
   float qscale;
   float* out;
   int32_t *sel_ids, *sel_count;
@@ -1226,8 +1231,8 @@ static void launch_fused(const FusedArgs& a, hipStream_t st) {
     const int nb = (a.heads + 7) / 8 * 8 * P;
 #define KVC_FUSED_ARGS                                                                                             \
   (const uint16_t*)a.q, a.cent, a.C, a.sizes, a.offsets, a.token_ids, a.app_offsets, a.app_ids, a.cap,          \
-      (const uint16_t*)a.kc, (const uint16_t*)a.vc, (const uint16_t*)a.kp, (const uint16_t*)a.vp, a.packed, a.heads, \
-      a.B, a.qscale, a.out, a.sel_ids, a.sel_count
+      (const uint16_t*)a.kc, (const uint16_t*)a.vc, (const uint16_t*)a.kp, (const uint16_t*)a.vp, a.packed, a.n_sink, \
+      a.heads, a.B, a.qscale, a.out, a.sel_ids, a.sel_count
     if (P == 2) select_decode_bf16_kernel<G, 2><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
     else if (P == 4) select_decode_bf16_kernel<G, 4><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
     else select_decode_bf16_kernel<G, 8><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
@@ -1236,8 +1241,8 @@ static void launch_fused(const FusedArgs& a, hipStream_t st) {
   else
     select_decode_kernel<KT, G><<<a.heads, SEL_THREADS, 0, st>>>(
         (const KT*)a.q, a.cent, a.C, a.sizes, a.offsets, a.token_ids, a.app_offsets, a.app_ids, a.cap,
-        (const KT*)a.kc, (const KT*)a.vc, (const KT*)a.kp, (const KT*)a.vp, a.packed, a.B, a.qscale, a.out,
-        a.sel_ids, a.sel_count);
+        (const KT*)a.kc, (const KT*)a.vc, (const KT*)a.kp, (const KT*)a.vp, a.packed, a.n_sink, a.B, a.qscale,
+        a.out, a.sel_ids, a.sel_count);
 }
 
 template <typename KT>
@@ -1255,10 +1260,10 @@ static hipError_t fused_dispatch(int G, const FusedArgs& a, hipStream_t st) {
 hipError_t launch_select_decode(int dtype, const void* q, int G, const float* cent, int heads, int C,
                                 const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids,
                                 const int32_t* app_offsets, const int32_t* app_ids, long long cap, const void* kc,
-                                const void* vc, const void* kp, const void* vp, int B, float scale, float* out,
-                                int32_t* sel_ids, int32_t* sel_count, hipStream_t st) {
+                                const void* vc, const void* kp, const void* vp, int n_sink, int B, float scale,
+                                float* out, int32_t* sel_ids, int32_t* sel_count, hipStream_t st) {
   FusedArgs a{q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc, vc,
-              kp ? kp : kc, vp ? vp : vc, kp && vp ? 1 : 0, B, scale * 1.4426950408889634f, out, sel_ids,
+              kp ? kp : kc, vp ? vp : vc, kp && vp ? 1 : 0, n_sink, B, scale * 1.4426950408889634f, out, sel_ids,
               sel_count};
   if (dtype == DT_BF16) return fused_dispatch<uint16_t>(G, a, st);
   return fused_dispatch<float>(G, a, st);

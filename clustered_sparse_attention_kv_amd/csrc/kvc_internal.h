@@ -13,14 +13,16 @@ constexpr int DEC_MAX_PAIRS = 512;  // splits x query heads one merge block hold
 int csr_blocks(int L);
 
 hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t v, hipStream_t st);
-hipError_t launch_init_centroids(int dtype, const void* keys, long long head_stride, int heads, int L,
+hipError_t launch_init_centroids(int dtype, const void* keys, long long head_stride, int heads, int lo, int L,
                                  const int32_t* init_idx, int C, int cpad, float* cent, float* cent_t, void* chat,
                                  int32_t* flags, hipStream_t st);
 hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
                          int cpad, int32_t* labels, long long label_stride, int32_t* queue, uint32_t* qcount,
                          float* top2, hipEvent_t* events, hipStream_t st);
+hipError_t launch_fill2d_i32(int32_t* p, int rows, long long stride, int cols, int value, hipStream_t st);
 hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, int L, int C, int32_t* hist,
-                      int32_t* sizes, int32_t* offsets, int32_t* token_ids, long long ids_stride, hipStream_t st);
+                      int32_t* sizes, int32_t* offsets, int32_t* token_ids, long long ids_stride, int id_base,
+                      hipStream_t st);
 hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cpad,
                          const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
                          float* cent, float* cent_t, void* chat, hipStream_t st);
@@ -31,16 +33,16 @@ hipError_t launch_append(int dtype, void* kc, void* vc, long long head_stride, i
                          hipStream_t st);
 hipError_t launch_select(int dtype, const void* q, int G, const float* cent, int heads, int C, const int32_t* sizes,
                          const int32_t* offsets, const int32_t* token_ids, const int32_t* app_offsets,
-                         const int32_t* app_ids, long long cap, int B, int32_t* sel_ids, int32_t* sel_count,
-                         hipStream_t st);
+                         const int32_t* app_ids, long long cap, int n_sink, int B, int32_t* sel_ids,
+                         int32_t* sel_count, hipStream_t st);
 hipError_t launch_decode(int dtype, const void* q, int G, const void* kc, const void* vc, long long head_stride,
                          int heads, const int32_t* sel_ids, const int32_t* sel_count, int B, float scale, float* out,
                          float* part, hipStream_t st);
 hipError_t launch_select_decode(int dtype, const void* q, int G, const float* cent, int heads, int C,
                                 const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids,
                                 const int32_t* app_offsets, const int32_t* app_ids, long long cap, const void* kc,
-                                const void* vc, const void* kp, const void* vp, int B, float scale, float* out,
-                                int32_t* sel_ids, int32_t* sel_count, hipStream_t st);
+                                const void* vc, const void* kp, const void* vp, int n_sink, int B, float scale,
+                                float* out, int32_t* sel_ids, int32_t* sel_count, hipStream_t st);
 // kp, vp: the packed copies (both non-null) or null (rows from the caches).
 void dense_split(int n, int G, int* nsplit, int* T);
 hipError_t launch_dense_decode(const void* q, int G, const void* kc, const void* vc, long long cap, int heads, int n,

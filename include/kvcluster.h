@@ -96,6 +96,9 @@ typedef struct kvc_index {
   void* k_packed;         /* optional (NULL): [heads, capacity, d] in dtype; kv_cluster_pack writes
                              the built tokens' key rows in index order (row i = token_ids[i]) */
   void* v_packed;         /* optional (NULL): the value rows in the same order */
+  int32_t n_sink;         /* attention sinks (III.B): tokens 0 .. n_sink-1 are kept out of the
+                             clustering (label -1) and always selected first; 0 = none. Set by
+                             the caller before kv_cluster_build. */
 } kvc_index;
 
 /* Rows of centroids_op per head: C rounded up to the matrix-core tile (32). */
@@ -108,9 +111,12 @@ size_t kv_cluster_build_workspace_bytes(int heads, int L, int C, int iters);
  * Prefill clustering (III.B; Sys-B). For every head, the first L rows of
  * `keys` ([heads, capacity, d], idx->dtype) are clustered into idx->C
  * clusters by `iters` iterations of cosine k-means:
+ *   - only rows idx->n_sink .. L-1 are clustered: the attention sinks before
+ *     them keep label -1 and are not in the index (kv_cluster_select puts them
+ *     first). Requires 0 <= n_sink and C <= L - n_sink;
  *   - initial centroids are the keys at init_idx[h*C + k] ([heads, C] int32
- *     token positions, distinct, in [0, L); the seeded shuffle that picks them
- *     is the caller's input). An index out of range sets bit 0 of
+ *     token positions, distinct, in [n_sink, L); the seeded shuffle that picks
+ *     them is the caller's input). An index out of range sets bit 0 of
  *     *idx->dev_flags and row 0 is used instead;
  *   - each iteration normalises the centroids (rounded once to idx->dtype),
  *     assigns every key to the centroid of largest cosine similarity (lowest
@@ -155,12 +161,13 @@ int kv_cluster_append(kvc_index* idx, void* k_cache, void* v_cache, const void* 
  *   - the G = q_heads / heads query heads of h are summed (fp64),
  *   - score_k = fp64 dot product of that sum with centroid k (ascending
  *     channel order), the logit of the centroid's attention weight,
- *   - clusters are taken in order of (score descending, id ascending), each
- *     contributing its tokens in ascending position order, until B tokens are
- *     taken; the last cluster is trimmed to fit.
+ *   - the idx->n_sink attention sinks come first (tokens 0 .. n_sink-1, as
+ *     many as B allows); then clusters are taken in order of (score
+ *     descending, id ascending), each contributing its tokens in ascending
+ *     position order, until B tokens are taken; the last cluster is trimmed.
  * q is [q_heads, d] in idx->dtype. sel_ids [heads, B] receives the selected
  * token positions (in rank order; -1 past the count) and sel_count [heads]
- * receives min(B, tokens in the index). Requires B >= 1 and G <= 8.
+ * receives min(B, n_sink + tokens in the index). Requires B >= 1 and G <= 8.
  */
 int kv_cluster_select(const kvc_index* idx, const void* q, int q_heads, int B, int32_t* sel_ids,
                       int32_t* sel_count, void* stream);
@@ -240,7 +247,8 @@ int kv_dense_decode(const void* q, int q_heads, const void* k_cache, const void*
 int kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token_ids, void* stream);
 
 /*
- * Single steps of the build, for checking each kernel on its own.
+ * Single steps of the build, for checking each kernel on its own (an index
+ * without attention sinks: kv_cluster_debug_update rejects n_sink != 0).
  *  - kv_cluster_debug_assign: labels [heads, capacity] of the first L keys
  *    under the given operand chat [heads, cpad(C), d] (same rule as the
  *    build). top2 (optional, [heads, L, 2] fp32) receives the matrix-core

@@ -156,13 +156,27 @@ def inertia(K: np.ndarray, chat: np.ndarray, labels: np.ndarray) -> float:
 
 
 def build(K: np.ndarray, C: int, iters: int, init_idx: np.ndarray, L: int | None = None,
-          mode: int = 0, early_exit: bool = True) -> dict:
+          mode: int = 0, early_exit: bool = True, n_sink: int = 0) -> dict:
     """Prefill clustering of every head of K [H, rows, d] over its first L rows.
 
     mode 0: centroids fp32, operand in the key type; mode 1: exact (fp64).
+    n_sink: the first n_sink rows are attention sinks (III.B keeps the first
+    tokens apart and clusters the rest): they get label -1, stay out of every
+    cluster, and init_idx holds positions >= n_sink. token_ids hold the
+    clustered tokens' positions (L - n_sink of them).
     Returns a dict with c, chat, labels, sizes, offsets, token_ids, inertia,
     iters_run.
     """
+    if n_sink:
+        H, rows, _ = K.shape
+        L = rows if L is None else L
+        r = build(np.ascontiguousarray(K[:, n_sink:L]), C, iters, np.asarray(init_idx, np.int32) - n_sink,
+                  mode=mode, early_exit=early_exit)
+        labels = np.full((H, L), -1, dtype=np.int32)
+        labels[:, n_sink:] = r["labels"]
+        r["labels"] = labels
+        r["token_ids"] = r["token_ids"] + np.int32(n_sink)
+        return r
     lib = _load()
     K = _c(K)
     H, rows, d = K.shape
@@ -194,7 +208,7 @@ class Index:
     def __init__(self, built: dict, capacity: int):
         H, L = built["labels"].shape
         self.H, self.C = built["sizes"].shape
-        self.n = L
+        self.n = L  # tokens, sinks included; the next one gets position n
         self.c = built["c"]
         self.chat = built["chat"]
         self.labels = np.full((H, capacity), -1, dtype=np.int32)
@@ -202,7 +216,8 @@ class Index:
         self.sizes = built["sizes"].copy()
         self.offsets = built["offsets"].copy()
         self.token_ids = np.full((H, capacity), -1, dtype=np.int32)
-        self.token_ids[:, :L] = built["token_ids"]
+        nc = built["token_ids"].shape[1]
+        self.token_ids[:, :nc] = built["token_ids"]
 
     def append(self, knew: np.ndarray) -> np.ndarray:
         """knew [H, d]: one new key per head; returns the labels."""
@@ -224,9 +239,25 @@ class Index:
 
 
 def select(q: np.ndarray, G: int, c: np.ndarray, sizes: np.ndarray, offsets: np.ndarray,
-           token_ids: np.ndarray, B: int):
+           token_ids: np.ndarray, B: int, n_sink: int = 0):
     """q [H*G, d]; c fp32 [H, C, d]; CSR arrays per head. Returns
-    (sel_ids [H, B], sel_count [H], scores [H, C], order [H, C])."""
+    (sel_ids [H, B], sel_count [H], scores [H, C], order [H, C]).
+
+    n_sink: attention sinks (III.B) are always recalled: the first min(B,
+    n_sink) entries are tokens 0 .. n_sink - 1, and the clusters fill the
+    remaining B - n_sink entries as without sinks."""
+    if n_sink:
+        H = c.shape[0]
+        ns = min(B, n_sink)
+        rest = max(B - n_sink, 1)
+        s2, c2, scores, order = select(q, G, c, sizes, offsets, token_ids, rest)
+        sel = np.full((H, B), -1, dtype=np.int32)
+        sel[:, :ns] = np.arange(ns, dtype=np.int32)
+        cnt = np.full(H, ns, dtype=np.int32)
+        if B > n_sink:
+            sel[:, n_sink:] = s2
+            cnt = cnt + c2
+        return sel, cnt, scores, order
     lib = _load()
     q = _c(q)
     c = _c(c, np.float32)

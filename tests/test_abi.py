@@ -76,6 +76,11 @@ def test_build_rejects(kvc):
     assert build(make_index(kvc, Cn=16), Lk=15) == INVALID          # L < C
     assert build(make_index(kvc, cap=256), Lk=257) == INVALID       # L > capacity
     assert build(make_index(kvc), iters=0) == INVALID
+    sinks = make_index(kvc, Cn=16)
+    sinks.n_sink = -1
+    assert build(sinks) == INVALID                                  # negative sink count
+    sinks.n_sink = 190
+    assert build(sinks, Lk=200) == INVALID                          # fewer clustered rows than C
     need = L.kv_cluster_build_workspace_bytes(4, 200, 16, 10)
     assert build(make_index(kvc), ws_bytes=need - 1) == WORKSPACE
 

@@ -254,6 +254,63 @@ def test_dense_decode_matches_full_attention():
         assert err <= 2e-3
 
 
+def test_attention_sinks_end_to_end():
+    """III.B: the first tokens are attention sinks, kept out of the clustering
+    and always recalled. Build, selection (split and fused, from the caches and
+    from the packed copy, budgets below, at and above the sink count), attention
+    and appends against the oracle with the same n_sink."""
+    w, n_sink = SMALL_APPEND, 16
+    base, K, V, init, means = make_inputs(w)
+    H = K.shape[0]
+    init = synth.init_idx(base, H, w.L - n_sink, w.C) + n_sink
+    idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w), packed=True, n_sink=n_sink)
+    Kc, Vc = K.copy(), V.copy()
+    Kc[:, w.L:], Vc[:, w.L:] = 0, 0
+    Kd, Vd = to_dev(Kc), to_dev(Vc)
+    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    torch.cuda.synchronize()
+    assert int(to_np(idx.dev_flags)[0]) == 0
+    ref = oracle.build(np.ascontiguousarray(K[:, :w.L]), w.C, w.iters, init, n_sink=n_sink)
+    gl = to_np(idx.labels)[:, :w.L]
+    assert np.all(gl[:, :n_sink] == -1)
+    assert np.array_equal(gl, ref["labels"])
+    assert np.array_equal(to_np(idx.centroids), ref["c"])
+    nc = w.L - n_sink
+    assert np.array_equal(to_np(idx.sizes), ref["sizes"]) and np.array_equal(to_np(idx.offsets), ref["offsets"])
+    assert np.array_equal(to_np(idx.token_ids)[:, :nc], ref["token_ids"])
+    built = dict(labels=gl, sizes=to_np(idx.sizes), offsets=to_np(idx.offsets),
+                 token_ids=to_np(idx.token_ids)[:, :nc], c=to_np(idx.centroids), chat=to_np(idx.centroids_op)[:, :w.C])
+    oi = oracle.Index(built, w.capacity)
+    scale = 1.0 / math.sqrt(w.d)
+    n = w.L
+    for step in range(4):
+        if step > 0:  # append one token per head
+            kvc.append(idx, Kd, Vd, to_dev(np.ascontiguousarray(K[:, n:n + 1])),
+                       to_dev(np.ascontiguousarray(V[:, n:n + 1])))
+            oi.append(np.ascontiguousarray(K[:, n]))
+            n += 1
+        if step == 0:
+            kvc.pack(idx, Kd, Vd)
+        q = queries(w, base, step, K, n, means)
+        for B in (w.B, 5, n_sink, n + 40):
+            osel, ocnt, _, _ = oracle.select(q, w.G, oi.c, oi.sizes, oi.offsets, oi.token_ids, B, n_sink=n_sink)
+            od = oracle.decode(q, w.G, K, V, osel, ocnt, scale)
+            sel, cnt = kvc.select(idx, to_dev(q), B)
+            out = kvc.sparse_decode(to_dev(q), Kd, Vd, sel, cnt, scale)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_np(sel), osel) and np.array_equal(to_np(cnt), ocnt), (step, B)
+            assert np.abs(to_np(out) - od).max() <= 2e-3
+            for pk in (1, 0):
+                idx._s.packed = pk
+                fsel = torch.full((H, B), -7, dtype=torch.int32, device="cuda")
+                fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel)
+                torch.cuda.synchronize()
+                assert np.array_equal(to_np(fsel), osel), (step, B, pk)
+                assert np.abs(to_np(fout) - od).max() <= 2e-3, (step, B, pk)
+            idx._s.packed = 1
+        say(f"  sinks: step {step}, {n} tokens, count {ocnt.tolist()}")
+
+
 def test_init_index_out_of_range_flag():
     w = SMALL
     base, K, V, init, _ = make_inputs(w)

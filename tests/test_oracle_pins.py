@@ -463,3 +463,31 @@ def test_recall_brute_force(orc):
         top = set(sorted(range(N), key=lambda t: (-z[t], t))[:B])
         want = len(top & set(sel[h, :cnt[h]].tolist())) / B
         assert r[g] == want, g
+
+
+# ------------------------------------------------------------------- sinks
+
+def test_sinks_stay_out_of_clusters_and_are_always_selected(orc, syn):
+    """III.B: the first tokens are kept as attention sinks and only the rest
+    are clustered. Building with n_sink equals building the remaining rows
+    alone (ids shifted by n_sink); the selection always starts with the sinks,
+    which count toward B, and the clusters fill the rest."""
+    n_sink, C, L, B = 16, 9, 300, 64
+    base = syn.config_seed(95)
+    K, _, _ = syn.mixture_keys(base, 2, L, 8, 6, 0.3, 0, 1.0, syn.F32)
+    init = syn.init_idx(base, 2, L - n_sink, C) + n_sink
+    r = orc.build(K, C, 5, init, n_sink=n_sink)
+    alone = orc.build(np.ascontiguousarray(K[:, n_sink:]), C, 5, init - n_sink)
+    assert np.all(r["labels"][:, :n_sink] == -1)
+    assert np.array_equal(r["labels"][:, n_sink:], alone["labels"])
+    assert np.array_equal(r["token_ids"], alone["token_ids"] + n_sink)
+    assert np.array_equal(r["c"], alone["c"]) and r["sizes"].sum(axis=1).tolist() == [L - n_sink] * 2
+    q = syn.normal_array(syn.stream_seed(base, 0, 9), 2 * 8, 1.0, syn.F32).reshape(2, 8)
+    sel, cnt, _, _ = orc.select(q, 1, r["c"], r["sizes"], r["offsets"], r["token_ids"], B, n_sink=n_sink)
+    rest, rcnt, _, _ = orc.select(q, 1, r["c"], r["sizes"], r["offsets"], r["token_ids"], B - n_sink)
+    assert cnt.tolist() == [B, B]
+    assert np.all(sel[:, :n_sink] == np.arange(n_sink))
+    assert np.array_equal(sel[:, n_sink:], rest)
+    # a budget within the sinks recalls sinks only
+    sel, cnt, _, _ = orc.select(q, 1, r["c"], r["sizes"], r["offsets"], r["token_ids"], 5, n_sink=n_sink)
+    assert cnt.tolist() == [5, 5] and np.all(sel == np.arange(5))
