@@ -112,6 +112,8 @@ def main():
     ap.add_argument("--decode-path", choices=["fused", "split"], default="fused",
                     help="fused: kv_cluster_select_decode (one kernel per step); "
                          "split: kv_cluster_select then kv_sparse_decode")
+    ap.add_argument("--sinks", type=int, default=0,
+                    help="attention sinks per head: kept out of the clustering, always selected (default 0)")
     ap.add_argument("--no-pack", action="store_true",
                     help="decode from the caches through the token ids (no cluster-ordered copy)")
     ap.add_argument("--cpu-heads", type=int, default=16, help="KV heads in the CPU baseline sample")
@@ -156,7 +158,7 @@ def main():
         K, _, means = synth.mixture_keys(base, H, cap, d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype,
                                          want_means=(w.query == "mixture"))
         V = synth.values(base, H, cap, d, w.dtype)
-        init = synth.init_idx(base, H, L, C)
+        init = synth.init_idx(base, H, L - args.sinks, C) + args.sinks
         qs = []
         for s in range(w.steps):
             n_cur = L + (s + 1 if w.append else 0)
@@ -172,7 +174,7 @@ def main():
             K[:, L:] = 0
             V[:, L:] = 0
         e["Kd"], e["Vd"] = to_dev(K), to_dev(V)
-        e["idx"] = kvc.ClusterIndex(H, C, cap, tdt, device=dev, packed=packed)
+        e["idx"] = kvc.ClusterIndex(H, C, cap, tdt, device=dev, packed=packed, n_sink=args.sinks)
         if li == 0:
             base0, init0, Q0 = base, init, Q
         lay.append(e)
@@ -325,7 +327,8 @@ def main():
         "config": {"workload": w.name, "layers": NL, "kv_heads_total": H * NL, "q_heads_total": H * G * NL, "G": G,
                    "L": L, "d": d, "C": C,
                    "kmeans_iters": w.iters, "B": B, "decode_steps_per_step": w.steps, "append": w.append,
-                   "decode_path": args.decode_path, "packed_kv": packed},
+                   "decode_path": args.decode_path, "packed_kv": packed,
+                   "sinks": args.sinks},
         "kmeans_tflops": kmeans_tflops,
         "kmeans_ms": mean(build_ms),
         "pack_ms": mean(pack_ms),
@@ -389,13 +392,15 @@ def cpu_baseline(w, args, base, init, Q):
     K, _, _ = synth.mixture_keys(base, nh, w.L, w.d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype)
     V = synth.values(base, nh, w.L, w.d, w.dtype)
     t0 = time.perf_counter()
-    built = oracle.build(K, w.C, 1, init[:nh], early_exit=False)   # one k-means iteration of the sample
+    built = oracle.build(K, w.C, 1, init[:nh], early_exit=False,  # one k-means iteration of the sample
+                         n_sink=args.sinks)
     t_iter = time.perf_counter() - t0
     scale = 1.0 / math.sqrt(w.d)
     t0 = time.perf_counter()
     for s in range(ns):
         q = np.ascontiguousarray(Q[s, :nh * w.G])
-        sel, cnt, _, _ = oracle.select(q, w.G, built["c"], built["sizes"], built["offsets"], built["token_ids"], w.B)
+        sel, cnt, _, _ = oracle.select(q, w.G, built["c"], built["sizes"], built["offsets"], built["token_ids"], w.B,
+                                       n_sink=args.sinks)
         oracle.decode(q, w.G, K, V, sel, cnt, scale)
     t_dec = (time.perf_counter() - t0) / ns
     per_step_full = t_dec * w.heads * w.layers / nh
