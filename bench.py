@@ -114,6 +114,11 @@ def main():
                          "split: kv_cluster_select then kv_sparse_decode")
     ap.add_argument("--sinks", type=int, default=0,
                     help="attention sinks per head: kept out of the clustering, always selected (default 0)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="append workloads: generated tokens join a window that is always recalled, and every "
+                         "WINDOW steps the window is clustered on its own into --window-clusters new clusters "
+                         "(default 0: each new token joins its nearest centroid)")
+    ap.add_argument("--window-clusters", type=int, default=4, help="clusters made from each window (default 4)")
     ap.add_argument("--no-pack", action="store_true",
                     help="decode from the caches through the token ids (no cluster-ordered copy)")
     ap.add_argument("--cpu-heads", type=int, default=16, help="KV heads in the CPU baseline sample")
@@ -142,6 +147,12 @@ def main():
     tdt = torch.bfloat16 if w.dtype == synth.BF16 else torch.float32
     packed = not args.no_pack and args.decode_path == "fused"
     fused = args.decode_path == "fused"
+    M, NC = args.window, args.window_clusters
+    if M and not w.append:
+        print("--window needs a workload that generates tokens (an append workload)", file=sys.stderr)
+        sys.exit(2)
+    n_windows = w.steps // M if M else 0
+    slots = C + n_windows * NC
 
     def to_dev(a):
         if a.dtype == np.uint16:
@@ -174,7 +185,10 @@ def main():
             K[:, L:] = 0
             V[:, L:] = 0
         e["Kd"], e["Vd"] = to_dev(K), to_dev(V)
-        e["idx"] = kvc.ClusterIndex(H, C, cap, tdt, device=dev, packed=packed, n_sink=args.sinks)
+        e["idx"] = kvc.ClusterIndex(H, C, cap, tdt, device=dev, packed=packed, n_sink=args.sinks, c_slots=slots)
+        # initial centroids of each window's clustering: seeded positions in the window
+        e["winit"] = [to_dev(synth.init_idx(synth.stream_seed(base, 7, k), H, M, NC) + np.int32(L + k * M))
+                      for k in range(n_windows)]
         if li == 0:
             base0, init0, Q0 = base, init, Q
         lay.append(e)
@@ -182,6 +196,8 @@ def main():
     log(f"[bench] generated {w.name} inputs ({NL} layer(s)) in {time.time() - t0:.1f}s")
     ws_build = torch.empty(kvc.build_workspace_bytes(H, L, C, w.iters), dtype=torch.uint8, device=dev)
     ws_dec = torch.empty(kvc.decode_workspace_bytes(H, H * G, B), dtype=torch.uint8, device=dev)
+    ws_win = (torch.empty(kvc.window_workspace_bytes(H, M, NC, w.iters), dtype=torch.uint8, device=dev)
+              if M else None)
     sel = torch.empty(H, B, dtype=torch.int32, device=dev)
     cnt = torch.empty(H, dtype=torch.int32, device=dev)
     out = torch.empty(H * G, d, dtype=torch.float32, device=dev)
@@ -199,11 +215,12 @@ def main():
     # the builds, 4 bracketing the builds, the packed copies and the decode
     # phase, and, on every SAMPLE-th decode step only (events between kernels
     # add dispatch gaps), 6 around that step's first-layer kernels (append,
-    # select, decode)
+    # select, decode), and 2 around each window clustering of the first layer
     SAMPLE = 8
     sampled = [s for s in range(w.steps) if s % SAMPLE == 0]
     A = 2 * w.iters * NL
-    per_pass = A + 4 + 6 * len(sampled)
+    WB = A + 4 + 6 * len(sampled)
+    per_pass = WB + 2 * n_windows
     total_passes = args.warmup + args.steps
     ev = HipEvents(per_pass * total_passes + 2)
 
@@ -225,8 +242,19 @@ def main():
                 rec = (lambda i: ev.record(e6 + i, sh)) if e6 is not None else (lambda i: None)
                 if w.append:
                     rec(0)
-                    kvc.append(e["idx"], e["Kd"], e["Vd"], e["Knew"][s].unsqueeze(1), e["Vnew"][s].unsqueeze(1))
+                    if M:
+                        kvc.append_window(e["idx"], e["Kd"], e["Vd"], e["Knew"][s].unsqueeze(1),
+                                          e["Vnew"][s].unsqueeze(1))
+                    else:
+                        kvc.append(e["idx"], e["Kd"], e["Vd"], e["Knew"][s].unsqueeze(1), e["Vnew"][s].unsqueeze(1))
                     rec(1)
+                    if M and (s + 1) % M == 0:
+                        k = (s + 1) // M - 1
+                        if li == 0:
+                            ev.record(o + WB + 2 * k, sh)
+                        kvc.cluster_window(e["idx"], e["Kd"], e["Vd"], NC, w.iters, e["winit"][k], workspace=ws_win)
+                        if li == 0:
+                            ev.record(o + WB + 2 * k + 1, sh)
                 rec(2)
                 if fused:
                     rec(3)
@@ -251,6 +279,7 @@ def main():
     total_ms = ev.ms(per_pass * total_passes, per_pass * total_passes + 1)
 
     assign_ms, build_ms, select_ms, decode_ms, append_ms, phase_ms, pack_ms = [], [], [], [], [], [], []
+    window_ms = []
     for p in range(args.warmup, total_passes):
         o = p * per_pass
         assign_ms += [ev.ms(o + 2 * t, o + 2 * t + 1) for t in range(w.iters * NL)]
@@ -264,6 +293,7 @@ def main():
                 append_ms.append(ev.ms(e6, e6 + 1))
             select_ms.append(ev.ms(e6 + 2, e6 + 3))
             decode_ms.append(ev.ms(e6 + 3, e6 + 4))
+        window_ms += [ev.ms(o + WB + 2 * k, o + WB + 2 * k + 1) for k in range(n_windows)]
 
     alg = algorithmic(w)
     mean = lambda x: sum(x) / len(x) if x else 0.0
@@ -328,7 +358,7 @@ def main():
                    "L": L, "d": d, "C": C,
                    "kmeans_iters": w.iters, "B": B, "decode_steps_per_step": w.steps, "append": w.append,
                    "decode_path": args.decode_path, "packed_kv": packed,
-                   "sinks": args.sinks},
+                   "sinks": args.sinks, "window": M, "window_clusters": NC if M else 0},
         "kmeans_tflops": kmeans_tflops,
         "kmeans_ms": mean(build_ms),
         "pack_ms": mean(pack_ms),
@@ -342,6 +372,9 @@ def main():
     }
     if w.append:
         result["append_us"] = mean(append_ms) * 1e3
+    if M:
+        result["cluster_window_us"] = mean(window_ms) * 1e3
+        result["clusters_after_pass"] = C + n_windows * NC
 
     # ---------------- full-KV comparator (dense decode over all L rows) -----
     if w.dtype == synth.BF16:

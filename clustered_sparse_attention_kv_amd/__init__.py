@@ -37,7 +37,8 @@ class _Index(C.Structure):
                 ("sizes", C.c_void_p), ("offsets", C.c_void_p), ("token_ids", C.c_void_p),
                 ("app_offsets", C.c_void_p), ("app_ids", C.c_void_p), ("dev_flags", C.c_void_p),
                 ("centroids_t", C.c_void_p), ("k_packed", C.c_void_p), ("v_packed", C.c_void_p),
-                ("n_sink", C.c_int32)]
+                ("n_sink", C.c_int32), ("c_slots", C.c_int32), ("c_active", C.c_int32),
+                ("window_start", C.c_int32)]
 
 
 def lib():
@@ -55,6 +56,10 @@ def lib():
         L.kv_cluster_build.argtypes = [p, p, i, i, p, p, sz, p]
         L.kv_cluster_build_timed.argtypes = [p, p, i, i, p, p, sz, p, p]
         L.kv_cluster_append.argtypes = [p, p, p, p, p, i, p]
+        L.kv_cluster_append_window.argtypes = [p, p, p, p, p, i, p]
+        L.kv_cluster_window_workspace_bytes.argtypes = [i, i, i, i]
+        L.kv_cluster_window_workspace_bytes.restype = sz
+        L.kv_cluster_cluster_window.argtypes = [p, p, p, i, i, p, p, sz, p]
         L.kv_cluster_select.argtypes = [p, p, i, i, p, p, p]
         L.kv_sparse_decode_workspace_bytes.argtypes = [i, i, i, i]
         L.kv_sparse_decode_workspace_bytes.restype = sz
@@ -69,8 +74,9 @@ def lib():
         L.kv_cluster_debug_update.argtypes = [p, p, i, p, sz, p]
         L.kv_cluster_status_string.argtypes = [i]
         L.kv_cluster_status_string.restype = C.c_char_p
-        for name in ("kv_cluster_build", "kv_cluster_build_timed", "kv_cluster_append", "kv_cluster_select", "kv_sparse_decode",
-                     "kv_cluster_select_decode", "kv_cluster_export_csr", "kv_cluster_pack", "kv_dense_decode", "kv_cluster_debug_assign",
+        for name in ("kv_cluster_build", "kv_cluster_build_timed", "kv_cluster_append", "kv_cluster_append_window",
+                     "kv_cluster_cluster_window", "kv_cluster_select", "kv_sparse_decode", "kv_cluster_select_decode",
+                     "kv_cluster_export_csr", "kv_cluster_pack", "kv_dense_decode", "kv_cluster_debug_assign",
                      "kv_cluster_debug_update"):
             getattr(L, name).restype = i
         _lib = L
@@ -130,23 +136,26 @@ class ClusterIndex:
     """Device memory of one cluster index (``kvc_index``), allocated with torch."""
 
     def __init__(self, heads: int, C_: int, capacity: int, dtype: torch.dtype = torch.bfloat16,
-                 d: int = HEAD_DIM, device="cuda", packed: bool = False, n_sink: int = 0):
+                 d: int = HEAD_DIM, device="cuda", packed: bool = False, n_sink: int = 0, c_slots: int = 0):
         """packed: also allocate the cluster-ordered copies of the keys and
         values (``kv_cluster_pack``), two more arrays of the caches' size.
         n_sink: attention sinks, kept out of the clustering and always
-        selected first."""
+        selected first. c_slots: cluster slots per head (>= C; 0 for C), room
+        for the clusters that ``cluster_window`` adds."""
         self.heads, self.C, self.capacity, self.d, self.dtype = heads, C_, capacity, d, dtype
+        S = c_slots if c_slots else C_
+        self.slots = S
         i32 = dict(dtype=torch.int32, device=device)
-        self.centroids = torch.zeros(heads, C_, d, dtype=torch.float32, device=device)
-        self.centroids_op = torch.zeros(heads, cpad(C_), d, dtype=dtype, device=device)
+        self.centroids = torch.zeros(heads, S, d, dtype=torch.float32, device=device)
+        self.centroids_op = torch.zeros(heads, cpad(S), d, dtype=dtype, device=device)
         self.labels = torch.full((heads, capacity), -1, **i32)
-        self.sizes = torch.zeros(heads, C_, **i32)
-        self.offsets = torch.zeros(heads, C_ + 1, **i32)
+        self.sizes = torch.zeros(heads, S, **i32)
+        self.offsets = torch.zeros(heads, S + 1, **i32)
         self.token_ids = torch.full((heads, capacity), -1, **i32)
-        self.app_offsets = torch.zeros(heads, C_ + 1, **i32)
+        self.app_offsets = torch.zeros(heads, S + 1, **i32)
         self.app_ids = torch.full((heads, capacity), -1, **i32)
         self.dev_flags = torch.zeros(1, **i32)
-        self.centroids_t = torch.zeros(heads, d // 4, C_, 4, dtype=torch.float32, device=device)
+        self.centroids_t = torch.zeros(heads, d // 4, S, 4, dtype=torch.float32, device=device)
         self.k_packed = torch.empty(heads, capacity, d, dtype=dtype, device=device) if packed else None
         self.v_packed = torch.empty(heads, capacity, d, dtype=dtype, device=device) if packed else None
         self._s = _Index(heads, d, C_, capacity, _dtype_code(dtype), 0, 0, 0,
@@ -155,7 +164,7 @@ class ClusterIndex:
                          self.app_offsets.data_ptr(), self.app_ids.data_ptr(), self.dev_flags.data_ptr(),
                          self.centroids_t.data_ptr(),
                          self.k_packed.data_ptr() if packed else None,
-                         self.v_packed.data_ptr() if packed else None, n_sink)
+                         self.v_packed.data_ptr() if packed else None, n_sink, c_slots, 0, 0)
         self.n_sink = n_sink
 
     @property
@@ -165,6 +174,14 @@ class ClusterIndex:
     @property
     def n_tokens(self) -> int:
         return self._s.n_tokens
+
+    @property
+    def c_active(self) -> int:
+        return self._s.c_active
+
+    @property
+    def window_start(self) -> int:
+        return self._s.window_start
 
     def ref(self):
         return C.byref(self._s)
@@ -205,14 +222,53 @@ def append(idx: ClusterIndex, k_cache: torch.Tensor, v_cache: torch.Tensor, k_ne
     """kv_cluster_append: k_new, v_new [heads, n_new, d]."""
     _cache_check(idx, k_cache, "k_cache")
     _cache_check(idx, v_cache, "v_cache")
+    k_new, v_new, n_new = _new_rows(idx, k_new, v_new)
+    _check(lib().kv_cluster_append(idx.ref(), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), n_new,
+                                   _stream(stream)), "kv_cluster_append")
+
+
+def _new_rows(idx: ClusterIndex, k_new: torch.Tensor, v_new: torch.Tensor):
     if k_new.dim() == 2:
         k_new, v_new = k_new.unsqueeze(1), v_new.unsqueeze(1)
     n_new = k_new.shape[1]
     for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
         if t.dtype != idx.dtype or tuple(t.shape) != (idx.heads, n_new, idx.d):
             raise ValueError(f"{nm} must be {idx.dtype} [{idx.heads}, n_new, {idx.d}]")
-    _check(lib().kv_cluster_append(idx.ref(), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), n_new,
-                                   _stream(stream)), "kv_cluster_append")
+    return k_new, v_new, n_new
+
+
+def append_window(idx: ClusterIndex, k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+                  v_new: torch.Tensor, stream=None):
+    """kv_cluster_append_window: k_new, v_new [heads, n_new, d] join the window
+    of generated tokens (recalled whole until cluster_window)."""
+    _cache_check(idx, k_cache, "k_cache")
+    _cache_check(idx, v_cache, "v_cache")
+    k_new, v_new, n_new = _new_rows(idx, k_new, v_new)
+    _check(lib().kv_cluster_append_window(idx.ref(), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), n_new,
+                                          _stream(stream)), "kv_cluster_append_window")
+
+
+def window_workspace_bytes(heads: int, m: int, n_clusters: int, iters: int) -> int:
+    return lib().kv_cluster_window_workspace_bytes(heads, m, n_clusters, iters)
+
+
+def cluster_window(idx: ClusterIndex, k_cache: torch.Tensor, v_cache: torch.Tensor, n_clusters: int, iters: int,
+                   init_idx: torch.Tensor, workspace: torch.Tensor | None = None, stream=None):
+    """kv_cluster_cluster_window: the window's tokens become n_clusters new
+    clusters; init_idx int32 [heads, n_clusters] holds token positions in the
+    window."""
+    _cache_check(idx, k_cache, "k_cache")
+    _cache_check(idx, v_cache, "v_cache")
+    if init_idx.dtype != torch.int32 or tuple(init_idx.shape) != (idx.heads, n_clusters):
+        raise ValueError("init_idx must be int32 [heads, n_clusters]")
+    m = idx.n_tokens - idx.window_start
+    need = window_workspace_bytes(idx.heads, max(m, 1), max(n_clusters, 1), max(iters, 1))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=k_cache.device)
+    _check(lib().kv_cluster_cluster_window(idx.ref(), _ptr(k_cache), _ptr(v_cache), n_clusters, iters,
+                                           _ptr(init_idx), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "kv_cluster_cluster_window")
+    return workspace
 
 
 def select(idx: ClusterIndex, q: torch.Tensor, B: int, sel_ids: torch.Tensor | None = None,
@@ -304,8 +360,8 @@ def dense_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
 
 
 def export_csr(idx: ClusterIndex, stream=None):
-    """Canonical index (built + appended parts): (offsets [heads, C+1], token_ids [heads, capacity])."""
-    off = torch.empty(idx.heads, idx.C + 1, dtype=torch.int32, device=idx.labels.device)
+    """Canonical index (main + appended parts): (offsets [heads, slots+1], token_ids [heads, capacity])."""
+    off = torch.empty(idx.heads, idx.slots + 1, dtype=torch.int32, device=idx.labels.device)
     ids = torch.full((idx.heads, idx.capacity), -1, dtype=torch.int32, device=idx.labels.device)
     _check(lib().kv_cluster_export_csr(idx.ref(), _ptr(off), _ptr(ids), _stream(stream)), "kv_cluster_export_csr")
     return off, ids

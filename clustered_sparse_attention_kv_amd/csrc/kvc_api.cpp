@@ -14,16 +14,44 @@ namespace {
 constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
+// cluster slots per head: the stride of every per-cluster array
+int slots(const kvc_index* idx) { return idx->c_slots ? idx->c_slots : idx->C; }
+
 bool index_ok(const kvc_index* idx) {
   return idx && idx->centroids && idx->centroids_op && idx->labels && idx->sizes && idx->offsets && idx->token_ids &&
-         idx->app_offsets && idx->app_ids && idx->dev_flags && idx->centroids_t && idx->heads >= 1 && idx->capacity >= 1 && idx->C >= 1 &&
-         (idx->dtype == KVC_F32 || idx->dtype == KVC_BF16) && idx->n_sink >= 0;
+         idx->app_offsets && idx->app_ids && idx->dev_flags && idx->centroids_t && idx->heads >= 1 &&
+         idx->capacity >= 1 && idx->C >= 1 && (idx->dtype == KVC_F32 || idx->dtype == KVC_BF16) &&
+         idx->n_sink >= 0 && (idx->c_slots == 0 || idx->c_slots >= idx->C);
 }
 
 int index_support(const kvc_index* idx) {
-  if (idx->d != KVC_HEAD_DIM || idx->C > KVC_MAX_C) return KVC_ERR_UNSUPPORTED;
+  if (idx->d != KVC_HEAD_DIM || idx->C > KVC_MAX_C || slots(idx) > KVC_MAX_C) return KVC_ERR_UNSUPPORTED;
   if ((long long)idx->heads * idx->capacity >= (1ll << 31)) return KVC_ERR_UNSUPPORTED;
   return KVC_OK;
+}
+
+// the host mirrors of a built index are consistent
+bool built_ok(const kvc_index* idx) {
+  return idx->n_build >= 1 && idx->c_active >= 1 && idx->c_active <= slots(idx) && idx->n_sink <= idx->n_build &&
+         idx->window_start >= idx->n_build && idx->window_start <= idx->n_tokens && idx->n_tokens <= idx->capacity;
+}
+
+// the index as the selection kernels read it
+IndexView view(const kvc_index* idx) {
+  IndexView x{};
+  x.cent_t = idx->centroids_t;
+  x.sizes = idx->sizes;
+  x.offsets = idx->offsets;
+  x.token_ids = idx->token_ids;
+  x.app_offsets = idx->app_offsets;
+  x.app_ids = idx->app_ids;
+  x.cap = idx->capacity;
+  x.cs = slots(idx);
+  x.ca = idx->c_active;
+  x.n_sink = idx->n_sink;
+  x.wlo = idx->window_start;
+  x.nw = idx->n_tokens - idx->window_start;
+  return x;
 }
 
 struct BuildWs {
@@ -46,6 +74,40 @@ BuildWs carve_build(void* base, int heads, int L, int C, int iters) {
   w.bytes = o;
   return w;
 }
+
+// Workspace of the window clustering: the build's scratch for m keys and nc
+// clusters, then the window's own clustering (nc clusters with strides nc and
+// cpad(nc), m tokens).
+struct WindowWs {
+  BuildWs b;
+  float *cent, *cent_t;
+  void* chat;
+  int32_t *labels, *sizes, *offsets, *ids;
+  size_t bytes;
+};
+
+WindowWs carve_window(void* base, int heads, int m, int nc, int iters) {
+  WindowWs w{};
+  w.b = carve_build(base, heads, m, nc, iters);
+  size_t o = w.b.bytes;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t bytes) {
+    char* p = b + o;
+    o = align_up(o + bytes);
+    return p;
+  };
+  w.cent = reinterpret_cast<float*>(take(sizeof(float) * (size_t)heads * nc * KVC_HEAD_DIM));
+  w.cent_t = reinterpret_cast<float*>(take(sizeof(float) * (size_t)heads * nc * KVC_HEAD_DIM));
+  w.chat = take(sizeof(float) * (size_t)heads * kv_cluster_cpad(nc) * KVC_HEAD_DIM);
+  w.labels = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)heads * m));
+  w.sizes = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)heads * nc));
+  w.offsets = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)heads * (nc + 1)));
+  w.ids = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)heads * m));
+  w.bytes = o;
+  return w;
+}
+
+size_t elem_bytes(int dtype) { return dtype == KVC_BF16 ? 2 : 4; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
 
@@ -70,36 +132,40 @@ int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, c
   if (!index_ok(idx) || !keys || !init_idx || !ws) return KVC_ERR_INVALID_ARG;
   if (int s = index_support(idx)) return s;
   const int H = idx->heads, C = idx->C, cap = idx->capacity, cpad = kv_cluster_cpad(C);
+  const int cs = slots(idx), cps = kv_cluster_cpad(cs);
   const int ns = idx->n_sink;
   if (ns < 0 || L - ns < C || L > cap || iters < 1 || iters > 100000) return KVC_ERR_INVALID_ARG;
   // the clustered rows: [ns, L); their labels start at labels + ns, and the
   // index stores their absolute positions
   const int Lc = L - ns;
-  const void* keys_c = static_cast<const char*>(keys) + (size_t)ns * KVC_HEAD_DIM * (idx->dtype == KVC_BF16 ? 2 : 4);
+  const void* keys_c = static_cast<const char*>(keys) + (size_t)ns * KVC_HEAD_DIM * elem_bytes(idx->dtype);
   const BuildWs w = carve_build(ws, H, Lc, C, iters);
   if (ws_bytes < w.bytes) return KVC_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const long long hs = (long long)cap * KVC_HEAD_DIM;
   idx->packed = 0;  // the index changes: any packed copy is stale
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.qcount), (size_t)iters * H, 0, st);
-  if (e == hipSuccess) e = launch_fill_i32(idx->app_offsets, (size_t)H * (C + 1), 0, st);
+  if (e == hipSuccess) e = launch_fill_i32(idx->app_offsets, (size_t)H * (cs + 1), 0, st);
   if (e == hipSuccess) e = launch_fill2d_i32(idx->labels, H, cap, ns, -1, st);  // sinks: in no cluster
   if (e == hipSuccess)
-    e = launch_init_centroids(idx->dtype, keys, hs, H, ns, L, init_idx, C, cpad, idx->centroids, idx->centroids_t,
-                              idx->centroids_op, idx->dev_flags, st);
+    e = launch_init_centroids(idx->dtype, keys, hs, H, ns, L, init_idx, C, cpad, cs, cps, idx->centroids,
+                              idx->centroids_t, idx->centroids_op, idx->dev_flags, st);
   for (int t = 0; t < iters && e == hipSuccess; ++t) {
     hipEvent_t* ev = assign_events ? (hipEvent_t*)assign_events + 2 * t : nullptr;
-    e = launch_assign(idx->dtype, keys_c, hs, H, Lc, idx->centroids_op, C, cpad, idx->labels + ns, cap, w.queue,
+    e = launch_assign(idx->dtype, keys_c, hs, H, Lc, idx->centroids_op, C, cpad, cps, idx->labels + ns, cap, w.queue,
                       w.qcount + (size_t)t * H, nullptr, ev, st);
     if (e == hipSuccess)
-      e = launch_csr(idx->labels + ns, cap, H, Lc, C, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, ns, st);
+      e = launch_csr(idx->labels + ns, cap, H, Lc, C, cs, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, ns,
+                     st);
     if (e == hipSuccess)
-      e = launch_update(idx->dtype, keys, hs, H, C, cpad, idx->sizes, idx->offsets, idx->token_ids, cap,
+      e = launch_update(idx->dtype, keys, hs, H, C, cs, cps, idx->sizes, idx->offsets, idx->token_ids, cap,
                         idx->centroids, idx->centroids_t, idx->centroids_op, st);
   }
   if (e != hipSuccess) return KVC_ERR_HIP;
   idx->n_build = L;
   idx->n_tokens = L;
+  idx->window_start = L;
+  idx->c_active = C;
   return KVC_OK;
 }
 
@@ -114,8 +180,8 @@ int kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.qcount), (size_t)H, 0, st);
   if (e == hipSuccess)
-    e = launch_assign(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, L, chat, C, cpad, labels, cap, w.queue,
-                      w.qcount, top2, nullptr, st);
+    e = launch_assign(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, L, chat, C, cpad, cpad, labels, cap,
+                      w.queue, w.qcount, top2, nullptr, st);
   if (e == hipSuccess && flagged)
     e = hipMemcpyAsync(flagged, w.qcount, sizeof(int32_t) * H, hipMemcpyDeviceToDevice, st);
   return hip_status(e);
@@ -124,15 +190,17 @@ int kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const
 int kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, size_t ws_bytes, void* stream) {
   if (!index_ok(idx) || !keys || !ws || idx->n_sink != 0) return KVC_ERR_INVALID_ARG;
   if (int s = index_support(idx)) return s;
-  const int H = idx->heads, C = idx->C, cap = idx->capacity, cpad = kv_cluster_cpad(C);
+  const int H = idx->heads, C = idx->C, cap = idx->capacity;
+  const int cs = slots(idx), cps = kv_cluster_cpad(cs);
   if (L < 1 || L > cap) return KVC_ERR_INVALID_ARG;
   const BuildWs w = carve_build(ws, H, L, C, 1);
   if (ws_bytes < w.bytes) return KVC_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   idx->packed = 0;  // the index changes: any packed copy is stale
-  hipError_t e = launch_csr(idx->labels, cap, H, L, C, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, 0, st);
+  hipError_t e =
+      launch_csr(idx->labels, cap, H, L, C, cs, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, 0, st);
   if (e == hipSuccess)
-    e = launch_update(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, C, cpad, idx->sizes, idx->offsets,
+    e = launch_update(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, C, cs, cps, idx->sizes, idx->offsets,
                       idx->token_ids, cap, idx->centroids, idx->centroids_t, idx->centroids_op, st);
   return hip_status(e);
 }
@@ -141,15 +209,78 @@ int kv_cluster_append(kvc_index* idx, void* k_cache, void* v_cache, const void* 
                       void* stream) {
   if (!index_ok(idx) || !k_cache || !v_cache || !k_new || !v_new || n_new < 1) return KVC_ERR_INVALID_ARG;
   if (int s = index_support(idx)) return s;
-  if (idx->n_build < 1) return KVC_ERR_INVALID_ARG;
+  if (!built_ok(idx)) return KVC_ERR_INVALID_ARG;
   if ((long long)idx->n_tokens + n_new > idx->capacity) return KVC_ERR_CAPACITY;
-  const int C = idx->C, cap = idx->capacity;
+  if (idx->window_start != idx->n_tokens) return KVC_ERR_INVALID_ARG;  // an open window: cluster it first
+  const int cs = slots(idx), cap = idx->capacity;
   hipError_t e = launch_append(idx->dtype, k_cache, v_cache, (long long)cap * KVC_HEAD_DIM, idx->heads, k_new, v_new,
-                               n_new, idx->n_tokens, idx->n_build, idx->centroids_op, C, kv_cluster_cpad(C),
+                               n_new, idx->n_tokens, idx->centroids_op, idx->c_active, cs, kv_cluster_cpad(cs),
                                idx->labels, cap, idx->sizes, idx->app_offsets, idx->app_ids,
                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return KVC_ERR_HIP;
   idx->n_tokens += n_new;
+  idx->window_start = idx->n_tokens;
+  return KVC_OK;
+}
+
+int kv_cluster_append_window(kvc_index* idx, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                             int n_new, void* stream) {
+  if (!index_ok(idx) || !k_cache || !v_cache || !k_new || !v_new || n_new < 1) return KVC_ERR_INVALID_ARG;
+  if (int s = index_support(idx)) return s;
+  if (!built_ok(idx)) return KVC_ERR_INVALID_ARG;
+  if ((long long)idx->n_tokens + n_new > idx->capacity) return KVC_ERR_CAPACITY;
+  hipError_t e = launch_window_append(idx->dtype, k_cache, v_cache, idx->capacity, idx->heads, k_new, v_new, n_new,
+                                      idx->n_tokens, idx->labels, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  idx->n_tokens += n_new;
+  return KVC_OK;
+}
+
+size_t kv_cluster_window_workspace_bytes(int heads, int m, int n_clusters, int iters) {
+  if (heads < 1 || m < 1 || n_clusters < 1 || iters < 1) return 0;
+  return carve_window(nullptr, heads, m, n_clusters, iters).bytes;
+}
+
+int kv_cluster_cluster_window(kvc_index* idx, const void* k_cache, const void* v_cache, int n_clusters, int iters,
+                              const int32_t* init_idx, void* ws, size_t ws_bytes, void* stream) {
+  if (!index_ok(idx) || !k_cache || !v_cache || !init_idx || !ws) return KVC_ERR_INVALID_ARG;
+  if (int s = index_support(idx)) return s;
+  if (!built_ok(idx)) return KVC_ERR_INVALID_ARG;
+  const int H = idx->heads, cap = idx->capacity, cs = slots(idx), cps = kv_cluster_cpad(cs);
+  const int wlo = idx->window_start, m = idx->n_tokens - wlo, nc = n_clusters, ca = idx->c_active;
+  if (nc < 1 || nc > m || ca + nc > cs || iters < 1 || iters > 100000) return KVC_ERR_INVALID_ARG;
+  const bool packed = idx->packed == 1;
+  if (packed && (!idx->k_packed || !idx->v_packed)) return KVC_ERR_INVALID_ARG;
+  const WindowWs w = carve_window(ws, H, m, nc, iters);
+  if (ws_bytes < w.bytes) return KVC_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const long long hs = (long long)cap * KVC_HEAD_DIM;
+  const int cpw = kv_cluster_cpad(nc);
+  // the window's keys: rows wlo .. n_tokens-1; the index stores absolute positions
+  const void* keys_w = static_cast<const char*>(k_cache) + (size_t)wlo * KVC_HEAD_DIM * elem_bytes(idx->dtype);
+  hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.b.qcount), (size_t)iters * H, 0, st);
+  if (e == hipSuccess)
+    e = launch_init_centroids(idx->dtype, k_cache, hs, H, wlo, idx->n_tokens, init_idx, nc, cpw, nc, cpw, w.cent,
+                              w.cent_t, w.chat, idx->dev_flags, st);
+  for (int t = 0; t < iters && e == hipSuccess; ++t) {
+    e = launch_assign(idx->dtype, keys_w, hs, H, m, w.chat, nc, cpw, cpw, w.labels, m, w.b.queue,
+                      w.b.qcount + (size_t)t * H, nullptr, nullptr, st);
+    if (e == hipSuccess) e = launch_csr(w.labels, m, H, m, nc, nc, w.b.hist, w.sizes, w.offsets, w.ids, m, wlo, st);
+    if (e == hipSuccess)
+      e = launch_update(idx->dtype, k_cache, hs, H, nc, nc, cpw, w.sizes, w.offsets, w.ids, m, w.cent, w.cent_t,
+                        w.chat, st);
+  }
+  if (e == hipSuccess)
+    e = launch_merge_window(idx->dtype, H, nc, m, wlo, w.cent, w.chat, w.labels, w.sizes, w.offsets, w.ids, ca, cs, cps,
+                            idx->centroids, idx->centroids_t, idx->centroids_op, idx->sizes, idx->offsets,
+                            idx->token_ids, idx->labels, cap, st);
+  // the packed copy gains the new members' rows, right after the existing ones
+  if (e == hipSuccess && packed)
+    e = launch_pack(idx->dtype, k_cache, v_cache, cap, H, idx->token_ids, m, idx->offsets + ca, nullptr, cs + 1,
+                    idx->k_packed, idx->v_packed, st);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  idx->c_active = ca + nc;
+  idx->window_start = idx->n_tokens;
   return KVC_OK;
 }
 
@@ -157,13 +288,13 @@ int kv_cluster_select(const kvc_index* idx, const void* q, int q_heads, int B, i
                       void* stream) {
   if (!index_ok(idx) || !q || !sel_ids || !sel_count || B < 1 || q_heads < 1) return KVC_ERR_INVALID_ARG;
   if (int s = index_support(idx)) return s;
-  if (idx->n_build < 1 || q_heads % idx->heads != 0) return KVC_ERR_INVALID_ARG;
+  if (!built_ok(idx) || q_heads % idx->heads != 0) return KVC_ERR_INVALID_ARG;
   const int G = q_heads / idx->heads;
   if (G > KVC_MAX_G) return KVC_ERR_UNSUPPORTED;
   if ((long long)idx->heads * B >= (1ll << 31)) return KVC_ERR_INVALID_ARG;
-  return hip_status(launch_select(idx->dtype, q, G, idx->centroids_t, idx->heads, idx->C, idx->sizes, idx->offsets,
-                                  idx->token_ids, idx->app_offsets, idx->app_ids, idx->capacity, idx->n_sink, B,
-                                  sel_ids, sel_count, static_cast<hipStream_t>(stream)));
+  const IndexView x = view(idx);
+  return hip_status(launch_select(idx->dtype, q, G, x, idx->heads, B, sel_ids, sel_count,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 size_t kv_sparse_decode_workspace_bytes(int heads, int q_heads, int d, int B) {
@@ -194,25 +325,26 @@ int kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, c
                              int32_t* sel_count, void* stream) {
   if (!index_ok(idx) || !q || !k_cache || !v_cache || !out || B < 1 || q_heads < 1) return KVC_ERR_INVALID_ARG;
   if (int s = index_support(idx)) return s;
-  if (idx->n_build < 1 || q_heads % idx->heads != 0) return KVC_ERR_INVALID_ARG;
+  if (!built_ok(idx) || q_heads % idx->heads != 0) return KVC_ERR_INVALID_ARG;
   const int G = q_heads / idx->heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVC_ERR_UNSUPPORTED;
   if ((long long)idx->heads * B >= (1ll << 31)) return KVC_ERR_INVALID_ARG;
+  const IndexView x = view(idx);
   const bool packed = idx->packed == 1 && idx->k_packed && idx->v_packed;
-  return hip_status(launch_select_decode(idx->dtype, q, G, idx->centroids_t, idx->heads, idx->C, idx->sizes,
-                                         idx->offsets, idx->token_ids, idx->app_offsets, idx->app_ids, idx->capacity,
-                                         k_cache, v_cache, packed ? idx->k_packed : nullptr,
-                                         packed ? idx->v_packed : nullptr, idx->n_sink, B, scale, out, sel_ids, sel_count,
-                                         static_cast<hipStream_t>(stream)));
+  return hip_status(launch_select_decode(idx->dtype, q, G, x, idx->heads, k_cache, v_cache,
+                                         packed ? idx->k_packed : nullptr, packed ? idx->v_packed : nullptr, B, scale,
+                                         out, sel_ids, sel_count, static_cast<hipStream_t>(stream)));
 }
 
 int kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, void* stream) {
   if (!index_ok(idx) || !k_cache || !v_cache || !idx->k_packed || !idx->v_packed) return KVC_ERR_INVALID_ARG;
   if (int s = index_support(idx)) return s;
-  if (idx->n_build < 1) return KVC_ERR_INVALID_ARG;
+  if (!built_ok(idx)) return KVC_ERR_INVALID_ARG;
+  // rows 0 .. offsets[h][c_active]-1: the main part, at most n_tokens - n_sink rows
+  const int cs = slots(idx);
   const int e = hip_status(launch_pack(idx->dtype, k_cache, v_cache, idx->capacity, idx->heads, idx->token_ids,
-                                       idx->n_build - idx->n_sink, idx->k_packed, idx->v_packed,
-                                       static_cast<hipStream_t>(stream)));
+                                       idx->n_tokens - idx->n_sink, nullptr, idx->offsets + idx->c_active, cs + 1,
+                                       idx->k_packed, idx->v_packed, static_cast<hipStream_t>(stream)));
   if (e == KVC_OK) idx->packed = 1;
   return e;
 }
@@ -220,8 +352,9 @@ int kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, vo
 int kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token_ids, void* stream) {
   if (!index_ok(idx) || !offsets || !token_ids) return KVC_ERR_INVALID_ARG;
   if (int s = index_support(idx)) return s;
-  return hip_status(launch_export_csr(idx->heads, idx->C, idx->offsets, idx->token_ids, idx->app_offsets,
-                                      idx->app_ids, idx->capacity, offsets, token_ids,
+  if (!built_ok(idx)) return KVC_ERR_INVALID_ARG;
+  return hip_status(launch_export_csr(idx->heads, idx->c_active, slots(idx), idx->offsets, idx->token_ids,
+                                      idx->app_offsets, idx->app_ids, idx->capacity, offsets, token_ids,
                                       static_cast<hipStream_t>(stream)));
 }
 

@@ -47,15 +47,17 @@ __device__ __forceinline__ void normalize_row(const float c0, const float c1, fl
 // ---------------------------------------------------------------------------
 // a1 + a2: initial centroids c_k = K[init_idx[k]] (exact copy to fp32) and
 // their normalised operand. One wave per centroid row, 4 rows per block.
-// Rows k in [C, cpad) of the operand are zeroed.
+// Rows k in [C, cpad) of the operand are zeroed. Per-cluster arrays have a
+// per-head stride of cs cluster slots (cs >= C; the operand has cps =
+// cpad(cs) rows per head), which leaves room for clusters added later.
 // The centroid pair (c0, c1) of channels 2*lane, 2*lane+1 of cluster k, also
-// stored in the chunk-major copy [d/4, C, 4] that selection reads coalesced.
-__device__ __forceinline__ void store_centroid(float* cent_row, float* cent_t_head, int C, int k, float c0, float c1) {
+// stored in the chunk-major copy [d/4, cs, 4] that selection reads coalesced.
+__device__ __forceinline__ void store_centroid(float* cent_row, float* cent_t_head, int cs, int k, float c0, float c1) {
   const int lane = lane_id();
   cent_row[2 * lane] = c0;
   cent_row[2 * lane + 1] = c1;
   const int j = 2 * lane;
-  float* t = cent_t_head + ((size_t)(j >> 2) * C + k) * 4 + (j & 3);
+  float* t = cent_t_head + ((size_t)(j >> 2) * cs + k) * 4 + (j & 3);
   t[0] = c0;
   t[1] = c1;
 }
@@ -63,7 +65,7 @@ __device__ __forceinline__ void store_centroid(float* cent_row, float* cent_t_he
 template <typename KT>
 __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restrict__ keys, long long head_stride,
                                                              int lo, int L, const int32_t* __restrict__ init_idx, int C,
-                                                             int cpad, float* __restrict__ cent,
+                                                             int cpad, int cs, int cps, float* __restrict__ cent,
                                                              float* __restrict__ cent_t, KT* __restrict__ chat,
                                                              int32_t* __restrict__ dev_flags) {
   __shared__ float rows[4][D];
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restric
   const int h = blockIdx.y;
   const int k = blockIdx.x * 4 + w;
   if (k >= cpad) return;
-  KT* out = chat + ((size_t)h * cpad + k) * D;
+  KT* out = chat + ((size_t)h * cps + k) * D;
   if (k >= C) {
     store_op(out, 2 * lane, 0.0);
     store_op(out, 2 * lane + 1, 0.0);
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restric
   }
   const KT* src = keys + (size_t)h * head_stride + (size_t)tok * D;
   const float c0 = load_f32(src, 2 * lane), c1 = load_f32(src, 2 * lane + 1);
-  store_centroid(cent + ((size_t)h * C + k) * D, cent_t + (size_t)h * C * D, C, k, c0, c1);
+  store_centroid(cent + ((size_t)h * cs + k) * D, cent_t + (size_t)h * cs * D, cs, k, c0, c1);
   normalize_row(c0, c1, rows[w], out);
 }
 
@@ -125,14 +127,14 @@ __device__ __forceinline__ void top2_update(float s, int u, float& m1, float& m2
 
 __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     const uint16_t* __restrict__ keys, long long head_stride, int L, const uint16_t* __restrict__ chat, int C,
-    int cpad, int32_t* __restrict__ labels, long long label_stride, int32_t* __restrict__ queue,
+    int cpad, int cps, int32_t* __restrict__ labels, long long label_stride, int32_t* __restrict__ queue,
     uint32_t* __restrict__ qcount, float* __restrict__ top2) {
   extern __shared__ u32x4 sC[];  // cpad rows x 16 chunks of 16 B, chunk c of row r at c ^ (r & 15)
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j16 = lane & 15, kb4 = lane >> 4;
 
-  const u32x4* Cg = reinterpret_cast<const u32x4*>(chat + (size_t)h * cpad * D);
+  const u32x4* Cg = reinterpret_cast<const u32x4*>(chat + (size_t)h * cps * D);
   for (int e = tid; e < cpad * 16; e += AS_THREADS) {
     const int r = e >> 4, c = e & 15;
     sC[r * 16 + (c ^ (r & 15))] = Cg[e];
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
 // banks. Rows come from the per-head queue (queue != null) or are all rows.
 template <typename KT, int MAXT>
 __global__ __launch_bounds__(256) void assign_exact_kernel(const KT* __restrict__ keys, long long head_stride, int L,
-                                                           const KT* __restrict__ chat, int C, int cpad,
+                                                           const KT* __restrict__ chat, int C, int cpad, int cps,
                                                            int32_t* __restrict__ labels, long long label_stride,
                                                            const int32_t* __restrict__ queue,
                                                            const uint32_t* __restrict__ qcount) {
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(256) void assign_exact_kernel(const KT* __restrict_
   const int n = queue ? (int)__atomic_load_n(qcount + h, __ATOMIC_RELAXED) : L;
   if (blockIdx.x * 4 * NK >= n) return;  // no key for this block (uniform): nothing staged
   const KT* Kh = keys + (size_t)h * head_stride;
-  const u32x4* Cg = reinterpret_cast<const u32x4*>(chat + (size_t)h * cpad * D);
+  const u32x4* Cg = reinterpret_cast<const u32x4*>(chat + (size_t)h * cps * D);
   if constexpr (STAGE) {
     for (int e = threadIdx.x; e < cpad * CHUNKS; e += 256) {
       const int r = e / CHUNKS, c = e % CHUNKS;
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(256) void csr_count_kernel(const int32_t* __restric
   for (int c = threadIdx.x; c < C; c += 256) out[c] = cnt[c];
 }
 
-__global__ __launch_bounds__(512) void csr_scan_kernel(int C, int nblk, int32_t* __restrict__ hist,
+__global__ __launch_bounds__(512) void csr_scan_kernel(int C, int cs, int nblk, int32_t* __restrict__ hist,
                                                        int32_t* __restrict__ sizes, int32_t* __restrict__ offsets) {
   __shared__ int sc[512];
   const int h = blockIdx.x, c = threadIdx.x;
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(512) void csr_scan_kernel(int C, int nblk, int32_t*
       hh[(size_t)b * C + c] = run;
       run += v;
     }
-    sizes[(size_t)h * C + c] = run;
+    sizes[(size_t)h * cs + c] = run;
   }
   sc[c] = c < C ? run : 0;
   __syncthreads();
@@ -445,10 +447,10 @@ __global__ __launch_bounds__(512) void csr_scan_kernel(int C, int nblk, int32_t*
   }
   const int excl = sc[c] - (c < C ? run : 0);
   if (c < C) {
-    offsets[(size_t)h * (C + 1) + c] = excl;
+    offsets[(size_t)h * (cs + 1) + c] = excl;
     for (int b = 0; b < nblk; ++b) hh[(size_t)b * C + c] += excl;
   }
-  if (c == C - 1) offsets[(size_t)h * (C + 1) + C] = sc[c];
+  if (c == C - 1) offsets[(size_t)h * (cs + 1) + C] = sc[c];
 }
 
 __global__ __launch_bounds__(CS_BLOCK) void csr_scatter_kernel(const int32_t* __restrict__ labels,
@@ -519,7 +521,7 @@ struct UpdRow<float> {
 
 template <typename KT>
 __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys, long long head_stride, int C,
-                                                     int cpad, const int32_t* __restrict__ sizes,
+                                                     int cs, int cps, const int32_t* __restrict__ sizes,
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ token_ids, long long ids_stride,
                                                      float* __restrict__ cent, float* __restrict__ cent_t,
@@ -531,11 +533,11 @@ __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys
   const int k = blockIdx.x * 4 + w;
   if (k >= C) return;
   // the same value in every lane: scalar registers, uniform branches
-  const int n = __builtin_amdgcn_readfirstlane(sizes[(size_t)h * C + k]);
-  const int off = __builtin_amdgcn_readfirstlane(offsets[(size_t)h * (C + 1) + k]);
+  const int n = __builtin_amdgcn_readfirstlane(sizes[(size_t)h * cs + k]);
+  const int off = __builtin_amdgcn_readfirstlane(offsets[(size_t)h * (cs + 1) + k]);
   const int32_t* ids = token_ids + (size_t)h * ids_stride + off;
   const KT* Kh = keys + (size_t)h * head_stride + 2 * lane;
-  float* cr = cent + ((size_t)h * C + k) * D;
+  float* cr = cent + ((size_t)h * cs + k) * D;
   float c0, c1;
   if (n > 0) {
     double a0 = 0.0, a1 = 0.0;
@@ -565,12 +567,50 @@ __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys
     }
     c0 = (float)(a0 / (double)n);
     c1 = (float)(a1 / (double)n);
-    store_centroid(cr, cent_t + (size_t)h * C * D, C, k, c0, c1);
+    store_centroid(cr, cent_t + (size_t)h * cs * D, cs, k, c0, c1);
   } else {
     c0 = cr[2 * lane];
     c1 = cr[2 * lane + 1];
   }
-  normalize_row(c0, c1, rows[w], chat + ((size_t)h * cpad + k) * D);
+  normalize_row(c0, c1, rows[w], chat + ((size_t)h * cps + k) * D);
+}
+
+// ---------------------------------------------------------------------------
+// Clustering of generated tokens (III.B: the tokens generated since the last
+// clustering are clustered on their own into a few new centroids). The window
+// is clustered by the kernels above into workspace arrays of nc clusters
+// (strides nc, cpad(nc) operand rows, m tokens per head); this kernel moves
+// the result into the index as clusters ca .. ca+nc-1: centroid rows (both
+// layouts and the operand), sizes, offsets continuing the prefix of the
+// existing clusters, member ids after the existing members (so the index
+// order stays the stable sort by label), and the window tokens' labels. One
+// block per head.
+template <typename KT>
+__global__ __launch_bounds__(256) void merge_window_kernel(
+    int nc, int m, int wlo, const float* __restrict__ cent_w, const KT* __restrict__ chat_w,
+    const int32_t* __restrict__ labels_w, const int32_t* __restrict__ sizes_w, const int32_t* __restrict__ offsets_w,
+    const int32_t* __restrict__ ids_w, int ca, int cs, int cps, float* __restrict__ cent, float* __restrict__ cent_t,
+    KT* __restrict__ chat, int32_t* __restrict__ sizes, int32_t* __restrict__ offsets, int32_t* __restrict__ token_ids,
+    int32_t* __restrict__ labels, long long cap) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int cpw = (nc + 31) / 32 * 32;
+  int32_t* off = offsets + (size_t)h * (cs + 1);
+  const int base = off[ca];  // members so far; entries ca+1 .. are written below, entry ca is not
+  for (int e = tid; e < nc * D; e += 256) {
+    const int k = e / D, j = e % D;
+    const float v = cent_w[((size_t)h * nc + k) * D + j];
+    cent[((size_t)h * cs + ca + k) * D + j] = v;
+    cent_t[(size_t)h * cs * D + ((size_t)(j >> 2) * cs + ca + k) * 4 + (j & 3)] = v;
+    chat[((size_t)h * cps + ca + k) * D + j] = chat_w[((size_t)h * cpw + k) * D + j];
+  }
+  for (int k = tid; k < nc; k += 256) {
+    sizes[(size_t)h * cs + ca + k] = sizes_w[(size_t)h * nc + k];
+    off[ca + k + 1] = base + offsets_w[(size_t)h * (nc + 1) + k + 1];
+  }
+  for (int i = tid; i < m; i += 256) {
+    token_ids[(size_t)h * cap + base + i] = ids_w[(size_t)h * m + i];
+    labels[(size_t)h * cap + wlo + i] = ca + labels_w[(size_t)h * m + i];
+  }
 }
 
 // rows x cols int32 values at a row stride (the attention sinks' labels)
@@ -601,21 +641,21 @@ hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t v, hipStream_t st) {
 }
 
 hipError_t launch_init_centroids(int dtype, const void* keys, long long head_stride, int heads, int lo, int L,
-                                 const int32_t* init_idx, int C, int cpad, float* cent, float* cent_t, void* chat,
-                                 int32_t* flags, hipStream_t st) {
+                                 const int32_t* init_idx, int C, int cpad, int cs, int cps, float* cent, float* cent_t,
+                                 void* chat, int32_t* flags, hipStream_t st) {
   dim3 grid(grid1(cpad, 4), heads);
   if (dtype == DT_BF16)
     init_centroids_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, lo, L, init_idx, C, cpad,
-                                                          cent, cent_t, (uint16_t*)chat, flags);
+                                                          cs, cps, cent, cent_t, (uint16_t*)chat, flags);
   else
-    init_centroids_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, lo, L, init_idx, C, cpad, cent,
-                                                       cent_t, (float*)chat, flags);
+    init_centroids_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, lo, L, init_idx, C, cpad, cs,
+                                                       cps, cent, cent_t, (float*)chat, flags);
   return hipGetLastError();
 }
 
 // The exact pass instantiated for the number of 64-centroid groups a lane owns.
 template <typename KT, int MAXT>
-hipError_t launch_exact_t(const KT* keys, long long head_stride, int L, const KT* chat, int C, int cpad,
+hipError_t launch_exact_t(const KT* keys, long long head_stride, int L, const KT* chat, int C, int cpad, int cps,
                           int32_t* labels, long long label_stride, const int32_t* queue, const uint32_t* qcount,
                           dim3 grid, size_t lds, hipStream_t st) {
   if (lds > 64 * 1024) {
@@ -627,19 +667,20 @@ hipError_t launch_exact_t(const KT* keys, long long head_stride, int L, const KT
       attr = true;
     }
   }
-  assign_exact_kernel<KT, MAXT><<<grid, 256, lds, st>>>(keys, head_stride, L, chat, C, cpad, labels, label_stride,
-                                                       queue, qcount);
+  assign_exact_kernel<KT, MAXT><<<grid, 256, lds, st>>>(keys, head_stride, L, chat, C, cpad, cps, labels,
+                                                       label_stride, queue, qcount);
   return hipGetLastError();
 }
 
 template <typename KT>
-hipError_t launch_exact(const KT* keys, long long head_stride, int L, const KT* chat, int C, int cpad,
+hipError_t launch_exact(const KT* keys, long long head_stride, int L, const KT* chat, int C, int cpad, int cps,
                         int32_t* labels, long long label_stride, const int32_t* queue, const uint32_t* qcount,
                         dim3 grid, size_t lds, hipStream_t st) {
   switch ((C + 63) / 64) {
 #define KVC_EXACT_CASE(T) \
   case T:                 \
-    return launch_exact_t<KT, T>(keys, head_stride, L, chat, C, cpad, labels, label_stride, queue, qcount, grid, lds, st);
+    return launch_exact_t<KT, T>(keys, head_stride, L, chat, C, cpad, cps, labels, label_stride, queue, qcount, grid, \
+                                 lds, st);
     KVC_EXACT_CASE(1)
     KVC_EXACT_CASE(2)
     KVC_EXACT_CASE(3)
@@ -655,7 +696,7 @@ hipError_t launch_exact(const KT* keys, long long head_stride, int L, const KT* 
 }
 
 hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
-                         int cpad, int32_t* labels, long long label_stride, int32_t* queue, uint32_t* qcount,
+                         int cpad, int cps, int32_t* labels, long long label_stride, int32_t* queue, uint32_t* qcount,
                          float* top2, hipEvent_t* events, hipStream_t st) {
   if (dtype == DT_BF16) {
     const size_t lds = (size_t)cpad * D * 2;
@@ -676,8 +717,8 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
       if (e0 != hipSuccess) return e0;
     }
     assign_bf16_mfma_kernel<<<grid, AS_THREADS, lds, st>>>((const uint16_t*)keys, head_stride, L,
-                                                             (const uint16_t*)chat, C, cpad, labels, label_stride,
-                                                             queue, qcount, top2);
+                                                             (const uint16_t*)chat, C, cpad, cps, labels,
+                                                             label_stride, queue, qcount, top2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (events) {
@@ -685,7 +726,7 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
       if (e != hipSuccess) return e;
     }
     // exact re-scoring of the uncertified keys; blocks without work exit at once
-    return launch_exact<uint16_t>((const uint16_t*)keys, head_stride, L, (const uint16_t*)chat, C, cpad, labels,
+    return launch_exact<uint16_t>((const uint16_t*)keys, head_stride, L, (const uint16_t*)chat, C, cpad, cps, labels,
                                   label_stride, queue, qcount, dim3(4, heads), lds, st);
   }
   dim3 g2(grid1(L, 8) < 64 ? grid1(L, 8) : 64, heads);
@@ -693,20 +734,20 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
     hipError_t e0 = hipEventRecord(events[0], st);
     if (e0 != hipSuccess) return e0;
   }
-  hipError_t e = launch_exact<float>((const float*)keys, head_stride, L, (const float*)chat, C, cpad, labels,
+  hipError_t e = launch_exact<float>((const float*)keys, head_stride, L, (const float*)chat, C, cpad, cps, labels,
                                      label_stride, nullptr, nullptr, g2, 0, st);
   if (e == hipSuccess && events) e = hipEventRecord(events[1], st);
   return e;
 }
 
-hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, int L, int C, int32_t* hist,
+hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, int L, int C, int cs, int32_t* hist,
                       int32_t* sizes, int32_t* offsets, int32_t* token_ids, long long ids_stride, int id_base,
                       hipStream_t st) {
   const int nblk = csr_blocks(L);
   csr_count_kernel<<<dim3(nblk, heads), 256, 0, st>>>(labels, label_stride, L, C, nblk, hist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  csr_scan_kernel<<<heads, 512, 0, st>>>(C, nblk, hist, sizes, offsets);
+  csr_scan_kernel<<<heads, 512, 0, st>>>(C, cs, nblk, hist, sizes, offsets);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   csr_scatter_kernel<<<dim3(nblk, heads), CS_BLOCK, 0, st>>>(labels, label_stride, L, C, nblk, hist, token_ids,
@@ -714,16 +755,32 @@ hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, 
   return hipGetLastError();
 }
 
-hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cpad,
+hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cs, int cps,
                          const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
                          float* cent, float* cent_t, void* chat, hipStream_t st) {
   dim3 grid(grid1(C, 4), heads);
   if (dtype == DT_BF16)
-    update_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, C, cpad, sizes, offsets,
+    update_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, C, cs, cps, sizes, offsets,
                                                   token_ids, ids_stride, cent, cent_t, (uint16_t*)chat);
   else
-    update_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, C, cpad, sizes, offsets, token_ids,
+    update_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, C, cs, cps, sizes, offsets, token_ids,
                                                ids_stride, cent, cent_t, (float*)chat);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_window(int dtype, int heads, int nc, int m, int wlo, const float* cent_w, const void* chat_w,
+                               const int32_t* labels_w, const int32_t* sizes_w, const int32_t* offsets_w,
+                               const int32_t* ids_w, int ca, int cs, int cps, float* cent, float* cent_t, void* chat,
+                               int32_t* sizes, int32_t* offsets, int32_t* token_ids, int32_t* labels, long long cap,
+                               hipStream_t st) {
+  if (dtype == DT_BF16)
+    merge_window_kernel<uint16_t><<<heads, 256, 0, st>>>(nc, m, wlo, cent_w, (const uint16_t*)chat_w, labels_w,
+                                                         sizes_w, offsets_w, ids_w, ca, cs, cps, cent, cent_t,
+                                                         (uint16_t*)chat, sizes, offsets, token_ids, labels, cap);
+  else
+    merge_window_kernel<float><<<heads, 256, 0, st>>>(nc, m, wlo, cent_w, (const float*)chat_w, labels_w, sizes_w,
+                                                      offsets_w, ids_w, ca, cs, cps, cent, cent_t, (float*)chat, sizes,
+                                                      offsets, token_ids, labels, cap);
   return hipGetLastError();
 }
 

@@ -15,23 +15,26 @@ namespace kvc {
 // ---------------------------------------------------------------------------
 // a6: append n_new tokens per head. One block per head; tokens in order.
 // label = argmax_k of the fp64 chain k_new . chat_k (ascending channel order,
-// lowest k on ties), the same rule as the build's assignment. The token id
+// lowest k on ties), the same rule as the build's assignment, over the C
+// clusters in use (per-head strides: cs slots, cps operand rows). The token id
 // joins the end of its cluster's appended list (ids only grow, so lists stay
-// ascending), shifting the later clusters' entries right by one.
+// ascending), shifting the later clusters' entries right by one; the prefix
+// entries of every slot after the cluster advance, so unused slots keep the
+// list's total.
 template <typename KT>
 __global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __restrict__ vc, long long head_stride,
                                                      const KT* __restrict__ knew, const KT* __restrict__ vnew,
-                                                     int n_new, int n0, int n_build, const KT* __restrict__ chat,
-                                                     int C, int cpad, int32_t* __restrict__ labels, long long cap,
+                                                     int n_new, int n0, const KT* __restrict__ chat, int C, int cs,
+                                                     int cps, int32_t* __restrict__ labels, long long cap,
                                                      int32_t* __restrict__ sizes, int32_t* __restrict__ app_offsets,
                                                      int32_t* __restrict__ app_ids) {
   __shared__ double kv[D];
   __shared__ double rs[4];
   __shared__ int rk[4];
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int32_t* aoff = app_offsets + (size_t)h * (C + 1);
+  int32_t* aoff = app_offsets + (size_t)h * (cs + 1);
   int32_t* aids = app_ids + (size_t)h * cap;
-  const KT* Ch = chat + (size_t)h * cpad * D;
+  const KT* Ch = chat + (size_t)h * cps * D;
   for (int t = 0; t < n_new; ++t) {
     const int pos = n0 + t;
     const KT* ks = knew + ((size_t)h * n_new + t) * D;
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __
       }
     const int lab = bi;
     // insert pos at the end of cluster lab's appended segment
-    const int a = pos - n_build;       // entries before this append
+    const int a = aoff[cs];            // entries before this append
     const int p = aoff[lab + 1];
     for (int hiend = a; hiend > p; hiend -= 256) {  // shift right to left, one chunk at a time
       const int lo = hiend - 256 > p ? hiend - 256 : p;
@@ -124,11 +127,28 @@ __global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __
     }
     if (tid == 0) {
       aids[p] = pos;
-      sizes[(size_t)h * C + lab] += 1;
+      sizes[(size_t)h * cs + lab] += 1;
       labels[(size_t)h * cap + pos] = lab;
     }
-    for (int k = lab + 1 + tid; k <= C; k += 256) aoff[k] += 1;
+    for (int k = lab + 1 + tid; k <= cs; k += 256) aoff[k] += 1;
     __syncthreads();
+  }
+}
+
+// Tokens that join the window of generated tokens (III.B; they are clustered
+// later, together): rows n0 .. n0+n_new-1 of the caches, label -1.
+template <typename KT>
+__global__ __launch_bounds__(256) void window_append_kernel(KT* __restrict__ kc, KT* __restrict__ vc, long long cap,
+                                                            const KT* __restrict__ knew,
+                                                            const KT* __restrict__ vnew, int n_new, int n0,
+                                                            int32_t* __restrict__ labels) {
+  const int h = blockIdx.y;
+  for (int e = blockIdx.x * 256 + threadIdx.x; e < n_new * D; e += gridDim.x * 256) {
+    const int t = e / D, j = e % D;
+    const size_t dst = ((size_t)h * cap + n0 + t) * D + j, src = ((size_t)h * n_new + t) * D + j;
+    kc[dst] = knew[src];
+    vc[dst] = vnew[src];
+    if (j == 0) labels[(size_t)h * cap + n0 + t] = -1;
   }
 }
 
@@ -142,6 +162,8 @@ __global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __
 //  5. Output position p < min(B, N) belongs to the last rank r with W_r <= p
 //     and takes member p - W_r of that cluster (built part, then appended
 //     part), so every cluster before the cut is whole and the last is trimmed.
+//     The attention sinks and the window of unclustered generated tokens come
+//     before every cluster.
 constexpr int SEL_THREADS = 512;
 
 struct SelShared {
@@ -204,21 +226,20 @@ __device__ __forceinline__ void bitonic_sort(Sh& S, unsigned long long& key, int
   if constexpr (SIZE < N) bitonic_sort<SIZE * 2, N>(S, key, id, tid);
 }
 
-// cent_t is the chunk-major copy [d/4, C, 4] of the head's centroids: thread k
-// reads chunk jj of its row at ((jj * C) + k) * 16 bytes, so a wave's loads are
+// cent_t is the chunk-major copy [d/4, cs, 4] of the head's centroids: thread k
+// reads chunk jj of its row at ((jj * cs) + k) * 16 bytes, so a wave's loads are
 // contiguous. The chain still runs over ascending j.
 template <typename QT>
-__device__ __forceinline__ void select_phase(SelShared& S, const QT* __restrict__ q, int G,
-                                             const float* __restrict__ cent_t, int C,
-                                             const int32_t* __restrict__ sizes, const int32_t* __restrict__ offsets,
-                                             const int32_t* __restrict__ app_offsets, int h) {
+__device__ __forceinline__ void select_phase(SelShared& S, const QT* __restrict__ q, int G, const IndexView& X,
+                                             int h) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int C = X.ca, cs = X.cs;
   if (tid < C) {  // per-cluster metadata, read while the scores are computed
-    S.mn[tid] = sizes[(size_t)h * C + tid];
-    const int o = offsets[(size_t)h * (C + 1) + tid];
+    S.mn[tid] = X.sizes[(size_t)h * cs + tid];
+    const int o = X.offsets[(size_t)h * (cs + 1) + tid];
     S.mo[tid] = o;
-    S.mb[tid] = offsets[(size_t)h * (C + 1) + tid + 1] - o;
-    S.ma[tid] = app_offsets[(size_t)h * (C + 1) + tid];
+    S.mb[tid] = X.offsets[(size_t)h * (cs + 1) + tid + 1] - o;
+    S.ma[tid] = X.app_offsets[(size_t)h * (cs + 1) + tid];
   }
   if (tid < D) {
     double s = 0.0;
@@ -229,13 +250,13 @@ __device__ __forceinline__ void select_phase(SelShared& S, const QT* __restrict_
   unsigned long long key = 0;
   int id = C + tid;  // padding entries: worst key, distinct ids past the clusters
   if (tid < C) {
-    const f32x4* ct = reinterpret_cast<const f32x4*>(cent_t + (size_t)h * C * D) + tid;
+    const f32x4* ct = reinterpret_cast<const f32x4*>(X.cent_t + (size_t)h * cs * D) + tid;
     double s = 0.0;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       f32x4 v[16];
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) v[jj] = ct[(size_t)(half * 16 + jj) * C];
+      for (int jj = 0; jj < 16; ++jj) v[jj] = ct[(size_t)(half * 16 + jj) * cs];
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj)
 #pragma unroll
@@ -276,17 +297,20 @@ __device__ __forceinline__ void select_phase(SelShared& S, const QT* __restrict_
   __syncthreads();
 }
 
-// Entry at output position p (< n_sink + total) of the ranked, trimmed
+// Entry at output position p (< n_sink + nw + total) of the ranked, trimmed
 // selection: positions below n_sink are the attention sinks (tokens 0 ..
-// n_sink - 1, always recalled first), the rest come from the clusters. The
-// entry is the token id, or with a packed copy (packed = true) the row of the
-// copy for a built member (its position in the index, offset + member) and
-// ~token for a sink or a token appended after the build (both are read from
-// the caches).
+// n_sink - 1, always recalled first), the next nw the window of generated
+// tokens not yet clustered (wlo .. wlo + nw - 1), the rest come from the
+// clusters. The entry is the token id, or with a packed copy (packed = true)
+// the row of the copy for a member of the index's main part (its position in
+// the index, offset + member) and ~token for a sink, a window token or a token
+// appended to a cluster (all read from the caches).
 __device__ __forceinline__ int select_emit(const SelShared& S, int p, const int32_t* __restrict__ ids_h,
-                                           const int32_t* __restrict__ app_h, bool packed, int n_sink) {
-  if (p < n_sink) return packed ? ~p : p;
-  p -= n_sink;
+                                           const int32_t* __restrict__ app_h, bool packed, const IndexView& X) {
+  if (p < X.n_sink) return packed ? ~p : p;
+  p -= X.n_sink;
+  if (p < X.nw) return packed ? ~(X.wlo + p) : X.wlo + p;
+  p -= X.nw;
   int lo = 0, hi = SEL_THREADS - 1;  // last r with W[r] <= p
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -313,24 +337,24 @@ __device__ __forceinline__ int sel_token(const int32_t* __restrict__ ids_h, int 
   return packed ? (id >= 0 ? ids_h[id] : ~id) : id;
 }
 
+// Selected entries of a head: sinks and window first, then min(B, ...) in all.
+__device__ __forceinline__ int select_count(const SelShared& S, const IndexView& X, int B) {
+  const int n = X.n_sink + X.nw + S.total;
+  return n < B ? n : B;
+}
+
 template <typename QT>
-__global__ __launch_bounds__(SEL_THREADS) void select_kernel(const QT* __restrict__ q, int G,
-                                                             const float* __restrict__ cent_t, int C,
-                                                             const int32_t* __restrict__ sizes,
-                                                             const int32_t* __restrict__ offsets,
-                                                             const int32_t* __restrict__ token_ids,
-                                                             const int32_t* __restrict__ app_offsets,
-                                                             const int32_t* __restrict__ app_ids, long long cap, int B,
-                                                             int n_sink, int32_t* __restrict__ sel_ids,
+__global__ __launch_bounds__(SEL_THREADS) void select_kernel(const QT* __restrict__ q, int G, const IndexView X,
+                                                             int B, int32_t* __restrict__ sel_ids,
                                                              int32_t* __restrict__ sel_count) {
   __shared__ SelShared S;
   const int h = blockIdx.x, tid = threadIdx.x;
-  select_phase(S, q, G, cent_t, C, sizes, offsets, app_offsets, h);
-  const int cnt = n_sink + S.total < B ? n_sink + S.total : B;
-  const int32_t* ids_h = token_ids + (size_t)h * cap;
-  const int32_t* app_h = app_ids + (size_t)h * cap;
+  select_phase(S, q, G, X, h);
+  const int cnt = select_count(S, X, B);
+  const int32_t* ids_h = X.token_ids + (size_t)h * X.cap;
+  const int32_t* app_h = X.app_ids + (size_t)h * X.cap;
   for (int p = tid; p < B; p += SEL_THREADS)
-    sel_ids[(size_t)h * B + p] = p < cnt ? select_emit(S, p, ids_h, app_h, false, n_sink) : -1;
+    sel_ids[(size_t)h * B + p] = p < cnt ? select_emit(S, p, ids_h, app_h, false, X) : -1;
   if (tid == 0) sel_count[h] = cnt;
 }
 
@@ -406,12 +430,9 @@ struct Row8<float> {
 // summed through LDS at the end.
 template <typename KT, int G>
 __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
-    const KT* __restrict__ q, const float* __restrict__ cent_t, int C, const int32_t* __restrict__ sizes,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ token_ids,
-    const int32_t* __restrict__ app_offsets, const int32_t* __restrict__ app_ids, long long cap,
-    const KT* __restrict__ kc, const KT* __restrict__ vc, const KT* __restrict__ kp, const KT* __restrict__ vp,
-    int packed, int n_sink, int B, float qscale, float* __restrict__ out, int32_t* __restrict__ sel_ids,
-    int32_t* __restrict__ sel_count) {
+    const KT* __restrict__ q, const IndexView X, const KT* __restrict__ kc, const KT* __restrict__ vc,
+    const KT* __restrict__ kp, const KT* __restrict__ vp, int packed, int B, float qscale, float* __restrict__ out,
+    int32_t* __restrict__ sel_ids, int32_t* __restrict__ sel_count) {
   constexpr int NW = SEL_THREADS / WAVE;                       // 8 waves
   constexpr int RS = (G <= 4 && sizeof(KT) == 2) ? 16 : (G <= 2 ? 8 : 4);  // row steps per load batch
   constexpr int NB = 16 / RS;                                  // batches per chunk
@@ -423,13 +444,14 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
   __shared__ float ored[NW][G][D];
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = lane >> 4, gl = lane & 15;
-  select_phase(S, q, G, cent_t, C, sizes, offsets, app_offsets, h);
-  const int cnt = n_sink + S.total < B ? n_sink + S.total : B;
+  select_phase(S, q, G, X, h);
+  const int cnt = select_count(S, X, B);
+  const long long cap = X.cap;
   if (sel_count && tid == 0) sel_count[h] = cnt;
   if (sel_ids)
     for (int p = cnt + tid; p < B; p += SEL_THREADS) sel_ids[(size_t)h * B + p] = -1;
-  const int32_t* ids_h = token_ids + (size_t)h * cap;
-  const int32_t* app_h = app_ids + (size_t)h * cap;
+  const int32_t* ids_h = X.token_ids + (size_t)h * cap;
+  const int32_t* app_h = X.app_ids + (size_t)h * cap;
   const KT* Kh = kc + (size_t)h * cap * D + 8 * gl;
   const KT* Vh = vc + (size_t)h * cap * D + 8 * gl;
   const KT* Kph = kp + (size_t)h * cap * D + 8 * gl;
@@ -456,7 +478,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
     const int nchunk = cnt - c0 < SEL_THREADS ? cnt - c0 : SEL_THREADS;
     {
       const int p = c0 + tid;
-      const int ent = tid < nchunk ? select_emit(S, p, ids_h, app_h, packed, n_sink) : 0;
+      const int ent = tid < nchunk ? select_emit(S, p, ids_h, app_h, packed, X) : 0;
       sel[tid] = ent;
       if (sel_ids && tid < nchunk) sel_ids[(size_t)h * B + p] = sel_token(ids_h, ent, packed);
     }
@@ -599,12 +621,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
 // of the keys and centroids; results do not depend on the placement.
 template <int G, int P>
 __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
-    const uint16_t* __restrict__ q, const float* __restrict__ cent_t, int C, const int32_t* __restrict__ sizes,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ token_ids,
-    const int32_t* __restrict__ app_offsets, const int32_t* __restrict__ app_ids, long long cap,
-    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, const uint16_t* __restrict__ kp,
-    const uint16_t* __restrict__ vp, int packed, int n_sink, int heads, int B, float qscale,
-    float* __restrict__ out, int32_t* __restrict__ sel_ids, int32_t* __restrict__ sel_count) {
+    const uint16_t* __restrict__ q, const IndexView X, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, int packed,
+    int heads, int B, float qscale, float* __restrict__ out, int32_t* __restrict__ sel_ids,
+    int32_t* __restrict__ sel_count) {
   static_assert(G <= 8, "at most 8 query heads per KV head");
   constexpr int NW = SEL_THREADS / WAVE;
   constexpr int EMIT = 2048;                 // selected ids staged per pass
@@ -624,14 +644,15 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
   if (h >= heads) return;  // whole block: the grid covers heads rounded up to 8
   const int vgrp = lane / (HC / 8), vgl = lane % (HC / 8);  // value row in the load, 8-channel chunk
   const int j16 = lane & 15, kb4 = lane >> 4;
-  select_phase(S, q, G, cent_t, C, sizes, offsets, app_offsets, h);
-  const int cnt = n_sink + S.total < B ? n_sink + S.total : B;
+  select_phase(S, q, G, X, h);
+  const int cnt = select_count(S, X, B);
+  const long long cap = X.cap;
   const bool writer = part == 0;  // one block per head publishes the selection
   if (writer && sel_count && tid == 0) sel_count[h] = cnt;
   if (writer && sel_ids)
     for (int p = cnt + tid; p < B; p += SEL_THREADS) sel_ids[(size_t)h * B + p] = -1;
-  const int32_t* ids_h = token_ids + (size_t)h * cap;
-  const int32_t* app_h = app_ids + (size_t)h * cap;
+  const int32_t* ids_h = X.token_ids + (size_t)h * cap;
+  const int32_t* app_h = X.app_ids + (size_t)h * cap;
   const uint16_t* Kh = kc + (size_t)h * cap * D + 8 * kb4;
   const uint16_t* Vh = vc + (size_t)h * cap * D + HC * part + 8 * vgl;
   const uint16_t* Kph = kp + (size_t)h * cap * D + 8 * kb4;
@@ -661,7 +682,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     const int nb = cnt - base < EMIT ? cnt - base : EMIT;
     if (base > 0) __syncthreads();  // every wave is done with the previous ids
     for (int p = tid; p < nb; p += SEL_THREADS) {
-      const int ent = select_emit(S, base + p, ids_h, app_h, packed, n_sink);
+      const int ent = select_emit(S, base + p, ids_h, app_h, packed, X);
       sel[p] = ent;
       if (writer && sel_ids) sel_ids[(size_t)h * B + base + p] = sel_token(ids_h, ent, packed);
     }
@@ -1138,19 +1159,23 @@ __global__ __launch_bounds__(256) void dense_decode_bf16_kernel(const uint16_t* 
 }
 
 // ---------------------------------------------------------------------------
-// Packed copy of the built tokens' key and value rows in index order: row i of
-// head h is the cache row token_ids[h][i] (i < n). 16 bytes per lane, one row
-// per D * sizeof(KT) / 16 lanes.
+// Packed copy of the index's key and value rows in index order: row i of head
+// h is the cache row token_ids[h][i], for i in [r0, r1): r0 = row0[h * stride]
+// (or 0 without row0), r1 = row1[h * stride] (or r0 + n without row1). 16
+// bytes per lane, one row per D * sizeof(KT) / 16 lanes.
 template <typename KT>
 __global__ __launch_bounds__(256) void pack_kernel(const KT* __restrict__ kc, const KT* __restrict__ vc, long long cap,
                                                    const int32_t* __restrict__ token_ids, int n,
-                                                   KT* __restrict__ kp, KT* __restrict__ vp) {
+                                                   const int32_t* __restrict__ row0, const int32_t* __restrict__ row1,
+                                                   long long stride, KT* __restrict__ kp, KT* __restrict__ vp) {
   constexpr int LPR = D * (int)sizeof(KT) / 16;  // lanes per row
   constexpr int RPB = 256 / LPR;                 // rows per block and pass
   const int h = blockIdx.y;
   const int l = threadIdx.x % LPR, rr = threadIdx.x / LPR;
   const size_t hb = (size_t)h * cap;
-  for (int i = blockIdx.x * RPB + rr; i < n; i += gridDim.x * RPB) {
+  const int r0 = row0 ? row0[(size_t)h * stride] : 0;
+  const int r1 = row1 ? row1[(size_t)h * stride] : r0 + n;
+  for (int i = r0 + blockIdx.x * RPB + rr; i < r1; i += gridDim.x * RPB) {
     const size_t src = (hb + (size_t)token_ids[hb + i]) * D, dst = (hb + (size_t)i) * D;
     const u32x4 k = reinterpret_cast<const u32x4*>(kc + src)[l];
     const u32x4 v = reinterpret_cast<const u32x4*>(vc + src)[l];
@@ -1160,17 +1185,19 @@ __global__ __launch_bounds__(256) void pack_kernel(const KT* __restrict__ kc, co
 }
 
 // ---------------------------------------------------------------------------
-// Canonical index (built + appended parts merged), one block per head.
-__global__ __launch_bounds__(256) void export_csr_kernel(int C, const int32_t* __restrict__ offsets,
+// Canonical index (main and appended parts merged) of the C clusters in use,
+// one block per head; prefix entries of unused slots hold the total.
+__global__ __launch_bounds__(256) void export_csr_kernel(int C, int cs, const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ token_ids,
                                                          const int32_t* __restrict__ app_offsets,
                                                          const int32_t* __restrict__ app_ids, long long cap,
                                                          int32_t* __restrict__ out_offsets,
                                                          int32_t* __restrict__ out_ids) {
   const int h = blockIdx.x;
-  const int32_t* off = offsets + (size_t)h * (C + 1);
-  const int32_t* aoff = app_offsets + (size_t)h * (C + 1);
-  for (int k = threadIdx.x; k <= C; k += 256) out_offsets[(size_t)h * (C + 1) + k] = off[k] + aoff[k];
+  const int32_t* off = offsets + (size_t)h * (cs + 1);
+  const int32_t* aoff = app_offsets + (size_t)h * (cs + 1);
+  for (int k = threadIdx.x; k <= cs; k += 256)
+    out_offsets[(size_t)h * (cs + 1) + k] = k <= C ? off[k] + aoff[k] : off[C] + aoff[C];
   for (int k = threadIdx.x; k < C; k += 256) {
     int dst = off[k] + aoff[k];
     for (int e = off[k]; e < off[k + 1]; ++e) out_ids[(size_t)h * cap + dst++] = token_ids[(size_t)h * cap + e];
@@ -1182,42 +1209,48 @@ __global__ __launch_bounds__(256) void export_csr_kernel(int C, const int32_t* _
 // Host launchers.
 
 hipError_t launch_append(int dtype, void* kc, void* vc, long long head_stride, int heads, const void* knew,
-                         const void* vnew, int n_new, int n0, int n_build, const void* chat, int C, int cpad,
+                         const void* vnew, int n_new, int n0, const void* chat, int ca, int cs, int cps,
                          int32_t* labels, long long cap, int32_t* sizes, int32_t* app_offsets, int32_t* app_ids,
                          hipStream_t st) {
   if (dtype == DT_BF16)
     append_kernel<uint16_t><<<heads, 256, 0, st>>>((uint16_t*)kc, (uint16_t*)vc, head_stride, (const uint16_t*)knew,
-                                                   (const uint16_t*)vnew, n_new, n0, n_build,
-                                                   (const uint16_t*)chat, C, cpad, labels, cap, sizes, app_offsets,
-                                                   app_ids);
+                                                   (const uint16_t*)vnew, n_new, n0, (const uint16_t*)chat, ca, cs, cps,
+                                                   labels, cap, sizes, app_offsets, app_ids);
   else
     append_kernel<float><<<heads, 256, 0, st>>>((float*)kc, (float*)vc, head_stride, (const float*)knew,
-                                                (const float*)vnew, n_new, n0, n_build, (const float*)chat, C, cpad,
-                                                labels, cap, sizes, app_offsets, app_ids);
+                                                (const float*)vnew, n_new, n0, (const float*)chat, ca, cs, cps, labels,
+                                                cap, sizes, app_offsets, app_ids);
   return hipGetLastError();
 }
 
-hipError_t launch_select(int dtype, const void* q, int G, const float* cent, int heads, int C, const int32_t* sizes,
-                         const int32_t* offsets, const int32_t* token_ids, const int32_t* app_offsets,
-                         const int32_t* app_ids, long long cap, int n_sink, int B, int32_t* sel_ids,
+hipError_t launch_window_append(int dtype, void* kc, void* vc, long long cap, int heads, const void* knew,
+                                const void* vnew, int n_new, int n0, int32_t* labels, hipStream_t st) {
+  const long long elems = (long long)n_new * D;
+  const dim3 grid((unsigned)((elems + 255) / 256 < 64 ? (elems + 255) / 256 : 64), heads);
+  if (dtype == DT_BF16)
+    window_append_kernel<uint16_t><<<grid, 256, 0, st>>>((uint16_t*)kc, (uint16_t*)vc, cap, (const uint16_t*)knew,
+                                                         (const uint16_t*)vnew, n_new, n0, labels);
+  else
+    window_append_kernel<float><<<grid, 256, 0, st>>>((float*)kc, (float*)vc, cap, (const float*)knew,
+                                                      (const float*)vnew, n_new, n0, labels);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(int dtype, const void* q, int G, const IndexView& x, int heads, int B, int32_t* sel_ids,
                          int32_t* sel_count, hipStream_t st) {
   if (dtype == DT_BF16)
-    select_kernel<uint16_t><<<heads, SEL_THREADS, 0, st>>>((const uint16_t*)q, G, cent, C, sizes, offsets, token_ids,
-                                                           app_offsets, app_ids, cap, B, n_sink, sel_ids, sel_count);
+    select_kernel<uint16_t><<<heads, SEL_THREADS, 0, st>>>((const uint16_t*)q, G, x, B, sel_ids, sel_count);
   else
-    select_kernel<float><<<heads, SEL_THREADS, 0, st>>>((const float*)q, G, cent, C, sizes, offsets, token_ids,
-                                                        app_offsets, app_ids, cap, B, n_sink, sel_ids, sel_count);
+    select_kernel<float><<<heads, SEL_THREADS, 0, st>>>((const float*)q, G, x, B, sel_ids, sel_count);
   return hipGetLastError();
 }
 
 struct FusedArgs {
   const void* q;
-  const float* cent;
-  int heads, C;
-  const int32_t *sizes, *offsets, *token_ids, *app_offsets, *app_ids;
-  long long cap;
+  IndexView x;
+  int heads;
   const void *kc, *vc, *kp, *vp;  // kp, vp: packed copies, or the caches when not packed
-  int packed, n_sink, B;
+  int packed, B;
   float qscale;
   float* out;
   int32_t *sel_ids, *sel_count;
@@ -1229,10 +1262,9 @@ static void launch_fused(const FusedArgs& a, hipStream_t st) {
     // enough blocks per head that the grid covers the 256 compute units
     const int P = a.heads >= 128 ? 2 : (a.heads >= 64 ? 4 : 8);
     const int nb = (a.heads + 7) / 8 * 8 * P;
-#define KVC_FUSED_ARGS                                                                                             \
-  (const uint16_t*)a.q, a.cent, a.C, a.sizes, a.offsets, a.token_ids, a.app_offsets, a.app_ids, a.cap,          \
-      (const uint16_t*)a.kc, (const uint16_t*)a.vc, (const uint16_t*)a.kp, (const uint16_t*)a.vp, a.packed, a.n_sink, \
-      a.heads, a.B, a.qscale, a.out, a.sel_ids, a.sel_count
+#define KVC_FUSED_ARGS                                                                                          \
+  (const uint16_t*)a.q, a.x, (const uint16_t*)a.kc, (const uint16_t*)a.vc, (const uint16_t*)a.kp,             \
+      (const uint16_t*)a.vp, a.packed, a.heads, a.B, a.qscale, a.out, a.sel_ids, a.sel_count
     if (P == 2) select_decode_bf16_kernel<G, 2><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
     else if (P == 4) select_decode_bf16_kernel<G, 4><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
     else select_decode_bf16_kernel<G, 8><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
@@ -1240,9 +1272,8 @@ static void launch_fused(const FusedArgs& a, hipStream_t st) {
   }
   else
     select_decode_kernel<KT, G><<<a.heads, SEL_THREADS, 0, st>>>(
-        (const KT*)a.q, a.cent, a.C, a.sizes, a.offsets, a.token_ids, a.app_offsets, a.app_ids, a.cap,
-        (const KT*)a.kc, (const KT*)a.vc, (const KT*)a.kp, (const KT*)a.vp, a.packed, a.n_sink, a.B, a.qscale,
-        a.out, a.sel_ids, a.sel_count);
+        (const KT*)a.q, a.x, (const KT*)a.kc, (const KT*)a.vc, (const KT*)a.kp, (const KT*)a.vp, a.packed, a.B,
+        a.qscale, a.out, a.sel_ids, a.sel_count);
 }
 
 template <typename KT>
@@ -1257,14 +1288,11 @@ static hipError_t fused_dispatch(int G, const FusedArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_select_decode(int dtype, const void* q, int G, const float* cent, int heads, int C,
-                                const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids,
-                                const int32_t* app_offsets, const int32_t* app_ids, long long cap, const void* kc,
-                                const void* vc, const void* kp, const void* vp, int n_sink, int B, float scale,
-                                float* out, int32_t* sel_ids, int32_t* sel_count, hipStream_t st) {
-  FusedArgs a{q, cent, heads, C, sizes, offsets, token_ids, app_offsets, app_ids, cap, kc, vc,
-              kp ? kp : kc, vp ? vp : vc, kp && vp ? 1 : 0, n_sink, B, scale * 1.4426950408889634f, out, sel_ids,
-              sel_count};
+hipError_t launch_select_decode(int dtype, const void* q, int G, const IndexView& x, int heads, const void* kc,
+                                const void* vc, const void* kp, const void* vp, int B, float scale, float* out,
+                                int32_t* sel_ids, int32_t* sel_count, hipStream_t st) {
+  FusedArgs a{q, x, heads, kc, vc, kp ? kp : kc, vp ? vp : vc, kp && vp ? 1 : 0, B, scale * 1.4426950408889634f,
+              out, sel_ids, sel_count};
   if (dtype == DT_BF16) return fused_dispatch<uint16_t>(G, a, st);
   return fused_dispatch<float>(G, a, st);
 }
@@ -1299,10 +1327,11 @@ hipError_t launch_decode(int dtype, const void* q, int G, const void* kc, const 
   return decode_dispatch<float>(q, G, kc, vc, head_stride, heads, sel_ids, sel_count, B, qscale, out, part, st);
 }
 
-hipError_t launch_export_csr(int heads, int C, const int32_t* offsets, const int32_t* token_ids,
+hipError_t launch_export_csr(int heads, int ca, int cs, const int32_t* offsets, const int32_t* token_ids,
                              const int32_t* app_offsets, const int32_t* app_ids, long long cap, int32_t* out_offsets,
                              int32_t* out_ids, hipStream_t st) {
-  export_csr_kernel<<<heads, 256, 0, st>>>(C, offsets, token_ids, app_offsets, app_ids, cap, out_offsets, out_ids);
+  export_csr_kernel<<<heads, 256, 0, st>>>(ca, cs, offsets, token_ids, app_offsets, app_ids, cap, out_offsets,
+                                           out_ids);
   return hipGetLastError();
 }
 
@@ -1345,14 +1374,16 @@ hipError_t launch_dense_decode(const void* q, int G, const void* kc, const void*
 }
 
 hipError_t launch_pack(int dtype, const void* kc, const void* vc, long long cap, int heads, const int32_t* token_ids,
-                       int n, void* kp, void* vp, hipStream_t st) {
+                       int n, const int32_t* row0, const int32_t* row1, long long stride, void* kp, void* vp,
+                       hipStream_t st) {
+  if (n < 1) return hipSuccess;
   const int bx = (n + 15) / 16 < 64 ? (n + 15) / 16 : 64;
   if (dtype == DT_BF16)
     pack_kernel<uint16_t><<<dim3(bx, heads), 256, 0, st>>>((const uint16_t*)kc, (const uint16_t*)vc, cap, token_ids,
-                                                          n, (uint16_t*)kp, (uint16_t*)vp);
+                                                          n, row0, row1, stride, (uint16_t*)kp, (uint16_t*)vp);
   else
-    pack_kernel<float><<<dim3(bx, heads), 256, 0, st>>>((const float*)kc, (const float*)vc, cap, token_ids, n,
-                                                       (float*)kp, (float*)vp);
+    pack_kernel<float><<<dim3(bx, heads), 256, 0, st>>>((const float*)kc, (const float*)vc, cap, token_ids, n, row0,
+                                                       row1, stride, (float*)kp, (float*)vp);
   return hipGetLastError();
 }
 

@@ -12,44 +12,65 @@ constexpr int DEC_MAX_PAIRS = 512;  // splits x query heads one merge block hold
 
 int csr_blocks(int L);
 
+// The index as the selection kernels read it: device arrays with per-head
+// strides of cs cluster slots (cs + 1 for the prefix arrays) and cap tokens;
+// clusters 0 .. ca-1 in use; ahead of the clusters, the n_sink attention sinks
+// (tokens 0 .. n_sink-1) and the nw window tokens wlo .. wlo+nw-1 are recalled.
+struct IndexView {
+  const float* cent_t;  // [heads, d/4, cs, 4]
+  const int32_t *sizes, *offsets, *token_ids, *app_offsets, *app_ids;
+  long long cap;
+  int cs, ca, n_sink, wlo, nw;
+};
+
 hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t v, hipStream_t st);
 hipError_t launch_init_centroids(int dtype, const void* keys, long long head_stride, int heads, int lo, int L,
-                                 const int32_t* init_idx, int C, int cpad, float* cent, float* cent_t, void* chat,
-                                 int32_t* flags, hipStream_t st);
+                                 const int32_t* init_idx, int C, int cpad, int cs, int cps, float* cent, float* cent_t,
+                                 void* chat, int32_t* flags, hipStream_t st);
 hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
-                         int cpad, int32_t* labels, long long label_stride, int32_t* queue, uint32_t* qcount,
+                         int cpad, int cps, int32_t* labels, long long label_stride, int32_t* queue, uint32_t* qcount,
                          float* top2, hipEvent_t* events, hipStream_t st);
 hipError_t launch_fill2d_i32(int32_t* p, int rows, long long stride, int cols, int value, hipStream_t st);
-hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, int L, int C, int32_t* hist,
+hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, int L, int C, int cs, int32_t* hist,
                       int32_t* sizes, int32_t* offsets, int32_t* token_ids, long long ids_stride, int id_base,
                       hipStream_t st);
-hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cpad,
+hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cs, int cps,
                          const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
                          float* cent, float* cent_t, void* chat, hipStream_t st);
+// Moves the window's clustering (nc clusters of the m tokens wlo .. wlo+m-1,
+// in arrays of stride nc / cpad(nc) / m per head) into the index as clusters
+// ca .. ca+nc-1.
+hipError_t launch_merge_window(int dtype, int heads, int nc, int m, int wlo, const float* cent_w, const void* chat_w,
+                               const int32_t* labels_w, const int32_t* sizes_w, const int32_t* offsets_w,
+                               const int32_t* ids_w, int ca, int cs, int cps, float* cent, float* cent_t, void* chat,
+                               int32_t* sizes, int32_t* offsets, int32_t* token_ids, int32_t* labels, long long cap,
+                               hipStream_t st);
 
 hipError_t launch_append(int dtype, void* kc, void* vc, long long head_stride, int heads, const void* knew,
-                         const void* vnew, int n_new, int n0, int n_build, const void* chat, int C, int cpad,
+                         const void* vnew, int n_new, int n0, const void* chat, int ca, int cs, int cps,
                          int32_t* labels, long long cap, int32_t* sizes, int32_t* app_offsets, int32_t* app_ids,
                          hipStream_t st);
-hipError_t launch_select(int dtype, const void* q, int G, const float* cent, int heads, int C, const int32_t* sizes,
-                         const int32_t* offsets, const int32_t* token_ids, const int32_t* app_offsets,
-                         const int32_t* app_ids, long long cap, int n_sink, int B, int32_t* sel_ids,
+hipError_t launch_window_append(int dtype, void* kc, void* vc, long long cap, int heads, const void* knew,
+                                const void* vnew, int n_new, int n0, int32_t* labels, hipStream_t st);
+hipError_t launch_select(int dtype, const void* q, int G, const IndexView& x, int heads, int B, int32_t* sel_ids,
                          int32_t* sel_count, hipStream_t st);
 hipError_t launch_decode(int dtype, const void* q, int G, const void* kc, const void* vc, long long head_stride,
                          int heads, const int32_t* sel_ids, const int32_t* sel_count, int B, float scale, float* out,
                          float* part, hipStream_t st);
-hipError_t launch_select_decode(int dtype, const void* q, int G, const float* cent, int heads, int C,
-                                const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids,
-                                const int32_t* app_offsets, const int32_t* app_ids, long long cap, const void* kc,
-                                const void* vc, const void* kp, const void* vp, int n_sink, int B, float scale,
-                                float* out, int32_t* sel_ids, int32_t* sel_count, hipStream_t st);
+hipError_t launch_select_decode(int dtype, const void* q, int G, const IndexView& x, int heads, const void* kc,
+                                const void* vc, const void* kp, const void* vp, int B, float scale, float* out,
+                                int32_t* sel_ids, int32_t* sel_count, hipStream_t st);
 // kp, vp: the packed copies (both non-null) or null (rows from the caches).
 void dense_split(int n, int G, int* nsplit, int* T);
 hipError_t launch_dense_decode(const void* q, int G, const void* kc, const void* vc, long long cap, int heads, int n,
                                float scale, float* out, float* part, hipStream_t st);
+// Rows i in [r0, r1) of the packed copies from the cache rows token_ids[h][i]:
+// r0 = row0[h * stride] (0 without row0), r1 = row1[h * stride] (r0 + n
+// without row1; n bounds r1 - r0 and sizes the grid).
 hipError_t launch_pack(int dtype, const void* kc, const void* vc, long long cap, int heads, const int32_t* token_ids,
-                       int n, void* kp, void* vp, hipStream_t st);
-hipError_t launch_export_csr(int heads, int C, const int32_t* offsets, const int32_t* token_ids,
+                       int n, const int32_t* row0, const int32_t* row1, long long stride, void* kp, void* vp,
+                       hipStream_t st);
+hipError_t launch_export_csr(int heads, int ca, int cs, const int32_t* offsets, const int32_t* token_ids,
                              const int32_t* app_offsets, const int32_t* app_ids, long long cap, int32_t* out_offsets,
                              int32_t* out_ids, hipStream_t st);
 

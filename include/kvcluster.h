@@ -70,6 +70,13 @@ typedef enum kvc_status {
  * cluster-major list so that no append moves the built index: the members of
  * cluster k are token_ids[offsets[k] .. offsets[k+1]) followed by
  * app_ids[app_offsets[k] .. app_offsets[k+1]), in ascending token order.
+ *
+ * Generated tokens can instead be clustered periodically (III.B; Sys-A): they
+ * join a window (kv_cluster_append_window) that every selection recalls whole,
+ * and kv_cluster_cluster_window turns the window into a few new clusters with
+ * ids c_active, c_active+1, ... . Every per-cluster array therefore has a
+ * per-head stride of c_slots cluster slots, of which the first c_active are in
+ * use.
  */
 typedef struct kvc_index {
   int32_t heads;    /* independent problems (batch x KV heads) */
@@ -83,11 +90,13 @@ typedef struct kvc_index {
                        the current build (kv_cluster_build resets it to 0) */
   float* centroids;       /* [heads, C, d] fp32: mean of each cluster's keys */
   void* centroids_op;     /* [heads, kv_cluster_cpad(C), d] unit-length centroids in `dtype`
-                             (the assignment operand); rows >= C are zero */
-  int32_t* labels;        /* [heads, capacity] cluster of every token */
+                             (the assignment operand); rows C .. cpad(C)-1 are zero after a build */
+  int32_t* labels;        /* [heads, capacity] cluster of every token (-1: none) */
   int32_t* sizes;         /* [heads, C] members per cluster, appended tokens included */
-  int32_t* offsets;       /* [heads, C+1] prefix sums of the built part's sizes */
-  int32_t* token_ids;     /* [heads, capacity] built tokens sorted by cluster, ascending within */
+  int32_t* offsets;       /* [heads, C+1] prefix sums of the main part's sizes (the built
+                             clusters, then clusters made from windows) */
+  int32_t* token_ids;     /* [heads, capacity] the main part: members sorted by cluster, ascending
+                             within */
   int32_t* app_offsets;   /* [heads, C+1] prefix sums of the appended part */
   int32_t* app_ids;       /* [heads, capacity] appended tokens, cluster-major, ascending within */
   int32_t* dev_flags;     /* [1] error bits set by kernels (bit 0: an init index out of range) */
@@ -99,6 +108,15 @@ typedef struct kvc_index {
   int32_t n_sink;         /* attention sinks (III.B): tokens 0 .. n_sink-1 are kept out of the
                              clustering (label -1) and always selected first; 0 = none. Set by
                              the caller before kv_cluster_build. */
+  int32_t c_slots;        /* cluster slots per head, C <= c_slots <= 512, or 0 for C: the per-head
+                             stride S of centroids [heads, S, d], centroids_op [heads,
+                             kv_cluster_cpad(S), d], sizes [heads, S], offsets and app_offsets
+                             [heads, S+1] and centroids_t [heads, d/4, S, 4] (the sizes written
+                             above for C hold when c_slots is 0) */
+  int32_t c_active;       /* host mirror: clusters in use, ids 0 .. c_active-1 (C after a build) */
+  int32_t window_start;   /* host mirror: first token of the window; tokens window_start ..
+                             n_tokens-1 are in no cluster yet (label -1) and every selection
+                             recalls them (n_build after a build) */
 } kvc_index;
 
 /* Rows of centroids_op per head: C rounded up to the matrix-core tile (32). */
@@ -124,8 +142,8 @@ size_t kv_cluster_build_workspace_bytes(int heads, int L, int C, int iters);
  *     (an empty cluster keeps its centroid).
  * On return (after synchronisation) the index holds the means of the final
  * assignment, their normalised operand, labels, sizes, offsets and
- * token_ids; the appended part is empty. idx->n_build and idx->n_tokens are
- * set to L on the host. Requires 1 <= C <= L <= capacity, iters >= 1, and a
+ * token_ids; the appended part is empty. idx->n_build, idx->n_tokens and
+ * idx->window_start are set to L and idx->c_active to C on the host. Requires 1 <= C <= L <= capacity, iters >= 1, and a
  * workspace of kv_cluster_build_workspace_bytes(heads, L, C, iters) bytes
  * (contents need not be initialised).
  */
@@ -148,26 +166,69 @@ int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, c
  * idx->dtype and are written into the caches; each new key joins the cluster
  * of largest cosine similarity under the current centroid operand, whose
  * centroids do not move. Sizes, labels and the appended list are updated;
- * idx->n_tokens advances on the host. Returns KVC_ERR_CAPACITY, enqueuing
- * nothing, if the tokens would not fit. (The pages re-cluster generated
- * tokens periodically instead, III.B; joining the nearest centroid is the
- * per-token alternative this call provides.)
+ * idx->n_tokens (and idx->window_start with it) advances on the host. The
+ * clusters in use are the candidates (idx->c_active). Returns
+ * KVC_ERR_CAPACITY, enqueuing nothing, if the tokens would not fit, and
+ * KVC_ERR_INVALID_ARG while a window is open (window_start < n_tokens). (The
+ * pages cluster generated tokens periodically instead, III.B: see
+ * kv_cluster_append_window; joining the nearest centroid is the per-token
+ * alternative this call provides.)
  */
 int kv_cluster_append(kvc_index* idx, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                       int n_new, void* stream);
+
+/*
+ * Decode-time append of n_new generated tokens per head to the window
+ * (III.B: generated tokens are clustered on their own, every m decoding
+ * steps; Sys-A): k_new and v_new ([heads, n_new, d], idx->dtype) become rows
+ * idx->n_tokens .. idx->n_tokens+n_new-1 of the caches with label -1, and
+ * idx->n_tokens advances on the host. Every selection recalls the window's
+ * tokens right after the attention sinks until kv_cluster_cluster_window
+ * clusters them. Requires a built index; KVC_ERR_CAPACITY if the tokens would
+ * not fit.
+ */
+int kv_cluster_append_window(kvc_index* idx, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                             int n_new, void* stream);
+
+/* Bytes of workspace kv_cluster_cluster_window needs for a window of m tokens. */
+size_t kv_cluster_window_workspace_bytes(int heads, int m, int n_clusters, int iters);
+
+/*
+ * Clustering of the window (III.B: the generated tokens alone, into a few new
+ * centroids, 4 every 320 steps on the pages; Sys-A): the m = n_tokens -
+ * window_start window tokens of every head are clustered into n_clusters
+ * clusters by `iters` iterations of the same cosine k-means as
+ * kv_cluster_build, from the initial centroids at init_idx ([heads,
+ * n_clusters] int32 token positions, distinct, in [window_start, n_tokens);
+ * one out of range sets bit 0 of *idx->dev_flags and row 0 is used instead).
+ * The new clusters take ids c_active .. c_active+n_clusters-1 (centroids,
+ * operand, sizes, offsets after those of the existing clusters, members
+ * after the existing members, labels); the existing clusters do not change.
+ * With idx->packed set, the new members' rows are added to the packed copy
+ * (read from k_cache and v_cache). Then c_active grows by n_clusters and the
+ * window is empty (window_start = n_tokens). Requires 1 <= n_clusters <= m,
+ * c_active + n_clusters <= the slots per head, iters >= 1, and a workspace of
+ * kv_cluster_window_workspace_bytes(heads, m, n_clusters, iters) bytes
+ * (contents need not be initialised).
+ */
+int kv_cluster_cluster_window(kvc_index* idx, const void* k_cache, const void* v_cache, int n_clusters, int iters,
+                              const int32_t* init_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Cluster-granular selection (III.C; Sys-C, Fig. 8) for every KV head h:
  *   - the G = q_heads / heads query heads of h are summed (fp64),
  *   - score_k = fp64 dot product of that sum with centroid k (ascending
  *     channel order), the logit of the centroid's attention weight,
- *   - the idx->n_sink attention sinks come first (tokens 0 .. n_sink-1, as
- *     many as B allows); then clusters are taken in order of (score
- *     descending, id ascending), each contributing its tokens in ascending
- *     position order, until B tokens are taken; the last cluster is trimmed.
+ *   - the idx->n_sink attention sinks come first (tokens 0 .. n_sink-1),
+ *     then the window (tokens window_start .. n_tokens-1), in position
+ *     order and as many as B allows; then the clusters in use are taken in
+ *     order of (score descending, id ascending), each contributing its
+ *     tokens in ascending position order, until B tokens are taken; the last
+ *     cluster is trimmed.
  * q is [q_heads, d] in idx->dtype. sel_ids [heads, B] receives the selected
- * token positions (in rank order; -1 past the count) and sel_count [heads]
- * receives min(B, n_sink + tokens in the index). Requires B >= 1 and G <= 8.
+ * token positions (in that order; -1 past the count) and sel_count [heads]
+ * receives min(B, n_sink + window + tokens in the clusters). Requires B >= 1
+ * and G <= 8.
  */
 int kv_cluster_select(const kvc_index* idx, const void* q, int q_heads, int B, int32_t* sel_ids,
                       int32_t* sel_count, void* stream);
@@ -193,15 +254,17 @@ int kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void
                      float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Cluster-ordered copy of the built tokens' keys and values: row i of head h
- * of idx->k_packed / idx->v_packed becomes row token_ids[h][i] of k_cache /
- * v_cache ([heads, capacity, d], idx->dtype), for i < idx->n_build. The
- * members of each cluster then lie in consecutive rows, and
- * kv_cluster_select_decode reads the selected built tokens from the copy
- * (tokens appended later still come from the caches through the appended
- * list). Sets idx->packed to 1; kv_cluster_build resets it. Costs a second
- * copy of the built part of the caches. Requires a built index and both
- * packed arrays; otherwise KVC_ERR_INVALID_ARG.
+ * Cluster-ordered copy of the keys and values of the index's main part: row i
+ * of head h of idx->k_packed / idx->v_packed becomes row token_ids[h][i] of
+ * k_cache / v_cache ([heads, capacity, d], idx->dtype), for i <
+ * offsets[h][c_active] (the built tokens and those clustered from windows).
+ * The members of each cluster then lie in consecutive rows, and
+ * kv_cluster_select_decode reads the selected main-part tokens from the copy
+ * (sinks, window tokens and tokens appended by kv_cluster_append still come
+ * from the caches). Sets idx->packed to 1; kv_cluster_build resets it, and
+ * kv_cluster_cluster_window extends the copy. Costs a second copy of that
+ * part of the caches. Requires a built index and both packed arrays;
+ * otherwise KVC_ERR_INVALID_ARG.
  */
 int kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, void* stream);
 
@@ -239,10 +302,11 @@ int kv_dense_decode(const void* q, int q_heads, const void* k_cache, const void*
                     int capacity, int d, int n, float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * The canonical index of every head (built and appended tokens merged):
- * offsets [heads, C+1] and token_ids [heads, capacity] with each cluster's
- * members in ascending order, as a stable counting sort of all labels would
- * give (Sys-C). For tests and checkpoints.
+ * The canonical index of every head (main and appended parts merged):
+ * offsets [heads, S+1] (S = slots per head; entries past c_active hold the
+ * total) and token_ids [heads, capacity] with each cluster's members in
+ * ascending order, as a stable counting sort of all labels of clustered
+ * tokens would give (Sys-C). For tests and checkpoints.
  */
 int kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token_ids, void* stream);
 
@@ -251,7 +315,7 @@ int kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token
  * without attention sinks: kv_cluster_debug_update rejects n_sink != 0).
  *  - kv_cluster_debug_assign: labels [heads, capacity] of the first L keys
  *    under the given operand chat [heads, cpad(C), d] (same rule as the
- *    build). top2 (optional, [heads, L, 2] fp32) receives the matrix-core
+ *    build; this chat has cpad(C) rows per head whatever the slot count). top2 (optional, [heads, L, 2] fp32) receives the matrix-core
  *    best and runner-up scores of bf16 keys; flagged (optional, [1]) the
  *    number of keys whose order the fp32 scores could not certify and which
  *    were re-scored in fp64. ws as for the build.

@@ -203,12 +203,15 @@ def build(K: np.ndarray, C: int, iters: int, init_idx: np.ndarray, L: int | None
 
 
 class Index:
-    """Canonical host-side cluster index of one build, grown by append()."""
+    """Canonical host-side cluster index of one build, grown by append()
+    (nearest centroid) or by add_window() + cluster_window() (generated tokens
+    clustered on their own, III.B)."""
 
     def __init__(self, built: dict, capacity: int):
         H, L = built["labels"].shape
         self.H, self.C = built["sizes"].shape
         self.n = L  # tokens, sinks included; the next one gets position n
+        self.window_start = L  # tokens window_start .. n-1 are in no cluster yet
         self.c = built["c"]
         self.chat = built["chat"]
         self.labels = np.full((H, capacity), -1, dtype=np.int32)
@@ -221,6 +224,8 @@ class Index:
 
     def append(self, knew: np.ndarray) -> np.ndarray:
         """knew [H, d]: one new key per head; returns the labels."""
+        if self.window_start != self.n:
+            raise ValueError("the window of generated tokens is not empty: cluster it first")
         lib = _load()
         knew = _c(knew)
         H, d = knew.shape
@@ -235,27 +240,61 @@ class Index:
             out[h] = lib.orc_append(d, self.C, self.n, _ptr(kh), _dt(kh), _ptr(ch), _dt(ch), _ptr(lab),
                                     _ptr(sz), _ptr(off), _ptr(ids))
         self.n += 1
+        self.window_start = self.n
         return out
+
+    def add_window(self, n_new: int = 1):
+        """n_new generated tokens per head join the window (label -1)."""
+        self.n += n_new
+
+    def cluster_window(self, K: np.ndarray, n_clusters: int, iters: int, init_idx: np.ndarray) -> dict:
+        """III.B: the window's tokens (positions window_start .. n-1 of the keys
+        K [H, rows, d]) are clustered on their own by the prefill k-means into
+        n_clusters new clusters, starting from the keys at init_idx ([H,
+        n_clusters] positions in the window). The new clusters get the next
+        ids, C .. C + n_clusters - 1; the existing ones do not change. Since
+        their ids are the largest, their members follow every existing member
+        in the canonical index. Returns the window's own build result."""
+        lo, hi = self.window_start, self.n
+        r = build(np.ascontiguousarray(K[:, lo:hi]), n_clusters, iters,
+                  np.asarray(init_idx, np.int32) - np.int32(lo))
+        C0, m = self.C, hi - lo
+        total = self.offsets[:, C0]
+        self.labels[:, lo:hi] = C0 + r["labels"]
+        self.c = np.concatenate([self.c, r["c"]], axis=1)
+        self.chat = np.concatenate([self.chat, r["chat"]], axis=1)
+        self.sizes = np.concatenate([self.sizes, r["sizes"]], axis=1)
+        self.offsets = np.concatenate([self.offsets, total[:, None] + r["offsets"][:, 1:]], axis=1)
+        for h in range(self.H):
+            self.token_ids[h, total[h]:total[h] + m] = r["token_ids"][h] + lo
+        self.C += n_clusters
+        self.window_start = hi
+        return r
 
 
 def select(q: np.ndarray, G: int, c: np.ndarray, sizes: np.ndarray, offsets: np.ndarray,
-           token_ids: np.ndarray, B: int, n_sink: int = 0):
+           token_ids: np.ndarray, B: int, n_sink: int = 0, window: tuple | None = None):
     """q [H*G, d]; c fp32 [H, C, d]; CSR arrays per head. Returns
     (sel_ids [H, B], sel_count [H], scores [H, C], order [H, C]).
 
-    n_sink: attention sinks (III.B) are always recalled: the first min(B,
-    n_sink) entries are tokens 0 .. n_sink - 1, and the clusters fill the
-    remaining B - n_sink entries as without sinks."""
-    if n_sink:
+    Tokens recalled ahead of every cluster, as many as B allows, in this
+    order: n_sink attention sinks (III.B; tokens 0 .. n_sink - 1), then the
+    window of generated tokens not yet clustered (window = (lo, hi): tokens lo
+    .. hi - 1). The clusters fill the remaining entries as on their own."""
+    fixed = np.arange(n_sink, dtype=np.int32)
+    if window is not None:
+        fixed = np.concatenate([fixed, np.arange(window[0], window[1], dtype=np.int32)])
+    nf = fixed.shape[0]
+    if nf:
         H = c.shape[0]
-        ns = min(B, n_sink)
-        rest = max(B - n_sink, 1)
+        ns = min(B, nf)
+        rest = max(B - nf, 1)
         s2, c2, scores, order = select(q, G, c, sizes, offsets, token_ids, rest)
         sel = np.full((H, B), -1, dtype=np.int32)
-        sel[:, :ns] = np.arange(ns, dtype=np.int32)
+        sel[:, :ns] = fixed[:ns]
         cnt = np.full(H, ns, dtype=np.int32)
-        if B > n_sink:
-            sel[:, n_sink:] = s2
+        if B > nf:
+            sel[:, nf:] = s2
             cnt = cnt + c2
         return sel, cnt, scores, order
     lib = _load()

@@ -36,9 +36,14 @@ def test_every_declared_function_is_exported(kvc):
         assert hasattr(kvc.lib(), n), n
 
 
-def make_index(kvc, heads=4, d=128, Cn=16, cap=256, dtype=1, n_build=0, n_tokens=0, null=None):
+def make_index(kvc, heads=4, d=128, Cn=16, cap=256, dtype=1, n_build=0, n_tokens=0, null=None, window=0):
+    """A descriptor with fake pointers; a "built" one (n_build > 0) has C
+    clusters in use and `window` tokens in its window."""
     ptrs = [FAKE] * 10
     s = kvc._Index(heads, d, Cn, cap, dtype, n_build, n_tokens, 0, *ptrs)
+    if n_build:
+        s.c_active = Cn
+        s.window_start = n_tokens - window
     if null:
         setattr(s, null, None)
     return s
@@ -129,6 +134,42 @@ def test_append_select_decode_reject(kvc):
     withp = make_index(kvc, n_build=200, n_tokens=200)
     withp.k_packed = FAKE
     assert L.kv_cluster_pack(C.byref(withp), p, None, None) == INVALID        # no v_cache
+
+
+def test_window_calls_reject(kvc):
+    """Generated-token window: appends, clustering and slot counts are checked
+    against the index state before anything is enqueued."""
+    L = kvc.lib()
+    p = C.c_void_p(FAKE)
+    # a nearest-centroid append needs an empty window
+    open_w = make_index(kvc, cap=256, n_build=200, n_tokens=210, window=10)
+    assert L.kv_cluster_append(C.byref(open_w), p, p, p, p, 1, None) == INVALID
+    assert L.kv_cluster_append_window(C.byref(open_w), p, p, p, p, 47, None) == CAPACITY
+    assert L.kv_cluster_append_window(C.byref(open_w), p, p, p, p, 0, None) == INVALID
+    assert L.kv_cluster_append_window(C.byref(make_index(kvc)), p, p, p, p, 1, None) == INVALID  # never built
+    # clustering the window: 1 <= n_clusters <= window, free slots, iters >= 1, workspace
+    ws = L.kv_cluster_window_workspace_bytes(4, 10, 2, 3)
+    assert ws > 0 and ws % 256 == 0 and L.kv_cluster_window_workspace_bytes(4, 0, 2, 3) == 0
+    slotted = make_index(kvc, Cn=16, cap=256, n_build=200, n_tokens=210, window=10)
+    slotted.c_slots = 20
+    cw = lambda idx, nc=2, it=3, b=ws: L.kv_cluster_cluster_window(C.byref(idx), p, p, nc, it, p, p, b, None)
+    assert cw(open_w) == INVALID                      # no free slot (c_slots = C)
+    assert cw(slotted, nc=0) == INVALID
+    assert cw(slotted, nc=11) == INVALID              # more clusters than window tokens
+    assert cw(slotted, nc=5) == INVALID               # 16 + 5 > 20 slots
+    assert cw(slotted, it=0) == INVALID
+    assert cw(slotted, b=ws - 1) == WORKSPACE
+    empty = make_index(kvc, Cn=16, cap=256, n_build=200, n_tokens=200)
+    empty.c_slots = 20
+    assert cw(empty, nc=1) == INVALID                 # empty window
+    assert cw(make_index(kvc), nc=1) == INVALID       # never built
+    # slot counts: at least C, at most 512
+    few = make_index(kvc, Cn=16)
+    few.c_slots = 8
+    assert L.kv_cluster_build(C.byref(few), p, 200, 3, p, p, 1 << 40, None) == INVALID
+    many = make_index(kvc, Cn=16)
+    many.c_slots = 600
+    assert L.kv_cluster_build(C.byref(many), p, 200, 3, p, p, 1 << 40, None) == UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(kvc, monkeypatch):

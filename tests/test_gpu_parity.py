@@ -25,6 +25,9 @@ SMALL = synth.Workload("small_bf16_ragged", 90, heads=3, G=2, L=1500, d=128, dty
 SMALL_APPEND = synth.Workload("small_bf16_append", 91, heads=2, G=1, L=1100, d=128, dtype=synth.BF16, M=24,
                               sigma=0.3, n_out=4, out_scale=10.0, C=37, iters=5, B=300, steps=20, query="noisy_key",
                               q_sigma=0.1, append=True)
+SMALL_WINDOW = synth.Workload("small_bf16_window", 92, heads=3, G=2, L=1100, d=128, dtype=synth.BF16, M=24,
+                              sigma=0.3, n_out=4, out_scale=10.0, C=37, iters=5, B=300, steps=130,
+                              query="noisy_key", q_sigma=0.1, append=True)
 CASES = {"cfg1_fp32": synth.workload(1), "small_bf16": SMALL}
 
 
@@ -309,6 +312,104 @@ def test_attention_sinks_end_to_end():
                 assert np.abs(to_np(fout) - od).max() <= 2e-3, (step, B, pk)
             idx._s.packed = 1
         say(f"  sinks: step {step}, {n} tokens, count {ocnt.tolist()}")
+
+
+def test_window_clustering_end_to_end():
+    """III.B / Sys-A: generated tokens join a window that every selection
+    recalls (after the attention sinks), and every m tokens the window alone is
+    clustered into nc new clusters. Each clustering is checked bit-exact
+    against the oracle (labels, centroids, operand, sizes, offsets, member ids,
+    the packed copy's new rows); selections (split and fused, from the caches
+    and from the packed copy, budgets that cut inside the window, after it and
+    past every token) and attention are checked along the way; a
+    nearest-centroid append after a clustering may pick a new cluster."""
+    w, n_sink, m, nc = SMALL_WINDOW, 8, 40, 4
+    base, K, V, _, means = make_inputs(w)
+    H = K.shape[0]
+    init = synth.init_idx(base, H, w.L - n_sink, w.C) + n_sink
+    slots = w.C + 3 * nc
+    idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w), packed=True, n_sink=n_sink, c_slots=slots)
+    Kc, Vc = K.copy(), V.copy()
+    Kc[:, w.L:], Vc[:, w.L:] = 0, 0
+    Kd, Vd = to_dev(Kc), to_dev(Vc)
+    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.pack(idx, Kd, Vd)
+    torch.cuda.synchronize()
+    ref = oracle.build(np.ascontiguousarray(K[:, :w.L]), w.C, w.iters, init, n_sink=n_sink)
+    assert np.array_equal(to_np(idx.labels)[:, :w.L], ref["labels"])
+    assert np.array_equal(to_np(idx.centroids)[:, :w.C], ref["c"])
+    assert idx.c_active == w.C and idx.window_start == w.L
+    oi = oracle.Index(ref, w.capacity)
+    scale = 1.0 / math.sqrt(w.d)
+    n, step, windows = w.L, 0, 0
+
+    def check_index():
+        ca, nt = oi.C, oi.n
+        assert idx.c_active == ca and idx.window_start == oi.window_start and idx.n_tokens == nt
+        assert np.array_equal(to_np(idx.labels)[:, :nt], oi.labels[:, :nt])
+        assert np.array_equal(to_np(idx.centroids)[:, :ca], oi.c)
+        assert np.array_equal(to_np(idx.centroids_op)[:, :ca], oi.chat)
+        assert np.array_equal(to_np(idx.sizes)[:, :ca], oi.sizes)
+        off, ids = kvc.export_csr(idx)
+        off, ids = to_np(off), to_np(ids)
+        assert np.array_equal(off[:, :ca + 1], oi.offsets) and np.all(off[:, ca + 1:] == oi.offsets[:, -1:])
+        total = int(oi.offsets[0, -1])
+        assert np.array_equal(ids[:, :total], oi.token_ids[:, :total])
+
+    def check_select(q, B):
+        win = (oi.window_start, oi.n)
+        osel, ocnt, _, _ = oracle.select(q, w.G, oi.c, oi.sizes, oi.offsets, oi.token_ids, B, n_sink=n_sink,
+                                         window=win)
+        od = oracle.decode(q, w.G, K, V, osel, ocnt, scale)
+        sel, cnt = kvc.select(idx, to_dev(q), B)
+        out = kvc.sparse_decode(to_dev(q), Kd, Vd, sel, cnt, scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(sel), osel) and np.array_equal(to_np(cnt), ocnt), (step, B)
+        assert np.abs(to_np(out) - od).max() <= 2e-3, (step, B)
+        for pk in (1, 0):
+            idx._s.packed = pk
+            fsel = torch.full((H, B), -7, dtype=torch.int32, device="cuda")
+            fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_np(fsel), osel), (step, B, pk)
+            assert np.abs(to_np(fout) - od).max() <= 2e-3, (step, B, pk)
+        idx._s.packed = 1
+
+    while n < w.capacity:
+        kvc.append_window(idx, Kd, Vd, to_dev(np.ascontiguousarray(K[:, n:n + 1])),
+                          to_dev(np.ascontiguousarray(V[:, n:n + 1])))
+        oi.add_window(1)
+        n += 1
+        step += 1
+        if n - oi.window_start == m and oi.C + nc <= slots:
+            init_w = synth.init_idx(synth.stream_seed(base, 7, windows), H, m, nc) + np.int32(n - m)
+            kvc.cluster_window(idx, Kd, Vd, nc, w.iters, to_dev(init_w))
+            oi.cluster_window(K, nc, w.iters, init_w)
+            torch.cuda.synchronize()
+            windows += 1
+            assert int(to_np(idx.dev_flags)[0]) == 0
+            check_index()
+            # the packed copy holds every member of the main part, in index order
+            total = int(oi.offsets[0, -1])
+            kp, vp = to_np(idx.k_packed), to_np(idx.v_packed)
+            for h in range(H):
+                rows = oi.token_ids[h, :total]
+                assert np.array_equal(kp[h, :total], K[h, rows]) and np.array_equal(vp[h, :total], V[h, rows])
+            say(f"  window {windows} clustered at {n} tokens: {oi.C} clusters, sizes of the new ones "
+                f"{oi.sizes[:, -nc:].tolist()}")
+            if windows == 3 and n < w.capacity:
+                # a nearest-centroid append, with the window empty
+                kvc.append(idx, Kd, Vd, to_dev(np.ascontiguousarray(K[:, n:n + 1])),
+                           to_dev(np.ascontiguousarray(V[:, n:n + 1])))
+                oi.append(np.ascontiguousarray(K[:, n]))
+                n += 1
+                torch.cuda.synchronize()
+                check_index()
+        if step % 9 == 1 or n == w.capacity:
+            q = queries(w, base, step, K, n, means)
+            for B in (w.B, n_sink + 10, n + 40):
+                check_select(q, B)
+    assert windows == 3
 
 
 def test_init_index_out_of_range_flag():

@@ -491,3 +491,100 @@ def test_sinks_stay_out_of_clusters_and_are_always_selected(orc, syn):
     # a budget within the sinks recalls sinks only
     sel, cnt, _, _ = orc.select(q, 1, r["c"], r["sizes"], r["offsets"], r["token_ids"], 5, n_sink=n_sink)
     assert cnt.tolist() == [5, 5] and np.all(sel == np.arange(5))
+
+
+# ------------------------------------------------- generated-token clustering
+
+def _canonical(labels: np.ndarray, C: int):
+    """Stable sort of the clustered tokens (label >= 0) by label, with numpy."""
+    ids = np.flatnonzero(labels >= 0)
+    order = np.argsort(labels[ids], kind="stable")
+    sizes = np.bincount(labels[ids], minlength=C)
+    return sizes, np.concatenate([[0], np.cumsum(sizes)]), ids[order].astype(np.int32)
+
+
+def test_window_clustering_extends_the_index(orc, syn):
+    """III.B: tokens generated during decoding are clustered on their own, into
+    a few new centroids, and until then stay uncompressed in a window that is
+    always recalled. The existing clusters do not change; the new clusters are
+    the prefill k-means of the window's keys alone, with the next ids; their
+    centroids are the exact means of their members; the canonical index equals
+    the stable sort of all labels; sinks and window come first in a selection,
+    as many as the budget allows."""
+    n_sink, C, L, d, m, nc, B = 4, 9, 300, 16, 40, 4, 64
+    H = 2
+    base = syn.config_seed(97)
+    K, _, _ = syn.mixture_keys(base, H, L + 2 * m + 3, d, 6, 0.3, 0, 1.0, syn.BF16)
+    init = syn.init_idx(base, H, L - n_sink, C) + n_sink
+    r = orc.build(np.ascontiguousarray(K[:, :L]), C, 5, init, n_sink=n_sink)
+    idx = orc.Index(r, K.shape[1])
+    idx.add_window(m)
+    assert np.all(idx.labels[:, L:L + m] == -1) and idx.window_start == L and idx.n == L + m
+    q = syn.normal_array(syn.stream_seed(base, 0, 9), H * d, 1.0, syn.BF16).reshape(H, d)
+    # selection with an open window: sinks, then the window, then the clusters
+    sel, cnt, _, _ = orc.select(q, 1, idx.c, idx.sizes, idx.offsets, idx.token_ids, B, n_sink=n_sink,
+                                window=(L, L + m))
+    rest, rcnt, _, _ = orc.select(q, 1, idx.c, idx.sizes, idx.offsets, idx.token_ids, B - n_sink - m)
+    assert cnt.tolist() == [B, B]
+    assert np.all(sel[:, :n_sink] == np.arange(n_sink)) and np.all(sel[:, n_sink:n_sink + m] == np.arange(L, L + m))
+    assert np.array_equal(sel[:, n_sink + m:], rest)
+    small, scnt, _, _ = orc.select(q, 1, idx.c, idx.sizes, idx.offsets, idx.token_ids, 10, n_sink=n_sink,
+                                   window=(L, L + m))
+    assert scnt.tolist() == [10, 10] and np.all(small == np.concatenate([np.arange(n_sink), np.arange(L, L + 6)]))
+    # cluster the window
+    before = dict(c=idx.c.copy(), sizes=idx.sizes.copy(), offsets=idx.offsets.copy(), ids=idx.token_ids.copy())
+    init_w = syn.init_idx(syn.config_seed(98), H, m, nc) + L
+    rw = idx.cluster_window(K, nc, 6, init_w)
+    assert idx.C == C + nc and idx.window_start == L + m
+    assert np.array_equal(idx.c[:, :C], before["c"]) and np.array_equal(idx.sizes[:, :C], before["sizes"])
+    assert np.array_equal(idx.offsets[:, :C + 1], before["offsets"])
+    nbuilt = L - n_sink
+    assert np.array_equal(idx.token_ids[:, :nbuilt], before["ids"][:, :nbuilt])
+    alone = orc.build(np.ascontiguousarray(K[:, L:L + m]), nc, 6, init_w - L)
+    assert np.array_equal(rw["labels"], alone["labels"]) and np.array_equal(rw["c"], alone["c"])
+    # the window's keys alone decide: other keys changed, same clustering
+    K2 = K.copy()
+    K2[:, :L] = K[:, ::-1][:, :L]
+    idx2 = orc.Index(r, K.shape[1])
+    idx2.add_window(m)
+    assert np.array_equal(idx2.cluster_window(K2, nc, 6, init_w)["labels"], rw["labels"])
+    kf = orc.to_f64(K)
+    for h in range(H):
+        lab = idx.labels[h, :L + m]
+        assert np.all(lab[:n_sink] == -1) and np.all((lab[L:] >= C) & (lab[L:] < C + nc))
+        s, o, i = _canonical(lab, C + nc)
+        assert np.array_equal(s, idx.sizes[h]) and np.array_equal(o, idx.offsets[h])
+        assert np.array_equal(i, idx.token_ids[h, :L + m - n_sink])
+        for k in range(C, C + nc):
+            mem = np.flatnonzero(lab == k)
+            if mem.size:  # exact mean of bf16 values, rounded once to fp32
+                want = np.array([math.fsum(kf[h, mem, j]) for j in range(d)]) / mem.size
+                assert np.array_equal(idx.c[h, k], want.astype(np.float32)), (h, k)
+    # an empty window recalls nothing extra; a nearest-centroid append may pick a new cluster
+    sel2, cnt2, _, _ = orc.select(q, 1, idx.c, idx.sizes, idx.offsets, idx.token_ids, B, n_sink=n_sink,
+                                  window=(L + m, L + m))
+    sel3, cnt3, _, _ = orc.select(q, 1, idx.c, idx.sizes, idx.offsets, idx.token_ids, B, n_sink=n_sink)
+    assert np.array_equal(sel2, sel3) and np.array_equal(cnt2, cnt3)
+    labs = idx.append(K[:, L + m])
+    for h in range(H):
+        assert labs[h] == int(np.argmax(orc.to_f64(idx.chat[h]) @ kf[h, L + m]))
+
+
+def test_window_clustering_two_groups_closed_form(orc):
+    """A window of two tight, orthogonal groups clustered into two centroids,
+    one started in each group: each group becomes a cluster and each centroid is
+    its group's mean (hand-computable values)."""
+    d, H = 4, 1
+    pre = np.array([[1, 1, 1, 1], [1, -1, 1, -1], [-1, 1, -1, 1], [1, 1, -1, -1]], np.float32)
+    win = np.array([[2, 0, 0, 0], [0, 0, 3, 0], [4, 0.5, 0, 0], [0, 0, 5, 0.5], [3, -0.5, 0, 0], [0, 0.25, 2, 0]],
+                   np.float32)
+    K = np.concatenate([pre, win])[None]
+    r = orc.build(np.ascontiguousarray(K[:, :4]), 2, 3, np.array([[0, 1]], np.int32))
+    idx = orc.Index(r, 10)
+    idx.add_window(6)
+    idx.cluster_window(K, 2, 4, np.array([[4, 5]], np.int32))
+    assert idx.labels[0, 4:10].tolist() == [2, 3, 2, 3, 2, 3]
+    assert np.array_equal(idx.c[0, 2], np.array([3, 0, 0, 0], np.float32))
+    assert np.array_equal(idx.c[0, 3], np.array([0, 0.25 / 3, 10 / 3, 0.5 / 3], np.float32))
+    assert idx.sizes[0].tolist()[2:] == [3, 3] and idx.offsets[0].tolist()[2:] == [4, 7, 10]
+    assert idx.token_ids[0, 4:10].tolist() == [4, 6, 8, 5, 7, 9]
