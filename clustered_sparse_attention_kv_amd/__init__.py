@@ -19,6 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvcluster.so")
 
 KVC_F32, KVC_BF16 = 0, 1
+COSINE, L2, INNER_PRODUCT = 0, 1, 2  # assignment distance (kvc_metric)
 HEAD_DIM, MAX_C, MAX_G = 128, 512, 8
 
 _lib = None
@@ -38,7 +39,7 @@ class _Index(C.Structure):
                 ("app_offsets", C.c_void_p), ("app_ids", C.c_void_p), ("dev_flags", C.c_void_p),
                 ("centroids_t", C.c_void_p), ("k_packed", C.c_void_p), ("v_packed", C.c_void_p),
                 ("n_sink", C.c_int32), ("c_slots", C.c_int32), ("c_active", C.c_int32),
-                ("window_start", C.c_int32)]
+                ("window_start", C.c_int32), ("metric", C.c_int32)]
 
 
 def lib():
@@ -136,12 +137,14 @@ class ClusterIndex:
     """Device memory of one cluster index (``kvc_index``), allocated with torch."""
 
     def __init__(self, heads: int, C_: int, capacity: int, dtype: torch.dtype = torch.bfloat16,
-                 d: int = HEAD_DIM, device="cuda", packed: bool = False, n_sink: int = 0, c_slots: int = 0):
+                 d: int = HEAD_DIM, device="cuda", packed: bool = False, n_sink: int = 0, c_slots: int = 0,
+                 metric: int = COSINE):
         """packed: also allocate the cluster-ordered copies of the keys and
         values (``kv_cluster_pack``), two more arrays of the caches' size.
         n_sink: attention sinks, kept out of the clustering and always
         selected first. c_slots: cluster slots per head (>= C; 0 for C), room
-        for the clusters that ``cluster_window`` adds."""
+        for the clusters that ``cluster_window`` adds. metric: assignment
+        distance, COSINE (the method's), L2 or INNER_PRODUCT."""
         self.heads, self.C, self.capacity, self.d, self.dtype = heads, C_, capacity, d, dtype
         S = c_slots if c_slots else C_
         self.slots = S
@@ -164,7 +167,8 @@ class ClusterIndex:
                          self.app_offsets.data_ptr(), self.app_ids.data_ptr(), self.dev_flags.data_ptr(),
                          self.centroids_t.data_ptr(),
                          self.k_packed.data_ptr() if packed else None,
-                         self.v_packed.data_ptr() if packed else None, n_sink, c_slots, 0, 0)
+                         self.v_packed.data_ptr() if packed else None, n_sink, c_slots, 0, 0, metric)
+        self.metric = metric
         self.n_sink = n_sink
 
     @property

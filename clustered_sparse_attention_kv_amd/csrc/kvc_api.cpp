@@ -21,7 +21,8 @@ bool index_ok(const kvc_index* idx) {
   return idx && idx->centroids && idx->centroids_op && idx->labels && idx->sizes && idx->offsets && idx->token_ids &&
          idx->app_offsets && idx->app_ids && idx->dev_flags && idx->centroids_t && idx->heads >= 1 &&
          idx->capacity >= 1 && idx->C >= 1 && (idx->dtype == KVC_F32 || idx->dtype == KVC_BF16) &&
-         idx->n_sink >= 0 && (idx->c_slots == 0 || idx->c_slots >= idx->C);
+         idx->n_sink >= 0 && (idx->c_slots == 0 || idx->c_slots >= idx->C) && idx->metric >= KVC_COSINE &&
+         idx->metric <= KVC_INNER_PRODUCT;
 }
 
 int index_support(const kvc_index* idx) {
@@ -148,18 +149,18 @@ int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, c
   if (e == hipSuccess) e = launch_fill_i32(idx->app_offsets, (size_t)H * (cs + 1), 0, st);
   if (e == hipSuccess) e = launch_fill2d_i32(idx->labels, H, cap, ns, -1, st);  // sinks: in no cluster
   if (e == hipSuccess)
-    e = launch_init_centroids(idx->dtype, keys, hs, H, ns, L, init_idx, C, cpad, cs, cps, idx->centroids,
+    e = launch_init_centroids(idx->dtype, keys, hs, H, ns, L, init_idx, C, cpad, cs, cps, idx->metric, idx->centroids,
                               idx->centroids_t, idx->centroids_op, idx->dev_flags, st);
   for (int t = 0; t < iters && e == hipSuccess; ++t) {
     hipEvent_t* ev = assign_events ? (hipEvent_t*)assign_events + 2 * t : nullptr;
-    e = launch_assign(idx->dtype, keys_c, hs, H, Lc, idx->centroids_op, C, cpad, cps, idx->labels + ns, cap, w.queue,
-                      w.qcount + (size_t)t * H, nullptr, ev, st);
+    e = launch_assign(idx->dtype, keys_c, hs, H, Lc, idx->centroids_op, C, cpad, cps, idx->metric, idx->labels + ns,
+                      cap, w.queue, w.qcount + (size_t)t * H, nullptr, ev, st);
     if (e == hipSuccess)
       e = launch_csr(idx->labels + ns, cap, H, Lc, C, cs, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, ns,
                      st);
     if (e == hipSuccess)
-      e = launch_update(idx->dtype, keys, hs, H, C, cs, cps, idx->sizes, idx->offsets, idx->token_ids, cap,
-                        idx->centroids, idx->centroids_t, idx->centroids_op, st);
+      e = launch_update(idx->dtype, keys, hs, H, C, cs, cps, idx->metric, idx->sizes, idx->offsets, idx->token_ids,
+                        cap, idx->centroids, idx->centroids_t, idx->centroids_op, st);
   }
   if (e != hipSuccess) return KVC_ERR_HIP;
   idx->n_build = L;
@@ -180,8 +181,8 @@ int kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.qcount), (size_t)H, 0, st);
   if (e == hipSuccess)
-    e = launch_assign(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, L, chat, C, cpad, cpad, labels, cap,
-                      w.queue, w.qcount, top2, nullptr, st);
+    e = launch_assign(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, L, chat, C, cpad, cpad, idx->metric, labels,
+                      cap, w.queue, w.qcount, top2, nullptr, st);
   if (e == hipSuccess && flagged)
     e = hipMemcpyAsync(flagged, w.qcount, sizeof(int32_t) * H, hipMemcpyDeviceToDevice, st);
   return hip_status(e);
@@ -200,8 +201,8 @@ int kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, s
   hipError_t e =
       launch_csr(idx->labels, cap, H, L, C, cs, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, 0, st);
   if (e == hipSuccess)
-    e = launch_update(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, C, cs, cps, idx->sizes, idx->offsets,
-                      idx->token_ids, cap, idx->centroids, idx->centroids_t, idx->centroids_op, st);
+    e = launch_update(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, C, cs, cps, idx->metric, idx->sizes,
+                      idx->offsets, idx->token_ids, cap, idx->centroids, idx->centroids_t, idx->centroids_op, st);
   return hip_status(e);
 }
 
@@ -215,7 +216,7 @@ int kv_cluster_append(kvc_index* idx, void* k_cache, void* v_cache, const void* 
   const int cs = slots(idx), cap = idx->capacity;
   hipError_t e = launch_append(idx->dtype, k_cache, v_cache, (long long)cap * KVC_HEAD_DIM, idx->heads, k_new, v_new,
                                n_new, idx->n_tokens, idx->centroids_op, idx->c_active, cs, kv_cluster_cpad(cs),
-                               idx->labels, cap, idx->sizes, idx->app_offsets, idx->app_ids,
+                               idx->metric, idx->labels, cap, idx->sizes, idx->app_offsets, idx->app_ids,
                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return KVC_ERR_HIP;
   idx->n_tokens += n_new;
@@ -260,15 +261,15 @@ int kv_cluster_cluster_window(kvc_index* idx, const void* k_cache, const void* v
   const void* keys_w = static_cast<const char*>(k_cache) + (size_t)wlo * KVC_HEAD_DIM * elem_bytes(idx->dtype);
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.b.qcount), (size_t)iters * H, 0, st);
   if (e == hipSuccess)
-    e = launch_init_centroids(idx->dtype, k_cache, hs, H, wlo, idx->n_tokens, init_idx, nc, cpw, nc, cpw, w.cent,
-                              w.cent_t, w.chat, idx->dev_flags, st);
+    e = launch_init_centroids(idx->dtype, k_cache, hs, H, wlo, idx->n_tokens, init_idx, nc, cpw, nc, cpw, idx->metric,
+                              w.cent, w.cent_t, w.chat, idx->dev_flags, st);
   for (int t = 0; t < iters && e == hipSuccess; ++t) {
-    e = launch_assign(idx->dtype, keys_w, hs, H, m, w.chat, nc, cpw, cpw, w.labels, m, w.b.queue,
+    e = launch_assign(idx->dtype, keys_w, hs, H, m, w.chat, nc, cpw, cpw, idx->metric, w.labels, m, w.b.queue,
                       w.b.qcount + (size_t)t * H, nullptr, nullptr, st);
     if (e == hipSuccess) e = launch_csr(w.labels, m, H, m, nc, nc, w.b.hist, w.sizes, w.offsets, w.ids, m, wlo, st);
     if (e == hipSuccess)
-      e = launch_update(idx->dtype, k_cache, hs, H, nc, nc, cpw, w.sizes, w.offsets, w.ids, m, w.cent, w.cent_t,
-                        w.chat, st);
+      e = launch_update(idx->dtype, k_cache, hs, H, nc, nc, cpw, idx->metric, w.sizes, w.offsets, w.ids, m, w.cent,
+                        w.cent_t, w.chat, st);
   }
   if (e == hipSuccess)
     e = launch_merge_window(idx->dtype, H, nc, m, wlo, w.cent, w.chat, w.labels, w.sizes, w.offsets, w.ids, ca, cs, cps,

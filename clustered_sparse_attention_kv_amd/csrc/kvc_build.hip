@@ -44,6 +44,23 @@ __device__ __forceinline__ void normalize_row(const float c0, const float c1, fl
   store_op(out_row, 2 * lane + 1, v1);
 }
 
+// The assignment operand of one centroid row under each distance (III.B
+// defines the semantic distance by the cosine and names L2 and inner product
+// as the alternatives): the unit direction for the cosine, the centroid itself
+// for L2 and inner product, rounded once to the operand type. metric is
+// uniform over the wave.
+template <typename OT>
+__device__ __forceinline__ void operand_row(int metric, const float c0, const float c1, float* lds_row,
+                                            OT* out_row) {
+  if (metric == M_COSINE) {
+    normalize_row(c0, c1, lds_row, out_row);
+    return;
+  }
+  const int lane = lane_id();
+  store_op(out_row, 2 * lane, (double)c0);
+  store_op(out_row, 2 * lane + 1, (double)c1);
+}
+
 // ---------------------------------------------------------------------------
 // a1 + a2: initial centroids c_k = K[init_idx[k]] (exact copy to fp32) and
 // their normalised operand. One wave per centroid row, 4 rows per block.
@@ -65,9 +82,9 @@ __device__ __forceinline__ void store_centroid(float* cent_row, float* cent_t_he
 template <typename KT>
 __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restrict__ keys, long long head_stride,
                                                              int lo, int L, const int32_t* __restrict__ init_idx, int C,
-                                                             int cpad, int cs, int cps, float* __restrict__ cent,
-                                                             float* __restrict__ cent_t, KT* __restrict__ chat,
-                                                             int32_t* __restrict__ dev_flags) {
+                                                             int cpad, int cs, int cps, int metric,
+                                                             float* __restrict__ cent, float* __restrict__ cent_t,
+                                                             KT* __restrict__ chat, int32_t* __restrict__ dev_flags) {
   __shared__ float rows[4][D];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.y;
@@ -87,7 +104,7 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restric
   const KT* src = keys + (size_t)h * head_stride + (size_t)tok * D;
   const float c0 = load_f32(src, 2 * lane), c1 = load_f32(src, 2 * lane + 1);
   store_centroid(cent + ((size_t)h * cs + k) * D, cent_t + (size_t)h * cs * D, cs, k, c0, c1);
-  normalize_row(c0, c1, rows[w], out);
+  operand_row(metric, c0, c1, rows[w], out);
 }
 
 // ---------------------------------------------------------------------------
@@ -114,6 +131,13 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restric
 // products of bf16 operands are exact) with a safety factor of 4. Keys that
 // fail it are queued for exact re-scoring (fix-up kernel below). Ties and
 // near-ties therefore always resolve by the fp64 rule, lowest id first.
+//
+// The L2 and inner-product variants (METRIC) use centroids that are not unit
+// length. The score is K_i . chat_k (inner product) or K_i . chat_k + b_k with
+// b_k = -||chat_k||^2 / 2 rounded to fp32 (L2, argmin of the distance), and the
+// certificate uses the head's largest operand norm A and largest |b_k|:
+//   best - runner_up > 2 * 4 * 2^-24 * ((d + 17) * ||K_i|| * A + 2 max|b_k|) * 1.02,
+// which also covers the rounding of b_k and of the addition.
 constexpr int AS_WAVES = 8;
 constexpr int AS_THREADS = AS_WAVES * WAVE;
 constexpr int AS_TILE = AS_WAVES * 64;
@@ -125,6 +149,7 @@ __device__ __forceinline__ void top2_update(float s, int u, float& m1, float& m2
   m1 = gt ? s : m1;
 }
 
+template <int METRIC>
 __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     const uint16_t* __restrict__ keys, long long head_stride, int L, const uint16_t* __restrict__ chat, int C,
     int cpad, int cps, int32_t* __restrict__ labels, long long label_stride, int32_t* __restrict__ queue,
@@ -139,12 +164,44 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     const int r = e >> 4, c = e & 15;
     sC[r * 16 + (c ^ (r & 15))] = Cg[e];
   }
+  // variants: after the operand, the per-centroid bias (L2; cpad floats) and
+  // the largest operand norm (one word), all in the dynamic allocation so the
+  // kernel has no static LDS
+  float* sBias = reinterpret_cast<float*>(sC + cpad * 16);
+  unsigned& sMaxNorm = *reinterpret_cast<unsigned*>(sBias + cpad);
+  float normA = 1.0f, biasM = 0.0f;
+  if constexpr (METRIC != M_COSINE) {
+    if (tid == 0) sMaxNorm = 0u;
+    __syncthreads();
+    for (int k = tid; k < cpad; k += AS_THREADS) {
+      double nn = 0.0;
+      if (k < C)
+        for (int c = 0; c < 16; ++c) {
+          const u32x4 v = Cg[(size_t)k * 16 + c];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const double lo = (double)__uint_as_float(v[q] << 16), hi = (double)__uint_as_float(v[q] & 0xFFFF0000u);
+            nn = fma(lo, lo, nn);
+            nn = fma(hi, hi, nn);
+          }
+        }
+      if constexpr (METRIC == M_L2) sBias[k] = (float)(-0.5 * nn);
+      atomicMax(&sMaxNorm, __float_as_uint((float)sqrt(nn) * 1.0000001f));
+    }
+  }
   __syncthreads();
+  if constexpr (METRIC != M_COSINE) {
+    normA = __uint_as_float(sMaxNorm);
+    biasM = METRIC == M_L2 ? 0.5f * normA * normA * 1.0000001f : 0.0f;
+  }
 
   const uint16_t* Kh = keys + (size_t)h * head_stride + 8 * kb4;
   const int ngroups = (L + AS_TILE - 1) / AS_TILE;
   const int nct = cpad >> 4;
   const float gamma = 2.0f * 4.0f * (float)(D + 16) * 5.9604644775390625e-8f * 1.02f;
+  // variants: threshold = g2 * ((d + 17) * A * ||K_i|| + 2 max|b_k|)
+  const float g2 = 2.0f * 4.0f * 5.9604644775390625e-8f * 1.02f;
+  const float gA = g2 * (float)(D + 17) * normA, gB = g2 * 2.0f * biasM;
   for (int grpi = blockIdx.x; grpi < ngroups; grpi += gridDim.x) {
     const int row0 = grpi * AS_TILE + wave * 64;
     u32x4 kn[4][4];
@@ -204,11 +261,17 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     };
     auto fold = [&](int ct, const f32x4 (&acc)[4], bool masked) {
       const int u0 = ct * 16;  // centroid of register r in this lane: u0 + 4 (lane / 16) + r
+      f32x4 bias = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (METRIC == M_L2) bias = *reinterpret_cast<const f32x4*>(sBias + u0 + 4 * kb4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool ok = !masked || u0 + 4 * kb4 + r < C;
 #pragma unroll
-        for (int T = 0; T < 4; ++T) top2_update(ok ? acc[T][r] : -INFINITY, u0 + r, m1[T], m2[T], i1[T]);
+        for (int T = 0; T < 4; ++T) {
+          float sc = acc[T][r];
+          if constexpr (METRIC == M_L2) sc += bias[r];
+          top2_update(ok ? sc : -INFINITY, u0 + r, m1[T], m2[T], i1[T]);
+        }
       }
     };
     auto interleave = [&]() {
@@ -261,7 +324,8 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     for (int T = 0; T < 4; ++T)
       if (T == kb4) {
         my_label = i1[T];
-        my_flag = !((m1[T] - m2[T]) > gamma * sqrtf(n2[T]));  // true for NaN and ties
+        const float thr = METRIC == M_COSINE ? gamma * sqrtf(n2[T]) : gA * sqrtf(n2[T]) + gB;
+        my_flag = !((m1[T] - m2[T]) > thr);  // true for NaN and ties
         my_m1 = m1[T];
         my_m2 = m2[T];
       }
@@ -298,10 +362,14 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
 // with the chunk index of row r XOR-ed by r (mod the chunk count), so the 64
 // lanes of a wave, reading 64 different rows at one chunk, spread over the
 // banks. Rows come from the per-head queue (queue != null) or are all rows.
+// Under the L2 distance the score is the chain minus nn_k / 2, nn_k the fp64
+// chain of chat_kj^2 over ascending j (computed once per block, kept in LDS
+// after the staged operand).
 template <typename KT, int MAXT>
 __global__ __launch_bounds__(256) void assign_exact_kernel(const KT* __restrict__ keys, long long head_stride, int L,
                                                            const KT* __restrict__ chat, int C, int cpad, int cps,
-                                                           int32_t* __restrict__ labels, long long label_stride,
+                                                           int metric, int32_t* __restrict__ labels,
+                                                           long long label_stride,
                                                            const int32_t* __restrict__ queue,
                                                            const uint32_t* __restrict__ qcount) {
   constexpr bool STAGE = sizeof(KT) == 2;
@@ -322,8 +390,19 @@ __global__ __launch_bounds__(256) void assign_exact_kernel(const KT* __restrict_
       const int r = e / CHUNKS, c = e % CHUNKS;
       smem[r * CHUNKS + (c ^ (r & (CHUNKS - 1)))] = Cg[e];
     }
-    __syncthreads();
   }
+  double* half_nn = reinterpret_cast<double*>(smem + (STAGE ? cpad * CHUNKS : 0));
+  if (metric == M_L2) {
+    for (int c = threadIdx.x; c < cpad; c += 256) {
+      double nn = 0.0;
+      for (int j = 0; j < D; ++j) {
+        const double x = (double)load_f32(chat + (size_t)h * cps * D, (size_t)c * D + j);
+        nn = fma(x, x, nn);
+      }
+      half_nn[c] = 0.5 * nn;
+    }
+  }
+  if (STAGE || metric == M_L2) __syncthreads();
   // lane's centroid rows; rows past cpad read the last (zero) padding row and
   // are excluded from the argmax, so no branch separates the chains
   int crow[MAXT];
@@ -372,6 +451,13 @@ __global__ __launch_bounds__(256) void assign_exact_kernel(const KT* __restrict_
         }
       }
     }
+    if (metric == M_L2)
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t) {
+        const double hn = half_nn[crow[t]];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) s[kk][t] = s[kk][t] - hn;
+      }
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       double best = -INFINITY;
@@ -521,7 +607,7 @@ struct UpdRow<float> {
 
 template <typename KT>
 __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys, long long head_stride, int C,
-                                                     int cs, int cps, const int32_t* __restrict__ sizes,
+                                                     int cs, int cps, int metric, const int32_t* __restrict__ sizes,
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ token_ids, long long ids_stride,
                                                      float* __restrict__ cent, float* __restrict__ cent_t,
@@ -572,7 +658,7 @@ __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys
     c0 = cr[2 * lane];
     c1 = cr[2 * lane + 1];
   }
-  normalize_row(c0, c1, rows[w], chat + ((size_t)h * cps + k) * D);
+  operand_row(metric, c0, c1, rows[w], chat + ((size_t)h * cps + k) * D);
 }
 
 // ---------------------------------------------------------------------------
@@ -641,22 +727,22 @@ hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t v, hipStream_t st) {
 }
 
 hipError_t launch_init_centroids(int dtype, const void* keys, long long head_stride, int heads, int lo, int L,
-                                 const int32_t* init_idx, int C, int cpad, int cs, int cps, float* cent, float* cent_t,
-                                 void* chat, int32_t* flags, hipStream_t st) {
+                                 const int32_t* init_idx, int C, int cpad, int cs, int cps, int metric, float* cent,
+                                 float* cent_t, void* chat, int32_t* flags, hipStream_t st) {
   dim3 grid(grid1(cpad, 4), heads);
   if (dtype == DT_BF16)
     init_centroids_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, lo, L, init_idx, C, cpad,
-                                                          cs, cps, cent, cent_t, (uint16_t*)chat, flags);
+                                                          cs, cps, metric, cent, cent_t, (uint16_t*)chat, flags);
   else
     init_centroids_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, lo, L, init_idx, C, cpad, cs,
-                                                       cps, cent, cent_t, (float*)chat, flags);
+                                                       cps, metric, cent, cent_t, (float*)chat, flags);
   return hipGetLastError();
 }
 
 // The exact pass instantiated for the number of 64-centroid groups a lane owns.
 template <typename KT, int MAXT>
 hipError_t launch_exact_t(const KT* keys, long long head_stride, int L, const KT* chat, int C, int cpad, int cps,
-                          int32_t* labels, long long label_stride, const int32_t* queue, const uint32_t* qcount,
+                          int metric, int32_t* labels, long long label_stride, const int32_t* queue, const uint32_t* qcount,
                           dim3 grid, size_t lds, hipStream_t st) {
   if (lds > 64 * 1024) {
     static bool attr = false;
@@ -667,20 +753,20 @@ hipError_t launch_exact_t(const KT* keys, long long head_stride, int L, const KT
       attr = true;
     }
   }
-  assign_exact_kernel<KT, MAXT><<<grid, 256, lds, st>>>(keys, head_stride, L, chat, C, cpad, cps, labels,
+  assign_exact_kernel<KT, MAXT><<<grid, 256, lds, st>>>(keys, head_stride, L, chat, C, cpad, cps, metric, labels,
                                                        label_stride, queue, qcount);
   return hipGetLastError();
 }
 
 template <typename KT>
 hipError_t launch_exact(const KT* keys, long long head_stride, int L, const KT* chat, int C, int cpad, int cps,
-                        int32_t* labels, long long label_stride, const int32_t* queue, const uint32_t* qcount,
+                        int metric, int32_t* labels, long long label_stride, const int32_t* queue, const uint32_t* qcount,
                         dim3 grid, size_t lds, hipStream_t st) {
   switch ((C + 63) / 64) {
 #define KVC_EXACT_CASE(T) \
   case T:                 \
-    return launch_exact_t<KT, T>(keys, head_stride, L, chat, C, cpad, cps, labels, label_stride, queue, qcount, grid, \
-                                 lds, st);
+    return launch_exact_t<KT, T>(keys, head_stride, L, chat, C, cpad, cps, metric, labels, label_stride, queue,  \
+                                 qcount, grid, lds, st);
     KVC_EXACT_CASE(1)
     KVC_EXACT_CASE(2)
     KVC_EXACT_CASE(3)
@@ -695,18 +781,30 @@ hipError_t launch_exact(const KT* keys, long long head_stride, int L, const KT* 
   }
 }
 
+template <int METRIC>
+static hipError_t launch_mfma_t(dim3 grid, size_t lds, const uint16_t* keys, long long head_stride, int L,
+                                const uint16_t* chat, int C, int cpad, int cps, int32_t* labels,
+                                long long label_stride, int32_t* queue, uint32_t* qcount, float* top2,
+                                hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)assign_bf16_mfma_kernel<METRIC>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  assign_bf16_mfma_kernel<METRIC><<<grid, AS_THREADS, lds, st>>>(keys, head_stride, L, chat, C, cpad, cps, labels,
+                                                                 label_stride, queue, qcount, top2);
+  return hipGetLastError();
+}
+
 hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
-                         int cpad, int cps, int32_t* labels, long long label_stride, int32_t* queue, uint32_t* qcount,
-                         float* top2, hipEvent_t* events, hipStream_t st) {
+                         int cpad, int cps, int metric, int32_t* labels, long long label_stride, int32_t* queue,
+                         uint32_t* qcount, float* top2, hipEvent_t* events, hipStream_t st) {
+  // the exact pass keeps nn_k / 2 per centroid after the staged operand under L2
+  const size_t lds_nn = metric == M_L2 ? (size_t)cpad * 8 : 0;
   if (dtype == DT_BF16) {
     const size_t lds = (size_t)cpad * D * 2;
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)assign_bf16_mfma_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
     // about one block per compute unit; each walks over 512-key groups of one head
     const int ngroups = grid1(L, AS_TILE);
     int gx = (256 + heads - 1) / heads;
@@ -716,26 +814,36 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
       hipError_t e0 = hipEventRecord(events[0], st);
       if (e0 != hipSuccess) return e0;
     }
-    assign_bf16_mfma_kernel<<<grid, AS_THREADS, lds, st>>>((const uint16_t*)keys, head_stride, L,
-                                                             (const uint16_t*)chat, C, cpad, cps, labels,
-                                                             label_stride, queue, qcount, top2);
-    hipError_t e = hipGetLastError();
+    const uint16_t* kk = (const uint16_t*)keys;
+    const uint16_t* cc = (const uint16_t*)chat;
+    hipError_t e;
+    // variants: the fp32 biases and the largest norm follow the staged operand
+    const size_t lds_var = lds + (size_t)cpad * 4 + 16;
+    if (metric == M_L2)
+      e = launch_mfma_t<M_L2>(grid, lds_var, kk, head_stride, L, cc, C, cpad, cps, labels, label_stride, queue,
+                              qcount, top2, st);
+    else if (metric == M_IP)
+      e = launch_mfma_t<M_IP>(grid, lds_var, kk, head_stride, L, cc, C, cpad, cps, labels, label_stride, queue,
+                              qcount, top2, st);
+    else
+      e = launch_mfma_t<M_COSINE>(grid, lds, kk, head_stride, L, cc, C, cpad, cps, labels, label_stride, queue,
+                                  qcount, top2, st);
     if (e != hipSuccess) return e;
     if (events) {
       e = hipEventRecord(events[1], st);
       if (e != hipSuccess) return e;
     }
     // exact re-scoring of the uncertified keys; blocks without work exit at once
-    return launch_exact<uint16_t>((const uint16_t*)keys, head_stride, L, (const uint16_t*)chat, C, cpad, cps, labels,
-                                  label_stride, queue, qcount, dim3(4, heads), lds, st);
+    return launch_exact<uint16_t>((const uint16_t*)keys, head_stride, L, (const uint16_t*)chat, C, cpad, cps, metric,
+                                  labels, label_stride, queue, qcount, dim3(4, heads), lds + lds_nn, st);
   }
   dim3 g2(grid1(L, 8) < 64 ? grid1(L, 8) : 64, heads);
   if (events) {
     hipError_t e0 = hipEventRecord(events[0], st);
     if (e0 != hipSuccess) return e0;
   }
-  hipError_t e = launch_exact<float>((const float*)keys, head_stride, L, (const float*)chat, C, cpad, cps, labels,
-                                     label_stride, nullptr, nullptr, g2, 0, st);
+  hipError_t e = launch_exact<float>((const float*)keys, head_stride, L, (const float*)chat, C, cpad, cps, metric,
+                                     labels, label_stride, nullptr, nullptr, g2, lds_nn, st);
   if (e == hipSuccess && events) e = hipEventRecord(events[1], st);
   return e;
 }
@@ -756,15 +864,15 @@ hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, 
 }
 
 hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cs, int cps,
-                         const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
+                         int metric, const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
                          float* cent, float* cent_t, void* chat, hipStream_t st) {
   dim3 grid(grid1(C, 4), heads);
   if (dtype == DT_BF16)
-    update_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, C, cs, cps, sizes, offsets,
-                                                  token_ids, ids_stride, cent, cent_t, (uint16_t*)chat);
+    update_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, C, cs, cps, metric, sizes,
+                                                  offsets, token_ids, ids_stride, cent, cent_t, (uint16_t*)chat);
   else
-    update_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, C, cs, cps, sizes, offsets, token_ids,
-                                               ids_stride, cent, cent_t, (float*)chat);
+    update_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, C, cs, cps, metric, sizes, offsets,
+                                               token_ids, ids_stride, cent, cent_t, (float*)chat);
   return hipGetLastError();
 }
 

@@ -16,7 +16,8 @@ namespace kvc {
 // a6: append n_new tokens per head. One block per head; tokens in order.
 // label = argmax_k of the fp64 chain k_new . chat_k (ascending channel order,
 // lowest k on ties), the same rule as the build's assignment, over the C
-// clusters in use (per-head strides: cs slots, cps operand rows). The token id
+// clusters in use (per-head strides: cs slots, cps operand rows); under the
+// L2 distance the score is the chain minus half the fp64 chain of chat_kj^2. The token id
 // joins the end of its cluster's appended list (ids only grow, so lists stay
 // ascending), shifting the later clusters' entries right by one; the prefix
 // entries of every slot after the cluster advance, so unused slots keep the
@@ -25,7 +26,7 @@ template <typename KT>
 __global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __restrict__ vc, long long head_stride,
                                                      const KT* __restrict__ knew, const KT* __restrict__ vnew,
                                                      int n_new, int n0, const KT* __restrict__ chat, int C, int cs,
-                                                     int cps, int32_t* __restrict__ labels, long long cap,
+                                                     int cps, int metric, int32_t* __restrict__ labels, long long cap,
                                                      int32_t* __restrict__ sizes, int32_t* __restrict__ app_offsets,
                                                      int32_t* __restrict__ app_ids) {
   __shared__ double kv[D];
@@ -56,7 +57,8 @@ __global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __
       const int c0 = tid, c1 = tid + 256;
       const u32x4* r0 = reinterpret_cast<const u32x4*>(Ch + (size_t)(c0 < C ? c0 : 0) * D);
       const u32x4* r1 = reinterpret_cast<const u32x4*>(Ch + (size_t)(c1 < C ? c1 : 0) * D);
-      double s0 = 0.0, s1 = 0.0;
+      double s0 = 0.0, s1 = 0.0, nn0 = 0.0, nn1 = 0.0;
+      const bool l2 = metric == M_L2;
 #pragma unroll 1
       for (int half = 0; half < 2; ++half) {
         u32x4 x0[HP], x1[HP];
@@ -80,7 +82,15 @@ __global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __
             const double kj = kv[(half * HP + i) * EPP + e];
             s0 = fma(kj, (double)a, s0);
             s1 = fma(kj, (double)b, s1);
+            if (l2) {
+              nn0 = fma((double)a, (double)a, nn0);
+              nn1 = fma((double)b, (double)b, nn1);
+            }
           }
+      }
+      if (l2) {
+        s0 = s0 - 0.5 * nn0;
+        s1 = s1 - 0.5 * nn1;
       }
       if (c0 < C) {
         best = s0;
@@ -1209,17 +1219,17 @@ __global__ __launch_bounds__(256) void export_csr_kernel(int C, int cs, const in
 // Host launchers.
 
 hipError_t launch_append(int dtype, void* kc, void* vc, long long head_stride, int heads, const void* knew,
-                         const void* vnew, int n_new, int n0, const void* chat, int ca, int cs, int cps,
+                         const void* vnew, int n_new, int n0, const void* chat, int ca, int cs, int cps, int metric,
                          int32_t* labels, long long cap, int32_t* sizes, int32_t* app_offsets, int32_t* app_ids,
                          hipStream_t st) {
   if (dtype == DT_BF16)
     append_kernel<uint16_t><<<heads, 256, 0, st>>>((uint16_t*)kc, (uint16_t*)vc, head_stride, (const uint16_t*)knew,
                                                    (const uint16_t*)vnew, n_new, n0, (const uint16_t*)chat, ca, cs, cps,
-                                                   labels, cap, sizes, app_offsets, app_ids);
+                                                   metric, labels, cap, sizes, app_offsets, app_ids);
   else
     append_kernel<float><<<heads, 256, 0, st>>>((float*)kc, (float*)vc, head_stride, (const float*)knew,
-                                                (const float*)vnew, n_new, n0, (const float*)chat, ca, cs, cps, labels,
-                                                cap, sizes, app_offsets, app_ids);
+                                                (const float*)vnew, n_new, n0, (const float*)chat, ca, cs, cps, metric,
+                                                labels, cap, sizes, app_offsets, app_ids);
   return hipGetLastError();
 }
 

@@ -6,6 +6,8 @@
 namespace kvc {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
+// assignment distance: the cosine (the method's), L2, inner product
+enum { M_COSINE = 0, M_L2 = 1, M_IP = 2 };
 
 constexpr int DEC_TOK = 64;      // selected tokens per decode block (split)
 constexpr int DEC_MAX_PAIRS = 512;  // splits x query heads one merge block holds
@@ -25,17 +27,17 @@ struct IndexView {
 
 hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t v, hipStream_t st);
 hipError_t launch_init_centroids(int dtype, const void* keys, long long head_stride, int heads, int lo, int L,
-                                 const int32_t* init_idx, int C, int cpad, int cs, int cps, float* cent, float* cent_t,
-                                 void* chat, int32_t* flags, hipStream_t st);
+                                 const int32_t* init_idx, int C, int cpad, int cs, int cps, int metric, float* cent,
+                                 float* cent_t, void* chat, int32_t* flags, hipStream_t st);
 hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
-                         int cpad, int cps, int32_t* labels, long long label_stride, int32_t* queue, uint32_t* qcount,
-                         float* top2, hipEvent_t* events, hipStream_t st);
+                         int cpad, int cps, int metric, int32_t* labels, long long label_stride, int32_t* queue,
+                         uint32_t* qcount, float* top2, hipEvent_t* events, hipStream_t st);
 hipError_t launch_fill2d_i32(int32_t* p, int rows, long long stride, int cols, int value, hipStream_t st);
 hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, int L, int C, int cs, int32_t* hist,
                       int32_t* sizes, int32_t* offsets, int32_t* token_ids, long long ids_stride, int id_base,
                       hipStream_t st);
 hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cs, int cps,
-                         const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
+                         int metric, const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
                          float* cent, float* cent_t, void* chat, hipStream_t st);
 // Moves the window's clustering (nc clusters of the m tokens wlo .. wlo+m-1,
 // in arrays of stride nc / cpad(nc) / m per head) into the index as clusters
@@ -47,7 +49,7 @@ hipError_t launch_merge_window(int dtype, int heads, int nc, int m, int wlo, con
                                hipStream_t st);
 
 hipError_t launch_append(int dtype, void* kc, void* vc, long long head_stride, int heads, const void* knew,
-                         const void* vnew, int n_new, int n0, const void* chat, int ca, int cs, int cps,
+                         const void* vnew, int n_new, int n0, const void* chat, int ca, int cs, int cps, int metric,
                          int32_t* labels, long long cap, int32_t* sizes, int32_t* app_offsets, int32_t* app_ids,
                          hipStream_t st);
 hipError_t launch_window_append(int dtype, void* kc, void* vc, long long cap, int heads, const void* knew,

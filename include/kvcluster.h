@@ -50,6 +50,15 @@ extern "C" {
 
 typedef enum kvc_dtype { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
 
+/* Assignment distance (III.B measures semantic distance by the cosine and
+ * names L2 and inner-product distance as the alternatives it is preferred to;
+ * the model-accuracy section compares the three). */
+typedef enum kvc_metric {
+  KVC_COSINE = 0,        /* argmax_k K . c_k / ||c_k|| (the method's) */
+  KVC_L2 = 1,            /* argmin_k ||K - c_k||^2 = argmax_k (K . c_k - ||c_k||^2 / 2) */
+  KVC_INNER_PRODUCT = 2  /* argmax_k K . c_k */
+} kvc_metric;
+
 typedef enum kvc_status {
   KVC_OK = 0,
   KVC_ERR_INVALID_ARG = 1, /* a null pointer, a size out of range, ... */
@@ -117,6 +126,10 @@ typedef struct kvc_index {
   int32_t window_start;   /* host mirror: first token of the window; tokens window_start ..
                              n_tokens-1 are in no cluster yet (label -1) and every selection
                              recalls them (n_build after a build) */
+  int32_t metric;         /* kvc_metric of every assignment (build, window clustering, append);
+                             KVC_COSINE (0) is the method's. Under L2 and inner product the
+                             operand centroids_op holds the centroids themselves, rounded once
+                             to dtype, instead of their unit directions. */
 } kvc_index;
 
 /* Rows of centroids_op per head: C rounded up to the matrix-core tile (32). */
@@ -139,7 +152,11 @@ size_t kv_cluster_build_workspace_bytes(int heads, int L, int C, int iters);
  *   - each iteration normalises the centroids (rounded once to idx->dtype),
  *     assigns every key to the centroid of largest cosine similarity (lowest
  *     id on an exact tie) and replaces each centroid by the mean of its keys
- *     (an empty cluster keeps its centroid).
+ *     (an empty cluster keeps its centroid). Under idx->metric KVC_L2 or
+ *     KVC_INNER_PRODUCT the operand is the centroid itself (rounded once) and
+ *     a key joins the centroid of least L2 distance (largest K . c - ||c||^2
+ *     / 2, both fp64 chains over ascending channels, then their fp64
+ *     difference) or of largest inner product.
  * On return (after synchronisation) the index holds the means of the final
  * assignment, their normalised operand, labels, sizes, offsets and
  * token_ids; the appended part is empty. idx->n_build, idx->n_tokens and

@@ -21,6 +21,7 @@ _SRC = os.path.join(_HERE, "kvc_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16, F64 = 0, 1, 2
+COSINE, L2, IP = 0, 1, 2  # assignment distance (III.B: cosine; L2 and inner product are the alternatives)
 
 _lib = None
 
@@ -46,14 +47,15 @@ def _load():
         lib.orc_round_bf16.argtypes = [d]
         lib.orc_round_bf16.restype = C.c_uint16
         lib.orc_normalize.argtypes = [i, i, p, i, p, i]
-        lib.orc_assign.argtypes = [i, i, i, p, i, ll, p, i, p, p]
+        lib.orc_operand.argtypes = [i, i, p, i, p, i, i]
+        lib.orc_assign.argtypes = [i, i, i, p, i, ll, p, i, i, p, p]
         lib.orc_update.argtypes = [i, i, i, p, i, ll, p, p, i, p]
         lib.orc_csr.argtypes = [i, i, p, p, p, p]
-        lib.orc_inertia.argtypes = [i, i, p, i, ll, p, i, p]
+        lib.orc_inertia.argtypes = [i, i, p, i, ll, p, i, i, p]
         lib.orc_inertia.restype = d
-        lib.orc_build.argtypes = [i, i, i, i, i, i, i, p, ll, p, p, p, p, p, p, p, p, p, i]
+        lib.orc_build.argtypes = [i, i, i, i, i, i, i, i, p, ll, p, p, p, p, p, p, p, p, p, i]
         lib.orc_build.restype = i
-        lib.orc_append.argtypes = [i, i, i, p, i, p, i, p, p, p, p]
+        lib.orc_append.argtypes = [i, i, i, p, i, p, i, i, p, p, p, p]
         lib.orc_append.restype = i
         lib.orc_select.argtypes = [i, i, i, i, i, p, i, p, p, p, p, ll, p, p, p, p]
         lib.orc_decode.argtypes = [i, i, i, p, i, p, p, i, ll, p, p, i, d, p]
@@ -113,14 +115,26 @@ def normalize(c: np.ndarray, optype: int) -> np.ndarray:
     return out
 
 
-def assign(K: np.ndarray, chat: np.ndarray):
+def operand(c: np.ndarray, optype: int, metric: int = COSINE) -> np.ndarray:
+    """c [C, d] -> the assignment operand in ``optype``: the unit direction
+    (cosine) or the centroid itself (L2, inner product), rounded once."""
+    lib = _load()
+    c = _c(c)
+    Cn, d = c.shape
+    out = np.empty((Cn, d), dtype=_np_of(optype))
+    lib.orc_operand(Cn, d, _ptr(c), _dt(c), _ptr(out), optype, metric)
+    return out
+
+
+def assign(K: np.ndarray, chat: np.ndarray, metric: int = COSINE):
     """K [L, d], chat [C, d] -> (labels int32 [L], best score fp64 [L])."""
     lib = _load()
     K, chat = _c(K), _c(chat)
     L, d = K.shape
     labels = np.empty(L, dtype=np.int32)
     best = np.empty(L, dtype=np.float64)
-    lib.orc_assign(L, d, chat.shape[0], _ptr(K), _dt(K), d, _ptr(chat), _dt(chat), _ptr(labels), _ptr(best))
+    lib.orc_assign(L, d, chat.shape[0], _ptr(K), _dt(K), d, _ptr(chat), _dt(chat), metric, _ptr(labels),
+                   _ptr(best))
     return labels, best
 
 
@@ -147,19 +161,20 @@ def csr(labels: np.ndarray, C: int):
     return sizes, offsets, ids
 
 
-def inertia(K: np.ndarray, chat: np.ndarray, labels: np.ndarray) -> float:
+def inertia(K: np.ndarray, chat: np.ndarray, labels: np.ndarray, metric: int = COSINE) -> float:
     lib = _load()
     K, chat = _c(K), _c(chat)
     labels = _c(labels, np.int32)
     L, d = K.shape
-    return lib.orc_inertia(L, d, _ptr(K), _dt(K), d, _ptr(chat), _dt(chat), _ptr(labels))
+    return lib.orc_inertia(L, d, _ptr(K), _dt(K), d, _ptr(chat), _dt(chat), metric, _ptr(labels))
 
 
 def build(K: np.ndarray, C: int, iters: int, init_idx: np.ndarray, L: int | None = None,
-          mode: int = 0, early_exit: bool = True, n_sink: int = 0) -> dict:
+          mode: int = 0, early_exit: bool = True, n_sink: int = 0, metric: int = COSINE) -> dict:
     """Prefill clustering of every head of K [H, rows, d] over its first L rows.
 
     mode 0: centroids fp32, operand in the key type; mode 1: exact (fp64).
+    metric: assignment distance, COSINE (the method's), L2 or IP.
     n_sink: the first n_sink rows are attention sinks (III.B keeps the first
     tokens apart and clusters the rest): they get label -1, stay out of every
     cluster, and init_idx holds positions >= n_sink. token_ids hold the
@@ -171,7 +186,7 @@ def build(K: np.ndarray, C: int, iters: int, init_idx: np.ndarray, L: int | None
         H, rows, _ = K.shape
         L = rows if L is None else L
         r = build(np.ascontiguousarray(K[:, n_sink:L]), C, iters, np.asarray(init_idx, np.int32) - n_sink,
-                  mode=mode, early_exit=early_exit)
+                  mode=mode, early_exit=early_exit, metric=metric)
         labels = np.full((H, L), -1, dtype=np.int32)
         labels[:, n_sink:] = r["labels"]
         r["labels"] = labels
@@ -193,7 +208,7 @@ def build(K: np.ndarray, C: int, iters: int, init_idx: np.ndarray, L: int | None
     ids = np.empty((H, L), dtype=np.int32)
     inert = np.empty((H, iters), dtype=np.float64)
     iters_run = np.empty(H, dtype=np.int32)
-    rc = lib.orc_build(H, L, d, C, iters, kdt, mode, _ptr(K), rows * d, _ptr(init_idx), _ptr(c), _ptr(chat),
+    rc = lib.orc_build(H, L, d, C, iters, kdt, mode, metric, _ptr(K), rows * d, _ptr(init_idx), _ptr(c), _ptr(chat),
                        _ptr(labels), _ptr(sizes), _ptr(offsets), _ptr(ids), _ptr(inert), _ptr(iters_run),
                        1 if early_exit else 0)
     if rc != 0:
@@ -207,8 +222,9 @@ class Index:
     (nearest centroid) or by add_window() + cluster_window() (generated tokens
     clustered on their own, III.B)."""
 
-    def __init__(self, built: dict, capacity: int):
+    def __init__(self, built: dict, capacity: int, metric: int = COSINE):
         H, L = built["labels"].shape
+        self.metric = metric
         self.H, self.C = built["sizes"].shape
         self.n = L  # tokens, sinks included; the next one gets position n
         self.window_start = L  # tokens window_start .. n-1 are in no cluster yet
@@ -237,7 +253,7 @@ class Index:
             sz = self.sizes[h]
             off = self.offsets[h]
             ids = self.token_ids[h]
-            out[h] = lib.orc_append(d, self.C, self.n, _ptr(kh), _dt(kh), _ptr(ch), _dt(ch), _ptr(lab),
+            out[h] = lib.orc_append(d, self.C, self.n, _ptr(kh), _dt(kh), _ptr(ch), _dt(ch), self.metric, _ptr(lab),
                                     _ptr(sz), _ptr(off), _ptr(ids))
         self.n += 1
         self.window_start = self.n
@@ -257,7 +273,7 @@ class Index:
         in the canonical index. Returns the window's own build result."""
         lo, hi = self.window_start, self.n
         r = build(np.ascontiguousarray(K[:, lo:hi]), n_clusters, iters,
-                  np.asarray(init_idx, np.int32) - np.int32(lo))
+                  np.asarray(init_idx, np.int32) - np.int32(lo), metric=self.metric)
         C0, m = self.C, hi - lo
         total = self.offsets[:, C0]
         self.labels[:, lo:hi] = C0 + r["labels"]

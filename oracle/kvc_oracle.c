@@ -37,6 +37,13 @@
 #define ORC_BF16 1
 #define ORC_F64 2
 
+/* Assignment distance. III.B defines the semantic distance by the cosine and
+ * names L2 and inner-product distance as the alternatives it is preferred to;
+ * the model-accuracy section compares the three. */
+#define ORC_COSINE 0
+#define ORC_L2 1
+#define ORC_IP 2
+
 /* ---------------------------------------------------------------- scalars */
 
 static double bf16_bits_to_f64(uint16_t b) {
@@ -112,20 +119,42 @@ void orc_normalize(int C, int d, const void* c, int cdt, void* chat, int optype)
 }
 
 /*
- * Assignment (III.B: each key joins the centroid of largest cosine
- * similarity). ||K_i|| is a positive per-key constant, so the cosine argmax is
- * argmax_k K_i . chat_k. Exact ties go to the lowest k.
+ * The assignment operand of C centroids, rounded once to optype.
+ *  - cosine: the unit direction (orc_normalize);
+ *  - L2 and inner product: the centroid itself, chat_kj = round_op(c_kj).
+ */
+void orc_operand(int C, int d, const void* c, int cdt, void* chat, int optype, int metric) {
+  if (metric == ORC_COSINE) {
+    orc_normalize(C, d, c, cdt, chat, optype);
+    return;
+  }
+  for (size_t e = 0; e < (size_t)C * d; ++e) st(chat, optype, e, ld(c, cdt, e));
+}
+
+/*
+ * Assignment (III.B: each key joins its nearest centroid under the semantic
+ * distance). Exact ties go to the lowest k.
+ *  - cosine: ||K_i|| is a positive per-key constant, so the cosine argmax is
+ *    argmax_k K_i . chat_k (chat the unit direction);
+ *  - inner product: argmax_k K_i . chat_k (chat the centroid);
+ *  - L2: argmin_k ||K_i - chat_k||^2 = argmax_k (K_i . chat_k - nn_k / 2),
+ *    since ||K_i||^2 is a per-key constant; nn_k = fp64 chain of chat_kj^2
+ *    over ascending j, and the score is the fp64 difference.
  *
  * The loop nest computes the chains of all k for one key together: each
  * s[k] is still the chain over ascending j, so the scores are the chain's.
  * best (optional) receives the winning score.
  */
 void orc_assign(int L, int d, int C, const void* K, int kdt, long long row_stride, const void* chat,
-                int optype, int32_t* labels, double* best) {
+                int optype, int metric, int32_t* labels, double* best) {
   double* cT = (double*)malloc(sizeof(double) * (size_t)d * C);
   double* s = (double*)malloc(sizeof(double) * (size_t)C);
+  double* half_nn = (double*)calloc((size_t)C, sizeof(double));
   for (int k = 0; k < C; ++k)
     for (int j = 0; j < d; ++j) cT[(size_t)j * C + k] = ld(chat, optype, (size_t)k * d + j);
+  if (metric == ORC_L2)
+    for (int k = 0; k < C; ++k)
+      half_nn[k] = 0.5 * chain_dot(d, chat, optype, (size_t)k * d, chat, optype, (size_t)k * d);
   for (int i = 0; i < L; ++i) {
     size_t ro = (size_t)i * (size_t)row_stride;
     for (int k = 0; k < C; ++k) s[k] = 0.0;
@@ -134,6 +163,8 @@ void orc_assign(int L, int d, int C, const void* K, int kdt, long long row_strid
       const double* cj = cT + (size_t)j * C;
       for (int k = 0; k < C; ++k) s[k] = fma(kij, cj[k], s[k]);
     }
+    if (metric == ORC_L2)
+      for (int k = 0; k < C; ++k) s[k] = s[k] - half_nn[k];
     int arg = 0;
     for (int k = 1; k < C; ++k)
       if (s[k] > s[arg]) arg = k;
@@ -142,6 +173,7 @@ void orc_assign(int L, int d, int C, const void* K, int kdt, long long row_strid
   }
   free(cT);
   free(s);
+  free(half_nn);
 }
 
 /*
@@ -186,16 +218,30 @@ void orc_csr(int L, int C, const int32_t* labels, int32_t* sizes, int32_t* offse
 }
 
 /*
- * Norm-weighted cosine distance of an assignment:
- * I = sum_i (||K_i|| - K_i . chat_{label_i}) = sum_i ||K_i|| (1 - cos).
+ * The k-means objective of an assignment under each distance:
+ *  - cosine: the norm-weighted cosine distance
+ *    I = sum_i (||K_i|| - K_i . chat_{label_i}) = sum_i ||K_i|| (1 - cos);
+ *  - L2: I = sum_i ||K_i - chat_{label_i}||^2;
+ *  - inner product: I = -sum_i K_i . chat_{label_i}.
  */
 double orc_inertia(int L, int d, const void* K, int kdt, long long row_stride, const void* chat,
-                   int optype, const int32_t* labels) {
+                   int optype, int metric, const int32_t* labels) {
   double I = 0.0;
   for (int i = 0; i < L; ++i) {
-    size_t ro = (size_t)i * (size_t)row_stride;
-    double nk = sqrt(chain_dot(d, K, kdt, ro, K, kdt, ro));
-    I += nk - chain_dot(d, K, kdt, ro, chat, optype, (size_t)labels[i] * d);
+    size_t ro = (size_t)i * (size_t)row_stride, co = (size_t)labels[i] * d;
+    if (metric == ORC_L2) {
+      double e = 0.0;
+      for (int j = 0; j < d; ++j) {
+        double t = ld(K, kdt, ro + j) - ld(chat, optype, co + j);
+        e = fma(t, t, e);
+      }
+      I += e;
+    } else if (metric == ORC_IP) {
+      I -= chain_dot(d, K, kdt, ro, chat, optype, co);
+    } else {
+      double nk = sqrt(chain_dot(d, K, kdt, ro, K, kdt, ro));
+      I += nk - chain_dot(d, K, kdt, ro, chat, optype, co);
+    }
   }
   return I;
 }
@@ -210,7 +256,8 @@ static size_t esize(int dt) { return dt == ORC_BF16 ? 2 : (dt == ORC_F32 ? 4 : 8
  * (the seeded shuffle is an input; the oracle copies those keys exactly).
  * mode: 0 = operand type of the input (fp32 centroids, chat in the key type),
  *       1 = exact (fp64 centroids, fp64 chat).
- * Per iteration t: chat = normalise(c); labels = assign(chat); c = update.
+ * metric: the assignment distance (cosine, the method's; L2 or inner product).
+ * Per iteration t: chat = operand(c); labels = assign(chat); c = update.
  * With early_exit, stops when labels repeat (every later iteration would
  * reproduce the same state). The outputs are the final centroids (means of
  * the final labels), chat_final = normalise(final c), labels and the
@@ -218,7 +265,7 @@ static size_t esize(int dt) { return dt == ORC_BF16 ? 2 : (dt == ORC_F32 ? 4 : 8
  * (NaN after an early exit); iters_run [H] the count.
  * Returns 0, or -1 if an init index is out of range.
  */
-int orc_build(int H, int L, int d, int C, int iters, int kdt, int mode, const void* K,
+int orc_build(int H, int L, int d, int C, int iters, int kdt, int mode, int metric, const void* K,
               long long head_stride, const int32_t* init_idx, void* c_out, void* chat_out,
               int32_t* labels, int32_t* sizes, int32_t* offsets, int32_t* token_ids, double* inertia,
               int32_t* iters_run, int early_exit) {
@@ -240,9 +287,9 @@ int orc_build(int H, int L, int d, int C, int iters, int kdt, int mode, const vo
         st(ch, cdt, (size_t)k * d + j, ld(Kh, kdt, (size_t)init_idx[(size_t)h * C + k] * d + j));
     int t = 0;
     for (; t < iters; ++t) {
-      orc_normalize(C, d, ch, cdt, chh, optype);
-      orc_assign(L, d, C, Kh, kdt, d, chh, optype, lab, NULL);
-      if (inertia) inertia[(size_t)h * iters + t] = orc_inertia(L, d, Kh, kdt, d, chh, optype, lab);
+      orc_operand(C, d, ch, cdt, chh, optype, metric);
+      orc_assign(L, d, C, Kh, kdt, d, chh, optype, metric, lab, NULL);
+      if (inertia) inertia[(size_t)h * iters + t] = orc_inertia(L, d, Kh, kdt, d, chh, optype, metric, lab);
       orc_update(L, d, C, Kh, kdt, d, lab, ch, cdt, NULL);
       if (early_exit && t > 0 && memcmp(prev, lab, sizeof(int32_t) * (size_t)L) == 0) { ++t; break; }
       memcpy(prev, lab, sizeof(int32_t) * (size_t)L);
@@ -250,7 +297,7 @@ int orc_build(int H, int L, int d, int C, int iters, int kdt, int mode, const vo
     if (inertia)
       for (int u = t; u < iters; ++u) inertia[(size_t)h * iters + u] = NAN;
     if (iters_run) iters_run[h] = t;
-    orc_normalize(C, d, ch, cdt, chh, optype);
+    orc_operand(C, d, ch, cdt, chh, optype, metric);
     orc_csr(L, C, lab, sizes + (size_t)h * C, offsets + (size_t)h * (C + 1), token_ids + (size_t)h * L);
     free(prev);
   }
@@ -265,10 +312,10 @@ int orc_build(int H, int L, int d, int C, int iters, int kdt, int mode, const vo
  * (sizes [C], offsets [C+1], token_ids [n_cur + 1]) are updated in place.
  * Returns the label.
  */
-int orc_append(int d, int C, int n_cur, const void* knew, int kdt, const void* chat, int optype,
+int orc_append(int d, int C, int n_cur, const void* knew, int kdt, const void* chat, int optype, int metric,
                int32_t* labels, int32_t* sizes, int32_t* offsets, int32_t* token_ids) {
   int32_t lab;
-  orc_assign(1, d, C, knew, kdt, d, chat, optype, &lab, NULL);
+  orc_assign(1, d, C, knew, kdt, d, chat, optype, metric, &lab, NULL);
   int pos = offsets[lab + 1];
   for (int p = n_cur; p > pos; --p) token_ids[p] = token_ids[p - 1];
   token_ids[pos] = n_cur;

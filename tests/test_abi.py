@@ -170,6 +170,11 @@ def test_window_calls_reject(kvc):
     many = make_index(kvc, Cn=16)
     many.c_slots = 600
     assert L.kv_cluster_build(C.byref(many), p, 200, 3, p, p, 1 << 40, None) == UNSUPPORTED
+    # the assignment distance is one of cosine, L2, inner product
+    for bad in (-1, 3):
+        odd = make_index(kvc, Cn=16)
+        odd.metric = bad
+        assert L.kv_cluster_build(C.byref(odd), p, 200, 3, p, p, 1 << 40, None) == INVALID
 
 
 def test_binding_fails_loudly_without_library(kvc, monkeypatch):

@@ -412,6 +412,75 @@ def test_window_clustering_end_to_end():
     assert windows == 3
 
 
+@pytest.mark.parametrize("metric", ["l2", "inner_product"])
+@pytest.mark.parametrize("case", ["small_bf16_append", "cfg1_fp32"])
+def test_distance_variants_end_to_end(case, metric):
+    """III.B's alternatives to the cosine (L2 and inner-product distance): one
+    assignment against a given operand (labels bit-exact; matrix-core scores
+    within the certificate's bound), the whole build (labels, centroids,
+    operand, index bit-exact), nearest-centroid appends under the same
+    distance, and the selection and attention on the result."""
+    w = SMALL_APPEND if case == "small_bf16_append" else synth.workload(1)
+    m, om = {"l2": (kvc.L2, oracle.L2), "inner_product": (kvc.INNER_PRODUCT, oracle.IP)}[metric]
+    say(f"[distance variant] {case} {metric}")
+    base, K, V, init, means = make_inputs(w)
+    H = K.shape[0]
+    bf = w.dtype == synth.BF16
+    opt = oracle.BF16 if bf else oracle.F32
+    # one assignment against the operand of the initial centroids
+    c0 = np.stack([oracle.to_f64(K[h, init[h]]).astype(np.float32) for h in range(H)])
+    chat = np.stack([oracle.operand(c0[h], opt, om) for h in range(H)])
+    want = np.stack([oracle.assign(K[h, :w.L], chat[h], om)[0] for h in range(H)])
+    idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w), metric=m)
+    labels, top2, flagged = kvc.debug_assign(idx, to_dev(K), w.L, to_dev(pad_op(chat, kvc.cpad(w.C))), want_top2=bf)
+    got = to_np(labels)[:, :w.L]
+    say(f"  assign: flagged per head {to_np(flagged).tolist()}, mismatches {(got != want).sum()}")
+    assert np.array_equal(got, want)
+    if bf:
+        best = np.stack([oracle.assign(K[h, :w.L], chat[h], om)[1] for h in range(H)])
+        kn = np.linalg.norm(oracle.to_f64(K[:, :w.L]), axis=2)
+        A = np.linalg.norm(oracle.to_f64(chat), axis=2).max(axis=1)[:, None]
+        bmax = 0.5 * A * A if om == oracle.L2 else 0.0 * A
+        bound = 4 * 2.0 ** -24 * ((w.d + 17) * kn * A + 2 * bmax) * 1.004
+        err = np.abs(to_np(top2)[..., 0] - best)
+        say(f"  max |fp32 best - fp64 best| / bound = {(err / bound).max():.3e}")
+        assert np.all(err <= bound)
+    # the whole build
+    Kc, Vc = K.copy(), V.copy()
+    Kc[:, w.L:], Vc[:, w.L:] = 0, 0
+    Kd, Vd = to_dev(Kc), to_dev(Vc)
+    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    torch.cuda.synchronize()
+    assert int(to_np(idx.dev_flags)[0]) == 0
+    ref = oracle.build(np.ascontiguousarray(K[:, :w.L]), w.C, w.iters, init, metric=om)
+    gl = to_np(idx.labels)[:, :w.L]
+    say(f"  build: label agreement {(gl == ref['labels']).mean():.6f}")
+    assert np.array_equal(gl, ref["labels"])
+    assert np.array_equal(to_np(idx.centroids), ref["c"])
+    assert np.array_equal(to_np(idx.centroids_op)[:, :w.C], ref["chat"])
+    assert np.array_equal(to_np(idx.sizes), ref["sizes"]) and np.array_equal(to_np(idx.offsets), ref["offsets"])
+    assert np.array_equal(to_np(idx.token_ids)[:, :w.L], ref["token_ids"])
+    oi = oracle.Index(ref, w.capacity, metric=om)
+    n = w.L
+    scale = 1.0 / math.sqrt(w.d)
+    for step in range(3):
+        if w.append and step > 0:
+            kvc.append(idx, Kd, Vd, to_dev(np.ascontiguousarray(K[:, n:n + 1])),
+                       to_dev(np.ascontiguousarray(V[:, n:n + 1])))
+            oi.append(np.ascontiguousarray(K[:, n]))
+            n += 1
+            torch.cuda.synchronize()
+            assert np.array_equal(to_np(idx.labels)[:, :n], oi.labels[:, :n])
+        q = queries(w, base, step, K, n, means)
+        osel, ocnt, _, _ = oracle.select(q, w.G, oi.c, oi.sizes, oi.offsets, oi.token_ids, w.B)
+        od = oracle.decode(q, w.G, K, V, osel, ocnt, scale)
+        fsel = torch.full((H, w.B), -7, dtype=torch.int32, device="cuda")
+        fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, w.B, scale, sel_ids=fsel)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(fsel), osel), step
+        assert np.abs(to_np(fout) - od).max() <= 2e-3, step
+
+
 def test_init_index_out_of_range_flag():
     w = SMALL
     base, K, V, init, _ = make_inputs(w)

@@ -588,3 +588,72 @@ def test_window_clustering_two_groups_closed_form(orc):
     assert np.array_equal(idx.c[0, 3], np.array([0, 0.25 / 3, 10 / 3, 0.5 / 3], np.float32))
     assert idx.sizes[0].tolist()[2:] == [3, 3] and idx.offsets[0].tolist()[2:] == [4, 7, 10]
     assert idx.token_ids[0, 4:10].tolist() == [4, 6, 8, 5, 7, 9]
+
+
+# ------------------------------------------------------------ distance variants
+
+def test_distance_variants_hand_cases(orc):
+    """III.B prefers the cosine to L2 and inner-product distance. Two small
+    cases worked by hand, where the three distances disagree:
+    (a) keys [1,0], [10,0], [0,1], [0,10], centroids started at the first two:
+        L2 keeps [10,0] alone, since the three others are closer to [1/3, 11/3],
+        while cosine and inner product split by direction;
+    (b) key [1, 0.5] against centroids [1,0] and [0,5]: cosine and L2 pick the
+        first, the inner product the longer second."""
+    K = np.array([[[1, 0], [10, 0], [0, 1], [0, 10]]], np.float32)
+    init = np.array([[0, 1]], np.int32)
+    got = {m: orc.build(K, 2, 6, init, metric=m)["labels"][0].tolist() for m in (orc.COSINE, orc.L2, orc.IP)}
+    assert got[orc.L2] == [0, 1, 0, 0]
+    assert got[orc.COSINE] == [1, 1, 0, 0] and got[orc.IP] == [1, 1, 0, 0]
+    r = orc.build(K, 2, 6, init, metric=orc.L2)
+    assert np.array_equal(r["c"][0], np.array([[1 / 3, 11 / 3], [10, 0]], np.float32))
+    assert np.array_equal(r["chat"][0], r["c"][0])  # L2 operand: the centroid itself (fp32 keys)
+    c = np.array([[1, 0], [0, 5]], np.float32)
+    k = np.array([[1, 0.5]], np.float32)
+    assert orc.assign(k, orc.operand(c, orc.F32, orc.COSINE), orc.COSINE)[0].tolist() == [0]
+    assert orc.assign(k, orc.operand(c, orc.F32, orc.L2), orc.L2)[0].tolist() == [0]
+    assert orc.assign(k, orc.operand(c, orc.F32, orc.IP), orc.IP)[0].tolist() == [1]
+    # the L2 score is K.c - ||c||^2 / 2: 1 - 0.5 and 2.5 - 12.5
+    assert orc.assign(k, c, orc.L2)[1].tolist() == [0.5]
+
+
+def test_distance_variants_brute_force(orc):
+    """L2: argmin of the squared distance; inner product: argmax of the dot
+    product; lowest index on ties. Small integer data keep every fp64 sum exact,
+    so numpy's brute force decides the same way."""
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        d, C, L = int(rng.integers(1, 9)), int(rng.integers(1, 12)), 60
+        K = rng.integers(-4, 5, (L, d)).astype(np.float32)
+        c = rng.integers(-4, 5, (C, d)).astype(np.float32)
+        lab, best = orc.assign(K, c, orc.L2)
+        dist = ((K[:, None, :].astype(np.float64) - c[None].astype(np.float64)) ** 2).sum(-1)
+        assert np.array_equal(lab, np.argmin(dist, axis=1)), trial
+        kn = (K.astype(np.float64) ** 2).sum(1)
+        assert np.allclose(best, (kn - dist.min(1)) / 2, rtol=0, atol=0), trial  # K.c - |c|^2/2 = (|K|^2 - dist)/2
+        lab, best = orc.assign(K, c, orc.IP)
+        dots = K.astype(np.float64) @ c.T.astype(np.float64)
+        assert np.array_equal(lab, np.argmax(dots, axis=1)) and np.array_equal(best, dots.max(1)), trial
+    # the operand of L2 and inner product is the centroid rounded once (bf16 here), no normalisation
+    cf = rng.standard_normal((9, 16)).astype(np.float32)
+    want = torch.from_numpy(cf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for m in (orc.L2, orc.IP):
+        assert np.array_equal(orc.operand(cf, orc.BF16, m), want)
+    assert np.array_equal(orc.operand(cf, orc.BF16, orc.COSINE), orc.normalize(cf, orc.BF16))
+
+
+def test_l2_kmeans_objective_non_increasing_exact_mode(orc, syn):
+    """Lloyd's k-means under L2: assigning to the nearest centroid and moving
+    each centroid to its members' mean never raise sum ||K_i - c_label||^2
+    (exact mode: fp64 centroids and operand)."""
+    base = syn.config_seed(99)
+    K, _, _ = syn.mixture_keys(base, 2, 700, 16, 10, 0.3, 2, 10.0, syn.F32)
+    init = syn.init_idx(base, 2, 700, 12)
+    r = orc.build(K, 12, 15, init, mode=1, early_exit=False, metric=orc.L2)
+    for h in range(2):
+        I = r["inertia"][h]
+        assert np.all(np.diff(I) <= 1e-12 * I[:-1]), I
+        # the recorded objective is the plain sum of squared distances
+        lab = orc.assign(K[h], r["chat"][h], orc.L2)[0]
+        direct = sum(float(((orc.to_f64(K[h, i]) - r["c"][h, lab[i]]) ** 2).sum()) for i in range(700))
+        assert math.isclose(orc.inertia(K[h], r["chat"][h], lab, orc.L2), direct, rel_tol=1e-12)
