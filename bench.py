@@ -114,6 +114,11 @@ def main():
                          "split: kv_cluster_select then kv_sparse_decode")
     ap.add_argument("--sinks", type=int, default=0,
                     help="attention sinks per head: kept out of the clustering, always selected (default 0)")
+    ap.add_argument("--metric", choices=["cosine", "l2", "inner_product"], default="cosine",
+                    help="assignment distance of the k-means (default cosine, the method's; L2 and inner product "
+                         "are the alternatives the pages compare it with)")
+    ap.add_argument("--recall-heads", type=int, default=16, help="KV heads in the recall sample")
+    ap.add_argument("--recall-steps", type=int, default=4, help="decode steps in the recall sample")
     ap.add_argument("--window", type=int, default=0,
                     help="append workloads: generated tokens join a window that is always recalled, and every "
                          "WINDOW steps the window is clustered on its own into --window-clusters new clusters "
@@ -148,6 +153,7 @@ def main():
     packed = not args.no_pack and args.decode_path == "fused"
     fused = args.decode_path == "fused"
     M, NC = args.window, args.window_clusters
+    metric = {"cosine": kvc.COSINE, "l2": kvc.L2, "inner_product": kvc.INNER_PRODUCT}[args.metric]
     if M and not w.append:
         print("--window needs a workload that generates tokens (an append workload)", file=sys.stderr)
         sys.exit(2)
@@ -185,7 +191,8 @@ def main():
             K[:, L:] = 0
             V[:, L:] = 0
         e["Kd"], e["Vd"] = to_dev(K), to_dev(V)
-        e["idx"] = kvc.ClusterIndex(H, C, cap, tdt, device=dev, packed=packed, n_sink=args.sinks, c_slots=slots)
+        e["idx"] = kvc.ClusterIndex(H, C, cap, tdt, device=dev, packed=packed, n_sink=args.sinks, c_slots=slots,
+                                    metric=metric)
         # initial centroids of each window's clustering: seeded positions in the window
         e["winit"] = [to_dev(synth.init_idx(synth.stream_seed(base, 7, k), H, M, NC) + np.int32(L + k * M))
                       for k in range(n_windows)]
@@ -358,7 +365,7 @@ def main():
                    "L": L, "d": d, "C": C,
                    "kmeans_iters": w.iters, "B": B, "decode_steps_per_step": w.steps, "append": w.append,
                    "decode_path": args.decode_path, "packed_kv": packed,
-                   "sinks": args.sinks, "window": M, "window_clusters": NC if M else 0},
+                   "sinks": args.sinks, "window": M, "window_clusters": NC if M else 0, "metric": args.metric},
         "kmeans_tflops": kmeans_tflops,
         "kmeans_ms": mean(build_ms),
         "pack_ms": mean(pack_ms),
@@ -402,11 +409,17 @@ def main():
     # ---------------- CPU oracle baseline (bounded sample) -----------------
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, args, base0, init0, Q0)
-        # selection quality of the GPU's selection at decode step 0, layer 0
-        # (oracle recall of the exact top-B attention tokens, sampled heads)
-        kvc.select(lay[0]["idx"], lay[0]["Qd"][0], B, sel, cnt)
-        torch.cuda.synchronize()
-        result["selection_recall"] = recall_sample(w, args, base0, Q0, sel.cpu().numpy(), cnt.cpu().numpy())
+        # selection quality: oracle recall of the exact top-B attention tokens
+        # by the GPU's selections of the first decode steps, layer 0, sampled
+        # heads, on a fresh build of the prompt (no generated tokens)
+        e0 = lay[0]
+        kvc.build(e0["idx"], e0["Kd"], L, w.iters, e0["init_d"], workspace=ws_build)
+        sels = []
+        for s_ in range(min(args.recall_steps, w.steps)):
+            kvc.select(e0["idx"], e0["Qd"][s_], B, sel, cnt)
+            torch.cuda.synchronize()
+            sels.append((s_, sel.cpu().numpy(), cnt.cpu().numpy()))
+        result["selection_recall"] = recall_sample(w, args, base0, Q0, sels)
     print(json.dumps(result), flush=True)
 
 
@@ -425,8 +438,9 @@ def cpu_baseline(w, args, base, init, Q):
     K, _, _ = synth.mixture_keys(base, nh, w.L, w.d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype)
     V = synth.values(base, nh, w.L, w.d, w.dtype)
     t0 = time.perf_counter()
+    metric = {"cosine": oracle.COSINE, "l2": oracle.L2, "inner_product": oracle.IP}[args.metric]
     built = oracle.build(K, w.C, 1, init[:nh], early_exit=False,  # one k-means iteration of the sample
-                         n_sink=args.sinks)
+                         n_sink=args.sinks, metric=metric)
     t_iter = time.perf_counter() - t0
     scale = 1.0 / math.sqrt(w.d)
     t0 = time.perf_counter()
@@ -444,20 +458,24 @@ def cpu_baseline(w, args, base, init, Q):
             "kmeans_gflops": flops_iter / t_iter / 1e9}
 
 
-def recall_sample(w, args, base, Q, sel, cnt):
+def recall_sample(w, args, base, Q, sels):
     """Recall of the exact top-B attention tokens (oracle, fp64) by the GPU's
-    selection, for the first KV heads of layer 0 at decode step 0."""
+    selections (a list of (decode step, sel_ids, sel_count)), for the first
+    KV heads of layer 0."""
     import numpy as np
 
     import oracle
     import synth
 
-    nh = min(8, w.heads)
+    nh = min(args.recall_heads, w.heads)
     K, _, _ = synth.mixture_keys(base, nh, w.L, w.d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype)
-    r = oracle.recall(np.ascontiguousarray(Q[0, :nh * w.G]), w.G, K, w.L, np.ascontiguousarray(sel[:nh]),
-                      np.ascontiguousarray(cnt[:nh]))
-    return {"mean": float(r.mean()), "min": float(r.min()), "budget": w.B,
-            "sample": f"{nh} KV heads ({nh * w.G} query heads), decode step 0, layer 0"}
+    rs = []
+    for s, sel, cnt in sels:
+        rs.append(oracle.recall(np.ascontiguousarray(Q[s, :nh * w.G]), w.G, K, w.L, np.ascontiguousarray(sel[:nh]),
+                                np.ascontiguousarray(cnt[:nh])))
+    r = np.concatenate(rs)
+    return {"mean": float(r.mean()), "min": float(r.min()), "budget": w.B, "metric": args.metric,
+            "sample": f"{nh} KV heads ({nh * w.G} query heads) x decode steps 0..{len(sels) - 1}, layer 0"}
 
 
 if __name__ == "__main__":
