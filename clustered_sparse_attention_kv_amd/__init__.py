@@ -42,6 +42,11 @@ class _Index(C.Structure):
                 ("window_start", C.c_int32), ("metric", C.c_int32)]
 
 
+class _Cache(C.Structure):
+    _fields_ = [("R", C.c_int32), ("B", C.c_int32), ("step", C.c_int32), ("reserved", C.c_int32),
+                ("k", C.c_void_p), ("v", C.c_void_p), ("table", C.c_void_p), ("stats", C.c_void_p)]
+
+
 def lib():
     """The loaded library; raises if it has not been built."""
     global _lib
@@ -73,12 +78,16 @@ def lib():
         L.kv_dense_decode.argtypes = [p, i, p, p, i, i, i, i, i, f, p, p, sz, p]
         L.kv_cluster_debug_assign.argtypes = [p, p, i, p, p, p, p, p, sz, p]
         L.kv_cluster_debug_update.argtypes = [p, p, i, p, sz, p]
+        L.kv_cluster_cache_reset.argtypes = [p, p, p]
+        L.kv_cluster_cache_workspace_bytes.argtypes = [i, i, i, i]
+        L.kv_cluster_cache_workspace_bytes.restype = sz
+        L.kv_cluster_cached_select_decode.argtypes = [p, p, p, i, p, p, f, p, p, p, p, sz, p]
         L.kv_cluster_status_string.argtypes = [i]
         L.kv_cluster_status_string.restype = C.c_char_p
         for name in ("kv_cluster_build", "kv_cluster_build_timed", "kv_cluster_append", "kv_cluster_append_window",
                      "kv_cluster_cluster_window", "kv_cluster_select", "kv_sparse_decode", "kv_cluster_select_decode",
                      "kv_cluster_export_csr", "kv_cluster_pack", "kv_dense_decode", "kv_cluster_debug_assign",
-                     "kv_cluster_debug_update"):
+                     "kv_cluster_debug_update", "kv_cluster_cache_reset", "kv_cluster_cached_select_decode"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -116,6 +125,46 @@ def _ptr(t: torch.Tensor | None):
     return C.c_void_p(t.data_ptr())
 
 
+_hip_rt = None
+
+
+def _hip():
+    """The HIP runtime that torch has loaded (for host-memory pointers)."""
+    global _hip_rt
+    if _hip_rt is None:
+        torch.cuda.init()
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        rt = C.CDLL(path or "libamdhip64.so")
+        rt.hipHostGetDevicePointer.argtypes = [C.POINTER(C.c_void_p), C.c_void_p, C.c_uint]
+        rt.hipHostGetDevicePointer.restype = C.c_int
+        _hip_rt = rt
+    return _hip_rt
+
+
+def _ptr_kv(t: torch.Tensor | None):
+    """Device-visible address of a K/V array: device memory, or pinned host
+    memory (``pin_memory=True``) mapped into the GPU's address space, for KV
+    that lives on the host."""
+    if t is None:
+        return None
+    if t.is_cuda:
+        return _ptr(t)
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    if not t.is_pinned():
+        raise ValueError("host K/V arrays must be pinned (allocate them with pin_memory=True)")
+    dptr = C.c_void_p()
+    rc = _hip().hipHostGetDevicePointer(C.byref(dptr), C.c_void_p(t.data_ptr()), 0)
+    if rc != 0 or not dptr.value:
+        raise RuntimeError(f"hipHostGetDevicePointer failed ({rc})")
+    return dptr
+
+
 def _stream(stream) -> C.c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return C.c_void_p(s.cuda_stream)
@@ -138,13 +187,14 @@ class ClusterIndex:
 
     def __init__(self, heads: int, C_: int, capacity: int, dtype: torch.dtype = torch.bfloat16,
                  d: int = HEAD_DIM, device="cuda", packed: bool = False, n_sink: int = 0, c_slots: int = 0,
-                 metric: int = COSINE):
+                 metric: int = COSINE, packed_on_host: bool = False):
         """packed: also allocate the cluster-ordered copies of the keys and
         values (``kv_cluster_pack``), two more arrays of the caches' size.
         n_sink: attention sinks, kept out of the clustering and always
         selected first. c_slots: cluster slots per head (>= C; 0 for C), room
         for the clusters that ``cluster_window`` adds. metric: assignment
-        distance, COSINE (the method's), L2 or INNER_PRODUCT."""
+        distance, COSINE (the method's), L2 or INNER_PRODUCT. packed_on_host:
+        the packed copies live in pinned host memory (offloaded KV)."""
         self.heads, self.C, self.capacity, self.d, self.dtype = heads, C_, capacity, d, dtype
         S = c_slots if c_slots else C_
         self.slots = S
@@ -159,15 +209,21 @@ class ClusterIndex:
         self.app_ids = torch.full((heads, capacity), -1, **i32)
         self.dev_flags = torch.zeros(1, **i32)
         self.centroids_t = torch.zeros(heads, d // 4, S, 4, dtype=torch.float32, device=device)
-        self.k_packed = torch.empty(heads, capacity, d, dtype=dtype, device=device) if packed else None
-        self.v_packed = torch.empty(heads, capacity, d, dtype=dtype, device=device) if packed else None
+        if packed and packed_on_host:
+            self.k_packed = torch.empty(heads, capacity, d, dtype=dtype, pin_memory=True)
+            self.v_packed = torch.empty(heads, capacity, d, dtype=dtype, pin_memory=True)
+        elif packed:
+            self.k_packed = torch.empty(heads, capacity, d, dtype=dtype, device=device)
+            self.v_packed = torch.empty(heads, capacity, d, dtype=dtype, device=device)
+        else:
+            self.k_packed = self.v_packed = None
         self._s = _Index(heads, d, C_, capacity, _dtype_code(dtype), 0, 0, 0,
                          self.centroids.data_ptr(), self.centroids_op.data_ptr(), self.labels.data_ptr(),
                          self.sizes.data_ptr(), self.offsets.data_ptr(), self.token_ids.data_ptr(),
                          self.app_offsets.data_ptr(), self.app_ids.data_ptr(), self.dev_flags.data_ptr(),
                          self.centroids_t.data_ptr(),
-                         self.k_packed.data_ptr() if packed else None,
-                         self.v_packed.data_ptr() if packed else None, n_sink, c_slots, 0, 0, metric)
+                         _ptr_kv(self.k_packed).value if packed else None,
+                         _ptr_kv(self.v_packed).value if packed else None, n_sink, c_slots, 0, 0, metric)
         self.metric = metric
         self.n_sink = n_sink
 
@@ -326,7 +382,7 @@ def select_decode(idx: ClusterIndex, q: torch.Tensor, k_cache: torch.Tensor, v_c
         raise ValueError("sel_ids must be int32 [heads, B]")
     if sel_count is not None and (sel_count.dtype != torch.int32 or sel_count.numel() != idx.heads):
         raise ValueError("sel_count must be int32 [heads]")
-    _check(lib().kv_cluster_select_decode(idx.ref(), _ptr(q), q.shape[0], _ptr(k_cache), _ptr(v_cache), B,
+    _check(lib().kv_cluster_select_decode(idx.ref(), _ptr(q), q.shape[0], _ptr_kv(k_cache), _ptr_kv(v_cache), B,
                                           float(scale), _ptr(out), _ptr(sel_ids), _ptr(sel_count), _stream(stream)),
            "kv_cluster_select_decode")
     return out
@@ -339,7 +395,70 @@ def pack(idx: ClusterIndex, k_cache: torch.Tensor, v_cache: torch.Tensor, stream
     _cache_check(idx, v_cache, "v_cache")
     if idx.k_packed is None:
         raise ValueError("the index has no packed arrays (create it with packed=True)")
-    _check(lib().kv_cluster_pack(idx.ref(), _ptr(k_cache), _ptr(v_cache), _stream(stream)), "kv_cluster_pack")
+    _check(lib().kv_cluster_pack(idx.ref(), _ptr_kv(k_cache), _ptr_kv(v_cache), _stream(stream)), "kv_cluster_pack")
+
+
+class ClusterCache:
+    """Device memory of a cluster cache (``kvc_cluster_cache``) for one index:
+    the rows of the last R + 1 steps, the per-cluster table and counters."""
+
+    def __init__(self, idx: ClusterIndex, R: int, B: int, device="cuda"):
+        self.R, self.B = R, B
+        self.k = torch.empty(idx.heads, (R + 1) * B, idx.d, dtype=idx.dtype, device=device)
+        self.v = torch.empty_like(self.k)
+        self.table = torch.empty(idx.heads, idx.slots, 3, dtype=torch.int32, device=device)
+        self.stats = torch.zeros(idx.heads, 4, dtype=torch.int64, device=device)
+        self._s = _Cache(R, B, 0, 0, self.k.data_ptr(), self.v.data_ptr(), self.table.data_ptr(),
+                         self.stats.data_ptr())
+
+    @property
+    def step(self) -> int:
+        return self._s.step
+
+    def ref(self):
+        return C.byref(self._s)
+
+    def hit_rates(self) -> dict:
+        """Cluster and token hit rates accumulated since the last reset."""
+        s = self.stats.sum(dim=0).tolist()
+        return {"clusters": s[0], "cluster_hits": s[1], "tokens": s[2], "token_hits": s[3],
+                "cluster_hit_rate": s[1] / max(s[0], 1), "token_hit_rate": s[3] / max(s[2], 1)}
+
+
+def cache_reset(idx: ClusterIndex, cache: ClusterCache, stream=None):
+    """kv_cluster_cache_reset."""
+    _check(lib().kv_cluster_cache_reset(idx.ref(), cache.ref(), _stream(stream)), "kv_cluster_cache_reset")
+
+
+def cache_workspace_bytes(heads: int, q_heads: int, B: int, d: int = HEAD_DIM) -> int:
+    return lib().kv_cluster_cache_workspace_bytes(heads, q_heads, d, B)
+
+
+def cached_select_decode(idx: ClusterIndex, cache: ClusterCache, q: torch.Tensor, k_cache: torch.Tensor,
+                         v_cache: torch.Tensor, scale: float, out: torch.Tensor | None = None,
+                         sel_ids: torch.Tensor | None = None, sel_count: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None, stream=None):
+    """kv_cluster_cached_select_decode: selection through the cluster cache and
+    attention over the assembled rows -> fp32 [q_heads, d]. k_cache, v_cache
+    may be pinned host tensors (offloaded KV)."""
+    _cache_check(idx, k_cache, "k_cache")
+    _cache_check(idx, v_cache, "v_cache")
+    if q.dtype != idx.dtype or q.dim() != 2 or q.shape[1] != idx.d:
+        raise ValueError(f"q must be {idx.dtype} [q_heads, {idx.d}]")
+    if out is None:
+        out = torch.empty(q.shape[0], idx.d, dtype=torch.float32, device=q.device)
+    if sel_ids is not None and (sel_ids.dtype != torch.int32 or tuple(sel_ids.shape) != (idx.heads, cache.B)):
+        raise ValueError("sel_ids must be int32 [heads, B]")
+    if sel_count is not None and (sel_count.dtype != torch.int32 or sel_count.numel() != idx.heads):
+        raise ValueError("sel_count must be int32 [heads]")
+    if workspace is None:
+        workspace = torch.empty(max(cache_workspace_bytes(idx.heads, q.shape[0], cache.B, idx.d), 1),
+                                dtype=torch.uint8, device=q.device)
+    _check(lib().kv_cluster_cached_select_decode(idx.ref(), cache.ref(), _ptr(q), q.shape[0], _ptr_kv(k_cache),
+                                                 _ptr_kv(v_cache), float(scale), _ptr(out), _ptr(sel_ids),
+                                                 _ptr(sel_count), _ptr(workspace), workspace.numel(),
+                                                 _stream(stream)), "kv_cluster_cached_select_decode")
+    return out
 
 
 def dense_decode_workspace_bytes(heads: int, q_heads: int, n: int, d: int = HEAD_DIM) -> int:

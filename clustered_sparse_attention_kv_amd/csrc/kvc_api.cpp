@@ -359,6 +359,58 @@ int kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token
                                       static_cast<hipStream_t>(stream)));
 }
 
+int kv_cluster_cache_reset(const kvc_index* idx, kvc_cluster_cache* cache, void* stream) {
+  if (!index_ok(idx) || !cache || !cache->table || !cache->stats) return KVC_ERR_INVALID_ARG;
+  if (int s = index_support(idx)) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int H = idx->heads, cs = slots(idx);
+  // table entries (step, row, members) = (never, 0, 0); counters 0
+  hipError_t e = launch_fill_i32(cache->table, (size_t)H * cs * 3, 0, st);
+  if (e == hipSuccess) e = launch_fill2d_i32(cache->table, H * cs, 3, 1, -(1 << 30), st);
+  if (e == hipSuccess) e = launch_fill_i32(reinterpret_cast<int32_t*>(cache->stats), (size_t)H * 4 * 2, 0, st);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  cache->step = 0;
+  return KVC_OK;
+}
+
+size_t kv_cluster_cache_workspace_bytes(int heads, int q_heads, int d, int B) {
+  if (heads < 1 || q_heads < heads || d < 1 || B < 1) return 0;
+  return align_up(sizeof(int32_t) * (size_t)heads * B) + align_up(sizeof(int32_t) * (size_t)heads) +
+         kv_sparse_decode_workspace_bytes(heads, q_heads, d, B);
+}
+
+int kv_cluster_cached_select_decode(const kvc_index* idx, kvc_cluster_cache* cache, const void* q, int q_heads,
+                                    const void* k_cache, const void* v_cache, float scale, float* out,
+                                    int32_t* sel_ids, int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
+  if (!index_ok(idx) || !cache || !q || !k_cache || !v_cache || !out || !ws || q_heads < 1) return KVC_ERR_INVALID_ARG;
+  if (!cache->k || !cache->v || !cache->table || !cache->stats || cache->R < 1 || cache->B < 1 || cache->step < 0)
+    return KVC_ERR_INVALID_ARG;
+  if (int s = index_support(idx)) return s;
+  if (!built_ok(idx) || q_heads % idx->heads != 0) return KVC_ERR_INVALID_ARG;
+  const int H = idx->heads, G = q_heads / H, B = cache->B, R = cache->R;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KVC_ERR_UNSUPPORTED;
+  if ((long long)H * (R + 1) * B >= (1ll << 31)) return KVC_ERR_INVALID_ARG;
+  if ((long long)((B + DEC_TOK - 1) / DEC_TOK) * G > DEC_MAX_PAIRS) return KVC_ERR_UNSUPPORTED;
+  if (ws_bytes < kv_cluster_cache_workspace_bytes(H, q_heads, KVC_HEAD_DIM, B)) return KVC_ERR_WORKSPACE;
+  char* w = static_cast<char*>(ws);
+  int32_t* rows = reinterpret_cast<int32_t*>(w);
+  int32_t* count = reinterpret_cast<int32_t*>(w + align_up(sizeof(int32_t) * (size_t)H * B));
+  float* part = reinterpret_cast<float*>(w + align_up(sizeof(int32_t) * (size_t)H * B) + align_up(sizeof(int32_t) * H));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool packed = idx->packed == 1 && idx->k_packed && idx->v_packed;
+  hipError_t e = launch_cache_assemble(idx->dtype, q, G, view(idx), H, k_cache, v_cache,
+                                       packed ? idx->k_packed : nullptr, packed ? idx->v_packed : nullptr, B, R,
+                                       cache->step, cache->k, cache->v, cache->table,
+                                       reinterpret_cast<long long*>(cache->stats), rows, count, sel_ids, sel_count,
+                                       st);
+  if (e == hipSuccess)
+    e = launch_decode(idx->dtype, q, G, cache->k, cache->v, (long long)(R + 1) * B * KVC_HEAD_DIM, H, rows, count, B,
+                      scale, out, part, st);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  cache->step += 1;
+  return KVC_OK;
+}
+
 size_t kv_dense_decode_workspace_bytes(int heads, int q_heads, int d, int n) {
   if (heads < 1 || q_heads < heads || q_heads % heads != 0 || d != KVC_HEAD_DIM || n < 1) return 0;
   const int G = q_heads / heads;

@@ -239,9 +239,10 @@ __device__ __forceinline__ void bitonic_sort(Sh& S, unsigned long long& key, int
 // cent_t is the chunk-major copy [d/4, cs, 4] of the head's centroids: thread k
 // reads chunk jj of its row at ((jj * cs) + k) * 16 bytes, so a wave's loads are
 // contiguous. The chain still runs over ascending j.
+// Returns the cluster id of rank tid (ids >= X.ca are padding).
 template <typename QT>
-__device__ __forceinline__ void select_phase(SelShared& S, const QT* __restrict__ q, int G, const IndexView& X,
-                                             int h) {
+__device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__ q, int G, const IndexView& X,
+                                            int h) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int C = X.ca, cs = X.cs;
   if (tid < C) {  // per-cluster metadata, read while the scores are computed
@@ -305,6 +306,7 @@ __device__ __forceinline__ void select_phase(SelShared& S, const QT* __restrict_
   S.abase[tid] = ab;
   if (tid == 0) S.total = tot;
   __syncthreads();
+  return id;
 }
 
 // Entry at output position p (< n_sink + nw + total) of the ranked, trimmed
@@ -366,6 +368,127 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const QT* __restric
   for (int p = tid; p < B; p += SEL_THREADS)
     sel_ids[(size_t)h * B + p] = p < cnt ? select_emit(S, p, ids_h, app_h, false, X) : -1;
   if (tid == 0) sel_count[h] = cnt;
+}
+
+// ---------------------------------------------------------------------------
+// Cluster cache for offloaded KV (Sys-A: the KV lives in CPU memory and the
+// selected clusters are loaded at each decoding step; Sys-D: a GPU cache keeps
+// the selected KV and the cluster labels of the last R decoding steps, so only
+// clusters absent from it are loaded). One block per KV head, decode step t:
+//  1. the selection of select_kernel (sinks, window, ranked clusters, trim);
+//  2. region t mod (R + 1) of the head's cache buffer ([(R + 1) * B, d])
+//     receives the selected rows in selection order (row region * B + p for
+//     entry p). A member e of cluster k comes from the cache when k's table
+//     entry was written at a step in [t - R, t - 1] and holds more than e
+//     members (those rows sit in that step's region, never the current one);
+//     every other row is read from its source: the packed copy or the caches,
+//     in host memory when the KV is offloaded;
+//  3. each selected cluster's entry becomes (t, its first row, members taken),
+//     and the head's counters add: clusters selected, clusters found in the
+//     cache, cluster tokens selected, tokens copied from the cache.
+// Sinks and window tokens are read from their source at every step and are
+// not counted. The decode then reads the region's rows in order.
+template <typename KT>
+__global__ __launch_bounds__(SEL_THREADS) void cache_assemble_kernel(
+    const KT* __restrict__ q, int G, const IndexView X, const KT* __restrict__ kc, const KT* __restrict__ vc,
+    const KT* __restrict__ kp, const KT* __restrict__ vp, int packed, int B, int R, int t, KT* __restrict__ ck,
+    KT* __restrict__ cv, int32_t* __restrict__ table, long long* __restrict__ stats, int32_t* __restrict__ rows,
+    int32_t* __restrict__ count, int32_t* __restrict__ sel_ids, int32_t* __restrict__ sel_count) {
+  __shared__ SelShared S;
+  __shared__ int hitlen[SEL_THREADS], hitrow[SEL_THREADS];  // per rank: cached members and their first row
+  __shared__ long long red[4][SEL_THREADS / WAVE];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int id = select_phase(S, q, G, X, h);
+  const int cnt = select_count(S, X, B);
+  const int fixed = X.n_sink + X.nw;
+  const int nclus = cnt > fixed ? cnt - fixed : 0;  // entries taken from clusters
+  const int region = t % (R + 1);
+  int32_t* tab = table + (size_t)h * X.cs * 3;
+  // rank tid: members taken from its cluster and that cluster's cached entry
+  int m = 0;
+  if (id < X.ca) {
+    m = nclus - S.W[tid];
+    m = m < S.mn[id] ? m : S.mn[id];
+    m = m > 0 ? m : 0;
+  }
+  int es = 0, er = 0, el = 0;
+  if (m > 0) {
+    es = tab[(size_t)id * 3];
+    er = tab[(size_t)id * 3 + 1];
+    el = tab[(size_t)id * 3 + 2];
+  }
+  const bool hit = m > 0 && es >= t - R && es < t && el > 0;
+  hitlen[tid] = hit ? el : 0;
+  hitrow[tid] = er;
+  __syncthreads();
+  if (m > 0) {  // the entry now points at this step's rows
+    tab[(size_t)id * 3] = t;
+    tab[(size_t)id * 3 + 1] = region * B + fixed + S.W[tid];
+    tab[(size_t)id * 3 + 2] = m;
+  }
+  {
+    long long v[4] = {m > 0 ? 1 : 0, hit ? 1 : 0, m, hit ? (el < m ? el : m) : 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v[i] += __shfl_xor(v[i], off);
+      if (lane == 0) red[i][w] = v[i];
+    }
+  }
+  const int32_t* ids_h = X.token_ids + (size_t)h * X.cap;
+  const int32_t* app_h = X.app_ids + (size_t)h * X.cap;
+  const size_t hb = (size_t)h * (R + 1) * B;
+  KT* ckh = ck + hb * D;
+  KT* cvh = cv + hb * D;
+  const KT* kch = kc + (size_t)h * X.cap * D;
+  const KT* vch = vc + (size_t)h * X.cap * D;
+  const KT* kph = kp + (size_t)h * X.cap * D;
+  const KT* vph = vp + (size_t)h * X.cap * D;
+  constexpr int LPR = D * (int)sizeof(KT) / 16;  // lanes per row, 16 bytes each
+  constexpr int RPP = SEL_THREADS / LPR;         // rows per pass
+  const int l = tid % LPR;
+  for (int p = tid / LPR; p < cnt; p += RPP) {
+    const int ent = select_emit(S, p, ids_h, app_h, packed, X);
+    const KT* sk = sel_row(kph, kch, ent);
+    const KT* sv = sel_row(vph, vch, ent);
+    if (p >= fixed) {
+      const int pc = p - fixed;
+      int lo = 0, hi = SEL_THREADS - 1;  // rank of entry p: last r with W[r] <= pc
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (S.W[mid] <= pc) lo = mid;
+        else hi = mid - 1;
+      }
+      const int e = pc - S.W[lo];
+      if (e < hitlen[lo]) {
+        sk = ckh + (size_t)(hitrow[lo] + e) * D;
+        sv = cvh + (size_t)(hitrow[lo] + e) * D;
+      }
+    }
+    const u32x4 a = reinterpret_cast<const u32x4*>(sk)[l];
+    const u32x4 b = reinterpret_cast<const u32x4*>(sv)[l];
+    const size_t dst = ((size_t)region * B + p) * D;
+    reinterpret_cast<u32x4*>(ckh + dst)[l] = a;
+    reinterpret_cast<u32x4*>(cvh + dst)[l] = b;
+    if (l == 0) {
+      rows[(size_t)h * B + p] = region * B + p;
+      if (sel_ids) sel_ids[(size_t)h * B + p] = sel_token(ids_h, ent, packed);
+    }
+  }
+  if (sel_ids)
+    for (int p = cnt + tid; p < B; p += SEL_THREADS) sel_ids[(size_t)h * B + p] = -1;
+  __syncthreads();
+  if (tid == 0) {
+    count[h] = cnt;
+    if (sel_count) sel_count[h] = cnt;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      long long sum = 0;
+#pragma unroll
+      for (int v = 0; v < SEL_THREADS / WAVE; ++v) sum += red[i][v];
+      stats[(size_t)h * 4 + i] += sum;
+    }
+  }
 }
 
 // Max / sum over the whole wave, result in every lane: row reductions by DPP,
@@ -1252,6 +1375,24 @@ hipError_t launch_select(int dtype, const void* q, int G, const IndexView& x, in
     select_kernel<uint16_t><<<heads, SEL_THREADS, 0, st>>>((const uint16_t*)q, G, x, B, sel_ids, sel_count);
   else
     select_kernel<float><<<heads, SEL_THREADS, 0, st>>>((const float*)q, G, x, B, sel_ids, sel_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_assemble(int dtype, const void* q, int G, const IndexView& x, int heads, const void* kc,
+                                 const void* vc, const void* kp, const void* vp, int B, int R, int t, void* ck,
+                                 void* cv, int32_t* table, long long* stats, int32_t* rows, int32_t* count,
+                                 int32_t* sel_ids, int32_t* sel_count, hipStream_t st) {
+  const int packed = kp && vp ? 1 : 0;
+  if (dtype == DT_BF16)
+    cache_assemble_kernel<uint16_t><<<heads, SEL_THREADS, 0, st>>>(
+        (const uint16_t*)q, G, x, (const uint16_t*)kc, (const uint16_t*)vc, (const uint16_t*)(packed ? kp : kc),
+        (const uint16_t*)(packed ? vp : vc), packed, B, R, t, (uint16_t*)ck, (uint16_t*)cv, table, stats, rows, count,
+        sel_ids, sel_count);
+  else
+    cache_assemble_kernel<float><<<heads, SEL_THREADS, 0, st>>>(
+        (const float*)q, G, x, (const float*)kc, (const float*)vc, (const float*)(packed ? kp : kc),
+        (const float*)(packed ? vp : vc), packed, B, R, t, (float*)ck, (float*)cv, table, stats, rows, count, sel_ids,
+        sel_count);
   return hipGetLastError();
 }
 

@@ -63,6 +63,13 @@ hipError_t launch_select_decode(int dtype, const void* q, int G, const IndexView
                                 const void* vc, const void* kp, const void* vp, int B, float scale, float* out,
                                 int32_t* sel_ids, int32_t* sel_count, hipStream_t st);
 // kp, vp: the packed copies (both non-null) or null (rows from the caches).
+// The cluster cache's step: selection, then the selected rows assembled into
+// region t mod (R + 1) of ck / cv ([heads, (R + 1) * B, d]) from the cache or
+// their source; rows / count receive the decode's row list and counts.
+hipError_t launch_cache_assemble(int dtype, const void* q, int G, const IndexView& x, int heads, const void* kc,
+                                 const void* vc, const void* kp, const void* vp, int B, int R, int t, void* ck,
+                                 void* cv, int32_t* table, long long* stats, int32_t* rows, int32_t* count,
+                                 int32_t* sel_ids, int32_t* sel_count, hipStream_t st);
 void dense_split(int n, int G, int* nsplit, int* T);
 hipError_t launch_dense_decode(const void* q, int G, const void* kc, const void* vc, long long cap, int heads, int n,
                                float scale, float* out, float* part, hipStream_t st);

@@ -298,6 +298,59 @@ int kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, c
                              const void* v_cache, int B, float scale, float* out, int32_t* sel_ids,
                              int32_t* sel_count, void* stream);
 
+/*
+ * GPU cache of selected clusters for offloaded KV (Sys-A: the KV lives in CPU
+ * memory and the selected clusters are loaded at each decoding step; Sys-D: a
+ * GPU cache keeps the selected KV and cluster labels of the last R decoding
+ * steps, and only clusters absent from it are loaded; the pages choose R = 1).
+ * The caller allocates every array (device memory) and sets R and B;
+ * kv_cluster_cache_reset fills the table and counters.
+ */
+typedef struct kvc_cluster_cache {
+  int32_t R;        /* decoding steps whose selections stay cached, R >= 1 */
+  int32_t B;        /* token budget of every cached step (the rows of one step) */
+  int32_t step;     /* host mirror: cached steps since the last reset */
+  int32_t reserved; /* 0 */
+  void* k;          /* [heads, (R + 1) * B, d] in the index's dtype: step t's rows are region
+                       t mod (R + 1), in selection order */
+  void* v;          /* the value rows, same layout */
+  int32_t* table;   /* [heads, S, 3] (S = cluster slots per head): for each cluster, the step of its
+                       last selection, its first row in the cache and the members taken then */
+  int64_t* stats;   /* [heads, 4], accumulated over steps: clusters selected, clusters found in the
+                       cache, cluster tokens selected, tokens copied from the cache */
+} kvc_cluster_cache;
+
+/* Empties the cache (no cluster cached, counters 0, step 0). Also needed
+ * after every kv_cluster_build of the index: cluster ids change meaning. */
+int kv_cluster_cache_reset(const kvc_index* idx, kvc_cluster_cache* cache, void* stream);
+
+/* Bytes of workspace kv_cluster_cached_select_decode needs. */
+size_t kv_cluster_cache_workspace_bytes(int heads, int q_heads, int d, int B);
+
+/*
+ * kv_cluster_select_decode through the cluster cache, for KV that lives in
+ * host memory: k_cache / v_cache (and the packed copy, when idx->packed is
+ * set) may be pinned host memory mapped into the GPU's address space (or
+ * device memory). At step t = cache->step, for every KV head:
+ *   - the selection of kv_cluster_select with B = cache->B;
+ *   - the selected rows are assembled, in selection order, into region
+ *     t mod (R + 1) of the cache. A member of cluster k is copied from the
+ *     cache when k was last selected at a step in [t - R, t - 1] with at
+ *     least that many members taken (members are taken in index order, so the
+ *     cached ones are a prefix); every other row (and every sink and window
+ *     token) is read from its source. The table and counters are updated;
+ *   - attention over the assembled rows (the split path of kv_sparse_decode),
+ *     fp32 out [q_heads, d].
+ * cache->step then advances on the host. sel_ids [heads, B] and sel_count
+ * [heads] (optional) receive the selection as token ids. Requires G =
+ * q_heads / heads in {1, 2, 4, 8}, ceil(B / 64) * G <= 512, R >= 1, B >= 1,
+ * and a workspace of kv_cluster_cache_workspace_bytes(heads, q_heads, d, B)
+ * bytes (contents need not be initialised).
+ */
+int kv_cluster_cached_select_decode(const kvc_index* idx, kvc_cluster_cache* cache, const void* q, int q_heads,
+                                    const void* k_cache, const void* v_cache, float scale, float* out,
+                                    int32_t* sel_ids, int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of workspace kv_dense_decode needs. */
 size_t kv_dense_decode_workspace_bytes(int heads, int q_heads, int d, int n);
 

@@ -356,3 +356,37 @@ def recall(q: np.ndarray, G: int, Kc: np.ndarray, N: int, sel_ids: np.ndarray, s
     lib.orc_recall(H, G, d, int(N), B, _ptr(q), _dt(q), _ptr(Kc), _dt(Kc), rows * d, _ptr(sel_ids),
                    _ptr(sel_count), _ptr(out))
     return out
+
+
+class ClusterCache:
+    """Counters of the GPU cluster cache (Sys-D: the GPU keeps the selected KV
+    and cluster labels of the last R decoding steps, and only clusters absent
+    from it are loaded), simulated from the selections.
+
+    Per head, the cache remembers for each cluster the step of its most recent
+    selection and how many members were taken then (selection takes a prefix
+    of each cluster's members in index order). At step t a selected cluster k
+    taking m members is found in the cache when its last selection was at a
+    step in [t - R, t - 1]; then min(m, members taken then) of its tokens are
+    cache hits. Sinks and window tokens (label -1) are not counted."""
+
+    def __init__(self, H: int, R: int):
+        self.R, self.t = R, 0
+        self.last = [dict() for _ in range(H)]
+        self.stats = np.zeros((H, 4), dtype=np.int64)  # clusters, cluster hits, tokens, token hits
+
+    def step(self, sel_ids: np.ndarray, sel_count: np.ndarray, labels: np.ndarray):
+        """sel_ids [H, B] token ids, sel_count [H], labels [H, rows] of the index."""
+        for h, last in enumerate(self.last):
+            ids = sel_ids[h, :sel_count[h]]
+            labs = labels[h, ids]
+            ks, ms = np.unique(labs[labs >= 0], return_counts=True)
+            for k, m in zip(ks.tolist(), ms.tolist()):
+                self.stats[h, 0] += 1
+                self.stats[h, 2] += m
+                if k in last and self.t - self.R <= last[k][0] < self.t:
+                    self.stats[h, 1] += 1
+                    self.stats[h, 3] += min(m, last[k][1])
+            for k, m in zip(ks.tolist(), ms.tolist()):
+                last[k] = (self.t, m)
+        self.t += 1

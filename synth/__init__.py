@@ -52,6 +52,7 @@ def _load():
         lib.synth_init_idx.argtypes = [u64, i, i, i, p]
         lib.synth_queries_noisy_key.argtypes = [u64, i, i, i, i, i, p, i, ll, d, p]
         lib.synth_queries_mixture.argtypes = [u64, i, i, i, i, i, p, d, i, p]
+        lib.synth_queries_drift.argtypes = [u64, i, i, i, i, i, p, d, d, i, p]
         lib.synth_normal_array.argtypes = [u64, C.c_size_t, d, i, p]
         _lib = lib
     return _lib
@@ -138,6 +139,17 @@ def queries_noisy_key(base: int, step: int, Hq: int, G: int, keys: np.ndarray, n
     keys = np.ascontiguousarray(keys)
     out = np.empty((Hq, d), dtype=keys.dtype)
     _load().synth_queries_noisy_key(base, step, Hq, G, d, n_cur, _p(keys), dtype, rows * d, sigma, _p(out))
+    return out
+
+
+def queries_drift(base: int, step: int, Hq: int, G: int, means: np.ndarray, sigma: float, p_change: float,
+                  dtype: int = BF16) -> np.ndarray:
+    """Mixture queries whose three components persist across steps, each
+    replaced with probability p_change per step; fresh N(0, sigma^2) noise."""
+    H, M, d = means.shape
+    means = np.ascontiguousarray(means, dtype=np.float64)
+    out = np.empty((Hq, d), dtype=_np(dtype))
+    _load().synth_queries_drift(base, step, Hq, G, d, M, _p(means), sigma, float(p_change), dtype, _p(out))
     return out
 
 

@@ -248,6 +248,41 @@ void synth_queries_mixture(uint64_t base, int step, int Hq, int G, int d, int M,
   }
 }
 
+/*
+ * Mixture queries that drift over decoding steps: query head g mixes three
+ * component means of its KV head, as synth_queries_mixture does, but each of
+ * the three slots keeps its component and weight until a change event (an
+ * independent per-slot, per-step draw below p_change), and only the noise is
+ * new at every step. Consecutive steps therefore attend to overlapping parts of
+ * the context. Stateless: the epoch of slot a at step t is the number of events
+ * in steps 1 .. t, recounted from the seed.
+ */
+void synth_queries_drift(uint64_t base, int step, int Hq, int G, int d, int M, const double* means, double sigma,
+                         double p_change, int dtype, void* out) {
+  const uint64_t nb = base ^ mix64((uint64_t)step + 0x5151);
+  for (int g = 0; g < Hq; ++g) {
+    const int h = g / G;
+    int pick[3];
+    double e[3], se = 0.0;
+    for (int a = 0; a < 3; ++a) {
+      const uint64_t slot = synth_stream_seed(base, (uint64_t)g, 100 + (uint64_t)a);
+      uint64_t epoch = 0;
+      for (int u = 1; u <= step; ++u)
+        if (uniform01(slot, (uint64_t)u) < p_change) ++epoch;
+      const uint64_t es = synth_stream_seed(slot, epoch, 1);
+      pick[a] = (int)below(es, 0, (uint32_t)M);
+      e[a] = -log(uniform01(es, 1));
+      se += e[a];
+    }
+    const uint64_t ns = synth_stream_seed(nb, (uint64_t)g, 9);
+    for (int j = 0; j < d; ++j) {
+      double v = 0.0;
+      for (int a = 0; a < 3; ++a) v += (e[a] / se) * means[((size_t)h * M + pick[a]) * d + j];
+      store(out, dtype, (size_t)g * d + j, v + sigma * normal01(ns, (uint64_t)j));
+    }
+  }
+}
+
 /* Plain N(0, sigma^2) array from one stream (used for tiny test cases). */
 void synth_normal_array(uint64_t seed, size_t n, double sigma, int dtype, void* out) {
 #pragma omp parallel for schedule(static)

@@ -177,6 +177,38 @@ def test_window_calls_reject(kvc):
         assert L.kv_cluster_build(C.byref(odd), p, 200, 3, p, p, 1 << 40, None) == INVALID
 
 
+def test_cluster_cache_calls_reject(kvc):
+    """The cluster cache: descriptor fields, index state, G, B and the
+    workspace are checked before anything is enqueued."""
+    L = kvc.lib()
+    p = C.c_void_p(FAKE)
+    built = make_index(kvc, heads=4, Cn=16, cap=256, n_build=200, n_tokens=200)
+    f = C.c_float(0.1)
+    ws = L.kv_cluster_cache_workspace_bytes(4, 16, 128, 64)
+    assert ws >= L.kv_sparse_decode_workspace_bytes(4, 16, 128, 64) + 4 * 64 * 4
+    assert L.kv_cluster_cache_workspace_bytes(0, 16, 128, 64) == 0
+
+    def cache(R=1, B=64, null=None):
+        c = kvc._Cache(R, B, 0, 0, FAKE, FAKE, FAKE, FAKE)
+        if null:
+            setattr(c, null, None)
+        return c
+
+    def run(idx=built, c=None, qh=16, b=ws):
+        return L.kv_cluster_cached_select_decode(C.byref(idx), C.byref(c or cache()), p, qh, p, p, f, p, None, None, p,
+                                                 b, None)
+    assert run(c=cache(R=0)) == INVALID
+    assert run(c=cache(B=0)) == INVALID
+    for field in ("k", "v", "table", "stats"):
+        assert run(c=cache(null=field)) == INVALID, field
+    assert run(idx=make_index(kvc)) == INVALID          # never built
+    assert run(qh=12) == UNSUPPORTED                    # G = 3
+    assert run(qh=10) == INVALID                        # 10 % 4 != 0
+    assert run(b=ws - 1) == WORKSPACE
+    assert run(c=cache(B=8192), b=1 << 40) == UNSUPPORTED  # 128 splits x 4 heads > 512 pairs
+    assert L.kv_cluster_cache_reset(C.byref(built), C.byref(cache(null="table")), None) == INVALID
+
+
 def test_binding_fails_loudly_without_library(kvc, monkeypatch):
     """The product path never falls back to anything else: no library, no call."""
     import clustered_sparse_attention_kv_amd as m

@@ -481,6 +481,56 @@ def test_distance_variants_end_to_end(case, metric):
         assert np.abs(to_np(fout) - od).max() <= 2e-3, step
 
 
+@pytest.mark.parametrize("where", ["device", "host"])
+def test_cluster_cache_matches_uncached_path(where):
+    """Sys-A / Sys-D: the KV lives in HBM or in pinned host memory (read by the
+    kernels over the host link), and each decode step assembles the selected
+    clusters through the R-step GPU cache. Every step, for R = 1 and 2 and with
+    attention sinks: the selection equals the oracle's; the attention equals
+    kv_sparse_decode over the same tokens bit for bit (the same kernel reads
+    the same rows in the same order) and the oracle's within 2e-3; the cache's
+    counters equal the oracle's simulation of the cache. The query sequence
+    repeats and drifts so that steps hit, partly hit and miss."""
+    w, n_sink = SMALL, 4
+    base, K, V, _, means = make_inputs(w)
+    H = K.shape[0]
+    host = where == "host"
+    init = synth.init_idx(base, H, w.L - n_sink, w.C) + n_sink
+    idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w), packed=True, n_sink=n_sink, packed_on_host=host)
+    Kd, Vd = to_dev(K), to_dev(V)
+    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    Ks, Vs = (Kd.cpu().pin_memory(), Vd.cpu().pin_memory()) if host else (Kd, Vd)
+    kvc.pack(idx, Ks, Vs)
+    torch.cuda.synchronize()
+    if host:
+        ids = to_np(idx.token_ids)[:, :w.L - n_sink]
+        for h in range(H):
+            assert np.array_equal(to_np(idx.k_packed)[h, :w.L - n_sink], K[h, ids[h]])
+    labels, c = to_np(idx.labels), to_np(idx.centroids)
+    sizes, offsets, token_ids = to_np(idx.sizes), to_np(idx.offsets), to_np(idx.token_ids)
+    scale = 1.0 / math.sqrt(w.d)
+    pattern = [0, 0, 1, 0, 2, 2, 1, 3, 3, 0]
+    for R in (1, 2):
+        cache = kvc.ClusterCache(idx, R, w.B)
+        kvc.cache_reset(idx, cache)
+        sim = oracle.ClusterCache(H, R)
+        for t, qs in enumerate(pattern):
+            q = queries(w, base, qs, K, w.L, means)
+            sel = torch.full((H, w.B), -7, dtype=torch.int32, device="cuda")
+            cnt = torch.empty(H, dtype=torch.int32, device="cuda")
+            out = kvc.cached_select_decode(idx, cache, to_dev(q), Ks, Vs, scale, sel_ids=sel, sel_count=cnt)
+            osel, ocnt, _, _ = oracle.select(q, w.G, c, sizes, offsets, token_ids, w.B, n_sink=n_sink)
+            ref = kvc.sparse_decode(to_dev(q), Kd, Vd, to_dev(osel), to_dev(ocnt), scale)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_np(sel), osel) and np.array_equal(to_np(cnt), ocnt), (R, t)
+            assert torch.equal(out, ref), (R, t)
+            assert np.abs(to_np(out) - oracle.decode(q, w.G, K, V, osel, ocnt, scale)).max() <= 2e-3
+            sim.step(osel, ocnt, labels)
+            assert np.array_equal(to_np(cache.stats), sim.stats), (R, t, to_np(cache.stats), sim.stats)
+        assert cache.step == len(pattern)
+        say(f"  {where}, R={R}: {cache.hit_rates()}")
+
+
 def test_init_index_out_of_range_flag():
     w = SMALL
     base, K, V, init, _ = make_inputs(w)

@@ -657,3 +657,27 @@ def test_l2_kmeans_objective_non_increasing_exact_mode(orc, syn):
         lab = orc.assign(K[h], r["chat"][h], orc.L2)[0]
         direct = sum(float(((orc.to_f64(K[h, i]) - r["c"][h, lab[i]]) ** 2).sum()) for i in range(700))
         assert math.isclose(orc.inertia(K[h], r["chat"][h], lab, orc.L2), direct, rel_tol=1e-12)
+
+
+# ------------------------------------------------------------- cluster cache
+
+def test_cluster_cache_counts_hand_case(orc):
+    """Sys-D: a cluster selected within the last R steps is not loaded again;
+    a hand-worked sequence of selections (clusters a, b, c = labels 0, 1, 2;
+    label -1 is a sink) and its hits for R = 1 and R = 2."""
+    labels = np.array([[0, 0, 0, 0, 0, 1, 1, 2, -1]])
+    steps = [[8, 0, 1, 2, 5, 6],   # a:3 b:2  (the sink 8 is not counted); nothing cached yet
+             [0, 1, 2, 7],         # a:3 c:1  a was taken at step 0: a hit, 3 tokens
+             [5, 6, 0],            # b:2 a:1  R=1: a (1 token); R=2: also b, taken at step 0 (2 tokens)
+             [0, 1, 2, 3, 4]]      # a:5      a was taken at step 2 with 1 member: 1 token
+    # clusters selected, cluster hits, cluster tokens selected, token hits
+    want = {1: [2 + 2 + 2 + 1, 1 + 1 + 1, 5 + 4 + 3 + 5, 3 + 1 + 1],
+            2: [2 + 2 + 2 + 1, 1 + 2 + 1, 5 + 4 + 3 + 5, 3 + 3 + 1]}
+    for R in (1, 2):
+        sim = orc.ClusterCache(1, R)
+        for s in steps:
+            sel = np.full((1, 8), -1, np.int32)
+            sel[0, :len(s)] = s
+            sim.step(sel, np.array([len(s)]), labels)
+        st = sim.stats[0]
+        assert st.tolist() == want[R], (R, st)

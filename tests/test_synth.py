@@ -43,3 +43,16 @@ def test_init_idx_and_queries(syn):
     qm = syn.queries_mixture(base, 3, 8, 4, means, 0.2)
     assert qm.shape == (8, 128)
     assert not np.array_equal(qm, syn.queries_mixture(base, 4, 8, 4, means, 0.2))
+
+
+def test_drifting_queries(syn):
+    """Drifting mixture queries: deterministic; with no change events (p = 0)
+    and no noise every step gives the same query; with a change at every step
+    (p = 1) consecutive queries differ; fresh noise alone keeps the mean part."""
+    base = syn.config_seed(4)
+    _, _, means = syn.mixture_keys(base, 2, 64, 16, 16, 0.3, 0, 1.0, syn.F32, want_means=True)
+    q = lambda s, sig, p: syn.queries_drift(base, s, 4, 2, means, sig, p, syn.F32)
+    assert np.array_equal(q(5, 0.2, 0.1), q(5, 0.2, 0.1))
+    assert all(np.array_equal(q(0, 0.0, 0.0), q(s, 0.0, 0.0)) for s in (1, 7, 30))
+    assert not np.array_equal(q(3, 0.0, 1.0), q(4, 0.0, 1.0))
+    assert not np.array_equal(q(3, 0.2, 0.0), q(4, 0.2, 0.0))
