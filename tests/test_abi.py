@@ -205,7 +205,7 @@ def test_cluster_cache_calls_reject(kvc):
     assert run(qh=12) == UNSUPPORTED                    # G = 3
     assert run(qh=10) == INVALID                        # 10 % 4 != 0
     assert run(b=ws - 1) == WORKSPACE
-    assert run(c=cache(B=8192), b=1 << 40) == UNSUPPORTED  # 128 splits x 4 heads > 512 pairs
+    assert run(c=cache(B=8192 + 64), b=1 << 40) == UNSUPPORTED  # 129 splits x 4 heads > 512 pairs
     assert L.kv_cluster_cache_reset(C.byref(built), C.byref(cache(null="table")), None) == INVALID
 
 
