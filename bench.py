@@ -119,6 +119,13 @@ def main():
                          "are the alternatives the pages compare it with)")
     ap.add_argument("--recall-heads", type=int, default=16, help="KV heads in the recall sample")
     ap.add_argument("--recall-steps", type=int, default=4, help="decode steps in the recall sample")
+    ap.add_argument("--offload", type=int, default=-1,
+                    help="KV in pinned host memory, read by the kernels over the host link: 0 loads every selected "
+                         "row from the host at each step; R >= 1 keeps the rows selected in the last R steps in a "
+                         "GPU cluster cache and loads only absent clusters (default -1: KV in HBM)")
+    ap.add_argument("--drift", type=float, default=-1.0,
+                    help="mixture workloads: queries whose three components persist across steps, each replaced "
+                         "with this probability per step (default: independent queries per step)")
     ap.add_argument("--window", type=int, default=0,
                     help="append workloads: generated tokens join a window that is always recalled, and every "
                          "WINDOW steps the window is clustered on its own into --window-clusters new clusters "
@@ -154,6 +161,13 @@ def main():
     fused = args.decode_path == "fused"
     M, NC = args.window, args.window_clusters
     metric = {"cosine": kvc.COSINE, "l2": kvc.L2, "inner_product": kvc.INNER_PRODUCT}[args.metric]
+    offload = args.offload
+    if offload >= 0 and not fused:
+        print("--offload runs the fused path", file=sys.stderr)
+        sys.exit(2)
+    if args.drift >= 0 and w.query != "mixture":
+        print("--drift needs a workload with mixture queries (4 or 5)", file=sys.stderr)
+        sys.exit(2)
     if M and not w.append:
         print("--window needs a workload that generates tokens (an append workload)", file=sys.stderr)
         sys.exit(2)
@@ -179,7 +193,9 @@ def main():
         qs = []
         for s in range(w.steps):
             n_cur = L + (s + 1 if w.append else 0)
-            if w.query == "mixture":
+            if w.query == "mixture" and args.drift >= 0:
+                qs.append(synth.queries_drift(base, s, H * G, G, means, w.q_sigma, args.drift, w.dtype))
+            elif w.query == "mixture":
                 qs.append(synth.queries_mixture(base, s, H * G, G, means, w.q_sigma, w.dtype))
             else:
                 qs.append(synth.queries_noisy_key(base, s, H * G, G, K, n_cur, w.q_sigma))
@@ -192,7 +208,15 @@ def main():
             V[:, L:] = 0
         e["Kd"], e["Vd"] = to_dev(K), to_dev(V)
         e["idx"] = kvc.ClusterIndex(H, C, cap, tdt, device=dev, packed=packed, n_sink=args.sinks, c_slots=slots,
-                                    metric=metric)
+                                    metric=metric, packed_on_host=offload >= 0)
+        if offload >= 0:
+            # the decode reads the KV from pinned host memory; the prefill
+            # clustering still runs on the copy in HBM
+            e["Kh"], e["Vh"] = e["Kd"].cpu().pin_memory(), e["Vd"].cpu().pin_memory()
+            if offload >= 1:
+                e["cache"] = kvc.ClusterCache(e["idx"], offload, B, device=dev)
+        else:
+            e["Kh"], e["Vh"] = e["Kd"], e["Vd"]
         # initial centroids of each window's clustering: seeded positions in the window
         e["winit"] = [to_dev(synth.init_idx(synth.stream_seed(base, 7, k), H, M, NC) + np.int32(L + k * M))
                       for k in range(n_windows)]
@@ -205,6 +229,8 @@ def main():
     ws_dec = torch.empty(kvc.decode_workspace_bytes(H, H * G, B), dtype=torch.uint8, device=dev)
     ws_win = (torch.empty(kvc.window_workspace_bytes(H, M, NC, w.iters), dtype=torch.uint8, device=dev)
               if M else None)
+    ws_cache = (torch.empty(kvc.cache_workspace_bytes(H, H * G, B), dtype=torch.uint8, device=dev)
+                if offload >= 1 else None)
     sel = torch.empty(H, B, dtype=torch.int32, device=dev)
     cnt = torch.empty(H, dtype=torch.int32, device=dev)
     out = torch.empty(H * G, d, dtype=torch.float32, device=dev)
@@ -241,6 +267,8 @@ def main():
         if packed:
             for e in lay:
                 kvc.pack(e["idx"], e["Kd"], e["Vd"])
+                if offload >= 1:
+                    kvc.cache_reset(e["idx"], e["cache"])
         ev.record(o + A + 1, sh)
         b = o + A + 4
         for s in range(w.steps):
@@ -263,9 +291,13 @@ def main():
                         if li == 0:
                             ev.record(o + WB + 2 * k + 1, sh)
                 rec(2)
-                if fused:
+                if fused and offload >= 1:
                     rec(3)
-                    kvc.select_decode(e["idx"], e["Qd"][s], e["Kd"], e["Vd"], B, scale, out=out)
+                    kvc.cached_select_decode(e["idx"], e["cache"], e["Qd"][s], e["Kh"], e["Vh"], scale, out=out,
+                                             workspace=ws_cache)
+                elif fused:
+                    rec(3)
+                    kvc.select_decode(e["idx"], e["Qd"][s], e["Kh"], e["Vh"], B, scale, out=out)
                 else:
                     kvc.select(e["idx"], e["Qd"][s], B, sel, cnt)
                     rec(3)
@@ -324,6 +356,8 @@ def main():
                                "share": dd_ms * n_dec * NL / total_ms}
         kernel_names["select_decode"] = ("select_decode_bf16_kernel" if w.dtype == synth.BF16
                                          else "select_decode_kernel")
+        if offload >= 1:
+            kernel_names["select_decode"] = "cache_assemble_kernel + decode_split_kernel + decode_combine_kernel"
     else:
         rl["sparse_decode"] = {"bound": "hbm", "achieved": alg["decode_bytes"] / (dd_ms / 1e3) / 1e9,
                                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "avg_us": dd_ms * 1e3,
@@ -365,7 +399,8 @@ def main():
                    "L": L, "d": d, "C": C,
                    "kmeans_iters": w.iters, "B": B, "decode_steps_per_step": w.steps, "append": w.append,
                    "decode_path": args.decode_path, "packed_kv": packed,
-                   "sinks": args.sinks, "window": M, "window_clusters": NC if M else 0, "metric": args.metric},
+                   "sinks": args.sinks, "window": M, "window_clusters": NC if M else 0, "metric": args.metric,
+                   "offload": offload, "query_drift": args.drift},
         "kmeans_tflops": kmeans_tflops,
         "kmeans_ms": mean(build_ms),
         "pack_ms": mean(pack_ms),
@@ -379,6 +414,18 @@ def main():
     }
     if w.append:
         result["append_us"] = mean(append_ms) * 1e3
+    if offload >= 0:
+        # bytes read from host memory per decode step: the selected K/V rows
+        # that did not come from the cache (all of them without one)
+        e_b = 2 if w.dtype == synth.BF16 else 4
+        sel_bytes = H * NL * min(B, L) * 2 * d * e_b
+        hit = lay[0]["cache"].hit_rates()["token_hit_rate"] if offload >= 1 else 0.0
+        host_bytes = sel_bytes * (1.0 - hit)
+        result["offload"] = {"R": offload, "kv": "pinned host memory, read by the kernels over the host link",
+                             "drift": args.drift, "host_bytes_per_step": host_bytes,
+                             "host_GBps": host_bytes / (step_ms / 1e3) / 1e9}
+        if offload >= 1:
+            result["offload"]["hit_rates"] = lay[0]["cache"].hit_rates()
     if M:
         result["cluster_window_us"] = mean(window_ms) * 1e3
         result["clusters_after_pass"] = C + n_windows * NC
