@@ -125,12 +125,19 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restric
 //
 // Each lane keeps the best score, the tile-uniform part of its centroid id
 // and the runner-up score of each of its keys; the 4 lanes of a key merge at
-// the end. The fp32 order is certified against the exact (fp64) order when
-//   best - runner_up > 2 * 4 * (d + 16) * 2^-24 * ||K_i|| * max||chat_k|| * 1.02,
+// the end. A score's register index within its tile (3 - r) replaces the two
+// low mantissa bits, so the running maximum carries its own index and the
+// fold costs a med3 and a max per score; that moves a value by at most 3 units
+// in the last place. The fp32 order is certified against the exact (fp64)
+// order when
+//   best - runner_up > 2 * 4 * (d + 16) * 2^-24 * ||K_i|| * max||chat_k|| * 1.02
+//                      + 2^-20 * |best|,
 // a bound on the error of any fp32 accumulation of d exact products (the
-// products of bf16 operands are exact) with a safety factor of 4. Keys that
-// fail it are queued for exact re-scoring (fix-up kernel below). Ties and
-// near-ties therefore always resolve by the fp64 rule, lowest id first.
+// products of bf16 operands are exact) with a safety factor of 4, plus the
+// index bits. Keys that fail it are queued for exact re-scoring (fix-up
+// kernel below). Ties and near-ties therefore always resolve by the fp64
+// rule, lowest id first. Only the tiles that hold centroids are computed; a
+// partial last tile masks its padding rows.
 //
 // The L2 and inner-product variants (METRIC) use centroids that are not unit
 // length. The score is K_i . chat_k (inner product) or K_i . chat_k + b_k with
@@ -142,11 +149,19 @@ constexpr int AS_WAVES = 8;
 constexpr int AS_THREADS = AS_WAVES * WAVE;
 constexpr int AS_TILE = AS_WAVES * 64;
 
-__device__ __forceinline__ void top2_update(float s, int u, float& m1, float& m2, int& i1) {
-  const bool gt = s > m1;
-  i1 = gt ? u : i1;
-  m2 = __builtin_amdgcn_fmed3f(m1, m2, s);
-  m1 = gt ? s : m1;
+// Running best and runner-up of one lane's key over the 4 scores of a tile
+// (index bits already in place); i1 takes the tile's first centroid when the
+// best moves into this tile. max(m1, e) of finite scores is taken as
+// med3(m1, e, FLT_MAX): one instruction, with no canonicalisation of the
+// bit-built operand.
+__device__ __forceinline__ void top2_tile(const float (&e)[4], int u0, float& m1, float& m2, int& i1) {
+  const float before = m1;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m2 = __builtin_amdgcn_fmed3f(m1, m2, e[r]);
+    m1 = __builtin_amdgcn_fmed3f(m1, e[r], 3.40282347e38f);
+  }
+  i1 = m1 > before ? u0 : i1;
 }
 
 template <int METRIC>
@@ -197,8 +212,10 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
 
   const uint16_t* Kh = keys + (size_t)h * head_stride + 8 * kb4;
   const int ngroups = (L + AS_TILE - 1) / AS_TILE;
-  const int nct = cpad >> 4;
+  const int ntl = (C + 15) >> 4;          // tiles holding centroids
+  const bool partial = (C & 15) != 0;     // the last of them holds padding rows
   const float gamma = 2.0f * 4.0f * (float)(D + 16) * 5.9604644775390625e-8f * 1.02f;
+  const float gbits = 9.5367431640625e-7f;  // 2^-20: the index bits of best and runner-up
   // variants: threshold = g2 * ((d + 17) * A * ||K_i|| + 2 max|b_k|)
   const float g2 = 2.0f * 4.0f * 5.9604644775390625e-8f * 1.02f;
   const float gA = g2 * (float)(D + 17) * normA, gB = g2 * 2.0f * biasM;
@@ -223,10 +240,9 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
         const u32x4 v = kn[T][s];
         kb[T][s] = __builtin_bit_cast(bf16x8, v);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float lo = __uint_as_float(v[q] << 16), hi = __uint_as_float(v[q] & 0xFFFF0000u);
-          ss = fmaf(lo, lo, ss);
-          ss = fmaf(hi, hi, ss);
+        for (int q = 0; q < 4; ++q) {  // two channels per packed dot product
+          const bf16x2 x = __builtin_bit_cast(bf16x2, v[q]);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
         }
       }
       n2[T] = ss;
@@ -264,14 +280,16 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
       f32x4 bias = {0.f, 0.f, 0.f, 0.f};
       if constexpr (METRIC == M_L2) bias = *reinterpret_cast<const f32x4*>(sBias + u0 + 4 * kb4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = !masked || u0 + 4 * kb4 + r < C;
+      for (int T = 0; T < 4; ++T) {
+        float e[4];
 #pragma unroll
-        for (int T = 0; T < 4; ++T) {
+        for (int r = 0; r < 4; ++r) {
           float sc = acc[T][r];
           if constexpr (METRIC == M_L2) sc += bias[r];
-          top2_update(ok ? sc : -INFINITY, u0 + r, m1[T], m2[T], i1[T]);
+          e[r] = __uint_as_float((__float_as_uint(sc) & ~3u) | (unsigned)(3 - r));
+          if (masked && u0 + 4 * kb4 + r >= C) e[r] = -INFINITY;
         }
+        top2_tile(e, u0, m1[T], m2[T], i1[T]);
       }
     };
     auto interleave = [&]() {
@@ -286,25 +304,33 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     f32x4 accA[4], accB[4];
     load_a(0, aA);
     mma(aA, accA);
-    load_a(1, aB);
+    load_a(ntl > 1 ? 1 : 0, aB);
     int ct = 0;
-    for (; ct + 2 < nct; ct += 2) {
+    for (; ct + 2 < ntl; ct += 2) {
       mma(aB, accB);       // tile ct + 1
       load_a(ct + 2, aA);
       fold(ct, accA, false);
       interleave();
       mma(aA, accA);       // tile ct + 2
-      load_a(ct + 3, aB);  // ct + 3 < nct: nct and ct are even
+      load_a(min(ct + 3, ntl - 1), aB);  // the next tile, or (unused) the last
       fold(ct + 1, accB, false);
       interleave();
     }
-    mma(aB, accB);  // tile nct - 1
-    fold(ct, accA, true);
-    fold(ct + 1, accB, true);
-    // merge the 4 lanes of each key (lanes 16 apart), then certify
+    // accA holds tile ct; tile ct + 1, when there is one, is the last
+    if (ct + 1 < ntl) {
+      mma(aB, accB);
+      fold(ct, accA, false);
+      if (partial) fold(ct + 1, accB, true);
+      else fold(ct + 1, accB, false);
+    } else {
+      if (partial) fold(ct, accA, true);
+      else fold(ct, accA, false);
+    }
+    // full centroid ids (tile, lane group, index bits), then merge the 4 lanes
+    // of each key (lanes 16 apart) and certify
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-      i1[T] += 4 * kb4;
+      i1[T] += 4 * kb4 + 3 - (int)(__float_as_uint(m1[T]) & 3u);
 #pragma unroll
       for (int m = 16; m <= 32; m <<= 1) {
         const float o1 = __shfl_xor(m1[T], m), o2 = __shfl_xor(m2[T], m);
@@ -324,7 +350,8 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     for (int T = 0; T < 4; ++T)
       if (T == kb4) {
         my_label = i1[T];
-        const float thr = METRIC == M_COSINE ? gamma * sqrtf(n2[T]) : gA * sqrtf(n2[T]) + gB;
+        const float thr = (METRIC == M_COSINE ? gamma * sqrtf(n2[T]) : gA * sqrtf(n2[T]) + gB) +
+                          gbits * fabsf(m1[T]);
         my_flag = !((m1[T] - m2[T]) > thr);  // true for NaN and ties
         my_m1 = m1[T];
         my_m2 = m2[T];
