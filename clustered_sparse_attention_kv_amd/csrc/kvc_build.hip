@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restric
 // certificate uses the head's largest operand norm A and largest |b_k|:
 //   best - runner_up > 2 * 4 * 2^-24 * ((d + 17) * ||K_i|| * A + 2 max|b_k|) * 1.02,
 // which also covers the rounding of b_k and of the addition.
-constexpr int AS_WAVES = 8;
+constexpr int AS_WAVES = 12;
 constexpr int AS_THREADS = AS_WAVES * WAVE;
 constexpr int AS_TILE = AS_WAVES * 64;
 
