@@ -531,6 +531,43 @@ def test_cluster_cache_matches_uncached_path(where):
         say(f"  {where}, R={R}: {cache.hit_rates()}")
 
 
+MANY = synth.Workload("many_clusters_bf16", 93, heads=3, G=2, L=3000, d=128, dtype=synth.BF16, M=40, sigma=0.3,
+                      n_out=4, out_scale=10.0, C=100, iters=4, B=300, steps=4, query="noisy_key", q_sigma=0.1)
+
+
+def test_selection_merge_and_full_ranking():
+    """Selection ranks clusters by merging per-wave sorted runs while the
+    budget needs at most 64 clusters, and by a sort of every cluster beyond
+    that: with 100 clusters, budgets needing a few, about 20, more than 64 and
+    all clusters (and sinks) select exactly as the oracle, split and fused."""
+    w, n_sink = MANY, 5
+    base, K, V, _, means = make_inputs(w)
+    H = K.shape[0]
+    init = synth.init_idx(base, H, w.L - n_sink, w.C) + n_sink
+    idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w), packed=True, n_sink=n_sink)
+    Kd, Vd = to_dev(K), to_dev(V)
+    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.pack(idx, Kd, Vd)
+    torch.cuda.synchronize()
+    c, sizes, offsets, token_ids = (to_np(idx.centroids), to_np(idx.sizes), to_np(idx.offsets),
+                                    to_np(idx.token_ids))
+    scale = 1.0 / math.sqrt(w.d)
+    for step, B in enumerate([3, 40, 300, 700, 2500, w.L + 60]):
+        q = queries(w, base, step, K, w.L, means)
+        osel, ocnt, _, order = oracle.select(q, w.G, c, sizes, offsets, token_ids, B, n_sink=n_sink)
+        # clusters the budget reaches (the count of ranks the selection needs)
+        ranks = [int(np.searchsorted(np.cumsum(sizes[h][order[h]]), max(B - n_sink, 0), side="left")) + 1
+                 for h in range(H)]
+        sel, cnt = kvc.select(idx, to_dev(q), B)
+        fsel = torch.full((H, B), -7, dtype=torch.int32, device="cuda")
+        fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel)
+        torch.cuda.synchronize()
+        say(f"  B={B}: clusters reached per head {ranks}, count {ocnt.tolist()}")
+        assert np.array_equal(to_np(sel), osel) and np.array_equal(to_np(cnt), ocnt), B
+        assert np.array_equal(to_np(fsel), osel), B
+        assert np.abs(to_np(fout) - oracle.decode(q, w.G, K, V, osel, ocnt, scale)).max() <= 2e-3, B
+
+
 def test_init_index_out_of_range_flag():
     w = SMALL
     base, K, V, init, _ = make_inputs(w)
