@@ -131,6 +131,9 @@ def main():
                          "WINDOW steps the window is clustered on its own into --window-clusters new clusters "
                          "(default 0: each new token joins its nearest centroid)")
     ap.add_argument("--window-clusters", type=int, default=4, help="clusters made from each window (default 4)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every decode step from the host (default: the decode steps of a pass are "
+                         "captured once in a HIP graph and replayed; the same kernels and work)")
     ap.add_argument("--no-pack", action="store_true",
                     help="decode from the caches through the token ids (no cluster-ordered copy)")
     ap.add_argument("--cpu-heads", type=int, default=16, help="KV heads in the CPU baseline sample")
@@ -257,8 +260,8 @@ def main():
     total_passes = args.warmup + args.steps
     ev = HipEvents(per_pass * total_passes + 2)
 
-    def one_pass(p: int):
-        o = p * per_pass
+    def prepare(o: int):
+        """Builds (and packed copies, cache resets) of every layer: each resets the index's state."""
         ev.record(o + A, sh)
         for li, e in enumerate(lay):
             kvc.build(e["idx"], e["Kd"], L, w.iters, e["init_d"], workspace=ws_build,
@@ -270,10 +273,14 @@ def main():
                 if offload >= 1:
                     kvc.cache_reset(e["idx"], e["cache"])
         ev.record(o + A + 1, sh)
-        b = o + A + 4
+
+    def decode_steps(o):
+        """The workload's decode steps; with o set, events around the kernels of
+        every SAMPLE-th step (first layer) and around each window clustering."""
+        b = o + A + 4 if o is not None else None
         for s in range(w.steps):
             for li, e in enumerate(lay):
-                e6 = b + 6 * (s // SAMPLE) if (s % SAMPLE == 0 and li == 0) else None
+                e6 = b + 6 * (s // SAMPLE) if (b is not None and s % SAMPLE == 0 and li == 0) else None
                 rec = (lambda i: ev.record(e6 + i, sh)) if e6 is not None else (lambda i: None)
                 if w.append:
                     rec(0)
@@ -285,10 +292,10 @@ def main():
                     rec(1)
                     if M and (s + 1) % M == 0:
                         k = (s + 1) // M - 1
-                        if li == 0:
+                        if li == 0 and o is not None:
                             ev.record(o + WB + 2 * k, sh)
                         kvc.cluster_window(e["idx"], e["Kd"], e["Vd"], NC, w.iters, e["winit"][k], workspace=ws_win)
-                        if li == 0:
+                        if li == 0 and o is not None:
                             ev.record(o + WB + 2 * k + 1, sh)
                 rec(2)
                 if fused and offload >= 1:
@@ -303,15 +310,41 @@ def main():
                     rec(3)
                     kvc.sparse_decode(e["Qd"][s], e["Kd"], e["Vd"], sel, cnt, scale, out=out, workspace=ws_dec)
                 rec(4)
+
+    def one_pass(p: int, graph=None):
+        o = p * per_pass
+        prepare(o)
+        if graph is None:
+            decode_steps(o)
+        else:
+            graph.replay()
         ev.record(o + A + 2, sh)
 
+    use_graph = not args.no_graph
+    # passes whose per-kernel events are read: launched step by step from the
+    # host (the warm-up passes with graphs, else the timed ones)
+    eager = list(range(max(args.warmup, 1))) if use_graph else list(range(args.warmup, total_passes))
+    graph = None
     for p in range(args.warmup):
         one_pass(p)
+    if use_graph:
+        if args.warmup == 0:
+            one_pass(0)  # a pass for the per-kernel events
+        torch.cuda.synchronize()
+        # capture one pass's decode steps after a build (the build resets the
+        # index state, so the captured arguments fit every pass)
+        prepare(0)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, capture_error_mode="relaxed"):
+            decode_steps(None)
+        torch.cuda.synchronize()
+        graph.replay()  # a warm replay before timing
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     ev.record(per_pass * total_passes, sh)
     for p in range(args.warmup, total_passes):
-        one_pass(p)
+        one_pass(p, graph)
     ev.record(per_pass * total_passes + 1, sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -325,6 +358,8 @@ def main():
         build_ms.append(ev.ms(o + A, o + A + 3))
         pack_ms.append(ev.ms(o + A + 3, o + A + 1))
         phase_ms.append(ev.ms(o + A + 1, o + A + 2))
+    for p in eager:
+        o = p * per_pass
         b = o + A + 4
         for i in range(len(sampled)):
             e6 = b + 6 * i
@@ -406,8 +441,10 @@ def main():
         "pack_ms": mean(pack_ms),
         "decode_step_us": step_ms * 1e3,
         "decode_step_hbm_frac": alg["step_bytes"] * NL / (step_ms / 1e3) / PEAK_HBM,
-        "kernel_timing": f"HIP events around every kernel of 1 in {SAMPLE} decode steps and around every "
-                         "assignment kernel; value from events bracketing each pass's decode phase",
+        "kernel_timing": f"HIP events around every kernel of 1 in {SAMPLE} decode steps (passes launched step "
+                         "by step) and around every assignment kernel; value from events bracketing each pass's "
+                         "decode phase",
+        "decode_launch": "HIP graph of the pass's decode steps, replayed" if use_graph else "step by step",
         "wall_s_timed": wall,
         "roofline": roofline,
         "rooflines": rl,

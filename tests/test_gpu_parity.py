@@ -568,6 +568,58 @@ def test_selection_merge_and_full_ranking():
         assert np.abs(to_np(fout) - oracle.decode(q, w.G, K, V, osel, ocnt, scale)).max() <= 2e-3, B
 
 
+def test_graph_replay_matches_eager():
+    """The benchmark captures a pass's decode steps (append, then fused
+    selection and attention) in a HIP graph after a build and replays it after
+    each new build. Every replay, with eager builds and synchronisations
+    between replays, gives the eager run's outputs bit for bit."""
+    w = SMALL_APPEND
+    base, K, V, init, means = make_inputs(w)
+    H = K.shape[0]
+    idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w), packed=True)
+    Kc, Vc = K.copy(), V.copy()
+    Kc[:, w.L:], Vc[:, w.L:] = 0, 0
+    Kd, Vd = to_dev(Kc), to_dev(Vc)
+    initd = to_dev(init)
+    ws = torch.empty(kvc.build_workspace_bytes(H, w.L, w.C, w.iters), dtype=torch.uint8, device="cuda")
+    steps = 6
+    Knew = [to_dev(np.ascontiguousarray(K[:, w.L + s:w.L + s + 1])) for s in range(steps)]
+    Vnew = [to_dev(np.ascontiguousarray(V[:, w.L + s:w.L + s + 1])) for s in range(steps)]
+    Q = [to_dev(queries(w, base, s, K, w.L + s + 1, means)) for s in range(steps)]
+    outs = [torch.empty(H * w.G, w.d, dtype=torch.float32, device="cuda") for _ in range(steps)]
+    scale = 1.0 / math.sqrt(w.d)
+
+    def prepare():
+        kvc.build(idx, Kd, w.L, w.iters, initd, workspace=ws)
+        kvc.pack(idx, Kd, Vd)
+
+    def run():
+        for s in range(steps):
+            kvc.append(idx, Kd, Vd, Knew[s], Vnew[s])
+            kvc.select_decode(idx, Q[s], Kd, Vd, w.B, scale, out=outs[s])
+
+    prepare()
+    run()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs]
+    prepare()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        prepare()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for s in range(steps):
+            assert torch.equal(outs[s], want[s]), (rep, s)
+    say(f"  {steps} captured steps, 3 replays identical to the eager run")
+
+
 def test_init_index_out_of_range_flag():
     w = SMALL
     base, K, V, init, _ = make_inputs(w)
