@@ -123,18 +123,18 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restric
 // chunk c at c ^ (r & 15): the 16 rows one read instruction touches land in
 // distinct banks).
 //
-// Each lane keeps the best score, the tile-uniform part of its centroid id
-// and the runner-up score of each of its keys; the 4 lanes of a key merge at
-// the end. A score's register index within its tile (3 - r) replaces the two
-// low mantissa bits, so the running maximum carries its own index and the
-// fold costs a med3 and a max per score; that moves a value by at most 3 units
-// in the last place. The fp32 order is certified against the exact (fp64)
-// order when
+// Each lane keeps the best and the runner-up score of each of its keys; the
+// 4 lanes of a key merge at the end. A score's place in the tile loop, the
+// code ((31 - tile) << 2) | (3 - r), replaces its seven low mantissa bits, so
+// the running maximum carries its own centroid id and the fold costs one
+// v_and_or_b32 and two v_med3_f32 per score; that moves a value by at most
+// 127 units in the last place. The fp32 order is certified against the exact
+// (fp64) order when
 //   best - runner_up > 2 * 4 * (d + 16) * 2^-24 * ||K_i|| * max||chat_k|| * 1.02
-//                      + 2^-20 * |best|,
+//                      + 2^-15 * max(|best|, |runner_up|) * 1.02,
 // a bound on the error of any fp32 accumulation of d exact products (the
 // products of bf16 operands are exact) with a safety factor of 4, plus the
-// index bits. Keys that fail it are queued for exact re-scoring (fix-up
+// code bits. Keys that fail it are queued for exact re-scoring (fix-up
 // kernel below). Ties and near-ties therefore always resolve by the fp64
 // rule, lowest id first. Only the tiles that hold centroids are computed; a
 // partial last tile masks its padding rows.
@@ -149,19 +149,12 @@ constexpr int AS_WAVES = 12;
 constexpr int AS_THREADS = AS_WAVES * WAVE;
 constexpr int AS_TILE = AS_WAVES * 64;
 
-// Running best and runner-up of one lane's key over the 4 scores of a tile
-// (index bits already in place); i1 takes the tile's first centroid when the
-// best moves into this tile. max(m1, e) of finite scores is taken as
-// med3(m1, e, FLT_MAX): one instruction, with no canonicalisation of the
-// bit-built operand.
-__device__ __forceinline__ void top2_tile(const float (&e)[4], int u0, float& m1, float& m2, int& i1) {
-  const float before = m1;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m2 = __builtin_amdgcn_fmed3f(m1, m2, e[r]);
-    m1 = __builtin_amdgcn_fmed3f(m1, e[r], 3.40282347e38f);
-  }
-  i1 = m1 > before ? u0 : i1;
+// Running best and runner-up with one more score (code bits already in
+// place). max(m1, e) of finite scores is taken as med3(m1, e, FLT_MAX): one
+// instruction, with no canonicalisation of the bit-built operand.
+__device__ __forceinline__ void top2_push(float e, float& m1, float& m2) {
+  m2 = __builtin_amdgcn_fmed3f(m1, m2, e);
+  m1 = __builtin_amdgcn_fmed3f(m1, e, 3.40282347e38f);
 }
 
 template <int METRIC>
@@ -212,10 +205,15 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
 
   const uint16_t* Kh = keys + (size_t)h * head_stride + 8 * kb4;
   const int ngroups = (L + AS_TILE - 1) / AS_TILE;
+  // the and-mask of the code bits, held in a vector register so that one
+  // v_and_or_b32 (which reads a single scalar operand) takes it beside the
+  // scalar code
+  unsigned vmask;
+  asm volatile("v_mov_b32 %0, 0xffffff80" : "=v"(vmask));
   const int ntl = (C + 15) >> 4;          // tiles holding centroids
   const bool partial = (C & 15) != 0;     // the last of them holds padding rows
   const float gamma = 2.0f * 4.0f * (float)(D + 16) * 5.9604644775390625e-8f * 1.02f;
-  const float gbits = 9.5367431640625e-7f;  // 2^-20: the index bits of best and runner-up
+  const float gbits = 3.0517578125e-5f * 1.02f;  // 2^-15: the code bits of best and runner-up
   // variants: threshold = g2 * ((d + 17) * A * ||K_i|| + 2 max|b_k|)
   const float g2 = 2.0f * 4.0f * 5.9604644775390625e-8f * 1.02f;
   const float gA = g2 * (float)(D + 17) * normA, gB = g2 * 2.0f * biasM;
@@ -248,12 +246,10 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
       n2[T] = ss;
     }
     float m1[4], m2[4];
-    int i1[4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
       m1[T] = -INFINITY;
       m2[T] = -INFINITY;
-      i1[T] = 0;
     }
     // centroid tiles in a pipeline: while the products of tile ct + 1 run on
     // the matrix cores, the vector units fold tile ct into the running best
@@ -277,19 +273,20 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     };
     auto fold = [&](int ct, const f32x4 (&acc)[4], bool masked) {
       const int u0 = ct * 16;  // centroid of register r in this lane: u0 + 4 (lane / 16) + r
+      const unsigned tcode = (unsigned)(31 - ct) << 2;
       f32x4 bias = {0.f, 0.f, 0.f, 0.f};
       if constexpr (METRIC == M_L2) bias = *reinterpret_cast<const f32x4*>(sBias + u0 + 4 * kb4);
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        float e[4];
+      for (int r = 0; r < 4; ++r) {
+        const unsigned code = tcode | (unsigned)(3 - r);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int T = 0; T < 4; ++T) {
           float sc = acc[T][r];
           if constexpr (METRIC == M_L2) sc += bias[r];
-          e[r] = __uint_as_float((__float_as_uint(sc) & ~3u) | (unsigned)(3 - r));
-          if (masked && u0 + 4 * kb4 + r >= C) e[r] = -INFINITY;
+          float e = __uint_as_float((__float_as_uint(sc) & vmask) | code);
+          if (masked && u0 + 4 * kb4 + r >= C) e = -INFINITY;
+          top2_push(e, m1[T], m2[T]);
         }
-        top2_tile(e, u0, m1[T], m2[T], i1[T]);
       }
     };
     auto interleave = [&]() {
@@ -326,11 +323,13 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
       if (partial) fold(ct, accA, true);
       else fold(ct, accA, false);
     }
-    // full centroid ids (tile, lane group, index bits), then merge the 4 lanes
-    // of each key (lanes 16 apart) and certify
+    // centroid ids from the code bits (tile, register) and the lane group,
+    // then merge the 4 lanes of each key (lanes 16 apart) and certify
+    int i1[4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-      i1[T] += 4 * kb4 + 3 - (int)(__float_as_uint(m1[T]) & 3u);
+      const unsigned code = __float_as_uint(m1[T]) & 127u;
+      i1[T] = 16 * (31 - (int)(code >> 2)) + 4 * kb4 + 3 - (int)(code & 3u);
 #pragma unroll
       for (int m = 16; m <= 32; m <<= 1) {
         const float o1 = __shfl_xor(m1[T], m), o2 = __shfl_xor(m2[T], m);
@@ -351,7 +350,7 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
       if (T == kb4) {
         my_label = i1[T];
         const float thr = (METRIC == M_COSINE ? gamma * sqrtf(n2[T]) : gA * sqrtf(n2[T]) + gB) +
-                          gbits * fabsf(m1[T]);
+                          gbits * fmaxf(fabsf(m1[T]), fabsf(m2[T]));
         my_flag = !((m1[T] - m2[T]) > thr);  // true for NaN and ties
         my_m1 = m1[T];
         my_m2 = m2[T];
