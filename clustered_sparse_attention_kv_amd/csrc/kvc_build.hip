@@ -126,9 +126,11 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restric
 // Each lane keeps the best and the runner-up score of each of its keys; the
 // 4 lanes of a key merge at the end. A score's place in the tile loop, the
 // code ((31 - tile) << 2) | (3 - r), replaces its seven low mantissa bits, so
-// the running maximum carries its own centroid id and the fold costs one
-// v_and_or_b32 and two v_med3_f32 per score; that moves a value by at most
-// 127 units in the last place. The fp32 order is certified against the exact
+// the running maximum carries its own centroid id. Two scores fold at a time:
+// with best m1 >= runner-up m2, the top two of {m1, m2, e1, e2} are
+// max3(m1, e1, e2) and max(med3(m1, e1, e2), m2), so a score costs one
+// v_and_or_b32 and one and a half further instructions. The code moves a value
+// by at most 127 units in the last place. The fp32 order is certified against the exact
 // (fp64) order when
 //   best - runner_up > 2 * 4 * (d + 16) * 2^-24 * ||K_i|| * max||chat_k|| * 1.02
 //                      + 2^-15 * max(|best|, |runner_up|) * 1.02,
@@ -149,12 +151,16 @@ constexpr int AS_WAVES = 12;
 constexpr int AS_THREADS = AS_WAVES * WAVE;
 constexpr int AS_TILE = AS_WAVES * 64;
 
-// Running best and runner-up with one more score (code bits already in
-// place). max(m1, e) of finite scores is taken as med3(m1, e, FLT_MAX): one
-// instruction, with no canonicalisation of the bit-built operand.
-__device__ __forceinline__ void top2_push(float e, float& m1, float& m2) {
-  m2 = __builtin_amdgcn_fmed3f(m1, m2, e);
-  m1 = __builtin_amdgcn_fmed3f(m1, e, 3.40282347e38f);
+// Running best and runner-up with two more scores (code bits in place; all
+// values finite or -inf). The maximum of the bit-built operands is a plain
+// v_max3_f32: the compiler would otherwise canonicalise each operand first.
+// max(x, m2) of finite values is med3(x, m2, FLT_MAX).
+__device__ __forceinline__ void top2_push2(float e1, float e2, float& m1, float& m2) {
+  const float mid = __builtin_amdgcn_fmed3f(m1, e1, e2);
+  m2 = __builtin_amdgcn_fmed3f(mid, m2, 3.40282347e38f);
+  float mx;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(mx) : "v"(m1), "v"(e1), "v"(e2));
+  m1 = mx;
 }
 
 template <int METRIC>
@@ -277,16 +283,17 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
       f32x4 bias = {0.f, 0.f, 0.f, 0.f};
       if constexpr (METRIC == M_L2) bias = *reinterpret_cast<const f32x4*>(sBias + u0 + 4 * kb4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const unsigned code = tcode | (unsigned)(3 - r);
+      for (int T = 0; T < 4; ++T) {
+        float e[4];
 #pragma unroll
-        for (int T = 0; T < 4; ++T) {
+        for (int r = 0; r < 4; ++r) {
           float sc = acc[T][r];
           if constexpr (METRIC == M_L2) sc += bias[r];
-          float e = __uint_as_float((__float_as_uint(sc) & vmask) | code);
-          if (masked && u0 + 4 * kb4 + r >= C) e = -INFINITY;
-          top2_push(e, m1[T], m2[T]);
+          e[r] = __uint_as_float((__float_as_uint(sc) & vmask) | (tcode | (unsigned)(3 - r)));
+          if (masked && u0 + 4 * kb4 + r >= C) e[r] = -INFINITY;
         }
+        top2_push2(e[0], e[1], m1[T], m2[T]);
+        top2_push2(e[2], e[3], m1[T], m2[T]);
       }
     };
     auto interleave = [&]() {
