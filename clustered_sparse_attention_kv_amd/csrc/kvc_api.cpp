@@ -59,6 +59,7 @@ struct BuildWs {
   uint32_t* qcount;  // [iters, heads]
   int32_t* queue;    // [heads, L]
   int32_t* hist;     // [heads, nblk, C]
+  void* op_t;        // [heads, d / 8, cpad(C)] 16-byte chunks: the bf16 operand chunk-major
   size_t bytes;
 };
 
@@ -72,6 +73,8 @@ BuildWs carve_build(void* base, int heads, int L, int C, int iters) {
   o = align_up(o + sizeof(int32_t) * (size_t)heads * L);
   w.hist = reinterpret_cast<int32_t*>(b + o);
   o = align_up(o + sizeof(int32_t) * (size_t)heads * csr_blocks(L) * C);
+  w.op_t = b + o;
+  o = align_up(o + sizeof(uint16_t) * (size_t)heads * kv_cluster_cpad(C) * KVC_HEAD_DIM);
   w.bytes = o;
   return w;
 }
@@ -154,7 +157,7 @@ int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, c
   for (int t = 0; t < iters && e == hipSuccess; ++t) {
     hipEvent_t* ev = assign_events ? (hipEvent_t*)assign_events + 2 * t : nullptr;
     e = launch_assign(idx->dtype, keys_c, hs, H, Lc, idx->centroids_op, C, cpad, cps, idx->metric, idx->labels + ns,
-                      cap, w.queue, w.qcount + (size_t)t * H, nullptr, ev, st);
+                      cap, w.queue, w.qcount + (size_t)t * H, w.op_t, nullptr, ev, st);
     if (e == hipSuccess)
       e = launch_csr(idx->labels + ns, cap, H, Lc, C, cs, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, ns,
                      st);
@@ -182,7 +185,7 @@ int kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.qcount), (size_t)H, 0, st);
   if (e == hipSuccess)
     e = launch_assign(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, L, chat, C, cpad, cpad, idx->metric, labels,
-                      cap, w.queue, w.qcount, top2, nullptr, st);
+                      cap, w.queue, w.qcount, w.op_t, top2, nullptr, st);
   if (e == hipSuccess && flagged)
     e = hipMemcpyAsync(flagged, w.qcount, sizeof(int32_t) * H, hipMemcpyDeviceToDevice, st);
   return hip_status(e);
@@ -265,7 +268,7 @@ int kv_cluster_cluster_window(kvc_index* idx, const void* k_cache, const void* v
                               w.cent, w.cent_t, w.chat, idx->dev_flags, st);
   for (int t = 0; t < iters && e == hipSuccess; ++t) {
     e = launch_assign(idx->dtype, keys_w, hs, H, m, w.chat, nc, cpw, cpw, idx->metric, w.labels, m, w.b.queue,
-                      w.b.qcount + (size_t)t * H, nullptr, nullptr, st);
+                      w.b.qcount + (size_t)t * H, w.b.op_t, nullptr, nullptr, st);
     if (e == hipSuccess) e = launch_csr(w.labels, m, H, m, nc, nc, w.b.hist, w.sizes, w.offsets, w.ids, m, wlo, st);
     if (e == hipSuccess)
       e = launch_update(idx->dtype, k_cache, hs, H, nc, nc, cpw, idx->metric, w.sizes, w.offsets, w.ids, m, w.cent,

@@ -167,16 +167,21 @@ template <int METRIC>
 __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     const uint16_t* __restrict__ keys, long long head_stride, int L, const uint16_t* __restrict__ chat, int C,
     int cpad, int cps, int32_t* __restrict__ labels, long long label_stride, int32_t* __restrict__ queue,
-    uint32_t* __restrict__ qcount, float* __restrict__ top2) {
+    uint32_t* __restrict__ qcount, u32x4* __restrict__ op_t, float* __restrict__ top2) {
   extern __shared__ u32x4 sC[];  // cpad rows x 16 chunks of 16 B, chunk c of row r at c ^ (r & 15)
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j16 = lane & 15, kb4 = lane >> 4;
 
   const u32x4* Cg = reinterpret_cast<const u32x4*>(chat + (size_t)h * cps * D);
+  // block 0 of each head also stores the chunk-major copy [16][cpad] that the
+  // exact pass reads (rows of one chunk contiguous)
+  u32x4* Ot = blockIdx.x == 0 ? op_t + (size_t)h * 16 * cpad : nullptr;
   for (int e = tid; e < cpad * 16; e += AS_THREADS) {
     const int r = e >> 4, c = e & 15;
-    sC[r * 16 + (c ^ (r & 15))] = Cg[e];
+    const u32x4 v = Cg[e];
+    sC[r * 16 + (c ^ (r & 15))] = v;
+    if (Ot) Ot[(size_t)c * cpad + r] = v;
   }
   // variants: after the operand, the per-centroid bias (L2; cpad floats) and
   // the largest operand norm (one word), all in the dynamic allocation so the
@@ -388,109 +393,112 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
 // ---------------------------------------------------------------------------
 // a3 exact path: label_i = argmax_k of the fp64 chain sum_j K_ij * chat_kj over
 // ascending j, lowest k on ties. Used for keys the matrix-core pass could not
-// certify, and for every key of fp32 inputs. One wave per key; lane c owns
-// centroids c, c+64, ...; channel j of the key reaches every lane through
-// readlane (a scalar operand of the fp64 fma). Operand rows are read in
-// 16-byte chunks; for bf16 the head's operand is staged in LDS once per block
-// with the chunk index of row r XOR-ed by r (mod the chunk count), so the 64
-// lanes of a wave, reading 64 different rows at one chunk, spread over the
-// banks. Rows come from the per-head queue (queue != null) or are all rows.
-// Under the L2 distance the score is the chain minus nn_k / 2, nn_k the fp64
-// chain of chat_kj^2 over ascending j (computed once per block, kept in LDS
-// after the staged operand).
-template <typename KT, int MAXT>
-__global__ __launch_bounds__(256) void assign_exact_kernel(const KT* __restrict__ keys, long long head_stride, int L,
-                                                           const KT* __restrict__ chat, int C, int cpad, int cps,
-                                                           int metric, int32_t* __restrict__ labels,
-                                                           long long label_stride,
-                                                           const int32_t* __restrict__ queue,
-                                                           const uint32_t* __restrict__ qcount) {
-  constexpr bool STAGE = sizeof(KT) == 2;
+// certify, and for every key of fp32 inputs. One wave per block and EX_NK keys
+// per wave and pass; lane c owns centroids c, c+64, ... The wave's keys are
+// written to LDS in fp64 and every lane reads channel j of a key from the same
+// address (a broadcast, a vector operand of the fp64 fma). bf16 operands are
+// read from the chunk-major copy [d/8][cpad] of 16-byte chunks that the
+// matrix-core pass stores, so the 64 lanes' rows at one chunk are one
+// contiguous kilobyte; the next chunk's loads are issued before the current
+// chunk's arithmetic. fp32 operands are read row by row. Grid (heads, waves
+// per head): blocks go to the 8 XCDs round robin, so with a multiple of 8 heads
+// the waves of head h share one XCD, whose L2 holds that head's operand. Rows
+// come from the per-head queue (queue != null) or are all rows. Under the L2
+// distance (L2D) the score is the chain minus nn_k / 2, nn_k the fp64 chain of
+// chat_kj^2 over ascending j, accumulated beside the products.
+constexpr int EX_NK = 2;
+template <typename KT, int MAXT, bool L2D>
+__global__ __launch_bounds__(64) void assign_exact_kernel(const KT* __restrict__ keys, long long head_stride, int L,
+                                                          const KT* __restrict__ chat, int C, int cpad, int cps,
+                                                          int32_t* __restrict__ labels, long long label_stride,
+                                                          const int32_t* __restrict__ queue,
+                                                          const uint32_t* __restrict__ qcount,
+                                                          const u32x4* __restrict__ op_t) {
+  constexpr bool BF = sizeof(KT) == 2;
   constexpr int CHUNKS = D * (int)sizeof(KT) / 16;  // 16-byte chunks per operand row
   constexpr int EPC = 16 / (int)sizeof(KT);         // elements per chunk
-  constexpr int NK = 2;                             // keys per wave and pass
-  extern __shared__ u32x4 smem[];
-  const int h = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nw = gridDim.x * 4;
+  constexpr int NK = EX_NK;
+  __shared__ __align__(16) double kl[NK * D];
+  const int h = blockIdx.x, lane = threadIdx.x;
   const int n = queue ? (int)__atomic_load_n(qcount + h, __ATOMIC_RELAXED) : L;
-  if (blockIdx.x * 4 * NK >= n) return;  // no key for this block (uniform): nothing staged
+  if ((int)blockIdx.y * NK >= n) return;  // no key for this wave
   const KT* Kh = keys + (size_t)h * head_stride;
   const u32x4* Cg = reinterpret_cast<const u32x4*>(chat + (size_t)h * cps * D);
-  if constexpr (STAGE) {
-    for (int e = threadIdx.x; e < cpad * CHUNKS; e += 256) {
-      const int r = e / CHUNKS, c = e % CHUNKS;
-      smem[r * CHUNKS + (c ^ (r & (CHUNKS - 1)))] = Cg[e];
-    }
-  }
-  double* half_nn = reinterpret_cast<double*>(smem + (STAGE ? cpad * CHUNKS : 0));
-  if (metric == M_L2) {
-    for (int c = threadIdx.x; c < cpad; c += 256) {
-      double nn = 0.0;
-      for (int j = 0; j < D; ++j) {
-        const double x = (double)load_f32(chat + (size_t)h * cps * D, (size_t)c * D + j);
-        nn = fma(x, x, nn);
-      }
-      half_nn[c] = 0.5 * nn;
-    }
-  }
-  if (STAGE || metric == M_L2) __syncthreads();
+  const u32x4* Ct = BF ? op_t + (size_t)h * CHUNKS * cpad : nullptr;
   // lane's centroid rows; rows past cpad read the last (zero) padding row and
   // are excluded from the argmax, so no branch separates the chains
   int crow[MAXT];
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) crow[t] = min(lane + 64 * t, cpad - 1);
-  for (int e = gw * NK; e < n; e += nw * NK) {
+  auto load = [&](int q, int t) {
+    if constexpr (BF) return Ct[(size_t)q * cpad + crow[t]];
+    else return Cg[(size_t)crow[t] * CHUNKS + q];
+  };
+  for (int e = (int)blockIdx.y * NK; e < n; e += (int)gridDim.y * NK) {
     int row[NK];
-    double k0[NK], k1[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const int ee = min(e + kk, n - 1);
       row[kk] = queue ? queue[(size_t)h * L + ee] : ee;
-      k0[kk] = (double)load_f32(Kh, (size_t)row[kk] * D + lane);
-      k1[kk] = (double)load_f32(Kh, (size_t)row[kk] * D + 64 + lane);
     }
-    double s[NK][MAXT];
+    // the previous pass's reads of kl are done (one wave, in order) before
+    // these writes, and the writes before the reads below
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
+    for (int kk = 0; kk < NK; ++kk) {
+      kl[kk * D + lane] = (double)load_f32(Kh, (size_t)row[kk] * D + lane);
+      kl[kk * D + 64 + lane] = (double)load_f32(Kh, (size_t)row[kk] * D + 64 + lane);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    double s[NK][MAXT], nn[MAXT];
 #pragma unroll
-      for (int t = 0; t < MAXT; ++t) s[kk][t] = 0.0;
+    for (int t = 0; t < MAXT; ++t) {
+      nn[t] = 0.0;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) s[kk][t] = 0.0;
+    }
+    u32x4 cur[MAXT];
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) cur[t] = load(0, t);
 #pragma unroll 1
     for (int q = 0; q < CHUNKS; ++q) {
+      u32x4 nxt[MAXT];
+      if (q + 1 < CHUNKS)
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) nxt[t] = load(q + 1, t);
       double kj[NK][EPC];
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
-        for (int i = 0; i < EPC; ++i) {
-          const int j = q * EPC + i;
-          const double src = j < 64 ? k0[kk] : k1[kk];
-          const int lo = __builtin_amdgcn_readlane((int)(__double_as_longlong(src) & 0xFFFFFFFFll), j & 63);
-          const int hi = __builtin_amdgcn_readlane((int)(__double_as_longlong(src) >> 32), j & 63);
-          kj[kk][i] = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
+        for (int i = 0; i < EPC; i += 2) {
+          const double2 v = *reinterpret_cast<const double2*>(kl + kk * D + q * EPC + i);
+          kj[kk][i] = v.x;
+          kj[kk][i + 1] = v.y;
         }
 #pragma unroll
       for (int t = 0; t < MAXT; ++t) {
-        const int c = crow[t];
-        const u32x4 v = STAGE ? smem[c * CHUNKS + (q ^ (c & (CHUNKS - 1)))] : Cg[(size_t)c * CHUNKS + q];
 #pragma unroll
         for (int i = 0; i < EPC; ++i) {
           float x;
-          if constexpr (STAGE) x = (i & 1) ? __uint_as_float(v[i >> 1] & 0xFFFF0000u) : __uint_as_float(v[i >> 1] << 16);
-          else x = __uint_as_float(v[i]);
+          if constexpr (BF)
+            x = (i & 1) ? __uint_as_float(cur[t][i >> 1] & 0xFFFF0000u) : __uint_as_float(cur[t][i >> 1] << 16);
+          else
+            x = __uint_as_float(cur[t][i]);
           const double xd = (double)x;
 #pragma unroll
           for (int kk = 0; kk < NK; ++kk) s[kk][t] = fma(kj[kk][i], xd, s[kk][t]);
+          if constexpr (L2D) nn[t] = fma(xd, xd, nn[t]);
         }
       }
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t) cur[t] = nxt[t];
     }
-    if (metric == M_L2)
+    if constexpr (L2D)
 #pragma unroll
-      for (int t = 0; t < MAXT; ++t) {
-        const double hn = half_nn[crow[t]];
+      for (int t = 0; t < MAXT; ++t)
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) s[kk][t] = s[kk][t] - hn;
-      }
+        for (int kk = 0; kk < NK; ++kk) s[kk][t] = s[kk][t] - 0.5 * nn[t];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       double best = -INFINITY;
@@ -772,34 +780,30 @@ hipError_t launch_init_centroids(int dtype, const void* keys, long long head_str
   return hipGetLastError();
 }
 
-// The exact pass instantiated for the number of 64-centroid groups a lane owns.
+// The exact pass instantiated for the number of 64-centroid groups a lane owns
+// and the distance; grid (heads, waves per head).
 template <typename KT, int MAXT>
 hipError_t launch_exact_t(const KT* keys, long long head_stride, int L, const KT* chat, int C, int cpad, int cps,
                           int metric, int32_t* labels, long long label_stride, const int32_t* queue, const uint32_t* qcount,
-                          dim3 grid, size_t lds, hipStream_t st) {
-  if (lds > 64 * 1024) {
-    static bool attr = false;
-    if (!attr) {
-      const hipError_t e = hipFuncSetAttribute((const void*)assign_exact_kernel<KT, MAXT>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
-  }
-  assign_exact_kernel<KT, MAXT><<<grid, 256, lds, st>>>(keys, head_stride, L, chat, C, cpad, cps, metric, labels,
-                                                       label_stride, queue, qcount);
+                          const u32x4* op_t, dim3 grid, hipStream_t st) {
+  if (metric == M_L2)
+    assign_exact_kernel<KT, MAXT, true><<<grid, 64, 0, st>>>(keys, head_stride, L, chat, C, cpad, cps, labels,
+                                                             label_stride, queue, qcount, op_t);
+  else
+    assign_exact_kernel<KT, MAXT, false><<<grid, 64, 0, st>>>(keys, head_stride, L, chat, C, cpad, cps, labels,
+                                                              label_stride, queue, qcount, op_t);
   return hipGetLastError();
 }
 
 template <typename KT>
 hipError_t launch_exact(const KT* keys, long long head_stride, int L, const KT* chat, int C, int cpad, int cps,
                         int metric, int32_t* labels, long long label_stride, const int32_t* queue, const uint32_t* qcount,
-                        dim3 grid, size_t lds, hipStream_t st) {
+                        const u32x4* op_t, dim3 grid, hipStream_t st) {
   switch ((C + 63) / 64) {
 #define KVC_EXACT_CASE(T) \
   case T:                 \
     return launch_exact_t<KT, T>(keys, head_stride, L, chat, C, cpad, cps, metric, labels, label_stride, queue,  \
-                                 qcount, grid, lds, st);
+                                 qcount, op_t, grid, st);
     KVC_EXACT_CASE(1)
     KVC_EXACT_CASE(2)
     KVC_EXACT_CASE(3)
@@ -817,7 +821,7 @@ hipError_t launch_exact(const KT* keys, long long head_stride, int L, const KT* 
 template <int METRIC>
 static hipError_t launch_mfma_t(dim3 grid, size_t lds, const uint16_t* keys, long long head_stride, int L,
                                 const uint16_t* chat, int C, int cpad, int cps, int32_t* labels,
-                                long long label_stride, int32_t* queue, uint32_t* qcount, float* top2,
+                                long long label_stride, int32_t* queue, uint32_t* qcount, u32x4* op_t, float* top2,
                                 hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
@@ -827,15 +831,14 @@ static hipError_t launch_mfma_t(dim3 grid, size_t lds, const uint16_t* keys, lon
     attr_set = true;
   }
   assign_bf16_mfma_kernel<METRIC><<<grid, AS_THREADS, lds, st>>>(keys, head_stride, L, chat, C, cpad, cps, labels,
-                                                                 label_stride, queue, qcount, top2);
+                                                                 label_stride, queue, qcount, op_t, top2);
   return hipGetLastError();
 }
 
 hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
                          int cpad, int cps, int metric, int32_t* labels, long long label_stride, int32_t* queue,
-                         uint32_t* qcount, float* top2, hipEvent_t* events, hipStream_t st) {
-  // the exact pass keeps nn_k / 2 per centroid after the staged operand under L2
-  const size_t lds_nn = metric == M_L2 ? (size_t)cpad * 8 : 0;
+                         uint32_t* qcount, void* op_t, float* top2, hipEvent_t* events, hipStream_t st) {
+  u32x4* ot = static_cast<u32x4*>(op_t);
   if (dtype == DT_BF16) {
     const size_t lds = (size_t)cpad * D * 2;
     // about one block per compute unit; each walks over 512-key groups of one head
@@ -854,29 +857,30 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
     const size_t lds_var = lds + (size_t)cpad * 4 + 16;
     if (metric == M_L2)
       e = launch_mfma_t<M_L2>(grid, lds_var, kk, head_stride, L, cc, C, cpad, cps, labels, label_stride, queue,
-                              qcount, top2, st);
+                              qcount, ot, top2, st);
     else if (metric == M_IP)
       e = launch_mfma_t<M_IP>(grid, lds_var, kk, head_stride, L, cc, C, cpad, cps, labels, label_stride, queue,
-                              qcount, top2, st);
+                              qcount, ot, top2, st);
     else
       e = launch_mfma_t<M_COSINE>(grid, lds, kk, head_stride, L, cc, C, cpad, cps, labels, label_stride, queue,
-                                  qcount, top2, st);
+                                  qcount, ot, top2, st);
     if (e != hipSuccess) return e;
     if (events) {
       e = hipEventRecord(events[1], st);
       if (e != hipSuccess) return e;
     }
-    // exact re-scoring of the uncertified keys; blocks without work exit at once
+    // exact re-scoring of the uncertified keys: 64 waves per head (128 keys a
+    // pass); waves without a key exit at once
     return launch_exact<uint16_t>((const uint16_t*)keys, head_stride, L, (const uint16_t*)chat, C, cpad, cps, metric,
-                                  labels, label_stride, queue, qcount, dim3(4, heads), lds + lds_nn, st);
+                                  labels, label_stride, queue, qcount, ot, dim3(heads, 64), st);
   }
-  dim3 g2(grid1(L, 8) < 64 ? grid1(L, 8) : 64, heads);
+  dim3 g2(heads, grid1(L, EX_NK) < 512 ? grid1(L, EX_NK) : 512);
   if (events) {
     hipError_t e0 = hipEventRecord(events[0], st);
     if (e0 != hipSuccess) return e0;
   }
   hipError_t e = launch_exact<float>((const float*)keys, head_stride, L, (const float*)chat, C, cpad, cps, metric,
-                                     labels, label_stride, nullptr, nullptr, g2, lds_nn, st);
+                                     labels, label_stride, nullptr, nullptr, nullptr, g2, st);
   if (e == hipSuccess && events) e = hipEventRecord(events[1], st);
   return e;
 }
