@@ -60,6 +60,7 @@ struct BuildWs {
   int32_t* queue;    // [heads, L]
   int32_t* hist;     // [heads, nblk, C]
   void* op_t;        // [heads, d / 8, cpad(C)] 16-byte chunks: the bf16 operand chunk-major
+  int32_t* dirty;    // [iters, heads, C]: clusters a key entered or left in that iteration
   size_t bytes;
 };
 
@@ -75,6 +76,8 @@ BuildWs carve_build(void* base, int heads, int L, int C, int iters) {
   o = align_up(o + sizeof(int32_t) * (size_t)heads * csr_blocks(L) * C);
   w.op_t = b + o;
   o = align_up(o + sizeof(uint16_t) * (size_t)heads * kv_cluster_cpad(C) * KVC_HEAD_DIM);
+  w.dirty = reinterpret_cast<int32_t*>(b + o);
+  o = align_up(o + sizeof(int32_t) * (size_t)iters * heads * C);
   w.bytes = o;
   return w;
 }
@@ -149,6 +152,7 @@ int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, c
   const long long hs = (long long)cap * KVC_HEAD_DIM;
   idx->packed = 0;  // the index changes: any packed copy is stale
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.qcount), (size_t)iters * H, 0, st);
+  if (e == hipSuccess) e = launch_fill_i32(w.dirty, (size_t)iters * H * C, 0, st);
   if (e == hipSuccess) e = launch_fill_i32(idx->app_offsets, (size_t)H * (cs + 1), 0, st);
   if (e == hipSuccess) e = launch_fill2d_i32(idx->labels, H, cap, ns, -1, st);  // sinks: in no cluster
   if (e == hipSuccess)
@@ -156,14 +160,17 @@ int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, c
                               idx->centroids_t, idx->centroids_op, idx->dev_flags, st);
   for (int t = 0; t < iters && e == hipSuccess; ++t) {
     hipEvent_t* ev = assign_events ? (hipEvent_t*)assign_events + 2 * t : nullptr;
+    // from the second iteration on, the assignment marks the clusters keys
+    // entered or left and the update recomputes only those
+    int32_t* dirty = t == 0 ? nullptr : w.dirty + (size_t)t * H * C;
     e = launch_assign(idx->dtype, keys_c, hs, H, Lc, idx->centroids_op, C, cpad, cps, idx->metric, idx->labels + ns,
-                      cap, w.queue, w.qcount + (size_t)t * H, w.op_t, nullptr, ev, st);
+                      cap, w.queue, w.qcount + (size_t)t * H, w.op_t, dirty, nullptr, ev, st);
     if (e == hipSuccess)
       e = launch_csr(idx->labels + ns, cap, H, Lc, C, cs, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, ns,
                      st);
     if (e == hipSuccess)
       e = launch_update(idx->dtype, keys, hs, H, C, cs, cps, idx->metric, idx->sizes, idx->offsets, idx->token_ids,
-                        cap, idx->centroids, idx->centroids_t, idx->centroids_op, st);
+                        cap, idx->centroids, idx->centroids_t, idx->centroids_op, dirty, st);
   }
   if (e != hipSuccess) return KVC_ERR_HIP;
   idx->n_build = L;
@@ -185,7 +192,7 @@ int kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.qcount), (size_t)H, 0, st);
   if (e == hipSuccess)
     e = launch_assign(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, L, chat, C, cpad, cpad, idx->metric, labels,
-                      cap, w.queue, w.qcount, w.op_t, top2, nullptr, st);
+                      cap, w.queue, w.qcount, w.op_t, nullptr, top2, nullptr, st);
   if (e == hipSuccess && flagged)
     e = hipMemcpyAsync(flagged, w.qcount, sizeof(int32_t) * H, hipMemcpyDeviceToDevice, st);
   return hip_status(e);
@@ -205,7 +212,8 @@ int kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, s
       launch_csr(idx->labels, cap, H, L, C, cs, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, 0, st);
   if (e == hipSuccess)
     e = launch_update(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, C, cs, cps, idx->metric, idx->sizes,
-                      idx->offsets, idx->token_ids, cap, idx->centroids, idx->centroids_t, idx->centroids_op, st);
+                      idx->offsets, idx->token_ids, cap, idx->centroids, idx->centroids_t, idx->centroids_op, nullptr,
+                      st);
   return hip_status(e);
 }
 
@@ -268,11 +276,11 @@ int kv_cluster_cluster_window(kvc_index* idx, const void* k_cache, const void* v
                               w.cent, w.cent_t, w.chat, idx->dev_flags, st);
   for (int t = 0; t < iters && e == hipSuccess; ++t) {
     e = launch_assign(idx->dtype, keys_w, hs, H, m, w.chat, nc, cpw, cpw, idx->metric, w.labels, m, w.b.queue,
-                      w.b.qcount + (size_t)t * H, w.b.op_t, nullptr, nullptr, st);
+                      w.b.qcount + (size_t)t * H, w.b.op_t, nullptr, nullptr, nullptr, st);
     if (e == hipSuccess) e = launch_csr(w.labels, m, H, m, nc, nc, w.b.hist, w.sizes, w.offsets, w.ids, m, wlo, st);
     if (e == hipSuccess)
       e = launch_update(idx->dtype, k_cache, hs, H, nc, nc, cpw, idx->metric, w.sizes, w.offsets, w.ids, m, w.cent,
-                        w.cent_t, w.chat, st);
+                        w.cent_t, w.chat, nullptr, st);
   }
   if (e == hipSuccess)
     e = launch_merge_window(idx->dtype, H, nc, m, wlo, w.cent, w.chat, w.labels, w.sizes, w.offsets, w.ids, ca, cs, cps,

@@ -147,6 +147,15 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restric
 // certificate uses the head's largest operand norm A and largest |b_k|:
 //   best - runner_up > 2 * 4 * 2^-24 * ((d + 17) * ||K_i|| * A + 2 max|b_k|) * 1.02,
 // which also covers the rounding of b_k and of the addition.
+// A key that changed cluster marks both clusters (flags per head, C of them;
+// old is the previous iteration's label, anything outside [0, C) is skipped):
+// the update recomputes only marked clusters, since a cluster whose member set
+// is unchanged gets the same centroid from the same ascending chain.
+__device__ __forceinline__ void mark_moved(int32_t* flags, int C, int old_label, int new_label) {
+  if ((unsigned)old_label < (unsigned)C) flags[old_label] = 1;
+  flags[new_label] = 1;
+}
+
 constexpr int AS_WAVES = 12;
 constexpr int AS_THREADS = AS_WAVES * WAVE;
 constexpr int AS_TILE = AS_WAVES * 64;
@@ -167,7 +176,7 @@ template <int METRIC>
 __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     const uint16_t* __restrict__ keys, long long head_stride, int L, const uint16_t* __restrict__ chat, int C,
     int cpad, int cps, int32_t* __restrict__ labels, long long label_stride, int32_t* __restrict__ queue,
-    uint32_t* __restrict__ qcount, u32x4* __restrict__ op_t, float* __restrict__ top2) {
+    uint32_t* __restrict__ qcount, u32x4* __restrict__ op_t, int32_t* __restrict__ dirty, float* __restrict__ top2) {
   extern __shared__ u32x4 sC[];  // cpad rows x 16 chunks of 16 B, chunk c of row r at c ^ (r & 15)
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -230,6 +239,9 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
   const float gA = g2 * (float)(D + 17) * normA, gB = g2 * 2.0f * biasM;
   for (int grpi = blockIdx.x; grpi < ngroups; grpi += gridDim.x) {
     const int row0 = grpi * AS_TILE + wave * 64;
+    // the label this lane's key had after the previous iteration, read early
+    const int prow = row0 + kb4 * 16 + j16;
+    const int old_label = dirty && prow < L ? labels[(size_t)h * label_stride + prow] : -1;
     u32x4 kn[4][4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
@@ -367,10 +379,14 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
         my_m1 = m1[T];
         my_m2 = m2[T];
       }
-    const int row = row0 + kb4 * 16 + j16;
+    const int row = prow;
     const bool valid = row < L;
     if (valid) {
-      labels[(size_t)h * label_stride + row] = my_label;
+      // a queued key's label is written by the exact pass, which also marks it
+      if (!my_flag) {
+        labels[(size_t)h * label_stride + row] = my_label;
+        if (dirty && old_label != my_label) mark_moved(dirty + (size_t)h * C, C, old_label, my_label);
+      }
       if (top2) {
         top2[((size_t)h * L + row) * 2] = my_m1;
         top2[((size_t)h * L + row) * 2 + 1] = my_m2;
@@ -413,7 +429,8 @@ __global__ __launch_bounds__(64) void assign_exact_kernel(const KT* __restrict__
                                                           int32_t* __restrict__ labels, long long label_stride,
                                                           const int32_t* __restrict__ queue,
                                                           const uint32_t* __restrict__ qcount,
-                                                          const u32x4* __restrict__ op_t) {
+                                                          const u32x4* __restrict__ op_t,
+                                                          int32_t* __restrict__ dirty) {
   constexpr bool BF = sizeof(KT) == 2;
   constexpr int CHUNKS = D * (int)sizeof(KT) / 16;  // 16-byte chunks per operand row
   constexpr int EPC = 16 / (int)sizeof(KT);         // elements per chunk
@@ -521,7 +538,14 @@ __global__ __launch_bounds__(64) void assign_exact_kernel(const KT* __restrict__
           bi = oi;
         }
       }
-      if (lane == 0 && e + kk < n) labels[(size_t)h * label_stride + row[kk]] = bi;
+      if (lane == 0 && e + kk < n) {
+        int32_t* lp = labels + (size_t)h * label_stride + row[kk];
+        if (dirty) {
+          const int old_label = *lp;
+          if (old_label != bi) mark_moved(dirty + (size_t)h * C, C, old_label, bi);
+        }
+        *lp = bi;
+      }
     }
   }
 }
@@ -652,13 +676,15 @@ __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ token_ids, long long ids_stride,
                                                      float* __restrict__ cent, float* __restrict__ cent_t,
-                                                     KT* __restrict__ chat) {
+                                                     KT* __restrict__ chat, const int32_t* __restrict__ dirty) {
   constexpr int GR = UpdRow<KT>::GROUP;
   __shared__ float rows[4][D];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.y;
   const int k = blockIdx.x * 4 + w;
   if (k >= C) return;
+  // with flags, a cluster no key entered or left keeps its centroid as it is
+  if (dirty && __builtin_amdgcn_readfirstlane(dirty[(size_t)h * C + k]) == 0) return;
   // the same value in every lane: scalar registers, uniform branches
   const int n = __builtin_amdgcn_readfirstlane(sizes[(size_t)h * cs + k]);
   const int off = __builtin_amdgcn_readfirstlane(offsets[(size_t)h * (cs + 1) + k]);
@@ -785,25 +811,25 @@ hipError_t launch_init_centroids(int dtype, const void* keys, long long head_str
 template <typename KT, int MAXT>
 hipError_t launch_exact_t(const KT* keys, long long head_stride, int L, const KT* chat, int C, int cpad, int cps,
                           int metric, int32_t* labels, long long label_stride, const int32_t* queue, const uint32_t* qcount,
-                          const u32x4* op_t, dim3 grid, hipStream_t st) {
+                          const u32x4* op_t, int32_t* dirty, dim3 grid, hipStream_t st) {
   if (metric == M_L2)
     assign_exact_kernel<KT, MAXT, true><<<grid, 64, 0, st>>>(keys, head_stride, L, chat, C, cpad, cps, labels,
-                                                             label_stride, queue, qcount, op_t);
+                                                             label_stride, queue, qcount, op_t, dirty);
   else
     assign_exact_kernel<KT, MAXT, false><<<grid, 64, 0, st>>>(keys, head_stride, L, chat, C, cpad, cps, labels,
-                                                              label_stride, queue, qcount, op_t);
+                                                              label_stride, queue, qcount, op_t, dirty);
   return hipGetLastError();
 }
 
 template <typename KT>
 hipError_t launch_exact(const KT* keys, long long head_stride, int L, const KT* chat, int C, int cpad, int cps,
                         int metric, int32_t* labels, long long label_stride, const int32_t* queue, const uint32_t* qcount,
-                        const u32x4* op_t, dim3 grid, hipStream_t st) {
+                        const u32x4* op_t, int32_t* dirty, dim3 grid, hipStream_t st) {
   switch ((C + 63) / 64) {
 #define KVC_EXACT_CASE(T) \
   case T:                 \
     return launch_exact_t<KT, T>(keys, head_stride, L, chat, C, cpad, cps, metric, labels, label_stride, queue,  \
-                                 qcount, op_t, grid, st);
+                                 qcount, op_t, dirty, grid, st);
     KVC_EXACT_CASE(1)
     KVC_EXACT_CASE(2)
     KVC_EXACT_CASE(3)
@@ -821,8 +847,8 @@ hipError_t launch_exact(const KT* keys, long long head_stride, int L, const KT* 
 template <int METRIC>
 static hipError_t launch_mfma_t(dim3 grid, size_t lds, const uint16_t* keys, long long head_stride, int L,
                                 const uint16_t* chat, int C, int cpad, int cps, int32_t* labels,
-                                long long label_stride, int32_t* queue, uint32_t* qcount, u32x4* op_t, float* top2,
-                                hipStream_t st) {
+                                long long label_stride, int32_t* queue, uint32_t* qcount, u32x4* op_t,
+                                int32_t* dirty, float* top2, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)assign_bf16_mfma_kernel<METRIC>,
@@ -831,13 +857,14 @@ static hipError_t launch_mfma_t(dim3 grid, size_t lds, const uint16_t* keys, lon
     attr_set = true;
   }
   assign_bf16_mfma_kernel<METRIC><<<grid, AS_THREADS, lds, st>>>(keys, head_stride, L, chat, C, cpad, cps, labels,
-                                                                 label_stride, queue, qcount, op_t, top2);
+                                                                 label_stride, queue, qcount, op_t, dirty, top2);
   return hipGetLastError();
 }
 
 hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
                          int cpad, int cps, int metric, int32_t* labels, long long label_stride, int32_t* queue,
-                         uint32_t* qcount, void* op_t, float* top2, hipEvent_t* events, hipStream_t st) {
+                         uint32_t* qcount, void* op_t, int32_t* dirty, float* top2, hipEvent_t* events,
+                         hipStream_t st) {
   u32x4* ot = static_cast<u32x4*>(op_t);
   if (dtype == DT_BF16) {
     const size_t lds = (size_t)cpad * D * 2;
@@ -857,13 +884,13 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
     const size_t lds_var = lds + (size_t)cpad * 4 + 16;
     if (metric == M_L2)
       e = launch_mfma_t<M_L2>(grid, lds_var, kk, head_stride, L, cc, C, cpad, cps, labels, label_stride, queue,
-                              qcount, ot, top2, st);
+                              qcount, ot, dirty, top2, st);
     else if (metric == M_IP)
       e = launch_mfma_t<M_IP>(grid, lds_var, kk, head_stride, L, cc, C, cpad, cps, labels, label_stride, queue,
-                              qcount, ot, top2, st);
+                              qcount, ot, dirty, top2, st);
     else
       e = launch_mfma_t<M_COSINE>(grid, lds, kk, head_stride, L, cc, C, cpad, cps, labels, label_stride, queue,
-                                  qcount, ot, top2, st);
+                                  qcount, ot, dirty, top2, st);
     if (e != hipSuccess) return e;
     if (events) {
       e = hipEventRecord(events[1], st);
@@ -872,7 +899,7 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
     // exact re-scoring of the uncertified keys: 64 waves per head (128 keys a
     // pass); waves without a key exit at once
     return launch_exact<uint16_t>((const uint16_t*)keys, head_stride, L, (const uint16_t*)chat, C, cpad, cps, metric,
-                                  labels, label_stride, queue, qcount, ot, dim3(heads, 64), st);
+                                  labels, label_stride, queue, qcount, ot, dirty, dim3(heads, 64), st);
   }
   dim3 g2(heads, grid1(L, EX_NK) < 512 ? grid1(L, EX_NK) : 512);
   if (events) {
@@ -880,7 +907,7 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
     if (e0 != hipSuccess) return e0;
   }
   hipError_t e = launch_exact<float>((const float*)keys, head_stride, L, (const float*)chat, C, cpad, cps, metric,
-                                     labels, label_stride, nullptr, nullptr, nullptr, g2, st);
+                                     labels, label_stride, nullptr, nullptr, nullptr, dirty, g2, st);
   if (e == hipSuccess && events) e = hipEventRecord(events[1], st);
   return e;
 }
@@ -902,14 +929,14 @@ hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, 
 
 hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cs, int cps,
                          int metric, const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
-                         float* cent, float* cent_t, void* chat, hipStream_t st) {
+                         float* cent, float* cent_t, void* chat, const int32_t* dirty, hipStream_t st) {
   dim3 grid(grid1(C, 4), heads);
   if (dtype == DT_BF16)
     update_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)keys, head_stride, C, cs, cps, metric, sizes,
-                                                  offsets, token_ids, ids_stride, cent, cent_t, (uint16_t*)chat);
+                                                  offsets, token_ids, ids_stride, cent, cent_t, (uint16_t*)chat, dirty);
   else
     update_kernel<float><<<grid, 256, 0, st>>>((const float*)keys, head_stride, C, cs, cps, metric, sizes, offsets,
-                                               token_ids, ids_stride, cent, cent_t, (float*)chat);
+                                               token_ids, ids_stride, cent, cent_t, (float*)chat, dirty);
   return hipGetLastError();
 }
 

@@ -31,14 +31,15 @@ hipError_t launch_init_centroids(int dtype, const void* keys, long long head_str
                                  float* cent_t, void* chat, int32_t* flags, hipStream_t st);
 hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
                          int cpad, int cps, int metric, int32_t* labels, long long label_stride, int32_t* queue,
-                         uint32_t* qcount, void* op_t, float* top2, hipEvent_t* events, hipStream_t st);
+                         uint32_t* qcount, void* op_t, int32_t* dirty, float* top2, hipEvent_t* events,
+                         hipStream_t st);
 hipError_t launch_fill2d_i32(int32_t* p, int rows, long long stride, int cols, int value, hipStream_t st);
 hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, int L, int C, int cs, int32_t* hist,
                       int32_t* sizes, int32_t* offsets, int32_t* token_ids, long long ids_stride, int id_base,
                       hipStream_t st);
 hipError_t launch_update(int dtype, const void* keys, long long head_stride, int heads, int C, int cs, int cps,
                          int metric, const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids, long long ids_stride,
-                         float* cent, float* cent_t, void* chat, hipStream_t st);
+                         float* cent, float* cent_t, void* chat, const int32_t* dirty, hipStream_t st);
 // Moves the window's clustering (nc clusters of the m tokens wlo .. wlo+m-1,
 // in arrays of stride nc / cpad(nc) / m per head) into the index as clusters
 // ca .. ca+nc-1.
