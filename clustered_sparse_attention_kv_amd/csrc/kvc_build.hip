@@ -553,12 +553,17 @@ __global__ __launch_bounds__(64) void assign_exact_kernel(const KT* __restrict__
 // ---------------------------------------------------------------------------
 // a5: stable counting sort of labels into the cluster index.
 // Blocks of CS_BLOCK tokens. count: per-block histograms. scan: per cluster
-// the exclusive prefix over blocks (block bases), sizes, and offsets as the
-// exclusive prefix of sizes over clusters. scatter: within a block, each
-// wave's histogram gives the wave bases; inside a wave the rank of a lane
-// among lower lanes of the same label comes from matching label bits with
-// ballots. Position = block base + wave base + rank keeps token order.
-constexpr int CS_BLOCK = 1024;
+// the exclusive prefix over blocks (block bases within the cluster), sizes,
+// and offsets as the exclusive prefix of sizes over clusters. scatter: wave w
+// of a block owns CS_BLOCK / 16 consecutive tokens, walked in chunks of 64 in
+// token order; the waves' histograms give each wave's base per cluster (after
+// the cluster offset and the block base), a lane's rank among lower lanes of
+// the same label in its chunk comes from matching label bits with ballots, and
+// the last lane of each label in a chunk advances the wave's running position.
+// Position = offset + block base + wave base + earlier chunks + rank keeps
+// token order.
+constexpr int CS_BLOCK = 4096;
+constexpr int CS_THREADS = 1024;
 
 __global__ __launch_bounds__(256) void csr_count_kernel(const int32_t* __restrict__ labels, long long label_stride,
                                                         int L, int C, int nblk, int32_t* __restrict__ hist) {
@@ -575,15 +580,22 @@ __global__ __launch_bounds__(256) void csr_count_kernel(const int32_t* __restric
 
 __global__ __launch_bounds__(512) void csr_scan_kernel(int C, int cs, int nblk, int32_t* __restrict__ hist,
                                                        int32_t* __restrict__ sizes, int32_t* __restrict__ offsets) {
+  constexpr int U = 16;  // block counts requested together
   __shared__ int sc[512];
   const int h = blockIdx.x, c = threadIdx.x;
   int32_t* hh = hist + (size_t)h * nblk * C;
   int run = 0;
   if (c < C) {
-    for (int b = 0; b < nblk; ++b) {
-      const int v = hh[(size_t)b * C + c];
-      hh[(size_t)b * C + c] = run;
-      run += v;
+    for (int b0 = 0; b0 < nblk; b0 += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = b0 + u < nblk ? hh[(size_t)(b0 + u) * C + c] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (b0 + u < nblk) {
+          hh[(size_t)(b0 + u) * C + c] = run;
+          run += v[u];
+        }
     }
     sizes[(size_t)h * cs + c] = run;
   }
@@ -596,49 +608,65 @@ __global__ __launch_bounds__(512) void csr_scan_kernel(int C, int cs, int nblk, 
     sc[c] += v;
     __syncthreads();
   }
-  const int excl = sc[c] - (c < C ? run : 0);
-  if (c < C) {
-    offsets[(size_t)h * (cs + 1) + c] = excl;
-    for (int b = 0; b < nblk; ++b) hh[(size_t)b * C + c] += excl;
-  }
+  if (c < C) offsets[(size_t)h * (cs + 1) + c] = sc[c] - run;
   if (c == C - 1) offsets[(size_t)h * (cs + 1) + C] = sc[c];
 }
 
-__global__ __launch_bounds__(CS_BLOCK) void csr_scatter_kernel(const int32_t* __restrict__ labels,
-                                                               long long label_stride, int L, int C, int nblk,
-                                                               const int32_t* __restrict__ hist,
-                                                               int32_t* __restrict__ token_ids, long long ids_stride,
-                                                               int id_base) {
-  constexpr int NW = CS_BLOCK / WAVE;
+__global__ __launch_bounds__(CS_THREADS) void csr_scatter_kernel(const int32_t* __restrict__ labels,
+                                                                 long long label_stride, int L, int C, int cs,
+                                                                 int nblk, const int32_t* __restrict__ hist,
+                                                                 const int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ token_ids,
+                                                                 long long ids_stride, int id_base) {
+  constexpr int NW = CS_THREADS / WAVE;
+  constexpr int PER = CS_BLOCK / CS_THREADS;  // chunks of 64 tokens per wave
   __shared__ int wh[NW][512];
   const int h = blockIdx.y, b = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  for (int e = tid; e < NW * 512; e += CS_BLOCK) (&wh[0][0])[e] = 0;
+  for (int e = tid; e < NW * 512; e += CS_THREADS) (&wh[0][0])[e] = 0;
+  const int t0 = b * CS_BLOCK + w * (PER * WAVE) + lane;
+  int lab[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = t0 + u * WAVE;
+    lab[u] = i < L ? labels[(size_t)h * label_stride + i] : -1;
+  }
   __syncthreads();
-  const int i = b * CS_BLOCK + tid;
-  const int lab = i < L ? labels[(size_t)h * label_stride + i] : -1;
-  if (lab >= 0) atomicAdd(&wh[w][lab], 1);
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (lab[u] >= 0) atomicAdd(&wh[w][lab[u]], 1);
   __syncthreads();
+  // per cluster: the cluster's offset plus the block base, then the waves in order
   const int32_t* base = hist + ((size_t)h * nblk + b) * C;
-  for (int c = tid; c < C; c += CS_BLOCK) {
-    int run = base[c];
+  for (int c = tid; c < C; c += CS_THREADS) {
+    int run = base[c] + offsets[(size_t)h * (cs + 1) + c];
+    int t[NW];
+#pragma unroll
+    for (int v = 0; v < NW; ++v) t[v] = wh[v][c];
+#pragma unroll
     for (int v = 0; v < NW; ++v) {
-      const int t = wh[v][c];
       wh[v][c] = run;
-      run += t;
+      run += t[v];
     }
   }
   __syncthreads();
-  unsigned long long same = __ballot(lab >= 0);
   const int nbits = 32 - __clz(C > 1 ? C - 1 : 1);
-  for (int bit = 0; bit < nbits; ++bit) {
-    const bool set = lab >= 0 && ((lab >> bit) & 1);
-    const unsigned long long bal = __ballot(set);
-    same &= set ? bal : ~bal;
-  }
-  if (lab >= 0) {
-    const int rank = __popcll(same & ((1ull << lane) - 1ull));
-    token_ids[(size_t)h * ids_stride + wh[w][lab] + rank] = id_base + i;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int l = lab[u];
+    unsigned long long same = __ballot(l >= 0);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = l >= 0 && ((l >> bit) & 1);
+      const unsigned long long bal = __ballot(set);
+      same &= set ? bal : ~bal;
+    }
+    if (l >= 0) {
+      // every lane reads the running position before the last lane of its
+      // label moves it (one wave; LDS operations in program order)
+      const int pos = wh[w][l] + __popcll(same & ((1ull << lane) - 1ull));
+      token_ids[(size_t)h * ids_stride + pos] = id_base + t0 + u * WAVE;
+      if ((same >> lane) == 1ull) wh[w][l] = pos + 1;
+    }
   }
 }
 
@@ -922,8 +950,8 @@ hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, 
   csr_scan_kernel<<<heads, 512, 0, st>>>(C, cs, nblk, hist, sizes, offsets);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  csr_scatter_kernel<<<dim3(nblk, heads), CS_BLOCK, 0, st>>>(labels, label_stride, L, C, nblk, hist, token_ids,
-                                                             ids_stride, id_base);
+  csr_scatter_kernel<<<dim3(nblk, heads), CS_THREADS, 0, st>>>(labels, label_stride, L, C, cs, nblk, hist, offsets,
+                                                               token_ids, ids_stride, id_base);
   return hipGetLastError();
 }
 
