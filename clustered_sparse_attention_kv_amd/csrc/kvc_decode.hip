@@ -166,8 +166,15 @@ __global__ __launch_bounds__(256) void window_append_kernel(KT* __restrict__ kc,
 // a7-a9: selection, computed by one block of 512 threads per KV head (C <= 512).
 //  1. qbar_j = fp64 sum over the head's G query heads (ascending g).
 //  2. score_k = fp64 chain qbar . c_k over ascending j; thread k owns cluster k.
-//  3. Bitonic sort of (score, k) into (score descending, k ascending) order;
-//     strides below 64 exchange through wave shuffles, larger ones through LDS.
+//  3. Order (score, k) by score descending, k ascending. Only clusters that
+//     can be selected need an order: a histogram of the scores (256 equal bins
+//     between the lowest and the highest, each cluster counted with its size)
+//     gives the bin where the size summed from the top first reaches the
+//     budget left for clusters (B less the sinks and the window); the clusters
+//     in that bin and above are the candidates, every other one ranks below
+//     them. Up to 64 candidates are sorted by one wave (bitonic, wave
+//     shuffles only); more fall back to a bitonic sort of all 512 entries,
+//     strides below 64 through wave shuffles, larger ones through LDS.
 //  4. Exclusive prefix W_r of sizes in rank order: rank r starts at W_r.
 //  5. Output position p < min(B, N) belongs to the last rank r with W_r <= p
 //     and takes member p - W_r of that cluster (built part, then appended
@@ -187,6 +194,11 @@ struct SelShared {
   int mn[SEL_THREADS], mo[SEL_THREADS], mb[SEL_THREADS], ma[SEL_THREADS];  // per cluster k: size, offset, built, app offset
   int wsum[SEL_THREADS / WAVE];
   int total;
+  double wlo[SEL_THREADS / WAVE], whi[SEL_THREADS / WAVE];  // per wave: lowest and highest score
+  int hist[256];                                            // cluster sizes per score bin
+  unsigned long long ckey[WAVE];                            // candidates (any order)
+  int cid[WAVE];
+  int ncand, bstar;
 };
 
 // Value of lane (lane ^ S) within the wave: DPP quad permutes for S = 1, 2,
@@ -241,8 +253,8 @@ __device__ __forceinline__ void bitonic_sort(Sh& S, unsigned long long& key, int
 // contiguous. The chain still runs over ascending j.
 // Returns the cluster id of rank tid (ids >= X.ca are padding).
 template <typename QT>
-__device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__ q, int G, const IndexView& X,
-                                            int h) {
+__device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__ q, int G, const IndexView& X, int h,
+                                            int B) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int C = X.ca, cs = X.cs;
   if (tid < C) {  // per-cluster metadata, read while the scores are computed
@@ -257,12 +269,14 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
     for (int g = 0; g < G; ++g) s = s + (double)load_f32(q, ((size_t)h * G + g) * D + tid);
     S.qbar[tid] = s;
   }
+  if (tid < 256) S.hist[tid] = 0;
+  if (tid == 0) S.ncand = 0;
   __syncthreads();
   unsigned long long key = 0;
   int id = C + tid;  // padding entries: worst key, distinct ids past the clusters
+  double sc = 0.0;
   if (tid < C) {
     const f32x4* ct = reinterpret_cast<const f32x4*>(X.cent_t + (size_t)h * cs * D) + tid;
-    double s = 0.0;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       f32x4 v[16];
@@ -271,12 +285,109 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s = fma(S.qbar[half * 64 + 4 * jj + i], (double)v[jj][i], s);
+        for (int i = 0; i < 4; ++i) sc = fma(S.qbar[half * 64 + 4 * jj + i], (double)v[jj][i], sc);
     }
-    key = ordered_key(s);
+    key = ordered_key(sc);
     id = tid;
   }
-  // bitonic sort, best first ("better" = larger key, then smaller id)
+  // lowest and highest score of the head
+  {
+    double lo = tid < C ? sc : INFINITY, hi = tid < C ? sc : -INFINITY;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      lo = fmin(lo, __shfl_xor(lo, off));
+      hi = fmax(hi, __shfl_xor(hi, off));
+    }
+    if (lane == 0) {
+      S.wlo[w] = lo;
+      S.whi[w] = hi;
+    }
+  }
+  __syncthreads();
+  double smin = S.wlo[0], smax = S.whi[0];
+#pragma unroll
+  for (int v = 1; v < SEL_THREADS / WAVE; ++v) {
+    smin = fmin(smin, S.wlo[v]);
+    smax = fmax(smax, S.whi[v]);
+  }
+  // bin of each cluster: monotone in the score (rounding is monotone)
+  int bin = 0;
+  if (tid < C && smax > smin) {
+    const double x = (sc - smin) * (256.0 / (smax - smin));
+    bin = x >= 255.0 ? 255 : (int)x;
+  }
+  if (tid < C && S.mn[tid] > 0) atomicAdd(&S.hist[bin], S.mn[tid]);
+  __syncthreads();
+  const int bc = B - X.n_sink - X.nw;  // entries left for clusters
+  if (w == 0) {
+    // size in bins >= b for lane's bins 4 lane .. 4 lane + 3; b* = the highest
+    // bin whose sum reaches bc (all bins when the clusters hold fewer)
+    int hb[4], t = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hb[i] = S.hist[4 * lane + i];
+      t += hb[i];
+    }
+    int above = t;  // inclusive suffix over lanes, then exclusive
+#pragma unroll
+    for (int off = 1; off < WAVE; off <<= 1) {
+      const int y = __shfl_down(above, off);
+      if (lane + off < WAVE) above += y;
+    }
+    above -= t;
+    int nq = 0, suf = above;
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      suf += hb[i];
+      nq += suf >= bc ? 1 : 0;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) nq += __shfl_xor(nq, off);
+    if (lane == 0) S.bstar = bc <= 0 ? 256 : (nq > 0 ? nq - 1 : 0);
+  }
+  __syncthreads();
+  if (tid < C && bin >= S.bstar) {
+    const int slot = atomicAdd(&S.ncand, 1);
+    if (slot < WAVE) {
+      S.ckey[slot] = key;
+      S.cid[slot] = id;
+    }
+  }
+  __syncthreads();
+  const int ncand = S.ncand;
+  if (ncand <= WAVE) {
+    // one wave orders the candidates; every other rank is padding
+    int fid = C + tid;
+    if (w == 0) {
+      unsigned long long k2 = lane < ncand ? S.ckey[lane] : 0ull;
+      int i2 = lane < ncand ? S.cid[lane] : C + lane;
+      bitonic_sort<2, WAVE>(S, k2, i2, lane);
+      int n = 0, ob = 0, nb = 0, ab = 0;
+      if (i2 < C) {
+        n = S.mn[i2];
+        ob = S.mo[i2];
+        nb = S.mb[i2];
+        ab = S.ma[i2];
+      }
+      int x = n;
+#pragma unroll
+      for (int off = 1; off < WAVE; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+      }
+      const int tot = __shfl(x, WAVE - 1);
+      S.W[lane] = x - n;
+      S.obase[lane] = ob;
+      S.nbase[lane] = nb;
+      S.abase[lane] = ab;
+      for (int r = WAVE + lane; r < SEL_THREADS; r += WAVE) S.W[r] = tot;
+      if (lane == 0) S.total = tot;
+      fid = i2;
+    }
+    __syncthreads();
+    return fid;
+  }
+  // bitonic sort of all entries, best first ("better" = larger key, then smaller id)
   bitonic_sort<2, SEL_THREADS>(S, key, id, tid);
   // thread r now holds rank r; prefix of sizes in rank order
   int n = 0, ob = 0, nb = 0, ab = 0;
@@ -361,7 +472,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const QT* __restric
                                                              int32_t* __restrict__ sel_count) {
   __shared__ SelShared S;
   const int h = blockIdx.x, tid = threadIdx.x;
-  select_phase(S, q, G, X, h);
+  select_phase(S, q, G, X, h, B);
   const int cnt = select_count(S, X, B);
   const int32_t* ids_h = X.token_ids + (size_t)h * X.cap;
   const int32_t* app_h = X.app_ids + (size_t)h * X.cap;
@@ -398,7 +509,7 @@ __global__ __launch_bounds__(SEL_THREADS) void cache_assemble_kernel(
   __shared__ int hitlen[SEL_THREADS], hitrow[SEL_THREADS];  // per rank: cached members and their first row
   __shared__ long long red[4][SEL_THREADS / WAVE];
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int id = select_phase(S, q, G, X, h);
+  const int id = select_phase(S, q, G, X, h, B);
   const int cnt = select_count(S, X, B);
   const int fixed = X.n_sink + X.nw;
   const int nclus = cnt > fixed ? cnt - fixed : 0;  // entries taken from clusters
@@ -577,7 +688,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
   __shared__ float ored[NW][G][D];
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = lane >> 4, gl = lane & 15;
-  select_phase(S, q, G, X, h);
+  select_phase(S, q, G, X, h, B);
   const int cnt = select_count(S, X, B);
   const long long cap = X.cap;
   if (sel_count && tid == 0) sel_count[h] = cnt;
@@ -777,7 +888,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
   if (h >= heads) return;  // whole block: the grid covers heads rounded up to 8
   const int vgrp = lane / (HC / 8), vgl = lane % (HC / 8);  // value row in the load, 8-channel chunk
   const int j16 = lane & 15, kb4 = lane >> 4;
-  select_phase(S, q, G, X, h);
+  select_phase(S, q, G, X, h, B);
   const int cnt = select_count(S, X, B);
   const long long cap = X.cap;
   const bool writer = part == 0;  // one block per head publishes the selection
