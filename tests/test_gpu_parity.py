@@ -536,10 +536,11 @@ MANY = synth.Workload("many_clusters_bf16", 93, heads=3, G=2, L=3000, d=128, dty
 
 
 def test_selection_merge_and_full_ranking():
-    """Selection ranks clusters by merging per-wave sorted runs while the
-    budget needs at most 64 clusters, and by a sort of every cluster beyond
-    that: with 100 clusters, budgets needing a few, about 20, more than 64 and
-    all clusters (and sinks) select exactly as the oracle, split and fused."""
+    """Selection orders only the clusters that can be selected (a size-weighted
+    score histogram finds them) with one wave while there are at most 64, and
+    sorts every cluster beyond that: with 100 clusters, budgets needing a few,
+    about 20, more than 64 and all clusters (and sinks) select exactly as the
+    oracle, split and fused."""
     w, n_sink = MANY, 5
     base, K, V, _, means = make_inputs(w)
     H = K.shape[0]
