@@ -260,9 +260,13 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
       for (int s = 0; s < 4; ++s) {
         const u32x4 v = kn[T][s];
         kb[T][s] = __builtin_bit_cast(bf16x8, v);
+        // the four words as scalars first: a bit cast of an indexed vector
+        // element inside this unrolled loop compiles to the first word four
+        // times
+        const unsigned e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {  // two channels per packed dot product
-          const bf16x2 x = __builtin_bit_cast(bf16x2, v[q]);
+          const bf16x2 x = __builtin_bit_cast(bf16x2, e[q]);
           ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
         }
       }

@@ -79,6 +79,16 @@ def test_assign_step_bit_exact(case):
             err = np.abs(t2[..., 0] - best)
             say(f"  max |fp32 best - fp64 best| / bound = {(err / bound).max():.3e}")
             assert np.all(err <= bound)
+            # the kernel certifies exactly the keys whose best and runner-up are
+            # further apart than the threshold from the exact key norm (up to
+            # keys on the threshold itself): a wrong norm in the kernel shows up
+            # as a different number of queued keys
+            m1, m2 = t2[..., 0].astype(np.float64), t2[..., 1].astype(np.float64)
+            thr = (2 * 4 * (w.d + 16) * 2.0 ** -24 * 1.02) * kn + 2.0 ** -15 * 1.02 * np.maximum(np.abs(m1), np.abs(m2))
+            want_flag = (~(m1 - m2 > thr)).sum(axis=1)
+            got_flag = to_np(flagged)
+            say(f"  queued per head: kernel {got_flag.tolist()}, from exact norms {want_flag.tolist()}")
+            assert np.all(np.abs(got_flag - want_flag) <= np.maximum(2, want_flag // 100))
         c0 = np.stack([oracle.update(K[h, :w.L], want[h], c0[h])[0] for h in range(H)])
 
 
