@@ -455,6 +455,16 @@ def test_distance_variants_end_to_end(case, metric):
         err = np.abs(to_np(top2)[..., 0] - best)
         say(f"  max |fp32 best - fp64 best| / bound = {(err / bound).max():.3e}")
         assert np.all(err <= bound)
+        # queued keys: exactly those within the threshold built from the exact
+        # key norms, the largest operand norm and the largest bias
+        t2 = to_np(top2).astype(np.float64)
+        m1, m2 = t2[..., 0], t2[..., 1]
+        thr = (2 * 4 * 2.0 ** -24 * 1.02) * ((w.d + 17) * kn * A + 2 * bmax) + \
+            2.0 ** -15 * 1.02 * np.maximum(np.abs(m1), np.abs(m2))
+        want_flag = (~(m1 - m2 > thr)).sum(axis=1)
+        got_flag = to_np(flagged)
+        say(f"  queued per head: kernel {got_flag.tolist()}, from exact norms {want_flag.tolist()}")
+        assert np.all(np.abs(got_flag - want_flag) <= np.maximum(2, want_flag // 100))
     # the whole build
     Kc, Vc = K.copy(), V.copy()
     Kc[:, w.L:], Vc[:, w.L:] = 0, 0
