@@ -61,6 +61,7 @@ struct BuildWs {
   int32_t* hist;     // [heads, nblk, C]
   void* op_t;        // [heads, d / 8, cpad(C)] 16-byte chunks: the bf16 operand chunk-major
   int32_t* dirty;    // [iters, heads, C]: clusters a key entered or left in that iteration
+  float* norm2;      // [heads, L]: each key's squared norm, from the first iteration on
   size_t bytes;
 };
 
@@ -78,6 +79,8 @@ BuildWs carve_build(void* base, int heads, int L, int C, int iters) {
   o = align_up(o + sizeof(uint16_t) * (size_t)heads * kv_cluster_cpad(C) * KVC_HEAD_DIM);
   w.dirty = reinterpret_cast<int32_t*>(b + o);
   o = align_up(o + sizeof(int32_t) * (size_t)iters * heads * C);
+  w.norm2 = reinterpret_cast<float*>(b + o);
+  o = align_up(o + sizeof(float) * (size_t)heads * L);
   w.bytes = o;
   return w;
 }
@@ -163,8 +166,10 @@ int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, c
     // from the second iteration on, the assignment marks the clusters keys
     // entered or left and the update recomputes only those
     int32_t* dirty = t == 0 ? nullptr : w.dirty + (size_t)t * H * C;
+    // the keys' norms (for the certificate) are computed once and kept
     e = launch_assign(idx->dtype, keys_c, hs, H, Lc, idx->centroids_op, C, cpad, cps, idx->metric, idx->labels + ns,
-                      cap, w.queue, w.qcount + (size_t)t * H, w.op_t, dirty, nullptr, ev, st);
+                      cap, w.queue, w.qcount + (size_t)t * H, w.op_t, dirty, w.norm2, t == 0 ? 1 : 2, nullptr, ev,
+                      st);
     if (e == hipSuccess)
       e = launch_csr(idx->labels + ns, cap, H, Lc, C, cs, w.hist, idx->sizes, idx->offsets, idx->token_ids, cap, ns,
                      st);
@@ -192,7 +197,7 @@ int kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.qcount), (size_t)H, 0, st);
   if (e == hipSuccess)
     e = launch_assign(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, L, chat, C, cpad, cpad, idx->metric, labels,
-                      cap, w.queue, w.qcount, w.op_t, nullptr, top2, nullptr, st);
+                      cap, w.queue, w.qcount, w.op_t, nullptr, nullptr, 0, top2, nullptr, st);
   if (e == hipSuccess && flagged)
     e = hipMemcpyAsync(flagged, w.qcount, sizeof(int32_t) * H, hipMemcpyDeviceToDevice, st);
   return hip_status(e);
@@ -276,7 +281,7 @@ int kv_cluster_cluster_window(kvc_index* idx, const void* k_cache, const void* v
                               w.cent, w.cent_t, w.chat, idx->dev_flags, st);
   for (int t = 0; t < iters && e == hipSuccess; ++t) {
     e = launch_assign(idx->dtype, keys_w, hs, H, m, w.chat, nc, cpw, cpw, idx->metric, w.labels, m, w.b.queue,
-                      w.b.qcount + (size_t)t * H, w.b.op_t, nullptr, nullptr, nullptr, st);
+                      w.b.qcount + (size_t)t * H, w.b.op_t, nullptr, nullptr, 0, nullptr, nullptr, st);
     if (e == hipSuccess) e = launch_csr(w.labels, m, H, m, nc, nc, w.b.hist, w.sizes, w.offsets, w.ids, m, wlo, st);
     if (e == hipSuccess)
       e = launch_update(idx->dtype, k_cache, hs, H, nc, nc, cpw, idx->metric, w.sizes, w.offsets, w.ids, m, w.cent,

@@ -176,7 +176,8 @@ template <int METRIC>
 __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     const uint16_t* __restrict__ keys, long long head_stride, int L, const uint16_t* __restrict__ chat, int C,
     int cpad, int cps, int32_t* __restrict__ labels, long long label_stride, int32_t* __restrict__ queue,
-    uint32_t* __restrict__ qcount, u32x4* __restrict__ op_t, int32_t* __restrict__ dirty, float* __restrict__ top2) {
+    uint32_t* __restrict__ qcount, u32x4* __restrict__ op_t, int32_t* __restrict__ dirty, float* __restrict__ norm2,
+    int norm_mode, float* __restrict__ top2) {
   extern __shared__ u32x4 sC[];  // cpad rows x 16 chunks of 16 B, chunk c of row r at c ^ (r & 15)
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -237,11 +238,16 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
   // variants: threshold = g2 * ((d + 17) * A * ||K_i|| + 2 max|b_k|)
   const float g2 = 2.0f * 4.0f * 5.9604644775390625e-8f * 1.02f;
   const float gA = g2 * (float)(D + 17) * normA, gB = g2 * 2.0f * biasM;
+  const u32x4* sA[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) sA[s] = sC + j16 * 16 + ((4 * s + kb4) ^ j16);
   for (int grpi = blockIdx.x; grpi < ngroups; grpi += gridDim.x) {
     const int row0 = grpi * AS_TILE + wave * 64;
     // the label this lane's key had after the previous iteration, read early
     const int prow = row0 + kb4 * 16 + j16;
     const int old_label = dirty && prow < L ? labels[(size_t)h * label_stride + prow] : -1;
+    // ||K||^2 of that key from an earlier iteration (norm_mode 2)
+    const float kept_n2 = norm_mode == 2 && prow < L ? norm2[(size_t)h * L + prow] : 0.f;
     u32x4 kn[4][4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
@@ -260,6 +266,7 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
       for (int s = 0; s < 4; ++s) {
         const u32x4 v = kn[T][s];
         kb[T][s] = __builtin_bit_cast(bf16x8, v);
+        if (norm_mode == 2) continue;
         // the four words as scalars first: a bit cast of an indexed vector
         // element inside this unrolled loop compiles to the first word four
         // times
@@ -285,10 +292,11 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     // vector instructions so that both units stay busy within a wave. The
     // tile count (cpad / 16) is even and only the last two tiles can hold
     // padding rows, so the loop body folds full tiles without masks.
+    // row ct * 16 + j16 of the operand: its chunk 4 s + kb4 sits at
+    // (4 s + kb4) ^ j16, the same for every tile, so only the tile's base moves
     auto load_a = [&](int ct, bf16x8 (&a)[4]) {
-      const int arow = ct * 16 + j16;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) a[s] = __builtin_bit_cast(bf16x8, sC[arow * 16 + ((4 * s + kb4) ^ (arow & 15))]);
+      for (int s = 0; s < 4; ++s) a[s] = __builtin_bit_cast(bf16x8, sA[s][ct * 256]);
     };
     auto mma = [&](const bf16x8 (&a)[4], f32x4 (&acc)[4]) {
 #pragma unroll
@@ -366,18 +374,20 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
         i1[T] = m1[T] > o1 ? i1[T] : (o1 > m1[T] ? oi : min(i1[T], oi));
         m1[T] = fmaxf(m1[T], o1);
         m2[T] = M2;
-        n2[T] += __shfl_xor(n2[T], m);
+        if (norm_mode != 2) n2[T] += __shfl_xor(n2[T], m);
       }
     }
     // lane kb4 == T publishes key j16 of tile T
     int my_label = 0;
     bool my_flag = false;
-    float my_m1 = 0.f, my_m2 = 0.f;
+    float my_m1 = 0.f, my_m2 = 0.f, my_n2 = 0.f;
 #pragma unroll
     for (int T = 0; T < 4; ++T)
       if (T == kb4) {
         my_label = i1[T];
-        const float thr = (METRIC == M_COSINE ? gamma * sqrtf(n2[T]) : gA * sqrtf(n2[T]) + gB) +
+        const float nn = norm_mode == 2 ? kept_n2 : n2[T];
+        if (norm_mode == 1) my_n2 = nn;
+        const float thr = (METRIC == M_COSINE ? gamma * sqrtf(nn) : gA * sqrtf(nn) + gB) +
                           gbits * fmaxf(fabsf(m1[T]), fabsf(m2[T]));
         my_flag = !((m1[T] - m2[T]) > thr);  // true for NaN and ties
         my_m1 = m1[T];
@@ -391,6 +401,7 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
         labels[(size_t)h * label_stride + row] = my_label;
         if (dirty && old_label != my_label) mark_moved(dirty + (size_t)h * C, C, old_label, my_label);
       }
+      if (norm_mode == 1) norm2[(size_t)h * L + row] = my_n2;
       if (top2) {
         top2[((size_t)h * L + row) * 2] = my_m1;
         top2[((size_t)h * L + row) * 2 + 1] = my_m2;
@@ -880,7 +891,7 @@ template <int METRIC>
 static hipError_t launch_mfma_t(dim3 grid, size_t lds, const uint16_t* keys, long long head_stride, int L,
                                 const uint16_t* chat, int C, int cpad, int cps, int32_t* labels,
                                 long long label_stride, int32_t* queue, uint32_t* qcount, u32x4* op_t,
-                                int32_t* dirty, float* top2, hipStream_t st) {
+                                int32_t* dirty, float* norm2, int norm_mode, float* top2, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)assign_bf16_mfma_kernel<METRIC>,
@@ -889,14 +900,15 @@ static hipError_t launch_mfma_t(dim3 grid, size_t lds, const uint16_t* keys, lon
     attr_set = true;
   }
   assign_bf16_mfma_kernel<METRIC><<<grid, AS_THREADS, lds, st>>>(keys, head_stride, L, chat, C, cpad, cps, labels,
-                                                                 label_stride, queue, qcount, op_t, dirty, top2);
+                                                                 label_stride, queue, qcount, op_t, dirty, norm2,
+                                                                 norm_mode, top2);
   return hipGetLastError();
 }
 
 hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
                          int cpad, int cps, int metric, int32_t* labels, long long label_stride, int32_t* queue,
-                         uint32_t* qcount, void* op_t, int32_t* dirty, float* top2, hipEvent_t* events,
-                         hipStream_t st) {
+                         uint32_t* qcount, void* op_t, int32_t* dirty, float* norm2, int norm_mode, float* top2,
+                         hipEvent_t* events, hipStream_t st) {
   u32x4* ot = static_cast<u32x4*>(op_t);
   if (dtype == DT_BF16) {
     const size_t lds = (size_t)cpad * D * 2;
@@ -916,13 +928,13 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
     const size_t lds_var = lds + (size_t)cpad * 4 + 16;
     if (metric == M_L2)
       e = launch_mfma_t<M_L2>(grid, lds_var, kk, head_stride, L, cc, C, cpad, cps, labels, label_stride, queue,
-                              qcount, ot, dirty, top2, st);
+                              qcount, ot, dirty, norm2, norm_mode, top2, st);
     else if (metric == M_IP)
       e = launch_mfma_t<M_IP>(grid, lds_var, kk, head_stride, L, cc, C, cpad, cps, labels, label_stride, queue,
-                              qcount, ot, dirty, top2, st);
+                              qcount, ot, dirty, norm2, norm_mode, top2, st);
     else
       e = launch_mfma_t<M_COSINE>(grid, lds, kk, head_stride, L, cc, C, cpad, cps, labels, label_stride, queue,
-                                  qcount, ot, dirty, top2, st);
+                                  qcount, ot, dirty, norm2, norm_mode, top2, st);
     if (e != hipSuccess) return e;
     if (events) {
       e = hipEventRecord(events[1], st);

@@ -31,8 +31,8 @@ hipError_t launch_init_centroids(int dtype, const void* keys, long long head_str
                                  float* cent_t, void* chat, int32_t* flags, hipStream_t st);
 hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int heads, int L, const void* chat, int C,
                          int cpad, int cps, int metric, int32_t* labels, long long label_stride, int32_t* queue,
-                         uint32_t* qcount, void* op_t, int32_t* dirty, float* top2, hipEvent_t* events,
-                         hipStream_t st);
+                         uint32_t* qcount, void* op_t, int32_t* dirty, float* norm2, int norm_mode, float* top2,
+                         hipEvent_t* events, hipStream_t st);
 hipError_t launch_fill2d_i32(int32_t* p, int rows, long long stride, int cols, int value, hipStream_t st);
 hipError_t launch_csr(const int32_t* labels, long long label_stride, int heads, int L, int C, int cs, int32_t* hist,
                       int32_t* sizes, int32_t* offsets, int32_t* token_ids, long long ids_stride, int id_base,
