@@ -193,10 +193,13 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
     sC[r * 16 + (c ^ (r & 15))] = v;
     if (Ot) Ot[(size_t)c * cpad + r] = v;
   }
+  // one zero tile past the operand: the tile loop reads one tile ahead without
+  // a bound
+  for (int e = tid; e < 16 * 16; e += AS_THREADS) sC[cpad * 16 + e] = u32x4{0u, 0u, 0u, 0u};
   // variants: after the operand, the per-centroid bias (L2; cpad floats) and
   // the largest operand norm (one word), all in the dynamic allocation so the
   // kernel has no static LDS
-  float* sBias = reinterpret_cast<float*>(sC + cpad * 16);
+  float* sBias = reinterpret_cast<float*>(sC + (cpad + 16) * 16);
   unsigned& sMaxNorm = *reinterpret_cast<unsigned*>(sBias + cpad);
   float normA = 1.0f, biasM = 0.0f;
   if constexpr (METRIC != M_COSINE) {
@@ -345,7 +348,7 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
       fold(ct, accA, false);
       interleave();
       mma(aA, accA);       // tile ct + 2
-      load_a(min(ct + 3, ntl - 1), aB);  // the next tile, or (unused) the last
+      load_a(ct + 3, aB);  // the next tile, or (unused) the zero tile past the operand
       fold(ct + 1, accB, false);
       interleave();
     }
@@ -911,7 +914,7 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
                          hipEvent_t* events, hipStream_t st) {
   u32x4* ot = static_cast<u32x4*>(op_t);
   if (dtype == DT_BF16) {
-    const size_t lds = (size_t)cpad * D * 2;
+    const size_t lds = (size_t)(cpad + 16) * D * 2;  // the operand and one zero tile
     // about one block per compute unit; each walks over 512-key groups of one head
     const int ngroups = grid1(L, AS_TILE);
     int gx = (256 + heads - 1) / heads;
