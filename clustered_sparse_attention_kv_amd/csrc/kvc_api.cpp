@@ -275,11 +275,17 @@ int kv_cluster_cluster_window(kvc_index* idx, const void* k_cache, const void* v
   const int cpw = kv_cluster_cpad(nc);
   // the window's keys: rows wlo .. n_tokens-1; the index stores absolute positions
   const void* keys_w = static_cast<const char*>(k_cache) + (size_t)wlo * KVC_HEAD_DIM * elem_bytes(idx->dtype);
-  hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.b.qcount), (size_t)iters * H, 0, st);
-  if (e == hipSuccess)
+  hipError_t e = hipSuccess;
+  // a small window: its whole k-means in one launch, same arithmetic
+  const bool fused = window_kmeans_fits(m, nc);
+  if (fused)
+    e = launch_window_kmeans(idx->dtype, k_cache, hs, H, wlo, idx->n_tokens, m, nc, cpw, iters, init_idx, idx->metric,
+                             w.cent, w.cent_t, w.chat, w.labels, w.sizes, w.offsets, w.ids, idx->dev_flags, st);
+  if (!fused && e == hipSuccess) e = launch_fill_i32(reinterpret_cast<int32_t*>(w.b.qcount), (size_t)iters * H, 0, st);
+  if (!fused && e == hipSuccess)
     e = launch_init_centroids(idx->dtype, k_cache, hs, H, wlo, idx->n_tokens, init_idx, nc, cpw, nc, cpw, idx->metric,
                               w.cent, w.cent_t, w.chat, idx->dev_flags, st);
-  for (int t = 0; t < iters && e == hipSuccess; ++t) {
+  for (int t = 0; !fused && t < iters && e == hipSuccess; ++t) {
     e = launch_assign(idx->dtype, keys_w, hs, H, m, w.chat, nc, cpw, cpw, idx->metric, w.labels, m, w.b.queue,
                       w.b.qcount + (size_t)t * H, w.b.op_t, nullptr, nullptr, 0, nullptr, nullptr, st);
     if (e == hipSuccess) e = launch_csr(w.labels, m, H, m, nc, nc, w.b.hist, w.sizes, w.offsets, w.ids, m, wlo, st);

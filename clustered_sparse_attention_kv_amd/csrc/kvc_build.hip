@@ -17,9 +17,10 @@ namespace kvc {
 // Normalisation of one centroid row held by one wave (2 channels per lane).
 // norm = sqrt(fp64 sum of c_j^2 over ascending j); chat_j = c_j / norm rounded
 // once to the operand type (zero when the norm is zero). The ascending sum is
-// one lane's chain so its order is fixed.
+// one lane's chain so its order is fixed (its loads are batched). Returns the
+// two rounded values this lane stored.
 template <typename OT>
-__device__ __forceinline__ void normalize_row(const float c0, const float c1, float* lds_row, OT* out_row) {
+__device__ __forceinline__ double2 normalize_row(const float c0, const float c1, float* lds_row, OT* out_row) {
   const int lane = lane_id();
   lds_row[2 * lane] = c0;
   lds_row[2 * lane + 1] = c1;
@@ -28,6 +29,7 @@ __device__ __forceinline__ void normalize_row(const float c0, const float c1, fl
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   double ss = 0.0;
   if (lane == 0) {
+#pragma unroll 16
     for (int j = 0; j < D; ++j) {
       const double v = (double)lds_row[j];
       ss = fma(v, v, ss);
@@ -42,6 +44,7 @@ __device__ __forceinline__ void normalize_row(const float c0, const float c1, fl
   const double v1 = nrm > 0.0 ? (double)c1 / nrm : 0.0;
   store_op(out_row, 2 * lane, v0);
   store_op(out_row, 2 * lane + 1, v1);
+  return double2{rounded_op(out_row, v0), rounded_op(out_row, v1)};
 }
 
 // The assignment operand of one centroid row under each distance (III.B
@@ -50,15 +53,13 @@ __device__ __forceinline__ void normalize_row(const float c0, const float c1, fl
 // for L2 and inner product, rounded once to the operand type. metric is
 // uniform over the wave.
 template <typename OT>
-__device__ __forceinline__ void operand_row(int metric, const float c0, const float c1, float* lds_row,
-                                            OT* out_row) {
-  if (metric == M_COSINE) {
-    normalize_row(c0, c1, lds_row, out_row);
-    return;
-  }
+__device__ __forceinline__ double2 operand_row(int metric, const float c0, const float c1, float* lds_row,
+                                               OT* out_row) {
+  if (metric == M_COSINE) return normalize_row(c0, c1, lds_row, out_row);
   const int lane = lane_id();
   store_op(out_row, 2 * lane, (double)c0);
   store_op(out_row, 2 * lane + 1, (double)c1);
+  return double2{rounded_op(out_row, (double)c0), rounded_op(out_row, (double)c1)};
 }
 
 // ---------------------------------------------------------------------------
@@ -773,6 +774,209 @@ __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys
   }
   operand_row(metric, c0, c1, rows[w], chat + ((size_t)h * cps + k) * D);
 }
+
+// ---------------------------------------------------------------------------
+// Clustering of a small window of generated tokens in one launch (nc <= 32
+// clusters): one block per head runs the whole k-means of the window's m keys
+// with the build's arithmetic. Initial centroids are the keys at init_idx;
+// a key's label is the argmax of the fp64 chains over ascending channels
+// against the operand rows (lowest cluster on ties; under the L2 distance the
+// chain minus half the fp64 chain of the row's squares); a cluster's mean is
+// the fp64 sum of its members in ascending token order divided by the count,
+// rounded once (an empty cluster keeps its centroid); operand rows as in the
+// build. The member lists are written once, after the last iteration. The
+// outputs are the arrays the window merge reads: centroids (both layouts),
+// operand rows (padding rows zeroed), labels, sizes, offsets and ids.
+constexpr int WK_MAXC = 32;
+template <typename KT>
+__global__ __launch_bounds__(256) void window_kmeans_kernel(
+    const KT* __restrict__ keys, long long head_stride, int wlo, int n_tokens, int m, int nc, int cpw, int iters,
+    const int32_t* __restrict__ init_idx, int metric, float* __restrict__ cent, float* __restrict__ cent_t,
+    KT* __restrict__ chat, int32_t* __restrict__ labels, int32_t* __restrict__ sizes,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ ids, int32_t* __restrict__ flags) {
+  constexpr int EPC = 16 / (int)sizeof(KT);  // elements per 16-byte chunk
+  constexpr int CH = D / EPC;                // chunks per row
+  constexpr int BATCH = 16;                  // member rows requested together
+  extern __shared__ int lab[];               // the m labels
+  __shared__ __align__(16) double op[WK_MAXC][D];  // operand rows in fp64 (exact)
+  __shared__ double hnn[WK_MAXC];            // half the fp64 chain of each row's squares (L2)
+  __shared__ float rows[4][D];
+  __shared__ int cnt[WK_MAXC];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const KT* Kw = keys + (size_t)h * head_stride + (size_t)wlo * D;  // row i of the window
+  float* cent_h = cent + (size_t)h * nc * D;
+  float* ct_h = cent_t + (size_t)h * nc * D;
+  KT* chat_h = chat + (size_t)h * cpw * D;
+  // operand row k (the values this wave just stored) into LDS in fp64, and nn_k / 2
+  auto refresh = [&](int k, double2 r) {
+    op[k][2 * lane] = r.x;
+    op[k][2 * lane + 1] = r.y;
+    if (metric == M_L2) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (lane == 0) {
+        double nn = 0.0;
+#pragma unroll 16
+        for (int j = 0; j < D; ++j) nn = fma(op[k][j], op[k][j], nn);
+        hnn[k] = 0.5 * nn;
+      }
+    }
+  };
+  // initial centroids (padding operand rows zeroed)
+  for (int k = w; k < cpw; k += 4) {
+    KT* out = chat_h + (size_t)k * D;
+    if (k >= nc) {
+      store_op(out, 2 * lane, 0.0);
+      store_op(out, 2 * lane + 1, 0.0);
+      continue;
+    }
+    int tok = init_idx[(size_t)h * nc + k];
+    if (tok < wlo || tok >= n_tokens) {
+      if (lane == 0) atomicOr(flags, 1);
+      tok = 0;
+    }
+    const KT* src = keys + (size_t)h * head_stride + (size_t)tok * D;
+    const float c0 = load_f32(src, 2 * lane), c1 = load_f32(src, 2 * lane + 1);
+    store_centroid(cent_h + (size_t)k * D, ct_h, nc, k, c0, c1);
+    refresh(k, operand_row(metric, c0, c1, rows[w], out));
+  }
+  __syncthreads();
+  for (int t = 0; t < iters; ++t) {
+    // assignment: one thread per key (its row in registers), one cluster's
+    // chain at a time over ascending channels
+    for (int i = tid; i < m; i += 256) {
+      const u32x4* kr = reinterpret_cast<const u32x4*>(Kw + (size_t)i * D);
+      u32x4 kv[CH];
+#pragma unroll
+      for (int q = 0; q < CH; ++q) kv[q] = kr[q];
+      double best = -INFINITY;
+      int bi = 0;
+      for (int k = 0; k < nc; ++k) {
+        // the row's words enter each cluster's pass afresh, so their fp64
+        // conversions are not hoisted out of this loop (128 doubles would
+        // leave no registers to batch the operand reads)
+#pragma unroll
+        for (int q = 0; q < CH; ++q) asm volatile("" : "+v"(kv[q]));
+        double sk = 0.0;
+        // the operand row in batches of 32 values, all requested before use
+        constexpr int OB = 32;
+#pragma unroll
+        for (int j0 = 0; j0 < D; j0 += OB) {
+          double ob[OB];
+#pragma unroll
+          for (int u = 0; u < OB; u += 2) {
+            const double2 t2 = *reinterpret_cast<const double2*>(&op[k][j0 + u]);
+            ob[u] = t2.x;
+            ob[u + 1] = t2.y;
+          }
+          __builtin_amdgcn_sched_barrier(0);  // keep the batch's reads ahead of its uses
+#pragma unroll
+          for (int u = 0; u < OB; ++u) {
+            const int j = j0 + u, q = j / EPC, e = j % EPC;
+            double x;
+            if constexpr (sizeof(KT) == 2)
+              x = (double)((e & 1) ? __uint_as_float(kv[q][e >> 1] & 0xFFFF0000u)
+                                   : __uint_as_float(kv[q][e >> 1] << 16));
+            else
+              x = (double)__uint_as_float(kv[q][e]);
+            sk = fma(x, ob[u], sk);
+          }
+        }
+        if (metric == M_L2) sk = sk - hnn[k];
+        if (sk > best) {
+          best = sk;
+          bi = k;
+        }
+      }
+      lab[i] = bi;
+    }
+    __syncthreads();
+    // update: one wave per cluster; members in ascending token order, rows
+    // requested BATCH at a time and summed in that order
+    for (int k = w; k < nc; k += 4) {
+      double a0 = 0.0, a1 = 0.0;
+      int n = 0;
+      for (int c0 = 0; c0 < m; c0 += 64) {
+        unsigned long long bits = __ballot(c0 + lane < m && lab[c0 + lane] == k);
+        while (bits) {
+          int mi[BATCH];
+          int nb = 0;
+#pragma unroll
+          for (int b = 0; b < BATCH; ++b) {
+            mi[b] = 0;
+            if (bits) {
+              mi[b] = c0 + __ffsll((long long)bits) - 1;
+              bits &= bits - 1;
+              ++nb;
+            }
+          }
+          float v0[BATCH], v1[BATCH];
+#pragma unroll
+          for (int b = 0; b < BATCH; ++b) {
+            const KT* r = Kw + (size_t)mi[b] * D;
+            v0[b] = b < nb ? load_f32(r, 2 * lane) : 0.f;
+            v1[b] = b < nb ? load_f32(r, 2 * lane + 1) : 0.f;
+          }
+#pragma unroll
+          for (int b = 0; b < BATCH; ++b)
+            if (b < nb) {
+              a0 += (double)v0[b];
+              a1 += (double)v1[b];
+            }
+          n += nb;
+        }
+      }
+      float c0, c1;
+      if (n > 0) {
+        c0 = (float)(a0 / (double)n);
+        c1 = (float)(a1 / (double)n);
+        store_centroid(cent_h + (size_t)k * D, ct_h, nc, k, c0, c1);
+      } else {
+        c0 = cent_h[(size_t)k * D + 2 * lane];
+        c1 = cent_h[(size_t)k * D + 2 * lane + 1];
+      }
+      refresh(k, operand_row(metric, c0, c1, rows[w], chat_h + (size_t)k * D));
+    }
+    __syncthreads();
+  }
+  // labels, sizes, offsets and member lists of the last assignment
+  for (int i = tid; i < m; i += 256) labels[(size_t)h * m + i] = lab[i];
+  if (tid < nc) {
+    int n = 0;
+    for (int i = 0; i < m; ++i) n += lab[i] == tid ? 1 : 0;
+    cnt[tid] = n;
+  }
+  __syncthreads();
+  if (tid < nc) {
+    int o = 0;
+    for (int k = 0; k < tid; ++k) o += cnt[k];
+    sizes[(size_t)h * nc + tid] = cnt[tid];
+    offsets[(size_t)h * (nc + 1) + tid] = o;
+    if (tid == nc - 1) offsets[(size_t)h * (nc + 1) + nc] = o + cnt[tid];
+    for (int i = 0; i < m; ++i)
+      if (lab[i] == tid) ids[(size_t)h * m + o++] = wlo + i;
+  }
+}
+
+hipError_t launch_window_kmeans(int dtype, const void* keys, long long head_stride, int heads, int wlo, int n_tokens,
+                                int m, int nc, int cpw, int iters, const int32_t* init_idx, int metric, float* cent,
+                                float* cent_t, void* chat, int32_t* labels, int32_t* sizes, int32_t* offsets,
+                                int32_t* ids, int32_t* flags, hipStream_t st) {
+  if (nc > WK_MAXC || (size_t)m * sizeof(int) > 64 * 1024) return hipErrorInvalidValue;
+  const size_t lds = (size_t)m * sizeof(int);
+  if (dtype == DT_BF16)
+    window_kmeans_kernel<uint16_t><<<heads, 256, lds, st>>>((const uint16_t*)keys, head_stride, wlo, n_tokens, m, nc,
+                                                            cpw, iters, init_idx, metric, cent, cent_t,
+                                                            (uint16_t*)chat, labels, sizes, offsets, ids, flags);
+  else
+    window_kmeans_kernel<float><<<heads, 256, lds, st>>>((const float*)keys, head_stride, wlo, n_tokens, m, nc, cpw,
+                                                         iters, init_idx, metric, cent, cent_t, (float*)chat, labels,
+                                                         sizes, offsets, ids, flags);
+  return hipGetLastError();
+}
+
+bool window_kmeans_fits(int m, int nc) { return nc <= WK_MAXC && (size_t)m * sizeof(int) <= 64 * 1024; }
 
 // ---------------------------------------------------------------------------
 // Clustering of generated tokens (III.B: the tokens generated since the last

@@ -73,6 +73,9 @@ __device__ __forceinline__ void load8(const float* p, float* o) {
 }
 
 __device__ __forceinline__ void store_op(uint16_t* p, size_t i, double v) { p[i] = f64_to_bf16_rne(v); }
+// the value store_op writes, as a double
+__device__ __forceinline__ double rounded_op(const uint16_t*, double v) { return (double)bf16_bits_to_f32(f64_to_bf16_rne(v)); }
+__device__ __forceinline__ double rounded_op(const float*, double v) { return (double)(float)v; }
 __device__ __forceinline__ void store_op(float* p, size_t i, double v) { p[i] = (float)v; }
 
 // Order-preserving map of an fp64 score to uint64 (larger score, larger key);

@@ -43,6 +43,12 @@ hipError_t launch_update(int dtype, const void* keys, long long head_stride, int
 // Moves the window's clustering (nc clusters of the m tokens wlo .. wlo+m-1,
 // in arrays of stride nc / cpad(nc) / m per head) into the index as clusters
 // ca .. ca+nc-1.
+// The window's whole k-means in one launch (small windows: see window_kmeans_fits).
+bool window_kmeans_fits(int m, int nc);
+hipError_t launch_window_kmeans(int dtype, const void* keys, long long head_stride, int heads, int wlo, int n_tokens,
+                                int m, int nc, int cpw, int iters, const int32_t* init_idx, int metric, float* cent,
+                                float* cent_t, void* chat, int32_t* labels, int32_t* sizes, int32_t* offsets,
+                                int32_t* ids, int32_t* flags, hipStream_t st);
 hipError_t launch_merge_window(int dtype, int heads, int nc, int m, int wlo, const float* cent_w, const void* chat_w,
                                const int32_t* labels_w, const int32_t* sizes_w, const int32_t* offsets_w,
                                const int32_t* ids_w, int ca, int cs, int cps, float* cent, float* cent_t, void* chat,
