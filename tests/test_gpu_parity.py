@@ -422,6 +422,49 @@ def test_window_clustering_end_to_end():
     assert windows == 3
 
 
+@pytest.mark.parametrize("metric", ["cosine", "l2", "inner_product"])
+@pytest.mark.parametrize("nc", [4, 40])
+def test_window_clustering_one_launch_and_general(metric, nc):
+    """Clustering a window of generated tokens takes one launch per call for
+    up to 32 new clusters and the build's kernels beyond that; under each
+    distance both give the oracle's result bit for bit (labels, centroids,
+    operand, sizes, offsets, member ids)."""
+    w, m = SMALL_WINDOW, 64
+    mk, om = {"cosine": (kvc.COSINE, oracle.COSINE), "l2": (kvc.L2, oracle.L2),
+              "inner_product": (kvc.INNER_PRODUCT, oracle.IP)}[metric]
+    say(f"[window clustering] {metric}, {nc} clusters")
+    base, K, V, init, _ = make_inputs(w)
+    H = K.shape[0]
+    idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w), c_slots=w.C + nc, metric=mk)
+    Kc, Vc = K.copy(), V.copy()
+    Kc[:, w.L:], Vc[:, w.L:] = 0, 0
+    Kd, Vd = to_dev(Kc), to_dev(Vc)
+    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    ref = oracle.build(np.ascontiguousarray(K[:, :w.L]), w.C, w.iters, init, metric=om)
+    oi = oracle.Index(ref, w.capacity, metric=om)
+    for n in range(w.L, w.L + m):
+        kvc.append_window(idx, Kd, Vd, to_dev(np.ascontiguousarray(K[:, n:n + 1])),
+                          to_dev(np.ascontiguousarray(V[:, n:n + 1])))
+        oi.add_window(1)
+    init_w = synth.init_idx(synth.stream_seed(base, 11, nc), H, m, nc) + np.int32(w.L)
+    kvc.cluster_window(idx, Kd, Vd, nc, w.iters, to_dev(init_w))
+    oi.cluster_window(K, nc, w.iters, init_w)
+    torch.cuda.synchronize()
+    assert int(to_np(idx.dev_flags)[0]) == 0
+    ca, nt = oi.C, oi.n
+    assert idx.c_active == ca == w.C + nc and idx.n_tokens == nt
+    assert np.array_equal(to_np(idx.labels)[:, :nt], oi.labels[:, :nt])
+    assert np.array_equal(to_np(idx.centroids)[:, :ca], oi.c)
+    assert np.array_equal(to_np(idx.centroids_op)[:, :ca], oi.chat)
+    assert np.array_equal(to_np(idx.sizes)[:, :ca], oi.sizes)
+    off, ids = kvc.export_csr(idx)
+    off, ids = to_np(off), to_np(ids)
+    assert np.array_equal(off[:, :ca + 1], oi.offsets)
+    total = int(oi.offsets[0, -1])
+    assert np.array_equal(ids[:, :total], oi.token_ids[:, :total])
+    say(f"  new clusters' sizes {oi.sizes[:, -nc:].sum(axis=1).tolist()} (of {m} tokens per head)")
+
+
 @pytest.mark.parametrize("metric", ["l2", "inner_product"])
 @pytest.mark.parametrize("case", ["small_bf16_append", "cfg1_fp32"])
 def test_distance_variants_end_to_end(case, metric):
