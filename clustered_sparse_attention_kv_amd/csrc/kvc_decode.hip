@@ -420,6 +420,22 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
   return id;
 }
 
+// Entry of member e of the cluster at rank r (built members first, then the
+// appended ones).
+__device__ __forceinline__ int rank_entry(const SelShared& S, int r, int e, const int32_t* __restrict__ ids_h,
+                                          const int32_t* __restrict__ app_h, bool packed) {
+  const int nb = S.nbase[r];
+  if (e < nb) return packed ? S.obase[r] + e : ids_h[S.obase[r] + e];
+  const int a = app_h[S.abase[r] + (e - nb)];
+  return packed ? ~a : a;
+}
+
+// Entry at a position below n_sink + nw: a sink or a window token.
+__device__ __forceinline__ int fixed_entry(int p, bool packed, const IndexView& X) {
+  const int t = p < X.n_sink ? p : X.wlo + (p - X.n_sink);
+  return packed ? ~t : t;
+}
+
 // Entry at output position p (< n_sink + nw + total) of the ranked, trimmed
 // selection: positions below n_sink are the attention sinks (tokens 0 ..
 // n_sink - 1, always recalled first), the next nw the window of generated
@@ -430,21 +446,35 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
 // appended to a cluster (all read from the caches).
 __device__ __forceinline__ int select_emit(const SelShared& S, int p, const int32_t* __restrict__ ids_h,
                                            const int32_t* __restrict__ app_h, bool packed, const IndexView& X) {
-  if (p < X.n_sink) return packed ? ~p : p;
-  p -= X.n_sink;
-  if (p < X.nw) return packed ? ~(X.wlo + p) : X.wlo + p;
-  p -= X.nw;
+  if (p < X.n_sink + X.nw) return fixed_entry(p, packed, X);
+  p -= X.n_sink + X.nw;
   int lo = 0, hi = SEL_THREADS - 1;  // last r with W[r] <= p
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (S.W[mid] <= p) lo = mid;
     else hi = mid - 1;
   }
-  const int e = p - S.W[lo];
-  const int nb = S.nbase[lo];
-  if (e < nb) return packed ? S.obase[lo] + e : ids_h[S.obase[lo] + e];
-  const int a = app_h[S.abase[lo] + (e - nb)];
-  return packed ? ~a : a;
+  return rank_entry(S, lo, p - S.W[lo], ids_h, app_h, packed);
+}
+
+// Calls f(p, entry) for every position p in [p0, p1) of the selection (p1 <=
+// the selected count): the sinks and the window by thread, then the clusters
+// by wave, wave v taking ranks v, v + 8, ... and its lanes their members, so
+// no position needs a search over the ranks.
+template <typename F>
+__device__ __forceinline__ void select_expand(const SelShared& S, int p0, int p1, const int32_t* __restrict__ ids_h,
+                                              const int32_t* __restrict__ app_h, bool packed, const IndexView& X,
+                                              F&& f) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int fixed = X.n_sink + X.nw;
+  for (int p = p0 + tid; p < p1 && p < fixed; p += SEL_THREADS) f(p, fixed_entry(p, packed, X));
+  for (int r = w; r < SEL_THREADS; r += SEL_THREADS / WAVE) {
+    const int st = fixed + S.W[r];  // position of the rank's first member
+    if (st >= p1) break;            // the starts do not decrease
+    const int en = fixed + (r + 1 < SEL_THREADS ? S.W[r + 1] : S.total);
+    const int lo = st > p0 ? st : p0, hi = en < p1 ? en : p1;
+    for (int p = lo + lane; p < hi; p += WAVE) f(p, rank_entry(S, r, p - st, ids_h, app_h, packed));
+  }
 }
 
 // Row of a staged selection entry: a row of the packed copy (id >= 0) or the
@@ -476,8 +506,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const QT* __restric
   const int cnt = select_count(S, X, B);
   const int32_t* ids_h = X.token_ids + (size_t)h * X.cap;
   const int32_t* app_h = X.app_ids + (size_t)h * X.cap;
-  for (int p = tid; p < B; p += SEL_THREADS)
-    sel_ids[(size_t)h * B + p] = p < cnt ? select_emit(S, p, ids_h, app_h, false, X) : -1;
+  select_expand(S, 0, cnt, ids_h, app_h, false, X, [&](int p, int ent) { sel_ids[(size_t)h * B + p] = ent; });
+  for (int p = cnt + tid; p < B; p += SEL_THREADS) sel_ids[(size_t)h * B + p] = -1;
   if (tid == 0) sel_count[h] = cnt;
 }
 
@@ -925,11 +955,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
   for (int base = 0; base < cnt; base += EMIT) {
     const int nb = cnt - base < EMIT ? cnt - base : EMIT;
     if (base > 0) __syncthreads();  // every wave is done with the previous ids
-    for (int p = tid; p < nb; p += SEL_THREADS) {
-      const int ent = select_emit(S, base + p, ids_h, app_h, packed, X);
-      sel[p] = ent;
-      if (writer && sel_ids) sel_ids[(size_t)h * B + base + p] = sel_token(ids_h, ent, packed);
-    }
+    select_expand(S, base, base + nb, ids_h, app_h, packed, X, [&](int p, int ent) {
+      sel[p - base] = ent;
+      if (writer && sel_ids) sel_ids[(size_t)h * B + p] = sel_token(ids_h, ent, packed);
+    });
     __syncthreads();
     for (int t0 = w * 64; t0 < nb; t0 += NW * 64) {
       const int n64 = nb - t0 < 64 ? nb - t0 : 64;
