@@ -198,18 +198,36 @@ struct SelShared {
   int hist[256];                                            // cluster sizes per score bin
   unsigned long long ckey[WAVE];                            // candidates (any order)
   int cid[WAVE];
-  int ncand, bstar;
+  int ncand;
 };
 
-// Value of lane (lane ^ S) within the wave: DPP quad permutes for S = 1, 2,
-// ds_swizzle in bit mode (xor mask, within 32 lanes) for S = 4 .. 16, and a
-// crossbar permute for S = 32.
+// Value of lane (lane ^ S) within the wave: DPP quad permutes for S = 1, 2;
+// for S = 4, 8 the partner lies in the same row of 16, S lanes up or down, so
+// two DPP row shifts and a select; ds_swizzle in bit mode (xor mask, within 32
+// lanes) for S = 16, and a crossbar permute for S = 32.
 template <int S>
 __device__ __forceinline__ int lane_xor(int v) {
   if constexpr (S == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
   else if constexpr (S == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
-  else if constexpr (S < 32) return __builtin_amdgcn_ds_swizzle(v, (S << 10) | 0x1F);
+  else if constexpr (S == 4 || S == 8) {
+    const int up = __builtin_amdgcn_update_dpp(0, v, 0x100 + S, 0xF, 0xF, false);  // row_shl: lane + S
+    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x110 + S, 0xF, 0xF, false);  // row_shr: lane - S
+    return (threadIdx.x & S) ? dn : up;
+  } else if constexpr (S < 32) return __builtin_amdgcn_ds_swizzle(v, (S << 10) | 0x1F);
   else return __shfl_xor(v, S);
+}
+
+// Inclusive prefix sum over the 64 lanes: row shifts by 1, 2, 4, 8 (zero
+// shifted in) scan each row of 16, then the last lane of row 0 (2) is added
+// to row 1 (3), and the last lane of row 1 to rows 2 and 3 (DPP, no LDS).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+  return x;
 }
 
 // One compare-exchange stage of the bitonic sort over the block (thread t
@@ -319,34 +337,29 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
   if (tid < C && S.mn[tid] > 0) atomicAdd(&S.hist[bin], S.mn[tid]);
   __syncthreads();
   const int bc = B - X.n_sink - X.nw;  // entries left for clusters
-  if (w == 0) {
-    // size in bins >= b for lane's bins 4 lane .. 4 lane + 3; b* = the highest
-    // bin whose sum reaches bc (all bins when the clusters hold fewer)
+  int bstar;
+  {
+    // every wave: size in bins >= b for lane's bins 4 lane .. 4 lane + 3;
+    // b* = the highest bin whose sum reaches bc (all bins when the clusters
+    // hold fewer)
     int hb[4], t = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       hb[i] = S.hist[4 * lane + i];
       t += hb[i];
     }
-    int above = t;  // inclusive suffix over lanes, then exclusive
-#pragma unroll
-    for (int off = 1; off < WAVE; off <<= 1) {
-      const int y = __shfl_down(above, off);
-      if (lane + off < WAVE) above += y;
-    }
-    above -= t;
-    int nq = 0, suf = above;
+    const int pre = wave_incl_scan(t);
+    int suf = __builtin_amdgcn_readlane(pre, WAVE - 1) - pre;  // size in the bins of later lanes
+    int nq = 0;
 #pragma unroll
     for (int i = 3; i >= 0; --i) {
       suf += hb[i];
       nq += suf >= bc ? 1 : 0;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) nq += __shfl_xor(nq, off);
-    if (lane == 0) S.bstar = bc <= 0 ? 256 : (nq > 0 ? nq - 1 : 0);
+    nq = __builtin_amdgcn_readlane(wave_incl_scan(nq), WAVE - 1);
+    bstar = bc <= 0 ? 256 : (nq > 0 ? nq - 1 : 0);
   }
-  __syncthreads();
-  if (tid < C && bin >= S.bstar) {
+  if (tid < C && bin >= bstar) {
     const int slot = atomicAdd(&S.ncand, 1);
     if (slot < WAVE) {
       S.ckey[slot] = key;
@@ -369,13 +382,8 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
         nb = S.mb[i2];
         ab = S.ma[i2];
       }
-      int x = n;
-#pragma unroll
-      for (int off = 1; off < WAVE; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-      }
-      const int tot = __shfl(x, WAVE - 1);
+      const int x = wave_incl_scan(n);
+      const int tot = __builtin_amdgcn_readlane(x, WAVE - 1);
       S.W[lane] = x - n;
       S.obase[lane] = ob;
       S.nbase[lane] = nb;
@@ -397,12 +405,7 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
     nb = S.mb[id];
     ab = S.ma[id];
   }
-  int x = n;
-#pragma unroll
-  for (int off = 1; off < WAVE; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_incl_scan(n);
   if (lane == WAVE - 1) S.wsum[w] = x;
   __syncthreads();
   int base = 0, tot = 0;
