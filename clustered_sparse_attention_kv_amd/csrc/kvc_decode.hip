@@ -374,7 +374,11 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
     if (w == 0) {
       unsigned long long k2 = lane < ncand ? S.ckey[lane] : 0ull;
       int i2 = lane < ncand ? S.cid[lane] : C + lane;
-      bitonic_sort<2, WAVE>(S, k2, i2, lane);
+      // a network over the smallest power of two lanes that holds them (lanes
+      // past it hold padding, which keeps its place at the end)
+      if (ncand <= 16) bitonic_sort<2, 16>(S, k2, i2, lane);
+      else if (ncand <= 32) bitonic_sort<2, 32>(S, k2, i2, lane);
+      else bitonic_sort<2, WAVE>(S, k2, i2, lane);
       int n = 0, ob = 0, nb = 0, ab = 0;
       if (i2 < C) {
         n = S.mn[i2];

@@ -600,10 +600,11 @@ MANY = synth.Workload("many_clusters_bf16", 93, heads=3, G=2, L=3000, d=128, dty
 
 def test_selection_merge_and_full_ranking():
     """Selection orders only the clusters that can be selected (a size-weighted
-    score histogram finds them) with one wave while there are at most 64, and
-    sorts every cluster beyond that: with 100 clusters, budgets needing a few,
-    about 20, more than 64 and all clusters (and sinks) select exactly as the
-    oracle, split and fused."""
+    score histogram finds them) with one wave while there are at most 64 (a
+    sorting network over 16, 32 or 64 lanes), and sorts every cluster beyond
+    that: with 100 clusters, budgets needing a few, about 20, about 40, more
+    than 64 and all clusters (and sinks) select exactly as the oracle, split
+    and fused."""
     w, n_sink = MANY, 5
     base, K, V, _, means = make_inputs(w)
     H = K.shape[0]
@@ -616,7 +617,7 @@ def test_selection_merge_and_full_ranking():
     c, sizes, offsets, token_ids = (to_np(idx.centroids), to_np(idx.sizes), to_np(idx.offsets),
                                     to_np(idx.token_ids))
     scale = 1.0 / math.sqrt(w.d)
-    for step, B in enumerate([3, 40, 300, 700, 2500, w.L + 60]):
+    for step, B in enumerate([3, 40, 300, 700, 1300, 2500, w.L + 60]):
         q = queries(w, base, step, K, w.L, means)
         osel, ocnt, _, order = oracle.select(q, w.G, c, sizes, offsets, token_ids, B, n_sink=n_sink)
         # clusters the budget reaches (the count of ranks the selection needs)
