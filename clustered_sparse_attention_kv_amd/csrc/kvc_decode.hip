@@ -199,6 +199,7 @@ struct SelShared {
   unsigned long long ckey[WAVE];                            // candidates (any order)
   int cid[WAVE];
   int ncand;
+  int nrank;  // ranks that can hold clusters: 64 after the candidates' sort, else all
 };
 
 // Value of lane (lane ^ S) within the wave: DPP quad permutes for S = 1, 2;
@@ -393,7 +394,10 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
       S.nbase[lane] = nb;
       S.abase[lane] = ab;
       for (int r = WAVE + lane; r < SEL_THREADS; r += WAVE) S.W[r] = tot;
-      if (lane == 0) S.total = tot;
+      if (lane == 0) {
+        S.total = tot;
+        S.nrank = WAVE;
+      }
       fid = i2;
     }
     __syncthreads();
@@ -422,7 +426,10 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
   S.obase[tid] = ob;
   S.nbase[tid] = nb;
   S.abase[tid] = ab;
-  if (tid == 0) S.total = tot;
+  if (tid == 0) {
+    S.total = tot;
+    S.nrank = SEL_THREADS;
+  }
   __syncthreads();
   return id;
 }
@@ -455,13 +462,30 @@ __device__ __forceinline__ int select_emit(const SelShared& S, int p, const int3
                                            const int32_t* __restrict__ app_h, bool packed, const IndexView& X) {
   if (p < X.n_sink + X.nw) return fixed_entry(p, packed, X);
   p -= X.n_sink + X.nw;
-  int lo = 0, hi = SEL_THREADS - 1;  // last r with W[r] <= p
+  int lo = 0, hi = S.nrank - 1;  // last r with W[r] <= p
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (S.W[mid] <= p) lo = mid;
     else hi = mid - 1;
   }
   return rank_entry(S, lo, p - S.W[lo], ids_h, app_h, packed);
+}
+
+// select_emit for two positions (p2 < 0: none), the two searches over the
+// ranks interleaved so that their LDS round trips overlap.
+__device__ __forceinline__ void select_emit2(const SelShared& S, int p1, int p2, const int32_t* __restrict__ ids_h,
+                                             const int32_t* __restrict__ app_h, bool packed, const IndexView& X,
+                                             int& e1, int& e2) {
+  const int fixed = X.n_sink + X.nw;
+  const int q1 = p1 - fixed, q2 = p2 - fixed;
+  int r1 = 0, r2 = 0;  // last r with W[r] <= q (the ranks' starts do not decrease)
+  for (int step = S.nrank >> 1; step >= 1; step >>= 1) {
+    const int w1 = S.W[r1 + step], w2 = S.W[r2 + step];
+    r1 += w1 <= q1 ? step : 0;
+    r2 += w2 <= q2 ? step : 0;
+  }
+  e1 = q1 < 0 ? fixed_entry(p1, packed, X) : rank_entry(S, r1, q1 - S.W[r1], ids_h, app_h, packed);
+  if (p2 >= 0) e2 = q2 < 0 ? fixed_entry(p2, packed, X) : rank_entry(S, r2, q2 - S.W[r2], ids_h, app_h, packed);
 }
 
 // Calls f(p, entry) for every position p in [p0, p1) of the selection (p1 <=
@@ -925,6 +949,16 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
   if (h >= heads) return;  // whole block: the grid covers heads rounded up to 8
   const int vgrp = lane / (HC / 8), vgl = lane % (HC / 8);  // value row in the load, 8-channel chunk
   const int j16 = lane & 15, kb4 = lane >> 4;
+  // queries as the B operand: column = query head (lane % 16 < G), k-step s
+  // holds channels 32 s + 8 (lane / 16) .. + 7; read first, so that their
+  // latency passes during the selection
+  bf16x8 qb[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (j16 < G) v = *reinterpret_cast<const u32x4*>(q + ((size_t)h * G + j16) * D + 32 * s + 8 * kb4);
+    qb[s] = __builtin_bit_cast(bf16x8, v);
+  }
   select_phase(S, q, G, X, h, B);
   const int cnt = select_count(S, X, B);
   const long long cap = X.cap;
@@ -939,15 +973,6 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
   const uint16_t* Kph = kp + (size_t)h * cap * D + 8 * kb4;
   const uint16_t* Vph = vp + (size_t)h * cap * D + HC * part + 8 * vgl;
 
-  // queries as the B operand: column = query head (lane % 16 < G), k-step s
-  // holds channels 32 s + 8 (lane / 16) .. + 7
-  bf16x8 qb[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (j16 < G) v = *reinterpret_cast<const u32x4*>(q + ((size_t)h * G + j16) * D + 32 * s + 8 * kb4);
-    qb[s] = __builtin_bit_cast(bf16x8, v);
-  }
   // per query head: the wave's running maximum (uniform), this lane's share
   // of the sum of weights, and the partial output of this lane's channels
   float o[G][8], m_run[G], l_run[G];
@@ -961,12 +986,23 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
 
   for (int base = 0; base < cnt; base += EMIT) {
     const int nb = cnt - base < EMIT ? cnt - base : EMIT;
-    if (base > 0) __syncthreads();  // every wave is done with the previous ids
-    select_expand(S, base, base + nb, ids_h, app_h, packed, X, [&](int p, int ent) {
-      sel[p - base] = ent;
-      if (writer && sel_ids) sel_ids[(size_t)h * B + p] = sel_token(ids_h, ent, packed);
-    });
-    __syncthreads();
+    // each wave stages the entries of its own slices (w, w + 8, ... of 64),
+    // one search over the ranks per entry, and starts on them with no block
+    // barrier: no wave reads another's part of sel
+    for (int t = w * 64 + lane; t < nb; t += 2 * NW * 64) {
+      const int t2 = t + NW * 64;  // the next slice's entry, searched alongside
+      int e1, e2 = 0;
+      select_emit2(S, base + t, t2 < nb ? base + t2 : -1, ids_h, app_h, packed, X, e1, e2);
+      sel[t] = e1;
+      if (t2 < nb) sel[t2] = e2;
+      if (writer && sel_ids) {
+        sel_ids[(size_t)h * B + base + t] = sel_token(ids_h, e1, packed);
+        if (t2 < nb) sel_ids[(size_t)h * B + base + t2] = sel_token(ids_h, e2, packed);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     for (int t0 = w * 64; t0 < nb; t0 += NW * 64) {
       const int n64 = nb - t0 < 64 ? nb - t0 : 64;
       bf16x8 ka[4][4];
