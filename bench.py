@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--decode-path", choices=["fused", "split"], default="fused",
                     help="fused: kv_cluster_select_decode (one kernel per step); "
                          "split: kv_cluster_select then kv_sparse_decode")
+    ap.add_argument("--token-split", choices=["auto", "on", "off"], default="auto",
+                    help="fused path: give kv_cluster_select_decode a workspace, so that the blocks of a KV head "
+                         "split the selected tokens and a second kernel merges them (auto: below 128 KV heads)")
     ap.add_argument("--sinks", type=int, default=0,
                     help="attention sinks per head: kept out of the clustering, always selected (default 0)")
     ap.add_argument("--metric", choices=["cosine", "l2", "inner_product"], default="cosine",
@@ -230,6 +233,9 @@ def main():
     log(f"[bench] generated {w.name} inputs ({NL} layer(s)) in {time.time() - t0:.1f}s")
     ws_build = torch.empty(kvc.build_workspace_bytes(H, L, C, w.iters), dtype=torch.uint8, device=dev)
     ws_dec = torch.empty(kvc.decode_workspace_bytes(H, H * G, B), dtype=torch.uint8, device=dev)
+    tsplit = fused and (args.token_split == "on" or (args.token_split == "auto" and H < 128))
+    ws_sd = (torch.empty(kvc.select_decode_workspace_bytes(H, H * G), dtype=torch.uint8, device=dev)
+             if tsplit else None)
     ws_win = (torch.empty(kvc.window_workspace_bytes(H, M, NC, w.iters), dtype=torch.uint8, device=dev)
               if M else None)
     ws_cache = (torch.empty(kvc.cache_workspace_bytes(H, H * G, B), dtype=torch.uint8, device=dev)
@@ -304,7 +310,7 @@ def main():
                                              workspace=ws_cache)
                 elif fused:
                     rec(3)
-                    kvc.select_decode(e["idx"], e["Qd"][s], e["Kh"], e["Vh"], B, scale, out=out)
+                    kvc.select_decode(e["idx"], e["Qd"][s], e["Kh"], e["Vh"], B, scale, out=out, workspace=ws_sd)
                 else:
                     kvc.select(e["idx"], e["Qd"][s], B, sel, cnt)
                     rec(3)
@@ -397,6 +403,8 @@ def main():
                                "share": dd_ms * n_dec * NL / total_ms}
         kernel_names["select_decode"] = ("select_decode_bf16_kernel" if w.dtype == synth.BF16
                                          else "select_decode_kernel")
+        if ws_sd is not None and w.dtype == synth.BF16 and G <= 4:
+            kernel_names["select_decode"] = "select_decode_bf16_kernel (token split) + decode_combine_kernel"
         if offload >= 1:
             kernel_names["select_decode"] = "cache_assemble_kernel + decode_split_kernel + decode_combine_kernel"
     else:
@@ -439,7 +447,7 @@ def main():
         "config": {"workload": w.name, "layers": NL, "kv_heads_total": H * NL, "q_heads_total": H * G * NL, "G": G,
                    "L": L, "d": d, "C": C,
                    "kmeans_iters": w.iters, "B": B, "decode_steps_per_step": w.steps, "append": w.append,
-                   "decode_path": args.decode_path, "packed_kv": packed,
+                   "decode_path": args.decode_path, "token_split": ws_sd is not None, "packed_kv": packed,
                    "sinks": args.sinks, "window": M, "window_clusters": NC if M else 0, "metric": args.metric,
                    "offload": offload, "query_drift": args.drift},
         "kmeans_tflops": kmeans_tflops,

@@ -70,7 +70,9 @@ def lib():
         L.kv_sparse_decode_workspace_bytes.argtypes = [i, i, i, i]
         L.kv_sparse_decode_workspace_bytes.restype = sz
         L.kv_sparse_decode.argtypes = [p, i, p, p, i, i, i, i, p, p, i, f, p, p, sz, p]
-        L.kv_cluster_select_decode.argtypes = [p, p, i, p, p, i, f, p, p, p, p]
+        L.kv_cluster_select_decode_workspace_bytes.argtypes = [i, i, i]
+        L.kv_cluster_select_decode_workspace_bytes.restype = sz
+        L.kv_cluster_select_decode.argtypes = [p, p, i, p, p, i, f, p, p, p, p, sz, p]
         L.kv_cluster_export_csr.argtypes = [p, p, p, p]
         L.kv_cluster_pack.argtypes = [p, p, p, p]
         L.kv_dense_decode_workspace_bytes.argtypes = [i, i, i, i]
@@ -368,10 +370,16 @@ def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out
 
 
+def select_decode_workspace_bytes(heads: int, q_heads: int, d: int = HEAD_DIM) -> int:
+    return int(lib().kv_cluster_select_decode_workspace_bytes(heads, q_heads, d))
+
+
 def select_decode(idx: ClusterIndex, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, B: int,
                   scale: float, out: torch.Tensor | None = None, sel_ids: torch.Tensor | None = None,
-                  sel_count: torch.Tensor | None = None, stream=None):
-    """kv_cluster_select_decode: selection and sparse attention in one kernel -> fp32 [q_heads, d]."""
+                  sel_count: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """kv_cluster_select_decode: selection and sparse attention -> fp32 [q_heads, d]. Without a workspace
+    one kernel; with one (select_decode_workspace_bytes), the blocks of a head split the tokens and a
+    second kernel merges their partial results."""
     _cache_check(idx, k_cache, "k_cache")
     _cache_check(idx, v_cache, "v_cache")
     if q.dtype != idx.dtype or q.dim() != 2 or q.shape[1] != idx.d:
@@ -382,8 +390,10 @@ def select_decode(idx: ClusterIndex, q: torch.Tensor, k_cache: torch.Tensor, v_c
         raise ValueError("sel_ids must be int32 [heads, B]")
     if sel_count is not None and (sel_count.dtype != torch.int32 or sel_count.numel() != idx.heads):
         raise ValueError("sel_count must be int32 [heads]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().kv_cluster_select_decode(idx.ref(), _ptr(q), q.shape[0], _ptr_kv(k_cache), _ptr_kv(v_cache), B,
-                                          float(scale), _ptr(out), _ptr(sel_ids), _ptr(sel_count), _stream(stream)),
+                                          float(scale), _ptr(out), _ptr(sel_ids), _ptr(sel_count), _ptr(workspace),
+                                          ws_bytes, _stream(stream)),
            "kv_cluster_select_decode")
     return out
 

@@ -343,20 +343,29 @@ int kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void
                                   scale, out, static_cast<float*>(ws), static_cast<hipStream_t>(stream)));
 }
 
+size_t kv_cluster_select_decode_workspace_bytes(int heads, int q_heads, int d) {
+  if (heads < 1 || q_heads < heads || d < 1) return 0;
+  const int G = q_heads / heads;
+  return align_up(sizeof(float) * heads * fused_blocks_per_head(heads) * G * (d + 2));
+}
+
 int kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, const void* k_cache,
                              const void* v_cache, int B, float scale, float* out, int32_t* sel_ids,
-                             int32_t* sel_count, void* stream) {
+                             int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
   if (!index_ok(idx) || !q || !k_cache || !v_cache || !out || B < 1 || q_heads < 1) return KVC_ERR_INVALID_ARG;
   if (int s = index_support(idx)) return s;
   if (!built_ok(idx) || q_heads % idx->heads != 0) return KVC_ERR_INVALID_ARG;
   const int G = q_heads / idx->heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVC_ERR_UNSUPPORTED;
   if ((long long)idx->heads * B >= (1ll << 31)) return KVC_ERR_INVALID_ARG;
+  if (ws && ws_bytes < kv_cluster_select_decode_workspace_bytes(idx->heads, q_heads, idx->d)) return KVC_ERR_WORKSPACE;
   const IndexView x = view(idx);
   const bool packed = idx->packed == 1 && idx->k_packed && idx->v_packed;
+  // the token split exists for bf16 and at most 4 query heads per KV head
+  float* part = ws && idx->dtype == KVC_BF16 && G <= 4 ? static_cast<float*>(ws) : nullptr;
   return hip_status(launch_select_decode(idx->dtype, q, G, x, idx->heads, k_cache, v_cache,
                                          packed ? idx->k_packed : nullptr, packed ? idx->v_packed : nullptr, B, scale,
-                                         out, sel_ids, sel_count, static_cast<hipStream_t>(stream)));
+                                         out, sel_ids, sel_count, part, static_cast<hipStream_t>(stream)));
 }
 
 int kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, void* stream) {

@@ -918,22 +918,26 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
 //    the max and sum (DPP reductions), and back as weights;
 //  - the value rows are gathered and weighted in fp32 on the vector units.
 // P blocks share each KV head (P = 2, or 4 and 8 when there are few heads,
-// so that the grid still covers the chip): all select and score all keys,
-// and block `part` gathers and weights channels [part D / P, (part + 1) D / P)
-// of the values (8 channels per lane), writing those output channels. The
+// so that the grid still covers the chip), and all of them select. Then
+// either (TS false) all score all keys, and block `part` gathers and weights
+// channels [part D / P, (part + 1) D / P) of the values (8 channels per
+// lane), writing those output channels; or (TS true) block `part` takes the
+// 64-entry slices part, part + P, ... with all channels and writes its
+// partial result (running maximum, sum, unnormalised output per query head)
+// to part_out [heads, P, G, D + 2], which decode_combine_kernel merges. The
 // blocks of a head get block indices 8 apart, so the round-robin dispatch
 // over the 8 XCDs places them on one XCD and its L2 serves the repeated reads
 // of the keys and centroids; results do not depend on the placement.
-template <int G, int P>
+template <int G, int P, bool TS>
 __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     const uint16_t* __restrict__ q, const IndexView X, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, int packed,
     int heads, int B, float qscale, float* __restrict__ out, int32_t* __restrict__ sel_ids,
-    int32_t* __restrict__ sel_count) {
+    int32_t* __restrict__ sel_count, float* __restrict__ part_out) {
   static_assert(G <= 8, "at most 8 query heads per KV head");
   constexpr int NW = SEL_THREADS / WAVE;
   constexpr int EMIT = 2048;                 // selected ids staged per pass
-  constexpr int HC = D / P;                  // value channels per block
+  constexpr int HC = TS ? D : D / P;         // value channels per block
   constexpr int RPS = WAVE / (HC / 8);       // value rows per load instruction (8 with 64 channels)
   constexpr int VR = 64 / RPS;               // value rows per lane per slice
   __shared__ SelShared S;
@@ -962,16 +966,20 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
   select_phase(S, q, G, X, h, B);
   const int cnt = select_count(S, X, B);
   const long long cap = X.cap;
-  const bool writer = part == 0;  // one block per head publishes the selection
+  // one block per head publishes the count and the unused entries; the
+  // selected entries come from the block that stages them (all from block 0
+  // without the token split)
+  const bool writer = part == 0;
   if (writer && sel_count && tid == 0) sel_count[h] = cnt;
   if (writer && sel_ids)
     for (int p = cnt + tid; p < B; p += SEL_THREADS) sel_ids[(size_t)h * B + p] = -1;
   const int32_t* ids_h = X.token_ids + (size_t)h * cap;
   const int32_t* app_h = X.app_ids + (size_t)h * cap;
+  const int vch = TS ? 0 : HC * part;  // the block's first value channel
   const uint16_t* Kh = kc + (size_t)h * cap * D + 8 * kb4;
-  const uint16_t* Vh = vc + (size_t)h * cap * D + HC * part + 8 * vgl;
+  const uint16_t* Vh = vc + (size_t)h * cap * D + vch + 8 * vgl;
   const uint16_t* Kph = kp + (size_t)h * cap * D + 8 * kb4;
-  const uint16_t* Vph = vp + (size_t)h * cap * D + HC * part + 8 * vgl;
+  const uint16_t* Vph = vp + (size_t)h * cap * D + vch + 8 * vgl;
 
   // per query head: the wave's running maximum (uniform), this lane's share
   // of the sum of weights, and the partial output of this lane's channels
@@ -984,112 +992,132 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     for (int c = 0; c < 8; ++c) o[g][c] = 0.f;
   }
 
-  for (int base = 0; base < cnt; base += EMIT) {
-    const int nb = cnt - base < EMIT ? cnt - base : EMIT;
-    // each wave stages the entries of its own slices (w, w + 8, ... of 64),
-    // one search over the ranks per entry, and starts on them with no block
-    // barrier: no wave reads another's part of sel
-    for (int t = w * 64 + lane; t < nb; t += 2 * NW * 64) {
-      const int t2 = t + NW * 64;  // the next slice's entry, searched alongside
-      int e1, e2 = 0;
-      select_emit2(S, base + t, t2 < nb ? base + t2 : -1, ids_h, app_h, packed, X, e1, e2);
-      sel[t] = e1;
-      if (t2 < nb) sel[t2] = e2;
-      if (writer && sel_ids) {
-        sel_ids[(size_t)h * B + base + t] = sel_token(ids_h, e1, packed);
-        if (t2 < nb) sel_ids[(size_t)h * B + base + t2] = sel_token(ids_h, e2, packed);
-      }
+  // one slice: the n64 (<= 64) entries staged at ss, gathered, scored and
+  // folded into the wave's running state
+  auto do_slice = [&](const int* ss, int n64) {
+    bf16x8 ka[4][4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const int t = T * 16 + j16;
+      const int id = t < n64 ? ss[t] : 0;
+      const uint16_t* src = sel_row(Kph, Kh, id);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        ka[T][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 32 * s));
+    }
+    Row8<uint16_t> vrow[VR];
+#pragma unroll
+    for (int r = 0; r < VR; ++r) {
+      const int t = r * RPS + vgrp;
+      const int id = t < n64 ? ss[t] : 0;
+      vrow[r].load(sel_row(Vph, Vh, id));
+    }
+    f32x4 acc[4] = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[T][s], qb[s], acc[T], 0, 0, 0);
+    // score of (row 16 T + 4 (lane / 16) + r, query head lane % 16) -> pw[w][row][g]
+    if (j16 < G) {
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = T * 16 + 4 * kb4 + r;
+          pw[w][t][j16] = t < n64 ? acc[T][r] * qscale : -INFINITY;
+        }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int t0 = w * 64; t0 < nb; t0 += NW * 64) {
-      const int n64 = nb - t0 < 64 ? nb - t0 : 64;
-      bf16x8 ka[4][4];
+    // lane = token of the slice: its G scores become weights. The running
+    // maximum moves (and the partial results are rescaled) only when the
+    // slice holds a larger score; the sums stay per lane until the end.
+    {
+      float sv[GP];
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        const int t = T * 16 + j16;
-        const int id = t < n64 ? sel[t0 + t] : 0;
-        const uint16_t* src = sel_row(Kph, Kh, id);
+      for (int g4 = 0; g4 < GP; g4 += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&pw[w][lane][g4]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          ka[T][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 32 * s));
+        for (int i = 0; i < 4; ++i) sv[g4 + i] = x[i];
       }
-      Row8<uint16_t> vrow[VR];
 #pragma unroll
-      for (int r = 0; r < VR; ++r) {
-        const int t = r * RPS + vgrp;
-        const int id = t < n64 ? sel[t0 + t] : 0;
-        vrow[r].load(sel_row(Vph, Vh, id));
+      for (int g = 0; g < G; ++g) {
+        const float smax = wave_max(sv[g]);
+        if (smax > m_run[g]) {  // uniform over the wave
+          const float f = m_run[g] == -INFINITY ? 0.f : exp2f(m_run[g] - smax);
+          l_run[g] *= f;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o[g][c] *= f;
+          m_run[g] = smax;
+        }
+        const float pv = m_run[g] == -INFINITY ? 0.f : exp2f(sv[g] - m_run[g]);
+        sv[g] = pv;
+        l_run[g] += pv;
       }
-      f32x4 acc[4] = {};
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int g4 = 0; g4 < GP; g4 += 4)
+        *reinterpret_cast<f32x4*>(&pw[w][lane][g4]) = f32x4{sv[g4], sv[g4 + 1], sv[g4 + 2], sv[g4 + 3]};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[T][s], qb[s], acc[T], 0, 0, 0);
-      // score of (row 16 T + 4 (lane / 16) + r, query head lane % 16) -> pw[w][row][g]
-      if (j16 < G) {
+    for (int r = 0; r < VR; ++r) {
+      const int t = r * RPS + vgrp;
+      float pv[GP];
 #pragma unroll
-        for (int T = 0; T < 4; ++T)
+      for (int g4 = 0; g4 < GP; g4 += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&pw[w][t][g4]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = T * 16 + 4 * kb4 + r;
-            pw[w][t][j16] = t < n64 ? acc[T][r] * qscale : -INFINITY;
-          }
+        for (int i = 0; i < 4; ++i) pv[g4 + i] = x[i];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[g][c] = fmaf(pv[g], vrow[r].at(c), o[g][c]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  if constexpr (!TS) {
+    for (int base = 0; base < cnt; base += EMIT) {
+      const int nb = cnt - base < EMIT ? cnt - base : EMIT;
+      // each wave stages the entries of its own slices (w, w + 8, ... of 64),
+      // one search over the ranks per entry, and starts on them with no block
+      // barrier: no wave reads another's part of sel
+      for (int t = w * 64 + lane; t < nb; t += 2 * NW * 64) {
+        const int t2 = t + NW * 64;  // the next slice's entry, searched alongside
+        int e1, e2 = 0;
+        select_emit2(S, base + t, t2 < nb ? base + t2 : -1, ids_h, app_h, packed, X, e1, e2);
+        sel[t] = e1;
+        if (t2 < nb) sel[t2] = e2;
+        if (writer && sel_ids) {
+          sel_ids[(size_t)h * B + base + t] = sel_token(ids_h, e1, packed);
+          if (t2 < nb) sel_ids[(size_t)h * B + base + t2] = sel_token(ids_h, e2, packed);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // lane = token of the slice: its G scores become weights. The running
-      // maximum moves (and the partial results are rescaled) only when the
-      // slice holds a larger score; the sums stay per lane until the end.
-      {
-        float sv[GP];
-#pragma unroll
-        for (int g4 = 0; g4 < GP; g4 += 4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&pw[w][lane][g4]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sv[g4 + i] = x[i];
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float smax = wave_max(sv[g]);
-          if (smax > m_run[g]) {  // uniform over the wave
-            const float f = m_run[g] == -INFINITY ? 0.f : exp2f(m_run[g] - smax);
-            l_run[g] *= f;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) o[g][c] *= f;
-            m_run[g] = smax;
-          }
-          const float pv = m_run[g] == -INFINITY ? 0.f : exp2f(sv[g] - m_run[g]);
-          sv[g] = pv;
-          l_run[g] += pv;
-        }
-#pragma unroll
-        for (int g4 = 0; g4 < GP; g4 += 4)
-          *reinterpret_cast<f32x4*>(&pw[w][lane][g4]) = f32x4{sv[g4], sv[g4 + 1], sv[g4 + 2], sv[g4 + 3]};
+      for (int t0 = w * 64; t0 < nb; t0 += NW * 64) do_slice(sel + t0, nb - t0 < 64 ? nb - t0 : 64);
+    }
+  } else {
+    // slices part, part + P, ...: wave w takes the block's slices w, w + 8, ...
+    // and stages each one's entries in its own 64 words of sel
+    for (int sl = part + P * w; sl * 64 < cnt; sl += P * NW) {
+      const int t0 = sl * 64, n64 = cnt - t0 < 64 ? cnt - t0 : 64;
+      if (lane < n64) {
+        const int ent = select_emit(S, t0 + lane, ids_h, app_h, packed, X);
+        sel[w * 64 + lane] = ent;
+        if (sel_ids) sel_ids[(size_t)h * B + t0 + lane] = sel_token(ids_h, ent, packed);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int r = 0; r < VR; ++r) {
-        const int t = r * RPS + vgrp;
-        float pv[GP];
-#pragma unroll
-        for (int g4 = 0; g4 < GP; g4 += 4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&pw[w][t][g4]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pv[g4 + i] = x[i];
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) o[g][c] = fmaf(pv[g], vrow[r].at(c), o[g][c]);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      do_slice(sel + w * 64, n64);
     }
   }
   // merge: the row groups of each wave (lanes 8 apart share channels), then the 8 waves
@@ -1135,7 +1163,16 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
         O = fmaf(f, ored[v][g][j], O);
       }
     }
-    out[((size_t)h * G + g) * D + HC * part + j] = L > 0.f ? O / L : 0.f;
+    if constexpr (TS) {
+      float* pd = part_out + (((size_t)h * P + part) * G + g) * (D + 2);
+      pd[j] = O;
+      if (j == 0) {
+        pd[D] = M;
+        pd[D + 1] = L;
+      }
+    } else {
+      out[((size_t)h * G + g) * D + HC * part + j] = L > 0.f ? O / L : 0.f;
+    }
   }
 }
 
@@ -1579,6 +1616,8 @@ hipError_t launch_cache_assemble(int dtype, const void* q, int G, const IndexVie
   return hipGetLastError();
 }
 
+int fused_blocks_per_head(int heads);
+
 struct FusedArgs {
   const void* q;
   IndexView x;
@@ -1588,20 +1627,30 @@ struct FusedArgs {
   float qscale;
   float* out;
   int32_t *sel_ids, *sel_count;
+  float* part;  // partial results of the token split, or null
 };
 
 template <typename KT, int G>
 static void launch_fused(const FusedArgs& a, hipStream_t st) {
   if constexpr (sizeof(KT) == 2) {
     // enough blocks per head that the grid covers the 256 compute units
-    const int P = a.heads >= 128 ? 2 : (a.heads >= 64 ? 4 : 8);
+    const int P = fused_blocks_per_head(a.heads);
     const int nb = (a.heads + 7) / 8 * 8 * P;
 #define KVC_FUSED_ARGS                                                                                          \
   (const uint16_t*)a.q, a.x, (const uint16_t*)a.kc, (const uint16_t*)a.vc, (const uint16_t*)a.kp,             \
-      (const uint16_t*)a.vp, a.packed, a.heads, a.B, a.qscale, a.out, a.sel_ids, a.sel_count
-    if (P == 2) select_decode_bf16_kernel<G, 2><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
-    else if (P == 4) select_decode_bf16_kernel<G, 4><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
-    else select_decode_bf16_kernel<G, 8><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
+      (const uint16_t*)a.vp, a.packed, a.heads, a.B, a.qscale, a.out, a.sel_ids, a.sel_count, a.part
+    if constexpr (G <= 4) {
+      if (a.part) {  // token split, then the merge of the P partial results
+        if (P == 2) select_decode_bf16_kernel<G, 2, true><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
+        else if (P == 4) select_decode_bf16_kernel<G, 4, true><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
+        else select_decode_bf16_kernel<G, 8, true><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
+        decode_combine_kernel<<<a.heads, 256, 0, st>>>(a.part, P, G, a.out);
+        return;
+      }
+    }
+    if (P == 2) select_decode_bf16_kernel<G, 2, false><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
+    else if (P == 4) select_decode_bf16_kernel<G, 4, false><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
+    else select_decode_bf16_kernel<G, 8, false><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
 #undef KVC_FUSED_ARGS
   }
   else
@@ -1622,11 +1671,15 @@ static hipError_t fused_dispatch(int G, const FusedArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Blocks per KV head of the fused kernel: enough that the grid covers the
+// 256 compute units.
+int fused_blocks_per_head(int heads) { return heads >= 128 ? 2 : (heads >= 64 ? 4 : 8); }
+
 hipError_t launch_select_decode(int dtype, const void* q, int G, const IndexView& x, int heads, const void* kc,
                                 const void* vc, const void* kp, const void* vp, int B, float scale, float* out,
-                                int32_t* sel_ids, int32_t* sel_count, hipStream_t st) {
+                                int32_t* sel_ids, int32_t* sel_count, float* part, hipStream_t st) {
   FusedArgs a{q, x, heads, kc, vc, kp ? kp : kc, vp ? vp : vc, kp && vp ? 1 : 0, B, scale * 1.4426950408889634f,
-              out, sel_ids, sel_count};
+              out, sel_ids, sel_count, part};
   if (dtype == DT_BF16) return fused_dispatch<uint16_t>(G, a, st);
   return fused_dispatch<float>(G, a, st);
 }

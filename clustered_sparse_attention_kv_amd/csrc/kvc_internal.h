@@ -68,7 +68,8 @@ hipError_t launch_decode(int dtype, const void* q, int G, const void* kc, const 
                          float* part, hipStream_t st);
 hipError_t launch_select_decode(int dtype, const void* q, int G, const IndexView& x, int heads, const void* kc,
                                 const void* vc, const void* kp, const void* vp, int B, float scale, float* out,
-                                int32_t* sel_ids, int32_t* sel_count, hipStream_t st);
+                                int32_t* sel_ids, int32_t* sel_count, float* part, hipStream_t st);
+int fused_blocks_per_head(int heads);
 // kp, vp: the packed copies (both non-null) or null (rows from the caches).
 // The cluster cache's step: selection, then the selected rows assembled into
 // region t mod (R + 1) of ck / cv ([heads, (R + 1) * B, d]) from the cache or

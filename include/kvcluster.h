@@ -286,17 +286,27 @@ int kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void
 int kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, void* stream);
 
 /*
- * kv_cluster_select followed by kv_sparse_decode in one kernel (one block per
- * KV head): the same selection and the same attention, without the selected
- * ids leaving the chip. With idx->packed set, the selected built tokens are
- * read from the packed copy (the same values, consecutive rows per cluster). k_cache and v_cache are [heads, idx->capacity, d] in
- * idx->dtype; q is [q_heads, d]; out is fp32 [q_heads, d]. sel_ids [heads, B]
- * and sel_count [heads] are optional (NULL) copies of the selection.
- * Requires G = q_heads / heads in {1, 2, 4, 8}. No workspace.
+ * kv_cluster_select followed by kv_sparse_decode in one kernel (several
+ * blocks per KV head, each making the selection): the same selection and the
+ * same attention, without the selected ids leaving the chip. With
+ * idx->packed set, the selected built tokens are read from the packed copy
+ * (the same values, consecutive rows per cluster). k_cache and v_cache are
+ * [heads, idx->capacity, d] in idx->dtype; q is [q_heads, d]; out is fp32
+ * [q_heads, d]. sel_ids [heads, B] and sel_count [heads] are optional (NULL)
+ * copies of the selection. Requires G = q_heads / heads in {1, 2, 4, 8}.
+ * ws is optional. Without it, every block of a head scores all the selected
+ * keys and weights a share of the value channels. With it (at least
+ * kv_cluster_select_decode_workspace_bytes(heads, q_heads, d) bytes, contents
+ * need not be initialised; bf16 and G <= 4 only, otherwise unused), the
+ * blocks of a head split the selected tokens instead, write partial results
+ * (running maximum, sum and output) to ws, and a second kernel merges them:
+ * the same attention up to fp32 summation order. ws_bytes is ignored when ws
+ * is NULL; a smaller ws gives KVC_ERR_WORKSPACE.
  */
+size_t kv_cluster_select_decode_workspace_bytes(int heads, int q_heads, int d);
 int kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, const void* k_cache,
                              const void* v_cache, int B, float scale, float* out, int32_t* sel_ids,
-                             int32_t* sel_count, void* stream);
+                             int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * GPU cache of selected clusters for offloaded KV (Sys-A: the KV lives in CPU

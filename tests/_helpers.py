@@ -44,3 +44,11 @@ def queries(w, base, step: int, K: np.ndarray, n_cur: int, means, heads: int | N
     if w.query == "mixture":
         return synth.queries_mixture(base, step, H * w.G, w.G, means, w.q_sigma, w.dtype)
     return synth.queries_noisy_key(base, step, H * w.G, w.G, K, n_cur, w.q_sigma)
+
+
+def split_ws(idx, q_heads: int) -> torch.Tensor:
+    """Workspace for the token split of the fused selection and attention, filled with NaN bytes (its
+    contents must not matter)."""
+    import clustered_sparse_attention_kv_amd as kvc
+    return torch.full((kvc.select_decode_workspace_bytes(idx.heads, q_heads, idx.d),), 0xFF, dtype=torch.uint8,
+                      device="cuda")

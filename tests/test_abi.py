@@ -103,8 +103,12 @@ def test_append_select_decode_reject(kvc):
     assert L.kv_cluster_select(C.byref(built), p, 16, 0, p, p, None) == INVALID
     assert L.kv_cluster_select(C.byref(make_index(kvc)), p, 16, 64, p, p, None) == INVALID
     f = C.c_float(0.1)
-    assert L.kv_cluster_select_decode(C.byref(built), p, 12, p, p, 64, f, p, None, None, None) == UNSUPPORTED
-    assert L.kv_cluster_select_decode(C.byref(built), p, 16, None, p, 64, f, p, None, None, None) == INVALID
+    assert L.kv_cluster_select_decode(C.byref(built), p, 12, p, p, 64, f, p, None, None, None, 0, None) == UNSUPPORTED
+    assert L.kv_cluster_select_decode(C.byref(built), p, 16, None, p, 64, f, p, None, None, None, 0, None) == INVALID
+    sd_ws = L.kv_cluster_select_decode_workspace_bytes(4, 16, 128)
+    assert sd_ws >= 4 * 8 * 4 * 130 * 4  # 4 heads x 8 blocks x 4 query heads x (128 + 2) floats
+    assert L.kv_cluster_select_decode(C.byref(built), p, 16, p, p, 64, f, p, None, None, p, sd_ws - 1,
+                                      None) == WORKSPACE
     ws = L.kv_sparse_decode_workspace_bytes(4, 16, 128, 64)
     dec = lambda **k: L.kv_sparse_decode(p, k.get("qh", 16), p, p, k.get("dt", 1), 4, 256, k.get("d", 128), p, p,
                                          k.get("B", 64), f, p, p, k.get("ws", ws), None)

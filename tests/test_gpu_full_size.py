@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import synth
-from _helpers import queries, to_dev, to_np
+from _helpers import queries, split_ws, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 kvc = pytest.importorskip("clustered_sparse_attention_kv_amd")
@@ -65,6 +65,11 @@ def check_step(w, idx, K, V, Kd, Vd, q, B, scale, c=None, sizes=None, offsets=No
     fsel = torch.empty(H, B, dtype=torch.int32, device="cuda")
     fcnt = torch.empty(H, dtype=torch.int32, device="cuda")
     fout = kvc.select_decode(idx, qd, Kd, Vd, B, scale, sel_ids=fsel, sel_count=fcnt)
+    # the token split (its own copies of the selection)
+    tsel = torch.empty(H, B, dtype=torch.int32, device="cuda")
+    tcnt = torch.empty(H, dtype=torch.int32, device="cuda")
+    tout = kvc.select_decode(idx, qd, Kd, Vd, B, scale, sel_ids=tsel, sel_count=tcnt,
+                             workspace=split_ws(idx, H * w.G))
     if split:
         sel, cnt = kvc.select(idx, qd, B)
         out = kvc.sparse_decode(qd, Kd, Vd, sel, cnt, scale)
@@ -75,8 +80,9 @@ def check_step(w, idx, K, V, Kd, Vd, q, B, scale, c=None, sizes=None, offsets=No
     token_ids = to_np(idx.token_ids) if token_ids is None else token_ids
     osel, ocnt, _, _ = oracle.select(q, w.G, c, sizes, offsets, token_ids, B)
     assert np.array_equal(to_np(fcnt), ocnt) and np.array_equal(to_np(fsel), osel)
+    assert np.array_equal(to_np(tcnt), ocnt) and np.array_equal(to_np(tsel), osel)
     od = oracle.decode(q, w.G, K, V, osel, ocnt, scale)
-    ferr = float(np.abs(to_np(fout) - od).max())
+    ferr = max(float(np.abs(to_np(fout) - od).max()), float(np.abs(to_np(tout) - od).max()))
     err = float(np.abs(to_np(out) - od).max()) if split else 0.0
     if split:
         assert np.array_equal(to_np(sel), osel) and np.array_equal(to_np(cnt), ocnt)

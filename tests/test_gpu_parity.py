@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from _helpers import make_inputs, queries, to_dev, to_np, torch_dtype
+from _helpers import split_ws, make_inputs, queries, to_dev, to_np, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +25,9 @@ SMALL = synth.Workload("small_bf16_ragged", 90, heads=3, G=2, L=1500, d=128, dty
 SMALL_APPEND = synth.Workload("small_bf16_append", 91, heads=2, G=1, L=1100, d=128, dtype=synth.BF16, M=24,
                               sigma=0.3, n_out=4, out_scale=10.0, C=37, iters=5, B=300, steps=20, query="noisy_key",
                               q_sigma=0.1, append=True)
+LONG_APPEND = synth.Workload("long_append_bf16", 94, heads=2, G=1, L=600, d=128, dtype=synth.BF16, M=12,
+                             sigma=0.3, n_out=4, out_scale=10.0, C=9, iters=3, B=300, steps=4400, query="noisy_key",
+                             q_sigma=0.1, append=True)
 SMALL_WINDOW = synth.Workload("small_bf16_window", 92, heads=3, G=2, L=1100, d=128, dtype=synth.BF16, M=24,
                               sigma=0.3, n_out=4, out_scale=10.0, C=37, iters=5, B=300, steps=130,
                               query="noisy_key", q_sigma=0.1, append=True)
@@ -178,16 +181,53 @@ def check_step(w, idx, base, K, V, Kd, Vd, means, gc, step, B, scale, packed):
     assert np.array_equal(to_np(sel), osel), B
     od = oracle.decode(q, w.G, K, V, to_np(sel), to_np(cnt), scale)
     err = np.abs(to_np(out) - od).max()
-    # the fused kernel: same selection, same attention
-    fsel = torch.full((H, B), -7, dtype=torch.int32, device="cuda")
-    fcnt = torch.empty(H, dtype=torch.int32, device="cuda")
-    fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel, sel_count=fcnt)
-    torch.cuda.synchronize()
-    assert np.array_equal(to_np(fcnt), ocnt) and np.array_equal(to_np(fsel), osel), B
-    ferr = np.abs(to_np(fout) - od).max()
+    # the fused kernel (one kernel, then the token split and its merge): same
+    # selection, same attention
+    ferrs = []
+    for ws in (None, split_ws(idx, H * w.G)):
+        fsel = torch.full((H, B), -7, dtype=torch.int32, device="cuda")
+        fcnt = torch.empty(H, dtype=torch.int32, device="cuda")
+        fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel, sel_count=fcnt, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(fcnt), ocnt) and np.array_equal(to_np(fsel), osel), (B, ws is None)
+        ferrs.append(np.abs(to_np(fout) - od).max())
     say(f"  B={B}{' packed' if packed else ''}: count {to_np(cnt).tolist()[:4]}, decode max abs err {err:.3e}, "
-        f"fused {ferr:.3e}")
-    assert err <= 2e-3 and ferr <= 2e-3
+        f"fused {ferrs[0]:.3e}, token split {ferrs[1]:.3e}")
+    assert err <= 2e-3 and max(ferrs) <= 2e-3
+
+
+def test_append_long_lists():
+    """Long appended lists: two calls of 2200 tokens per head (one launch
+    each, the tokens inserted in order, every insert shifting the later
+    clusters' entries); the labels, sizes and exported index equal the
+    oracle's after each call."""
+    w = LONG_APPEND
+    base, K, V, init, means = make_inputs(w)
+    H = K.shape[0]
+    idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w), packed=True)
+    Kc, Vc = np.zeros_like(K), np.zeros_like(V)
+    Kc[:, :w.L], Vc[:, :w.L] = K[:, :w.L], V[:, :w.L]
+    Kd, Vd = to_dev(Kc), to_dev(Vc)
+    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    torch.cuda.synchronize()
+    built = dict(labels=to_np(idx.labels)[:, :w.L], sizes=to_np(idx.sizes), offsets=to_np(idx.offsets),
+                 token_ids=to_np(idx.token_ids)[:, :w.L], c=to_np(idx.centroids),
+                 chat=to_np(idx.centroids_op)[:, :w.C])
+    oi = oracle.Index(built, w.capacity)
+    n = w.L
+    for nn in (2200, 2200):
+        kvc.append(idx, Kd, Vd, to_dev(np.ascontiguousarray(K[:, n:n + nn])),
+                   to_dev(np.ascontiguousarray(V[:, n:n + nn])))
+        for t in range(nn):
+            oi.append(np.ascontiguousarray(K[:, n + t]))
+        n += nn
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(idx.labels)[:, :n], oi.labels[:, :n]), n
+        assert np.array_equal(to_np(idx.sizes), oi.sizes), n
+        off, ids = kvc.export_csr(idx)
+        assert np.array_equal(to_np(off), oi.offsets), n
+        assert np.array_equal(to_np(ids)[:, :n], oi.token_ids[:, :n]), n
+    say(f"[long append] {n - w.L} tokens per head, sizes {oi.sizes[0].tolist()}")
 
 
 def test_append_then_select_decode():
@@ -230,13 +270,13 @@ def test_append_then_select_decode():
         od = oracle.decode(q, w.G, K, V, osel, ocnt, scale)
         assert np.abs(to_np(out) - od).max() <= 2e-3
         # fused, from the packed copy plus the appended rows, then from the caches alone
-        for pk in (1, 0):
+        for pk, ws in ((1, None), (0, None), (1, split_ws(idx, H * w.G)), (0, split_ws(idx, H * w.G))):
             idx._s.packed = pk
             fsel = torch.full((H, w.B), -7, dtype=torch.int32, device="cuda")
-            fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, w.B, scale, sel_ids=fsel)
+            fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, w.B, scale, sel_ids=fsel, workspace=ws)
             torch.cuda.synchronize()
-            assert np.array_equal(to_np(fsel), osel), pk
-            assert np.abs(to_np(fout) - od).max() <= 2e-3, pk
+            assert np.array_equal(to_np(fsel), osel), (pk, ws is None)
+            assert np.abs(to_np(fout) - od).max() <= 2e-3, (pk, ws is None)
         idx._s.packed = 1
     off, ids = kvc.export_csr(idx)
     assert np.array_equal(to_np(off), oi.offsets)
@@ -313,13 +353,13 @@ def test_attention_sinks_end_to_end():
             torch.cuda.synchronize()
             assert np.array_equal(to_np(sel), osel) and np.array_equal(to_np(cnt), ocnt), (step, B)
             assert np.abs(to_np(out) - od).max() <= 2e-3
-            for pk in (1, 0):
+            for pk, ws in ((1, None), (0, None), (1, split_ws(idx, H * w.G))):
                 idx._s.packed = pk
                 fsel = torch.full((H, B), -7, dtype=torch.int32, device="cuda")
-                fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel)
+                fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel, workspace=ws)
                 torch.cuda.synchronize()
-                assert np.array_equal(to_np(fsel), osel), (step, B, pk)
-                assert np.abs(to_np(fout) - od).max() <= 2e-3, (step, B, pk)
+                assert np.array_equal(to_np(fsel), osel), (step, B, pk, ws is None)
+                assert np.abs(to_np(fout) - od).max() <= 2e-3, (step, B, pk, ws is None)
             idx._s.packed = 1
         say(f"  sinks: step {step}, {n} tokens, count {ocnt.tolist()}")
 
@@ -624,13 +664,16 @@ def test_selection_merge_and_full_ranking():
         ranks = [int(np.searchsorted(np.cumsum(sizes[h][order[h]]), max(B - n_sink, 0), side="left")) + 1
                  for h in range(H)]
         sel, cnt = kvc.select(idx, to_dev(q), B)
-        fsel = torch.full((H, B), -7, dtype=torch.int32, device="cuda")
-        fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel)
         torch.cuda.synchronize()
         say(f"  B={B}: clusters reached per head {ranks}, count {ocnt.tolist()}")
         assert np.array_equal(to_np(sel), osel) and np.array_equal(to_np(cnt), ocnt), B
-        assert np.array_equal(to_np(fsel), osel), B
-        assert np.abs(to_np(fout) - oracle.decode(q, w.G, K, V, osel, ocnt, scale)).max() <= 2e-3, B
+        od = oracle.decode(q, w.G, K, V, osel, ocnt, scale)
+        for ws in (None, split_ws(idx, H * w.G)):
+            fsel = torch.full((H, B), -7, dtype=torch.int32, device="cuda")
+            fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel, workspace=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_np(fsel), osel), (B, ws is None)
+            assert np.abs(to_np(fout) - od).max() <= 2e-3, (B, ws is None)
 
 
 def test_graph_replay_matches_eager():
