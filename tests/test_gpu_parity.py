@@ -416,13 +416,13 @@ def test_window_clustering_end_to_end():
         torch.cuda.synchronize()
         assert np.array_equal(to_np(sel), osel) and np.array_equal(to_np(cnt), ocnt), (step, B)
         assert np.abs(to_np(out) - od).max() <= 2e-3, (step, B)
-        for pk in (1, 0):
+        for pk, ws in ((1, None), (0, None), (1, split_ws(idx, H * w.G))):
             idx._s.packed = pk
             fsel = torch.full((H, B), -7, dtype=torch.int32, device="cuda")
-            fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel)
+            fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_ids=fsel, workspace=ws)
             torch.cuda.synchronize()
-            assert np.array_equal(to_np(fsel), osel), (step, B, pk)
-            assert np.abs(to_np(fout) - od).max() <= 2e-3, (step, B, pk)
+            assert np.array_equal(to_np(fsel), osel), (step, B, pk, ws is None)
+            assert np.abs(to_np(fout) - od).max() <= 2e-3, (step, B, pk, ws is None)
         idx._s.packed = 1
 
     while n < w.capacity:
@@ -678,9 +678,10 @@ def test_selection_merge_and_full_ranking():
 
 def test_graph_replay_matches_eager():
     """The benchmark captures a pass's decode steps (append, then fused
-    selection and attention) in a HIP graph after a build and replays it after
-    each new build. Every replay, with eager builds and synchronisations
-    between replays, gives the eager run's outputs bit for bit."""
+    selection and attention, with or without the token split and its merge
+    kernel) in a HIP graph after a build and replays it after each new build.
+    Every replay, with eager builds and synchronisations between replays,
+    gives the eager run's outputs bit for bit."""
     w = SMALL_APPEND
     base, K, V, init, means = make_inputs(w)
     H = K.shape[0]
@@ -701,10 +702,13 @@ def test_graph_replay_matches_eager():
         kvc.build(idx, Kd, w.L, w.iters, initd, workspace=ws)
         kvc.pack(idx, Kd, Vd)
 
+    wsd = split_ws(idx, H * w.G)
+
     def run():
         for s in range(steps):
             kvc.append(idx, Kd, Vd, Knew[s], Vnew[s])
-            kvc.select_decode(idx, Q[s], Kd, Vd, w.B, scale, out=outs[s])
+            # every other step with the token split (its second kernel in the graph too)
+            kvc.select_decode(idx, Q[s], Kd, Vd, w.B, scale, out=outs[s], workspace=wsd if s % 2 == 0 else None)
 
     prepare()
     run()
