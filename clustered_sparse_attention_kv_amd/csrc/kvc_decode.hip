@@ -22,16 +22,17 @@ namespace kvc {
 // ascending), shifting the later clusters' entries right by one; the prefix
 // entries of every slot after the cluster advance, so unused slots keep the
 // list's total.
+constexpr int APP_THREADS = 512;  // one thread per cluster (C <= 512)
 template <typename KT>
-__global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __restrict__ vc, long long head_stride,
+__global__ __launch_bounds__(APP_THREADS) void append_kernel(KT* __restrict__ kc, KT* __restrict__ vc, long long head_stride,
                                                      const KT* __restrict__ knew, const KT* __restrict__ vnew,
                                                      int n_new, int n0, const KT* __restrict__ chat, int C, int cs,
                                                      int cps, int metric, int32_t* __restrict__ labels, long long cap,
                                                      int32_t* __restrict__ sizes, int32_t* __restrict__ app_offsets,
                                                      int32_t* __restrict__ app_ids) {
   __shared__ double kv[D];
-  __shared__ double rs[4];
-  __shared__ int rk[4];
+  __shared__ double rs[APP_THREADS / WAVE];
+  __shared__ int rk[APP_THREADS / WAVE];
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int32_t* aoff = app_offsets + (size_t)h * (cs + 1);
   int32_t* aids = app_ids + (size_t)h * cap;
@@ -46,59 +47,40 @@ __global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __
       kv[tid] = (double)load_f32(ks, tid);
     }
     __syncthreads();
-    // thread tid scores centroids tid and tid + 256 (C <= 512): half rows of
-    // both operand rows are requested at once in 16-byte pieces, then the two
-    // fp64 chains run side by side over ascending j
+    // thread tid scores centroid tid (C <= 512): half rows requested at once
+    // in 16-byte pieces, then the fp64 chain over ascending j
     double best = -INFINITY;
     int bi = 0x7FFFFFFF;
     {
       constexpr int EPP = 16 / (int)sizeof(KT);  // elements per 16-byte piece
       constexpr int HP = D / EPP / 2;            // pieces per half row
-      const int c0 = tid, c1 = tid + 256;
+      const int c0 = tid;
       const u32x4* r0 = reinterpret_cast<const u32x4*>(Ch + (size_t)(c0 < C ? c0 : 0) * D);
-      const u32x4* r1 = reinterpret_cast<const u32x4*>(Ch + (size_t)(c1 < C ? c1 : 0) * D);
-      double s0 = 0.0, s1 = 0.0, nn0 = 0.0, nn1 = 0.0;
+      double s0 = 0.0, nn0 = 0.0;
       const bool l2 = metric == M_L2;
 #pragma unroll 1
       for (int half = 0; half < 2; ++half) {
-        u32x4 x0[HP], x1[HP];
+        u32x4 x0[HP];
 #pragma unroll
-        for (int i = 0; i < HP; ++i) {
-          x0[i] = r0[half * HP + i];
-          x1[i] = r1[half * HP + i];
-        }
+        for (int i = 0; i < HP; ++i) x0[i] = r0[half * HP + i];
 #pragma unroll
         for (int i = 0; i < HP; ++i)
 #pragma unroll
           for (int e = 0; e < EPP; ++e) {
-            float a, b;
-            if constexpr (sizeof(KT) == 2) {
+            float a;
+            if constexpr (sizeof(KT) == 2)
               a = (e & 1) ? __uint_as_float(x0[i][e >> 1] & 0xFFFF0000u) : __uint_as_float(x0[i][e >> 1] << 16);
-              b = (e & 1) ? __uint_as_float(x1[i][e >> 1] & 0xFFFF0000u) : __uint_as_float(x1[i][e >> 1] << 16);
-            } else {
+            else
               a = __uint_as_float(x0[i][e]);
-              b = __uint_as_float(x1[i][e]);
-            }
             const double kj = kv[(half * HP + i) * EPP + e];
             s0 = fma(kj, (double)a, s0);
-            s1 = fma(kj, (double)b, s1);
-            if (l2) {
-              nn0 = fma((double)a, (double)a, nn0);
-              nn1 = fma((double)b, (double)b, nn1);
-            }
+            if (l2) nn0 = fma((double)a, (double)a, nn0);
           }
       }
-      if (l2) {
-        s0 = s0 - 0.5 * nn0;
-        s1 = s1 - 0.5 * nn1;
-      }
+      if (l2) s0 = s0 - 0.5 * nn0;
       if (c0 < C) {
         best = s0;
         bi = c0;
-      }
-      if (c1 < C && s1 > best) {
-        best = s1;
-        bi = c1;
       }
     }
 #pragma unroll
@@ -117,7 +99,7 @@ __global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __
     __syncthreads();
     best = rs[0];
     bi = rk[0];
-    for (int v = 1; v < 4; ++v)
+    for (int v = 1; v < APP_THREADS / WAVE; ++v)
       if (rs[v] > best || (rs[v] == best && rk[v] < bi)) {
         best = rs[v];
         bi = rk[v];
@@ -126,8 +108,8 @@ __global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __
     // insert pos at the end of cluster lab's appended segment
     const int a = aoff[cs];            // entries before this append
     const int p = aoff[lab + 1];
-    for (int hiend = a; hiend > p; hiend -= 256) {  // shift right to left, one chunk at a time
-      const int lo = hiend - 256 > p ? hiend - 256 : p;
+    for (int hiend = a; hiend > p; hiend -= APP_THREADS) {  // shift right to left, one chunk at a time
+      const int lo = hiend - APP_THREADS > p ? hiend - APP_THREADS : p;
       const int e = lo + tid;
       int v = 0;
       if (e < hiend) v = aids[e];
@@ -140,7 +122,7 @@ __global__ __launch_bounds__(256) void append_kernel(KT* __restrict__ kc, KT* __
       sizes[(size_t)h * cs + lab] += 1;
       labels[(size_t)h * cap + pos] = lab;
     }
-    for (int k = lab + 1 + tid; k <= cs; k += 256) aoff[k] += 1;
+    for (int k = lab + 1 + tid; k <= cs; k += APP_THREADS) aoff[k] += 1;
     __syncthreads();
   }
 }
@@ -1566,11 +1548,11 @@ hipError_t launch_append(int dtype, void* kc, void* vc, long long head_stride, i
                          int32_t* labels, long long cap, int32_t* sizes, int32_t* app_offsets, int32_t* app_ids,
                          hipStream_t st) {
   if (dtype == DT_BF16)
-    append_kernel<uint16_t><<<heads, 256, 0, st>>>((uint16_t*)kc, (uint16_t*)vc, head_stride, (const uint16_t*)knew,
+    append_kernel<uint16_t><<<heads, APP_THREADS, 0, st>>>((uint16_t*)kc, (uint16_t*)vc, head_stride, (const uint16_t*)knew,
                                                    (const uint16_t*)vnew, n_new, n0, (const uint16_t*)chat, ca, cs, cps,
                                                    metric, labels, cap, sizes, app_offsets, app_ids);
   else
-    append_kernel<float><<<heads, 256, 0, st>>>((float*)kc, (float*)vc, head_stride, (const float*)knew,
+    append_kernel<float><<<heads, APP_THREADS, 0, st>>>((float*)kc, (float*)vc, head_stride, (const float*)knew,
                                                 (const float*)vnew, n_new, n0, (const float*)chat, ca, cs, cps, metric,
                                                 labels, cap, sizes, app_offsets, app_ids);
   return hipGetLastError();
