@@ -233,7 +233,9 @@ def main():
     log(f"[bench] generated {w.name} inputs ({NL} layer(s)) in {time.time() - t0:.1f}s")
     ws_build = torch.empty(kvc.build_workspace_bytes(H, L, C, w.iters), dtype=torch.uint8, device=dev)
     ws_dec = torch.empty(kvc.decode_workspace_bytes(H, H * G, B), dtype=torch.uint8, device=dev)
-    tsplit = fused and (args.token_split == "on" or (args.token_split == "auto" and H < 128))
+    # the library uses the workspace for bf16 and at most 4 query heads per KV head
+    tsplit = (fused and w.dtype == synth.BF16 and G <= 4
+              and (args.token_split == "on" or (args.token_split == "auto" and H < 128)))
     ws_sd = (torch.empty(kvc.select_decode_workspace_bytes(H, H * G), dtype=torch.uint8, device=dev)
              if tsplit else None)
     ws_win = (torch.empty(kvc.window_workspace_bytes(H, M, NC, w.iters), dtype=torch.uint8, device=dev)
@@ -403,7 +405,7 @@ def main():
                                "share": dd_ms * n_dec * NL / total_ms}
         kernel_names["select_decode"] = ("select_decode_bf16_kernel" if w.dtype == synth.BF16
                                          else "select_decode_kernel")
-        if ws_sd is not None and w.dtype == synth.BF16 and G <= 4:
+        if ws_sd is not None:
             kernel_names["select_decode"] = "select_decode_bf16_kernel (token split) + decode_combine_kernel"
         if offload >= 1:
             kernel_names["select_decode"] = "cache_assemble_kernel + decode_split_kernel + decode_combine_kernel"
