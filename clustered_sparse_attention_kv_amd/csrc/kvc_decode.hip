@@ -885,11 +885,11 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// a7-a11 fused, bf16. After the selection phase the selected ids (up to 2048
-// at a time) are staged in LDS, and each wave then runs on its own over
-// 64-token slices (wave w takes slices w, w + 8, ...), keeping an online
-// softmax per query head (running max, sum and partial output); the waves'
-// states are merged once at the end. Per slice:
+// a7-a11 fused, bf16. After the selection phase each wave runs on its own
+// over 64-token slices (wave w takes the block's slices w, w + 8, ...): it
+// stages a slice's selected entries in its own part of LDS and keeps an
+// online softmax per query head (running max, sum and partial output); the
+// waves' states are merged once at the end. Per slice:
 //  - query-key products on the matrix cores: the 64 keys form the A operand
 //    of four v_mfma_f32_16x16x32_bf16 tiles of 16 rows (lane = row lane % 16,
 //    16-byte piece 32 s + 8 (lane / 16) of the row, so one load instruction
