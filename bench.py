@@ -457,8 +457,12 @@ def main():
         "pack_ms": mean(pack_ms),
         "decode_step_us": step_ms * 1e3,
         "decode_step_hbm_frac": alg["step_bytes"] * NL / (step_ms / 1e3) / PEAK_HBM,
-        "kernel_timing": ("HIP events around every assignment kernel; the fused kernel's launch time is the "
-                          "event-bracketed decode phase over its launches (the phase replays only that kernel)"
+        "kernel_timing": (("HIP events around every assignment kernel; the fused kernel's launch time is the "
+                           "event-bracketed decode phase over its launches (the phase replays only that kernel)")
+                          if phase_only and ws_sd is None else
+                          ("HIP events around every assignment kernel; the time per decode step of the fused "
+                           "kernel and the merge of its token split is the event-bracketed decode phase over its "
+                           "steps (the phase replays only those two kernels)")
                           if phase_only else
                           f"HIP events around every kernel of 1 in {SAMPLE} decode steps (passes launched step "
                           "by step) and around every assignment kernel; value from events bracketing each pass's "
