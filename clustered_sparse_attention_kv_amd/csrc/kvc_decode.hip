@@ -1102,7 +1102,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
       do_slice(sel + w * 64, n64);
     }
   }
-  // merge: the row groups of each wave (lanes 8 apart share channels), then the 8 waves
+  // merge: the row groups of each wave (lanes HC / 8 apart share channels), then the 8 waves
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
