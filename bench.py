@@ -85,7 +85,9 @@ def source_digest() -> str:
 
 
 def algorithmic(w):
-    """Algorithmic work of one pass, per kernel launch."""
+    """Algorithmic work of one pass, per kernel launch: the bytes each launch must move (selection and
+    attention: centroids, index metadata, selected K/V rows, queries and outputs) and the flops the
+    assignment must compute (2 L C d per head)."""
     e = 2 if w.dtype == 1 else 4
     S = min(w.B, w.capacity)
     H, G, C, d = w.heads, w.G, w.C, w.d
@@ -144,8 +146,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build runs the path on a single MI355X "
-              "(the path shards by KV head with no exchange; see DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the path runs on a single MI355X (across GPUs it would shard "
+              "by KV head, with no exchange between them). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
