@@ -60,6 +60,8 @@ def _load():
         lib.orc_select.argtypes = [i, i, i, i, i, p, i, p, p, p, p, ll, p, p, p, p]
         lib.orc_decode.argtypes = [i, i, i, p, i, p, p, i, ll, p, p, i, d, p]
         lib.orc_recall.argtypes = [i, i, i, i, i, p, i, p, i, ll, p, p, p]
+        lib.orc_init.argtypes = [i, i, i, i, C.c_uint64, p]
+        lib.orc_init.restype = i
         _lib = lib
     return _lib
 
@@ -169,9 +171,24 @@ def inertia(K: np.ndarray, chat: np.ndarray, labels: np.ndarray, metric: int = C
     return lib.orc_inertia(L, d, _ptr(K), _dt(K), d, _ptr(chat), _dt(chat), metric, _ptr(labels))
 
 
-def build(K: np.ndarray, C: int, iters: int, init_idx: np.ndarray, L: int | None = None,
-          mode: int = 0, early_exit: bool = True, n_sink: int = 0, metric: int = COSINE) -> dict:
+def init_positions(H: int, L: int, C: int, seed: int, n_sink: int = 0) -> np.ndarray:
+    """Initial centroid positions [H, C] int32: per head, the first C entries of
+    a partial Fisher-Yates shuffle of the clustered rows n_sink .. L-1, driven
+    by SplitMix64 from state seed ^ (0x9E3779B97F4A7C15 * (h + 1))."""
+    lib = _load()
+    out = np.empty((H, C), dtype=np.int32)
+    if lib.orc_init(H, n_sink, L, C, seed & ((1 << 64) - 1), _ptr(out)) != 0:
+        raise ValueError("init_positions needs 1 <= C <= L - n_sink")
+    return out
+
+
+def build(K: np.ndarray, C: int, iters: int, init_idx: np.ndarray | None = None, L: int | None = None,
+          mode: int = 0, early_exit: bool = True, n_sink: int = 0, metric: int = COSINE,
+          seed: int | None = None) -> dict:
     """Prefill clustering of every head of K [H, rows, d] over its first L rows.
+
+    The initial centroids are the keys at init_idx [H, C], or, with init_idx
+    None, at init_positions(H, L, C, seed, n_sink) (the seeded shuffle).
 
     mode 0: centroids fp32, operand in the key type; mode 1: exact (fp64).
     metric: assignment distance, COSINE (the method's), L2 or IP.
@@ -182,6 +199,10 @@ def build(K: np.ndarray, C: int, iters: int, init_idx: np.ndarray, L: int | None
     Returns a dict with c, chat, labels, sizes, offsets, token_ids, inertia,
     iters_run.
     """
+    if init_idx is None:
+        if seed is None:
+            raise ValueError("build needs init_idx or a seed")
+        init_idx = init_positions(K.shape[0], K.shape[1] if L is None else L, C, seed, n_sink)
     if n_sink:
         H, rows, _ = K.shape
         L = rows if L is None else L

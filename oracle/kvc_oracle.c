@@ -249,6 +249,54 @@ double orc_inertia(int L, int d, const void* K, int kdt, long long row_stride, c
 static size_t esize(int dt) { return dt == ORC_BF16 ? 2 : (dt == ORC_F32 ? 4 : 8); }
 
 /*
+ * Initial centroids by a seeded shuffle (the pages leave the initialisation
+ * open; III.B only says that the k-means iterates until the assignment
+ * settles). The reading: the initial centroids are the keys at the first C
+ * positions of a seeded random permutation of the clustered rows.
+ *
+ * Generator: SplitMix64 (Steele, Lea and Flood, "Fast splittable
+ * pseudorandom number generators", OOPSLA 2014; the widely used 64-bit
+ * finaliser constants): the state advances by the golden-ratio increment
+ * 0x9E3779B97F4A7C15 and each output is the state after the advance, mixed by
+ *   z ^= z >> 30; z *= 0xBF58476D1CE4E5B9; z ^= z >> 27; z *= 0x94D049BB133111EB;
+ *   z ^= z >> 31.
+ * Head h starts from state seed ^ (0x9E3779B97F4A7C15 * (h + 1)) (mod 2^64).
+ *
+ * Shuffle: the clustered rows are lo .. L-1 (lo = the attention sinks kept
+ * apart), n = L - lo of them. perm = (0, 1, ..., n-1); for i = 0 .. C-1 in
+ * order, j = i + (next output mod (n - i)) and perm[i], perm[j] swap (a
+ * partial Fisher-Yates shuffle). out[h*C + k] = lo + perm[k].
+ * Requires 1 <= C <= n.
+ */
+static uint64_t splitmix64_next(uint64_t* state) {
+  *state += 0x9E3779B97F4A7C15ULL;
+  uint64_t z = *state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+int orc_init(int H, int lo, int L, int C, uint64_t seed, int32_t* out) {
+  int n = L - lo;
+  if (lo < 0 || C < 1 || C > n) return -1;
+  int32_t* perm = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+  for (int h = 0; h < H; ++h) {
+    uint64_t state = seed ^ (0x9E3779B97F4A7C15ULL * (uint64_t)(h + 1));
+    for (int i = 0; i < n; ++i) perm[i] = i;
+    for (int i = 0; i < C; ++i) {
+      uint64_t r = splitmix64_next(&state);
+      int j = i + (int)(r % (uint64_t)(n - i));
+      int32_t t = perm[i];
+      perm[i] = perm[j];
+      perm[j] = t;
+      out[(size_t)h * C + i] = lo + perm[i];
+    }
+  }
+  free(perm);
+  return 0;
+}
+
+/*
  * Prefill clustering of H independent heads (III.B; Sys-B batches heads).
  * K: keys [H, *, d] with head stride head_stride elements and row stride d;
  * the first L rows of each head are clustered.

@@ -681,3 +681,118 @@ def test_cluster_cache_counts_hand_case(orc):
             sim.step(sel, np.array([len(s)]), labels)
         st = sim.stats[0]
         assert st.tolist() == want[R], (R, st)
+
+
+# -------------------------------------------------------- initialisation
+
+def _golden_init():
+    with open(os.path.join(GOLDEN, "init_shuffle_L10.json")) as f:
+        return json.load(f)
+
+
+def test_init_shuffle_hand_worked(orc):
+    """The seeded partial Fisher-Yates shuffle that picks the initial centroids
+    (the reading of the open initialisation of III.B), against permutations
+    worked step by step, including a draw that lands on a position an earlier
+    swap moved, a draw with no swap, and the attention sinks kept apart."""
+    g = _golden_init()
+    for case in g["cases"] + [g["published_vector"]]:
+        seed, h = int(case["seed"], 16), case["head"]
+        got = orc.init_positions(h + 1, case["L"], case["C"], seed, n_sink=case["n_sink"])[h]
+        assert got.tolist() == case["positions"], case
+
+
+def test_init_shuffle_generator_is_published_splitmix64(orc):
+    """Head 0 of seed 0x9E3779B97F4A7C15 starts from state 0, so its draws are
+    SplitMix64's published seed-0 outputs; with n rows a draw r picks
+    i + r mod (n - i). Checked over several n, so that every bit of the three
+    outputs matters to some modulus."""
+    pub = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    for n in (3, 10, 97, 1000, 65521, 1 << 20):
+        perm = list(range(n))
+        for i, r in enumerate(pub):
+            j = i + r % (n - i)
+            perm[i], perm[j] = perm[j], perm[i]
+        got = orc.init_positions(1, n, 3, 0x9E3779B97F4A7C15)[0]
+        assert got.tolist() == perm[:3], n
+
+
+def test_init_shuffle_full_permutation_uniform(orc):
+    """With C = n the shuffle is a full Fisher-Yates shuffle: every one of the
+    n! orders is equally likely. Over 48,000 heads (independent streams) each
+    of the 24 orders of n = 4 appears about 2,000 times (chi-square, p = 1e-6);
+    the classic mistake j = r mod n (not i + r mod (n - i)) fails this."""
+    from scipy.stats import chi2
+    H = 48000
+    p = orc.init_positions(H, 4, 4, 12345)
+    assert np.all(np.sort(p, axis=1) == np.arange(4))
+    code = p[:, 0] * 64 + p[:, 1] * 16 + p[:, 2] * 4 + p[:, 3]
+    _, counts = np.unique(code, return_counts=True)
+    assert counts.size == 24
+    exp = H / 24
+    stat = float(((counts - exp) ** 2 / exp).sum())
+    assert stat < chi2.ppf(1 - 1e-6, 23), stat
+
+
+def test_init_shuffle_distinct_in_range(orc):
+    """Positions are distinct clustered rows (n_sink .. L-1); with C = 1 the
+    first draw alone decides (uniform over the rows: every row is hit over
+    many heads)."""
+    p = orc.init_positions(16, 1500, 400, 7, n_sink=5)
+    for row in p:
+        assert len(set(row.tolist())) == 400
+        assert row.min() >= 5 and row.max() < 1500
+    one = orc.init_positions(20000, 25, 1, 99, n_sink=5)[:, 0]
+    assert set(one.tolist()) == set(range(5, 25))
+    with pytest.raises(ValueError):
+        orc.init_positions(1, 10, 11, 1)
+
+
+def test_build_from_seed_uses_the_shuffle(orc, syn):
+    """A build given a seed starts from the keys at init_positions(seed)."""
+    K, _, _ = syn.mixture_keys(syn.config_seed(91), 3, 600, 16, 8, 0.3, 0, 1.0, syn.F32, want_means=False)
+    a = orc.build(K, 12, 4, seed=2024)
+    b = orc.build(K, 12, 4, orc.init_positions(3, 600, 12, 2024))
+    for k in ("labels", "c", "token_ids"):
+        assert np.array_equal(a[k], b[k])
+
+
+# ----------------------------------------------------------- objectives
+
+def test_inertia_hand_cases_all_distances(orc):
+    """The k-means objective of each distance (III.B: cosine; L2 and inner
+    product are the alternatives) on a case worked by hand:
+    K = (3, 4), (0, -2); operand rows (1, 0), (0, 1); labels 0, 1.
+      cosine: sum ||K_i|| - K_i . chat = (5 - 3) + (2 - (-2)) = 6
+      L2: ||(2, 4)||^2 + ||(0, -3)||^2 = 20 + 9 = 29
+      inner product: -(3 + (-2)) = -1."""
+    K = np.array([[3.0, 4.0], [0.0, -2.0]], dtype=np.float32)
+    chat = np.array([[1.0, 0.0], [0.0, 1.0]], dtype=np.float64)
+    lab = np.array([0, 1], dtype=np.int32)
+    assert orc.inertia(K, chat, lab, orc.COSINE) == 6.0
+    assert orc.inertia(K, chat, lab, orc.L2) == 29.0
+    assert orc.inertia(K, chat, lab, orc.IP) == -1.0
+    # the inner-product objective is minus the sum of the chosen products
+    lab2 = np.array([1, 0], dtype=np.int32)
+    assert orc.inertia(K, chat, lab2, orc.IP) == -(4.0 + 0.0)
+
+
+def test_normalize_bf16_rounds_once_from_fp64(orc):
+    """The bf16 operand is the fp64 quotient c_j / ||c|| rounded once (RNE), with
+    ||c||^2 the ascending sum of exact squares: bit for bit, on rows chosen so
+    that rounding through fp32 first would differ on some components."""
+    rng = np.random.default_rng(11)
+    c = (rng.standard_normal((4000, 64)) * rng.uniform(0.01, 40, (4000, 1))).astype(np.float32)
+    got = orc.normalize(c, BF16)
+    q = np.empty(c.shape, dtype=np.float64)
+    for k in range(c.shape[0]):
+        s = 0.0
+        for v in c[k].tolist():
+            s += v * v  # exact square of an fp32 value, summed in ascending order
+        n = math.sqrt(s)
+        q[k] = [v / n for v in c[k].tolist()]
+    want = orc.round_bf16(q)
+    assert np.array_equal(got, want)
+    # the case is sensitive: rounding through fp32 changes some components
+    via32 = orc.round_bf16(q.astype(np.float32).astype(np.float64))
+    assert int((via32 != want).sum()) >= 1
