@@ -197,7 +197,6 @@ def main():
         K, _, means = synth.mixture_keys(base, H, cap, d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype,
                                          want_means=(w.query == "mixture"))
         V = synth.values(base, H, cap, d, w.dtype)
-        init = synth.init_idx(base, H, L - args.sinks, C) + args.sinks
         qs = []
         for s in range(w.steps):
             n_cur = L + (s + 1 if w.append else 0)
@@ -208,7 +207,8 @@ def main():
             else:
                 qs.append(synth.queries_noisy_key(base, s, H * G, G, K, n_cur, w.q_sigma))
         Q = np.stack(qs)
-        e = {"Qd": to_dev(Q), "init_d": to_dev(init)}
+        # the build draws its initial centroids from this seed (seeded shuffle on the device)
+        e = {"Qd": to_dev(Q), "seed": base}
         if w.append:  # appended rows come in through the append call
             e["Knew"] = to_dev(np.ascontiguousarray(K[:, L:].transpose(1, 0, 2)))  # [steps, H, d]
             e["Vnew"] = to_dev(np.ascontiguousarray(V[:, L:].transpose(1, 0, 2)))
@@ -229,7 +229,7 @@ def main():
         e["winit"] = [to_dev(synth.init_idx(synth.stream_seed(base, 7, k), H, M, NC) + np.int32(L + k * M))
                       for k in range(n_windows)]
         if li == 0:
-            base0, init0, Q0 = base, init, Q
+            base0, Q0 = base, Q
         lay.append(e)
         del K, V
     log(f"[bench] generated {w.name} inputs ({NL} layer(s)) in {time.time() - t0:.1f}s")
@@ -274,7 +274,7 @@ def main():
         """Builds (and packed copies, cache resets) of every layer: each resets the index's state."""
         ev.record(o + A, sh)
         for li, e in enumerate(lay):
-            kvc.build(e["idx"], e["Kd"], L, w.iters, e["init_d"], workspace=ws_build,
+            kvc.build(e["idx"], e["Kd"], L, w.iters, seed=e["seed"], workspace=ws_build,
                       assign_events=ev.sub(o + 2 * w.iters * li, 2 * w.iters))
         ev.record(o + A + 3, sh)
         if packed:
@@ -517,12 +517,12 @@ def main():
 
     # ---------------- CPU oracle baseline (bounded sample) -----------------
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, args, base0, init0, Q0)
+        result["cpu_baseline"] = cpu_baseline(w, args, base0, Q0)
         # selection quality: oracle recall of the exact top-B attention tokens
         # by the GPU's selections of the first decode steps, layer 0, sampled
         # heads, on a fresh build of the prompt (no generated tokens)
         e0 = lay[0]
-        kvc.build(e0["idx"], e0["Kd"], L, w.iters, e0["init_d"], workspace=ws_build)
+        kvc.build(e0["idx"], e0["Kd"], L, w.iters, seed=e0["seed"], workspace=ws_build)
         sels = []
         for s_ in range(min(args.recall_steps, w.steps)):
             kvc.select(e0["idx"], e0["Qd"][s_], B, sel, cnt)
@@ -532,7 +532,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(w, args, base, init, Q):
+def cpu_baseline(w, args, base, Q):
     """The oracle as it stands on the host cores: select + decode of a sample
     of KV heads over a few decode steps, scaled to the whole workload's heads."""
     import numpy as np
@@ -548,7 +548,7 @@ def cpu_baseline(w, args, base, init, Q):
     V = synth.values(base, nh, w.L, w.d, w.dtype)
     t0 = time.perf_counter()
     metric = {"cosine": oracle.COSINE, "l2": oracle.L2, "inner_product": oracle.IP}[args.metric]
-    built = oracle.build(K, w.C, 1, init[:nh], early_exit=False,  # one k-means iteration of the sample
+    built = oracle.build(K, w.C, 1, seed=base, early_exit=False,  # one k-means iteration of the sample
                          n_sink=args.sinks, metric=metric)
     t_iter = time.perf_counter() - t0
     scale = 1.0 / math.sqrt(w.d)

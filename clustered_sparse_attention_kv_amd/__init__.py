@@ -59,8 +59,15 @@ def lib():
         L.kv_cluster_cpad.restype = i
         L.kv_cluster_build_workspace_bytes.argtypes = [i, i, i, i]
         L.kv_cluster_build_workspace_bytes.restype = sz
-        L.kv_cluster_build.argtypes = [p, p, i, i, p, p, sz, p]
-        L.kv_cluster_build_timed.argtypes = [p, p, i, i, p, p, sz, p, p]
+        u64 = C.c_uint64
+        L.kv_cluster_index_bytes.argtypes = [i, i, i, i, i, i]
+        L.kv_cluster_index_bytes.restype = sz
+        L.kv_cluster_index_init.argtypes = [p, i, i, i, i, i, i, i, i, p, sz, p]
+        L.kv_cluster_init_positions.argtypes = [i, i, i, i, u64, p, p]
+        L.kv_cluster_build.argtypes = [p, p, i, i, u64, p, sz, p]
+        L.kv_cluster_build_from.argtypes = [p, p, i, i, p, p, sz, p]
+        L.kv_cluster_build_timed.argtypes = [p, p, i, i, u64, p, p, sz, p, p]
+        L.kv_cluster_debug_scores.argtypes = [p, p, i, p, p]
         L.kv_cluster_append.argtypes = [p, p, p, p, p, i, p]
         L.kv_cluster_append_window.argtypes = [p, p, p, p, p, i, p]
         L.kv_cluster_window_workspace_bytes.argtypes = [i, i, i, i]
@@ -86,7 +93,8 @@ def lib():
         L.kv_cluster_cached_select_decode.argtypes = [p, p, p, i, p, p, f, p, p, p, p, sz, p]
         L.kv_cluster_status_string.argtypes = [i]
         L.kv_cluster_status_string.restype = C.c_char_p
-        for name in ("kv_cluster_build", "kv_cluster_build_timed", "kv_cluster_append", "kv_cluster_append_window",
+        for name in ("kv_cluster_index_init", "kv_cluster_init_positions", "kv_cluster_build_from",
+                     "kv_cluster_debug_scores", "kv_cluster_build", "kv_cluster_build_timed", "kv_cluster_append", "kv_cluster_append_window",
                      "kv_cluster_cluster_window", "kv_cluster_select", "kv_sparse_decode", "kv_cluster_select_decode",
                      "kv_cluster_export_csr", "kv_cluster_pack", "kv_dense_decode", "kv_cluster_debug_assign",
                      "kv_cluster_debug_update", "kv_cluster_cache_reset", "kv_cluster_cached_select_decode"):
@@ -200,17 +208,34 @@ class ClusterIndex:
         self.heads, self.C, self.capacity, self.d, self.dtype = heads, C_, capacity, d, dtype
         S = c_slots if c_slots else C_
         self.slots = S
-        i32 = dict(dtype=torch.int32, device=device)
-        self.centroids = torch.zeros(heads, S, d, dtype=torch.float32, device=device)
-        self.centroids_op = torch.zeros(heads, cpad(S), d, dtype=dtype, device=device)
-        self.labels = torch.full((heads, capacity), -1, **i32)
-        self.sizes = torch.zeros(heads, S, **i32)
-        self.offsets = torch.zeros(heads, S + 1, **i32)
-        self.token_ids = torch.full((heads, capacity), -1, **i32)
-        self.app_offsets = torch.zeros(heads, S + 1, **i32)
-        self.app_ids = torch.full((heads, capacity), -1, **i32)
-        self.dev_flags = torch.zeros(1, **i32)
-        self.centroids_t = torch.zeros(heads, d // 4, S, 4, dtype=torch.float32, device=device)
+        # one allocation laid out by the library (kv_cluster_index_bytes / kv_cluster_index_init)
+        nbytes = lib().kv_cluster_index_bytes(heads, d, C_, capacity, _dtype_code(dtype), c_slots)
+        if nbytes == 0:
+            raise ValueError(f"invalid index sizes heads={heads} d={d} C={C_} capacity={capacity} c_slots={c_slots}")
+        self._mem = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self._s = _Index()
+        _check(lib().kv_cluster_index_init(C.byref(self._s), heads, d, C_, capacity, _dtype_code(dtype), c_slots,
+                                           n_sink, metric, C.c_void_p(self._mem.data_ptr()), nbytes,
+                                           _stream(None)), "kv_cluster_index_init")
+        base = self._mem.data_ptr()
+
+        def arr(ptr, t, shape):
+            n = 1
+            for x in shape:
+                n *= x
+            off = ptr - base
+            return self._mem[off:off + n * torch.empty((), dtype=t).element_size()].view(t).view(shape)
+
+        self.centroids = arr(self._s.centroids, torch.float32, (heads, S, d))
+        self.centroids_op = arr(self._s.centroids_op, dtype, (heads, cpad(S), d))
+        self.labels = arr(self._s.labels, torch.int32, (heads, capacity))
+        self.sizes = arr(self._s.sizes, torch.int32, (heads, S))
+        self.offsets = arr(self._s.offsets, torch.int32, (heads, S + 1))
+        self.token_ids = arr(self._s.token_ids, torch.int32, (heads, capacity))
+        self.app_offsets = arr(self._s.app_offsets, torch.int32, (heads, S + 1))
+        self.app_ids = arr(self._s.app_ids, torch.int32, (heads, capacity))
+        self.dev_flags = arr(self._s.dev_flags, torch.int32, (1,))
+        self.centroids_t = arr(self._s.centroids_t, torch.float32, (heads, d // 4, S, 4))
         if packed and packed_on_host:
             self.k_packed = torch.empty(heads, capacity, d, dtype=dtype, pin_memory=True)
             self.v_packed = torch.empty(heads, capacity, d, dtype=dtype, pin_memory=True)
@@ -219,13 +244,9 @@ class ClusterIndex:
             self.v_packed = torch.empty(heads, capacity, d, dtype=dtype, device=device)
         else:
             self.k_packed = self.v_packed = None
-        self._s = _Index(heads, d, C_, capacity, _dtype_code(dtype), 0, 0, 0,
-                         self.centroids.data_ptr(), self.centroids_op.data_ptr(), self.labels.data_ptr(),
-                         self.sizes.data_ptr(), self.offsets.data_ptr(), self.token_ids.data_ptr(),
-                         self.app_offsets.data_ptr(), self.app_ids.data_ptr(), self.dev_flags.data_ptr(),
-                         self.centroids_t.data_ptr(),
-                         _ptr_kv(self.k_packed).value if packed else None,
-                         _ptr_kv(self.v_packed).value if packed else None, n_sink, c_slots, 0, 0, metric)
+        if packed:
+            self._s.k_packed = _ptr_kv(self.k_packed).value
+            self._s.v_packed = _ptr_kv(self.v_packed).value
         self.metric = metric
         self.n_sink = n_sink
 
@@ -255,28 +276,55 @@ def _cache_check(idx: ClusterIndex, t: torch.Tensor, name: str):
                          f"{t.dtype} {list(t.shape)}")
 
 
-def build(idx: ClusterIndex, keys: torch.Tensor, L: int, iters: int, init_idx: torch.Tensor,
-          workspace: torch.Tensor | None = None, stream=None, assign_events=None):
-    """kv_cluster_build: cluster the first L rows of keys [heads, capacity, d].
+def init_positions(heads: int, L: int, C_: int, seed: int, n_sink: int = 0, device="cuda", stream=None):
+    """kv_cluster_init_positions: the seeded initial centroid positions, int32 [heads, C]."""
+    out = torch.empty(heads, C_, dtype=torch.int32, device=device)
+    _check(lib().kv_cluster_init_positions(heads, n_sink, L, C_, seed & ((1 << 64) - 1), _ptr(out),
+                                           _stream(stream)), "kv_cluster_init_positions")
+    return out
+
+
+def build(idx: ClusterIndex, keys: torch.Tensor, L: int, iters: int, seed: int | None = None,
+          init_idx: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None,
+          assign_events=None):
+    """kv_cluster_build: cluster the first L rows of keys [heads, capacity, d],
+    from the seeded initial positions (seed) or from init_idx int32 [heads, C]
+    (kv_cluster_build_from).
 
     assign_events: optional ctypes array of 2*iters hipEvent_t handles
     (kv_cluster_build_timed) recorded around each assignment kernel."""
     _cache_check(idx, keys, "keys")
-    if init_idx.dtype != torch.int32 or tuple(init_idx.shape) != (idx.heads, idx.C):
+    if (seed is None) == (init_idx is None):
+        raise ValueError("build takes exactly one of seed and init_idx")
+    if init_idx is not None and (init_idx.dtype != torch.int32 or tuple(init_idx.shape) != (idx.heads, idx.C)):
         raise ValueError("init_idx must be int32 [heads, C]")
     need = build_workspace_bytes(idx.heads, L, idx.C, iters)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=keys.device)
-    if assign_events is None:
-        _check(lib().kv_cluster_build(idx.ref(), _ptr(keys), L, iters, _ptr(init_idx), _ptr(workspace),
-                                      workspace.numel(), _stream(stream)), "kv_cluster_build")
-    else:
+    seed = 0 if seed is None else seed & ((1 << 64) - 1)
+    if assign_events is not None:
         if len(assign_events) < 2 * iters:
             raise ValueError("assign_events needs 2 * iters handles")
-        _check(lib().kv_cluster_build_timed(idx.ref(), _ptr(keys), L, iters, _ptr(init_idx), _ptr(workspace),
-                                            workspace.numel(), assign_events, _stream(stream)),
+        _check(lib().kv_cluster_build_timed(idx.ref(), _ptr(keys), L, iters, seed, _ptr(init_idx),
+                                            _ptr(workspace), workspace.numel(), assign_events, _stream(stream)),
                "kv_cluster_build_timed")
+    elif init_idx is None:
+        _check(lib().kv_cluster_build(idx.ref(), _ptr(keys), L, iters, seed, _ptr(workspace), workspace.numel(),
+                                      _stream(stream)), "kv_cluster_build")
+    else:
+        _check(lib().kv_cluster_build_from(idx.ref(), _ptr(keys), L, iters, _ptr(init_idx), _ptr(workspace),
+                                           workspace.numel(), _stream(stream)), "kv_cluster_build_from")
     return workspace
+
+
+def debug_scores(idx: ClusterIndex, q: torch.Tensor, stream=None) -> torch.Tensor:
+    """kv_cluster_debug_scores: the fp64 selection scores [heads, c_active] of q [q_heads, d]."""
+    if q.dtype != idx.dtype or q.dim() != 2 or q.shape[1] != idx.d:
+        raise ValueError(f"q must be {idx.dtype} [q_heads, {idx.d}]")
+    out = torch.empty(idx.heads, max(idx.c_active, 1), dtype=torch.float64, device=q.device)
+    _check(lib().kv_cluster_debug_scores(idx.ref(), _ptr(q), q.shape[0], _ptr(out), _stream(stream)),
+           "kv_cluster_debug_scores")
+    return out
 
 
 def append(idx: ClusterIndex, k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,

@@ -25,7 +25,7 @@ bool index_ok(const kvc_index* idx) {
          idx->metric <= KVC_INNER_PRODUCT;
 }
 
-int index_support(const kvc_index* idx) {
+kvc_status index_support(const kvc_index* idx) {
   if (idx->d != KVC_HEAD_DIM || idx->C > KVC_MAX_C || slots(idx) > KVC_MAX_C) return KVC_ERR_UNSUPPORTED;
   if ((long long)idx->heads * idx->capacity >= (1ll << 31)) return KVC_ERR_UNSUPPORTED;
   return KVC_OK;
@@ -56,6 +56,7 @@ IndexView view(const kvc_index* idx) {
 }
 
 struct BuildWs {
+  int32_t* init;     // [heads, C]: initial centroid positions drawn from the seed
   uint32_t* qcount;  // [iters, heads]
   int32_t* queue;    // [heads, L]
   int32_t* hist;     // [heads, nblk, C]
@@ -69,6 +70,8 @@ BuildWs carve_build(void* base, int heads, int L, int C, int iters) {
   BuildWs w{};
   size_t o = 0;
   char* b = static_cast<char*>(base);
+  w.init = reinterpret_cast<int32_t*>(b + o);
+  o = align_up(o + sizeof(int32_t) * (size_t)heads * C);
   w.qcount = reinterpret_cast<uint32_t*>(b + o);
   o = align_up(o + sizeof(uint32_t) * (size_t)iters * heads);
   w.queue = reinterpret_cast<int32_t*>(b + o);
@@ -119,7 +122,7 @@ WindowWs carve_window(void* base, int heads, int m, int nc, int iters) {
 
 size_t elem_bytes(int dtype) { return dtype == KVC_BF16 ? 2 : 4; }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
+kvc_status status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
 
 }  // namespace
 
@@ -127,20 +130,113 @@ extern "C" {
 
 int kv_cluster_cpad(int C) { return C < 1 ? 0 : (C + 31) / 32 * 32; }
 
+namespace {
+// The arrays of one index in one allocation (256-byte aligned each).
+struct IndexLayout {
+  size_t centroids, centroids_op, labels, sizes, offsets, token_ids, app_offsets, app_ids, dev_flags, centroids_t,
+      bytes;
+};
+IndexLayout index_layout(int heads, int d, int C, int capacity, int dtype, int c_slots) {
+  IndexLayout l{};
+  const size_t H = (size_t)heads, S = (size_t)(c_slots ? c_slots : C), cap = (size_t)capacity;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  l.centroids = take(sizeof(float) * H * S * d);
+  l.centroids_op = take(elem_bytes(dtype) * H * (size_t)kv_cluster_cpad((int)S) * d);
+  l.labels = take(sizeof(int32_t) * H * cap);
+  l.sizes = take(sizeof(int32_t) * H * S);
+  l.offsets = take(sizeof(int32_t) * H * (S + 1));
+  l.token_ids = take(sizeof(int32_t) * H * cap);
+  l.app_offsets = take(sizeof(int32_t) * H * (S + 1));
+  l.app_ids = take(sizeof(int32_t) * H * cap);
+  l.dev_flags = take(sizeof(int32_t));
+  l.centroids_t = take(sizeof(float) * H * S * d);
+  l.bytes = o;
+  return l;
+}
+bool index_sizes_ok(int heads, int d, int C, int capacity, int dtype, int c_slots) {
+  return heads >= 1 && d == KVC_HEAD_DIM && C >= 1 && C <= KVC_MAX_C && capacity >= 1 &&
+         (dtype == KVC_F32 || dtype == KVC_BF16) && (c_slots == 0 || (c_slots >= C && c_slots <= KVC_MAX_C)) &&
+         (long long)heads * capacity < (1ll << 31);
+}
+}  // namespace
+
+size_t kv_cluster_index_bytes(int heads, int d, int C, int capacity, kvc_dtype dtype, int c_slots) {
+  if (!index_sizes_ok(heads, d, C, capacity, dtype, c_slots)) return 0;
+  return index_layout(heads, d, C, capacity, dtype, c_slots).bytes;
+}
+
+kvc_status kv_cluster_index_init(kvc_index* idx, int heads, int d, int C, int capacity, kvc_dtype dtype, int c_slots,
+                                 int n_sink, kvc_metric metric, void* mem, size_t mem_bytes, void* stream) {
+  if (!idx || !mem || n_sink < 0 || metric < KVC_COSINE || metric > KVC_INNER_PRODUCT) return KVC_ERR_INVALID_ARG;
+  if (heads >= 1 && C >= 1 && capacity >= 1 && (d != KVC_HEAD_DIM || C > KVC_MAX_C || c_slots > KVC_MAX_C))
+    return KVC_ERR_UNSUPPORTED;
+  if (!index_sizes_ok(heads, d, C, capacity, dtype, c_slots)) return KVC_ERR_INVALID_ARG;
+  const IndexLayout l = index_layout(heads, d, C, capacity, dtype, c_slots);
+  if (mem_bytes < l.bytes) return KVC_ERR_WORKSPACE;
+  char* b = static_cast<char*>(mem);
+  kvc_index x{};
+  x.heads = heads;
+  x.d = d;
+  x.C = C;
+  x.capacity = capacity;
+  x.dtype = dtype;
+  x.centroids = reinterpret_cast<float*>(b + l.centroids);
+  x.centroids_op = b + l.centroids_op;
+  x.labels = reinterpret_cast<int32_t*>(b + l.labels);
+  x.sizes = reinterpret_cast<int32_t*>(b + l.sizes);
+  x.offsets = reinterpret_cast<int32_t*>(b + l.offsets);
+  x.token_ids = reinterpret_cast<int32_t*>(b + l.token_ids);
+  x.app_offsets = reinterpret_cast<int32_t*>(b + l.app_offsets);
+  x.app_ids = reinterpret_cast<int32_t*>(b + l.app_ids);
+  x.dev_flags = reinterpret_cast<int32_t*>(b + l.dev_flags);
+  x.centroids_t = reinterpret_cast<float*>(b + l.centroids_t);
+  x.n_sink = n_sink;
+  x.c_slots = c_slots;
+  x.metric = metric;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t cap = (size_t)heads * capacity;
+  hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(b), l.bytes / sizeof(int32_t), 0, st);
+  if (e == hipSuccess) e = launch_fill_i32(x.labels, cap, -1, st);
+  if (e == hipSuccess) e = launch_fill_i32(x.token_ids, cap, -1, st);
+  if (e == hipSuccess) e = launch_fill_i32(x.app_ids, cap, -1, st);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  *idx = x;
+  return KVC_OK;
+}
+
 size_t kv_cluster_build_workspace_bytes(int heads, int L, int C, int iters) {
   if (heads < 1 || L < 1 || C < 1 || iters < 1) return 0;
   return carve_build(nullptr, heads, L, C, iters).bytes;
 }
 
-int kv_cluster_build(kvc_index* idx, const void* keys, int L, int iters, const int32_t* init_idx, void* ws,
-                     size_t ws_bytes, void* stream) {
-  return kv_cluster_build_timed(idx, keys, L, iters, init_idx, ws, ws_bytes, nullptr, stream);
+kvc_status kv_cluster_build(kvc_index* idx, const void* keys, int L, int iters, uint64_t seed, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return kv_cluster_build_timed(idx, keys, L, iters, seed, nullptr, ws, ws_bytes, nullptr, stream);
 }
 
-int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, const int32_t* init_idx, void* ws,
-                           size_t ws_bytes, void* const* assign_events, void* stream) {
-  if (!index_ok(idx) || !keys || !init_idx || !ws) return KVC_ERR_INVALID_ARG;
-  if (int s = index_support(idx)) return s;
+kvc_status kv_cluster_build_from(kvc_index* idx, const void* keys, int L, int iters, const int32_t* init_idx,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  if (!init_idx) return KVC_ERR_INVALID_ARG;
+  return kv_cluster_build_timed(idx, keys, L, iters, 0, init_idx, ws, ws_bytes, nullptr, stream);
+}
+
+kvc_status kv_cluster_init_positions(int heads, int n_sink, int L, int C, uint64_t seed, int32_t* out,
+                                     void* stream) {
+  if (!out || heads < 1 || n_sink < 0 || C < 1 || L < 1 || (long long)L - n_sink < C) return KVC_ERR_INVALID_ARG;
+  if (C > KVC_MAX_C) return KVC_ERR_UNSUPPORTED;
+  return status(launch_init_positions(heads, n_sink, L, C, seed, out, static_cast<hipStream_t>(stream)));
+}
+
+kvc_status kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, uint64_t seed,
+                                  const int32_t* init_idx, void* ws, size_t ws_bytes, void* const* assign_events,
+                                  void* stream) {
+  if (!index_ok(idx) || !keys || !ws) return KVC_ERR_INVALID_ARG;
+  if (kvc_status s = index_support(idx)) return s;
   const int H = idx->heads, C = idx->C, cap = idx->capacity, cpad = kv_cluster_cpad(C);
   const int cs = slots(idx), cps = kv_cluster_cpad(cs);
   const int ns = idx->n_sink;
@@ -158,6 +254,11 @@ int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, c
   if (e == hipSuccess) e = launch_fill_i32(w.dirty, (size_t)iters * H * C, 0, st);
   if (e == hipSuccess) e = launch_fill_i32(idx->app_offsets, (size_t)H * (cs + 1), 0, st);
   if (e == hipSuccess) e = launch_fill2d_i32(idx->labels, H, cap, ns, -1, st);  // sinks: in no cluster
+  // without explicit positions, the seeded shuffle draws them into the workspace
+  if (e == hipSuccess && !init_idx) {
+    e = launch_init_positions(H, ns, L, C, seed, w.init, st);
+    init_idx = w.init;
+  }
   if (e == hipSuccess)
     e = launch_init_centroids(idx->dtype, keys, hs, H, ns, L, init_idx, C, cpad, cs, cps, idx->metric, idx->centroids,
                               idx->centroids_t, idx->centroids_op, idx->dev_flags, st);
@@ -185,10 +286,10 @@ int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, c
   return KVC_OK;
 }
 
-int kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const void* chat, int32_t* labels,
+kvc_status kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const void* chat, int32_t* labels,
                             float* top2, int32_t* flagged, void* ws, size_t ws_bytes, void* stream) {
   if (!index_ok(idx) || !keys || !chat || !labels || !ws) return KVC_ERR_INVALID_ARG;
-  if (int s = index_support(idx)) return s;
+  if (kvc_status s = index_support(idx)) return s;
   const int H = idx->heads, C = idx->C, cap = idx->capacity, cpad = kv_cluster_cpad(C);
   if (L < 1 || L > cap) return KVC_ERR_INVALID_ARG;
   const BuildWs w = carve_build(ws, H, L, C, 1);
@@ -200,12 +301,21 @@ int kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const
                       cap, w.queue, w.qcount, w.op_t, nullptr, nullptr, 0, top2, nullptr, st);
   if (e == hipSuccess && flagged)
     e = hipMemcpyAsync(flagged, w.qcount, sizeof(int32_t) * H, hipMemcpyDeviceToDevice, st);
-  return hip_status(e);
+  return status(e);
 }
 
-int kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, size_t ws_bytes, void* stream) {
+kvc_status kv_cluster_debug_scores(const kvc_index* idx, const void* q, int q_heads, double* scores, void* stream) {
+  if (!index_ok(idx) || !q || !scores || q_heads < 1) return KVC_ERR_INVALID_ARG;
+  if (kvc_status s = index_support(idx)) return s;
+  if (!built_ok(idx) || q_heads % idx->heads != 0) return KVC_ERR_INVALID_ARG;
+  const int G = q_heads / idx->heads;
+  if (G > KVC_MAX_G) return KVC_ERR_UNSUPPORTED;
+  return status(launch_debug_scores(idx->dtype, q, G, view(idx), idx->heads, scores, static_cast<hipStream_t>(stream)));
+}
+
+kvc_status kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, size_t ws_bytes, void* stream) {
   if (!index_ok(idx) || !keys || !ws || idx->n_sink != 0) return KVC_ERR_INVALID_ARG;
-  if (int s = index_support(idx)) return s;
+  if (kvc_status s = index_support(idx)) return s;
   const int H = idx->heads, C = idx->C, cap = idx->capacity;
   const int cs = slots(idx), cps = kv_cluster_cpad(cs);
   if (L < 1 || L > cap) return KVC_ERR_INVALID_ARG;
@@ -219,13 +329,13 @@ int kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, s
     e = launch_update(idx->dtype, keys, (long long)cap * KVC_HEAD_DIM, H, C, cs, cps, idx->metric, idx->sizes,
                       idx->offsets, idx->token_ids, cap, idx->centroids, idx->centroids_t, idx->centroids_op, nullptr,
                       st);
-  return hip_status(e);
+  return status(e);
 }
 
-int kv_cluster_append(kvc_index* idx, void* k_cache, void* v_cache, const void* k_new, const void* v_new, int n_new,
+kvc_status kv_cluster_append(kvc_index* idx, void* k_cache, void* v_cache, const void* k_new, const void* v_new, int n_new,
                       void* stream) {
   if (!index_ok(idx) || !k_cache || !v_cache || !k_new || !v_new || n_new < 1) return KVC_ERR_INVALID_ARG;
-  if (int s = index_support(idx)) return s;
+  if (kvc_status s = index_support(idx)) return s;
   if (!built_ok(idx)) return KVC_ERR_INVALID_ARG;
   if ((long long)idx->n_tokens + n_new > idx->capacity) return KVC_ERR_CAPACITY;
   if (idx->window_start != idx->n_tokens) return KVC_ERR_INVALID_ARG;  // an open window: cluster it first
@@ -240,10 +350,10 @@ int kv_cluster_append(kvc_index* idx, void* k_cache, void* v_cache, const void* 
   return KVC_OK;
 }
 
-int kv_cluster_append_window(kvc_index* idx, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+kvc_status kv_cluster_append_window(kvc_index* idx, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                              int n_new, void* stream) {
   if (!index_ok(idx) || !k_cache || !v_cache || !k_new || !v_new || n_new < 1) return KVC_ERR_INVALID_ARG;
-  if (int s = index_support(idx)) return s;
+  if (kvc_status s = index_support(idx)) return s;
   if (!built_ok(idx)) return KVC_ERR_INVALID_ARG;
   if ((long long)idx->n_tokens + n_new > idx->capacity) return KVC_ERR_CAPACITY;
   hipError_t e = launch_window_append(idx->dtype, k_cache, v_cache, idx->capacity, idx->heads, k_new, v_new, n_new,
@@ -258,10 +368,10 @@ size_t kv_cluster_window_workspace_bytes(int heads, int m, int n_clusters, int i
   return carve_window(nullptr, heads, m, n_clusters, iters).bytes;
 }
 
-int kv_cluster_cluster_window(kvc_index* idx, const void* k_cache, const void* v_cache, int n_clusters, int iters,
+kvc_status kv_cluster_cluster_window(kvc_index* idx, const void* k_cache, const void* v_cache, int n_clusters, int iters,
                               const int32_t* init_idx, void* ws, size_t ws_bytes, void* stream) {
   if (!index_ok(idx) || !k_cache || !v_cache || !init_idx || !ws) return KVC_ERR_INVALID_ARG;
-  if (int s = index_support(idx)) return s;
+  if (kvc_status s = index_support(idx)) return s;
   if (!built_ok(idx)) return KVC_ERR_INVALID_ARG;
   const int H = idx->heads, cap = idx->capacity, cs = slots(idx), cps = kv_cluster_cpad(cs);
   const int wlo = idx->window_start, m = idx->n_tokens - wlo, nc = n_clusters, ca = idx->c_active;
@@ -307,16 +417,16 @@ int kv_cluster_cluster_window(kvc_index* idx, const void* k_cache, const void* v
   return KVC_OK;
 }
 
-int kv_cluster_select(const kvc_index* idx, const void* q, int q_heads, int B, int32_t* sel_ids, int32_t* sel_count,
+kvc_status kv_cluster_select(const kvc_index* idx, const void* q, int q_heads, int B, int32_t* sel_ids, int32_t* sel_count,
                       void* stream) {
   if (!index_ok(idx) || !q || !sel_ids || !sel_count || B < 1 || q_heads < 1) return KVC_ERR_INVALID_ARG;
-  if (int s = index_support(idx)) return s;
+  if (kvc_status s = index_support(idx)) return s;
   if (!built_ok(idx) || q_heads % idx->heads != 0) return KVC_ERR_INVALID_ARG;
   const int G = q_heads / idx->heads;
   if (G > KVC_MAX_G) return KVC_ERR_UNSUPPORTED;
   if ((long long)idx->heads * B >= (1ll << 31)) return KVC_ERR_INVALID_ARG;
   const IndexView x = view(idx);
-  return hip_status(launch_select(idx->dtype, q, G, x, idx->heads, B, sel_ids, sel_count,
+  return status(launch_select(idx->dtype, q, G, x, idx->heads, B, sel_ids, sel_count,
                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -327,7 +437,7 @@ size_t kv_sparse_decode_workspace_bytes(int heads, int q_heads, int d, int B) {
   return align_up(sizeof(float) * heads * nsplit * G * (d + 2));
 }
 
-int kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
+kvc_status kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
                      int capacity, int d, const int32_t* sel_ids, const int32_t* sel_count, int B, float scale,
                      float* out, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !sel_ids || !sel_count || !out || !ws) return KVC_ERR_INVALID_ARG;
@@ -339,7 +449,7 @@ int kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void
   if ((long long)heads * B >= (1ll << 31)) return KVC_ERR_INVALID_ARG;
   if ((long long)((B + DEC_TOK - 1) / DEC_TOK) * G > DEC_MAX_PAIRS) return KVC_ERR_UNSUPPORTED;
   if (ws_bytes < kv_sparse_decode_workspace_bytes(heads, q_heads, d, B)) return KVC_ERR_WORKSPACE;
-  return hip_status(launch_decode(dtype, q, G, k_cache, v_cache, (long long)capacity * d, heads, sel_ids, sel_count, B,
+  return status(launch_decode(dtype, q, G, k_cache, v_cache, (long long)capacity * d, heads, sel_ids, sel_count, B,
                                   scale, out, static_cast<float*>(ws), static_cast<hipStream_t>(stream)));
 }
 
@@ -349,11 +459,11 @@ size_t kv_cluster_select_decode_workspace_bytes(int heads, int q_heads, int d) {
   return align_up(sizeof(float) * heads * fused_blocks_per_head(heads) * G * (d + 2));
 }
 
-int kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, const void* k_cache,
+kvc_status kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, const void* k_cache,
                              const void* v_cache, int B, float scale, float* out, int32_t* sel_ids,
                              int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
   if (!index_ok(idx) || !q || !k_cache || !v_cache || !out || B < 1 || q_heads < 1) return KVC_ERR_INVALID_ARG;
-  if (int s = index_support(idx)) return s;
+  if (kvc_status s = index_support(idx)) return s;
   if (!built_ok(idx) || q_heads % idx->heads != 0) return KVC_ERR_INVALID_ARG;
   const int G = q_heads / idx->heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVC_ERR_UNSUPPORTED;
@@ -363,36 +473,36 @@ int kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, c
   const bool packed = idx->packed == 1 && idx->k_packed && idx->v_packed;
   // the token split exists for bf16 and at most 4 query heads per KV head
   float* part = ws && idx->dtype == KVC_BF16 && G <= 4 ? static_cast<float*>(ws) : nullptr;
-  return hip_status(launch_select_decode(idx->dtype, q, G, x, idx->heads, k_cache, v_cache,
+  return status(launch_select_decode(idx->dtype, q, G, x, idx->heads, k_cache, v_cache,
                                          packed ? idx->k_packed : nullptr, packed ? idx->v_packed : nullptr, B, scale,
                                          out, sel_ids, sel_count, part, static_cast<hipStream_t>(stream)));
 }
 
-int kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, void* stream) {
+kvc_status kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, void* stream) {
   if (!index_ok(idx) || !k_cache || !v_cache || !idx->k_packed || !idx->v_packed) return KVC_ERR_INVALID_ARG;
-  if (int s = index_support(idx)) return s;
+  if (kvc_status s = index_support(idx)) return s;
   if (!built_ok(idx)) return KVC_ERR_INVALID_ARG;
   // rows 0 .. offsets[h][c_active]-1: the main part, at most n_tokens - n_sink rows
   const int cs = slots(idx);
-  const int e = hip_status(launch_pack(idx->dtype, k_cache, v_cache, idx->capacity, idx->heads, idx->token_ids,
+  const kvc_status e = status(launch_pack(idx->dtype, k_cache, v_cache, idx->capacity, idx->heads, idx->token_ids,
                                        idx->n_tokens - idx->n_sink, nullptr, idx->offsets + idx->c_active, cs + 1,
                                        idx->k_packed, idx->v_packed, static_cast<hipStream_t>(stream)));
   if (e == KVC_OK) idx->packed = 1;
   return e;
 }
 
-int kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token_ids, void* stream) {
+kvc_status kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token_ids, void* stream) {
   if (!index_ok(idx) || !offsets || !token_ids) return KVC_ERR_INVALID_ARG;
-  if (int s = index_support(idx)) return s;
+  if (kvc_status s = index_support(idx)) return s;
   if (!built_ok(idx)) return KVC_ERR_INVALID_ARG;
-  return hip_status(launch_export_csr(idx->heads, idx->c_active, slots(idx), idx->offsets, idx->token_ids,
+  return status(launch_export_csr(idx->heads, idx->c_active, slots(idx), idx->offsets, idx->token_ids,
                                       idx->app_offsets, idx->app_ids, idx->capacity, offsets, token_ids,
                                       static_cast<hipStream_t>(stream)));
 }
 
-int kv_cluster_cache_reset(const kvc_index* idx, kvc_cluster_cache* cache, void* stream) {
+kvc_status kv_cluster_cache_reset(const kvc_index* idx, kvc_cluster_cache* cache, void* stream) {
   if (!index_ok(idx) || !cache || !cache->table || !cache->stats) return KVC_ERR_INVALID_ARG;
-  if (int s = index_support(idx)) return s;
+  if (kvc_status s = index_support(idx)) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int H = idx->heads, cs = slots(idx);
   // table entries (step, row, members) = (never, 0, 0); counters 0
@@ -410,13 +520,13 @@ size_t kv_cluster_cache_workspace_bytes(int heads, int q_heads, int d, int B) {
          kv_sparse_decode_workspace_bytes(heads, q_heads, d, B);
 }
 
-int kv_cluster_cached_select_decode(const kvc_index* idx, kvc_cluster_cache* cache, const void* q, int q_heads,
+kvc_status kv_cluster_cached_select_decode(const kvc_index* idx, kvc_cluster_cache* cache, const void* q, int q_heads,
                                     const void* k_cache, const void* v_cache, float scale, float* out,
                                     int32_t* sel_ids, int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
   if (!index_ok(idx) || !cache || !q || !k_cache || !v_cache || !out || !ws || q_heads < 1) return KVC_ERR_INVALID_ARG;
   if (!cache->k || !cache->v || !cache->table || !cache->stats || cache->R < 1 || cache->B < 1 || cache->step < 0)
     return KVC_ERR_INVALID_ARG;
-  if (int s = index_support(idx)) return s;
+  if (kvc_status s = index_support(idx)) return s;
   if (!built_ok(idx) || q_heads % idx->heads != 0) return KVC_ERR_INVALID_ARG;
   const int H = idx->heads, G = q_heads / H, B = cache->B, R = cache->R;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVC_ERR_UNSUPPORTED;
@@ -451,7 +561,7 @@ size_t kv_dense_decode_workspace_bytes(int heads, int q_heads, int d, int n) {
   return align_up(sizeof(float) * (size_t)heads * nsplit * G * (KVC_HEAD_DIM + 2));
 }
 
-int kv_dense_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
+kvc_status kv_dense_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
                     int capacity, int d, int n, float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !out || !ws || heads < 1 || q_heads < 1) return KVC_ERR_INVALID_ARG;
   if (dtype != KVC_BF16 && dtype != KVC_F32) return KVC_ERR_INVALID_ARG;
@@ -462,12 +572,12 @@ int kv_dense_decode(const void* q, int q_heads, const void* k_cache, const void*
   if (n < 1 || n > capacity) return KVC_ERR_INVALID_ARG;
   if ((long long)heads * capacity >= (1ll << 31)) return KVC_ERR_UNSUPPORTED;
   if (ws_bytes < kv_dense_decode_workspace_bytes(heads, q_heads, d, n)) return KVC_ERR_WORKSPACE;
-  return hip_status(launch_dense_decode(q, G, k_cache, v_cache, capacity, heads, n, scale, out,
+  return status(launch_dense_decode(q, G, k_cache, v_cache, capacity, heads, n, scale, out,
                                         static_cast<float*>(ws), static_cast<hipStream_t>(stream)));
 }
 
-const char* kv_cluster_status_string(int status) {
-  switch (status) {
+const char* kv_cluster_status_string(kvc_status s) {
+  switch (s) {
     case KVC_OK: return "ok";
     case KVC_ERR_INVALID_ARG: return "invalid argument";
     case KVC_ERR_UNSUPPORTED: return "unsupported by the GPU path (d must be 128, C <= 512, G in {1,2,4,8})";

@@ -63,6 +63,74 @@ __device__ __forceinline__ double2 operand_row(int metric, const float c0, const
 }
 
 // ---------------------------------------------------------------------------
+// a1: initial centroid positions by a seeded partial Fisher-Yates shuffle of
+// the n = L - lo clustered rows (the pages leave the initialisation open;
+// III.B only says that the k-means iterates until the assignment settles).
+// Swap i (i = 0 .. C-1) exchanges entries i and j_i = i + (r_i mod (n - i)) of
+// the permutation, with r_i the i-th SplitMix64 output from state
+// seed ^ (0x9E3779B97F4A7C15 * (h + 1)); position k is lo + perm[k].
+//
+// SplitMix64's i-th output depends only on i (the state after i + 1 steps is
+// the start plus (i + 1) increments), so all j_i are drawn at once, one thread
+// per swap. The sequential result then follows from which earlier swap last
+// wrote a position: before swap i, entry p (p >= i) holds p unless an earlier
+// swap i' targeted it (j_i' = p), in which case it holds a_i', the value entry
+// i' had when swap i' ran. With P_i the last i' < i with j_i' = i and Q_i the
+// last i' < i with j_i' = j_i:
+//   a_i = P_i < 0 ? i : a_{P_i},      perm[i] = Q_i < 0 ? j_i : a_{Q_i}.
+// a_i refers only to smaller indices, so repeated substitution settles it (at
+// least the smallest unsettled index settles per round). One block per head.
+constexpr int INIT_THREADS = 512;  // one thread per swap (C <= 512)
+__global__ __launch_bounds__(INIT_THREADS) void init_positions_kernel(unsigned long long seed, int lo, int L, int C,
+                                                                      int32_t* __restrict__ out) {
+  __shared__ int J[INIT_THREADS];
+  __shared__ int A[INIT_THREADS];
+  __shared__ int unsettled;
+  const int h = blockIdx.x, i = threadIdx.x;
+  const unsigned long long gamma = 0x9E3779B97F4A7C15ull;
+  const long long n = (long long)L - lo;
+  if (i < C) {
+    unsigned long long z = (seed ^ (gamma * (unsigned long long)(h + 1))) + gamma * (unsigned long long)(i + 1);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    J[i] = i + (int)(z % (unsigned long long)(n - i));
+  }
+  __syncthreads();
+  int P = -1, Q = -1;
+  if (i < C) {
+    const int ji = J[i];
+    for (int t = 0; t < i; ++t) {
+      const int jt = J[t];
+      P = jt == i ? t : P;
+      Q = jt == ji ? t : Q;
+    }
+    A[i] = P < 0 ? i : -1;
+  }
+  for (;;) {
+    if (i == 0) unsettled = 0;
+    __syncthreads();
+    if (i < C && A[i] < 0) {
+      const int v = A[P];
+      if (v >= 0) A[i] = v;
+      else unsettled = 1;
+    }
+    __syncthreads();
+    const int more = unsettled;
+    __syncthreads();
+    if (!more) break;
+  }
+  if (i < C) out[(size_t)h * C + i] = lo + (Q < 0 ? J[i] : A[Q]);
+}
+
+hipError_t launch_init_positions(int heads, int lo, int L, int C, unsigned long long seed, int32_t* out,
+                                 hipStream_t st) {
+  if (C < 1 || C > INIT_THREADS || lo < 0 || (long long)L - lo < C) return hipErrorInvalidValue;
+  init_positions_kernel<<<heads, INIT_THREADS, 0, st>>>(seed, lo, L, C, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // a1 + a2: initial centroids c_k = K[init_idx[k]] (exact copy to fp32) and
 // their normalised operand. One wave per centroid row, 4 rows per block.
 // Rows k in [C, cpad) of the operand are zeroed. Per-cluster arrays have a
@@ -188,11 +256,27 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
   // block 0 of each head also stores the chunk-major copy [16][cpad] that the
   // exact pass reads (rows of one chunk contiguous)
   u32x4* Ot = blockIdx.x == 0 ? op_t + (size_t)h * 16 * cpad : nullptr;
+  // a non-finite component in operand row 0 (possible under L2 and inner
+  // product) makes cluster 0's score NaN for some keys, and the sequential
+  // argmax rule then keeps them in cluster 0 where the fold below would skip
+  // the NaN: every key of such a head goes to the exact pass
+  // (one 16-byte slot after the zero tile: the kernel keeps all of its LDS in
+  // the dynamic allocation, whose size limit leaves no room for static LDS)
+  int& row0_bad = *reinterpret_cast<int*>(sC + (cpad + 16) * 16);
+  if (tid == 0) row0_bad = 0;
+  __syncthreads();
   for (int e = tid; e < cpad * 16; e += AS_THREADS) {
     const int r = e >> 4, c = e & 15;
     const u32x4 v = Cg[e];
     sC[r * 16 + (c ^ (r & 15))] = v;
     if (Ot) Ot[(size_t)c * cpad + r] = v;
+    if (r == 0) {
+      bool bad = false;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        bad |= (v[q] & 0x7F80u) == 0x7F80u || (v[q] & 0x7F800000u) == 0x7F800000u;
+      if (bad) row0_bad = 1;
+    }
   }
   // one zero tile past the operand: the tile loop reads one tile ahead without
   // a bound
@@ -200,7 +284,7 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
   // variants: after the operand, the per-centroid bias (L2; cpad floats) and
   // the largest operand norm (one word), all in the dynamic allocation so the
   // kernel has no static LDS
-  float* sBias = reinterpret_cast<float*>(sC + (cpad + 16) * 16);
+  float* sBias = reinterpret_cast<float*>(sC + (cpad + 16) * 16 + 1);
   unsigned& sMaxNorm = *reinterpret_cast<unsigned*>(sBias + cpad);
   float normA = 1.0f, biasM = 0.0f;
   if constexpr (METRIC != M_COSINE) {
@@ -393,7 +477,7 @@ __global__ __launch_bounds__(AS_THREADS) void assign_bf16_mfma_kernel(
         if (norm_mode == 1) my_n2 = nn;
         const float thr = (METRIC == M_COSINE ? gamma * sqrtf(nn) : gA * sqrtf(nn) + gB) +
                           gbits * fmaxf(fabsf(m1[T]), fabsf(m2[T]));
-        my_flag = !((m1[T] - m2[T]) > thr);  // true for NaN and ties
+        my_flag = !((m1[T] - m2[T]) > thr) || row0_bad;  // true for NaN and ties
         my_m1 = m1[T];
         my_m2 = m2[T];
       }
@@ -557,6 +641,11 @@ __global__ __launch_bounds__(64) void assign_exact_kernel(const KT* __restrict__
           bi = oi;
         }
       }
+      // non-finite scores follow the sequential rule (start from cluster 0,
+      // move only to a strictly larger score): when cluster 0 scores NaN, or
+      // no score exceeds -inf, the key stays in cluster 0
+      const double s0 = __shfl(s[kk][0], 0);  // cluster 0's score (lane 0 owns it)
+      if (bi >= C || s0 != s0) bi = 0;
       if (lane == 0 && e + kk < n) {
         int32_t* lp = labels + (size_t)h * label_stride + row[kk];
         if (dirty) {
@@ -1118,7 +1207,7 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
                          hipEvent_t* events, hipStream_t st) {
   u32x4* ot = static_cast<u32x4*>(op_t);
   if (dtype == DT_BF16) {
-    const size_t lds = (size_t)(cpad + 16) * D * 2;  // the operand and one zero tile
+    const size_t lds = (size_t)(cpad + 16) * D * 2 + 16;  // the operand, one zero tile and a flag
     // about one block per compute unit; each walks over 512-key groups of one head
     const int ngroups = grid1(L, AS_TILE);
     int gx = (256 + heads - 1) / heads;

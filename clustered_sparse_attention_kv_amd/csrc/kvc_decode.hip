@@ -108,6 +108,10 @@ __global__ __launch_bounds__(APP_THREADS) void append_kernel(KT* __restrict__ kc
     // insert pos at the end of cluster lab's appended segment
     const int a = aoff[cs];            // entries before this append
     const int p = aoff[lab + 1];
+    // every thread holds both bounds before any thread moves them (the prefix
+    // increments below), so all threads run the shift loop the same number of
+    // times and meet its barriers together
+    __syncthreads();
     for (int hiend = a; hiend > p; hiend -= APP_THREADS) {  // shift right to left, one chunk at a time
       const int lo = hiend - APP_THREADS > p ? hiend - APP_THREADS : p;
       const int e = lo + tid;
@@ -249,9 +253,37 @@ __device__ __forceinline__ void bitonic_sort(Sh& S, unsigned long long& key, int
   if constexpr (SIZE < N) bitonic_sort<SIZE * 2, N>(S, key, id, tid);
 }
 
-// cent_t is the chunk-major copy [d/4, cs, 4] of the head's centroids: thread k
-// reads chunk jj of its row at ((jj * cs) + k) * 16 bytes, so a wave's loads are
-// contiguous. The chain still runs over ascending j.
+// qbar_j of KV head h: the fp64 sum over its G query heads in ascending order
+// (III.C ranks clusters by their centroid's attention weight to the query; the
+// query heads sharing a KV head share one selection).
+template <typename QT>
+__device__ __forceinline__ double query_sum(const QT* __restrict__ q, int G, int h, int j) {
+  double s = 0.0;
+  for (int g = 0; g < G; ++g) s = s + (double)load_f32(q, ((size_t)h * G + g) * D + j);
+  return s;
+}
+
+// Score of cluster k: the fp64 chain over ascending j of qbar_j * c_kj. The
+// centroids come from the chunk-major copy [d/4, cs, 4] of the head: chunk jj
+// of row k sits at ((jj * cs) + k) * 16 bytes, so the 64 lanes of a wave
+// scoring consecutive clusters read 1 KiB contiguously.
+__device__ __forceinline__ double centroid_score(const double* qbar, const float* __restrict__ cent_t_head, int cs,
+                                                 int k) {
+  const f32x4* ct = reinterpret_cast<const f32x4*>(cent_t_head) + k;
+  double sc = 0.0;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    f32x4 v[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) v[jj] = ct[(size_t)(half * 16 + jj) * cs];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc = fma(qbar[half * 64 + 4 * jj + i], (double)v[jj][i], sc);
+  }
+  return sc;
+}
+
 // Returns the cluster id of rank tid (ids >= X.ca are padding).
 template <typename QT>
 __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__ q, int G, const IndexView& X, int h,
@@ -265,11 +297,7 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
     S.mb[tid] = X.offsets[(size_t)h * (cs + 1) + tid + 1] - o;
     S.ma[tid] = X.app_offsets[(size_t)h * (cs + 1) + tid];
   }
-  if (tid < D) {
-    double s = 0.0;
-    for (int g = 0; g < G; ++g) s = s + (double)load_f32(q, ((size_t)h * G + g) * D + tid);
-    S.qbar[tid] = s;
-  }
+  if (tid < D) S.qbar[tid] = query_sum(q, G, h, tid);
   if (tid < 256) S.hist[tid] = 0;
   if (tid == 0) S.ncand = 0;
   __syncthreads();
@@ -277,17 +305,7 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
   int id = C + tid;  // padding entries: worst key, distinct ids past the clusters
   double sc = 0.0;
   if (tid < C) {
-    const f32x4* ct = reinterpret_cast<const f32x4*>(X.cent_t + (size_t)h * cs * D) + tid;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      f32x4 v[16];
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) v[jj] = ct[(size_t)(half * 16 + jj) * cs];
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc = fma(S.qbar[half * 64 + 4 * jj + i], (double)v[jj][i], sc);
-    }
+    sc = centroid_score(S.qbar, X.cent_t + (size_t)h * cs * D, cs, tid);
     key = ordered_key(sc);
     id = tid;
   }
@@ -507,6 +525,28 @@ __device__ __forceinline__ int sel_token(const int32_t* __restrict__ ids_h, int 
 __device__ __forceinline__ int select_count(const SelShared& S, const IndexView& X, int B) {
   const int n = X.n_sink + X.nw + S.total;
   return n < B ? n : B;
+}
+
+// The selection's scores of every cluster in use (for tests): one block per
+// KV head, the same query sum and chains as select_phase.
+template <typename QT>
+__global__ __launch_bounds__(SEL_THREADS) void debug_scores_kernel(const QT* __restrict__ q, int G, const IndexView X,
+                                                                   double* __restrict__ scores) {
+  __shared__ double qbar[D];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  if (tid < D) qbar[tid] = query_sum(q, G, h, tid);
+  __syncthreads();
+  for (int k = tid; k < X.ca; k += SEL_THREADS)
+    scores[(size_t)h * X.ca + k] = centroid_score(qbar, X.cent_t + (size_t)h * X.cs * D, X.cs, k);
+}
+
+hipError_t launch_debug_scores(int dtype, const void* q, int G, const IndexView& x, int heads, double* scores,
+                               hipStream_t st) {
+  if (dtype == DT_BF16)
+    debug_scores_kernel<uint16_t><<<heads, SEL_THREADS, 0, st>>>((const uint16_t*)q, G, x, scores);
+  else
+    debug_scores_kernel<float><<<heads, SEL_THREADS, 0, st>>>((const float*)q, G, x, scores);
+  return hipGetLastError();
 }
 
 template <typename QT>
@@ -1176,7 +1216,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const KT* __restrict_
   const int h = blockIdx.y, sp = blockIdx.x, nsplit = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = lane >> 4, gl = lane & 15;
-  const int cnt = sel_count[h];
+  // the caller's count, clamped to the row of B entries; entries outside
+  // [0, capacity) are skipped
+  const int cnt = min(max(sel_count[h], 0), B);
+  const long long cap = head_stride / D;
   const int t0 = sp * DEC_TOK;
   const int ntok = cnt - t0 < 0 ? 0 : (cnt - t0 > DEC_TOK ? DEC_TOK : cnt - t0);
 
@@ -1190,10 +1233,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const KT* __restrict_
   const KT* Kh = kc + (size_t)h * head_stride + 8 * gl;
   const KT* Vh = vc + (size_t)h * head_stride + 8 * gl;
   Row8<KT> kr[4], vr[4];
+  bool ok[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = w * 16 + r * 4 + grp;
-    const int id = t < ntok ? sel_ids[(size_t)h * B + t0 + t] : 0;
+    int id = t < ntok ? sel_ids[(size_t)h * B + t0 + t] : 0;
+    ok[r] = t < ntok && id >= 0 && id < cap;
+    id = ok[r] ? id : 0;
     kr[r].load(Kh + (size_t)id * D);
     vr[r].load(Vh + (size_t)id * D);
   }
@@ -1206,7 +1252,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const KT* __restrict_
 #pragma unroll
       for (int c = 0; c < 8; ++c) s = fmaf(qv[g][c], kr[r].at(c), s);
       s = row16_sum(s);
-      if (gl == 0) ps[g][t] = t < ntok ? s : -INFINITY;
+      if (gl == 0) ps[g][t] = ok[r] ? s : -INFINITY;
     }
   }
   __syncthreads();

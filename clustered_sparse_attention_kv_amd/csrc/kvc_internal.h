@@ -26,6 +26,9 @@ struct IndexView {
 };
 
 hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t v, hipStream_t st);
+// Initial centroid positions [heads, C] of the seeded partial shuffle of rows lo .. L-1.
+hipError_t launch_init_positions(int heads, int lo, int L, int C, unsigned long long seed, int32_t* out,
+                                 hipStream_t st);
 hipError_t launch_init_centroids(int dtype, const void* keys, long long head_stride, int heads, int lo, int L,
                                  const int32_t* init_idx, int C, int cpad, int cs, int cps, int metric, float* cent,
                                  float* cent_t, void* chat, int32_t* flags, hipStream_t st);
@@ -61,6 +64,8 @@ hipError_t launch_append(int dtype, void* kc, void* vc, long long head_stride, i
                          hipStream_t st);
 hipError_t launch_window_append(int dtype, void* kc, void* vc, long long cap, int heads, const void* knew,
                                 const void* vnew, int n_new, int n0, int32_t* labels, hipStream_t st);
+hipError_t launch_debug_scores(int dtype, const void* q, int G, const IndexView& x, int heads, double* scores,
+                               hipStream_t st);
 hipError_t launch_select(int dtype, const void* q, int G, const IndexView& x, int heads, int B, int32_t* sel_ids,
                          int32_t* sel_count, hipStream_t st);
 hipError_t launch_decode(int dtype, const void* q, int G, const void* kc, const void* vc, long long head_stride,

@@ -135,8 +135,44 @@ typedef struct kvc_index {
 /* Rows of centroids_op per head: C rounded up to the matrix-core tile (32). */
 int kv_cluster_cpad(int C);
 
+/*
+ * Device memory of one index (every array of kvc_index except the optional
+ * packed copies), for `heads` heads of dimension d, C clusters, `capacity`
+ * tokens per head, element type dtype and c_slots cluster slots (0 for C).
+ * The caller allocates it (one allocation); 0 for invalid sizes.
+ */
+size_t kv_cluster_index_bytes(int heads, int d, int C, int capacity, kvc_dtype dtype, int c_slots);
+
+/*
+ * Lays an index out in caller memory: sets the size fields of *idx (heads,
+ * d, C, capacity, dtype, c_slots, n_sink, metric; host mirrors 0; k_packed
+ * and v_packed NULL, for the caller to set) and points every array into mem
+ * (device memory of at least kv_cluster_index_bytes(...) bytes, each array
+ * 256-byte aligned). Enqueues on stream the fills that give a fresh index:
+ * labels, token_ids and app_ids -1, every other array 0. Requires d = 128,
+ * 1 <= C <= c_slots (or c_slots 0) <= 512, capacity >= 1, n_sink >= 0.
+ */
+kvc_status kv_cluster_index_init(kvc_index* idx, int heads, int d, int C, int capacity, kvc_dtype dtype, int c_slots,
+                                 int n_sink, kvc_metric metric, void* mem, size_t mem_bytes, void* stream);
+
 /* Bytes of workspace kv_cluster_build needs for these sizes. */
 size_t kv_cluster_build_workspace_bytes(int heads, int L, int C, int iters);
+
+/*
+ * Initial centroid positions (the pages leave the initialisation open; III.B
+ * only says that the k-means iterates until the assignment settles; the
+ * reading here is a seeded random choice of C distinct keys). For every head
+ * h, the clustered rows are n_sink .. L-1 (n = L - n_sink of them) and the
+ * positions are n_sink + perm[0 .. C-1] of a partial Fisher-Yates shuffle:
+ * perm = (0, 1, ..., n-1); for i = 0 .. C-1, j = i + (r_i mod (n - i)) and
+ * perm[i], perm[j] swap, with r_i the i-th output of SplitMix64 (Steele, Lea
+ * and Flood 2014: the state advances by 0x9E3779B97F4A7C15, then z ^= z >> 30,
+ * z *= 0xBF58476D1CE4E5B9, z ^= z >> 27, z *= 0x94D049BB133111EB, z ^= z >> 31)
+ * started from state seed ^ (0x9E3779B97F4A7C15 * (h + 1)), arithmetic mod
+ * 2^64. out is [heads, C] int32 (device). Requires 1 <= C <= min(512, n)
+ * (KVC_ERR_UNSUPPORTED above 512); enqueues one kernel on stream.
+ */
+kvc_status kv_cluster_init_positions(int heads, int n_sink, int L, int C, uint64_t seed, int32_t* out, void* stream);
 
 /*
  * Prefill clustering (III.B; Sys-B). For every head, the first L rows of
@@ -145,14 +181,14 @@ size_t kv_cluster_build_workspace_bytes(int heads, int L, int C, int iters);
  *   - only rows idx->n_sink .. L-1 are clustered: the attention sinks before
  *     them keep label -1 and are not in the index (kv_cluster_select puts them
  *     first). Requires 0 <= n_sink and C <= L - n_sink;
- *   - initial centroids are the keys at init_idx[h*C + k] ([heads, C] int32
- *     token positions, distinct, in [n_sink, L); the seeded shuffle that picks
- *     them is the caller's input). An index out of range sets bit 0 of
- *     *idx->dev_flags and row 0 is used instead;
+ *   - the initial centroids are the keys at the positions
+ *     kv_cluster_init_positions(heads, n_sink, L, C, seed) gives, drawn on the
+ *     device into the workspace;
  *   - each iteration normalises the centroids (rounded once to idx->dtype),
  *     assigns every key to the centroid of largest cosine similarity (lowest
- *     id on an exact tie) and replaces each centroid by the mean of its keys
- *     (an empty cluster keeps its centroid). Under idx->metric KVC_L2 or
+ *     id on an exact tie; a key whose scores are all NaN or -inf goes to
+ *     cluster 0) and replaces each centroid by the mean of its keys (an empty
+ *     cluster keeps its centroid). Under idx->metric KVC_L2 or
  *     KVC_INNER_PRODUCT the operand is the centroid itself (rounded once) and
  *     a key joins the centroid of least L2 distance (largest K . c - ||c||^2
  *     / 2, both fp64 chains over ascending channels, then their fp64
@@ -160,22 +196,34 @@ size_t kv_cluster_build_workspace_bytes(int heads, int L, int C, int iters);
  * On return (after synchronisation) the index holds the means of the final
  * assignment, their normalised operand, labels, sizes, offsets and
  * token_ids; the appended part is empty. idx->n_build, idx->n_tokens and
- * idx->window_start are set to L and idx->c_active to C on the host. Requires 1 <= C <= L <= capacity, iters >= 1, and a
- * workspace of kv_cluster_build_workspace_bytes(heads, L, C, iters) bytes
- * (contents need not be initialised).
+ * idx->window_start are set to L and idx->c_active to C on the host.
+ * Requires 1 <= C <= L <= capacity, iters >= 1, C <= 512, and a workspace of
+ * kv_cluster_build_workspace_bytes(heads, L, C, iters) bytes (contents need
+ * not be initialised).
  */
-int kv_cluster_build(kvc_index* idx, const void* keys, int L, int iters, const int32_t* init_idx, void* ws,
-                     size_t ws_bytes, void* stream);
+kvc_status kv_cluster_build(kvc_index* idx, const void* keys, int L, int iters, uint64_t seed, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /*
- * kv_cluster_build with timing: assign_events (host array of 2*iters
+ * kv_cluster_build from caller-chosen initial positions instead of the
+ * seeded shuffle: init_idx ([heads, C] int32, device) holds distinct token
+ * positions in [n_sink, L). An index out of range sets bit 0 of
+ * *idx->dev_flags and row 0 is used instead. Otherwise identical.
+ */
+kvc_status kv_cluster_build_from(kvc_index* idx, const void* keys, int L, int iters, const int32_t* init_idx,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kv_cluster_build with timing: initial positions from init_idx, or from the
+ * seed when init_idx is NULL. assign_events (host array of 2*iters
  * hipEvent_t handles created by the caller, or NULL) receives, for iteration
  * t, events recorded on `stream` right before and right after the launch of
  * that iteration's assignment kernel (the matrix-core pass for bf16 keys, the
  * fp64 pass for fp32 keys). Otherwise identical to kv_cluster_build.
  */
-int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, const int32_t* init_idx, void* ws,
-                           size_t ws_bytes, void* const* assign_events, void* stream);
+kvc_status kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, uint64_t seed,
+                                  const int32_t* init_idx, void* ws, size_t ws_bytes, void* const* assign_events,
+                                  void* stream);
 
 /*
  * Decode-time append of n_new tokens per head (rows idx->n_tokens ..
@@ -191,7 +239,7 @@ int kv_cluster_build_timed(kvc_index* idx, const void* keys, int L, int iters, c
  * kv_cluster_append_window; joining the nearest centroid is the per-token
  * alternative this call provides.)
  */
-int kv_cluster_append(kvc_index* idx, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+kvc_status kv_cluster_append(kvc_index* idx, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                       int n_new, void* stream);
 
 /*
@@ -204,7 +252,7 @@ int kv_cluster_append(kvc_index* idx, void* k_cache, void* v_cache, const void* 
  * clusters them. Requires a built index; KVC_ERR_CAPACITY if the tokens would
  * not fit.
  */
-int kv_cluster_append_window(kvc_index* idx, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+kvc_status kv_cluster_append_window(kvc_index* idx, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                              int n_new, void* stream);
 
 /* Bytes of workspace kv_cluster_cluster_window needs for a window of m tokens. */
@@ -228,7 +276,7 @@ size_t kv_cluster_window_workspace_bytes(int heads, int m, int n_clusters, int i
  * kv_cluster_window_workspace_bytes(heads, m, n_clusters, iters) bytes
  * (contents need not be initialised).
  */
-int kv_cluster_cluster_window(kvc_index* idx, const void* k_cache, const void* v_cache, int n_clusters, int iters,
+kvc_status kv_cluster_cluster_window(kvc_index* idx, const void* k_cache, const void* v_cache, int n_clusters, int iters,
                               const int32_t* init_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -247,7 +295,7 @@ int kv_cluster_cluster_window(kvc_index* idx, const void* k_cache, const void* v
  * receives min(B, n_sink + window + tokens in the clusters). Requires B >= 1
  * and G <= 8.
  */
-int kv_cluster_select(const kvc_index* idx, const void* q, int q_heads, int B, int32_t* sel_ids,
+kvc_status kv_cluster_select(const kvc_index* idx, const void* q, int q_heads, int B, int32_t* sel_ids,
                       int32_t* sel_count, void* stream);
 
 /* Bytes of workspace kv_sparse_decode needs. */
@@ -260,13 +308,14 @@ size_t kv_sparse_decode_workspace_bytes(int heads, int q_heads, int d, int B);
  *   out[g] = sum_i softmax_i(scale * q_g . K[h, i]) V[h, i]
  * over i in sel_ids[h*B .. h*B + sel_count[h]) (fp32 accumulation, fp32
  * output [q_heads, d]; zero when sel_count[h] is 0). k_cache and v_cache are
- * [heads, capacity, d] in `dtype`, q is [q_heads, d] in `dtype`. The selected
- * positions must lie in [0, capacity). The selected set is split into blocks
+ * [heads, capacity, d] in `dtype`, q is [q_heads, d] in `dtype`. A count
+ * outside [0, B] is taken as its nearest bound, and entries outside [0,
+ * capacity) are skipped (they get no weight). The selected set is split into blocks
  * of 64 tokens whose partial results (running max, sum, output) go to the
  * workspace (kv_sparse_decode_workspace_bytes(heads, q_heads, d, B) bytes,
  * contents need not be initialised) and are merged by a second kernel.
  */
-int kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
+kvc_status kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
                      int capacity, int d, const int32_t* sel_ids, const int32_t* sel_count, int B, float scale,
                      float* out, void* ws, size_t ws_bytes, void* stream);
 
@@ -283,7 +332,7 @@ int kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void
  * part of the caches. Requires a built index and both packed arrays;
  * otherwise KVC_ERR_INVALID_ARG.
  */
-int kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, void* stream);
+kvc_status kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, void* stream);
 
 /*
  * kv_cluster_select followed by kv_sparse_decode in one kernel (several
@@ -304,7 +353,7 @@ int kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, vo
  * is NULL; a smaller ws gives KVC_ERR_WORKSPACE.
  */
 size_t kv_cluster_select_decode_workspace_bytes(int heads, int q_heads, int d);
-int kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, const void* k_cache,
+kvc_status kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, const void* k_cache,
                              const void* v_cache, int B, float scale, float* out, int32_t* sel_ids,
                              int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
 
@@ -332,7 +381,7 @@ typedef struct kvc_cluster_cache {
 
 /* Empties the cache (no cluster cached, counters 0, step 0). Also needed
  * after every kv_cluster_build of the index: cluster ids change meaning. */
-int kv_cluster_cache_reset(const kvc_index* idx, kvc_cluster_cache* cache, void* stream);
+kvc_status kv_cluster_cache_reset(const kvc_index* idx, kvc_cluster_cache* cache, void* stream);
 
 /* Bytes of workspace kv_cluster_cached_select_decode needs. */
 size_t kv_cluster_cache_workspace_bytes(int heads, int q_heads, int d, int B);
@@ -357,7 +406,7 @@ size_t kv_cluster_cache_workspace_bytes(int heads, int q_heads, int d, int B);
  * and a workspace of kv_cluster_cache_workspace_bytes(heads, q_heads, d, B)
  * bytes (contents need not be initialised).
  */
-int kv_cluster_cached_select_decode(const kvc_index* idx, kvc_cluster_cache* cache, const void* q, int q_heads,
+kvc_status kv_cluster_cached_select_decode(const kvc_index* idx, kvc_cluster_cache* cache, const void* q, int q_heads,
                                     const void* k_cache, const void* v_cache, float scale, float* out,
                                     int32_t* sel_ids, int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
 
@@ -378,7 +427,7 @@ size_t kv_dense_decode_workspace_bytes(int heads, int q_heads, int d, int n);
  * not be initialised) and are merged by a second kernel. Requires
  * 1 <= n <= capacity and G in {1, 2, 4, 8}.
  */
-int kv_dense_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
+kvc_status kv_dense_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
                     int capacity, int d, int n, float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -388,7 +437,7 @@ int kv_dense_decode(const void* q, int q_heads, const void* k_cache, const void*
  * ascending order, as a stable counting sort of all labels of clustered
  * tokens would give (Sys-C). For tests and checkpoints.
  */
-int kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token_ids, void* stream);
+kvc_status kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token_ids, void* stream);
 
 /*
  * Single steps of the build, for checking each kernel on its own (an index
@@ -404,12 +453,22 @@ int kv_cluster_export_csr(const kvc_index* idx, int32_t* offsets, int32_t* token
  *    update plus normalisation, writing idx->centroids (in: previous
  *    centroids, kept for empty clusters) and idx->centroids_op.
  */
-int kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const void* chat, int32_t* labels,
+kvc_status kv_cluster_debug_assign(const kvc_index* idx, const void* keys, int L, const void* chat, int32_t* labels,
                             float* top2, int32_t* flagged, void* ws, size_t ws_bytes, void* stream);
-int kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, size_t ws_bytes, void* stream);
+kvc_status kv_cluster_debug_update(kvc_index* idx, const void* keys, int L, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The selection scores of kv_cluster_select (III.C; Sys-C: clusters rank by
+ * the attention weight of their centroid to the query): scores [heads,
+ * c_active] (device, fp64) receives, for KV head h and cluster k, the fp64
+ * chain over ascending channels j of qbar_j * centroids[h][k][j], where
+ * qbar_j is the fp64 sum over g = 0 .. G-1 (ascending) of q[h*G + g][j] and G
+ * = q_heads / heads; the very values the selection orders. For tests.
+ */
+kvc_status kv_cluster_debug_scores(const kvc_index* idx, const void* q, int q_heads, double* scores, void* stream);
 
 /* Static text for a status code. */
-const char* kv_cluster_status_string(int status);
+const char* kv_cluster_status_string(kvc_status s);
 
 #ifdef __cplusplus
 }

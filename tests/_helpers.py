@@ -5,6 +5,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+import oracle
 import synth
 
 
@@ -28,14 +29,16 @@ def torch_dtype(w) -> torch.dtype:
 
 def make_inputs(w, layer: int = 0, heads: int | None = None):
     """Keys/values [H, capacity, d] (prompt rows plus, for append workloads,
-    the decode-time tokens at rows L..), init indices and the key-space means."""
+    the decode-time tokens at rows L..), the initial positions the seeded
+    shuffle draws (the oracle's, from seed = base; the GPU build draws its own
+    from the same seed) and the key-space means."""
     H = w.heads if heads is None else heads
     base = synth.config_seed(w.config, layer)
     cap = w.capacity
     K, _, means = synth.mixture_keys(base, H, cap, w.d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype,
                                      want_means=(w.query == "mixture"))
     V = synth.values(base, H, cap, w.d, w.dtype)
-    init = synth.init_idx(base, H, w.L, w.C)
+    init = oracle.init_positions(H, w.L, w.C, base)
     return base, K, V, init, means
 
 

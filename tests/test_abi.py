@@ -26,12 +26,15 @@ def kvc():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(kv_\w+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:int|size_t|kvc_status|const char\*)\s+(kv_\w+)\(", text, re.M)))
 
 
 def test_every_declared_function_is_exported(kvc):
     names = declared_functions()
-    assert len(names) >= 10
+    assert len(names) >= 25
+    for n in ("kv_cluster_build", "kv_cluster_append", "kv_cluster_select", "kv_sparse_decode",
+              "kv_cluster_index_bytes", "kv_cluster_debug_scores", "kv_cluster_init_positions"):
+        assert n in names, n
     for n in names:
         assert hasattr(kvc.lib(), n), n
 
@@ -66,12 +69,12 @@ def test_build_rejects(kvc):
     L = kvc.lib()
     p = C.c_void_p(FAKE)
 
-    def build(idx, Lk=200, iters=10, ws_bytes=1 << 40, keys=p, init=p):
-        return L.kv_cluster_build(C.byref(idx) if idx is not None else None, keys, Lk, iters, init, p, ws_bytes, None)
+    def build(idx, Lk=200, iters=10, ws_bytes=1 << 40, keys=p, seed=5):
+        return L.kv_cluster_build(C.byref(idx) if idx is not None else None, keys, Lk, iters, seed, p, ws_bytes, None)
 
     assert build(None) == INVALID
     assert build(make_index(kvc), keys=None) == INVALID
-    assert build(make_index(kvc), init=None) == INVALID
+    assert L.kv_cluster_build_from(C.byref(make_index(kvc)), p, 200, 10, None, p, 1 << 40, None) == INVALID
     for field in ("centroids", "centroids_op", "labels", "sizes", "offsets", "token_ids", "app_offsets", "app_ids",
                   "dev_flags", "centroids_t"):
         assert build(make_index(kvc, null=field)) == INVALID, field
@@ -88,6 +91,63 @@ def test_build_rejects(kvc):
     assert build(sinks, Lk=200) == INVALID                          # fewer clustered rows than C
     need = L.kv_cluster_build_workspace_bytes(4, 200, 16, 10)
     assert build(make_index(kvc), ws_bytes=need - 1) == WORKSPACE
+    # the timed variant takes positions or (NULL positions) the seed, with the same checks
+    assert L.kv_cluster_build_timed(C.byref(make_index(kvc)), p, 200, 10, 5, None, p, need - 1, None,
+                                    None) == WORKSPACE
+
+
+def test_init_positions_rejects(kvc):
+    L = kvc.lib()
+    p = C.c_void_p(FAKE)
+    assert L.kv_cluster_init_positions(4, 0, 100, 10, 1, None, None) == INVALID
+    assert L.kv_cluster_init_positions(0, 0, 100, 10, 1, p, None) == INVALID
+    assert L.kv_cluster_init_positions(4, 0, 100, 0, 1, p, None) == INVALID
+    assert L.kv_cluster_init_positions(4, 95, 100, 6, 1, p, None) == INVALID   # 5 rows for 6 positions
+    assert L.kv_cluster_init_positions(4, -1, 100, 6, 1, p, None) == INVALID
+    assert L.kv_cluster_init_positions(4, 0, 1000, 513, 1, p, None) == UNSUPPORTED
+
+
+def test_index_layout(kvc):
+    """kv_cluster_index_bytes covers every array of the index (each 256-byte
+    aligned), and kv_cluster_index_init rejects bad sizes and small memory
+    before it enqueues anything."""
+    L = kvc.lib()
+    H, d, Cn, cap = 3, 128, 40, 1000
+
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    for dt, e in ((1, 2), (0, 4)):
+        for S in (0, 64):
+            s_ = S or Cn
+            cpad = (s_ + 31) // 32 * 32
+            want = (al(4 * H * s_ * d) + al(e * H * cpad * d) + al(4 * H * cap) + al(4 * H * s_) + al(4 * H * (s_ + 1))
+                    + al(4 * H * cap) + al(4 * H * (s_ + 1)) + al(4 * H * cap) + al(4) + al(4 * H * s_ * d))
+            assert L.kv_cluster_index_bytes(H, d, Cn, cap, dt, S) == want, (dt, S)
+    assert L.kv_cluster_index_bytes(H, 64, Cn, cap, 1, 0) == 0
+    assert L.kv_cluster_index_bytes(H, d, 600, cap, 1, 0) == 0
+    assert L.kv_cluster_index_bytes(H, d, Cn, cap, 1, 20) == 0       # fewer slots than clusters
+    assert L.kv_cluster_index_bytes(0, d, Cn, cap, 1, 0) == 0
+    idx = kvc._Index()
+    p = C.c_void_p(FAKE)
+    need = L.kv_cluster_index_bytes(H, d, Cn, cap, 1, 0)
+    assert L.kv_cluster_index_init(C.byref(idx), H, d, Cn, cap, 1, 0, 0, 0, p, need - 1, None) == WORKSPACE
+    assert L.kv_cluster_index_init(C.byref(idx), H, d, Cn, cap, 1, 0, 0, 0, None, need, None) == INVALID
+    assert L.kv_cluster_index_init(None, H, d, Cn, cap, 1, 0, 0, 0, p, need, None) == INVALID
+    assert L.kv_cluster_index_init(C.byref(idx), H, 64, Cn, cap, 1, 0, 0, 0, p, need, None) == UNSUPPORTED
+    assert L.kv_cluster_index_init(C.byref(idx), H, d, Cn, cap, 1, 0, -1, 0, p, need, None) == INVALID
+    assert L.kv_cluster_index_init(C.byref(idx), H, d, Cn, cap, 1, 0, 0, 3, p, need, None) == INVALID
+    assert idx.centroids is None   # untouched on error
+
+
+def test_debug_scores_rejects(kvc):
+    L = kvc.lib()
+    p = C.c_void_p(FAKE)
+    built = make_index(kvc, heads=4, n_build=200, n_tokens=200)
+    assert L.kv_cluster_debug_scores(C.byref(built), p, 6, p, None) == INVALID          # 6 % 4 != 0
+    assert L.kv_cluster_debug_scores(C.byref(built), p, 36, p, None) == UNSUPPORTED     # G = 9
+    assert L.kv_cluster_debug_scores(C.byref(built), p, 16, None, None) == INVALID
+    assert L.kv_cluster_debug_scores(C.byref(make_index(kvc)), p, 16, p, None) == INVALID  # never built
 
 
 def test_append_select_decode_reject(kvc):
@@ -170,15 +230,15 @@ def test_window_calls_reject(kvc):
     # slot counts: at least C, at most 512
     few = make_index(kvc, Cn=16)
     few.c_slots = 8
-    assert L.kv_cluster_build(C.byref(few), p, 200, 3, p, p, 1 << 40, None) == INVALID
+    assert L.kv_cluster_build(C.byref(few), p, 200, 3, 1, p, 1 << 40, None) == INVALID
     many = make_index(kvc, Cn=16)
     many.c_slots = 600
-    assert L.kv_cluster_build(C.byref(many), p, 200, 3, p, p, 1 << 40, None) == UNSUPPORTED
+    assert L.kv_cluster_build(C.byref(many), p, 200, 3, 1, p, 1 << 40, None) == UNSUPPORTED
     # the assignment distance is one of cosine, L2, inner product
     for bad in (-1, 3):
         odd = make_index(kvc, Cn=16)
         odd.metric = bad
-        assert L.kv_cluster_build(C.byref(odd), p, 200, 3, p, p, 1 << 40, None) == INVALID
+        assert L.kv_cluster_build(C.byref(odd), p, 200, 3, 1, p, 1 << 40, None) == INVALID
 
 
 def test_cluster_cache_calls_reject(kvc):

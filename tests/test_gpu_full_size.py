@@ -2,10 +2,11 @@
 the benchmark times (kv_cluster_build, then kv_cluster_select_decode per
 decode step; the split select + decode path is checked beside it).
 
-The GPU runs every head. The oracle re-runs the k-means on sampled heads
-(whole heads, every key); the cluster index, selection and decode are checked
-for every head given the GPU's own clustering (integer results bit-exact,
-attention within 2e-3)."""
+The GPU runs every head, and the oracle re-runs the k-means of every head of
+the layers it checks (all 32 heads of workloads 2 and 3, all 128 of workload
+4, all 64 of four of workload 5's 32 layers); the cluster index, selection and
+decode are checked for every head given the GPU's own clustering (integer
+results bit-exact, attention within 2e-3)."""
 import math
 import sys
 
@@ -31,31 +32,40 @@ def gen(w, layer=0):
     K, _, means = synth.mixture_keys(base, w.heads, w.capacity, w.d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype,
                                      want_means=(w.query == "mixture"))
     V = synth.values(base, w.heads, w.capacity, w.d, w.dtype)
-    init = synth.init_idx(base, w.heads, w.L, w.C)
+    init = oracle.init_positions(w.heads, w.L, w.C, base)
     return base, K, V, init, means
 
 
-def check_build(w, K, init, idx, sample):
+def check_build(w, K, init, idx, heads=None):
+    """The oracle's k-means of the given heads (all by default) against the
+    GPU's: label agreement, centroids of clusters with identical membership,
+    operand from the GPU's centroids; the index bit-exact given the GPU's
+    labels on every head."""
     gl = to_np(idx.labels)[:, :w.L]
     gc = to_np(idx.centroids)
     opt = oracle.BF16 if w.dtype == synth.BF16 else oracle.F32
-    # index: bit-exact given the GPU's labels, every head
     sizes, offsets, ids = to_np(idx.sizes), to_np(idx.offsets), to_np(idx.token_ids)[:, :w.L]
     for h in range(w.heads):
         s, o, i = oracle.csr(gl[h], w.C)
         assert np.array_equal(sizes[h], s) and np.array_equal(offsets[h], o) and np.array_equal(ids[h], i), h
-    # k-means on sampled heads, whole heads
+    sample = list(range(w.heads)) if heads is None else list(heads)
     Ks = np.ascontiguousarray(K[sample, :w.L])
     ref = oracle.build(Ks, w.C, w.iters, np.ascontiguousarray(init[sample]))
     agree = (gl[sample] == ref["labels"]).mean()
-    worst = 0.0
+    worst, same, total = 0.0, 0, 0
+    gop = to_np(idx.centroids_op)
     for a, h in enumerate(sample):
+        ro, ri = ref["offsets"][a], ref["token_ids"][a]
         for k in range(w.C):
-            if np.array_equal(np.flatnonzero(gl[h] == k), np.flatnonzero(ref["labels"][a] == k)):
+            total += 1
+            if ro[k + 1] - ro[k] == offsets[h, k + 1] - offsets[h, k] and np.array_equal(
+                    ri[ro[k]:ro[k + 1]], ids[h, offsets[h, k]:offsets[h, k + 1]]):
+                same += 1
                 nrm = max(np.linalg.norm(ref["c"][a, k]), 1e-30)
                 worst = max(worst, np.linalg.norm(gc[h, k] - ref["c"][a, k]) / nrm)
-        assert np.array_equal(to_np(idx.centroids_op)[h, :w.C], oracle.normalize(gc[h], opt))
-    say(f"  heads {sample}: label agreement {agree:.6f}, centroid rel err {worst:.2e}")
+        assert np.array_equal(gop[h, :w.C], oracle.normalize(gc[h], opt))
+    say(f"  {len(sample)} heads: label agreement {agree:.6f}, {same}/{total} clusters with identical members, "
+        f"centroid rel err {worst:.2e}")
     assert agree >= 0.999 and worst <= 1e-3
 
 
@@ -97,10 +107,10 @@ def test_full_size_build_select_decode(cfg):
     base, K, V, init, means = gen(w)
     idx = kvc.ClusterIndex(w.heads, w.C, w.capacity, torch.bfloat16, packed=True)
     Kd, Vd = to_dev(K), to_dev(V)
-    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.build(idx, Kd, w.L, w.iters, seed=base)
     torch.cuda.synchronize()
     assert int(to_np(idx.dev_flags)[0]) == 0
-    check_build(w, K, init, idx, [0, w.heads - 1])
+    check_build(w, K, init, idx)
     scale = 1.0 / math.sqrt(w.d)
     for step in (0, 1, w.steps - 1):
         q = queries(w, base, step, K, w.L, means)
@@ -140,9 +150,9 @@ def test_full_size_append_workload():
     Vp[:, w.L:] = 0
     idx = kvc.ClusterIndex(w.heads, w.C, w.capacity, torch.bfloat16)
     Kd, Vd = to_dev(Kp), to_dev(Vp)
-    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.build(idx, Kd, w.L, w.iters, seed=base)
     torch.cuda.synchronize()
-    check_build(w, K, init, idx, [5])
+    check_build(w, K, init, idx)
     built = dict(labels=to_np(idx.labels)[:, :w.L], sizes=to_np(idx.sizes), offsets=to_np(idx.offsets),
                  token_ids=to_np(idx.token_ids)[:, :w.L], c=to_np(idx.centroids),
                  chat=to_np(idx.centroids_op)[:, :w.C])
@@ -163,22 +173,29 @@ def test_full_size_append_workload():
             say(f"  step {s}: {n + 1} tokens, decode max abs err fused {ferr:.2e}, split {err:.2e}")
 
 
-def test_full_size_layer_stack_sampled_layers():
-    """The 32-layer stack runs layer by layer through the same calls; two
-    layers (the first and the last, independent seeded mixtures) are built and
-    checked at their full size."""
+@pytest.mark.parametrize("layer", [0, 10, 21, 31])
+def test_full_size_layer_stack(layer):
+    """The 32-layer stack runs layer by layer through the same calls; four
+    layers (independent seeded mixtures, the first and the last among them)
+    are built and checked at their full size: the k-means of all 64 KV heads
+    against the oracle's, then 8 of the 64 decode steps on the benchmark's
+    configuration (the fused kernel reading the packed copy, and the token
+    split), every head."""
     w = synth.workload(5)
     scale = 1.0 / math.sqrt(w.d)
-    for layer in (0, w.layers - 1):
-        say(f"[full size] {w.name} layer {layer}: {w.heads} heads x {w.L} keys, C={w.C}, B={w.B}")
-        base, K, V, init, means = gen(w, layer)
-        idx = kvc.ClusterIndex(w.heads, w.C, w.capacity, torch.bfloat16)
-        Kd, Vd = to_dev(K), to_dev(V)
-        kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
-        torch.cuda.synchronize()
-        check_build(w, K, init, idx, [layer % w.heads])
-        q = queries(w, base, 0, K, w.L, means)
-        ferr, _ = check_step(w, idx, K, V, Kd, Vd, q, w.B, scale, split=False)
-        say(f"  decode max abs err fused {ferr:.2e}")
-        del Kd, Vd, idx
-        torch.cuda.empty_cache()
+    say(f"[full size] {w.name} layer {layer}: {w.heads} heads x {w.L} keys, C={w.C}, B={w.B}")
+    base, K, V, init, means = gen(w, layer)
+    idx = kvc.ClusterIndex(w.heads, w.C, w.capacity, torch.bfloat16, packed=True)
+    Kd, Vd = to_dev(K), to_dev(V)
+    kvc.build(idx, Kd, w.L, w.iters, seed=base)
+    torch.cuda.synchronize()
+    check_build(w, K, init, idx)
+    kvc.pack(idx, Kd, Vd)
+    worst = 0.0
+    for step in range(0, w.steps, 8):
+        q = queries(w, base, step, K, w.L, means)
+        ferr, _ = check_step(w, idx, K, V, Kd, Vd, q, w.B, scale, split=(step == 0))
+        worst = max(worst, ferr)
+    say(f"  8 decode steps: decode max abs err {worst:.2e}")
+    del Kd, Vd, idx
+    torch.cuda.empty_cache()

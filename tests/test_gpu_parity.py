@@ -46,10 +46,10 @@ def pad_op(chat: np.ndarray, cpad: int) -> np.ndarray:
     return out
 
 
-def built_gpu(w, K, init, packed=False):
+def built_gpu(w, K, seed, packed=False):
     idx = kvc.ClusterIndex(K.shape[0], w.C, w.capacity, torch_dtype(w), packed=packed)
     Kd = to_dev(K)
-    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.build(idx, Kd, w.L, w.iters, seed=seed)
     torch.cuda.synchronize()
     return idx, Kd
 
@@ -129,7 +129,7 @@ def test_build_select_decode_end_to_end(case):
     say(f"[end to end] {case}")
     base, K, V, init, means = make_inputs(w)
     H = K.shape[0]
-    idx, Kd = built_gpu(w, K, init, packed=True)
+    idx, Kd = built_gpu(w, K, base, packed=True)
     assert int(to_np(idx.dev_flags)[0]) == 0
     ref = oracle.build(np.ascontiguousarray(K[:, :w.L]), w.C, w.iters, init)
     gl = to_np(idx.labels)[:, :w.L]
@@ -208,7 +208,7 @@ def test_append_long_lists():
     Kc, Vc = np.zeros_like(K), np.zeros_like(V)
     Kc[:, :w.L], Vc[:, :w.L] = K[:, :w.L], V[:, :w.L]
     Kd, Vd = to_dev(Kc), to_dev(Vc)
-    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.build(idx, Kd, w.L, w.iters, seed=base)
     torch.cuda.synchronize()
     built = dict(labels=to_np(idx.labels)[:, :w.L], sizes=to_np(idx.sizes), offsets=to_np(idx.offsets),
                  token_ids=to_np(idx.token_ids)[:, :w.L], c=to_np(idx.centroids),
@@ -240,7 +240,7 @@ def test_append_then_select_decode():
     Vc = np.zeros_like(V)
     Kc[:, :w.L], Vc[:, :w.L] = K[:, :w.L], V[:, :w.L]
     Kd, Vd = to_dev(Kc), to_dev(Vc)
-    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.build(idx, Kd, w.L, w.iters, seed=base)
     kvc.pack(idx, Kd, Vd)
     torch.cuda.synchronize()
     assert idx._s.packed == 1
@@ -315,12 +315,12 @@ def test_attention_sinks_end_to_end():
     w, n_sink = SMALL_APPEND, 16
     base, K, V, init, means = make_inputs(w)
     H = K.shape[0]
-    init = synth.init_idx(base, H, w.L - n_sink, w.C) + n_sink
+    init = oracle.init_positions(H, w.L, w.C, base, n_sink)
     idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w), packed=True, n_sink=n_sink)
     Kc, Vc = K.copy(), V.copy()
     Kc[:, w.L:], Vc[:, w.L:] = 0, 0
     Kd, Vd = to_dev(Kc), to_dev(Vc)
-    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.build(idx, Kd, w.L, w.iters, seed=base)
     torch.cuda.synchronize()
     assert int(to_np(idx.dev_flags)[0]) == 0
     ref = oracle.build(np.ascontiguousarray(K[:, :w.L]), w.C, w.iters, init, n_sink=n_sink)
@@ -376,13 +376,13 @@ def test_window_clustering_end_to_end():
     w, n_sink, m, nc = SMALL_WINDOW, 8, 40, 4
     base, K, V, _, means = make_inputs(w)
     H = K.shape[0]
-    init = synth.init_idx(base, H, w.L - n_sink, w.C) + n_sink
+    init = oracle.init_positions(H, w.L, w.C, base, n_sink)
     slots = w.C + 3 * nc
     idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w), packed=True, n_sink=n_sink, c_slots=slots)
     Kc, Vc = K.copy(), V.copy()
     Kc[:, w.L:], Vc[:, w.L:] = 0, 0
     Kd, Vd = to_dev(Kc), to_dev(Vc)
-    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.build(idx, Kd, w.L, w.iters, seed=base)
     kvc.pack(idx, Kd, Vd)
     torch.cuda.synchronize()
     ref = oracle.build(np.ascontiguousarray(K[:, :w.L]), w.C, w.iters, init, n_sink=n_sink)
@@ -479,7 +479,7 @@ def test_window_clustering_one_launch_and_general(metric, nc):
     Kc, Vc = K.copy(), V.copy()
     Kc[:, w.L:], Vc[:, w.L:] = 0, 0
     Kd, Vd = to_dev(Kc), to_dev(Vc)
-    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.build(idx, Kd, w.L, w.iters, seed=base)
     ref = oracle.build(np.ascontiguousarray(K[:, :w.L]), w.C, w.iters, init, metric=om)
     oi = oracle.Index(ref, w.capacity, metric=om)
     for n in range(w.L, w.L + m):
@@ -552,7 +552,7 @@ def test_distance_variants_end_to_end(case, metric):
     Kc, Vc = K.copy(), V.copy()
     Kc[:, w.L:], Vc[:, w.L:] = 0, 0
     Kd, Vd = to_dev(Kc), to_dev(Vc)
-    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.build(idx, Kd, w.L, w.iters, seed=base)
     torch.cuda.synchronize()
     assert int(to_np(idx.dev_flags)[0]) == 0
     ref = oracle.build(np.ascontiguousarray(K[:, :w.L]), w.C, w.iters, init, metric=om)
@@ -598,10 +598,10 @@ def test_cluster_cache_matches_uncached_path(where):
     base, K, V, _, means = make_inputs(w)
     H = K.shape[0]
     host = where == "host"
-    init = synth.init_idx(base, H, w.L - n_sink, w.C) + n_sink
+    init = oracle.init_positions(H, w.L, w.C, base, n_sink)
     idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w), packed=True, n_sink=n_sink, packed_on_host=host)
     Kd, Vd = to_dev(K), to_dev(V)
-    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.build(idx, Kd, w.L, w.iters, seed=base)
     Ks, Vs = (Kd.cpu().pin_memory(), Vd.cpu().pin_memory()) if host else (Kd, Vd)
     kvc.pack(idx, Ks, Vs)
     torch.cuda.synchronize()
@@ -648,10 +648,10 @@ def test_selection_merge_and_full_ranking():
     w, n_sink = MANY, 5
     base, K, V, _, means = make_inputs(w)
     H = K.shape[0]
-    init = synth.init_idx(base, H, w.L - n_sink, w.C) + n_sink
+    init = oracle.init_positions(H, w.L, w.C, base, n_sink)
     idx = kvc.ClusterIndex(H, w.C, w.capacity, torch_dtype(w), packed=True, n_sink=n_sink)
     Kd, Vd = to_dev(K), to_dev(V)
-    kvc.build(idx, Kd, w.L, w.iters, to_dev(init))
+    kvc.build(idx, Kd, w.L, w.iters, seed=base)
     kvc.pack(idx, Kd, Vd)
     torch.cuda.synchronize()
     c, sizes, offsets, token_ids = (to_np(idx.centroids), to_np(idx.sizes), to_np(idx.offsets),
@@ -699,7 +699,7 @@ def test_graph_replay_matches_eager():
     scale = 1.0 / math.sqrt(w.d)
 
     def prepare():
-        kvc.build(idx, Kd, w.L, w.iters, initd, workspace=ws)
+        kvc.build(idx, Kd, w.L, w.iters, init_idx=initd, workspace=ws)
         kvc.pack(idx, Kd, Vd)
 
     wsd = split_ws(idx, H * w.G)
@@ -738,6 +738,6 @@ def test_init_index_out_of_range_flag():
     bad = init.copy()
     bad[1, 5] = w.L + 3
     idx = kvc.ClusterIndex(K.shape[0], w.C, w.capacity, torch.bfloat16)
-    kvc.build(idx, to_dev(K), w.L, 1, to_dev(bad))
+    kvc.build(idx, to_dev(K), w.L, 1, init_idx=to_dev(bad))
     torch.cuda.synchronize()
     assert int(to_np(idx.dev_flags)[0]) & 1
