@@ -77,6 +77,7 @@ def lib():
         L.kv_sparse_decode_workspace_bytes.argtypes = [i, i, i, i]
         L.kv_sparse_decode_workspace_bytes.restype = sz
         L.kv_sparse_decode.argtypes = [p, i, p, p, i, i, i, i, p, p, i, f, p, p, sz, p]
+        L.kv_sparse_decode_noalloc.argtypes = [p, i, p, p, i, i, i, i, p, p, i, f, p, p]
         L.kv_cluster_select_decode_workspace_bytes.argtypes = [i, i, i]
         L.kv_cluster_select_decode_workspace_bytes.restype = sz
         L.kv_cluster_select_decode.argtypes = [p, p, i, p, p, i, f, p, p, p, p, sz, p]
@@ -95,7 +96,8 @@ def lib():
         L.kv_cluster_status_string.restype = C.c_char_p
         for name in ("kv_cluster_index_init", "kv_cluster_init_positions", "kv_cluster_build_from",
                      "kv_cluster_debug_scores", "kv_cluster_build", "kv_cluster_build_timed", "kv_cluster_append", "kv_cluster_append_window",
-                     "kv_cluster_cluster_window", "kv_cluster_select", "kv_sparse_decode", "kv_cluster_select_decode",
+                     "kv_cluster_cluster_window", "kv_cluster_select", "kv_sparse_decode", "kv_sparse_decode_noalloc",
+                     "kv_cluster_select_decode",
                      "kv_cluster_export_csr", "kv_cluster_pack", "kv_dense_decode", "kv_cluster_debug_assign",
                      "kv_cluster_debug_update", "kv_cluster_cache_reset", "kv_cluster_cached_select_decode"):
             getattr(L, name).restype = i
@@ -415,6 +417,24 @@ def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _check(lib().kv_sparse_decode(_ptr(q), q.shape[0], _ptr(k_cache), _ptr(v_cache), _dtype_code(q.dtype), heads,
                                   capacity, d, _ptr(sel_ids), _ptr(sel_count), B, float(scale), _ptr(out),
                                   _ptr(workspace), workspace.numel(), _stream(stream)), "kv_sparse_decode")
+    return out
+
+
+def sparse_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, sel_ids: torch.Tensor,
+                          sel_count: torch.Tensor, scale: float, out: torch.Tensor | None = None, stream=None):
+    """kv_sparse_decode_noalloc: kv_sparse_decode with the partial results in
+    the library's fixed device scratch (no workspace) -> fp32 [q_heads, d]."""
+    heads, capacity, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype or q.dtype != k_cache.dtype:
+        raise ValueError("q, k_cache and v_cache must share a type; k and v caches a shape")
+    B = sel_ids.shape[1]
+    if sel_ids.dtype != torch.int32 or sel_ids.shape[0] != heads or sel_count.numel() != heads:
+        raise ValueError("sel_ids must be int32 [heads, B], sel_count int32 [heads]")
+    if out is None:
+        out = torch.empty(q.shape[0], d, dtype=torch.float32, device=q.device)
+    _check(lib().kv_sparse_decode_noalloc(_ptr(q), q.shape[0], _ptr(k_cache), _ptr(v_cache), _dtype_code(q.dtype),
+                                          heads, capacity, d, _ptr(sel_ids), _ptr(sel_count), B, float(scale),
+                                          _ptr(out), _stream(stream)), "kv_sparse_decode_noalloc")
     return out
 
 

@@ -437,10 +437,11 @@ size_t kv_sparse_decode_workspace_bytes(int heads, int q_heads, int d, int B) {
   return align_up(sizeof(float) * heads * nsplit * G * (d + 2));
 }
 
-kvc_status kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
-                     int capacity, int d, const int32_t* sel_ids, const int32_t* sel_count, int B, float scale,
-                     float* out, void* ws, size_t ws_bytes, void* stream) {
-  if (!q || !k_cache || !v_cache || !sel_ids || !sel_count || !out || !ws) return KVC_ERR_INVALID_ARG;
+namespace {
+kvc_status sparse_decode_check(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype,
+                               int heads, int capacity, int d, const int32_t* sel_ids, const int32_t* sel_count,
+                               int B, const float* out) {
+  if (!q || !k_cache || !v_cache || !sel_ids || !sel_count || !out) return KVC_ERR_INVALID_ARG;
   if (heads < 1 || q_heads < 1 || capacity < 1 || B < 1 || q_heads % heads != 0) return KVC_ERR_INVALID_ARG;
   if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_INVALID_ARG;
   if (d != KVC_HEAD_DIM) return KVC_ERR_UNSUPPORTED;
@@ -448,9 +449,33 @@ kvc_status kv_sparse_decode(const void* q, int q_heads, const void* k_cache, con
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVC_ERR_UNSUPPORTED;
   if ((long long)heads * B >= (1ll << 31)) return KVC_ERR_INVALID_ARG;
   if ((long long)((B + DEC_TOK - 1) / DEC_TOK) * G > DEC_MAX_PAIRS) return KVC_ERR_UNSUPPORTED;
+  return KVC_OK;
+}
+}  // namespace
+
+kvc_status kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype,
+                            int heads, int capacity, int d, const int32_t* sel_ids, const int32_t* sel_count, int B,
+                            float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (kvc_status s = sparse_decode_check(q, q_heads, k_cache, v_cache, dtype, heads, capacity, d, sel_ids,
+                                         sel_count, B, out))
+    return s;
+  if (!ws) return KVC_ERR_INVALID_ARG;
   if (ws_bytes < kv_sparse_decode_workspace_bytes(heads, q_heads, d, B)) return KVC_ERR_WORKSPACE;
-  return status(launch_decode(dtype, q, G, k_cache, v_cache, (long long)capacity * d, heads, sel_ids, sel_count, B,
-                                  scale, out, static_cast<float*>(ws), static_cast<hipStream_t>(stream)));
+  return status(launch_decode(dtype, q, q_heads / heads, k_cache, v_cache, (long long)capacity * d, heads, sel_ids,
+                              sel_count, B, scale, out, static_cast<float*>(ws), static_cast<hipStream_t>(stream)));
+}
+
+kvc_status kv_sparse_decode_noalloc(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype,
+                                    int heads, int capacity, int d, const int32_t* sel_ids, const int32_t* sel_count,
+                                    int B, float scale, float* out, void* stream) {
+  if (kvc_status s = sparse_decode_check(q, q_heads, k_cache, v_cache, dtype, heads, capacity, d, sel_ids,
+                                         sel_count, B, out))
+    return s;
+  if (kv_sparse_decode_workspace_bytes(heads, q_heads, d, B) > KVC_NOALLOC_SCRATCH_BYTES) return KVC_ERR_TOO_LARGE;
+  void* part = nullptr;
+  if (noalloc_scratch(&part) != hipSuccess) return KVC_ERR_HIP;
+  return status(launch_decode(dtype, q, q_heads / heads, k_cache, v_cache, (long long)capacity * d, heads, sel_ids,
+                              sel_count, B, scale, out, static_cast<float*>(part), static_cast<hipStream_t>(stream)));
 }
 
 size_t kv_cluster_select_decode_workspace_bytes(int heads, int q_heads, int d) {
@@ -584,6 +609,7 @@ const char* kv_cluster_status_string(kvc_status s) {
     case KVC_ERR_WORKSPACE: return "workspace too small";
     case KVC_ERR_CAPACITY: return "index capacity exceeded";
     case KVC_ERR_HIP: return "HIP launch failure";
+    case KVC_ERR_TOO_LARGE: return "request larger than the fixed device scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

@@ -7,6 +7,8 @@
 // one is trimmed; indexing works per KV head), II.A "LLM Inference and KV
 // Cache" (the latest query attends to the cached keys and values) and III.A
 // "Problem Formulation" (attention over the B selected tokens).
+#include <mutex>
+
 #include "kvc_device.h"
 #include "kvc_internal.h"
 
@@ -1740,6 +1742,35 @@ hipError_t launch_decode(int dtype, const void* q, int G, const void* kc, const 
   if (dtype == DT_BF16)
     return decode_dispatch<uint16_t>(q, G, kc, vc, head_stride, heads, sel_ids, sel_count, B, qscale, out, part, st);
   return decode_dispatch<float>(q, G, kc, vc, head_stride, heads, sel_ids, sel_count, B, qscale, out, part, st);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed device scratch of the allocation-free decode entry point: the split-K
+// partial results live in this file-scope array, which every GPU the library
+// runs on holds until the process ends. In host code the array's name is a
+// stand-in, not a device address: host code reaches the memory only through
+// the address hipGetSymbolAddress returns with the device current, looked up
+// once per device and kept.
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_export_csr(int heads, int ca, int cs, const int32_t* offsets, const int32_t* token_ids,

@@ -14,6 +14,11 @@ constexpr int DEC_MAX_PAIRS = 512;  // splits x query heads one merge block hold
 
 int csr_blocks(int L);
 
+// Bytes of the fixed device scratch of kv_sparse_decode_noalloc.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)16 << 20;
+// The current device's address of that scratch (looked up once per device).
+hipError_t noalloc_scratch(void** ptr);
+
 // The index as the selection kernels read it: device arrays with per-head
 // strides of cs cluster slots (cs + 1 for the prefix arrays) and cap tokens;
 // clusters 0 .. ca-1 in use; ahead of the clusters, the n_sink attention sinks

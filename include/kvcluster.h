@@ -65,7 +65,8 @@ typedef enum kvc_status {
   KVC_ERR_UNSUPPORTED = 2, /* valid for the method, not for this GPU path (d != 128, C > 512, G > 8) */
   KVC_ERR_WORKSPACE = 3,   /* workspace smaller than the matching *_workspace_bytes() */
   KVC_ERR_CAPACITY = 4,    /* an append would pass the index capacity */
-  KVC_ERR_HIP = 5          /* a kernel launch failed */
+  KVC_ERR_HIP = 5,         /* a kernel launch failed */
+  KVC_ERR_TOO_LARGE = 6    /* larger than the fixed scratch of kv_sparse_decode_noalloc */
 } kvc_status;
 
 /*
@@ -318,6 +319,26 @@ size_t kv_sparse_decode_workspace_bytes(int heads, int q_heads, int d, int B);
 kvc_status kv_sparse_decode(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype, int heads,
                      int capacity, int d, const int32_t* sel_ids, const int32_t* sel_count, int B, float scale,
                      float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kv_sparse_decode for callers that cannot allocate device memory or hand
+ * over a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. The same kernels and the same result;
+ * the split-K partial results go to a fixed device scratch of
+ * KVC_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends (a static device array; no allocation, no
+ * allocating library call). The caller still passes inputs and output.
+ * Returns KVC_ERR_TOO_LARGE, enqueuing nothing, when the request needs more
+ * than that (kv_sparse_decode_workspace_bytes(heads, q_heads, d, B) >
+ * KVC_NOALLOC_SCRATCH_BYTES), and the other status codes as
+ * kv_sparse_decode. Every call on one GPU shares its scratch, so calls that
+ * overlap on one GPU (concurrent streams) race; calls ordered on one stream
+ * do not. Nothing in the scratch needs clearing between calls.
+ */
+#define KVC_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+kvc_status kv_sparse_decode_noalloc(const void* q, int q_heads, const void* k_cache, const void* v_cache, int dtype,
+                                    int heads, int capacity, int d, const int32_t* sel_ids,
+                                    const int32_t* sel_count, int B, float scale, float* out, void* stream);
 
 /*
  * Cluster-ordered copy of the keys and values of the index's main part: row i

@@ -54,8 +54,8 @@ def make_index(kvc, heads=4, d=128, Cn=16, cap=256, dtype=1, n_build=0, n_tokens
 
 def test_status_strings_and_sizes(kvc):
     L = kvc.lib()
-    for code in range(6):
-        assert L.kv_cluster_status_string(code)
+    for code in range(7):
+        assert L.kv_cluster_status_string(code) != b"unknown status"
     assert L.kv_cluster_status_string(99) == b"unknown status"
     assert [L.kv_cluster_cpad(c) for c in (1, 32, 33, 400, 512)] == [32, 32, 64, 416, 512]
     a = L.kv_cluster_build_workspace_bytes(128, 32768, 400, 10)
@@ -179,6 +179,13 @@ def test_append_select_decode_reject(kvc):
     assert dec(ws=ws - 1) == WORKSPACE
     assert dec(B=0) == INVALID
     assert dec(qh=32, B=4096 + 64, ws=1 << 40) == UNSUPPORTED   # 65 splits x 8 heads > 512 pairs
+    # the allocation-free variant: the same checks, and requests beyond its
+    # fixed scratch are refused before anything is enqueued
+    na = lambda **k: L.kv_sparse_decode_noalloc(p, k.get("qh", 16), p, p, 1, k.get("heads", 4), 256, k.get("d", 128),
+                                                p, p, k.get("B", 64), f, k.get("out", p), None)
+    assert na(d=64) == UNSUPPORTED and na(qh=10) == INVALID and na(B=0) == INVALID and na(out=None) == INVALID
+    assert L.kv_sparse_decode_workspace_bytes(8192, 8192 * 8, 128, 1024) > 16 << 20
+    assert na(heads=8192, qh=8192 * 8, B=1024) == 6  # KVC_ERR_TOO_LARGE
     assert L.kv_cluster_export_csr(C.byref(built), None, p, None) == INVALID
     # the dense comparator: bf16 only, 1 <= n <= capacity, enough workspace
     dws = L.kv_dense_decode_workspace_bytes(4, 16, 128, 200)
