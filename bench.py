@@ -116,7 +116,8 @@ def main():
                          "split: kv_cluster_select then kv_sparse_decode")
     ap.add_argument("--token-split", choices=["auto", "on", "off"], default="auto",
                     help="fused path: give kv_cluster_select_decode a workspace, so that the blocks of a KV head "
-                         "split the selected tokens and a second kernel merges them (auto: below 128 KV heads)")
+                         "split the selected tokens and the last of them merges the partial results (auto: "
+                         "wherever the path has it, bf16 with at most 4 query heads per KV head)")
     ap.add_argument("--sinks", type=int, default=0,
                     help="attention sinks per head: kept out of the clustering, always selected (default 0)")
     ap.add_argument("--metric", choices=["cosine", "l2", "inner_product"], default="cosine",
@@ -236,9 +237,9 @@ def main():
     ws_build = torch.empty(kvc.build_workspace_bytes(H, L, C, w.iters), dtype=torch.uint8, device=dev)
     ws_dec = torch.empty(kvc.decode_workspace_bytes(H, H * G, B), dtype=torch.uint8, device=dev)
     # the library uses the workspace for bf16 and at most 4 query heads per KV head
-    tsplit = (fused and w.dtype == synth.BF16 and G <= 4
-              and (args.token_split == "on" or (args.token_split == "auto" and H < 128)))
-    ws_sd = (torch.empty(kvc.select_decode_workspace_bytes(H, H * G), dtype=torch.uint8, device=dev)
+    tsplit = fused and w.dtype == synth.BF16 and G <= 4 and args.token_split in ("on", "auto")
+    # (its arrival counters must start at zero; every call leaves them zero)
+    ws_sd = (torch.zeros(kvc.select_decode_workspace_bytes(H, H * G), dtype=torch.uint8, device=dev)
              if tsplit else None)
     ws_win = (torch.empty(kvc.window_workspace_bytes(H, M, NC, w.iters), dtype=torch.uint8, device=dev)
               if M else None)
@@ -408,7 +409,7 @@ def main():
         kernel_names["select_decode"] = ("select_decode_bf16_kernel" if w.dtype == synth.BF16
                                          else "select_decode_kernel")
         if ws_sd is not None:
-            kernel_names["select_decode"] = "select_decode_bf16_kernel (token split) + decode_combine_kernel"
+            kernel_names["select_decode"] = "select_decode_bf16_kernel (token split, merged by the last block)"
         if offload >= 1:
             kernel_names["select_decode"] = "cache_assemble_kernel + decode_split_kernel + decode_combine_kernel"
     else:
@@ -462,9 +463,9 @@ def main():
         "kernel_timing": (("HIP events around every assignment kernel; the fused kernel's launch time is the "
                            "event-bracketed decode phase over its launches (the phase replays only that kernel)")
                           if phase_only and ws_sd is None else
-                          ("HIP events around every assignment kernel; the time per decode step of the fused "
-                           "kernel and the merge of its token split is the event-bracketed decode phase over its "
-                           "steps (the phase replays only those two kernels)")
+                          ("HIP events around every assignment kernel; the fused kernel's launch time (token "
+                           "split, merged in the kernel) is the event-bracketed decode phase over its launches "
+                           "(the phase replays only that kernel)")
                           if phase_only else
                           f"HIP events around every kernel of 1 in {SAMPLE} decode steps (passes launched step "
                           "by step) and around every assignment kernel; value from events bracketing each pass's "

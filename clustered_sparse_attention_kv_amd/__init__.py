@@ -446,8 +446,8 @@ def select_decode(idx: ClusterIndex, q: torch.Tensor, k_cache: torch.Tensor, v_c
                   scale: float, out: torch.Tensor | None = None, sel_ids: torch.Tensor | None = None,
                   sel_count: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
     """kv_cluster_select_decode: selection and sparse attention -> fp32 [q_heads, d]. Without a workspace
-    one kernel; with one (select_decode_workspace_bytes), the blocks of a head split the tokens and a
-    second kernel merges their partial results."""
+    one kernel; with one (select_decode_workspace_bytes, its arrival counters zero before the first call), the
+    blocks of a head split the tokens and the last of them merges their partial results."""
     _cache_check(idx, k_cache, "k_cache")
     _cache_check(idx, v_cache, "v_cache")
     if q.dtype != idx.dtype or q.dim() != 2 or q.shape[1] != idx.d:

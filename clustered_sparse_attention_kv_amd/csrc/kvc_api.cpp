@@ -481,7 +481,8 @@ kvc_status kv_sparse_decode_noalloc(const void* q, int q_heads, const void* k_ca
 size_t kv_cluster_select_decode_workspace_bytes(int heads, int q_heads, int d) {
   if (heads < 1 || q_heads < heads || d < 1) return 0;
   const int G = q_heads / heads;
-  return align_up(sizeof(float) * heads * fused_blocks_per_head(heads) * G * (d + 2));
+  // the arrival counters [heads], then the partial results [heads, P, G, d + 2]
+  return align_up(sizeof(int32_t) * heads) + align_up(sizeof(float) * heads * fused_blocks_per_head(heads) * G * (d + 2));
 }
 
 kvc_status kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, const void* k_cache,
@@ -497,10 +498,13 @@ kvc_status kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_h
   const IndexView x = view(idx);
   const bool packed = idx->packed == 1 && idx->k_packed && idx->v_packed;
   // the token split exists for bf16 and at most 4 query heads per KV head
-  float* part = ws && idx->dtype == KVC_BF16 && G <= 4 ? static_cast<float*>(ws) : nullptr;
+  const bool ts = ws && idx->dtype == KVC_BF16 && G <= 4;
+  int32_t* arrive = ts ? static_cast<int32_t*>(ws) : nullptr;
+  float* part =
+      ts ? reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(sizeof(int32_t) * idx->heads)) : nullptr;
   return status(launch_select_decode(idx->dtype, q, G, x, idx->heads, k_cache, v_cache,
                                          packed ? idx->k_packed : nullptr, packed ? idx->v_packed : nullptr, B, scale,
-                                         out, sel_ids, sel_count, part, static_cast<hipStream_t>(stream)));
+                                         out, sel_ids, sel_count, part, arrive, static_cast<hipStream_t>(stream)));
 }
 
 kvc_status kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_cache, void* stream) {

@@ -258,32 +258,46 @@ __device__ __forceinline__ void bitonic_sort(Sh& S, unsigned long long& key, int
 // qbar_j of KV head h: the fp64 sum over its G query heads in ascending order
 // (III.C ranks clusters by their centroid's attention weight to the query; the
 // query heads sharing a KV head share one selection).
+// (all G values are requested before the sum, which runs in ascending g)
 template <typename QT>
 __device__ __forceinline__ double query_sum(const QT* __restrict__ q, int G, int h, int j) {
+  float v[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) v[g] = g < G ? load_f32(q, ((size_t)h * G + g) * D + j) : 0.f;
   double s = 0.0;
-  for (int g = 0; g < G; ++g) s = s + (double)load_f32(q, ((size_t)h * G + g) * D + j);
+#pragma unroll
+  for (int g = 0; g < 8; ++g)
+    if (g < G) s = s + (double)v[g];
   return s;
 }
 
 // Score of cluster k: the fp64 chain over ascending j of qbar_j * c_kj. The
 // centroids come from the chunk-major copy [d/4, cs, 4] of the head: chunk jj
 // of row k sits at ((jj * cs) + k) * 16 bytes, so the 64 lanes of a wave
-// scoring consecutive clusters read 1 KiB contiguously.
-__device__ __forceinline__ double centroid_score(const double* qbar, const float* __restrict__ cent_t_head, int cs,
-                                                 int k) {
+// scoring consecutive clusters read 1 KiB contiguously. The row's 32 chunks
+// are requested together (centroid_load), so that a caller can issue them
+// before it waits for anything else, and then chained (centroid_chain).
+struct CentroidRow {
+  f32x4 v[D / 4];
+};
+__device__ __forceinline__ void centroid_load(CentroidRow& r, const float* __restrict__ cent_t_head, int cs, int k) {
   const f32x4* ct = reinterpret_cast<const f32x4*>(cent_t_head) + k;
+#pragma unroll
+  for (int jj = 0; jj < D / 4; ++jj) r.v[jj] = ct[(size_t)jj * cs];
+}
+__device__ __forceinline__ double centroid_chain(const double* qbar, const CentroidRow& r) {
   double sc = 0.0;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    f32x4 v[16];
+  for (int jj = 0; jj < D / 4; ++jj)
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) v[jj] = ct[(size_t)(half * 16 + jj) * cs];
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc = fma(qbar[half * 64 + 4 * jj + i], (double)v[jj][i], sc);
-  }
+    for (int i = 0; i < 4; ++i) sc = fma(qbar[4 * jj + i], (double)r.v[jj][i], sc);
   return sc;
+}
+__device__ __forceinline__ double centroid_score(const double* qbar, const float* __restrict__ cent_t_head, int cs,
+                                                 int k) {
+  CentroidRow r;
+  centroid_load(r, cent_t_head, cs, k);
+  return centroid_chain(qbar, r);
 }
 
 // Returns the cluster id of rank tid (ids >= X.ca are padding).
@@ -292,22 +306,39 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
                                             int B) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int C = X.ca, cs = X.cs;
-  if (tid < C) {  // per-cluster metadata, read while the scores are computed
-    S.mn[tid] = X.sizes[(size_t)h * cs + tid];
-    const int o = X.offsets[(size_t)h * (cs + 1) + tid];
-    S.mo[tid] = o;
-    S.mb[tid] = X.offsets[(size_t)h * (cs + 1) + tid + 1] - o;
-    S.ma[tid] = X.app_offsets[(size_t)h * (cs + 1) + tid];
+  // Requests in this order: the query and the per-cluster metadata, then the
+  // thread's centroid row (32 chunks at once). Loads complete in order, so the
+  // LDS stores of the query sum and the metadata wait for their own loads
+  // only, and the centroid rows arrive while the block meets at the barrier.
+  // (Every block of a head streams the head's whole centroids: sharing the
+  // scores between a head's blocks through device memory costs several
+  // device-coherent round trips, more than the reads it saves.)
+  double qs = 0.0;
+  if (tid < D) qs = query_sum(q, G, h, tid);
+  int mn = 0, mo = 0, mo1 = 0, ma = 0;
+  if (tid < C) {
+    mn = X.sizes[(size_t)h * cs + tid];
+    mo = X.offsets[(size_t)h * (cs + 1) + tid];
+    mo1 = X.offsets[(size_t)h * (cs + 1) + tid + 1];
+    ma = X.app_offsets[(size_t)h * (cs + 1) + tid];
   }
-  if (tid < D) S.qbar[tid] = query_sum(q, G, h, tid);
+  CentroidRow crow;
+  if (tid < C) centroid_load(crow, X.cent_t + (size_t)h * cs * D, cs, tid);
+  if (tid < C) {  // per-cluster metadata
+    S.mn[tid] = mn;
+    S.mo[tid] = mo;
+    S.mb[tid] = mo1 - mo;
+    S.ma[tid] = ma;
+  }
+  if (tid < D) S.qbar[tid] = qs;
   if (tid < 256) S.hist[tid] = 0;
   if (tid == 0) S.ncand = 0;
   __syncthreads();
   unsigned long long key = 0;
   int id = C + tid;  // padding entries: worst key, distinct ids past the clusters
   double sc = 0.0;
+  if (tid < C) sc = centroid_chain(S.qbar, crow);
   if (tid < C) {
-    sc = centroid_score(S.qbar, X.cent_t + (size_t)h * cs * D, cs, tid);
     key = ordered_key(sc);
     id = tid;
   }
@@ -529,26 +560,38 @@ __device__ __forceinline__ int select_count(const SelShared& S, const IndexView&
   return n < B ? n : B;
 }
 
-// The selection's scores of every cluster in use (for tests): one block per
-// KV head, the same query sum and chains as select_phase.
+// The selection's scores of the clusters in use, spread over the whole chip:
+// block (y, h) scores clusters 64 y .. 64 y + 63 of KV head h with the same
+// query sum and chains as select_phase, into scores[h * stride + k]. The fused
+// decode reads them (so its blocks do not each stream the head's centroids),
+// and the debug export returns them.
+constexpr int SCORE_THREADS = 64;
 template <typename QT>
-__global__ __launch_bounds__(SEL_THREADS) void debug_scores_kernel(const QT* __restrict__ q, int G, const IndexView X,
-                                                                   double* __restrict__ scores) {
+__global__ __launch_bounds__(SCORE_THREADS) void scores_kernel(const QT* __restrict__ q, int G, const IndexView X,
+                                                               double* __restrict__ scores, int stride) {
   __shared__ double qbar[D];
   const int h = blockIdx.x, tid = threadIdx.x;
-  if (tid < D) qbar[tid] = query_sum(q, G, h, tid);
+  const int k = blockIdx.y * SCORE_THREADS + tid;
+  CentroidRow crow;
+  if (k < X.ca) centroid_load(crow, X.cent_t + (size_t)h * X.cs * D, X.cs, k);
+  for (int j = tid; j < D; j += SCORE_THREADS) qbar[j] = query_sum(q, G, h, j);
   __syncthreads();
-  for (int k = tid; k < X.ca; k += SEL_THREADS)
-    scores[(size_t)h * X.ca + k] = centroid_score(qbar, X.cent_t + (size_t)h * X.cs * D, X.cs, k);
+  if (k < X.ca) scores[(size_t)h * stride + k] = centroid_chain(qbar, crow);
+}
+
+hipError_t launch_scores(int dtype, const void* q, int G, const IndexView& x, int heads, double* scores, int stride,
+                         hipStream_t st) {
+  const dim3 grid(heads, (x.ca + SCORE_THREADS - 1) / SCORE_THREADS);
+  if (dtype == DT_BF16)
+    scores_kernel<uint16_t><<<grid, SCORE_THREADS, 0, st>>>((const uint16_t*)q, G, x, scores, stride);
+  else
+    scores_kernel<float><<<grid, SCORE_THREADS, 0, st>>>((const float*)q, G, x, scores, stride);
+  return hipGetLastError();
 }
 
 hipError_t launch_debug_scores(int dtype, const void* q, int G, const IndexView& x, int heads, double* scores,
                                hipStream_t st) {
-  if (dtype == DT_BF16)
-    debug_scores_kernel<uint16_t><<<heads, SEL_THREADS, 0, st>>>((const uint16_t*)q, G, x, scores);
-  else
-    debug_scores_kernel<float><<<heads, SEL_THREADS, 0, st>>>((const float*)q, G, x, scores);
-  return hipGetLastError();
+  return launch_scores(dtype, q, G, x, heads, scores, x.ca, st);
 }
 
 template <typename QT>
@@ -952,18 +995,20 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
 // blocks of a head get block indices 8 apart, so the round-robin dispatch
 // over the 8 XCDs places them on one XCD and its L2 serves the repeated reads
 // of the keys and centroids; results do not depend on the placement.
-template <int G, int P, bool TS>
+template <int G, int P, bool TS, int NT = 4>
 __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     const uint16_t* __restrict__ q, const IndexView X, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, int packed,
     int heads, int B, float qscale, float* __restrict__ out, int32_t* __restrict__ sel_ids,
-    int32_t* __restrict__ sel_count, float* __restrict__ part_out) {
+    int32_t* __restrict__ sel_count, float* __restrict__ part_out, int32_t* __restrict__ arrive) {
   static_assert(G <= 8, "at most 8 query heads per KV head");
   constexpr int NW = SEL_THREADS / WAVE;
   constexpr int EMIT = 2048;                 // selected ids staged per pass
   constexpr int HC = TS ? D : D / P;         // value channels per block
   constexpr int RPS = WAVE / (HC / 8);       // value rows per load instruction (8 with 64 channels)
-  constexpr int VR = 64 / RPS;               // value rows per lane per slice
+  constexpr int ST = 16 * NT;                // tokens per slice (NT tiles of 16 rows)
+  static_assert(TS || NT == 4, "slices of 64 tokens without the token split");
+  constexpr int VR = ST / RPS;               // value rows per lane per slice
   __shared__ SelShared S;
   __shared__ int sel[EMIT];
   constexpr int GP = G < 4 ? 4 : G;          // floats per token in pw (16-byte rows)
@@ -1016,12 +1061,12 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     for (int c = 0; c < 8; ++c) o[g][c] = 0.f;
   }
 
-  // one slice: the n64 (<= 64) entries staged at ss, gathered, scored and
+  // one slice: the n64 (<= ST) entries staged at ss, gathered, scored and
   // folded into the wave's running state
   auto do_slice = [&](const int* ss, int n64) {
-    bf16x8 ka[4][4];
+    bf16x8 ka[NT][4];
 #pragma unroll
-    for (int T = 0; T < 4; ++T) {
+    for (int T = 0; T < NT; ++T) {
       const int t = T * 16 + j16;
       const int id = t < n64 ? ss[t] : 0;
       const uint16_t* src = sel_row(Kph, Kh, id);
@@ -1036,15 +1081,15 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
       const int id = t < n64 ? ss[t] : 0;
       vrow[r].load(sel_row(Vph, Vh, id));
     }
-    f32x4 acc[4] = {};
+    f32x4 acc[NT] = {};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[T][s], qb[s], acc[T], 0, 0, 0);
+      for (int T = 0; T < NT; ++T) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[T][s], qb[s], acc[T], 0, 0, 0);
     // score of (row 16 T + 4 (lane / 16) + r, query head lane % 16) -> pw[w][row][g]
     if (j16 < G) {
 #pragma unroll
-      for (int T = 0; T < 4; ++T)
+      for (int T = 0; T < NT; ++T)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = T * 16 + 4 * kb4 + r;
@@ -1063,7 +1108,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
       for (int g4 = 0; g4 < GP; g4 += 4) {
         const f32x4 x = *reinterpret_cast<const f32x4*>(&pw[w][lane][g4]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[g4 + i] = x[i];
+        for (int i = 0; i < 4; ++i) sv[g4 + i] = lane < ST ? x[i] : -INFINITY;  // lanes past the slice: no token
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -1131,8 +1176,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
   } else {
     // slices part, part + P, ...: wave w takes the block's slices w, w + 8, ...
     // and stages each one's entries in its own 64 words of sel
-    for (int sl = part + P * w; sl * 64 < cnt; sl += P * NW) {
-      const int t0 = sl * 64, n64 = cnt - t0 < 64 ? cnt - t0 : 64;
+    for (int sl = part + P * w; sl * ST < cnt; sl += P * NW) {
+      const int t0 = sl * ST, n64 = cnt - t0 < ST ? cnt - t0 : ST;
       if (lane < n64) {
         const int ent = select_emit(S, t0 + lane, ids_h, app_h, packed, X);
         sel[w * 64 + lane] = ent;
@@ -1188,14 +1233,58 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
       }
     }
     if constexpr (TS) {
+      // device-coherent stores (written through this XCD's L2), read below by
+      // whichever block of the head merges
       float* pd = part_out + (((size_t)h * P + part) * G + g) * (D + 2);
-      pd[j] = O;
+      __hip_atomic_store(pd + j, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (j == 0) {
-        pd[D] = M;
-        pd[D + 1] = L;
+        __hip_atomic_store(pd + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(pd + D + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     } else {
       out[((size_t)h * G + g) * D + HC * part + j] = L > 0.f ? O / L : 0.f;
+    }
+  }
+  if constexpr (TS) {
+    // The last of the head's P blocks to arrive merges the P partial results
+    // in block order. Each block's partial results were stored device-coherent
+    // (above); every thread waits for its stores to complete before the block
+    // arrives, and the merging block reads them device-coherent after it has
+    // seen the other P - 1 arrivals. No cache-wide write-back or invalidate is
+    // involved (both cost tens of microseconds per launch here). The merging
+    // block resets the counter for the next call.
+    __shared__ int last;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are complete
+    __syncthreads();
+    if (tid == 0) last = __hip_atomic_fetch_add(arrive + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == P - 1;
+    __syncthreads();
+    if (last) {
+      const float* ph = part_out + (size_t)h * P * G * (D + 2);
+      auto ld = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+      for (int e = tid; e < G * D; e += SEL_THREADS) {
+        const int g = e / D, j = e % D;
+        float mp[P], lp[P], op[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const float* pp = ph + (p * G + g) * (D + 2);
+          mp[p] = ld(pp + D);
+          lp[p] = ld(pp + D + 1);
+          op[p] = ld(pp + j);
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < P; ++p) M = fmaxf(M, mp[p]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const float f = mp[p] == -INFINITY ? 0.f : exp2f(mp[p] - M);
+          L = fmaf(f, lp[p], L);
+          O = fmaf(f, op[p], O);
+        }
+        out[((size_t)h * G + g) * D + j] = L > 0.f ? O / L : 0.f;
+      }
+      if (tid == 0) arrive[h] = 0;
     }
   }
 }
@@ -1657,8 +1746,11 @@ struct FusedArgs {
   float qscale;
   float* out;
   int32_t *sel_ids, *sel_count;
-  float* part;  // partial results of the token split, or null
+  float* part;      // partial results of the token split, or null
+  int32_t* arrive;  // [heads] arrival counters of the token split (zero between calls)
 };
+
+int fused_slice_tiles(int B, int P);
 
 template <typename KT, int G>
 static void launch_fused(const FusedArgs& a, hipStream_t st) {
@@ -1668,13 +1760,22 @@ static void launch_fused(const FusedArgs& a, hipStream_t st) {
     const int nb = (a.heads + 7) / 8 * 8 * P;
 #define KVC_FUSED_ARGS                                                                                          \
   (const uint16_t*)a.q, a.x, (const uint16_t*)a.kc, (const uint16_t*)a.vc, (const uint16_t*)a.kp,             \
-      (const uint16_t*)a.vp, a.packed, a.heads, a.B, a.qscale, a.out, a.sel_ids, a.sel_count, a.part
+      (const uint16_t*)a.vp, a.packed, a.heads, a.B, a.qscale, a.out, a.sel_ids, a.sel_count, a.part, a.arrive
     if constexpr (G <= 4) {
-      if (a.part) {  // token split, then the merge of the P partial results
-        if (P == 2) select_decode_bf16_kernel<G, 2, true><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
-        else if (P == 4) select_decode_bf16_kernel<G, 4, true><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
-        else select_decode_bf16_kernel<G, 8, true><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);
-        decode_combine_kernel<<<a.heads, 256, 0, st>>>(a.part, P, G, a.out);
+      if (a.part) {  // token split; the last block of each head merges
+        // slices of 64, 32 or 16 tokens: the longest that still gives each of
+        // a block's 8 waves one slice (short budgets take 16)
+        const int nt = fused_slice_tiles(a.B, P);
+#define KVC_TS_LAUNCH(PP)                                                                                       \
+  {                                                                                                               \
+    if (nt == 4) select_decode_bf16_kernel<G, PP, true, 4><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);            \
+    else if (nt == 2) select_decode_bf16_kernel<G, PP, true, 2><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);       \
+    else select_decode_bf16_kernel<G, PP, true, 1><<<nb, SEL_THREADS, 0, st>>>(KVC_FUSED_ARGS);                    \
+  }
+        if (P == 2) KVC_TS_LAUNCH(2)
+        else if (P == 4) KVC_TS_LAUNCH(4)
+        else KVC_TS_LAUNCH(8)
+#undef KVC_TS_LAUNCH
         return;
       }
     }
@@ -1705,11 +1806,21 @@ static hipError_t fused_dispatch(int G, const FusedArgs& a, hipStream_t st) {
 // 256 compute units.
 int fused_blocks_per_head(int heads) { return heads >= 128 ? 2 : (heads >= 64 ? 4 : 8); }
 
+// 16-row tiles per slice of the token split: 4 (64 tokens) while the budget's
+// 64-token slices give each of the P blocks at least 8 (one per wave), then 2
+// and 1.
+int fused_slice_tiles(int B, int P) {
+  if ((B + 63) / 64 >= 8 * P) return 4;
+  if ((B + 31) / 32 >= 8 * P) return 2;
+  return 1;
+}
+
 hipError_t launch_select_decode(int dtype, const void* q, int G, const IndexView& x, int heads, const void* kc,
                                 const void* vc, const void* kp, const void* vp, int B, float scale, float* out,
-                                int32_t* sel_ids, int32_t* sel_count, float* part, hipStream_t st) {
+                                int32_t* sel_ids, int32_t* sel_count, float* part, int32_t* arrive,
+                                hipStream_t st) {
   FusedArgs a{q, x, heads, kc, vc, kp ? kp : kc, vp ? vp : vc, kp && vp ? 1 : 0, B, scale * 1.4426950408889634f,
-              out, sel_ids, sel_count, part};
+              out, sel_ids, sel_count, part, arrive};
   if (dtype == DT_BF16) return fused_dispatch<uint16_t>(G, a, st);
   return fused_dispatch<float>(G, a, st);
 }

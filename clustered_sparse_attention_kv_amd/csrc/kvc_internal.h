@@ -9,6 +9,7 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 // assignment distance: the cosine (the method's), L2, inner product
 enum { M_COSINE = 0, M_L2 = 1, M_IP = 2 };
 
+constexpr int MAX_C = 512;       // largest cluster count (slots) per head
 constexpr int DEC_TOK = 64;      // selected tokens per decode block (split)
 constexpr int DEC_MAX_PAIRS = 512;  // splits x query heads one merge block holds
 
@@ -78,7 +79,11 @@ hipError_t launch_decode(int dtype, const void* q, int G, const void* kc, const 
                          float* part, hipStream_t st);
 hipError_t launch_select_decode(int dtype, const void* q, int G, const IndexView& x, int heads, const void* kc,
                                 const void* vc, const void* kp, const void* vp, int B, float scale, float* out,
-                                int32_t* sel_ids, int32_t* sel_count, float* part, hipStream_t st);
+                                int32_t* sel_ids, int32_t* sel_count, float* part, int32_t* arrive,
+                                hipStream_t st);
+// The selection's scores of the clusters in use: scores[h * stride + k].
+hipError_t launch_scores(int dtype, const void* q, int G, const IndexView& x, int heads, double* scores, int stride,
+                         hipStream_t st);
 int fused_blocks_per_head(int heads);
 // kp, vp: the packed copies (both non-null) or null (rows from the caches).
 // The cluster cache's step: selection, then the selected rows assembled into

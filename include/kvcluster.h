@@ -366,12 +366,16 @@ kvc_status kv_cluster_pack(kvc_index* idx, const void* k_cache, const void* v_ca
  * copies of the selection. Requires G = q_heads / heads in {1, 2, 4, 8}.
  * ws is optional. Without it, every block of a head scores all the selected
  * keys and weights a share of the value channels. With it (at least
- * kv_cluster_select_decode_workspace_bytes(heads, q_heads, d) bytes, contents
- * need not be initialised; bf16 and G <= 4 only, otherwise unused), the
- * blocks of a head split the selected tokens instead, write partial results
- * (running maximum, sum and output) to ws, and a second kernel merges them:
- * the same attention up to fp32 summation order. ws_bytes is ignored when ws
- * is NULL; a smaller ws gives KVC_ERR_WORKSPACE.
+ * kv_cluster_select_decode_workspace_bytes(heads, q_heads, d) bytes; bf16 and
+ * G <= 4 only, otherwise unused), the blocks of a head split the selected
+ * tokens instead and write partial results (running maximum, sum and output);
+ * the last block of each head to finish merges them: the same attention up
+ * to fp32 summation order. The workspace starts with one arrival counter per
+ * KV head (int32, the first 4 * heads bytes rounded up to 256), which must be
+ * zero before the first call on that workspace; every call leaves them zero
+ * (the rest need not be initialised). Calls that share a workspace must not
+ * overlap. ws_bytes is ignored when ws is
+ * NULL; a smaller ws gives KVC_ERR_WORKSPACE.
  */
 size_t kv_cluster_select_decode_workspace_bytes(int heads, int q_heads, int d);
 kvc_status kv_cluster_select_decode(const kvc_index* idx, const void* q, int q_heads, const void* k_cache,

@@ -50,8 +50,10 @@ def queries(w, base, step: int, K: np.ndarray, n_cur: int, means, heads: int | N
 
 
 def split_ws(idx, q_heads: int) -> torch.Tensor:
-    """Workspace for the token split of the fused selection and attention, filled with NaN bytes (its
-    contents must not matter)."""
+    """Workspace for the token split of the fused selection and attention: the per-head arrival
+    counters zero, the partial results filled with NaN bytes (their contents must not matter)."""
     import clustered_sparse_attention_kv_amd as kvc
-    return torch.full((kvc.select_decode_workspace_bytes(idx.heads, q_heads, idx.d),), 0xFF, dtype=torch.uint8,
-                      device="cuda")
+    ws = torch.full((kvc.select_decode_workspace_bytes(idx.heads, q_heads, idx.d),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    ws[:(4 * idx.heads + 255) // 256 * 256] = 0
+    return ws
