@@ -10,8 +10,9 @@ clusters for every KV head and runs sparse attention over the recalled tokens
 Inputs are generated on the host with the seeded generator and copied to HBM
 before timing starts. The timed region holds exactly --steps passes between
 two synchronisations. Kernel durations come from HIP events recorded on the
-stream the kernels run on. The CPU oracle is timed on a bounded sample of
-the same workload as a reported baseline.
+stream the kernels run on. The CPU oracle is timed over the same workload as
+a reported baseline. After the headline workload 4, a cold-stack record runs
+the decode of workload 5's 32 layers, whose K/V no cache holds.
 
 Prints one JSON line.
 """
@@ -142,8 +143,11 @@ def main():
                          "captured once in a HIP graph and replayed; the same kernels and work)")
     ap.add_argument("--no-pack", action="store_true",
                     help="decode from the caches through the token ids (no cluster-ordered copy)")
-    ap.add_argument("--cpu-heads", type=int, default=16, help="KV heads in the CPU baseline sample")
-    ap.add_argument("--cpu-steps", type=int, default=32, help="decode steps in the CPU baseline sample")
+    ap.add_argument("--no-cold-stack", action="store_true",
+                    help="workload 4: skip the cold-stack record (workload 5's 32 layers, whose 34 GB of K/V "
+                         "no cache holds, decoded after the headline measurement)")
+    ap.add_argument("--cold-steps", type=int, default=2, help="timed passes of the cold-stack record")
+    ap.add_argument("--no-full-kv", action="store_true", help="skip the full-KV comparator")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -151,7 +155,6 @@ def main():
               "by KV head, with no exchange between them). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import clustered_sparse_attention_kv_amd as kvc
@@ -161,8 +164,39 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     kvc.lib()  # fails loudly without the built library
+    result = measure(synth.workload(args.workload), args)
+    if args.workload == 4 and not args.no_cold_stack:
+        # the same path over the 32-layer stack of workload 5: every decode step
+        # streams 1.5 GB of centroids and K/V rows, far past the 256 MB
+        # Infinity Cache, so its rate is the DRAM-bound one
+        torch.cuda.empty_cache()
+        log("[bench] cold stack: workload 5 (32 layers)")
+        cold = argparse.Namespace(**vars(args))
+        cold.workload, cold.steps, cold.warmup = 5, args.cold_steps, 1
+        cold.no_cpu, cold.no_full_kv = True, True
+        w5 = synth.workload(5)
+        r5 = measure(w5, cold)
+        sd = r5["rooflines"].get("select_decode", {})
+        result["cold_stack"] = {
+            "workload": w5.name, "layers": w5.layers, "kv_heads_per_layer": w5.heads, "B": w5.B,
+            "decode_steps_per_s": r5["value"], "step_us": r5["decode_step_us"],
+            "us_per_layer": r5["decode_step_us"] / w5.layers,
+            "hbm_frac": r5["decode_step_hbm_frac"], "kernel": sd.get("kernel"),
+            "bytes_per_step": algorithmic(w5)["step_bytes"] * w5.layers,
+            "kmeans_tflops": r5["kmeans_tflops"], "kmeans_ms_per_layer": r5["kmeans_ms"] / w5.layers,
+            "steps": cold.steps, "warmup": cold.warmup, "decode_launch": r5["decode_launch"]}
+    print(json.dumps(result), flush=True)
+
+
+def measure(w, args):
+    """One workload through the whole path: returns the bench record (without printing it)."""
+    import numpy as np
+    import torch
+
+    import clustered_sparse_attention_kv_amd as kvc
+    import synth
+
     dev = torch.device("cuda:0")
-    w = synth.workload(args.workload)
     NL = w.layers
     H, G, L, d, C, B, cap = w.heads, w.G, w.L, w.d, w.C, w.B, w.capacity
     tdt = torch.bfloat16 if w.dtype == synth.BF16 else torch.float32
@@ -494,7 +528,7 @@ def main():
         result["clusters_after_pass"] = C + n_windows * NC
 
     # ---------------- full-KV comparator (dense decode over all L rows) -----
-    if w.dtype == synth.BF16:
+    if w.dtype == synth.BF16 and not args.no_full_kv:
         e0 = lay[0]
         ws_dense = torch.empty(kvc.dense_decode_workspace_bytes(H, H * G, L), dtype=torch.uint8, device=dev)
         for i in range(3):
@@ -518,6 +552,7 @@ def main():
 
     # ---------------- CPU oracle baseline (bounded sample) -----------------
     if not args.no_cpu:
+        log("[bench] CPU oracle over the workload")
         result["cpu_baseline"] = cpu_baseline(w, args, base0, Q0)
         # selection quality: oracle recall of the exact top-B attention tokens
         # by the GPU's selections of the first decode steps, layer 0, sampled
@@ -530,42 +565,49 @@ def main():
             torch.cuda.synchronize()
             sels.append((s_, sel.cpu().numpy(), cnt.cpu().numpy()))
         result["selection_recall"] = recall_sample(w, args, base0, Q0, sels)
-    print(json.dumps(result), flush=True)
+    return result
 
 
 def cpu_baseline(w, args, base, Q):
-    """The oracle as it stands on the host cores: select + decode of a sample
-    of KV heads over a few decode steps, scaled to the whole workload's heads."""
+    """The oracle as it stands, on the host cores, over the whole workload: the
+    k-means of every KV head (all iterations), then every decode step (append
+    for the append workloads, selection and attention of every head). A stack
+    of layers runs its first layer and is scaled to all of them."""
     import numpy as np
 
     import oracle
     import synth
 
-    nh = min(args.cpu_heads, w.heads)
-    ns = min(args.cpu_steps, w.steps)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-    # the sample's inputs: the first nh KV heads of the same workload
-    K, _, _ = synth.mixture_keys(base, nh, w.L, w.d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype)
-    V = synth.values(base, nh, w.L, w.d, w.dtype)
-    t0 = time.perf_counter()
+    rows = w.capacity
+    K, _, _ = synth.mixture_keys(base, w.heads, rows, w.d, w.M, w.sigma, w.n_out, w.out_scale, w.dtype)
+    V = synth.values(base, w.heads, rows, w.d, w.dtype)
     metric = {"cosine": oracle.COSINE, "l2": oracle.L2, "inner_product": oracle.IP}[args.metric]
-    built = oracle.build(K, w.C, 1, seed=base, early_exit=False,  # one k-means iteration of the sample
-                         n_sink=args.sinks, metric=metric)
-    t_iter = time.perf_counter() - t0
-    scale = 1.0 / math.sqrt(w.d)
     t0 = time.perf_counter()
-    for s in range(ns):
-        q = np.ascontiguousarray(Q[s, :nh * w.G])
-        sel, cnt, _, _ = oracle.select(q, w.G, built["c"], built["sizes"], built["offsets"], built["token_ids"], w.B,
-                                       n_sink=args.sinks)
+    built = oracle.build(np.ascontiguousarray(K[:, :w.L]), w.C, w.iters, seed=base, early_exit=False,
+                         n_sink=args.sinks, metric=metric)
+    t_km = time.perf_counter() - t0
+    scale = 1.0 / math.sqrt(w.d)
+    index = oracle.Index(built, rows, metric=metric) if w.append else None
+    t0 = time.perf_counter()
+    for s in range(w.steps):
+        q = np.ascontiguousarray(Q[s])
+        if index is not None:
+            index.append(np.ascontiguousarray(K[:, w.L + s]))
+            c, sz, off, ids = index.c, index.sizes, index.offsets, index.token_ids
+        else:
+            c, sz, off, ids = built["c"], built["sizes"], built["offsets"], built["token_ids"]
+        sel, cnt, _, _ = oracle.select(q, w.G, c, sz, off, ids, w.B, n_sink=args.sinks)
         oracle.decode(q, w.G, K, V, sel, cnt, scale)
-    t_dec = (time.perf_counter() - t0) / ns
-    per_step_full = t_dec * w.heads * w.layers / nh
-    flops_iter = 2.0 * nh * w.L * w.C * w.d
-    return {"value": 1.0 / per_step_full, "unit": "decode steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{nh} of {w.heads * w.layers} KV heads (layer 0) x {ns} decode steps (select + decode), "
-                      f"scaled x{w.heads * w.layers / nh:.0f}; plus one k-means iteration of the {nh} heads",
-            "kmeans_gflops": flops_iter / t_iter / 1e9}
+    t_dec = time.perf_counter() - t0
+    per_step = t_dec / w.steps * w.layers
+    flops = 2.0 * w.iters * w.heads * w.L * w.C * w.d
+    sample = (f"the whole workload: k-means of all {w.heads} KV heads ({w.iters} iterations, no early exit) and all "
+              f"{w.steps} decode steps ({'append, ' if w.append else ''}selection and attention of every head)")
+    if w.layers > 1:
+        sample = f"layer 0 of {w.layers} ({sample[len('the whole workload: '):]}), decode time scaled x{w.layers}"
+    return {"value": 1.0 / per_step, "unit": "decode steps/s", "cores": threads, "kind": "oracle", "sample": sample,
+            "kmeans_s": t_km, "kmeans_gflops": flops / t_km / 1e9, "decode_s": t_dec}
 
 
 def recall_sample(w, args, base, Q, sels):

@@ -310,9 +310,11 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
   // thread's centroid row (32 chunks at once). Loads complete in order, so the
   // LDS stores of the query sum and the metadata wait for their own loads
   // only, and the centroid rows arrive while the block meets at the barrier.
-  // (Every block of a head streams the head's whole centroids: sharing the
-  // scores between a head's blocks through device memory costs several
-  // device-coherent round trips, more than the reads it saves.)
+  // (Every block of a head streams the head's whole centroids and runs every
+  // chain: sharing the scores between a head's blocks through device memory
+  // costs several device-coherent round trips, more than the reads it saves,
+  // and streaming the block's own share first with the rest after a barrier,
+  // to find the rest in L2, serialises the fp64 chains and is slower too.)
   double qs = 0.0;
   if (tid < D) qs = query_sum(q, G, h, tid);
   int mn = 0, mo = 0, mo1 = 0, ma = 0;
