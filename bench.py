@@ -79,7 +79,7 @@ class HipEvents:
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for name in ("kvc_build.hip", "kvc_decode.hip", "kvc_device.h"):
+    for name in ("kvc_build.hip", "kvc_decode.hip", "kvc_device.h", "kvc_host.cpp"):
         with open(os.path.join(ROOT, "clustered_sparse_attention_kv_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -6,7 +6,7 @@ import subprocess
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(_HERE)
-SOURCES = ["kvc_build.hip", "kvc_decode.hip", "kvc_api.cpp"]
+SOURCES = ["kvc_build.hip", "kvc_decode.hip", "kvc_api.cpp", "kvc_host.cpp"]
 OUT = os.path.join(_HERE, "libkvcluster.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

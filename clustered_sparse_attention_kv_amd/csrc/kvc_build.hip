@@ -670,7 +670,7 @@ __global__ __launch_bounds__(64) void assign_exact_kernel(const KT* __restrict__
 // the last lane of each label in a chunk advances the wave's running position.
 // Position = offset + block base + wave base + earlier chunks + rank keeps
 // token order.
-constexpr int CS_BLOCK = 4096;
+constexpr int CS_BLOCK = CSR_BLOCK_TOKENS;
 constexpr int CS_THREADS = 1024;
 
 __global__ __launch_bounds__(256) void csr_count_kernel(const int32_t* __restrict__ labels, long long label_stride,
@@ -876,7 +876,7 @@ __global__ __launch_bounds__(256) void update_kernel(const KT* __restrict__ keys
 // build. The member lists are written once, after the last iteration. The
 // outputs are the arrays the window merge reads: centroids (both layouts),
 // operand rows (padding rows zeroed), labels, sizes, offsets and ids.
-constexpr int WK_MAXC = 32;
+constexpr int WK_MAXC = WINDOW_KMEANS_MAX_C;
 template <typename KT>
 __global__ __launch_bounds__(256) void window_kmeans_kernel(
     const KT* __restrict__ keys, long long head_stride, int wlo, int n_tokens, int m, int nc, int cpw, int iters,
@@ -1052,7 +1052,7 @@ hipError_t launch_window_kmeans(int dtype, const void* keys, long long head_stri
                                 int m, int nc, int cpw, int iters, const int32_t* init_idx, int metric, float* cent,
                                 float* cent_t, void* chat, int32_t* labels, int32_t* sizes, int32_t* offsets,
                                 int32_t* ids, int32_t* flags, hipStream_t st) {
-  if (nc > WK_MAXC || (size_t)m * sizeof(int) > 64 * 1024) return hipErrorInvalidValue;
+  if (!window_kmeans_fits(m, nc)) return hipErrorInvalidValue;
   const size_t lds = (size_t)m * sizeof(int);
   if (dtype == DT_BF16)
     window_kmeans_kernel<uint16_t><<<heads, 256, lds, st>>>((const uint16_t*)keys, head_stride, wlo, n_tokens, m, nc,
@@ -1065,7 +1065,6 @@ hipError_t launch_window_kmeans(int dtype, const void* keys, long long head_stri
   return hipGetLastError();
 }
 
-bool window_kmeans_fits(int m, int nc) { return nc <= WK_MAXC && (size_t)m * sizeof(int) <= 64 * 1024; }
 
 // ---------------------------------------------------------------------------
 // Clustering of generated tokens (III.B: the tokens generated since the last
@@ -1295,7 +1294,5 @@ hipError_t launch_merge_window(int dtype, int heads, int nc, int m, int wlo, con
                                                       offsets, token_ids, labels, cap);
   return hipGetLastError();
 }
-
-int csr_blocks(int L) { return (L + CS_BLOCK - 1) / CS_BLOCK; }
 
 }  // namespace kvc

@@ -1737,8 +1737,6 @@ hipError_t launch_cache_assemble(int dtype, const void* q, int G, const IndexVie
   return hipGetLastError();
 }
 
-int fused_blocks_per_head(int heads);
-
 struct FusedArgs {
   const void* q;
   IndexView x;
@@ -1751,8 +1749,6 @@ struct FusedArgs {
   float* part;      // partial results of the token split, or null
   int32_t* arrive;  // [heads] arrival counters of the token split (zero between calls)
 };
-
-int fused_slice_tiles(int B, int P);
 
 template <typename KT, int G>
 static void launch_fused(const FusedArgs& a, hipStream_t st) {
@@ -1806,16 +1802,6 @@ static hipError_t fused_dispatch(int G, const FusedArgs& a, hipStream_t st) {
 
 // Blocks per KV head of the fused kernel: enough that the grid covers the
 // 256 compute units.
-int fused_blocks_per_head(int heads) { return heads >= 128 ? 2 : (heads >= 64 ? 4 : 8); }
-
-// 16-row tiles per slice of the token split: 4 (64 tokens) while the budget's
-// 64-token slices give each of the P blocks at least 8 (one per wave), then 2
-// and 1.
-int fused_slice_tiles(int B, int P) {
-  if ((B + 63) / 64 >= 8 * P) return 4;
-  if ((B + 31) / 32 >= 8 * P) return 2;
-  return 1;
-}
 
 hipError_t launch_select_decode(int dtype, const void* q, int G, const IndexView& x, int heads, const void* kc,
                                 const void* vc, const void* kp, const void* vp, int B, float scale, float* out,
@@ -1894,17 +1880,6 @@ hipError_t launch_export_csr(int heads, int ca, int cs, const int32_t* offsets, 
   return hipGetLastError();
 }
 
-// Split of the dense pass: 64-token multiples, at most DEC_MAX_PAIRS / G splits.
-void dense_split(int n, int G, int* nsplit, int* T) {
-  int ns = (n + 511) / 512;
-  const int cap = DEC_MAX_PAIRS / G;
-  if (ns > cap) ns = cap;
-  if (ns < 1) ns = 1;
-  int t = (n + ns - 1) / ns;
-  t = (t + 63) / 64 * 64;
-  *T = t;
-  *nsplit = (n + t - 1) / t;
-}
 
 hipError_t launch_dense_decode(const void* q, int G, const void* kc, const void* vc, long long cap, int heads, int n,
                                float scale, float* out, float* part, hipStream_t st) {

@@ -13,7 +13,17 @@ constexpr int MAX_C = 512;       // largest cluster count (slots) per head
 constexpr int DEC_TOK = 64;      // selected tokens per decode block (split)
 constexpr int DEC_MAX_PAIRS = 512;  // splits x query heads one merge block holds
 
+// Host-side sizing shared by the launchers and the workspace arithmetic of the
+// C ABI (kvc_host.cpp).
+constexpr int CSR_BLOCK_TOKENS = 4096;  // tokens per block of the counting sort
 int csr_blocks(int L);
+// Blocks per KV head of the fused selection and attention: enough that the
+// grid covers the 256 compute units.
+int fused_blocks_per_head(int heads);
+// 16-row tiles per slice of the token split (4, 2 or 1).
+int fused_slice_tiles(int B, int P);
+// Split of the dense pass over n rows: nsplit blocks of T rows.
+void dense_split(int n, int G, int* nsplit, int* T);
 
 // Bytes of the fixed device scratch of kv_sparse_decode_noalloc.
 constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)16 << 20;
@@ -52,7 +62,9 @@ hipError_t launch_update(int dtype, const void* keys, long long head_stride, int
 // Moves the window's clustering (nc clusters of the m tokens wlo .. wlo+m-1,
 // in arrays of stride nc / cpad(nc) / m per head) into the index as clusters
 // ca .. ca+nc-1.
-// The window's whole k-means in one launch (small windows: see window_kmeans_fits).
+// The window's whole k-means in one launch, for windows whose labels fit the
+// kernel's LDS (at most 16384 tokens) and at most WINDOW_KMEANS_MAX_C clusters.
+constexpr int WINDOW_KMEANS_MAX_C = 32;
 bool window_kmeans_fits(int m, int nc);
 hipError_t launch_window_kmeans(int dtype, const void* keys, long long head_stride, int heads, int wlo, int n_tokens,
                                 int m, int nc, int cpw, int iters, const int32_t* init_idx, int metric, float* cent,
@@ -84,7 +96,6 @@ hipError_t launch_select_decode(int dtype, const void* q, int G, const IndexView
 // The selection's scores of the clusters in use: scores[h * stride + k].
 hipError_t launch_scores(int dtype, const void* q, int G, const IndexView& x, int heads, double* scores, int stride,
                          hipStream_t st);
-int fused_blocks_per_head(int heads);
 // kp, vp: the packed copies (both non-null) or null (rows from the caches).
 // The cluster cache's step: selection, then the selected rows assembled into
 // region t mod (R + 1) of ck / cv ([heads, (R + 1) * B, d]) from the cache or
@@ -93,7 +104,6 @@ hipError_t launch_cache_assemble(int dtype, const void* q, int G, const IndexVie
                                  const void* vc, const void* kp, const void* vp, int B, int R, int t, void* ck,
                                  void* cv, int32_t* table, long long* stats, int32_t* rows, int32_t* count,
                                  int32_t* sel_ids, int32_t* sel_count, hipStream_t st);
-void dense_split(int n, int G, int* nsplit, int* T);
 hipError_t launch_dense_decode(const void* q, int G, const void* kc, const void* vc, long long cap, int heads, int n,
                                float scale, float* out, float* part, hipStream_t st);
 // Rows i in [r0, r1) of the packed copies from the cache rows token_ids[h][i]:
