@@ -24,6 +24,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -78,10 +79,16 @@ class HipEvents:
 
 
 def source_digest() -> str:
+    """Digest of the kernel sources' code: comments and blank or indentation-only differences do not
+    change it, any change to a statement does."""
     h = hashlib.sha256()
-    for name in ("kvc_build.hip", "kvc_decode.hip", "kvc_device.h", "kvc_host.cpp"):
-        with open(os.path.join(ROOT, "clustered_sparse_attention_kv_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    for name in ("kvc_build.hip", "kvc_decode.hip", "kvc_device.h", "kvc_internal.h", "kvc_host.cpp"):
+        with open(os.path.join(ROOT, "clustered_sparse_attention_kv_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [" ".join(l.split()) for l in text.splitlines()]
+        h.update("\n".join(l for l in lines if l).encode())
     return h.hexdigest()[:16]
 
 

@@ -186,8 +186,8 @@ __global__ __launch_bounds__(256) void init_centroids_kernel(const KT* __restric
 // instruction reads 64 contiguous bytes of 16 key rows. D[centroid][key]
 // gives each lane 4 centroids (4 (l / 16) + r) of one key per tile.
 //
-// Block = 8 waves x 64 keys (4 tiles of 16 per wave); the grid holds about
-// one block per compute unit and each block walks over 512-key groups of one
+// Block = 12 waves x 64 keys (4 tiles of 16 per wave); the grid holds about
+// one block per compute unit and each block walks over 768-key groups of one
 // head, so the head's operand is staged in LDS once per block (row r's 16-byte
 // chunk c at c ^ (r & 15): the 16 rows one read instruction touches land in
 // distinct banks).
@@ -1207,7 +1207,7 @@ hipError_t launch_assign(int dtype, const void* keys, long long head_stride, int
   u32x4* ot = static_cast<u32x4*>(op_t);
   if (dtype == DT_BF16) {
     const size_t lds = (size_t)(cpad + 16) * D * 2 + 16;  // the operand, one zero tile and a flag
-    // about one block per compute unit; each walks over 512-key groups of one head
+    // about one block per compute unit; each walks over 768-key groups of one head
     const int ngroups = grid1(L, AS_TILE);
     int gx = (256 + heads - 1) / heads;
     gx = gx < 1 ? 1 : (gx > ngroups ? ngroups : gx);

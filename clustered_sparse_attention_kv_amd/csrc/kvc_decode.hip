@@ -991,9 +991,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_kernel(
 // either (TS false) all score all keys, and block `part` gathers and weights
 // channels [part D / P, (part + 1) D / P) of the values (8 channels per
 // lane), writing those output channels; or (TS true) block `part` takes the
-// 64-entry slices part, part + P, ... with all channels and writes its
-// partial result (running maximum, sum, unnormalised output per query head)
-// to part_out [heads, P, G, D + 2], which decode_combine_kernel merges. The
+// slices part, part + P, ... (16 NT entries each) with all channels and
+// writes its partial result (running maximum, sum, unnormalised output per
+// query head) to part_out [heads, P, G, D + 2], and the last of the head's
+// blocks to arrive merges the P partial results (below). The
 // blocks of a head get block indices 8 apart, so the round-robin dispatch
 // over the 8 XCDs places them on one XCD and its L2 serves the repeated reads
 // of the keys and centroids; results do not depend on the placement.
