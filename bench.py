@@ -470,7 +470,10 @@ def measure(w, args):
             traffic = rec.get("bytes_per_launch", {})
     for k, r in rl.items():
         r["frac"] = r["achieved"] / r["peak"]
-        r["traffic"] = traffic.get(kernel_names[k])
+        # the record is keyed by the kernel's symbol name (the first word of the display name); a
+        # phase of several kernels has none
+        name = kernel_names[k]
+        r["traffic"] = None if "+" in name else traffic.get(name.split()[0])
         r["kernel"] = kernel_names[k]
     dominant = max(rl, key=lambda k: rl[k]["share"])
     roofline = {k2: rl[dominant][k2] for k2 in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
