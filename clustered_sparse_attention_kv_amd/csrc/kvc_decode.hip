@@ -293,12 +293,6 @@ __device__ __forceinline__ double centroid_chain(const double* qbar, const Centr
     for (int i = 0; i < 4; ++i) sc = fma(qbar[4 * jj + i], (double)r.v[jj][i], sc);
   return sc;
 }
-__device__ __forceinline__ double centroid_score(const double* qbar, const float* __restrict__ cent_t_head, int cs,
-                                                 int k) {
-  CentroidRow r;
-  centroid_load(r, cent_t_head, cs, k);
-  return centroid_chain(qbar, r);
-}
 
 // Returns the cluster id of rank tid (ids >= X.ca are padding).
 template <typename QT>
