@@ -564,9 +564,10 @@ def measure(w, args):
     if not args.no_cpu:
         log("[bench] CPU oracle over the workload")
         result["cpu_baseline"] = cpu_baseline(w, args, base0, Q0)
-        # selection quality: oracle recall of the exact top-B attention tokens
-        # by the GPU's selections of the first decode steps, layer 0, sampled
-        # heads, on a fresh build of the prompt (no generated tokens)
+        # still the CPU leg, after the timed region: the oracle's exact top-B
+        # attention tokens against the GPU's selections of the first decode
+        # steps (layer 0, sampled heads, a fresh build of the prompt, no
+        # generated tokens), reported as the selection_recall diagnostic
         e0 = lay[0]
         kvc.build(e0["idx"], e0["Kd"], L, w.iters, seed=e0["seed"], workspace=ws_build)
         sels = []
