@@ -18,7 +18,8 @@
  * Conventions shared by every call:
  *  - Memory. Every pointer argument is DEVICE memory unless stated otherwise,
  *    owned by the caller. The library never allocates, frees or
- *    synchronises, and it keeps no device state between calls.
+ *    synchronises. Its one piece of device state is the fixed scratch
+ *    array of kv_sparse_decode_noalloc (below), which that call alone uses.
  *  - Streams. `stream` is a hipStream_t passed as void* (NULL is the null
  *    stream). Every call only enqueues work on it; results are valid once
  *    the stream has been synchronised.
