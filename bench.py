@@ -154,6 +154,9 @@ def main():
                     help="workload 4: skip the cold-stack record (workload 5's 32 layers, whose 34 GB of K/V "
                          "no cache holds, decoded after the headline measurement)")
     ap.add_argument("--cold-steps", type=int, default=2, help="timed passes of the cold-stack record")
+    ap.add_argument("--no-unpacked", action="store_true",
+                    help="workload 4: skip the unpacked record (the same decode reading the rows from the caches "
+                         "through the token ids, without the cluster-ordered copy)")
     ap.add_argument("--no-full-kv", action="store_true", help="skip the full-KV comparator")
     args = ap.parse_args()
 
@@ -172,6 +175,20 @@ def main():
         sys.exit(1)
     kvc.lib()  # fails loudly without the built library
     result = measure(synth.workload(args.workload), args)
+    if args.workload == 4 and not args.no_pack and not args.no_unpacked:
+        # the headline decodes from the cluster-ordered copy; the same workload
+        # without it reads every selected row from the caches through the ids
+        torch.cuda.empty_cache()
+        log("[bench] unpacked: workload 4 without the cluster-ordered copy")
+        up = argparse.Namespace(**vars(args))
+        up.no_pack, up.no_cpu, up.no_full_kv = True, True, True
+        up.steps, up.warmup = max(1, min(args.steps, 3)), 1
+        ru = measure(synth.workload(4), up)
+        sd = ru["rooflines"].get("select_decode", {})
+        result["unpacked"] = {
+            "decode_steps_per_s": ru["value"], "step_us": ru["decode_step_us"],
+            "hbm_frac": ru["decode_step_hbm_frac"], "kernel": sd.get("kernel"),
+            "steps": up.steps, "warmup": up.warmup, "decode_launch": ru["decode_launch"]}
     if args.workload == 4 and not args.no_cold_stack:
         # the same path over the 32-layer stack of workload 5: every decode step
         # streams 1.5 GB of centroids and K/V rows, far past the 256 MB
