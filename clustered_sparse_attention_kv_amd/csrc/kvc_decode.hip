@@ -1187,20 +1187,47 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     }
   }
   // merge: the row groups of each wave (lanes HC / 8 apart share channels), then the 8 waves
+  if constexpr (TS) {
+    // four row groups of 16 lanes (vgrp = lane / 16), each lane NV = 8 G
+    // values: a transposed reduction. Swapping the 32-lane halves of values i
+    // and i + NV / 2 and adding leaves value i summed over the halves in lanes
+    // 0-31 and value i + NV / 2 in lanes 32-63; swapping 16-lane rows of those
+    // sums pairwise (i, i + NV / 4) and adding leaves row r holding value
+    // i + r NV / 4, summed over all four row groups. Each lane then writes its
+    // NV / 4 values: lane operations only, no LDS round trip.
+    constexpr int NV = G * 8;
+    float r1[NV / 2];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float v = o[g][c];
-#pragma unroll
-      for (int m = HC / 8; m < WAVE; m <<= 1) v += __shfl_xor(v, m);
-      o[g][c] = v;
+    for (int i = 0; i < NV / 2; ++i) {
+      const int j = i + NV / 2;
+      const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[i >> 3][i & 7]),
+                                                      __float_as_uint(o[j >> 3][j & 7]), false, false);
+      r1[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
     }
-  if (vgrp == 0) {
+#pragma unroll
+    for (int i = 0; i < NV / 4; ++i) {
+      const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(r1[i]), __float_as_uint(r1[i + NV / 4]), false,
+                                                      false);
+      const float r2 = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+      const int v = i + vgrp * (NV / 4);
+      ored[w][v >> 3][8 * vgl + (v & 7)] = r2;
+    }
+  } else {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) ored[w][g][8 * vgl + c] = o[g][c];
+      for (int c = 0; c < 8; ++c) {
+        float v = o[g][c];
+#pragma unroll
+        for (int m = HC / 8; m < WAVE; m <<= 1) v += __shfl_xor(v, m);
+        o[g][c] = v;
+      }
+    if (vgrp == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) ored[w][g][8 * vgl + c] = o[g][c];
+    }
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) l_run[g] = wave_sum(l_run[g]);
