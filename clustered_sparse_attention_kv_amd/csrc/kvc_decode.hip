@@ -190,10 +190,12 @@ struct SelShared {
   int nrank;  // ranks that can hold clusters: 64 after the candidates' sort, else all
 };
 
-// Value of lane (lane ^ S) within the wave: DPP quad permutes for S = 1, 2;
-// for S = 4, 8 the partner lies in the same row of 16, S lanes up or down, so
-// two DPP row shifts and a select; ds_swizzle in bit mode (xor mask, within 32
-// lanes) for S = 16, and a crossbar permute for S = 32.
+// Value of lane (lane ^ S) within the wave, with lane operations only (no
+// LDS): DPP quad permutes for S = 1, 2; for S = 4, 8 the partner lies in the
+// same row of 16, S lanes up or down, so two DPP row shifts and a select; for
+// S = 16 and 32 a swap of 16-lane rows or 32-lane halves (v_permlane16_swap /
+// v_permlane32_swap of the value with itself gives the lower partner rows in
+// one result and the upper ones in the other) and a select.
 template <int S>
 __device__ __forceinline__ int lane_xor(int v) {
   if constexpr (S == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
@@ -202,8 +204,44 @@ __device__ __forceinline__ int lane_xor(int v) {
     const int up = __builtin_amdgcn_update_dpp(0, v, 0x100 + S, 0xF, 0xF, false);  // row_shl: lane + S
     const int dn = __builtin_amdgcn_update_dpp(0, v, 0x110 + S, 0xF, 0xF, false);  // row_shr: lane - S
     return (threadIdx.x & S) ? dn : up;
-  } else if constexpr (S < 32) return __builtin_amdgcn_ds_swizzle(v, (S << 10) | 0x1F);
-  else return __shfl_xor(v, S);
+  } else if constexpr (S == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((threadIdx.x & 16) ? p[0] : p[1]);
+  } else {
+    static_assert(S == 32, "lane distance");
+    const auto p = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((threadIdx.x & 32) ? p[0] : p[1]);
+  }
+}
+
+// fp64 minimum and maximum over the wave (every lane gets them): DPP steps on
+// both 32-bit halves, as wave_max below.
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ double dpp64(double v) {
+  const unsigned long long x = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, RM, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(x >> 32), (int)(x >> 32), CTRL, RM, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+__device__ __forceinline__ void wave_min_max(double& lo, double& hi) {
+  lo = fmin(lo, dpp64<0xB1>(lo));
+  hi = fmax(hi, dpp64<0xB1>(hi));
+  lo = fmin(lo, dpp64<0x4E>(lo));
+  hi = fmax(hi, dpp64<0x4E>(hi));
+  lo = fmin(lo, dpp64<0x141>(lo));
+  hi = fmax(hi, dpp64<0x141>(hi));
+  lo = fmin(lo, dpp64<0x140>(lo));
+  hi = fmax(hi, dpp64<0x140>(hi));
+  lo = fmin(lo, dpp64<0x142, 0xA>(lo));
+  hi = fmax(hi, dpp64<0x142, 0xA>(hi));
+  lo = fmin(lo, dpp64<0x143, 0xC>(lo));
+  hi = fmax(hi, dpp64<0x143, 0xC>(hi));
+  const unsigned long long l = (unsigned long long)__double_as_longlong(lo);
+  const unsigned long long u = (unsigned long long)__double_as_longlong(hi);
+  lo = __longlong_as_double((long long)(((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(l >> 32), 63) << 32) |
+                                        (unsigned)__builtin_amdgcn_readlane((int)l, 63)));
+  hi = __longlong_as_double((long long)(((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(u >> 32), 63) << 32) |
+                                        (unsigned)__builtin_amdgcn_readlane((int)u, 63)));
 }
 
 // Inclusive prefix sum over the 64 lanes: row shifts by 1, 2, 4, 8 (zero
@@ -341,11 +379,7 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
   // lowest and highest score of the head
   {
     double lo = tid < C ? sc : INFINITY, hi = tid < C ? sc : -INFINITY;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      lo = fmin(lo, __shfl_xor(lo, off));
-      hi = fmax(hi, __shfl_xor(hi, off));
-    }
+    wave_min_max(lo, hi);
     if (lane == 0) {
       S.wlo[w] = lo;
       S.whi[w] = hi;
