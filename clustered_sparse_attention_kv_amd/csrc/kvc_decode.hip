@@ -35,6 +35,7 @@ __global__ __launch_bounds__(APP_THREADS) void append_kernel(KT* __restrict__ kc
   __shared__ double kv[D];
   __shared__ double rs[APP_THREADS / WAVE];
   __shared__ int rk[APP_THREADS / WAVE];
+  __shared__ double s_score0;  // cluster 0's score
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int32_t* aoff = app_offsets + (size_t)h * (cs + 1);
   int32_t* aids = app_ids + (size_t)h * cap;
@@ -80,10 +81,11 @@ __global__ __launch_bounds__(APP_THREADS) void append_kernel(KT* __restrict__ kc
           }
       }
       if (l2) s0 = s0 - 0.5 * nn0;
-      if (c0 < C) {
+      if (c0 < C && s0 > best) {  // a NaN or -inf score never leads
         best = s0;
         bi = c0;
       }
+      if (tid == 0) s_score0 = s0;
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -106,7 +108,11 @@ __global__ __launch_bounds__(APP_THREADS) void append_kernel(KT* __restrict__ kc
         best = rs[v];
         bi = rk[v];
       }
-    const int lab = bi;
+    // non-finite scores follow the sequential rule (start from cluster 0, move
+    // only to a strictly larger score): when cluster 0 scores NaN, or no score
+    // exceeds -inf, the token joins cluster 0
+    const double sc0 = s_score0;
+    const int lab = (bi >= C || sc0 != sc0) ? 0 : bi;
     // insert pos at the end of cluster lab's appended segment
     const int a = aoff[cs];            // entries before this append
     const int p = aoff[lab + 1];

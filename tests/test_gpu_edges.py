@@ -9,6 +9,8 @@ of the GPU path's limits, through the C ABI:
   selection (duplicated centroids: the lowest id ranks first);
 - one cluster, and the largest cluster count the path supports (512);
 - zero and NaN key rows;
+- non-finite scores in the nearest-centroid append (a NaN operand row of
+  cluster 0 or of a later cluster, an infinite one, a NaN key);
 - a caller's selected count outside [0, B] in the standalone decode.
 
 Integer results bit-exact; attention within 2e-3 max-abs."""
@@ -28,6 +30,9 @@ kvc = pytest.importorskip("clustered_sparse_attention_kv_amd")
 
 G8 = synth.Workload("g8_bf16", 95, heads=4, G=8, L=2000, d=128, dtype=synth.BF16, M=24, sigma=0.3, n_out=4,
                     out_scale=10.0, C=48, iters=5, B=256, steps=3, query="mixture", q_sigma=0.2)
+APPEND_NF = synth.Workload("append_nonfinite_bf16", 97, heads=3, G=1, L=700, d=128, dtype=synth.BF16, M=12,
+                           sigma=0.3, n_out=4, out_scale=10.0, C=20, iters=4, B=100, steps=12, query="noisy_key",
+                           q_sigma=0.1, append=True)
 TIES = synth.Workload("ties_bf16", 96, heads=3, G=2, L=1300, d=128, dtype=synth.BF16, M=16, sigma=0.3, n_out=4,
                       out_scale=10.0, C=24, iters=6, B=200, steps=2, query="noisy_key", q_sigma=0.1)
 
@@ -266,6 +271,50 @@ def test_zero_and_nan_key_rows():
         assert np.array_equal(np.sort(ids[h]), np.arange(w.L))
         s, o, i = oracle.csr(lab[h], w.C)
         assert np.array_equal(sizes[h], s) and np.array_equal(ids[h], i)
+
+
+def test_append_non_finite_scores():
+    """The append's argmax follows the sequential rule (start from cluster 0,
+    move only to a strictly larger score) when scores are not finite: a NaN
+    operand row of a later cluster never wins (head 0), a NaN row of cluster 0
+    keeps every token there (head 1), an infinite component makes its cluster
+    score +-inf or NaN by the key's sign (head 2), and a NaN key goes to
+    cluster 0. Labels, sizes and index bit-exact with the oracle."""
+    w = APPEND_NF
+    base, K, V, init, means = make_inputs(w)
+    H = K.shape[0]
+    K = K.copy()
+    K[2, w.L + 3] = 0x7FC0                  # a NaN key (bf16 quiet NaN)
+    idx = kvc.ClusterIndex(H, w.C, w.capacity, torch.bfloat16)
+    Kc, Vc = np.zeros_like(K), np.zeros_like(V)
+    Kc[:, :w.L], Vc[:, :w.L] = K[:, :w.L], V[:, :w.L]
+    Kd, Vd = to_dev(Kc), to_dev(Vc)
+    kvc.build(idx, Kd, w.L, w.iters, seed=base)
+    torch.cuda.synchronize()
+    op = to_np(idx.centroids_op)
+    op[0, 5] = 0x7FC0                       # NaN row of a later cluster
+    op[1, 0] = 0x7FC0                       # NaN row of cluster 0
+    op[2, 3, 7] = 0x7F80                    # +inf in one channel
+    idx.centroids_op.copy_(to_dev(op))
+    built = dict(labels=to_np(idx.labels)[:, :w.L], sizes=to_np(idx.sizes), offsets=to_np(idx.offsets),
+                 token_ids=to_np(idx.token_ids)[:, :w.L], c=to_np(idx.centroids), chat=op[:, :w.C])
+    oi = oracle.Index(built, w.capacity)
+    labs = []
+    for t in range(w.steps):
+        n = w.L + t
+        kvc.append(idx, Kd, Vd, to_dev(np.ascontiguousarray(K[:, n:n + 1])),
+                   to_dev(np.ascontiguousarray(V[:, n:n + 1])))
+        labs.append(oi.append(np.ascontiguousarray(K[:, n])))
+    torch.cuda.synchronize()
+    n = w.L + w.steps
+    assert np.array_equal(to_np(idx.labels)[:, :n], oi.labels[:, :n])
+    assert np.array_equal(to_np(idx.sizes), oi.sizes)
+    off, ids = kvc.export_csr(idx)
+    assert np.array_equal(to_np(off), oi.offsets)
+    assert np.array_equal(to_np(ids)[:, :n], oi.token_ids[:, :n])
+    labs = np.stack(labs, axis=1)
+    assert np.all(labs[1] == 0) and np.all(labs[0] != 5) and labs[2, 3] == 0
+    say(f"  non-finite append labels: {labs.tolist()}")
 
 
 def test_sparse_decode_clamps_the_count():
