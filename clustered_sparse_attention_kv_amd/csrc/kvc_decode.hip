@@ -194,6 +194,10 @@ struct SelShared {
   int cid[WAVE];
   int ncand;
   int nrank;  // ranks that can hold clusters: 64 after the candidates' sort, else all
+  // early gather (select_phase<true>): clusters above the cut bin, one ballot
+  // per wave, and the flag wave 0 raises once the ranks are in LDS
+  unsigned long long cmask[SEL_THREADS / WAVE];
+  int ready;
 };
 
 // Value of lane (lane ^ S) within the wave, with lane operations only (no
@@ -339,9 +343,18 @@ __device__ __forceinline__ double centroid_chain(const double* qbar, const Centr
 }
 
 // Returns the cluster id of rank tid (ids >= X.ca are padding).
-template <typename QT>
+// EARLY (with early_ok): when at most 64 candidates need an order, wave 0
+// sorts them while the other waves return at once; *early is then true, the
+// ranks (W, obase, ..., total, nrank) are valid once S.ready is 1 (wave 0
+// sets it after writing them, with a release fence), and cmask marks the
+// clusters in bins above the cut: their sizes sum to less than the budget
+// left for clusters, so each is selected whole and they hold the first ranks.
+// Otherwise *early is false and every rank is in LDS on return (block
+// barrier), as without EARLY.
+template <bool EARLY = false, typename QT>
 __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__ q, int G, const IndexView& X, int h,
-                                            int B) {
+                                            int B, bool early_ok = false, bool* early = nullptr) {
+  if constexpr (EARLY) *early = false;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int C = X.ca, cs = X.cs;
   // Requests in this order: the query and the per-cluster metadata, then the
@@ -372,7 +385,10 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
   }
   if (tid < D) S.qbar[tid] = qs;
   if (tid < 256) S.hist[tid] = 0;
-  if (tid == 0) S.ncand = 0;
+  if (tid == 0) {
+    S.ncand = 0;
+    S.ready = 0;
+  }
   __syncthreads();
   unsigned long long key = 0;
   int id = C + tid;  // padding entries: worst key, distinct ids past the clusters
@@ -429,6 +445,10 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
     nq = __builtin_amdgcn_readlane(wave_incl_scan(nq), WAVE - 1);
     bstar = bc <= 0 ? 256 : (nq > 0 ? nq - 1 : 0);
   }
+  if constexpr (EARLY) {
+    const unsigned long long cm = __ballot(tid < C && bin > bstar && S.mn[tid] > 0);
+    if (lane == 0) S.cmask[w] = cm;
+  }
   if (tid < C && bin >= bstar) {
     const int slot = atomicAdd(&S.ncand, 1);
     if (slot < WAVE) {
@@ -468,10 +488,23 @@ __device__ __forceinline__ int select_phase(SelShared& S, const QT* __restrict__
         S.nrank = WAVE;
       }
       fid = i2;
+      if constexpr (EARLY) {
+        if (early_ok) {  // the ranks are in LDS: raise the flag after them
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          if (lane == 0) __hip_atomic_store(&S.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
+    }
+    if constexpr (EARLY) {
+      if (early_ok) {
+        *early = true;
+        return fid;
+      }
     }
     __syncthreads();
     return fid;
   }
+  if constexpr (EARLY) *early = false;
   // bitonic sort of all entries, best first ("better" = larger key, then smaller id)
   bitonic_sort<2, SEL_THREADS>(S, key, id, tid);
   // thread r now holds rank r; prefix of sizes in rank order
@@ -517,6 +550,34 @@ __device__ __forceinline__ int rank_entry(const SelShared& S, int r, int e, cons
 __device__ __forceinline__ int fixed_entry(int p, bool packed, const IndexView& X) {
   const int t = p < X.n_sink ? p : X.wlo + (p - X.n_sink);
   return packed ? ~t : t;
+}
+
+// Entry of member e of cluster k (built members first, then the appended
+// ones): rank_entry with the cluster's own offsets.
+__device__ __forceinline__ int cluster_entry(const SelShared& S, int k, int e, const int32_t* __restrict__ ids_h,
+                                             const int32_t* __restrict__ app_h, bool packed) {
+  const int nb = S.mb[k];
+  if (e < nb) return packed ? S.mo[k] + e : ids_h[S.mo[k] + e];
+  const int a = app_h[S.ma[k] + (e - nb)];
+  return packed ? ~a : a;
+}
+
+// Position of the set bit of rank r (from 0) in m (r < popcount(m)).
+__device__ __forceinline__ int nth_set_bit(unsigned long long m, int r) {
+  int pos = 0;
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) {
+    const unsigned long long lo = m & ((1ull << sh) - 1ull);
+    const int c = __popcll(lo);
+    if (r >= c) {
+      r -= c;
+      m >>= sh;
+      pos += sh;
+    } else {
+      m = lo;
+    }
+  }
+  return pos;
 }
 
 // Entry at output position p (< n_sink + nw + total) of the ranked, trimmed
@@ -598,9 +659,8 @@ __device__ __forceinline__ int select_count(const SelShared& S, const IndexView&
 
 // The selection's scores of the clusters in use, spread over the whole chip:
 // block (y, h) scores clusters 64 y .. 64 y + 63 of KV head h with the same
-// query sum and chains as select_phase, into scores[h * stride + k]. The fused
-// decode reads them (so its blocks do not each stream the head's centroids),
-// and the debug export returns them.
+// query sum and chains as select_phase, into scores[h * stride + k], which the
+// debug export returns.
 constexpr int SCORE_THREADS = 64;
 template <typename QT>
 __global__ __launch_bounds__(SCORE_THREADS) void scores_kernel(const QT* __restrict__ q, int G, const IndexView X,
@@ -1069,14 +1129,17 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
     if (j16 < G) v = *reinterpret_cast<const u32x4*>(q + ((size_t)h * G + j16) * D + 32 * s + 8 * kb4);
     qb[s] = __builtin_bit_cast(bf16x8, v);
   }
-  select_phase(S, q, G, X, h, B);
-  const int cnt = select_count(S, X, B);
+  // with the token split and no selected ids to return, the gather of the
+  // clusters above the cut starts before the candidates are ranked (below)
+  bool early = false;
+  select_phase<TS>(S, q, G, X, h, B, TS && sel_ids == nullptr, &early);
+  const int cnt = early ? 0 : select_count(S, X, B);  // (early: known once the ranks are)
   const long long cap = X.cap;
   // one block per head publishes the count and the unused entries; the
   // selected entries come from the block that stages them (all from block 0
   // without the token split)
   const bool writer = part == 0;
-  if (writer && sel_count && tid == 0) sel_count[h] = cnt;
+  if (writer && sel_count && tid == 0) sel_count[h] = select_count(S, X, B);  // wave 0 holds the ranks
   if (writer && sel_ids)
     for (int p = cnt + tid; p < B; p += SEL_THREADS) sel_ids[(size_t)h * B + p] = -1;
   const int32_t* ids_h = X.token_ids + (size_t)h * cap;
@@ -1211,12 +1274,80 @@ __global__ __launch_bounds__(SEL_THREADS) void select_decode_bf16_kernel(
       for (int t0 = w * 64; t0 < nb; t0 += NW * 64) do_slice(sel + t0, nb - t0 < 64 ? nb - t0 : 64);
     }
   } else {
+    // Early: output positions [0, P1) hold the sinks, the window and then the
+    // clusters above the cut bin in id order (each selected whole, together the
+    // first ranks), and the rank order takes over from P1. The softmax and the
+    // weighted sum do not depend on the order of the tokens, so a slice inside
+    // [0, P1) is staged and gathered before the candidates are ranked; a slice
+    // reaching past P1 waits for wave 0's flag. Every wave builds the same list
+    // of those clusters: lane i holds the i-th (ck) and its exclusive prefix of
+    // sizes (cpre).
+    const int nfix = X.n_sink + X.nw < B ? X.n_sink + X.nw : B;
+    int P1 = 0, ck = 0, cpre = 0, ncl = 0;
+    if (early) {
+      unsigned long long cmv[NW];
+      int cbase[NW + 1];
+      cbase[0] = 0;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        cmv[v] = S.cmask[v];
+        cbase[v + 1] = cbase[v] + __popcll(cmv[v]);
+      }
+      ncl = cbase[NW];
+      P1 = nfix;
+      if (ncl <= WAVE) {
+        unsigned long long m = 0;
+        int r = 0, kb = 0;
+#pragma unroll
+        for (int v = 0; v < NW; ++v)
+          if (lane >= cbase[v] && lane < cbase[v + 1]) {
+            m = cmv[v];
+            r = lane - cbase[v];
+            kb = v * WAVE;
+          }
+        ck = lane < ncl ? kb + nth_set_bit(m, r) : 0;
+        const int n = lane < ncl ? S.mn[ck] : 0;
+        const int x = wave_incl_scan(n);
+        cpre = x - n;
+        P1 = nfix + __builtin_amdgcn_readlane(x, WAVE - 1);
+      }
+    }
+    bool ranked = !early;
+    int lim_r = cnt;  // the selected count once ranked
     // slices part, part + P, ...: wave w takes the block's slices w, w + 8, ...
     // and stages each one's entries in its own 64 words of sel
-    for (int sl = part + P * w; sl * ST < cnt; sl += P * NW) {
-      const int t0 = sl * ST, n64 = cnt - t0 < ST ? cnt - t0 : ST;
+    for (int sl = part + P * w;; sl += P * NW) {
+      const int t0 = sl * ST;
+      if (!ranked && t0 + ST > P1) {  // the slice needs the ranks
+        while (__hip_atomic_load(&S.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+          __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        ranked = true;
+        lim_r = select_count(S, X, B);
+      }
+      const int lim = ranked ? lim_r : P1;
+      if (t0 >= lim) break;
+      const int n64 = lim - t0 < ST ? lim - t0 : ST;
+      const int p = t0 + lane;
+      int ent = 0;
+      if (lane < n64 && (p < nfix || p >= P1)) ent = select_emit(S, p, ids_h, app_h, packed, X);
+      // positions of the clusters above the cut in the slice: q in [qa, qb)
+      const int qa = (t0 > nfix ? t0 : nfix) - nfix;
+      const int qb = (t0 + n64 < P1 ? t0 + n64 : P1) - nfix;
+      if (qa < qb) {
+        // the clusters that overlap the slice, one at a time (wave-uniform
+        // loop; lane 0's prefix is 0 <= qa, so both ballots hold lane 0)
+        const unsigned long long lo = __ballot(lane < ncl && cpre <= qa);
+        const unsigned long long hi = __ballot(lane < ncl && cpre <= qb - 1);
+        const int ilo = 63 - __clzll(lo), ihi = 63 - __clzll(hi);
+        const int qq = p - nfix;
+        for (int i = ilo; i <= ihi; ++i) {
+          const int k = __builtin_amdgcn_readlane(ck, i), pre = __builtin_amdgcn_readlane(cpre, i);
+          if (lane < n64 && p >= nfix && p < P1 && qq >= pre && qq < pre + S.mn[k])
+            ent = cluster_entry(S, k, qq - pre, ids_h, app_h, packed);
+        }
+      }
       if (lane < n64) {
-        const int ent = select_emit(S, t0 + lane, ids_h, app_h, packed, X);
         sel[w * 64 + lane] = ent;
         if (sel_ids) sel_ids[(size_t)h * B + t0 + lane] = sel_token(ids_h, ent, packed);
       }

@@ -75,6 +75,10 @@ def check_decode_paths(w, idx, K, V, Kd, Vd, q, B, packed_too=True):
         torch.cuda.synchronize()
         assert np.array_equal(to_np(fsel), osel) and np.array_equal(to_np(fcnt), ocnt)
         errs.append(float(np.abs(to_np(fout) - od).max()))
+        if ws is not None:  # no ids to return: the clusters above the cut are gathered before the ranking
+            fout = kvc.select_decode(idx, qd, Kd, Vd, B, scale, workspace=ws)
+            torch.cuda.synchronize()
+            errs.append(float(np.abs(to_np(fout) - od).max()))
     if packed_too and idx.k_packed is not None:
         kvc.pack(idx, Kd, Vd)
         for ws in wss:
@@ -84,6 +88,10 @@ def check_decode_paths(w, idx, K, V, Kd, Vd, q, B, packed_too=True):
             torch.cuda.synchronize()
             assert np.array_equal(to_np(fsel), osel) and np.array_equal(to_np(fcnt), ocnt)
             errs.append(float(np.abs(to_np(fout) - od).max()))
+            if ws is not None:
+                fout = kvc.select_decode(idx, qd, Kd, Vd, B, scale, workspace=ws)
+                torch.cuda.synchronize()
+                errs.append(float(np.abs(to_np(fout) - od).max()))
     assert max(errs) <= 2e-3, errs
     return errs
 

@@ -80,6 +80,8 @@ def check_step(w, idx, K, V, Kd, Vd, q, B, scale, c=None, sizes=None, offsets=No
     tcnt = torch.empty(H, dtype=torch.int32, device="cuda")
     tout = kvc.select_decode(idx, qd, Kd, Vd, B, scale, sel_ids=tsel, sel_count=tcnt,
                              workspace=split_ws(idx, H * w.G))
+    # and without ids to return (the clusters above the cut gathered before the ranking)
+    eout = kvc.select_decode(idx, qd, Kd, Vd, B, scale, workspace=split_ws(idx, H * w.G))
     if split:
         sel, cnt = kvc.select(idx, qd, B)
         out = kvc.sparse_decode(qd, Kd, Vd, sel, cnt, scale)
@@ -92,7 +94,8 @@ def check_step(w, idx, K, V, Kd, Vd, q, B, scale, c=None, sizes=None, offsets=No
     assert np.array_equal(to_np(fcnt), ocnt) and np.array_equal(to_np(fsel), osel)
     assert np.array_equal(to_np(tcnt), ocnt) and np.array_equal(to_np(tsel), osel)
     od = oracle.decode(q, w.G, K, V, osel, ocnt, scale)
-    ferr = max(float(np.abs(to_np(fout) - od).max()), float(np.abs(to_np(tout) - od).max()))
+    ferr = max(float(np.abs(to_np(fout) - od).max()), float(np.abs(to_np(tout) - od).max()),
+               float(np.abs(to_np(eout) - od).max()))
     err = float(np.abs(to_np(out) - od).max()) if split else 0.0
     if split:
         assert np.array_equal(to_np(sel), osel) and np.array_equal(to_np(cnt), ocnt)

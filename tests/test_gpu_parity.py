@@ -191,6 +191,12 @@ def check_step(w, idx, base, K, V, Kd, Vd, means, gc, step, B, scale, packed):
         torch.cuda.synchronize()
         assert np.array_equal(to_np(fcnt), ocnt) and np.array_equal(to_np(fsel), osel), (B, ws is None)
         ferrs.append(np.abs(to_np(fout) - od).max())
+        if ws is not None:  # no ids to return: the clusters above the cut are gathered before the ranking
+            fcnt2 = torch.empty(H, dtype=torch.int32, device="cuda")
+            fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, sel_count=fcnt2, workspace=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_np(fcnt2), ocnt), B
+            ferrs.append(np.abs(to_np(fout) - od).max())
     say(f"  B={B}{' packed' if packed else ''}: count {to_np(cnt).tolist()[:4]}, decode max abs err {err:.3e}, "
         f"fused {ferrs[0]:.3e}, token split {ferrs[1]:.3e}")
     assert err <= 2e-3 and max(ferrs) <= 2e-3
@@ -360,6 +366,10 @@ def test_attention_sinks_end_to_end():
                 torch.cuda.synchronize()
                 assert np.array_equal(to_np(fsel), osel), (step, B, pk, ws is None)
                 assert np.abs(to_np(fout) - od).max() <= 2e-3, (step, B, pk, ws is None)
+                if ws is not None:
+                    fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, workspace=ws)
+                    torch.cuda.synchronize()
+                    assert np.abs(to_np(fout) - od).max() <= 2e-3, (step, B, pk, "no ids")
             idx._s.packed = 1
         say(f"  sinks: step {step}, {n} tokens, count {ocnt.tolist()}")
 
@@ -423,6 +433,10 @@ def test_window_clustering_end_to_end():
             torch.cuda.synchronize()
             assert np.array_equal(to_np(fsel), osel), (step, B, pk, ws is None)
             assert np.abs(to_np(fout) - od).max() <= 2e-3, (step, B, pk, ws is None)
+            if ws is not None:
+                fout = kvc.select_decode(idx, to_dev(q), Kd, Vd, B, scale, workspace=ws)
+                torch.cuda.synchronize()
+                assert np.abs(to_np(fout) - od).max() <= 2e-3, (step, B, pk, "no ids")
         idx._s.packed = 1
 
     while n < w.capacity:
