@@ -325,6 +325,55 @@ def test_append_non_finite_scores():
     say(f"  non-finite append labels: {labs.tolist()}")
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_fused_decode_random_shapes(seed):
+    """The fused selection and attention with the token split, with and
+    without selected ids to return (without them, the clusters above the cut
+    bin are gathered before the candidates are ranked), from the caches and
+    from the packed copy, on seeded random shapes: head counts, query heads
+    per KV head, context lengths, cluster counts from 1 to 400, budgets from 1
+    token to more than the context, with and without attention sinks.
+    Selection bit-exact and attention within 2e-3 of the oracle."""
+    rng = np.random.default_rng(4000 + seed)
+    H = int(rng.integers(1, 5))
+    G = int(rng.choice([1, 2, 4]))
+    L = int(rng.integers(300, 3000))
+    n_sink = int(rng.choice([0, 5]))
+    C = int(min(rng.choice([1, 7, 40, 150, 400]), L - n_sink))
+    w = synth.Workload(f"random_{seed}", 200 + seed, heads=H, G=G, L=L, d=128, dtype=synth.BF16, M=16, sigma=0.3,
+                       n_out=4, out_scale=10.0, C=C, iters=3, B=1, steps=3, query="noisy_key", q_sigma=0.1)
+    base, K, V, init, means = make_inputs(w)
+    idx = kvc.ClusterIndex(H, C, L, torch.bfloat16, packed=True, n_sink=n_sink)
+    Kd, Vd = to_dev(K), to_dev(V)
+    kvc.build(idx, Kd, L, w.iters, seed=base)
+    torch.cuda.synchronize()
+    c, sizes, offsets, ids = to_np(idx.centroids), to_np(idx.sizes), to_np(idx.offsets), to_np(idx.token_ids)
+    scale = 1.0 / math.sqrt(w.d)
+    budgets = sorted({1, int(rng.integers(2, 64)), int(rng.integers(64, L)), L + 50})
+    errs = []
+    for step, B in enumerate(budgets):
+        q = queries(w, base, step, K, L, means)
+        qd = to_dev(q)
+        osel, ocnt, _, _ = oracle.select(q, G, c, sizes, offsets, ids, B, n_sink=n_sink)
+        od = oracle.decode(q, G, K, V, osel, ocnt, scale)
+        for pk in (0, 1):
+            if pk:
+                kvc.pack(idx, Kd, Vd)
+            idx._s.packed = pk
+            ws = split_ws(idx, H * G)
+            fsel = torch.full((H, B), -7, dtype=torch.int32, device="cuda")
+            fcnt = torch.empty(H, dtype=torch.int32, device="cuda")
+            fout = kvc.select_decode(idx, qd, Kd, Vd, B, scale, sel_ids=fsel, sel_count=fcnt, workspace=ws)
+            ecnt = torch.empty(H, dtype=torch.int32, device="cuda")
+            eout = kvc.select_decode(idx, qd, Kd, Vd, B, scale, sel_count=ecnt, workspace=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_np(fsel), osel) and np.array_equal(to_np(fcnt), ocnt), (B, pk)
+            assert np.array_equal(to_np(ecnt), ocnt), (B, pk)
+            errs += [float(np.abs(to_np(fout) - od).max()), float(np.abs(to_np(eout) - od).max())]
+    say(f"  H={H} G={G} L={L} C={C} sinks={n_sink} budgets={budgets}: max abs err {max(errs):.2e}")
+    assert max(errs) <= 2e-3, errs
+
+
 def test_sparse_decode_clamps_the_count():
     """kv_sparse_decode takes a count above B as B and a negative one as 0,
     and gives entries outside [0, capacity) no weight."""
